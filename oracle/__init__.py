@@ -1,0 +1,355 @@
+"""CPU oracle for the DSpark per-step draft -> schedule -> verify path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package; only the tests, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP implementation.
+
+Plain, slow, fp64 NumPy, request by request and position by position, in the
+order and notation of the pages:
+
+* "DSpark: speculative decoding that fixes suffix quality and production
+  verification waste" (papers.franksyz.com explainer), sections 2-4 and 7-10;
+* llama.cpp PR #25173 "spec: add DSpark speculative decoding", description
+  (anchor-first block, Markov bias on device, greedy losslessness).
+
+Inputs are widened exactly (fp32 -> fp64, bfloat16 bits -> fp64).  Every
+uniform-driven or argmax decision is also reported with a flag when it falls
+within 1e-6 of its decision boundary, so that a comparison against a
+different-precision implementation can tell a legitimate rounding flip from a
+bug.
+
+Readings of points the pages leave open (each also listed in the design notes):
+  * position 0 is biased with prev = anchor (anchor-first block);
+  * the bias is added to the logits before the temperature: q = softmax((U+B)/T);
+  * draft and target use the same per-request temperature; T <= 0 (or NaN)
+    means greedy for both;
+  * inverse-CDF sampling walks the vocabulary in index order and returns the
+    first index whose inclusive cumulative mass exceeds u * Z (strict); if
+    rounding leaves none, the last index with positive mass;
+  * greedy acceptance: accept y_k iff y_k is the lowest-index argmax of the
+    target row; correction and bonus are that argmax (the T -> 0 limit);
+  * the residual max(0, p - q) with zero total mass falls back to p;
+  * q_stats = (max_v s_v, Z) with s = U + B and Z = sum_v exp((s_v - max s)/T);
+    for greedy requests (max s, 1), q_tok = 1, p_tok = 1 on a match else 0;
+  * survival a is the fp32 left-to-right running product of c clamped to
+    [0, 1] (NaN -> 0), so the schedule is reproducible bit for bit;
+  * the scheduler ranks candidates by (a descending, k ascending, r ascending)
+    and takes min(K, R*gamma) of them; each request keeps its anchor row, so
+    it owns l[r] + 1 verify rows.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "NEAR", "widen", "markov_bias", "inverse_cdf", "draft_block", "survival",
+    "schedule", "verify", "step", "DraftResult", "ScheduleResult", "VerifyResult",
+]
+
+#: width of the band around a decision boundary inside which a flip caused by
+#: rounding is tolerated (in normalised probability-mass units)
+NEAR = 1e-6
+
+
+def widen(W: np.ndarray, wdtype: str) -> np.ndarray:
+    """Weights as fp64: bf16 bit patterns (uint16) or fp32 values, exactly."""
+    if wdtype == "bf16":
+        bits = np.asarray(W, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if wdtype == "f32":
+        return np.asarray(W, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown wdtype {wdtype!r}")
+
+
+def markov_bias(W1_64: np.ndarray, W2_64: np.ndarray, prev) -> np.ndarray:
+    """Markov head bias conditioned on the previous token.
+
+    The explainer (section 7) writes the drafter logits as base logits U_k
+    plus a prefix-dependent bias B_k, the Markov head using a low-rank
+    factorisation instead of a V x V transition table; the llama.cpp PR
+    (description) gives bias(prev) = markov_w2 . markov_w1[prev].  For a
+    vector of prev ids this returns one bias row per id, shape [len(prev), V].
+    """
+    prev = np.atleast_1d(np.asarray(prev, dtype=np.int64))
+    return (W2_64 @ W1_64[prev].T).T
+
+
+def inverse_cdf(w: np.ndarray, u: float):
+    """Inverse-CDF draw from the unnormalised non-negative weights ``w``.
+
+    Returns (index, Z, flag): the first index whose inclusive cumulative sum
+    exceeds u * Z, Z = total mass, and whether u * Z lies within NEAR * Z of
+    either edge of the chosen interval."""
+    C = np.cumsum(w)
+    Z = float(C[-1])
+    theta = float(u) * Z
+    y = int(np.searchsorted(C, theta, side="right"))
+    if y >= len(w):
+        y = int(np.flatnonzero(w > 0)[-1])
+    lo = float(C[y - 1]) if y > 0 else 0.0
+    flag = min(abs(float(C[y]) - theta), abs(theta - lo)) <= NEAR * Z
+    return y, Z, bool(flag)
+
+
+def _is_greedy(T: float) -> bool:
+    return not (T > 0.0)
+
+
+def _argmax_with_gap(s: np.ndarray):
+    """Lowest-index argmax and whether the runner-up is within the near-tie band."""
+    y = int(np.argmax(s))
+    if len(s) == 1:
+        return y, False
+    top = float(s[y])
+    rest = np.delete(s, y)
+    gap = top - float(rest.max())
+    return y, bool(gap <= NEAR * max(1.0, abs(top)))
+
+
+@dataclass
+class DraftResult:
+    y: np.ndarray            # int32 [R, gamma]   (-1 where not computed)
+    q_tok: np.ndarray        # fp64 [R, gamma]
+    q_stats: np.ndarray      # fp64 [R, gamma, 2]  (max s, Z)
+    flags: dict = field(default_factory=dict)   # (r, k) -> kind
+    s: Optional[dict] = None                    # (r, k) -> fp64 biased logits, if kept
+
+
+def draft_block(U, W1, W2, wdtype, anchor, temp, u_draft, *,
+                requests: Optional[Sequence[int]] = None,
+                prev_override: Optional[np.ndarray] = None,
+                keep_s: bool = False) -> DraftResult:
+    """Draft one block left to right.
+
+    For each request and k = 0..gamma-1: prev = anchor at k = 0, else the
+    token drafted at k-1 (or ``prev_override[r, k-1]`` to teacher-force a
+    prefix); s = U_k + W2 . W1[prev]; greedy takes the lowest-index argmax of
+    s; sampled draws by inverse CDF from exp(s/T - max) with u_draft[r, k].
+    (Explainer sections 2, 6, 7; llama.cpp PR description: anchor-first block
+    sampled left to right with bias(prev).)"""
+    U = np.asarray(U)
+    R, gamma, V = U.shape
+    reqs = list(range(R)) if requests is None else [int(r) for r in requests]
+    W1_64, W2_64 = widen(W1, wdtype), widen(W2, wdtype)
+    y = np.full((R, gamma), -1, dtype=np.int32)
+    q_tok = np.full((R, gamma), np.nan)
+    q_stats = np.full((R, gamma, 2), np.nan)
+    flags = {}
+    kept = {} if keep_s else None
+    prev = {r: int(anchor[r]) for r in reqs}
+    for k in range(gamma):
+        if k > 0:
+            for r in reqs:
+                prev[r] = int(prev_override[r, k - 1]) if prev_override is not None else int(y[r, k - 1])
+        B = markov_bias(W1_64, W2_64, [prev[r] for r in reqs]) if reqs else None
+        for i, r in enumerate(reqs):
+            s = U[r, k].astype(np.float64) + B[i]
+            if keep_s:
+                kept[(r, k)] = s
+            T = float(temp[r])
+            Ms = float(s.max())
+            if _is_greedy(T):
+                yk, near = _argmax_with_gap(s)
+                y[r, k] = yk
+                q_tok[r, k] = 1.0
+                q_stats[r, k] = (Ms, 1.0)
+                if near:
+                    flags[(r, k)] = "draft-near-tie"
+            else:
+                x = s / T
+                w = np.exp(x - x.max())
+                yk, Z, near = inverse_cdf(w, float(u_draft[r, k]))
+                y[r, k] = yk
+                q_tok[r, k] = float(w[yk]) / Z
+                q_stats[r, k] = (Ms, Z)
+                if near:
+                    flags[(r, k)] = "draft-cdf-boundary"
+    return DraftResult(y=y, q_tok=q_tok, q_stats=q_stats, flags=flags, s=kept)
+
+
+def survival(c) -> np.ndarray:
+    """Survival a[r, k]: the probability that the prefix up to k survives, the
+    running product of the per-position acceptance estimates c (explainer
+    section 8; section 5: a suffix position's value is a product of conditional
+    acceptance rates).  Defined as the fp32 left-to-right product of c clamped
+    to [0, 1] (NaN -> 0)."""
+    c = np.asarray(c, dtype=np.float32)
+    cc = np.where(np.isnan(c), np.float32(0), np.clip(c, np.float32(0), np.float32(1))).astype(np.float32)
+    a = np.empty_like(cc)
+    if cc.shape[1] == 0:
+        return a
+    a[:, 0] = cc[:, 0]
+    for k in range(1, cc.shape[1]):
+        a[:, k] = (a[:, k - 1] * cc[:, k]).astype(np.float32)
+    return a
+
+
+@dataclass
+class ScheduleResult:
+    a: np.ndarray            # fp32 [R, gamma]
+    l: np.ndarray            # int32 [R]
+    row_offsets: np.ndarray  # int32 [R + 1]
+    row_req: np.ndarray      # int32 [n_rows]
+    row_pos: np.ndarray      # int32 [n_rows]
+    row_tok: np.ndarray      # int32 [n_rows]
+    expected_tokens: float
+    Kc: int
+
+
+def schedule(c, K: int, anchor, y) -> ScheduleResult:
+    """Causal, prefix-closed global top-K verify scheduler.
+
+    Rank every candidate (r, k) by survival a[r, k] (descending), breaking ties
+    by k then r (ascending), and keep the first Kc = min(K, R*gamma): a top-K
+    prefix selection over current cumulative confidence within a capacity
+    fixed ahead of time (explainer sections 9-10).  Because a is
+    non-increasing in k the selection is prefix-closed ("no verifying position
+    5 alone").  The decision reads only c and K, never the drafted tokens
+    (section 4, causal admission).  The variable-length verify work is then
+    flattened into contiguous rows with per-request offsets instead of padding
+    (section 13): request r owns rows off[r] .. off[r] + l[r], row j of which
+    is fed the anchor (j = 0) or y[r, j-1]."""
+    a = survival(c)
+    R, gamma = a.shape
+    Kc = int(min(max(int(K), 0), R * gamma))
+    cand = sorted((-float(a[r, k]), k, r) for r in range(R) for k in range(gamma))[:Kc]
+    l = np.zeros(R, dtype=np.int64)
+    sel_a = []
+    for negv, k, r in cand:
+        l[r] += 1
+        sel_a.append(-negv)
+    off = np.zeros(R + 1, dtype=np.int64)
+    off[1:] = np.cumsum(l + 1)
+    n_rows = int(off[-1])
+    row_req = np.empty(n_rows, dtype=np.int32)
+    row_pos = np.empty(n_rows, dtype=np.int32)
+    row_tok = np.empty(n_rows, dtype=np.int32)
+    for r in range(R):
+        for j in range(int(l[r]) + 1):
+            i = int(off[r]) + j
+            row_req[i] = r
+            row_pos[i] = j
+            row_tok[i] = int(anchor[r]) if j == 0 else int(y[r, j - 1])
+    return ScheduleResult(a=a, l=l.astype(np.int32), row_offsets=off.astype(np.int32),
+                          row_req=row_req, row_pos=row_pos, row_tok=row_tok,
+                          expected_tokens=R + math.fsum(sel_a), Kc=Kc)
+
+
+@dataclass
+class VerifyResult:
+    n_accept: np.ndarray     # int32 [R]  (-1 where not computed)
+    out_tok: np.ndarray      # int32 [R]
+    p_tok: np.ndarray        # fp64 [R, gamma]
+    flags: dict = field(default_factory=dict)   # (stage, r, j) -> kind
+
+    def emitted(self, r: int, y) -> list:
+        n = int(self.n_accept[r])
+        return [int(t) for t in y[r, :n]] + [int(self.out_tok[r])]
+
+
+def _softmax_T(row: np.ndarray, T: float) -> np.ndarray:
+    x = np.asarray(row, dtype=np.float64) / T
+    e = np.exp(x - x.max())
+    return e / math.fsum(e)
+
+
+def verify(target_rows, row_offsets, U, W1, W2, wdtype, anchor, y, q_tok, temp,
+           u_accept, u_final, *, requests: Optional[Sequence[int]] = None) -> VerifyResult:
+    """Verify drafted blocks against target logits.
+
+    Request r owns target rows off[r] .. off[r+1]-1; its verify length is
+    l = rows - 1 and row j is the target distribution p_j at draft position j
+    (row l is the bonus position).  Left to right: accept y_j with probability
+    min(1, p_j(y_j) / q(y_j)) (accept iff u_accept < p/q); the first rejection
+    discards the rest of the block (explainer section 2).  On a rejection at
+    j the correction is drawn from the normalised residual max(0, p_j - q_j)
+    (section 3: resampling from the full p would double-count the overlap);
+    if every verified draft is accepted a bonus token is drawn from p_l.  The
+    drafter distribution q_j is recomputed from U_j and the Markov bias with
+    prev = anchor (j = 0) or y_{j-1}.  Greedy requests accept iff the draft is
+    the target argmax, and emit the argmax as correction or bonus, which makes
+    the output identical to target-only greedy decoding (llama.cpp PR,
+    "Losslessness")."""
+    target_rows = np.asarray(target_rows)
+    off = np.asarray(row_offsets, dtype=np.int64)
+    R = len(off) - 1
+    gamma = np.asarray(y).shape[1]
+    reqs = list(range(R)) if requests is None else [int(r) for r in requests]
+    W1_64 = W2_64 = None
+    n_accept = np.full(R, -1, dtype=np.int32)
+    out_tok = np.full(R, -1, dtype=np.int32)
+    p_tok = np.full((R, gamma), np.nan)
+    flags = {}
+    for r in reqs:
+        i0 = int(off[r])
+        l = int(off[r + 1]) - i0 - 1
+        if l < 0 or l > gamma:
+            raise ValueError(f"request {r}: {l + 1} verify rows for gamma={gamma}")
+        T = float(temp[r])
+        greedy = _is_greedy(T)
+        p_tok[r, :] = 0.0
+        n = l
+        for j in range(l):
+            t = target_rows[i0 + j]
+            if greedy:
+                ok = int(y[r, j]) == int(np.argmax(t))
+                p_tok[r, j] = 1.0 if ok else 0.0
+            else:
+                p = _softmax_T(t, T)
+                p_tok[r, j] = float(p[int(y[r, j])])
+                ratio = p_tok[r, j] / float(q_tok[r, j])
+                uu = float(u_accept[r, j])
+                ok = uu < ratio
+                if ratio < 1.0 and abs(uu - ratio) <= NEAR:
+                    flags[("accept", r, j)] = "accept-boundary"
+            if not ok and n == l:
+                n = j
+        n_accept[r] = n
+        if n < l:
+            t = target_rows[i0 + n]
+            if greedy:
+                out_tok[r] = int(np.argmax(t))
+            else:
+                if W1_64 is None:
+                    W1_64, W2_64 = widen(W1, wdtype), widen(W2, wdtype)
+                prev = int(anchor[r]) if n == 0 else int(y[r, n - 1])
+                s = np.asarray(U[r, n], dtype=np.float64) + markov_bias(W1_64, W2_64, [prev])[0]
+                q = _softmax_T(s, T)
+                p = _softmax_T(t, T)
+                w = np.maximum(0.0, p - q)
+                if math.fsum(w) == 0.0:
+                    out, _, near = inverse_cdf(p, float(u_final[r]))
+                else:
+                    out, _, near = inverse_cdf(w, float(u_final[r]))
+                out_tok[r] = out
+                if near:
+                    flags[("final", r, n)] = "residual-cdf-boundary"
+        else:
+            t = target_rows[i0 + l]
+            if greedy:
+                out_tok[r] = int(np.argmax(t))
+            else:
+                x = np.asarray(t, dtype=np.float64) / T
+                out, _, near = inverse_cdf(np.exp(x - x.max()), float(u_final[r]))
+                out_tok[r] = out
+                if near:
+                    flags[("final", r, l)] = "bonus-cdf-boundary"
+    return VerifyResult(n_accept=n_accept, out_tok=out_tok, p_tok=p_tok, flags=flags)
+
+
+def step(inp, *, K: Optional[int] = None, requests: Optional[Sequence[int]] = None):
+    """One whole oracle step on a ``synth.StepInputs``-like object:
+    draft -> schedule -> gather the scheduled target rows -> verify.
+    Returns (DraftResult, ScheduleResult, target_rows, VerifyResult)."""
+    d = draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
+                    requests=requests)
+    y = d.y
+    sch = schedule(inp.c, inp.K if K is None else K, inp.anchor, np.where(y < 0, 0, y))
+    rows = np.asarray(inp.target)[sch.row_req.astype(np.int64), sch.row_pos.astype(np.int64)]
+    v = verify(rows, sch.row_offsets, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, y,
+               d.q_tok, inp.temp, inp.u_accept, inp.u_final, requests=requests)
+    return d, sch, rows, v
