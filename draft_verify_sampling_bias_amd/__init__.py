@@ -1,0 +1,321 @@
+"""Python binding of libdspark (the DSpark draft -> schedule -> verify hot path
+on MI355X / gfx950).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+outputs and workspaces are allocated with torch on the inputs' device, and
+the C entry points of ``libdspark.so`` (declared in include/dspark.h) are
+called on the current torch stream.  Every step of the computation runs in the
+library's HIP kernels; there is no other implementation to fall back to, and
+the first call fails loudly (ImportError) if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "LIB_PATH", "get_lib", "Status", "DsparkError", "dspark_draft_block", "dspark_schedule",
+    "dspark_verify", "dspark_schedule_rows", "dspark_draft_workspace_size",
+    "dspark_verify_workspace_size", "dspark_status_string", "dspark_abi_version",
+    "DraftArgs", "ScheduleArgs", "VerifyArgs", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
+
+W_F32, W_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
+    "dspark_schedule", "dspark_verify", "dspark_schedule_rows", "dspark_status_string",
+    "dspark_abi_version",
+)
+
+
+class Status:
+    OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_ABI, ERR_HIP = range(9)
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({dspark_status_string(status)})")
+
+
+_p = ctypes.c_void_p
+
+
+class DraftArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("V", ctypes.c_int32), ("rank", ctypes.c_int32), ("wdtype", ctypes.c_int32),
+                ("U", _p), ("W1", _p), ("W2", _p), ("anchor", _p), ("temp", _p), ("u_draft", _p),
+                ("y", _p), ("q_tok", _p), ("q_stats", _p), ("workspace", _p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("prof_events", _p)]
+
+
+class ScheduleArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("K", ctypes.c_int64), ("c", _p), ("anchor", _p), ("y", _p), ("a", _p), ("l", _p),
+                ("row_offsets", _p), ("row_req", _p), ("row_pos", _p), ("row_tok", _p),
+                ("expected_tokens", _p), ("stream", _p)]
+
+
+class VerifyArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("V", ctypes.c_int32), ("rank", ctypes.c_int32), ("wdtype", ctypes.c_int32),
+                ("n_rows", ctypes.c_int64), ("target", _p), ("row_offsets", _p), ("U", _p), ("W1", _p),
+                ("W2", _p), ("anchor", _p), ("temp", _p), ("y", _p), ("q_tok", _p), ("q_stats", _p),
+                ("u_accept", _p), ("u_final", _p), ("n_accept", _p), ("out_tok", _p), ("p_tok", _p),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("stream", _p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m draft_verify_sampling_bias_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    L.dspark_draft_workspace_size.argtypes = [P(DraftArgs), P(ctypes.c_size_t)]
+    L.dspark_verify_workspace_size.argtypes = [P(VerifyArgs), P(ctypes.c_size_t)]
+    L.dspark_draft_block.argtypes = [P(DraftArgs)]
+    L.dspark_schedule.argtypes = [P(ScheduleArgs)]
+    L.dspark_verify.argtypes = [P(VerifyArgs)]
+    for f in ("dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
+              "dspark_schedule", "dspark_verify", "dspark_abi_version"):
+        getattr(L, f).restype = ctypes.c_int
+    L.dspark_schedule_rows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+    L.dspark_schedule_rows.restype = ctypes.c_int64
+    L.dspark_status_string.argtypes = [ctypes.c_int]
+    L.dspark_status_string.restype = ctypes.c_char_p
+    L.dspark_abi_version.argtypes = []
+    return L
+
+
+_LIB = None
+
+
+def get_lib():
+    """The loaded libdspark.so (ctypes.CDLL); raises ImportError if it has not
+    been built."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def dspark_status_string(status: int) -> str:
+    return get_lib().dspark_status_string(int(status)).decode()
+
+
+def dspark_abi_version() -> int:
+    return int(get_lib().dspark_abi_version())
+
+
+def dspark_schedule_rows(R: int, gamma: int, K: int) -> int:
+    return int(get_lib().dspark_schedule_rows(int(R), int(gamma), int(K)))
+
+
+def _check(fn: str, status: int):
+    if status != Status.OK:
+        raise DsparkError(fn, status)
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _want(t, name: str, dtype, shape: Sequence[int], device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _wdtype(W1, W2):
+    torch = _torch()
+    if W1.dtype != W2.dtype:
+        raise TypeError("W1 and W2 must share a dtype")
+    if W1.dtype == torch.bfloat16:
+        return W_BF16
+    if W1.dtype == torch.float32:
+        return W_F32
+    raise TypeError(f"W1/W2 dtype {W1.dtype}: expected torch.bfloat16 or torch.float32")
+
+
+def _stream(device, stream):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if workspace is not None:
+        if workspace.device != device or workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace must hold {nbytes} bytes on {device}")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def draft_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int) -> int:
+    a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wdtype)
+    n = ctypes.c_size_t(0)
+    _check("dspark_draft_workspace_size", get_lib().dspark_draft_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return int(n.value)
+
+
+def verify_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, n_rows: int) -> int:
+    a = VerifyArgs(struct_size=ctypes.sizeof(VerifyArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wdtype,
+                   n_rows=n_rows)
+    n = ctypes.c_size_t(0)
+    _check("dspark_verify_workspace_size", get_lib().dspark_verify_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return int(n.value)
+
+
+dspark_draft_workspace_size = draft_workspace_bytes
+dspark_verify_workspace_size = verify_workspace_bytes
+
+
+def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=None, stream=None,
+                       prof_events=None):
+    """Draft gamma tokens per request (include/dspark.h, dspark_draft_block).
+
+    U [R, gamma, V] fp32; W1, W2 [V, rank] bf16 or fp32; anchor [R] int32;
+    temp [R] fp32; u_draft [R, gamma] fp32.  Returns (y int32 [R, gamma],
+    q_tok fp32 [R, gamma], q_stats fp32 [R, gamma, 2]).  ``out`` may supply
+    those three tensors; ``prof_events`` a list of 2*gamma torch.cuda.Event
+    (already recorded once) timed around each position's fused bias kernel."""
+    torch = _torch()
+    dev = U.device
+    R, gamma, V = U.shape
+    rank = W1.shape[1]
+    wd = _wdtype(W1, W2)
+    _want(U, "U", torch.float32, (R, gamma, V), dev)
+    _want(W1, "W1", W1.dtype, (V, rank), dev)
+    _want(W2, "W2", W1.dtype, (V, rank), dev)
+    _want(anchor, "anchor", torch.int32, (R,), dev)
+    _want(temp, "temp", torch.float32, (R,), dev)
+    _want(u_draft, "u_draft", torch.float32, (R, gamma), dev)
+    if out is None:
+        y = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+        q_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+        q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
+    else:
+        y, q_tok, q_stats = out
+        _want(y, "y", torch.int32, (R, gamma), dev)
+        _want(q_tok, "q_tok", torch.float32, (R, gamma), dev)
+        _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
+    nbytes = draft_workspace_bytes(R, gamma, V, rank, wd)
+    ws = _workspace(nbytes, dev, workspace)
+    ev_arr = None
+    if prof_events is not None:
+        if len(prof_events) != 2 * gamma:
+            raise ValueError(f"prof_events needs {2 * gamma} events")
+        ev_arr = (ctypes.c_void_p * len(prof_events))(*[e.cuda_event for e in prof_events])
+    a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd,
+                  U=_ptr(U), W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp),
+                  u_draft=_ptr(u_draft), y=_ptr(y), q_tok=_ptr(q_tok), q_stats=_ptr(q_stats),
+                  workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(),
+                  stream=_stream(dev, stream),
+                  prof_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+    _check("dspark_draft_block", get_lib().dspark_draft_block(ctypes.byref(a)))
+    return y, q_tok, q_stats
+
+
+def dspark_schedule(c, K: int, anchor, y, *, out=None, want_expected: bool = True, stream=None):
+    """Survival + causal prefix-closed top-K schedule (include/dspark.h,
+    dspark_schedule).  c [R, gamma] fp32; anchor [R] int32; y [R, gamma] int32.
+    Returns a dict with a, l, row_offsets, row_req, row_pos, row_tok and
+    expected_tokens (or None)."""
+    torch = _torch()
+    dev = c.device
+    R, gamma = c.shape
+    _want(c, "c", torch.float32, (R, gamma), dev)
+    _want(anchor, "anchor", torch.int32, (R,), dev)
+    _want(y, "y", torch.int32, (R, gamma), dev)
+    n_rows = dspark_schedule_rows(R, gamma, K)
+    if n_rows < 0:
+        raise ValueError("invalid R / gamma")
+    if out is None:
+        out = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                   l=torch.empty(R, dtype=torch.int32, device=dev),
+                   row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
+                   row_req=torch.empty(n_rows, dtype=torch.int32, device=dev),
+                   row_pos=torch.empty(n_rows, dtype=torch.int32, device=dev),
+                   row_tok=torch.empty(n_rows, dtype=torch.int32, device=dev),
+                   expected_tokens=torch.empty(1, dtype=torch.float32, device=dev) if want_expected else None)
+    else:
+        _want(out["a"], "a", torch.float32, (R, gamma), dev)
+        _want(out["l"], "l", torch.int32, (R,), dev)
+        _want(out["row_offsets"], "row_offsets", torch.int32, (R + 1,), dev)
+        for f in ("row_req", "row_pos", "row_tok"):
+            _want(out[f], f, torch.int32, (n_rows,), dev)
+    a = ScheduleArgs(struct_size=ctypes.sizeof(ScheduleArgs), R=R, gamma=gamma, K=int(K), c=_ptr(c),
+                     anchor=_ptr(anchor), y=_ptr(y), a=_ptr(out["a"]), l=_ptr(out["l"]),
+                     row_offsets=_ptr(out["row_offsets"]), row_req=_ptr(out["row_req"]),
+                     row_pos=_ptr(out["row_pos"]), row_tok=_ptr(out["row_tok"]),
+                     expected_tokens=_ptr(out.get("expected_tokens")), stream=_stream(dev, stream))
+    _check("dspark_schedule", get_lib().dspark_schedule(ctypes.byref(a)))
+    return out
+
+
+def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final, *,
+                  out=None, workspace=None, stream=None):
+    """Accept / reject against target logits (include/dspark.h, dspark_verify).
+
+    target [n_rows, V] fp32; row_offsets [R+1] int32; the draft inputs and
+    outputs; u_accept [R, gamma] fp32; u_final [R] fp32.  Returns
+    (n_accept int32 [R], out_tok int32 [R], p_tok fp32 [R, gamma])."""
+    torch = _torch()
+    dev = target.device
+    R, gamma, V = U.shape
+    rank = W1.shape[1]
+    wd = _wdtype(W1, W2)
+    n_rows = target.shape[0]
+    _want(target, "target", torch.float32, (n_rows, V), dev)
+    _want(row_offsets, "row_offsets", torch.int32, (R + 1,), dev)
+    _want(U, "U", torch.float32, (R, gamma, V), dev)
+    _want(W1, "W1", W1.dtype, (V, rank), dev)
+    _want(W2, "W2", W1.dtype, (V, rank), dev)
+    _want(anchor, "anchor", torch.int32, (R,), dev)
+    _want(temp, "temp", torch.float32, (R,), dev)
+    _want(y, "y", torch.int32, (R, gamma), dev)
+    _want(q_tok, "q_tok", torch.float32, (R, gamma), dev)
+    _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
+    _want(u_accept, "u_accept", torch.float32, (R, gamma), dev)
+    _want(u_final, "u_final", torch.float32, (R,), dev)
+    if out is None:
+        n_accept = torch.empty(R, dtype=torch.int32, device=dev)
+        out_tok = torch.empty(R, dtype=torch.int32, device=dev)
+        p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    else:
+        n_accept, out_tok, p_tok = out
+        _want(n_accept, "n_accept", torch.int32, (R,), dev)
+        _want(out_tok, "out_tok", torch.int32, (R,), dev)
+        _want(p_tok, "p_tok", torch.float32, (R, gamma), dev)
+    nbytes = verify_workspace_bytes(R, gamma, V, rank, wd, n_rows)
+    ws = _workspace(nbytes, dev, workspace)
+    a = VerifyArgs(struct_size=ctypes.sizeof(VerifyArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd,
+                   n_rows=n_rows, target=_ptr(target), row_offsets=_ptr(row_offsets), U=_ptr(U),
+                   W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp), y=_ptr(y),
+                   q_tok=_ptr(q_tok), q_stats=_ptr(q_stats), u_accept=_ptr(u_accept), u_final=_ptr(u_final),
+                   n_accept=_ptr(n_accept), out_tok=_ptr(out_tok), p_tok=_ptr(p_tok), workspace=_ptr(ws),
+                   workspace_bytes=ws.numel() * ws.element_size(), stream=_stream(dev, stream))
+    _check("dspark_verify", get_lib().dspark_verify(ctypes.byref(a)))
+    return n_accept, out_tok, p_tok

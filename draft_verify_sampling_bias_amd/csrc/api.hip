@@ -1,0 +1,170 @@
+// C ABI of libdspark: host-side checks, workspace carve-up and kernel
+// launches on the caller's stream.  No allocation, no synchronisation.
+
+#include <hip/hip_runtime.h>
+
+#include "dspark.h"
+#include "launchers.h"
+#include "plan.h"
+
+using namespace dspark;
+
+namespace {
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
+
+template <typename T>
+inline T* ws_at(void* ws, std::size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dspark_abi_version(void) { return DSPARK_ABI_VERSION; }
+
+const char* dspark_status_string(int status) { return status_string(status); }
+
+int64_t dspark_schedule_rows(int32_t R, int32_t gamma, int64_t K) { return schedule_rows(R, gamma, K); }
+
+int dspark_draft_workspace_size(const dspark_draft_args* args, size_t* bytes) {
+  if (bytes == nullptr) return DSPARK_ERR_NULL;
+  DraftPlan plan;
+  const int st = plan_draft(args, &plan);
+  if (st != DSPARK_OK) return st;
+  *bytes = plan.total;
+  return DSPARK_OK;
+}
+
+int dspark_verify_workspace_size(const dspark_verify_args* args, size_t* bytes) {
+  if (bytes == nullptr) return DSPARK_ERR_NULL;
+  VerifyPlan plan;
+  const int st = plan_verify(args, &plan);
+  if (st != DSPARK_OK) return st;
+  *bytes = plan.total;
+  return DSPARK_OK;
+}
+
+int dspark_draft_block(const dspark_draft_args* a) {
+  DraftPlan plan;
+  int st = validate_draft(a, &plan);
+  if (st != DSPARK_OK || a->R == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(a->stream);
+
+  TileParams tp{};
+  tp.W1 = a->W1;
+  tp.W2 = a->W2;
+  tp.V = a->V;
+  tp.rank = a->rank;
+  tp.R = a->R;
+  tp.n_tiles = plan.n_tiles;
+  tp.temp = a->temp;
+  tp.U_stride = static_cast<int64_t>(a->gamma) * a->V;
+  tp.part = ws_at<float>(a->workspace, plan.part_off);
+
+  FinishParams fp{};
+  fp.part = tp.part;
+  fp.n_tiles = plan.n_tiles;
+  fp.V = a->V;
+  fp.rank = a->rank;
+  fp.R = a->R;
+  fp.gamma = a->gamma;
+  fp.W1 = a->W1;
+  fp.W2 = a->W2;
+  fp.U_stride = tp.U_stride;
+  fp.temp = a->temp;
+  fp.u_draft = a->u_draft;
+  fp.y = a->y;
+  fp.q_tok = a->q_tok;
+  fp.q_stats = a->q_stats;
+
+  for (int k = 0; k < a->gamma; ++k) {
+    // prev = anchor for the first position, the token drafted just before otherwise
+    tp.prev_base = (k == 0) ? a->anchor : a->y + (k - 1);
+    tp.prev_stride = (k == 0) ? 1 : a->gamma;
+    tp.U_base = a->U + static_cast<int64_t>(k) * a->V;
+    if (a->prof_events) {
+      if (hipEventRecord(static_cast<hipEvent_t>(a->prof_events[2 * k]), s) != hipSuccess) return DSPARK_ERR_HIP;
+    }
+    st = hip_status(launch_bias_tile(tp, a->wdtype, false, s));
+    if (st != DSPARK_OK) return st;
+    if (a->prof_events) {
+      if (hipEventRecord(static_cast<hipEvent_t>(a->prof_events[2 * k + 1]), s) != hipSuccess)
+        return DSPARK_ERR_HIP;
+    }
+    fp.prev_base = tp.prev_base;
+    fp.prev_stride = tp.prev_stride;
+    fp.U_base = tp.U_base;
+    fp.k = k;
+    st = hip_status(launch_draft_finish(fp, a->wdtype, s));
+    if (st != DSPARK_OK) return st;
+  }
+  return DSPARK_OK;
+}
+
+int dspark_schedule(const dspark_schedule_args* a) {
+  const int st = validate_schedule(a);
+  if (st != DSPARK_OK || a->R == 0) return st;
+  return hip_status(launch_schedule(*a, static_cast<hipStream_t>(a->stream)));
+}
+
+int dspark_verify(const dspark_verify_args* a) {
+  VerifyPlan plan;
+  int st = validate_verify(a, &plan);
+  if (st != DSPARK_OK || a->R == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(a->stream);
+
+  VerifyParams vp{};
+  vp.R = a->R;
+  vp.gamma = a->gamma;
+  vp.V = a->V;
+  vp.rank = a->rank;
+  vp.n_chunks = plan.n_chunks;
+  vp.n_tiles = plan.n_tiles;
+  vp.n_rows = a->n_rows;
+  vp.target = a->target;
+  vp.row_offsets = a->row_offsets;
+  vp.U = a->U;
+  vp.W1 = a->W1;
+  vp.W2 = a->W2;
+  vp.anchor = a->anchor;
+  vp.temp = a->temp;
+  vp.y = a->y;
+  vp.q_tok = a->q_tok;
+  vp.q_stats = a->q_stats;
+  vp.u_accept = a->u_accept;
+  vp.u_final = a->u_final;
+  vp.n_accept = a->n_accept;
+  vp.out_tok = a->out_tok;
+  vp.p_tok = a->p_tok;
+  vp.vpart = ws_at<float>(a->workspace, plan.vpart_off);
+  vp.rs_info = ws_at<int32_t>(a->workspace, plan.rsinfo_off);
+  vp.rs_stats = ws_at<float>(a->workspace, plan.rsstats_off);
+  vp.rpart = ws_at<float>(a->workspace, plan.rpart_off);
+
+  st = hip_status(launch_verify_stats(vp, s));
+  if (st != DSPARK_OK) return st;
+  st = hip_status(launch_verify_finish(vp, s));
+  if (st != DSPARK_OK) return st;
+
+  // residual pass: rebuild q for the rejected position and sum max(0, p - q)
+  TileParams tp{};
+  tp.W1 = a->W1;
+  tp.W2 = a->W2;
+  tp.V = a->V;
+  tp.rank = a->rank;
+  tp.R = a->R;
+  tp.n_tiles = plan.n_tiles;
+  tp.temp = a->temp;
+  tp.rs_info = vp.rs_info;
+  tp.rs_stats = vp.rs_stats;
+  tp.U = a->U;
+  tp.target = a->target;
+  tp.part = vp.rpart;
+  st = hip_status(launch_bias_tile(tp, a->wdtype, true, s));
+  if (st != DSPARK_OK) return st;
+  return hip_status(launch_residual_finish(vp, a->wdtype, s));
+}
+
+}  // extern "C"

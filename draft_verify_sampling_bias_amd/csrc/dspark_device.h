@@ -1,0 +1,139 @@
+// Device helpers shared by the libdspark kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace dspark {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kIntMax = 0x7fffffff;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// 2^x on the hardware transcendental unit (v_exp_f32, 1 ulp).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Scale that turns (logit - max) into a base-2 exponent at temperature T;
+// 0 marks a greedy request (T <= 0 or NaN).
+__device__ __forceinline__ float temp_scale(float T) { return (T > 0.0f) ? (kLog2e / T) : 0.0f; }
+
+// (m, i) <- better of (m, i) and (m2, i2): larger value, lower index on ties.
+__device__ __forceinline__ void amax_merge(float& m, int& i, float m2, int i2) {
+  if (m2 > m || (m2 == m && i2 < i)) {
+    m = m2;
+    i = i2;
+  }
+}
+
+__device__ __forceinline__ void wave_amax(float& m, int& i) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    float m2 = __shfl_xor(m, d);
+    int i2 = __shfl_xor(i, d);
+    amax_merge(m, i, m2, i2);
+  }
+}
+
+// Butterfly sum: every lane ends with the same bits (a + b == b + a).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+
+__device__ __forceinline__ int wave_min_int(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = min(x, __shfl_xor(x, d));
+  return x;
+}
+
+__device__ __forceinline__ int wave_max_int(int x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = max(x, __shfl_xor(x, d));
+  return x;
+}
+
+// Inclusive scan inside a wavefront (Hillis-Steele, fixed order).
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float o = __shfl_up(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Block-wide (256 threads = 4 waves) inclusive scan.  Returns the inclusive
+// prefix of this thread; *excl gets the exclusive prefix, computed so that
+// the intervals [excl, incl) of consecutive threads meet exactly; *total is
+// the sum over the block (equal to the last thread's inclusive prefix).
+// `lds` needs 4 floats.  Contains two __syncthreads().
+__device__ __forceinline__ float block256_scan(float x, float* lds, float* excl, float* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float v = wave_incl_scan(x);
+  if (lane == 63) lds[wave] = v;
+  __syncthreads();
+  const float w0 = lds[0], w1 = lds[1], w2 = lds[2], w3 = lds[3];
+  __syncthreads();
+  float off = 0.0f;
+  if (wave == 1) off = w0;
+  if (wave == 2) off = w0 + w1;
+  if (wave == 3) off = (w0 + w1) + w2;
+  const float incl = off + v;
+  const float prev = __shfl_up(incl, 1);
+  *excl = (lane == 0) ? off : prev;
+  *total = ((w0 + w1) + w2) + w3;
+  return incl;
+}
+
+// Block-wide (256 threads) argmax with lowest-index ties; all threads get it.
+// `lm`, `li` need 4 entries each.  Contains two __syncthreads().
+__device__ __forceinline__ void block256_amax(float& m, int& i, float* lm, int* li) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  wave_amax(m, i);
+  if (lane == 0) {
+    lm[wave] = m;
+    li[wave] = i;
+  }
+  __syncthreads();
+  m = lm[0];
+  i = li[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) amax_merge(m, i, lm[w], li[w]);
+  __syncthreads();
+}
+
+// Block-wide (256 threads) min / max of an int; all threads get it.
+__device__ __forceinline__ int block256_min_int(int x, int* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_min_int(x);
+  if (lane == 0) lds[wave] = x;
+  __syncthreads();
+  x = min(min(lds[0], lds[1]), min(lds[2], lds[3]));
+  __syncthreads();
+  return x;
+}
+
+__device__ __forceinline__ int block256_max_int(int x, int* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_max_int(x);
+  if (lane == 0) lds[wave] = x;
+  __syncthreads();
+  x = max(max(lds[0], lds[1]), max(lds[2], lds[3]));
+  __syncthreads();
+  return x;
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+}  // namespace dspark

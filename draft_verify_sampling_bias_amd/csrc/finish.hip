@@ -1,0 +1,163 @@
+// Per-request finish kernels of the draft and of the residual correction.
+//
+// Draft (one workgroup per request, once per block position): combines the
+// tile records of the fused bias kernel into the position's maximum, lowest
+// argmax and normaliser Z, and for a sampled request draws the token by
+// inverse CDF with its uniform ("DSpark" explainer sections 2 and 7: the
+// block is drafted left to right from q = softmax((U_k + B_k)/T); llama.cpp
+// PR #25173: anchor-first, bias(prev) = markov_w2 . markov_w1[prev]).
+//
+// Residual (one workgroup per request that rejected a sampled draft): draws
+// the correction from max(0, p - q) normalised (explainer section 3), using
+// the tile sums written by the residual pass of the fused bias kernel; if that
+// residual has no mass it draws from p.
+
+#include "dspark_device.h"
+#include "launchers.h"
+#include "plan.h"
+#include "sample_device.h"
+
+namespace dspark {
+namespace {
+
+template <typename WT>
+__global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
+  __shared__ float hs[DSPARK_MAX_RANK];
+  __shared__ LocScratch sh;
+  __shared__ float e32[32], s32[32];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int V = p.V;
+  const float c = temp_scale(p.temp[n]);
+  const float* part = p.part + static_cast<int64_t>(n) * p.n_tiles * kPartFloats;
+  const int64_t o = static_cast<int64_t>(n) * p.gamma + p.k;
+  if (c > 0.0f) {
+    const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
+    load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
+  }
+  float m = -INFINITY;
+  int im = kIntMax;
+  for (int t = tid; t < p.n_tiles; t += 256)
+    amax_merge(m, im, part[t * kPartFloats], __float_as_int(part[t * kPartFloats + 1]));
+  block256_amax(m, im, sh.fred, sh.ired);
+  const int I = clampi(im, 0, V - 1);
+  if (c == 0.0f) {
+    if (tid == 0) {
+      p.y[o] = I;
+      p.q_tok[o] = 1.0f;
+      p.q_stats[2 * o] = m;
+      p.q_stats[2 * o + 1] = 1.0f;
+    }
+    return;
+  }
+  const float u = clamp_uniform(p.u_draft[o]);
+  auto mass = [&](int t) { return tile_record_mass(part + t * kPartFloats, m, c, true); };
+  const Located L = locate_segments(p.n_tiles, mass, u, &sh);
+  const int tile = L.index < 0 ? I / kTileRows : L.index;
+  const float* rec = part + tile * kPartFloats;
+  const float mt = rec[0];
+  const float scale = exp2_hw((mt - m) * c);
+  float th_sub;
+  const int sub = pick_sub(rec, L.fallback ? INFINITY : (u * L.Z - L.P) / scale, L.fallback, &th_sub);
+  const int v0 = tile * kTileRows + sub * kSubRows;
+  const int i = tid >> 3;
+  const int v = v0 + i;
+  const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V);
+  if ((tid & 7) == 0) {
+    float s = -INFINITY, e = 0.0f;
+    if (v < V) {
+      s = p.U_base[static_cast<int64_t>(n) * p.U_stride + v] + b;
+      e = exp2_hw((s - mt) * c);
+    }
+    e32[i] = e;
+    s32[i] = s;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int pos = pick32(e32, th_sub);
+    if (tid == 0) {
+      const int yy = (pos >= 0) ? v0 + pos : I;
+      const float sy = (pos >= 0) ? s32[pos] : m;
+      p.y[o] = yy;
+      p.q_tok[o] = exp2_hw((sy - m) * c) / L.Z;
+      p.q_stats[2 * o] = m;
+      p.q_stats[2 * o + 1] = L.Z;
+    }
+  }
+}
+
+template <typename WT>
+__global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
+  __shared__ float hs[DSPARK_MAX_RANK];
+  __shared__ ChunkScratch sh;
+  __shared__ float e32[32];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const int32_t* info = p.rs_info + 4 * static_cast<int64_t>(n);
+  if (info[0] == 0) return;
+  const int V = p.V;
+  const int prev = clampi(info[1], 0, V - 1);
+  const int64_t urow = info[2], trow = info[3];
+  const float* st = p.rs_stats + 4 * static_cast<int64_t>(n);
+  const float Mq = st[0], iZq = 1.0f / st[1], Mp = st[2], iZp = 1.0f / st[3];
+  const float c = temp_scale(p.temp[n]);
+  const float u = clamp_uniform(p.u_final[n]);
+  load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
+  const float* part = p.rpart + static_cast<int64_t>(n) * p.n_tiles * kPartFloats;
+  auto mass = [&](int t) { return tile_record_mass(part + t * kPartFloats, 0.0f, 0.0f, false); };
+  const Located L = locate_segments(p.n_tiles, mass, u, &sh.loc);
+  const float* tr = p.target + trow * V;
+  int out = -1;
+  if (L.Z > 0.0f && L.index >= 0) {
+    const float* rec = part + L.index * kPartFloats;
+    float th_sub;
+    const int sub = pick_sub(rec, L.fallback ? INFINITY : (u * L.Z - L.P), L.fallback, &th_sub);
+    const int v0 = L.index * kTileRows + sub * kSubRows;
+    const int i = tid >> 3;
+    const int v = v0 + i;
+    const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V);
+    if ((tid & 7) == 0) {
+      float w = 0.0f;
+      if (v < V) {
+        const float s = p.U[urow * V + v] + b;
+        const float q = exp2_hw((s - Mq) * c) * iZq;
+        const float pp = exp2_hw((tr[v] - Mp) * c) * iZp;
+        w = fmaxf(pp - q, 0.0f);
+      }
+      e32[i] = w;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int pos = pick32(e32, th_sub);
+      if (tid == 0) sh.ired[0] = (pos >= 0) ? v0 + pos : -1;
+    }
+    __syncthreads();
+    out = sh.ired[0];
+    __syncthreads();
+  }
+  if (out < 0) {
+    // no residual mass: the correction is drawn from p itself
+    out = chunk_draw(p.vpart + trow * p.n_chunks * kChunkFloats, p.n_chunks, tr, V, Mp, c, u, &sh);
+  }
+  if (tid == 0) p.out_tok[n] = clampi(out, 0, V - 1);
+}
+
+}  // namespace
+
+hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {
+  if (p.R == 0) return hipSuccess;
+  if (wdtype == DSPARK_W_BF16)
+    hipLaunchKernelGGL(draft_finish_kernel<uint16_t>, dim3(p.R), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(draft_finish_kernel<float>, dim3(p.R), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t s) {
+  if (p.R == 0) return hipSuccess;
+  if (wdtype == DSPARK_W_BF16)
+    hipLaunchKernelGGL(residual_finish_kernel<uint16_t>, dim3(p.R), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(residual_finish_kernel<float>, dim3(p.R), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -1,0 +1,144 @@
+// Host-side argument checks and workspace layout (pure C++17).
+#include "plan.h"
+
+#include <cstdint>
+
+namespace dspark {
+namespace {
+
+inline bool aligned(const void* p, std::size_t a) {
+  return (reinterpret_cast<std::uintptr_t>(p) % a) == 0;
+}
+
+inline std::size_t round_up(std::size_t x, std::size_t a) { return (x + a - 1) / a * a; }
+
+inline int n_tiles_for(int32_t V) { return (V + kTileRows - 1) / kTileRows; }
+
+}  // namespace
+
+int check_dims(int32_t R, int32_t gamma, int32_t V, int32_t rank, int32_t wdtype) {
+  if (wdtype != DSPARK_W_F32 && wdtype != DSPARK_W_BF16) return DSPARK_ERR_DTYPE;
+  if (R < 0 || gamma < 1 || V < 1 || rank < 1) return DSPARK_ERR_SHAPE;
+  if (gamma > DSPARK_MAX_GAMMA || V > DSPARK_MAX_VOCAB) return DSPARK_ERR_UNSUPPORTED;
+  if (rank < 8 || rank > DSPARK_MAX_RANK || rank % 8 != 0) return DSPARK_ERR_UNSUPPORTED;
+  // request index is kept in 24 bits by the kernels' composite keys; the
+  // [R, gamma, V] logits must be addressable with 64-bit offsets (always).
+  if (R > (1 << 24)) return DSPARK_ERR_UNSUPPORTED;
+  return DSPARK_OK;
+}
+
+int plan_draft(const dspark_draft_args* a, DraftPlan* plan) {
+  if (a == nullptr || plan == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_draft_args)) return DSPARK_ERR_ABI;
+  int st = check_dims(a->R, a->gamma, a->V, a->rank, a->wdtype);
+  if (st != DSPARK_OK) return st;
+  plan->n_tiles = n_tiles_for(a->V);
+  plan->part_off = 0;
+  std::size_t part = static_cast<std::size_t>(a->R) * plan->n_tiles * kPartFloats * sizeof(float);
+  plan->total = round_up(part, kWsAlign);
+  return DSPARK_OK;
+}
+
+int validate_draft(const dspark_draft_args* a, DraftPlan* plan) {
+  int st = plan_draft(a, plan);
+  if (st != DSPARK_OK) return st;
+  if (a->R == 0) return DSPARK_OK;
+  if (!a->U || !a->W1 || !a->W2 || !a->anchor || !a->temp || !a->u_draft || !a->y ||
+      !a->q_tok || !a->q_stats)
+    return DSPARK_ERR_NULL;
+  if (!aligned(a->U, 16) || !aligned(a->W1, 16) || !aligned(a->W2, 16)) return DSPARK_ERR_ALIGN;
+  if (!aligned(a->anchor, 4) || !aligned(a->temp, 4) || !aligned(a->u_draft, 4) ||
+      !aligned(a->y, 4) || !aligned(a->q_tok, 4) || !aligned(a->q_stats, 8))
+    return DSPARK_ERR_ALIGN;
+  if (a->workspace == nullptr || a->workspace_bytes < plan->total) return DSPARK_ERR_WORKSPACE;
+  if (!aligned(a->workspace, kWsAlign)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
+  if (a == nullptr || plan == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_verify_args)) return DSPARK_ERR_ABI;
+  int st = check_dims(a->R, a->gamma, a->V, a->rank, a->wdtype);
+  if (st != DSPARK_OK) return st;
+  const int64_t max_rows = static_cast<int64_t>(a->R) * (a->gamma + 1);
+  if (a->n_rows < a->R || a->n_rows > max_rows) return DSPARK_ERR_SHAPE;
+  plan->n_tiles = n_tiles_for(a->V);
+  plan->n_chunks = (a->V + kChunk - 1) / kChunk;
+  std::size_t off = 0;
+  plan->vpart_off = off;
+  off = round_up(off + static_cast<std::size_t>(a->n_rows) * plan->n_chunks * kChunkFloats * sizeof(float),
+                 kWsAlign);
+  plan->rsinfo_off = off;
+  off = round_up(off + static_cast<std::size_t>(a->R) * 4 * sizeof(int32_t), kWsAlign);
+  plan->rsstats_off = off;
+  off = round_up(off + static_cast<std::size_t>(a->R) * 4 * sizeof(float), kWsAlign);
+  plan->rpart_off = off;
+  off = round_up(off + static_cast<std::size_t>(a->R) * plan->n_tiles * kPartFloats * sizeof(float),
+                 kWsAlign);
+  plan->total = off;
+  return DSPARK_OK;
+}
+
+int validate_verify(const dspark_verify_args* a, VerifyPlan* plan) {
+  int st = plan_verify(a, plan);
+  if (st != DSPARK_OK) return st;
+  if (a->R == 0) return DSPARK_OK;
+  if (!a->target || !a->row_offsets || !a->U || !a->W1 || !a->W2 || !a->anchor || !a->temp ||
+      !a->y || !a->q_tok || !a->q_stats || !a->u_accept || !a->u_final || !a->n_accept ||
+      !a->out_tok || !a->p_tok)
+    return DSPARK_ERR_NULL;
+  if (!aligned(a->target, 16) || !aligned(a->U, 16) || !aligned(a->W1, 16) || !aligned(a->W2, 16))
+    return DSPARK_ERR_ALIGN;
+  if (!aligned(a->row_offsets, 4) || !aligned(a->anchor, 4) || !aligned(a->temp, 4) ||
+      !aligned(a->y, 4) || !aligned(a->q_tok, 4) || !aligned(a->q_stats, 8) ||
+      !aligned(a->u_accept, 4) || !aligned(a->u_final, 4) || !aligned(a->n_accept, 4) ||
+      !aligned(a->out_tok, 4) || !aligned(a->p_tok, 4))
+    return DSPARK_ERR_ALIGN;
+  if (a->workspace == nullptr || a->workspace_bytes < plan->total) return DSPARK_ERR_WORKSPACE;
+  if (!aligned(a->workspace, kWsAlign)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+int validate_schedule(const dspark_schedule_args* a) {
+  if (a == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_schedule_args)) return DSPARK_ERR_ABI;
+  if (a->R < 0 || a->gamma < 1) return DSPARK_ERR_SHAPE;
+  if (a->gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
+  const int64_t per_thread = (static_cast<int64_t>(a->R) + 1023) / 1024 * a->gamma;
+  if (per_thread > DSPARK_SCHED_KEYS_PER_THREAD) return DSPARK_ERR_UNSUPPORTED;
+  if (a->R == 0) return DSPARK_OK;
+  if (!a->c || !a->anchor || !a->y || !a->a || !a->l || !a->row_offsets || !a->row_req ||
+      !a->row_pos || !a->row_tok)
+    return DSPARK_ERR_NULL;
+  if (!aligned(a->c, 4) || !aligned(a->anchor, 4) || !aligned(a->y, 4) || !aligned(a->a, 4) ||
+      !aligned(a->l, 4) || !aligned(a->row_offsets, 4) || !aligned(a->row_req, 4) ||
+      !aligned(a->row_pos, 4) || !aligned(a->row_tok, 4) ||
+      (a->expected_tokens && !aligned(a->expected_tokens, 4)))
+    return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+int64_t schedule_rows(int32_t R, int32_t gamma, int64_t K) {
+  if (R < 0 || gamma < 1) return -1;
+  const int64_t n = static_cast<int64_t>(R) * gamma;
+  int64_t kc = K < 0 ? 0 : K;
+  if (kc > n) kc = n;
+  return static_cast<int64_t>(R) + kc;
+}
+
+const char* status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_NULL: return "a required pointer is NULL";
+    case DSPARK_ERR_SHAPE: return "a size argument is out of range";
+    case DSPARK_ERR_DTYPE: return "unknown weight dtype";
+    case DSPARK_ERR_ALIGN: return "a pointer is not aligned as required";
+    case DSPARK_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSPARK_ERR_UNSUPPORTED: return "arguments outside the library's supported limits";
+    case DSPARK_ERR_ABI: return "struct_size does not match this library's ABI";
+    case DSPARK_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // namespace dspark

@@ -1,0 +1,259 @@
+// Inverse-CDF location over per-tile partial sums, shared by the finish
+// kernels (256 threads per workgroup, one request per workgroup).
+//
+// An inverse-CDF draw walks the vocabulary in index order and returns the
+// first entry whose inclusive cumulative mass exceeds u * Z.  The vocabulary
+// is covered by tiles whose masses were reduced by an earlier kernel, so the
+// walk is done in three levels: a block-wide prefix over tile masses picks the
+// tile, a prefix over its four 32-row sub-sums picks the sub-tile, and only
+// that sub-tile's 32 entries are recomputed and scanned.  Intervals of
+// consecutive threads meet exactly (block256_scan), so exactly one thread owns
+// any threshold; where rounding between levels leaves the threshold past the
+// last entry of a chosen range, the last positive-mass entry of that range is
+// returned (zero-mass entries are never returned).
+#pragma once
+
+#include "dspark_device.h"
+#include "plan.h"
+
+namespace dspark {
+
+struct LocScratch {
+  float scan[4];
+  float fred[4];
+  int ired[4];
+  int sel;
+  float P;
+};
+
+struct Located {
+  int index;       // selected segment (-1 if no mass at all)
+  float P;         // cumulative mass before it
+  float Z;         // total mass
+  bool fallback;   // threshold fell past the end: take the last positive entry
+};
+
+__device__ __forceinline__ float clamp_uniform(float u) {
+  // [0, 1); NaN -> 0
+  return fminf(fmaxf(u, 0.0f), 0x1.fffffep-1f);
+}
+
+// Block-wide location over `n` segments with masses mass(t) >= 0 at threshold
+// u * Z.  Each thread sums a contiguous run of segments.
+template <class Mass>
+__device__ Located locate_segments(int n, Mass mass, float u, LocScratch* sh) {
+  const int tid = threadIdx.x;
+  const int seg = (n + 255) / 256;
+  const int t0 = min(tid * seg, n), t1 = min(t0 + seg, n);
+  float ts = 0.0f;
+  int lastpos = -1;
+  for (int t = t0; t < t1; ++t) {
+    const float x = mass(t);
+    ts += x;
+    if (x > 0.0f) lastpos = t;
+  }
+  float excl, Z;
+  const float incl = block256_scan(ts, sh->scan, &excl, &Z);
+  const float theta = u * Z;
+  const int first = block256_min_int((incl > theta) ? tid : 256, sh->ired);
+  const int glast = block256_max_int(lastpos, sh->ired);
+  if (tid == first) {
+    float run = excl;
+    int found = -1;
+    float P = excl, Plast = excl;
+    int seglast = -1;
+    for (int t = t0; t < t1; ++t) {
+      const float x = mass(t);
+      const float nx = run + x;
+      if (x > 0.0f) {
+        seglast = t;
+        Plast = run;
+        if (nx > theta) {
+          found = t;
+          P = run;
+          break;
+        }
+      }
+      run = nx;
+    }
+    sh->sel = (found >= 0) ? found : -(seglast + 2);  // encode "segment fallback"
+    sh->P = (found >= 0) ? P : Plast;
+  }
+  __syncthreads();
+  Located L;
+  L.Z = Z;
+  L.fallback = false;
+  if (first < 256) {
+    const int s = sh->sel;
+    if (s >= 0) {
+      L.index = s;
+      L.P = sh->P;
+    } else {
+      L.index = -(s + 2);
+      L.P = sh->P;
+      L.fallback = true;
+    }
+  } else {
+    L.index = glast;
+    L.P = 0.0f;
+    L.fallback = true;
+  }
+  __syncthreads();
+  return L;
+}
+
+// Mass of one (request, tile) record; `scaled` re-expresses the tile's sum
+// (taken relative to the tile maximum) relative to the global maximum M.
+__device__ __forceinline__ float tile_record_mass(const float* rec, float M, float c, bool scaled) {
+  const float s = ((rec[2] + rec[3]) + rec[4]) + rec[5];
+  return scaled ? s * exp2_hw((rec[0] - M) * c) : s;
+}
+
+// Sub-tile choice inside tile record `rec` for local threshold th (tile units).
+// Returns sub index (0..3) and writes the remaining threshold into *th_sub.
+__device__ __forceinline__ int pick_sub(const float* rec, float th, bool fallback, float* th_sub) {
+  int sub = -1, lastsub = -1;
+  float before = 0.0f, cum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float x = rec[2 + w];
+    const float nc = cum + x;
+    if (x > 0.0f) {
+      lastsub = w;
+      if (sub < 0 && !fallback && nc > th) {
+        sub = w;
+        before = cum;
+      }
+    }
+    cum = nc;
+  }
+  if (sub < 0) {
+    *th_sub = INFINITY;
+    return lastsub < 0 ? 0 : lastsub;
+  }
+  *th_sub = th - before;
+  return sub;
+}
+
+// Wave 0: first of 32 weights whose inclusive prefix exceeds theta, else the
+// last positive one, else -1.
+__device__ __forceinline__ int pick32(const float* e32, float theta) {
+  const int lane = threadIdx.x & 63;
+  const float x = (lane < 32) ? e32[lane] : 0.0f;
+  const float cum = wave_incl_scan(x);
+  const unsigned long long hit = __ballot(lane < 32 && x > 0.0f && cum > theta);
+  if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
+  const unsigned long long pos = __ballot(lane < 32 && x > 0.0f);
+  return pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
+}
+
+// Eight consecutive weights of a row times h (fp32 accumulate, fixed order).
+__device__ __forceinline__ float dot8(const uint16_t* row, const float* h, int k) {
+  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(row + k);
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc = fmaf(__uint_as_float(raw[q] << 16), h[k + 2 * q], acc);
+    acc = fmaf(__uint_as_float(raw[q] & 0xffff0000u), h[k + 2 * q + 1], acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float dot8(const float* row, const float* h, int k) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(row + k);
+  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(row + k + 4);
+  float acc = 0.0f;
+  acc = fmaf(a[0], h[k + 0], acc);
+  acc = fmaf(a[1], h[k + 1], acc);
+  acc = fmaf(a[2], h[k + 2], acc);
+  acc = fmaf(a[3], h[k + 3], acc);
+  acc = fmaf(b[0], h[k + 4], acc);
+  acc = fmaf(b[1], h[k + 5], acc);
+  acc = fmaf(b[2], h[k + 6], acc);
+  acc = fmaf(b[3], h[k + 7], acc);
+  return acc;
+}
+
+// Markov bias W2[v, :] . h for v = row of this thread's group of 8 lanes
+// (row index = threadIdx.x >> 3 within the 32 rows).  All 8 lanes return it.
+template <typename WT>
+__device__ __forceinline__ float row_bias(const WT* W2, const float* hs, int rank, int v, int V) {
+  const int part = threadIdx.x & 7;
+  float acc = 0.0f;
+  if (v < V) {
+    const WT* row = W2 + static_cast<int64_t>(v) * rank;
+    for (int k = part * 8; k < rank; k += 64) acc += dot8(row, hs, k);
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  return acc;
+}
+
+template <typename WT>
+__device__ __forceinline__ float weight_at(const WT* w, int64_t i);
+template <>
+__device__ __forceinline__ float weight_at<uint16_t>(const uint16_t* w, int64_t i) {
+  return bf16_to_f32(w[i]);
+}
+template <>
+__device__ __forceinline__ float weight_at<float>(const float* w, int64_t i) {
+  return w[i];
+}
+
+// h = W1[prev, :] as fp32 into LDS (no barrier).
+template <typename WT>
+__device__ __forceinline__ void load_h(const WT* W1, int prev, int rank, float* hs) {
+  for (int k = threadIdx.x; k < rank; k += 256) hs[k] = weight_at<WT>(W1, static_cast<int64_t>(prev) * rank + k);
+}
+
+struct ChunkScratch {
+  LocScratch loc;
+  float scan[4];
+  int ired[4];
+};
+
+// Inverse-CDF draw with uniform u from p ~ exp((t - M)/T) over one target row,
+// using the row's per-chunk records (max, argmax, sum of exp2((t - max) c)).
+// Returns the token (all threads), or -1 if the row has no mass.
+__device__ __forceinline__ int chunk_draw(const float* vrec, int n_chunks, const float* __restrict__ trow, int V,
+                                          float M, float c, float u, ChunkScratch* sh) {
+  auto mass = [&](int ch) { return vrec[ch * kChunkFloats + 2] * exp2_hw((vrec[ch * kChunkFloats] - M) * c); };
+  const Located L = locate_segments(n_chunks, mass, u, &sh->loc);
+  if (L.index < 0) return -1;
+  const int ch = L.index;
+  const float mc = vrec[ch * kChunkFloats];
+  const float scale = exp2_hw((mc - M) * c);
+  const float th = L.fallback ? INFINITY : (u * L.Z - L.P) / scale;
+  const int tid = threadIdx.x;
+  const int v0 = ch * kChunk + tid * 16;
+  float e[16];
+  float ts = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int v = v0 + j;
+    e[j] = (v < V) ? exp2_hw((trow[v] - mc) * c) : 0.0f;
+    ts += e[j];
+  }
+  float excl, tot;
+  const float incl = block256_scan(ts, sh->scan, &excl, &tot);
+  int cand = kIntMax, lastpos = -1;
+  if (incl > th) {
+    float run = excl;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float nx = run + e[j];
+      if (cand == kIntMax && e[j] > 0.0f && nx > th) cand = v0 + j;
+      run = nx;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (e[j] > 0.0f) lastpos = v0 + j;
+  // the first thread whose interval reaches th owns the answer
+  const int first = block256_min_int(cand, sh->ired);
+  if (first != kIntMax) return first;
+  return block256_max_int(lastpos, sh->ired);
+}
+
+}  // namespace dspark

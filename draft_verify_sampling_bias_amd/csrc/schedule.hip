@@ -1,0 +1,191 @@
+// Causal prefix-closed global top-K verify scheduler ("DSpark" explainer
+// sections 4, 5, 8-10 and 13).
+//
+// One workgroup of 1024 threads.  Thread t owns requests t, t + 1024, ...;
+// their survival values a[r, k] (fp32 running product of the clamped c) live
+// in registers as 64-bit keys (~bits(a) << 32 | k << 24 | r), whose ascending
+// order is (a descending, k ascending, r ascending).  The Kc-th smallest key is
+// found by an 8-pass radix select (8-bit digits, LDS histograms); a candidate
+// is selected iff its key is <= that threshold, which gives exactly Kc
+// selections.  Then l[r], an exclusive scan of l[r] + 1 for the row offsets,
+// and the flattened rows.  Nothing here reads the drafted tokens except the
+// copy into row_tok.
+
+#include "dspark_device.h"
+#include "launchers.h"
+
+namespace dspark {
+namespace {
+
+constexpr int kSchedThreads = 1024;
+constexpr int kSlots = DSPARK_SCHED_KEYS_PER_THREAD;
+
+__device__ __forceinline__ int wave_excl_scan_int(int v, int* total) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(x, d);
+    if (lane >= d) x += o;
+  }
+  *total = __shfl(x, 63);
+  return x - v;
+}
+
+// exclusive scan over the 1024 threads; returns excl, *total = block sum
+__device__ __forceinline__ int block1024_excl_scan_int(int v, int* lds16, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int wt;
+  const int ex = wave_excl_scan_int(v, &wt);
+  if (lane == 0) lds16[wave] = wt;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int x = lds16[w];
+    if (w < wave) off += x;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + ex;
+}
+
+__global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule_args a) {
+  __shared__ unsigned int hist[256];
+  __shared__ unsigned long long s_prefix;
+  __shared__ int s_rem;
+  __shared__ int s_i16[16];
+  __shared__ float s_f16[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = a.R, gamma = a.gamma;
+  const int JR = (R + kSchedThreads - 1) / kSchedThreads;
+  const int used = JR * gamma;
+
+  unsigned long long key[kSlots];
+  bool valid[kSlots];
+  float run = 1.0f;
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    const int j = s / gamma, k = s - j * gamma;
+    const int r = j * kSchedThreads + tid;
+    valid[s] = (s < used) && (r < R);
+    key[s] = ~0ull;
+    if (valid[s]) {
+      const int64_t o = static_cast<int64_t>(r) * gamma + k;
+      float ck = fminf(fmaxf(a.c[o], 0.0f), 1.0f);  // NaN -> 0
+      run = (k == 0) ? ck : run * ck;
+      const float av = (run == 0.0f) ? 0.0f : run;  // no -0
+      a.a[o] = av;
+      const unsigned int bits = __float_as_uint(av);
+      key[s] = (static_cast<unsigned long long>(~bits) << 32) | (static_cast<unsigned long long>(k) << 24) |
+               static_cast<unsigned long long>(r);
+    }
+  }
+
+  const int64_t n = static_cast<int64_t>(R) * gamma;
+  const int64_t Kc = a.K < 0 ? 0 : (a.K > n ? n : a.K);
+  unsigned long long thr = 0;
+  bool none = (Kc == 0), all = (Kc == n);
+  if (!none && !all) {
+    unsigned long long prefix = 0;
+    int rem = static_cast<int>(Kc);
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < kSlots; ++s) {
+        if (valid[s] && (pass == 0 || (key[s] >> (shift + 8)) == (prefix >> (shift + 8))))
+          atomicAdd(&hist[(key[s] >> shift) & 255ull], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+        int tot;
+        const int ex = wave_excl_scan_int(h0 + h1 + h2 + h3, &tot);
+        if (ex < rem && rem <= ex + h0 + h1 + h2 + h3) {
+          const int hs[4] = {h0, h1, h2, h3};
+          int cb = ex;
+          for (int q = 0; q < 4; ++q) {
+            if (rem <= cb + hs[q]) {
+              s_prefix = prefix | (static_cast<unsigned long long>(4 * lane + q) << shift);
+              s_rem = rem - cb;
+              break;
+            }
+            cb += hs[q];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = s_prefix;
+      rem = s_rem;
+    }
+    thr = prefix;
+  }
+
+  // l[r] and this thread's contribution to the expected token count
+  int lj[kSlots];  // l per owned request (indexed by j), kept in the first JR slots
+  float esum = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) lj[s] = 0;
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    if (valid[s]) {
+      const bool sel = all || (!none && key[s] <= thr);
+      if (sel) {
+        const int j = s / gamma;
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q)
+          if (q == j) lj[q] += 1;
+        esum += __uint_as_float(~static_cast<unsigned int>(key[s] >> 32));
+      }
+    }
+  }
+
+  // row offsets: exclusive scan of l[r] + 1 in request order (round j covers
+  // requests j*1024 .. j*1024+1023)
+  int carry = 0;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    if (j < JR) {
+      const int r = j * kSchedThreads + tid;
+      const int cnt = (r < R) ? lj[j] + 1 : 0;
+      int tot;
+      const int ex = block1024_excl_scan_int(cnt, s_i16, &tot);
+      if (r < R) {
+        const int off = carry + ex;
+        a.l[r] = lj[j];
+        a.row_offsets[r] = off;
+        const int anchor = a.anchor[r];
+        for (int pos = 0; pos <= lj[j]; ++pos) {
+          a.row_req[off + pos] = r;
+          a.row_pos[off + pos] = pos;
+          a.row_tok[off + pos] = (pos == 0) ? anchor : a.y[static_cast<int64_t>(r) * gamma + pos - 1];
+        }
+      }
+      carry += tot;
+    }
+  }
+  if (tid == 0) a.row_offsets[R] = carry;
+
+  if (a.expected_tokens != nullptr) {
+    esum = wave_sum(esum);
+    if (lane == 0) s_f16[wave] = esum;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.0f;
+      for (int w = 0; w < 16; ++w) t += s_f16[w];
+      a.expected_tokens[0] = static_cast<float>(R) + t;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_schedule(const dspark_schedule_args& a, hipStream_t s) {
+  if (a.R == 0) return hipSuccess;
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dspark

@@ -1,0 +1,298 @@
+/*
+ * libdspark: the per-step draft -> schedule -> verify hot path of DSpark
+ * speculative decoding, for AMD Instinct MI355X (gfx950 / CDNA4).
+ *
+ * Sources of the operations (web pages; cited by title and section):
+ *   [EXP]  "DSpark: speculative decoding that fixes suffix quality and
+ *          production verification waste" (papers.franksyz.com explainer),
+ *          sections 2-5 and 7-13.
+ *   [PR]   llama.cpp PR #25173 "spec: add DSpark speculative decoding",
+ *          description and review thread.
+ *
+ * One step for R requests, block size gamma, vocabulary V, Markov rank r:
+ *   dspark_draft_block  drafts gamma tokens per request left to right;
+ *   dspark_schedule     computes survival and picks the verify rows;
+ *   (the caller runs the target model over those rows)
+ *   dspark_verify       accepts / rejects and emits one correction or bonus.
+ *
+ * Conventions shared by every call:
+ *   - Every array pointer is a DEVICE pointer (memory of the current HIP
+ *     device), except the argument struct itself, which lives on the host.
+ *   - All arrays are dense, row-major, with the shapes given below.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     never allocates or frees memory and keeps no pointer after returning.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream).  No call synchronises the host or
+ *     copies device data to the host.  Every output size is known on the host
+ *     before the call.
+ *   - Errors: argument checks (NULL pointers, sizes, limits, alignment,
+ *     struct_size, workspace size) run on the host before anything is
+ *     enqueued; on failure a nonzero dspark_status is returned and nothing is
+ *     enqueued.  A failed kernel launch returns DSPARK_ERR_HIP.  Device data
+ *     (token ids, logits, offsets, probabilities) is not inspected on the
+ *     host; out-of-range ids and offsets are clamped inside the kernels so no
+ *     access leaves its buffer, but the results are then unspecified.
+ *   - No C++ exception crosses this interface and nothing is printed.
+ *   - Calls that share a workspace must not overlap in time.
+ *   - Argument structs are versioned: set struct_size = sizeof(the struct).
+ */
+#ifndef DSPARK_H_
+#define DSPARK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSPARK_ABI_VERSION 1
+
+/* limits checked on the host */
+#define DSPARK_MAX_GAMMA 16          /* block size gamma in [1, 16]                 */
+#define DSPARK_MAX_RANK 512          /* Markov rank r in [8, 512], r % 8 == 0       */
+#define DSPARK_MAX_VOCAB (1 << 30)   /* V in [1, 2^30]                              */
+#define DSPARK_SCHED_KEYS_PER_THREAD 16  /* dspark_schedule: ceil(R/1024)*gamma <= 16 */
+
+typedef enum dspark_status {
+  DSPARK_OK = 0,
+  DSPARK_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  DSPARK_ERR_SHAPE = 2,       /* a size is out of range                            */
+  DSPARK_ERR_DTYPE = 3,       /* unknown weight dtype                              */
+  DSPARK_ERR_ALIGN = 4,       /* a pointer is not aligned as required              */
+  DSPARK_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
+  DSPARK_ERR_UNSUPPORTED = 6, /* valid but outside this library's limits           */
+  DSPARK_ERR_ABI = 7,         /* struct_size does not match this library          */
+  DSPARK_ERR_HIP = 8          /* a HIP runtime call or kernel launch failed        */
+} dspark_status;
+
+/* Element type of the Markov factors W1, W2. */
+typedef enum dspark_wdtype {
+  DSPARK_W_F32 = 0,           /* IEEE binary32                                     */
+  DSPARK_W_BF16 = 1           /* bfloat16 bit patterns (uint16)                    */
+} dspark_wdtype;
+
+/* --------------------------------------------------------------------------
+ * dspark_draft_block: draft one block of gamma tokens per request.
+ *
+ * [EXP] section 7: drafter logits are base logits U_k plus a prefix-dependent
+ * bias B_k; the Markov head's bias depends only on the previous sampled token
+ * and is a low-rank factorisation instead of a V x V transition table.
+ * [PR] description: the block is anchor-first (position 0 already predicts
+ * the first draft token) and sampled left to right with
+ * bias(prev) = markov_w2 . markov_w1[prev], computed on the device.
+ * [EXP] section 6: a parallel backbone produces U for all positions; the
+ * light sequential head corrects each next position.
+ *
+ * For k = 0 .. gamma-1, sequentially (y[:, k-1] feeds position k):
+ *   prev[r]  = anchor[r] if k == 0 else y[r, k-1]
+ *   s[r, v]  = U[r, k, v] + sum_j W2[v, j] * W1[prev[r], j]
+ *   greedy (temp[r] <= 0 or NaN):
+ *     y[r, k] = lowest index v with maximal s[r, v]; q_tok = 1;
+ *     q_stats = (max_v s, 1)
+ *   sampled (temp[r] = T > 0):
+ *     x = s / T, m = max x, Z = sum_v exp(x_v - m);
+ *     y[r, k] = first v (in index order) whose inclusive cumulative sum of
+ *               exp(x - m) exceeds u_draft[r, k] * Z (never a zero-mass entry);
+ *     q_tok[r, k] = exp(x_y - m) / Z;  q_stats[r, k] = (max_v s, Z)
+ *
+ * Arguments (device arrays unless stated):
+ *   R, gamma, V, rank   host ints; R >= 0 (R == 0 is a no-op), gamma in
+ *                       [1, DSPARK_MAX_GAMMA], V in [1, DSPARK_MAX_VOCAB],
+ *                       rank in [8, DSPARK_MAX_RANK] with rank % 8 == 0.
+ *   wdtype              dspark_wdtype of W1 and W2.
+ *   U        float [R, gamma, V]  base logits; 16-byte aligned.
+ *   W1, W2   wdtype [V, rank]     Markov factors (markov_w1, markov_w2);
+ *                                 16-byte aligned.
+ *   anchor   int32 [R]            last committed token (prev for k = 0).
+ *   temp     float [R]            per-request temperature; <= 0 => greedy.
+ *   u_draft  float [R, gamma]     uniforms in [0, 1) (read by sampled rows).
+ *   y        int32 [R, gamma]     out: drafted tokens.
+ *   q_tok    float [R, gamma]     out: drafter probability of y.
+ *   q_stats  float [R, gamma, 2]  out: (max_v s, Z) per position, consumed by
+ *                                 dspark_verify to rebuild q on a rejection.
+ *   workspace, workspace_bytes    scratch of at least
+ *                                 dspark_draft_workspace_size() bytes,
+ *                                 256-byte aligned.
+ *   stream   hipStream_t as void*.
+ *   prof_events  optional (NULL normally): host array of 2*gamma hipEvent_t
+ *                handles; event 2k / 2k+1 are recorded on `stream` just before
+ *                / after the fused bias + softmax kernel of position k, for
+ *                timing that kernel alone.
+ * -------------------------------------------------------------------------- */
+typedef struct dspark_draft_args {
+  uint32_t struct_size;
+  int32_t R, gamma, V, rank;
+  int32_t wdtype;
+  const float* U;
+  const void* W1;
+  const void* W2;
+  const int32_t* anchor;
+  const float* temp;
+  const float* u_draft;
+  int32_t* y;
+  float* q_tok;
+  float* q_stats;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+  void* const* prof_events;
+} dspark_draft_args;
+
+/* --------------------------------------------------------------------------
+ * dspark_schedule: survival and the causal, prefix-closed verify schedule.
+ *
+ * [EXP] section 8: the confidence head estimates the conditional acceptance
+ * c[r, k]; the scheduler uses the cumulative survival a[r, k] (probability
+ * the prefix survives).  Section 5: a suffix position's value is a product
+ * of conditional acceptance rates.  Section 9: the chosen work is
+ * prefix-closed (no verifying position 5 alone).  Section 10: capacity K is
+ * fixed ahead of time; the current cumulative confidence picks a top-K
+ * prefix selection inside it.  Section 4: admission must not read the
+ * drafted tokens (this call's decision reads only c and K).  Section 13: the
+ * variable-length verify tokens are flattened into contiguous rows with
+ * per-sequence markers instead of padding.
+ *
+ *   a[r, 0] = c'[r, 0], a[r, k] = fl32(a[r, k-1] * c'[r, k]) with
+ *             c' = c clamped to [0, 1] (NaN -> 0) and -0 written as +0;
+ *   Kc      = min(max(K, 0), R * gamma);
+ *   the Kc candidates (r, k) first in the order (a descending, k ascending,
+ *   r ascending) are selected; l[r] = number selected for request r (always a
+ *   prefix 0 .. l[r]-1 because a is non-increasing in k);
+ *   row_offsets[0] = 0, row_offsets[r+1] = row_offsets[r] + l[r] + 1;
+ *   for row i = row_offsets[r] + j, j = 0 .. l[r]:
+ *     row_req[i] = r, row_pos[i] = j,
+ *     row_tok[i] = anchor[r] if j == 0 else y[r, j-1]   (the token fed to the
+ *     target at that row; row j verifies draft j, row l[r] is the bonus row);
+ *   expected_tokens = R + sum of a over the selected candidates.
+ *
+ * Arguments (device arrays unless stated):
+ *   R, gamma   host ints; R >= 0, gamma in [1, DSPARK_MAX_GAMMA],
+ *              ceil(R / 1024) * gamma <= DSPARK_SCHED_KEYS_PER_THREAD.
+ *   K          host int64 capacity in draft positions (any value; clamped).
+ *   c          float [R, gamma]  per-position acceptance estimates.
+ *   anchor     int32 [R]; y int32 [R, gamma] (drafted tokens; only copied
+ *              into row_tok, never read by the decision).
+ *   a          float [R, gamma]  out: survival.
+ *   l          int32 [R]         out: verified draft count per request.
+ *   row_offsets int32 [R + 1]    out.
+ *   row_req, row_pos, row_tok  int32 [dspark_schedule_rows(R, gamma, K)] out.
+ *   expected_tokens  float [1]   optional out (may be NULL).
+ *   stream     hipStream_t as void*.
+ * -------------------------------------------------------------------------- */
+typedef struct dspark_schedule_args {
+  uint32_t struct_size;
+  int32_t R, gamma;
+  int64_t K;
+  const float* c;
+  const int32_t* anchor;
+  const int32_t* y;
+  float* a;
+  int32_t* l;
+  int32_t* row_offsets;
+  int32_t* row_req;
+  int32_t* row_pos;
+  int32_t* row_tok;
+  float* expected_tokens;
+  void* stream;
+} dspark_schedule_args;
+
+/* --------------------------------------------------------------------------
+ * dspark_verify: accept / reject drafted tokens against target logits.
+ *
+ * [EXP] section 2: the target verifies the prefix under a causal mask;
+ * verification runs left to right and after the first rejection the later
+ * drafts are discarded; if all are accepted a bonus token comes from the
+ * target's next distribution, otherwise a correction from the residual.
+ * Section 3: accept v with probability min(1, p(v)/q(v)); the correction
+ * takes only the target's mass in excess of the drafter, max(0, p - q)
+ * normalised (resampling from full p would double-count the overlap).
+ * [PR] "Losslessness": greedy decoding stays identical to target-only
+ * greedy.
+ *
+ * Request r owns target rows row_offsets[r] .. row_offsets[r+1]-1, so its
+ * verify length is l = rows - 1 (0 <= l <= gamma); row j holds the target
+ * logits t_j for draft position j, row l is the bonus position.
+ *   greedy (temp[r] <= 0 or NaN):
+ *     accept y_j iff y_j is the lowest-index argmax of t_j; p_tok = 1 or 0;
+ *     n = first rejected j (else l); out_tok = lowest-index argmax of t_n.
+ *   sampled (T = temp[r] > 0):
+ *     p_j = softmax(t_j / T); p_tok[r, j] = p_j(y_j);
+ *     accept iff u_accept[r, j] < p_tok[r, j] / q_tok[r, j];
+ *     n = first rejected j, else l;
+ *     n < l: q_n = softmax((U[r, n] + W2 . W1[prev]) / T) rebuilt with
+ *            prev = anchor (n = 0) or y[r, n-1] and q_stats[r, n];
+ *            out_tok = inverse-CDF draw with u_final[r] from max(0, p_n - q_n)
+ *            (from p_n if that has no mass);
+ *     n = l: out_tok = inverse-CDF draw with u_final[r] from p_l (bonus).
+ *   Emitted tokens for the step: y[r, 0 .. n-1] followed by out_tok[r].
+ *   p_tok[r, j] = 0 for j >= l.
+ *
+ * Arguments (device arrays unless stated):
+ *   R, gamma, V, rank, wdtype  as for dspark_draft_block.
+ *   n_rows     host int64: total rows = row_offsets[R]; R <= n_rows <=
+ *              R * (gamma + 1).
+ *   target     float [n_rows, V]  target logits; 16-byte aligned.
+ *   row_offsets int32 [R + 1]     (from dspark_schedule, or r*(gamma+1) for
+ *                                  fixed-length verify).
+ *   U, W1, W2, anchor, temp       the inputs given to dspark_draft_block.
+ *   y, q_tok, q_stats             outputs of dspark_draft_block.
+ *   u_accept   float [R, gamma]   uniforms in [0, 1).
+ *   u_final    float [R]          uniform in [0, 1).
+ *   n_accept   int32 [R]          out: accepted draft count n.
+ *   out_tok    int32 [R]          out: correction or bonus token.
+ *   p_tok      float [R, gamma]   out: target probability of each draft.
+ *   workspace, workspace_bytes    >= dspark_verify_workspace_size(); 256-byte
+ *                                 aligned.
+ *   stream     hipStream_t as void*.
+ * -------------------------------------------------------------------------- */
+typedef struct dspark_verify_args {
+  uint32_t struct_size;
+  int32_t R, gamma, V, rank;
+  int32_t wdtype;
+  int64_t n_rows;
+  const float* target;
+  const int32_t* row_offsets;
+  const float* U;
+  const void* W1;
+  const void* W2;
+  const int32_t* anchor;
+  const float* temp;
+  const int32_t* y;
+  const float* q_tok;
+  const float* q_stats;
+  const float* u_accept;
+  const float* u_final;
+  int32_t* n_accept;
+  int32_t* out_tok;
+  float* p_tok;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+} dspark_verify_args;
+
+/* Workspace bytes needed by a call with these arguments (only the size
+ * fields are read).  Returns DSPARK_OK and writes *bytes, or an error status
+ * for invalid sizes. */
+int dspark_draft_workspace_size(const dspark_draft_args* args, size_t* bytes);
+int dspark_verify_workspace_size(const dspark_verify_args* args, size_t* bytes);
+
+int dspark_draft_block(const dspark_draft_args* args);
+int dspark_schedule(const dspark_schedule_args* args);
+int dspark_verify(const dspark_verify_args* args);
+
+/* Host-side: number of verify rows dspark_schedule emits,
+ * R + min(max(K, 0), R * gamma); -1 for R < 0 or gamma < 1. */
+int64_t dspark_schedule_rows(int32_t R, int32_t gamma, int64_t K);
+
+/* Static description of a status code (never NULL). */
+const char* dspark_status_string(int status);
+
+/* DSPARK_ABI_VERSION of the loaded library. */
+int dspark_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H_ */

@@ -1,0 +1,150 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
+through the C ABI binding, and compare with the CPU oracle.
+
+Comparison rules (decisions are compared, values within tolerance):
+  * token ids, accept counts and schedules must be identical, except at a
+    decision the oracle flags as lying within 1e-6 of its boundary (near-tie
+    argmax, CDF edge, u within 1e-6 of p/q); such flips are counted;
+  * the oracle is teacher-forced with the GPU's drafted prefix, so a flagged
+    flip does not cascade into later positions;
+  * probabilities (q_tok, p_tok, Z) and survival within 1e-5 relative.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+import synth
+
+REL = 1e-5
+FLT_MIN = np.finfo(np.float32).tiny
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def upload(inp: synth.StepInputs, device="cuda:0"):
+    torch = torch_mod()
+
+    def f(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    if inp.wdtype == "bf16":
+        W1 = torch.from_numpy(inp.W1.view(np.int16)).to(device).view(torch.bfloat16)
+        W2 = torch.from_numpy(inp.W2.view(np.int16)).to(device).view(torch.bfloat16)
+    else:
+        W1, W2 = f(inp.W1), f(inp.W2)
+    return dict(U=f(inp.U), W1=W1, W2=W2, anchor=f(inp.anchor), temp=f(inp.temp), u_draft=f(inp.u_draft),
+                u_accept=f(inp.u_accept), u_final=f(inp.u_final), c=f(inp.c), target=f(inp.target))
+
+
+def gpu_step(d, K, gamma):
+    """draft -> schedule -> gather rows -> verify on the GPU; returns numpy results."""
+    import draft_verify_sampling_bias_amd as ds
+    torch = torch_mod()
+    y, q_tok, q_stats = ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"])
+    sch = ds.dspark_schedule(d["c"], K, d["anchor"], y)
+    rows = d["target"][sch["row_req"].long(), sch["row_pos"].long()].contiguous()
+    n_acc, out_tok, p_tok = ds.dspark_verify(rows, sch["row_offsets"], d["U"], d["W1"], d["W2"], d["anchor"],
+                                             d["temp"], y, q_tok, q_stats, d["u_accept"], d["u_final"])
+    torch.cuda.synchronize()
+    res = dict(y=y, q_tok=q_tok, q_stats=q_stats, n_accept=n_acc, out_tok=out_tok, p_tok=p_tok, rows=rows,
+               **{k: v for k, v in sch.items() if v is not None})
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def rel_ok(g, o, rel=REL, abs_floor=0.0):
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    tiny = np.abs(o) < FLT_MIN
+    ok = np.abs(g - o) <= rel * np.abs(o) + abs_floor
+    ok |= tiny & (np.abs(g) < 2 * FLT_MIN)
+    return ok
+
+
+@dataclass
+class Tally:
+    decisions: int = 0
+    flagged: int = 0
+    flagged_flips: int = 0
+    failures: list = field(default_factory=list)
+
+    def check(self):
+        assert not self.failures, "\n".join(self.failures[:20])
+
+    def summary(self):
+        return (f"decisions={self.decisions} flagged={self.flagged} "
+                f"flagged_flips={self.flagged_flips} unflagged_mismatches={len(self.failures)}")
+
+
+def compare_draft(inp, g, reqs, tally: Tally):
+    """Teacher-forced comparison of the drafted ids, q_tok and q_stats."""
+    y_g = g["y"]
+    d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
+                           requests=reqs, prev_override=y_g)
+    for r in reqs:
+        for k in range(inp.gamma):
+            tally.decisions += 1
+            flag = (r, k) in d.flags
+            tally.flagged += flag
+            if y_g[r, k] != d.y[r, k]:
+                if flag:
+                    tally.flagged_flips += 1
+                else:
+                    tally.failures.append(f"draft r={r} k={k}: gpu y={y_g[r, k]} oracle y={d.y[r, k]} "
+                                          f"(T={inp.temp[r]})")
+                    continue
+            elif not rel_ok(g["q_tok"][r, k], d.q_tok[r, k]):
+                tally.failures.append(f"draft q_tok r={r} k={k}: {g['q_tok'][r, k]} vs {d.q_tok[r, k]}")
+            if not rel_ok(g["q_stats"][r, k, 0], d.q_stats[r, k, 0], abs_floor=1e-5):
+                tally.failures.append(f"draft max s r={r} k={k}: {g['q_stats'][r, k, 0]} vs {d.q_stats[r, k, 0]}")
+            if not rel_ok(g["q_stats"][r, k, 1], d.q_stats[r, k, 1]):
+                tally.failures.append(f"draft Z r={r} k={k}: {g['q_stats'][r, k, 1]} vs {d.q_stats[r, k, 1]}")
+    return d
+
+
+def compare_schedule(inp, g, K):
+    s = oracle.schedule(inp.c, K, inp.anchor, g["y"])
+    np.testing.assert_array_equal(g["a"], s.a)
+    np.testing.assert_array_equal(g["l"], s.l)
+    np.testing.assert_array_equal(g["row_offsets"], s.row_offsets)
+    np.testing.assert_array_equal(g["row_req"], s.row_req)
+    np.testing.assert_array_equal(g["row_pos"], s.row_pos)
+    np.testing.assert_array_equal(g["row_tok"], s.row_tok)
+    if "expected_tokens" in g:
+        assert rel_ok(g["expected_tokens"][0], s.expected_tokens), (g["expected_tokens"][0], s.expected_tokens)
+    return s
+
+
+def compare_verify(inp, g, reqs, tally: Tally):
+    """Oracle verify on the GPU's drafted tokens and q_tok, the GPU's rows."""
+    v = oracle.verify(g["rows"], g["row_offsets"], inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"],
+                      g["q_tok"], inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+    off = g["row_offsets"]
+    for r in reqs:
+        l = int(off[r + 1] - off[r] - 1)
+        tally.decisions += l + 1
+        fl_acc = [j for j in range(l) if ("accept", r, j) in v.flags]
+        fl_fin = [j for j in range(l + 1) if ("final", r, j) in v.flags]
+        tally.flagged += len(fl_acc) + len(fl_fin)
+        ng, no = int(g["n_accept"][r]), int(v.n_accept[r])
+        if ng != no:
+            if min(ng, no) in fl_acc:
+                tally.flagged_flips += 1
+                continue
+            tally.failures.append(f"verify n_accept r={r}: gpu {ng} oracle {no} (T={inp.temp[r]})")
+            continue
+        if int(g["out_tok"][r]) != int(v.out_tok[r]):
+            if no in fl_fin:
+                tally.flagged_flips += 1
+            else:
+                tally.failures.append(f"verify out_tok r={r} n={no}: gpu {g['out_tok'][r]} oracle {v.out_tok[r]} "
+                                      f"(T={inp.temp[r]}, l={l})")
+        for j in range(inp.gamma):
+            if not rel_ok(g["p_tok"][r, j], v.p_tok[r, j]):
+                tally.failures.append(f"verify p_tok r={r} j={j}: {g['p_tok'][r, j]} vs {v.p_tok[r, j]}")
+    return v

@@ -1,0 +1,144 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/dspark.h declares, and rejects invalid arguments on the host before
+enqueuing anything (no GPU is touched: every call here fails validation or is
+a host-only query)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import draft_verify_sampling_bias_amd as ds
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+FAKE = 0x10000  # 64 KiB-aligned non-NULL address; never dereferenced by failing calls
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(dspark_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_and_library_exports_everything():
+    names = _declared()
+    assert set(names) == set(ds.EXPORTED_SYMBOLS), names
+    lib = ds.get_lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ds.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_abi_version_and_strings():
+    assert ds.dspark_abi_version() == 1
+    for s in range(9):
+        assert ds.dspark_status_string(s)
+    assert ds.dspark_status_string(123) == "unknown status"
+
+
+def test_schedule_rows():
+    assert ds.dspark_schedule_rows(64, 7, 448) == 64 + 448
+    assert ds.dspark_schedule_rows(64, 7, 10 ** 12) == 64 + 448
+    assert ds.dspark_schedule_rows(256, 5, 300) == 556
+    assert ds.dspark_schedule_rows(8, 3, -5) == 8
+    assert ds.dspark_schedule_rows(0, 3, 5) == 0
+    assert ds.dspark_schedule_rows(-1, 3, 5) == -1
+    assert ds.dspark_schedule_rows(4, 0, 5) == -1
+
+
+def test_workspace_sizes_match_struct_layout():
+    # a struct_size mismatch would return DSPARK_ERR_ABI
+    assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1) == 64 * 1187 * 8 * 4
+    nb = ds.verify_workspace_bytes(64, 7, 151936, 512, 1, 512)
+    assert nb >= 512 * 38 * 16 + 64 * 1187 * 32
+
+
+def _draft_args(**kw):
+    base = dict(struct_size=ctypes.sizeof(ds.DraftArgs), R=4, gamma=3, V=1000, rank=64, wdtype=1,
+                U=FAKE, W1=FAKE, W2=FAKE, anchor=FAKE, temp=FAKE, u_draft=FAKE, y=FAKE, q_tok=FAKE,
+                q_stats=FAKE, workspace=None, workspace_bytes=0, stream=None, prof_events=None)
+    base.update(kw)
+    return ds.DraftArgs(**base)
+
+
+def _call(fn, args):
+    return getattr(ds.get_lib(), fn)(ctypes.byref(args))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), ds.Status.ERR_ABI),
+    (dict(R=-1), ds.Status.ERR_SHAPE),
+    (dict(gamma=0), ds.Status.ERR_SHAPE),
+    (dict(gamma=17), ds.Status.ERR_UNSUPPORTED),
+    (dict(V=0), ds.Status.ERR_SHAPE),
+    (dict(rank=12), ds.Status.ERR_UNSUPPORTED),
+    (dict(rank=520), ds.Status.ERR_UNSUPPORTED),
+    (dict(wdtype=7), ds.Status.ERR_DTYPE),
+    (dict(U=None), ds.Status.ERR_NULL),
+    (dict(q_stats=None), ds.Status.ERR_NULL),
+    (dict(U=FAKE + 4), ds.Status.ERR_ALIGN),
+    (dict(W2=FAKE + 8), ds.Status.ERR_ALIGN),
+    (dict(), ds.Status.ERR_WORKSPACE),
+    (dict(workspace=FAKE, workspace_bytes=100), ds.Status.ERR_WORKSPACE),
+    (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), ds.Status.ERR_ALIGN),
+])
+def test_draft_rejects_invalid_arguments(kw, status):
+    assert _call("dspark_draft_block", _draft_args(**kw)) == status
+
+
+def test_zero_requests_is_a_noop():
+    assert _call("dspark_draft_block", _draft_args(R=0, U=None, W1=None)) == ds.Status.OK
+    a = ds.ScheduleArgs(struct_size=ctypes.sizeof(ds.ScheduleArgs), R=0, gamma=3, K=5)
+    assert _call("dspark_schedule", a) == ds.Status.OK
+    v = ds.VerifyArgs(struct_size=ctypes.sizeof(ds.VerifyArgs), R=0, gamma=3, V=100, rank=8, wdtype=1, n_rows=0)
+    assert _call("dspark_verify", v) == ds.Status.OK
+
+
+def _verify_args(**kw):
+    base = dict(struct_size=ctypes.sizeof(ds.VerifyArgs), R=4, gamma=3, V=1000, rank=64, wdtype=1, n_rows=16,
+                workspace=None, workspace_bytes=0, stream=None)
+    for f in ("target", "row_offsets", "U", "W1", "W2", "anchor", "temp", "y", "q_tok", "q_stats", "u_accept",
+              "u_final", "n_accept", "out_tok", "p_tok"):
+        base[f] = FAKE
+    base.update(kw)
+    return ds.VerifyArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=4), ds.Status.ERR_ABI),
+    (dict(n_rows=3), ds.Status.ERR_SHAPE),
+    (dict(n_rows=17), ds.Status.ERR_SHAPE),
+    (dict(target=None), ds.Status.ERR_NULL),
+    (dict(u_final=None), ds.Status.ERR_NULL),
+    (dict(target=FAKE + 4), ds.Status.ERR_ALIGN),
+    (dict(q_stats=FAKE + 4), ds.Status.ERR_ALIGN),
+    (dict(), ds.Status.ERR_WORKSPACE),
+])
+def test_verify_rejects_invalid_arguments(kw, status):
+    assert _call("dspark_verify", _verify_args(**kw)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=0), ds.Status.ERR_ABI),
+    (dict(gamma=0), ds.Status.ERR_SHAPE),
+    (dict(R=1025, gamma=9), ds.Status.ERR_UNSUPPORTED),   # ceil(R/1024) * gamma > 16
+    (dict(c=None), ds.Status.ERR_NULL),
+    (dict(row_tok=FAKE + 2), ds.Status.ERR_ALIGN),
+])
+def test_schedule_rejects_invalid_arguments(kw, status):
+    base = dict(struct_size=ctypes.sizeof(ds.ScheduleArgs), R=8, gamma=4, K=10)
+    for f in ("c", "anchor", "y", "a", "l", "row_offsets", "row_req", "row_pos", "row_tok"):
+        base[f] = FAKE
+    base.update(kw)
+    assert _call("dspark_schedule", ds.ScheduleArgs(**base)) == status
+
+
+def test_null_args_pointer():
+    lib = ds.get_lib()
+    assert lib.dspark_draft_block(None) == ds.Status.ERR_NULL
+    assert lib.dspark_verify(None) == ds.Status.ERR_NULL
+    assert lib.dspark_schedule(None) == ds.Status.ERR_NULL

@@ -1,0 +1,99 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases are compared in full; the full-size configurations are compared
+exactly on the schedule and on a seeded sample of requests for draft and
+verify (every request's draft and verify are independent of the others).
+"""
+import numpy as np
+import pytest
+import torch  # noqa: F401  (first import is slow on a fresh box: pay it at collection)
+
+import synth
+from gpu_harness import Tally, compare_draft, compare_schedule, compare_verify, gpu_step, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(inp, K=None, reqs=None, label=""):
+    K = inp.K if K is None else K
+    d = upload(inp)
+    g = gpu_step(d, K, inp.gamma)
+    reqs = list(range(inp.R)) if reqs is None else list(reqs)
+    t = Tally()
+    compare_draft(inp, g, reqs, t)
+    compare_schedule(inp, g, K)
+    compare_verify(inp, g, reqs, t)
+    print(f"[{label or inp.name}] K={K} {t.summary()}", flush=True)
+    t.check()
+    return g
+
+
+@pytest.mark.parametrize("policy", ["greedy", "sampled"])
+def test_config1(policy):
+    _run(synth.make_config(1, policy))
+
+
+SMALL = [
+    # (seed, R, gamma, V, rank, wdtype, policy, K_mode)
+    (11, 3, 4, 1000, 64, "bf16", "sampled", "fixed"),        # ragged last tile, one chunk
+    (12, 3, 4, 1000, 64, "bf16", "greedy", "fixed"),
+    (13, 70, 3, 4099, 40, "bf16", "temps", "uniformK"),      # V % 4 != 0, rank % 16 == 8, 2 chunks
+    (14, 130, 2, 2300, 512, "bf16", "mixed", "uniformK"),    # 3 request chunks, rank 512
+    (15, 5, 3, 777, 24, "f32", "temps", "fixed"),            # fp32 weights
+    (16, 33, 6, 1536, 256, "f32", "mixed", "uniformK"),      # fp32, 2 chunks
+    (17, 2, 1, 9000, 8, "bf16", "sampled", "fixed"),         # gamma = 1, minimum rank
+    (18, 9, 16, 513, 128, "bf16", "temps", "uniformK"),      # maximum gamma
+    (19, 4, 5, 5, 16, "bf16", "sampled", "fixed"),           # tiny vocabulary
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_small_shapes(case):
+    seed, R, gamma, V, rank, wd, pol, km = case
+    inp = synth.make_custom(seed, R, gamma, V, rank, wdtype=wd, policy=pol, K_mode=km, U_std=3.0, noise_std=1.0)
+    _run(inp)
+
+
+def test_target_only_fallback_K0():
+    """K = 0: nothing is verified, one row per request, the emitted token is
+    the bonus draw from row 0 (target-only decoding)."""
+    inp = synth.make_custom(21, 16, 4, 3000, 64, policy="mixed")
+    g = _run(inp, K=0)
+    assert (g["l"] == 0).all() and (g["n_accept"] == 0).all()
+
+
+def test_high_acceptance_and_greedy_identity():
+    """Target = drafter base logits with small noise and no Markov bias: most
+    drafts are accepted; greedy requests emit the target argmax chain."""
+    inp = synth.make_custom(22, 24, 5, 2048, 32, policy="mixed", noise_std=0.05, W_std=0.0)
+    g = _run(inp)
+    assert g["n_accept"].mean() > 1.0
+    rows, off = g["rows"], g["row_offsets"]
+    for r in np.flatnonzero(inp.temp <= 0):
+        n = g["n_accept"][r]
+        am = [int(np.argmax(rows[off[r] + j])) for j in range(n + 1)]
+        assert list(g["y"][r, :n]) + [int(g["out_tok"][r])] == am
+
+
+def test_run_twice_bit_identical():
+    import draft_verify_sampling_bias_amd  # noqa: F401
+    inp = synth.make_custom(23, 40, 5, 5000, 256, policy="mixed", K_mode="uniformK")
+    d = upload(inp)
+    g1 = gpu_step(d, inp.K, inp.gamma)
+    g2 = gpu_step(d, inp.K, inp.gamma)
+    for k in g1:
+        np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+
+
+def _sample(R, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(R, size=min(n, R), replace=False).tolist())
+
+
+@pytest.mark.parametrize("cfg,policy", [(2, "greedy"), (2, "sampled"), (3, None), (4, None), (5, None)])
+def test_full_size_configs(cfg, policy):
+    inp = synth.make_config(cfg, policy)
+    reqs = _sample(inp.R, 4, cfg)
+    if cfg == 5:  # include both greedy and sampled requests
+        reqs = sorted(set(reqs) | {int(np.flatnonzero(inp.temp <= 0)[0]), int(np.flatnonzero(inp.temp > 0)[0])})
+    _run(inp, reqs=reqs, label=f"config{cfg}-{policy or 'default'}")
