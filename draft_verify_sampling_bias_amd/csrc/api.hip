@@ -18,6 +18,20 @@ inline T* ws_at(void* ws, std::size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// Compute units of the current device (persistent-grid sizing), cached per
+// device; 256 if the query fails.
+int current_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,14 +72,16 @@ int dspark_draft_block(const dspark_draft_args* a) {
   tp.V = a->V;
   tp.rank = a->rank;
   tp.R = a->R;
-  tp.n_tiles = plan.n_tiles;
+  tp.seg_rows = plan.seg_rows;
+  tp.n_seg = plan.n_seg;
   tp.temp = a->temp;
   tp.U_stride = static_cast<int64_t>(a->gamma) * a->V;
   tp.part = ws_at<float>(a->workspace, plan.part_off);
 
   FinishParams fp{};
   fp.part = tp.part;
-  fp.n_tiles = plan.n_tiles;
+  fp.seg_rows = plan.seg_rows;
+  fp.n_seg = plan.n_seg;
   fp.V = a->V;
   fp.rank = a->rank;
   fp.R = a->R;
@@ -79,6 +95,7 @@ int dspark_draft_block(const dspark_draft_args* a) {
   fp.q_tok = a->q_tok;
   fp.q_stats = a->q_stats;
 
+  const int cu = current_cu_count();
   for (int k = 0; k < a->gamma; ++k) {
     // prev = anchor for the first position, the token drafted just before otherwise
     tp.prev_base = (k == 0) ? a->anchor : a->y + (k - 1);
@@ -87,7 +104,7 @@ int dspark_draft_block(const dspark_draft_args* a) {
     if (a->prof_events) {
       if (hipEventRecord(static_cast<hipEvent_t>(a->prof_events[2 * k]), s) != hipSuccess) return DSPARK_ERR_HIP;
     }
-    st = hip_status(launch_bias_tile(tp, a->wdtype, false, s));
+    st = hip_status(launch_bias_tile(tp, a->wdtype, false, cu, s));
     if (st != DSPARK_OK) return st;
     if (a->prof_events) {
       if (hipEventRecord(static_cast<hipEvent_t>(a->prof_events[2 * k + 1]), s) != hipSuccess)
@@ -121,7 +138,8 @@ int dspark_verify(const dspark_verify_args* a) {
   vp.V = a->V;
   vp.rank = a->rank;
   vp.n_chunks = plan.n_chunks;
-  vp.n_tiles = plan.n_tiles;
+  vp.seg_rows = plan.seg_rows;
+  vp.n_seg = plan.n_seg;
   vp.n_rows = a->n_rows;
   vp.target = a->target;
   vp.row_offsets = a->row_offsets;
@@ -155,14 +173,17 @@ int dspark_verify(const dspark_verify_args* a) {
   tp.V = a->V;
   tp.rank = a->rank;
   tp.R = a->R;
-  tp.n_tiles = plan.n_tiles;
+  tp.seg_rows = plan.seg_rows;
+  tp.n_seg = plan.n_seg;
   tp.temp = a->temp;
   tp.rs_info = vp.rs_info;
   tp.rs_stats = vp.rs_stats;
   tp.U = a->U;
   tp.target = a->target;
+  tp.u_rows = static_cast<int64_t>(a->R) * a->gamma;
+  tp.t_rows = a->n_rows;
   tp.part = vp.rpart;
-  st = hip_status(launch_bias_tile(tp, a->wdtype, true, s));
+  st = hip_status(launch_bias_tile(tp, a->wdtype, true, current_cu_count(), s));
   if (st != DSPARK_OK) return st;
   return hip_status(launch_residual_finish(vp, a->wdtype, s));
 }

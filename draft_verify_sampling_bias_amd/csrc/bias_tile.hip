@@ -3,19 +3,33 @@
 // The Markov head's bias for request n is B[n, v] = sum_j W2[v, j] * W1[prev_n, j]
 // ("DSpark" explainer, section 7; llama.cpp PR #25173 description:
 // bias(prev) = markov_w2 . markov_w1[prev]).  For a batch of requests this is
-// the product B^T = W2 . H^T with H = W1[prev] gathered row by row.  One
-// workgroup owns 128 vocabulary rows (four wavefronts of 32) and all requests:
-// each W2 row is read from HBM once per position and stays in registers as
-// MFMA A fragments while every request chunk streams past it, so the work is
-// bound by the W2 + U streams, with the contraction on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).  The epilogue adds the base
-// logits U and reduces each request's 128 values in registers and LDS to a
-// small record; neither B nor s = U + B is ever written to memory.
+// the product B^T = W2 . H^T with H = W1[prev] gathered row by row: W2 is
+// streamed from HBM once per draft position as MFMA A fragments, H sits in
+// LDS, and the epilogue adds the base logits U and reduces each request's
+// values over a vocabulary segment (one wavefront's rows) in registers to one
+// record of two floats.  Neither B nor s = U + B is ever written to memory,
+// and no wavefront waits for another after the prologue.
 //
-// MFMA operand layout (32x32 output, wave64): A lane l holds row (l & 31),
-// 8 consecutive k at 8 * (l >> 5); B lane l holds column (l & 31), the same k;
-// accumulator element i of lane l is row 8*(i/4) + 4*(l>>5) + (i%4), column
-// (l & 31).  Here rows are vocabulary entries and columns are requests.
+//   draft record    (max_v s, sum_v exp((s_v - max)/T))  sampled request
+//                   (max_v s, lowest argmax as int bits)  greedy request
+//   residual record (0, sum_v max(0, p_v - q_v))
+//
+// Paths:
+//   bias_seg16      bf16 weights, R <= 64.  v_mfma_f32_16x16x32_bf16; each
+//                   wavefront owns 16-row segments; persistent workgroups of
+//                   4 wavefronts (one per CU) gather H once and prefetch the
+//                   next segment's W2 / U fragments while computing the
+//                   current one.
+//   bias_seg32      bf16 weights, R > 64.  v_mfma_f32_32x32x16_bf16; each
+//                   wavefront keeps its 32 rows of W2 in registers while the
+//                   request chunks (64 at a time) stream through LDS.
+//   bias_seg32_f32  fp32 weights.  v_mfma_f32_32x32x2_f32.
+//
+// Operand layouts (wave64).  16x16x32: A lane l holds row (l & 15), 8 k at
+// 8 * (l >> 4) of each 32-k step; B likewise for its column; accumulator i of
+// lane l is row 4*(l>>4) + i, column (l & 15).  32x32x16: A lane l holds row
+// (l & 31), 8 k at 8 * (l >> 5); accumulator i is row 8*(i/4) + 4*(l>>5) +
+// (i%4), column (l & 31).  Rows are vocabulary entries, columns requests.
 
 #include "dspark_device.h"
 #include "launchers.h"
@@ -24,39 +38,29 @@
 namespace dspark {
 namespace {
 
-constexpr int kNchBf16 = 64;  // requests per chunk: two 32-wide MFMA column blocks
-constexpr int kNchF32 = 32;   // requests per chunk in the fp32-weight kernel
-
-// Loads this lane's 16 logits of one request row: rows vw + 8g + 4*khalf + e,
-// g = 0..3, e = 0..3.  Entries past V, or of an inactive request, read as -inf.
-__device__ __forceinline__ void load_row16(const float* __restrict__ row, int vbase, int V, bool vec4,
-                                           bool ok, float (&x)[16]) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int v = vbase + 8 * g;
-    if (ok && vec4 && v < V) {
-      const f32x4_t t = *reinterpret_cast<const f32x4_t*>(row + v);
-      x[4 * g + 0] = t[0];
-      x[4 * g + 1] = t[1];
-      x[4 * g + 2] = t[2];
-      x[4 * g + 3] = t[3];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * g + e] = (ok && v + e < V) ? row[v + e] : -INFINITY;
-    }
-  }
+// LDS-only workgroup barrier: orders LDS traffic without draining the
+// wavefront's outstanding global loads (a full __syncthreads() waits for
+// every in-flight prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ int acc_row(int i, int khalf) { return 8 * (i >> 2) + 4 * khalf + (i & 3); }
+__device__ __forceinline__ void amax_sel(float& m, int& i, float m2, int i2) {
+  const bool take = (m2 > m) | ((m2 == m) & (i2 < i));
+  m = take ? m2 : m;
+  i = take ? i2 : i;
+}
 
-// Per-request values staged in LDS for one chunk.
-struct ChunkInfo {
+// Per-request values staged in LDS.
+struct ReqInfo {
   int act, prev, urow, trow;
   float c, Mq, iZq, Mp, iZp;
 };
 
-__device__ __forceinline__ ChunkInfo fetch_info(const TileParams& p, int n, bool resid) {
-  ChunkInfo ci{0, 0, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ ReqInfo fetch_info(const TileParams& p, int n, bool resid) {
+  ReqInfo ci{0, 0, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (n >= p.R) return ci;
   ci.c = temp_scale(p.temp[n]);
   if (!resid) {
@@ -75,156 +79,318 @@ __device__ __forceinline__ ChunkInfo fetch_info(const TileParams& p, int n, bool
     ci.iZp = 1.0f / st[3];
   }
   ci.prev = clampi(ci.prev, 0, p.V - 1);
+  // rows of inactive requests are never used, but their loads are still
+  // issued: keep every row index inside its buffer
+  ci.urow = ci.act ? static_cast<int>(min(max(static_cast<int64_t>(ci.urow), int64_t{0}), p.u_rows - 1)) : 0;
+  ci.trow = ci.act ? static_cast<int>(min(max(static_cast<int64_t>(ci.trow), int64_t{0}), p.t_rows - 1)) : 0;
   return ci;
 }
 
-// Draft epilogue, phase 1: s = acc + U (in place in x), per-lane then per-wave
-// max / lowest argmax of this wave's 32 rows for the lane's request.
-__device__ __forceinline__ void draft_phase1(const f32x16_t& acc, float (&x)[16], int vw, int khalf,
-                                             int V, float* wm, int* wi) {
-  float m = -INFINITY;
-  int im = kIntMax;
+__device__ __forceinline__ const float* u_row(const TileParams& p, const ReqInfo& ci, int n, bool resid) {
+  return resid ? p.U + static_cast<int64_t>(ci.urow) * p.V : p.U_base + static_cast<int64_t>(n) * p.U_stride;
+}
+
+// Four consecutive logits starting at v (clamped addresses; the caller masks).
+template <bool VEC4>
+__device__ __forceinline__ f32x4_t load4(const float* row, int v, int V) {
+  if (VEC4) {
+    return *reinterpret_cast<const f32x4_t*>(row + min(v, V - 4));
+  } else {
+    f32x4_t r;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int v = vw + acc_row(i, khalf);
-    const float s = acc[i] + x[i];
-    x[i] = s;
-    if (v < V && s > m) {
-      m = s;
-      im = v;
-    }
-  }
-  amax_merge(m, im, __shfl_xor(m, 32), __shfl_xor(im, 32));
-  if (khalf == 0) {
-    *wm = m;
-    *wi = im;
+    for (int e = 0; e < 4; ++e) r[e] = row[min(v + e, V - 1)];
+    return r;
   }
 }
 
-// Draft epilogue, phase 2: tile max from the four wave maxima, then this
-// wave's sum of exp((s - M)/T); lane (khalf == 0) writes the record.
-__device__ __forceinline__ void draft_phase2(const float (&x)[16], int vw, int khalf, int V, int wave,
-                                             const float* wm /*[4][32] at lane*/, const int* wi, int lrow,
-                                             float c, float* rec) {
-  float M = wm[lrow];
-  int I = wi[lrow];
+// ---------------------------------------------------------------------------
+// 16-row path
+// ---------------------------------------------------------------------------
+template <int KS, bool RESID>
+struct Seg16Regs {
+  bf16x8_t w[KS];     // W2 rows vw + (lane & 15), k = 32 ks + 8 (lane >> 4) .. +8
+  f32x4_t u[4];       // U[request 16 nb + (lane & 15)][vw + 4 (lane >> 4) .. +4]
+  f32x4_t t[RESID ? 4 : 1];  // target values, residual mode
+};
+
+template <int KS, bool RESID, bool VEC4>
+__device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s_ci, int vw, int lane,
+                                           Seg16Regs<KS, RESID>& f) {
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int V = p.V, rank = p.rank;
+  const int v = min(vw + l16, V - 1);
+  const uint16_t* w2 = static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(v) * rank;
 #pragma unroll
-  for (int w = 1; w < 4; ++w) amax_merge(M, I, wm[w * 32 + lrow], wi[w * 32 + lrow]);
-  float e = 0.0f;
-  if (c > 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int v = vw + acc_row(i, khalf);
-      if (v < V) e += exp2_hw((x[i] - M) * c);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    const int k = ks * 32 + kq * 8;
+    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(w2 + min(k, rank - 8));
+    if (k >= rank) raw = u32x4_t{0u, 0u, 0u, 0u};
+    f.w[ks] = __builtin_bit_cast(bf16x8_t, raw);
   }
-  const float eo = __shfl_xor(e, 32);
-  const float tot = khalf ? (eo + e) : (e + eo);
-  if (khalf == 0 && rec != nullptr) {
-    if (wave == 0) {
-      rec[0] = M;
-      rec[1] = __int_as_float(I);
-    }
-    rec[2 + wave] = tot;
+  const int vu = vw + kq * 4;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int nn = nb * 16 + l16;
+    const ReqInfo& ci = s_ci[nn];
+    f.u[nb] = load4<VEC4>(u_row(p, ci, nn < p.R ? nn : 0, RESID), vu, V);
+    if (RESID) f.t[nb] = load4<VEC4>(p.target + static_cast<int64_t>(ci.trow) * V, vu, V);
   }
 }
 
-// Residual epilogue: this wave's sum of max(0, p - q) for the lane's request.
-__device__ __forceinline__ void resid_epilogue(const f32x16_t& acc, const float (&x)[16],
-                                               const float* __restrict__ trow, int vw, int khalf, int V,
-                                               bool vec4, bool ok, const ChunkInfo& ci, int wave,
-                                               float* rec) {
-  float t[16];
-  load_row16(trow, vw + 4 * khalf, V, vec4, ok, t);
-  float w = 0.0f;
-  if (ok) {
+template <int KS>
+__device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16_t* Hs, int lane, f32x4_t (&acc)[4]) {
+  constexpr int RS = KS * 32 + 8;
+  const int l16 = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int v = vw + acc_row(i, khalf);
-      if (v < V) {
-        const float s = acc[i] + x[i];
-        const float q = exp2_hw((s - ci.Mq) * ci.c) * ci.iZq;
-        const float pp = exp2_hw((t[i] - ci.Mp) * ci.c) * ci.iZp;
-        w += fmaxf(pp - q, 0.0f);
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* h0 = Hs + l16 * RS + kq * 8;
+  u32x4_t b[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[ks], __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb],
+                                                        0, 0, 0);
+    // keep the B reads one step ahead only: unrestricted hoisting of all of
+    // them exhausts the register file
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int KS, bool RESID>
+__device__ __forceinline__ void seg16_epilogue(const TileParams& p, const ReqInfo* s_ci, int wt, int lane,
+                                               const Seg16Regs<KS, RESID>& f, const f32x4_t (&acc)[4]) {
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int V = p.V, R = p.R;
+  const int vb = wt * kSegSmall + kq * 4;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int nn = nb * 16 + l16;
+    const ReqInfo& ci = s_ci[nn];
+    const bool okn = (nn < R) && ci.act;
+    f32x4_t s = acc[nb] + f.u[nb];
+    float x, y;
+    if (!RESID) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = (okn && vb + i < V) ? s[i] : -INFINITY;
+      float m = s[0];
+      int im = vb;
+#pragma unroll
+      for (int i = 1; i < 4; ++i) {
+        const bool gt = s[i] > m;
+        m = gt ? s[i] : m;
+        im = gt ? vb + i : im;
       }
+      amax_sel(m, im, __shfl_xor(m, 16), __shfl_xor(im, 16));
+      amax_sel(m, im, __shfl_xor(m, 32), __shfl_xor(im, 32));
+      float e = 0.f;
+      if (ci.c > 0.f) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e += exp2_hw((s[i] - m) * ci.c);
+      }
+      e += __shfl_xor(e, 16);
+      e += __shfl_xor(e, 32);
+      x = m;
+      y = (ci.c > 0.f) ? e : __int_as_float(im);
+    } else {
+      float w = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q = exp2_hw((s[i] - ci.Mq) * ci.c) * ci.iZq;
+        const float pp = exp2_hw((f.t[nb][i] - ci.Mp) * ci.c) * ci.iZp;
+        w += (okn && vb + i < V) ? fmaxf(pp - q, 0.f) : 0.f;
+      }
+      w += __shfl_xor(w, 16);
+      w += __shfl_xor(w, 32);
+      x = 0.f;
+      y = w;
+    }
+    if (kq == 0 && okn) {
+      float2* rec = reinterpret_cast<float2*>(p.part) + static_cast<int64_t>(nn) * p.n_seg + wt;
+      *rec = make_float2(x, y);
     }
   }
-  const float wo = __shfl_xor(w, 32);
-  const float tot = khalf ? (wo + w) : (w + wo);
-  if (khalf == 0 && ok && rec != nullptr) rec[2 + wave] = tot;
+}
+
+constexpr int kSeg16Waves = 4;  // one wavefront per SIMD: the prefetched tile needs ~260 registers
+
+template <int KS, bool RESID, bool VEC4>
+__global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16(TileParams p) {
+  constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
+  __shared__ ReqInfo s_ci[kSmallMaxR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = p.R, rank = p.rank;
+  const int n_wt = p.n_seg;
+
+  if (RESID) {
+    int any = 0;
+    for (int n = tid; n < R; n += kSeg16Waves * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
+    if (!__syncthreads_or(any)) return;
+  }
+  if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, tid, RESID);
+  lds_barrier();
+  {
+    constexpr int G = KS * 4;  // 16-byte groups per H row
+    const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
+    for (int q = tid; q < kSmallMaxR * G; q += kSeg16Waves * 64) {
+      const int nn = q / G, g = q - nn * G;
+      const ReqInfo& ci = s_ci[nn];
+      u32x4_t val = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(ci.prev) * rank +
+                                                       min(g * 8, rank - 8));
+      if (g * 8 >= rank || !ci.act) val = u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = val;
+    }
+  }
+  const int stride = gridDim.x * kSeg16Waves;
+  int wt = blockIdx.x * kSeg16Waves + wave;
+  Seg16Regs<KS, RESID> fa, fb;
+  seg16_load<KS, RESID, VEC4>(p, s_ci, min(wt, n_wt - 1) * kSegSmall, lane, fa);
+  lds_barrier();
+  while (wt < n_wt) {
+    f32x4_t acc[4];
+    const int wt1 = wt + stride;
+    if (wt1 < n_wt) seg16_load<KS, RESID, VEC4>(p, s_ci, wt1 * kSegSmall, lane, fb);
+    seg16_mfma<KS>(fa.w, Hs, lane, acc);
+    seg16_epilogue<KS, RESID>(p, s_ci, wt, lane, fa, acc);
+    if (wt1 >= n_wt) break;
+    const int wt2 = wt1 + stride;
+    if (wt2 < n_wt) seg16_load<KS, RESID, VEC4>(p, s_ci, wt2 * kSegSmall, lane, fa);
+    seg16_mfma<KS>(fb.w, Hs, lane, acc);
+    seg16_epilogue<KS, RESID>(p, s_ci, wt1, lane, fb, acc);
+    wt = wt2;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 weights: W2 fragments cached in registers for the whole kernel.
-// KREG = number of 16-wide k steps held (rank <= 16 * KREG).
+// 32-row paths: one wavefront = one 32-row segment, requests in chunks
 // ---------------------------------------------------------------------------
-template <int KREG, bool RESID>
-__global__ void __launch_bounds__(256) bias_tile_bf16(TileParams p) {
-  constexpr int RS = KREG * 16 + 8;  // LDS row stride (bf16 elements): 16-byte pad vs bank conflicts
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[kNchBf16 * RS];
-  __shared__ ChunkInfo s_ci[kNchBf16];
-  __shared__ float s_wm[2][4 * 32];
-  __shared__ int s_wi[2][4 * 32];
+__device__ __forceinline__ int acc32_row(int i, int khalf) { return 8 * (i >> 2) + 4 * khalf + (i & 3); }
 
+// Loads this lane's 16 logits of one request row for the 32x32 layout.
+template <bool VEC4>
+__device__ __forceinline__ void load16_32(const float* row, int vbase, int V, float (&x)[16]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4_t t = load4<VEC4>(row, vbase + 8 * g, V);
+    x[4 * g + 0] = t[0];
+    x[4 * g + 1] = t[1];
+    x[4 * g + 2] = t[2];
+    x[4 * g + 3] = t[3];
+  }
+}
+
+// Per-wave record of one 32-row segment for the lane's request.
+template <bool RESID, bool VEC4>
+__device__ __forceinline__ void seg32_epilogue(const TileParams& p, const ReqInfo& ci, bool okn, int n, int seg,
+                                               int khalf, const f32x16_t& acc, const float (&x)[16]) {
+  const int V = p.V;
+  const int vw = seg * kSegLarge;
+  float rx, ry;
+  if (!RESID) {
+    float s[16];
+    float m = -INFINITY;
+    int im = kIntMax;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int v = vw + acc32_row(i, khalf);
+      s[i] = (okn && v < V) ? acc[i] + x[i] : -INFINITY;
+      const bool gt = s[i] > m;
+      m = gt ? s[i] : m;
+      im = gt ? v : im;
+    }
+    amax_sel(m, im, __shfl_xor(m, 32), __shfl_xor(im, 32));
+    float e = 0.f;
+    if (ci.c > 0.f) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) e += exp2_hw((s[i] - m) * ci.c);
+    }
+    const float eo = __shfl_xor(e, 32);
+    e = khalf ? (eo + e) : (e + eo);
+    rx = m;
+    ry = (ci.c > 0.f) ? e : __int_as_float(im);
+  } else {
+    float t[16];
+    load16_32<VEC4>(p.target + static_cast<int64_t>(ci.trow) * V, vw + 4 * khalf, V, t);
+    float w = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int v = vw + acc32_row(i, khalf);
+      const float q = exp2_hw((acc[i] + x[i] - ci.Mq) * ci.c) * ci.iZq;
+      const float pp = exp2_hw((t[i] - ci.Mp) * ci.c) * ci.iZp;
+      w += (okn && v < V) ? fmaxf(pp - q, 0.f) : 0.f;
+    }
+    const float wo = __shfl_xor(w, 32);
+    w = khalf ? (wo + w) : (w + wo);
+    rx = 0.f;
+    ry = w;
+  }
+  if (khalf == 0 && okn) {
+    float2* rec = reinterpret_cast<float2*>(p.part) + static_cast<int64_t>(n) * p.n_seg + seg;
+    *rec = make_float2(rx, ry);
+  }
+}
+
+constexpr int kNch32 = 64;  // requests per chunk (two 32-wide column blocks)
+
+template <int KREG, bool RESID, bool VEC4>
+__global__ void __launch_bounds__(256) bias_seg32(TileParams p) {
+  constexpr int RS = KREG * 16 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[kNch32 * RS];
+  __shared__ ReqInfo s_ci[kNch32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, khalf = lane >> 5;
-  const int tile = blockIdx.x;
-  const int vw = tile * kTileRows + wave * kSubRows;
+  const int seg = blockIdx.x * 4 + wave;
   const int V = p.V, rank = p.rank, R = p.R;
-  const bool vec4 = (V & 3) == 0;
 
   if (RESID) {
     int any = 0;
     for (int n = tid; n < R; n += 256) any |= p.rs_info[4 * static_cast<int64_t>(n)];
     if (!__syncthreads_or(any)) return;
   }
-
-  // W2 rows of this wave as A fragments, all k.
   bf16x8_t wf[KREG];
   {
-    const int v = vw + lrow;
-    const uint16_t* w2 = static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(v < V ? v : 0) * rank;
+    const int v = min(seg * kSegLarge + lrow, V - 1);
+    const uint16_t* w2 = static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(v) * rank;
 #pragma unroll
     for (int ks = 0; ks < KREG; ++ks) {
       const int k0 = ks * 16 + khalf * 8;
-      u32x4_t raw = {0u, 0u, 0u, 0u};
-      if (v < V && k0 < rank) raw = *reinterpret_cast<const u32x4_t*>(w2 + k0);
+      u32x4_t raw = *reinterpret_cast<const u32x4_t*>(w2 + min(k0, rank - 8));
+      if (k0 >= rank) raw = u32x4_t{0u, 0u, 0u, 0u};
       wf[ks] = __builtin_bit_cast(bf16x8_t, raw);
     }
   }
-
-  for (int n0 = 0; n0 < R; n0 += kNchBf16) {
-    __syncthreads();  // previous chunk done with LDS
-    if (tid < kNchBf16) s_ci[tid] = fetch_info(p, n0 + tid, RESID);
-    __syncthreads();
-
-    // H = W1[prev] rows of this chunk into LDS; k >= rank zero-filled.
+  for (int n0 = 0; n0 < R; n0 += kNch32) {
+    lds_barrier();  // previous chunk done with LDS
+    if (tid < kNch32) s_ci[tid] = fetch_info(p, n0 + tid, RESID);
+    lds_barrier();
     {
       constexpr int G = KREG * 2;
-      const int gv = rank / 8;
       const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
-      for (int q = tid; q < kNchBf16 * G; q += 256) {
+      for (int q = tid; q < kNch32 * G; q += 256) {
         const int nn = q / G, g = q - nn * G;
-        u32x4_t val = {0u, 0u, 0u, 0u};
-        if (g < gv && s_ci[nn].act)
-          val = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank + g * 8);
+        const ReqInfo& ci = s_ci[nn];
+        u32x4_t val = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(ci.prev) * rank +
+                                                         min(g * 8, rank - 8));
+        if (g * 8 >= rank || !ci.act) val = u32x4_t{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = val;
       }
     }
-
-    // Base logits of this lane's rows for both column blocks.
     float x[2][16];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int nn = nb * 32 + lrow, n = n0 + nn;
-      const ChunkInfo& ci = s_ci[nn];
-      const bool ok = (n < R) && ci.act;
-      const float* urow = RESID ? (p.U + static_cast<int64_t>(ci.urow) * V)
-                                : (p.U_base + static_cast<int64_t>(ok ? n : 0) * p.U_stride);
-      load_row16(urow, vw + 4 * khalf, V, vec4, ok, x[nb]);
+      load16_32<VEC4>(u_row(p, s_ci[nn], n < R ? n : 0, RESID), seg * kSegLarge + 4 * khalf, V, x[nb]);
     }
-    __syncthreads();  // H ready
-
+    lds_barrier();  // H ready
     f32x16_t acc[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -234,135 +400,111 @@ __global__ void __launch_bounds__(256) bias_tile_bf16(TileParams p) {
 #pragma unroll
         for (int ks = 0; ks < KREG; ++ks) {
           const u32x4_t braw = *reinterpret_cast<const u32x4_t*>(hrow + ks * 16);
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], __builtin_bit_cast(bf16x8_t, braw),
-                                                            acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], __builtin_bit_cast(bf16x8_t, braw), acc[nb], 0,
+                                                            0, 0);
         }
       }
     }
-
-    if (!RESID) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        draft_phase1(acc[nb], x[nb], vw, khalf, V, &s_wm[nb][wave * 32 + lrow], &s_wi[nb][wave * 32 + lrow]);
-      __syncthreads();
+    if (seg < p.n_seg) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int nn = nb * 32 + lrow, n = n0 + nn;
-        float* rec = (n < R) ? p.part + (static_cast<int64_t>(n) * p.n_tiles + tile) * kPartFloats : nullptr;
-        draft_phase2(x[nb], vw, khalf, V, wave, s_wm[nb], s_wi[nb], lrow, s_ci[nn].c, rec);
-      }
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int nn = nb * 32 + lrow, n = n0 + nn;
-        const ChunkInfo ci = s_ci[nn];
-        const bool ok = (n < R) && ci.act;
-        float* rec = ok ? p.part + (static_cast<int64_t>(n) * p.n_tiles + tile) * kPartFloats : nullptr;
-        resid_epilogue(acc[nb], x[nb], p.target + static_cast<int64_t>(ci.trow) * V, vw, khalf, V, vec4, ok,
-                       ci, wave, rec);
+        const ReqInfo& ci = s_ci[nn];
+        seg32_epilogue<RESID, VEC4>(p, ci, (n < R) && ci.act, n, seg, khalf, acc[nb], x[nb]);
       }
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// fp32 weights: v_mfma_f32_32x32x2_f32, W2 streamed from memory per k step.
-// A lane l holds W2[row l&31][k = 2*ks + (l>>5)]; B the same k of H.
-// ---------------------------------------------------------------------------
-template <bool RESID>
-__global__ void __launch_bounds__(256) bias_tile_f32(TileParams p) {
+template <bool RESID, bool VEC4>
+__global__ void __launch_bounds__(256) bias_seg32_f32(TileParams p) {
+  constexpr int NCH = 32;
   constexpr int RS = DSPARK_MAX_RANK + 4;
-  __shared__ __attribute__((aligned(16))) float Hf[kNchF32 * RS];
-  __shared__ ChunkInfo s_ci[kNchF32];
-  __shared__ float s_wm[4 * 32];
-  __shared__ int s_wi[4 * 32];
-
+  __shared__ __attribute__((aligned(16))) float Hf[NCH * RS];
+  __shared__ ReqInfo s_ci[NCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, khalf = lane >> 5;
-  const int tile = blockIdx.x;
-  const int vw = tile * kTileRows + wave * kSubRows;
+  const int seg = blockIdx.x * 4 + wave;
   const int V = p.V, rank = p.rank, R = p.R;
-  const bool vec4 = (V & 3) == 0;
 
   if (RESID) {
     int any = 0;
     for (int n = tid; n < R; n += 256) any |= p.rs_info[4 * static_cast<int64_t>(n)];
     if (!__syncthreads_or(any)) return;
   }
-  const int v_a = vw + lrow;
-  const float* w2row = static_cast<const float*>(p.W2) + static_cast<int64_t>(v_a < V ? v_a : 0) * rank;
-
-  for (int n0 = 0; n0 < R; n0 += kNchF32) {
-    __syncthreads();
-    if (tid < kNchF32) s_ci[tid] = fetch_info(p, n0 + tid, RESID);
-    __syncthreads();
+  const int v_a = seg * kSegLarge + lrow;
+  const float* w2row = static_cast<const float*>(p.W2) + static_cast<int64_t>(min(v_a, V - 1)) * rank;
+  for (int n0 = 0; n0 < R; n0 += NCH) {
+    lds_barrier();
+    if (tid < NCH) s_ci[tid] = fetch_info(p, n0 + tid, RESID);
+    lds_barrier();
     {
       const float* w1 = static_cast<const float*>(p.W1);
-      for (int q = tid; q < kNchF32 * rank; q += 256) {
+      for (int q = tid; q < NCH * rank; q += 256) {
         const int nn = q / rank, k = q - nn * rank;
-        Hf[nn * RS + k] = s_ci[nn].act ? w1[static_cast<int64_t>(s_ci[nn].prev) * rank + k] : 0.0f;
+        const ReqInfo& ci = s_ci[nn];
+        Hf[nn * RS + k] = ci.act ? w1[static_cast<int64_t>(ci.prev) * rank + k] : 0.0f;
       }
     }
     float x[16];
     {
-      const int nn = lrow, n = n0 + nn;
-      const ChunkInfo& ci = s_ci[nn];
-      const bool ok = (n < R) && ci.act;
-      const float* urow = RESID ? (p.U + static_cast<int64_t>(ci.urow) * V)
-                                : (p.U_base + static_cast<int64_t>(ok ? n : 0) * p.U_stride);
-      load_row16(urow, vw + 4 * khalf, V, vec4, ok, x);
+      const int n = n0 + lrow;
+      load16_32<VEC4>(u_row(p, s_ci[lrow], n < R ? n : 0, RESID), seg * kSegLarge + 4 * khalf, V, x);
     }
-    __syncthreads();
-
+    lds_barrier();
     f32x16_t acc = f32x16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const float* hrow = &Hf[lrow * RS + khalf];
     for (int ks = 0; ks < rank / 2; ++ks) {
       const float a = (v_a < V) ? w2row[2 * ks + khalf] : 0.0f;
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, hrow[2 * ks], acc, 0, 0, 0);
     }
-
-    const int n = n0 + lrow;
-    if (!RESID) {
-      draft_phase1(acc, x, vw, khalf, V, &s_wm[wave * 32 + lrow], &s_wi[wave * 32 + lrow]);
-      __syncthreads();
-      float* rec = (n < R) ? p.part + (static_cast<int64_t>(n) * p.n_tiles + tile) * kPartFloats : nullptr;
-      draft_phase2(x, vw, khalf, V, wave, s_wm, s_wi, lrow, s_ci[lrow].c, rec);
-    } else {
-      const ChunkInfo ci = s_ci[lrow];
-      const bool ok = (n < R) && ci.act;
-      float* rec = ok ? p.part + (static_cast<int64_t>(n) * p.n_tiles + tile) * kPartFloats : nullptr;
-      resid_epilogue(acc, x, p.target + static_cast<int64_t>(ci.trow) * V, vw, khalf, V, vec4, ok, ci, wave,
-                     rec);
+    if (seg < p.n_seg) {
+      const int n = n0 + lrow;
+      const ReqInfo& ci = s_ci[lrow];
+      seg32_epilogue<RESID, VEC4>(p, ci, (n < R) && ci.act, n, seg, khalf, acc, x);
     }
   }
 }
 
-template <bool RESID>
-hipError_t launch_bf16(const TileParams& p, hipStream_t s) {
-  const dim3 grid(p.n_tiles), block(256);
-  if (p.rank <= 64) {
-    hipLaunchKernelGGL((bias_tile_bf16<4, RESID>), grid, block, 0, s, p);
-  } else if (p.rank <= 128) {
-    hipLaunchKernelGGL((bias_tile_bf16<8, RESID>), grid, block, 0, s, p);
-  } else if (p.rank <= 256) {
-    hipLaunchKernelGGL((bias_tile_bf16<16, RESID>), grid, block, 0, s, p);
-  } else {
-    hipLaunchKernelGGL((bias_tile_bf16<32, RESID>), grid, block, 0, s, p);
+template <bool RESID, bool VEC4>
+hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t s) {
+  if (wdtype == DSPARK_W_F32) {
+    hipLaunchKernelGGL((bias_seg32_f32<RESID, VEC4>), dim3((p.n_seg + 3) / 4), dim3(256), 0, s, p);
+    return hipGetLastError();
   }
+  if (p.seg_rows == kSegSmall) {
+    const int blocks = max(1, min((p.n_seg + kSeg16Waves - 1) / kSeg16Waves, num_cu));
+    const dim3 grid(blocks), block(kSeg16Waves * 64);
+    if (p.rank <= 64)
+      hipLaunchKernelGGL((bias_seg16<2, RESID, VEC4>), grid, block, 0, s, p);
+    else if (p.rank <= 128)
+      hipLaunchKernelGGL((bias_seg16<4, RESID, VEC4>), grid, block, 0, s, p);
+    else if (p.rank <= 256)
+      hipLaunchKernelGGL((bias_seg16<8, RESID, VEC4>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((bias_seg16<16, RESID, VEC4>), grid, block, 0, s, p);
+    return hipGetLastError();
+  }
+  const dim3 grid((p.n_seg + 3) / 4), block(256);
+  if (p.rank <= 64)
+    hipLaunchKernelGGL((bias_seg32<4, RESID, VEC4>), grid, block, 0, s, p);
+  else if (p.rank <= 128)
+    hipLaunchKernelGGL((bias_seg32<8, RESID, VEC4>), grid, block, 0, s, p);
+  else if (p.rank <= 256)
+    hipLaunchKernelGGL((bias_seg32<16, RESID, VEC4>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((bias_seg32<32, RESID, VEC4>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, hipStream_t s) {
-  if (p.R == 0 || p.n_tiles == 0) return hipSuccess;
-  if (wdtype == DSPARK_W_BF16) return residual ? launch_bf16<true>(p, s) : launch_bf16<false>(p, s);
-  const dim3 grid(p.n_tiles), block(256);
-  if (residual)
-    hipLaunchKernelGGL((bias_tile_f32<true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((bias_tile_f32<false>), grid, block, 0, s, p);
-  return hipGetLastError();
+hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s) {
+  if (p.R == 0 || p.n_seg == 0) return hipSuccess;
+  if (residual && (p.u_rows < 1 || p.t_rows < 1)) return hipErrorInvalidValue;
+  const bool vec4 = (p.V % 4) == 0;
+  if (residual) return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s) : launch_mode<true, false>(p, wdtype, num_cu, s);
+  return vec4 ? launch_mode<false, true>(p, wdtype, num_cu, s) : launch_mode<false, false>(p, wdtype, num_cu, s);
 }
 
 }  // namespace dspark

@@ -1,16 +1,16 @@
 // Per-request finish kernels of the draft and of the residual correction.
 //
 // Draft (one workgroup per request, once per block position): combines the
-// tile records of the fused bias kernel into the position's maximum, lowest
-// argmax and normaliser Z, and for a sampled request draws the token by
+// segment records of the fused bias kernel into the position's maximum,
+// lowest argmax and normaliser Z, and for a sampled request draws the token by
 // inverse CDF with its uniform ("DSpark" explainer sections 2 and 7: the
 // block is drafted left to right from q = softmax((U_k + B_k)/T); llama.cpp
 // PR #25173: anchor-first, bias(prev) = markov_w2 . markov_w1[prev]).
 //
 // Residual (one workgroup per request that rejected a sampled draft): draws
 // the correction from max(0, p - q) normalised (explainer section 3), using
-// the tile sums written by the residual pass of the fused bias kernel; if that
-// residual has no mass it draws from p.
+// the segment sums written by the residual pass of the fused bias kernel; if
+// that residual has no mass it draws from p.
 
 #include "dspark_device.h"
 #include "launchers.h"
@@ -20,15 +20,18 @@
 namespace dspark {
 namespace {
 
+// Rescan of one segment: thread group i (2^lpr_log2 lanes) owns row v0 + i.
+__device__ __forceinline__ int lanes_log2(int seg_rows) { return seg_rows == kSegSmall ? 4 : 3; }
+
 template <typename WT>
 __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ LocScratch sh;
   __shared__ float e32[32], s32[32];
   const int n = blockIdx.x, tid = threadIdx.x;
-  const int V = p.V;
+  const int V = p.V, n_seg = p.n_seg;
   const float c = temp_scale(p.temp[n]);
-  const float* part = p.part + static_cast<int64_t>(n) * p.n_tiles * kPartFloats;
+  const float2* rec = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
   const int64_t o = static_cast<int64_t>(n) * p.gamma + p.k;
   if (c > 0.0f) {
     const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
@@ -36,50 +39,59 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   }
   float m = -INFINITY;
   int im = kIntMax;
-  for (int t = tid; t < p.n_tiles; t += 256)
-    amax_merge(m, im, part[t * kPartFloats], __float_as_int(part[t * kPartFloats + 1]));
+  if (c == 0.0f) {
+    for (int t = tid; t < n_seg; t += 256) {
+      const float2 r = rec[t];
+      amax_merge(m, im, r.x, __float_as_int(r.y));
+    }
+  } else {
+    for (int t = tid; t < n_seg; t += 256) m = fmaxf(m, rec[t].x);
+    im = 0;
+  }
   block256_amax(m, im, sh.fred, sh.ired);
-  const int I = clampi(im, 0, V - 1);
+  const float M = m;
   if (c == 0.0f) {
     if (tid == 0) {
-      p.y[o] = I;
+      p.y[o] = clampi(im, 0, V - 1);
       p.q_tok[o] = 1.0f;
-      p.q_stats[2 * o] = m;
+      p.q_stats[2 * o] = M;
       p.q_stats[2 * o + 1] = 1.0f;
     }
     return;
   }
   const float u = clamp_uniform(p.u_draft[o]);
-  auto mass = [&](int t) { return tile_record_mass(part + t * kPartFloats, m, c, true); };
-  const Located L = locate_segments(p.n_tiles, mass, u, &sh);
-  const int tile = L.index < 0 ? I / kTileRows : L.index;
-  const float* rec = part + tile * kPartFloats;
-  const float mt = rec[0];
-  const float scale = exp2_hw((mt - m) * c);
-  float th_sub;
-  const int sub = pick_sub(rec, L.fallback ? INFINITY : (u * L.Z - L.P) / scale, L.fallback, &th_sub);
-  const int v0 = tile * kTileRows + sub * kSubRows;
-  const int i = tid >> 3;
+  auto mass = [&](int t) {
+    const float2 r = rec[t];
+    return r.y * exp2_hw((r.x - M) * c);
+  };
+  const Located L = locate_segments(n_seg, mass, u, &sh);
+  const int seg = L.index < 0 ? 0 : L.index;
+  const float ms = rec[seg].x;
+  const float th = L.fallback ? INFINITY : (u * L.Z - L.P) / exp2_hw((ms - M) * c);
+  const int lg = lanes_log2(p.seg_rows);
+  const int v0 = seg * p.seg_rows;
+  const int i = tid >> lg;
   const int v = v0 + i;
-  const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V);
-  if ((tid & 7) == 0) {
+  const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);
+  if ((tid & ((1 << lg) - 1)) == 0) {
     float s = -INFINITY, e = 0.0f;
     if (v < V) {
       s = p.U_base[static_cast<int64_t>(n) * p.U_stride + v] + b;
-      e = exp2_hw((s - mt) * c);
+      e = exp2_hw((s - ms) * c);
     }
     e32[i] = e;
     s32[i] = s;
   }
+  if (tid >= p.seg_rows && tid < 32) e32[tid] = 0.0f;
   __syncthreads();
   if (tid < 64) {
-    const int pos = pick32(e32, th_sub);
+    const int pos = pick32(e32, th);
     if (tid == 0) {
-      const int yy = (pos >= 0) ? v0 + pos : I;
-      const float sy = (pos >= 0) ? s32[pos] : m;
+      const int yy = (pos >= 0) ? v0 + pos : min(v0, V - 1);
+      const float sy = (pos >= 0) ? s32[pos] : M;
       p.y[o] = yy;
-      p.q_tok[o] = exp2_hw((sy - m) * c) / L.Z;
-      p.q_stats[2 * o] = m;
+      p.q_tok[o] = exp2_hw((sy - M) * c) / L.Z;
+      p.q_stats[2 * o] = M;
       p.q_stats[2 * o + 1] = L.Z;
     }
   }
@@ -90,31 +102,32 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ ChunkScratch sh;
   __shared__ float e32[32];
+  __shared__ int s_out;
   const int n = blockIdx.x, tid = threadIdx.x;
   const int32_t* info = p.rs_info + 4 * static_cast<int64_t>(n);
   if (info[0] == 0) return;
   const int V = p.V;
   const int prev = clampi(info[1], 0, V - 1);
-  const int64_t urow = info[2], trow = info[3];
+  const int64_t urow = min(max(static_cast<int64_t>(info[2]), int64_t{0}), static_cast<int64_t>(p.R) * p.gamma - 1);
+  const int64_t trow = min(max(static_cast<int64_t>(info[3]), int64_t{0}), p.n_rows - 1);
   const float* st = p.rs_stats + 4 * static_cast<int64_t>(n);
   const float Mq = st[0], iZq = 1.0f / st[1], Mp = st[2], iZp = 1.0f / st[3];
   const float c = temp_scale(p.temp[n]);
   const float u = clamp_uniform(p.u_final[n]);
   load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
-  const float* part = p.rpart + static_cast<int64_t>(n) * p.n_tiles * kPartFloats;
-  auto mass = [&](int t) { return tile_record_mass(part + t * kPartFloats, 0.0f, 0.0f, false); };
-  const Located L = locate_segments(p.n_tiles, mass, u, &sh.loc);
+  const float2* rec = reinterpret_cast<const float2*>(p.rpart) + static_cast<int64_t>(n) * p.n_seg;
+  auto mass = [&](int t) { return rec[t].y; };
+  const Located L = locate_segments(p.n_seg, mass, u, &sh.loc);
   const float* tr = p.target + trow * V;
   int out = -1;
   if (L.Z > 0.0f && L.index >= 0) {
-    const float* rec = part + L.index * kPartFloats;
-    float th_sub;
-    const int sub = pick_sub(rec, L.fallback ? INFINITY : (u * L.Z - L.P), L.fallback, &th_sub);
-    const int v0 = L.index * kTileRows + sub * kSubRows;
-    const int i = tid >> 3;
+    const float th = L.fallback ? INFINITY : (u * L.Z - L.P);
+    const int lg = lanes_log2(p.seg_rows);
+    const int v0 = L.index * p.seg_rows;
+    const int i = tid >> lg;
     const int v = v0 + i;
-    const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V);
-    if ((tid & 7) == 0) {
+    const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);
+    if ((tid & ((1 << lg) - 1)) == 0) {
       float w = 0.0f;
       if (v < V) {
         const float s = p.U[urow * V + v] + b;
@@ -124,14 +137,14 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
       }
       e32[i] = w;
     }
+    if (tid >= p.seg_rows && tid < 32) e32[tid] = 0.0f;
     __syncthreads();
     if (tid < 64) {
-      const int pos = pick32(e32, th_sub);
-      if (tid == 0) sh.ired[0] = (pos >= 0) ? v0 + pos : -1;
+      const int pos = pick32(e32, th);
+      if (tid == 0) s_out = (pos >= 0) ? v0 + pos : -1;
     }
     __syncthreads();
-    out = sh.ired[0];
-    __syncthreads();
+    out = s_out;
   }
   if (out < 0) {
     // no residual mass: the correction is drawn from p itself

@@ -9,18 +9,19 @@
 
 namespace dspark {
 
-// One launch of the fused Markov-bias + softmax-statistics tile kernel.
+// One launch of the fused Markov-bias + softmax-statistics kernel.
 //   draft mode:    request n uses prev = prev_base[n * prev_stride] and the
-//                  base-logit row U_base + n * U_stride; writes per (n, tile)
-//                  the max / lowest argmax of s = U + B and, for sampled
-//                  requests, the four 32-row sums of exp((s - max)/T).
+//                  base-logit row U_base + n * U_stride; writes per (n, segment)
+//                  the record (max of s = U + B, sum of exp((s - max)/T)) for a
+//                  sampled request or (max, lowest argmax) for a greedy one.
 //   residual mode: request n takes (flag, prev, U row, target row) from
-//                  rs_info and (Mq, Zq, Mp, Zp) from rs_stats and writes the
-//                  four 32-row sums of max(0, p - q); flag 0 => skipped.
+//                  rs_info and (Mq, Zq, Mp, Zp) from rs_stats and writes
+//                  (0, sum of max(0, p - q)) per segment; flag 0 => skipped.
 struct TileParams {
   const void* W1;
   const void* W2;
-  int V, rank, R, n_tiles;
+  int V, rank, R;
+  int seg_rows, n_seg;
   const int32_t* prev_base;
   int prev_stride;
   const float* U_base;
@@ -28,15 +29,16 @@ struct TileParams {
   const float* temp;
   const int32_t* rs_info;
   const float* rs_stats;
-  const float* U;        // [R * gamma, V] (residual mode)
-  const float* target;   // [n_rows, V]   (residual mode)
-  float* part;           // [R][n_tiles][kPartFloats]
+  const float* U;        // [u_rows = R * gamma, V] (residual mode)
+  const float* target;   // [t_rows = n_rows, V]    (residual mode)
+  int64_t u_rows, t_rows;
+  float* part;           // [R][n_seg][kRecFloats]
 };
 
-// Per-position draft finish: turns the tile records into y / q_tok / q_stats.
+// Per-position draft finish: turns the segment records into y / q_tok / q_stats.
 struct FinishParams {
   const float* part;
-  int n_tiles, V, rank, R, gamma, k;
+  int seg_rows, n_seg, V, rank, R, gamma, k;
   const void* W1;
   const void* W2;
   const int32_t* prev_base;
@@ -51,7 +53,7 @@ struct FinishParams {
 };
 
 struct VerifyParams {
-  int R, gamma, V, rank, n_chunks, n_tiles;
+  int R, gamma, V, rank, n_chunks, seg_rows, n_seg;
   int64_t n_rows;
   const float* target;
   const int32_t* row_offsets;
@@ -71,10 +73,10 @@ struct VerifyParams {
   float* vpart;      // [n_rows][n_chunks][kChunkFloats]
   int32_t* rs_info;  // [R][4]
   float* rs_stats;   // [R][4]
-  float* rpart;      // [R][n_tiles][kPartFloats]
+  float* rpart;      // [R][n_seg][kRecFloats]
 };
 
-hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, hipStream_t s);
+hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s);
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s);
 hipError_t launch_verify_stats(const VerifyParams& p, hipStream_t s);
 hipError_t launch_verify_finish(const VerifyParams& p, hipStream_t s);

@@ -12,7 +12,6 @@ inline bool aligned(const void* p, std::size_t a) {
 
 inline std::size_t round_up(std::size_t x, std::size_t a) { return (x + a - 1) / a * a; }
 
-inline int n_tiles_for(int32_t V) { return (V + kTileRows - 1) / kTileRows; }
 
 }  // namespace
 
@@ -32,9 +31,10 @@ int plan_draft(const dspark_draft_args* a, DraftPlan* plan) {
   if (a->struct_size != sizeof(dspark_draft_args)) return DSPARK_ERR_ABI;
   int st = check_dims(a->R, a->gamma, a->V, a->rank, a->wdtype);
   if (st != DSPARK_OK) return st;
-  plan->n_tiles = n_tiles_for(a->V);
+  plan->seg_rows = seg_rows_for(a->R, a->wdtype);
+  plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
   plan->part_off = 0;
-  std::size_t part = static_cast<std::size_t>(a->R) * plan->n_tiles * kPartFloats * sizeof(float);
+  std::size_t part = static_cast<std::size_t>(a->R) * plan->n_seg * kRecFloats * sizeof(float);
   plan->total = round_up(part, kWsAlign);
   return DSPARK_OK;
 }
@@ -62,7 +62,8 @@ int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
   if (st != DSPARK_OK) return st;
   const int64_t max_rows = static_cast<int64_t>(a->R) * (a->gamma + 1);
   if (a->n_rows < a->R || a->n_rows > max_rows) return DSPARK_ERR_SHAPE;
-  plan->n_tiles = n_tiles_for(a->V);
+  plan->seg_rows = seg_rows_for(a->R, a->wdtype);
+  plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
   plan->n_chunks = (a->V + kChunk - 1) / kChunk;
   std::size_t off = 0;
   plan->vpart_off = off;
@@ -73,8 +74,7 @@ int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
   plan->rsstats_off = off;
   off = round_up(off + static_cast<std::size_t>(a->R) * 4 * sizeof(float), kWsAlign);
   plan->rpart_off = off;
-  off = round_up(off + static_cast<std::size_t>(a->R) * plan->n_tiles * kPartFloats * sizeof(float),
-                 kWsAlign);
+  off = round_up(off + static_cast<std::size_t>(a->R) * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
   plan->total = off;
   return DSPARK_OK;
 }

@@ -9,29 +9,39 @@
 
 namespace dspark {
 
-// Vocabulary rows per workgroup of the fused bias + softmax kernels
-// (4 wavefronts x one 32-row MFMA tile each).
-constexpr int kTileRows = 128;
-constexpr int kSubRows = 32;                 // rows per wavefront sub-tile
-constexpr int kPartFloats = 8;               // floats per (request, tile) record
+// The fused bias + softmax kernels reduce each request's logits over
+// vocabulary segments of 16 rows (bf16 weights, R <= 64: one 16x16x32 MFMA
+// row block per wavefront) or 32 rows (otherwise: 32x32 MFMA row blocks) to
+// one record of two floats per (request, segment).
+constexpr int kSegSmall = 16;
+constexpr int kSegLarge = 32;
+constexpr int kSmallMaxR = 64;               // requests held by the 16-row path
+constexpr int kRecFloats = 2;                // floats per (request, segment) record
 // Target-row elements per workgroup of the verify statistics kernel.
 constexpr int kChunk = 4096;
 constexpr int kChunkFloats = 4;              // floats per (row, chunk) record
 constexpr std::size_t kWsAlign = 256;
 
+// Rows per segment for a batch of R requests with weights of type wdtype.
+inline int seg_rows_for(int32_t R, int32_t wdtype) {
+  return (wdtype == DSPARK_W_BF16 && R <= kSmallMaxR) ? kSegSmall : kSegLarge;
+}
+
 struct DraftPlan {
-  int n_tiles = 0;
-  std::size_t part_off = 0;   // [R][n_tiles][kPartFloats] float
+  int seg_rows = 0;
+  int n_seg = 0;
+  std::size_t part_off = 0;   // [R][n_seg][kRecFloats] float
   std::size_t total = 0;
 };
 
 struct VerifyPlan {
-  int n_tiles = 0;
+  int seg_rows = 0;
+  int n_seg = 0;
   int n_chunks = 0;
   std::size_t vpart_off = 0;    // [n_rows][n_chunks][kChunkFloats] float
   std::size_t rsinfo_off = 0;   // [R][4] int32: flag, prev, U row, target row
   std::size_t rsstats_off = 0;  // [R][4] float: Mq, 1/Zq, Mp, 1/Zp
-  std::size_t rpart_off = 0;    // [R][n_tiles][kPartFloats] float
+  std::size_t rpart_off = 0;    // [R][n_seg][kRecFloats] float
   std::size_t total = 0;
 };
 

@@ -1,12 +1,13 @@
-// Inverse-CDF location over per-tile partial sums, shared by the finish
+// Inverse-CDF location over per-segment partial sums, shared by the finish
 // kernels (256 threads per workgroup, one request per workgroup).
 //
 // An inverse-CDF draw walks the vocabulary in index order and returns the
 // first entry whose inclusive cumulative mass exceeds u * Z.  The vocabulary
-// is covered by tiles whose masses were reduced by an earlier kernel, so the
-// walk is done in three levels: a block-wide prefix over tile masses picks the
-// tile, a prefix over its four 32-row sub-sums picks the sub-tile, and only
-// that sub-tile's 32 entries are recomputed and scanned.  Intervals of
+// is covered by segments whose masses were reduced by an earlier kernel, so
+// the walk is done in two levels: a block-wide prefix over segment masses
+// picks the segment, and only that segment's 16 or 32 entries are recomputed
+// and scanned (a target row, which is an input, is rescanned in chunks of
+// 4096 entries instead).  Intervals of
 // consecutive threads meet exactly (block256_scan), so exactly one thread owns
 // any threshold; where rounding between levels leaves the threshold past the
 // last entry of a chosen range, the last positive-mass entry of that range is
@@ -102,39 +103,6 @@ __device__ Located locate_segments(int n, Mass mass, float u, LocScratch* sh) {
   return L;
 }
 
-// Mass of one (request, tile) record; `scaled` re-expresses the tile's sum
-// (taken relative to the tile maximum) relative to the global maximum M.
-__device__ __forceinline__ float tile_record_mass(const float* rec, float M, float c, bool scaled) {
-  const float s = ((rec[2] + rec[3]) + rec[4]) + rec[5];
-  return scaled ? s * exp2_hw((rec[0] - M) * c) : s;
-}
-
-// Sub-tile choice inside tile record `rec` for local threshold th (tile units).
-// Returns sub index (0..3) and writes the remaining threshold into *th_sub.
-__device__ __forceinline__ int pick_sub(const float* rec, float th, bool fallback, float* th_sub) {
-  int sub = -1, lastsub = -1;
-  float before = 0.0f, cum = 0.0f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float x = rec[2 + w];
-    const float nc = cum + x;
-    if (x > 0.0f) {
-      lastsub = w;
-      if (sub < 0 && !fallback && nc > th) {
-        sub = w;
-        before = cum;
-      }
-    }
-    cum = nc;
-  }
-  if (sub < 0) {
-    *th_sub = INFINITY;
-    return lastsub < 0 ? 0 : lastsub;
-  }
-  *th_sub = th - before;
-  return sub;
-}
-
 // Wave 0: first of 32 weights whose inclusive prefix exceeds theta, else the
 // last positive one, else -1.
 __device__ __forceinline__ int pick32(const float* e32, float theta) {
@@ -174,19 +142,19 @@ __device__ __forceinline__ float dot8(const float* row, const float* h, int k) {
   return acc;
 }
 
-// Markov bias W2[v, :] . h for v = row of this thread's group of 8 lanes
-// (row index = threadIdx.x >> 3 within the 32 rows).  All 8 lanes return it.
+// Markov bias W2[v, :] . h for one vocabulary row per group of 2^lpr_log2
+// consecutive lanes (row index = threadIdx.x >> lpr_log2).  Every lane of the
+// group returns the same value.
 template <typename WT>
-__device__ __forceinline__ float row_bias(const WT* W2, const float* hs, int rank, int v, int V) {
-  const int part = threadIdx.x & 7;
+__device__ __forceinline__ float row_bias(const WT* W2, const float* hs, int rank, int v, int V, int lpr_log2) {
+  const int lpr = 1 << lpr_log2;
+  const int part = threadIdx.x & (lpr - 1);
   float acc = 0.0f;
   if (v < V) {
     const WT* row = W2 + static_cast<int64_t>(v) * rank;
-    for (int k = part * 8; k < rank; k += 64) acc += dot8(row, hs, k);
+    for (int k = part * 8; k < rank; k += lpr * 8) acc += dot8(row, hs, k);
   }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
+  for (int d = 1; d < lpr; d <<= 1) acc += __shfl_xor(acc, d);
   return acc;
 }
 

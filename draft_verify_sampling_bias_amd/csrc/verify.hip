@@ -117,6 +117,15 @@ __global__ void __launch_bounds__(256) verify_stats_kernel(VerifyParams p) {
   }
 }
 
+// marks request n as needing no residual pass (all four words written)
+__device__ __forceinline__ void clear_residual(const VerifyParams& p, int n) {
+  int32_t* inf = p.rs_info + 4 * static_cast<int64_t>(n);
+  inf[0] = 0;
+  inf[1] = 0;
+  inf[2] = 0;
+  inf[3] = 0;
+}
+
 __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
   __shared__ float rM[DSPARK_MAX_GAMMA + 1], rZ[DSPARK_MAX_GAMMA + 1];
   __shared__ int rI[DSPARK_MAX_GAMMA + 1];
@@ -133,7 +142,7 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
     if (tid == 0) {
       p.n_accept[n] = 0;
       p.out_tok[n] = -1;
-      p.rs_info[4 * static_cast<int64_t>(n)] = 0;
+      clear_residual(p, n);
     }
     return;
   }
@@ -192,7 +201,7 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
   if (c == 0.0f) {
     if (tid == 0) {
       p.out_tok[n] = rI[nacc];
-      p.rs_info[4 * static_cast<int64_t>(n)] = 0;
+      clear_residual(p, n);
     }
     return;
   }
@@ -202,7 +211,7 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
                                V, rM[l], c, u, &sh);
     if (tid == 0) {
       p.out_tok[n] = (out >= 0) ? out : rI[l];
-      p.rs_info[4 * static_cast<int64_t>(n)] = 0;
+      clear_residual(p, n);
     }
   } else if (tid == 0) {
     const int prev = (nacc == 0) ? p.anchor[n] : p.y[og + nacc - 1];
