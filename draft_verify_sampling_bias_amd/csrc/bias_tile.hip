@@ -113,6 +113,10 @@ struct Seg16Regs {
   f32x4_t t[RESID ? 4 : 1];  // target values, residual mode
 };
 
+// Issues the loads of segment [vw, vw + 16).  Rows past V re-read row V - 1
+// and columns k >= rank re-read the row's last 8 weights; both are masked at
+// use, so no instruction touches the loaded registers before the MFMA or the
+// epilogue needs them.
 template <int KS, bool RESID, bool VEC4>
 __device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s_ci, int vw, int lane,
                                            Seg16Regs<KS, RESID>& f) {
@@ -123,9 +127,7 @@ __device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int k = ks * 32 + kq * 8;
-    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(w2 + min(k, rank - 8));
-    if (k >= rank) raw = u32x4_t{0u, 0u, 0u, 0u};
-    f.w[ks] = __builtin_bit_cast(bf16x8_t, raw);
+    f.w[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(w2 + min(k, rank - 8)));
   }
   const int vu = vw + kq * 4;
 #pragma unroll
@@ -138,7 +140,8 @@ __device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s
 }
 
 template <int KS>
-__device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16_t* Hs, int lane, f32x4_t (&acc)[4]) {
+__device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
+                                           f32x4_t (&acc)[4]) {
   constexpr int RS = KS * 32 + 8;
   const int l16 = lane & 15, kq = lane >> 4;
 #pragma unroll
@@ -155,32 +158,64 @@ __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16
       for (int nb = 0; nb < 4; ++nb)
         b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
     }
+    // the empty asm pins the zeroing here: hoisted next to the load (across
+    // the loop's back edge) it would wait on the whole prefetch
+    bf16x8_t a = w[ks];
+    asm volatile("" : "+v"(a));
+    a = (ks * 32 + kq * 8 < rank) ? a : bf16x8_t{};
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[ks], __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb],
-                                                        0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb], 0, 0,
+                                                        0);
     // keep the B reads one step ahead only: unrestricted hoisting of all of
     // them exhausts the register file
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
+// Per-lane copies of the request constants of the lane's four requests
+// (request 16 nb + (lane & 15)), kept in registers for the whole walk.
+template <bool RESID>
+struct LaneReq {
+  float c[4];  // log2(e) / T, 0 for greedy
+  float Mq[RESID ? 4 : 1], iZq[RESID ? 4 : 1], Mp[RESID ? 4 : 1], iZp[RESID ? 4 : 1];
+};
+
+template <bool RESID>
+__device__ __forceinline__ void lane_req(const ReqInfo* s_ci, int lane, LaneReq<RESID>& q) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const ReqInfo ci = s_ci[nb * 16 + (lane & 15)];
+    q.c[nb] = ci.c;
+    if (RESID) {
+      q.Mq[nb] = ci.Mq;
+      q.iZq[nb] = ci.iZq;
+      q.Mp[nb] = ci.Mp;
+      q.iZp[nb] = ci.iZp;
+    }
+  }
+}
+
+// Epilogue of one 16-row segment, branch-free: reduces the 16 rows held by
+// the four lanes (lane & 15) + 16 j of each request column and stores the
+// segment's record.  All four lanes hold the reduced record and all store it
+// (same value, same address); records of absent requests land in padding
+// rows of the workspace and are never read.
 template <int KS, bool RESID>
-__device__ __forceinline__ void seg16_epilogue(const TileParams& p, const ReqInfo* s_ci, int wt, int lane,
+__device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneReq<RESID>& q, int wt, int lane,
                                                const Seg16Regs<KS, RESID>& f, const f32x4_t (&acc)[4]) {
   const int l16 = lane & 15, kq = lane >> 4;
-  const int V = p.V, R = p.R;
+  const int V = p.V;
   const int vb = wt * kSegSmall + kq * 4;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     const int nn = nb * 16 + l16;
-    const ReqInfo& ci = s_ci[nn];
-    const bool okn = (nn < R) && ci.act;
+    const float c = q.c[nb];
     f32x4_t s = acc[nb] + f.u[nb];
     float x, y;
     if (!RESID) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = (okn && vb + i < V) ? s[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) s[i] = (vb + i < V) ? s[i] : -INFINITY;
       float m = s[0];
       int im = vb;
 #pragma unroll
@@ -191,37 +226,40 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const ReqInf
       }
       amax_sel(m, im, __shfl_xor(m, 16), __shfl_xor(im, 16));
       amax_sel(m, im, __shfl_xor(m, 32), __shfl_xor(im, 32));
+      // exp2(-inf) = 0 for rows past V; a greedy request (c = 0) keeps im
       float e = 0.f;
-      if (ci.c > 0.f) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e += exp2_hw((s[i] - m) * ci.c);
-      }
+      for (int i = 0; i < 4; ++i) e += exp2_hw((s[i] - m) * c);
       e += __shfl_xor(e, 16);
       e += __shfl_xor(e, 32);
       x = m;
-      y = (ci.c > 0.f) ? e : __int_as_float(im);
+      y = (c > 0.f) ? e : __int_as_float(im);
     } else {
       float w = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float q = exp2_hw((s[i] - ci.Mq) * ci.c) * ci.iZq;
-        const float pp = exp2_hw((f.t[nb][i] - ci.Mp) * ci.c) * ci.iZp;
-        w += (okn && vb + i < V) ? fmaxf(pp - q, 0.f) : 0.f;
+        const float qq = exp2_hw((s[i] - q.Mq[nb]) * c) * q.iZq[nb];
+        const float pp = exp2_hw((f.t[nb][i] - q.Mp[nb]) * c) * q.iZp[nb];
+        // rows past V add +0 (a bit mask, not a branch around the exps)
+        const float d = fmaxf(pp - qq, 0.f);
+        w += __int_as_float(__float_as_int(d) & -static_cast<int>(vb + i < V));
       }
       w += __shfl_xor(w, 16);
       w += __shfl_xor(w, 32);
       x = 0.f;
       y = w;
     }
-    if (kq == 0 && okn) {
-      float2* rec = reinterpret_cast<float2*>(p.part) + static_cast<int64_t>(nn) * p.n_seg + wt;
-      *rec = make_float2(x, y);
-    }
+    float2* rec = reinterpret_cast<float2*>(p.part) + static_cast<int64_t>(nn) * p.n_seg + wt;
+    *rec = make_float2(x, y);
   }
 }
 
 constexpr int kSeg16Waves = 4;  // one wavefront per SIMD: the prefetched tile needs ~260 registers
 
+// Wavefront w of the grid handles segments w, w + W, w + 2W, ... (W = all
+// wavefronts), so at any moment the grid streams one contiguous stretch of
+// W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
+// each of 64 rows.
 template <int KS, bool RESID, bool VEC4>
 __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16(TileParams p) {
   constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
@@ -229,7 +267,7 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16(TileParams p) {
   __shared__ ReqInfo s_ci[kSmallMaxR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = p.R, rank = p.rank;
-  const int n_wt = p.n_seg;
+  const int n_seg = p.n_seg;
 
   if (RESID) {
     int any = 0;
@@ -250,23 +288,31 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16(TileParams p) {
       *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = val;
     }
   }
-  const int stride = gridDim.x * kSeg16Waves;
-  int wt = blockIdx.x * kSeg16Waves + wave;
+  // wavefront-uniform walk state (scalar registers, scalar branches)
+  const int n_waves = gridDim.x * kSeg16Waves;
+  int sg = blockIdx.x * kSeg16Waves + __builtin_amdgcn_readfirstlane(wave);
   Seg16Regs<KS, RESID> fa, fb;
-  seg16_load<KS, RESID, VEC4>(p, s_ci, min(wt, n_wt - 1) * kSegSmall, lane, fa);
+  seg16_load<KS, RESID, VEC4>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
   lds_barrier();
-  while (wt < n_wt) {
+  if (sg >= n_seg) return;
+  LaneReq<RESID> lq;
+  lane_req<RESID>(s_ci, lane, lq);
+  // Ping-pong prefetch.  The prefetch issued on a wavefront's last segment
+  // re-reads segment n_seg - 1 (a cache hit, never used) so that the load
+  // stream, and with it the compiler's wait counts, is the same every trip.
+  while (true) {
     f32x4_t acc[4];
-    const int wt1 = wt + stride;
-    if (wt1 < n_wt) seg16_load<KS, RESID, VEC4>(p, s_ci, wt1 * kSegSmall, lane, fb);
-    seg16_mfma<KS>(fa.w, Hs, lane, acc);
-    seg16_epilogue<KS, RESID>(p, s_ci, wt, lane, fa, acc);
-    if (wt1 >= n_wt) break;
-    const int wt2 = wt1 + stride;
-    if (wt2 < n_wt) seg16_load<KS, RESID, VEC4>(p, s_ci, wt2 * kSegSmall, lane, fa);
-    seg16_mfma<KS>(fb.w, Hs, lane, acc);
-    seg16_epilogue<KS, RESID>(p, s_ci, wt1, lane, fb, acc);
-    wt = wt2;
+    const int s1 = sg + n_waves;
+    seg16_load<KS, RESID, VEC4>(p, s_ci, min(s1, n_seg - 1) * kSegSmall, lane, fb);
+    seg16_mfma<KS>(fa.w, Hs, rank, lane, acc);
+    seg16_epilogue<KS, RESID>(p, lq, sg, lane, fa, acc);
+    if (s1 >= n_seg) break;
+    const int s2 = s1 + n_waves;
+    seg16_load<KS, RESID, VEC4>(p, s_ci, min(s2, n_seg - 1) * kSegSmall, lane, fa);
+    seg16_mfma<KS>(fb.w, Hs, rank, lane, acc);
+    seg16_epilogue<KS, RESID>(p, lq, s1, lane, fb, acc);
+    if (s2 >= n_seg) break;
+    sg = s2;
   }
 }
 
@@ -473,6 +519,7 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     return hipGetLastError();
   }
   if (p.seg_rows == kSegSmall) {
+    // persistent: at most one workgroup (four wavefronts, one per SIMD) per CU
     const int blocks = max(1, min((p.n_seg + kSeg16Waves - 1) / kSeg16Waves, num_cu));
     const dim3 grid(blocks), block(kSeg16Waves * 64);
     if (p.rank <= 64)
@@ -502,6 +549,8 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
 hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s) {
   if (p.R == 0 || p.n_seg == 0) return hipSuccess;
   if (residual && (p.u_rows < 1 || p.t_rows < 1)) return hipErrorInvalidValue;
+  // the 16-row path holds at most kSmallMaxR requests (LDS tile, record rows)
+  if (p.seg_rows == kSegSmall && (p.R > kSmallMaxR || wdtype != DSPARK_W_BF16)) return hipErrorInvalidValue;
   const bool vec4 = (p.V % 4) == 0;
   if (residual) return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s) : launch_mode<true, false>(p, wdtype, num_cu, s);
   return vec4 ? launch_mode<false, true>(p, wdtype, num_cu, s) : launch_mode<false, false>(p, wdtype, num_cu, s);

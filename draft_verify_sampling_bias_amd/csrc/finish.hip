@@ -26,12 +26,12 @@ __device__ __forceinline__ int lanes_log2(int seg_rows) { return seg_rows == kSe
 template <typename WT>
 __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
-  __shared__ LocScratch sh;
+  __shared__ Loc2Scratch sh;
   __shared__ float e32[32], s32[32];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int V = p.V, n_seg = p.n_seg;
   const float c = temp_scale(p.temp[n]);
-  const float2* rec = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
+  const float2* fine = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
   const int64_t o = static_cast<int64_t>(n) * p.gamma + p.k;
   if (c > 0.0f) {
     const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
@@ -39,13 +39,17 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   }
   float m = -INFINITY;
   int im = kIntMax;
+  // coalesced pass over the segment records: maximum (and, greedy, the
+  // lowest argmax carried in the records' second word)
   if (c == 0.0f) {
+#pragma unroll 8
     for (int t = tid; t < n_seg; t += 256) {
-      const float2 r = rec[t];
+      const float2 r = fine[t];
       amax_merge(m, im, r.x, __float_as_int(r.y));
     }
   } else {
-    for (int t = tid; t < n_seg; t += 256) m = fmaxf(m, rec[t].x);
+#pragma unroll 8
+    for (int t = tid; t < n_seg; t += 256) m = fmaxf(m, fine[t].x);
     im = 0;
   }
   block256_amax(m, im, sh.fred, sh.ired);
@@ -61,13 +65,13 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   }
   const float u = clamp_uniform(p.u_draft[o]);
   auto mass = [&](int t) {
-    const float2 r = rec[t];
+    const float2 r = fine[t];
     return r.y * exp2_hw((r.x - M) * c);
   };
-  const Located L = locate_segments(n_seg, mass, u, &sh);
-  const int seg = L.index < 0 ? 0 : L.index;
-  const float ms = rec[seg].x;
-  const float th = L.fallback ? INFINITY : (u * L.Z - L.P) / exp2_hw((ms - M) * c);
+  const Located2 L = locate_blocked(n_seg, mass, u, &sh);
+  const int seg = L.seg < 0 ? 0 : L.seg;
+  const float ms = fine[seg].x;
+  const float th = L.fallback ? INFINITY : L.rem / exp2_hw((ms - M) * c);
   const int lg = lanes_log2(p.seg_rows);
   const int v0 = seg * p.seg_rows;
   const int i = tid >> lg;
@@ -100,6 +104,7 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
 template <typename WT>
 __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
+  __shared__ Loc2Scratch sh2;
   __shared__ ChunkScratch sh;
   __shared__ float e32[32];
   __shared__ int s_out;
@@ -115,15 +120,15 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   const float c = temp_scale(p.temp[n]);
   const float u = clamp_uniform(p.u_final[n]);
   load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
-  const float2* rec = reinterpret_cast<const float2*>(p.rpart) + static_cast<int64_t>(n) * p.n_seg;
-  auto mass = [&](int t) { return rec[t].y; };
-  const Located L = locate_segments(p.n_seg, mass, u, &sh.loc);
+  const float2* fine = reinterpret_cast<const float2*>(p.rpart) + static_cast<int64_t>(n) * p.n_seg;
+  auto mass = [&](int t) { return fine[t].y; };
+  const Located2 L = locate_blocked(p.n_seg, mass, u, &sh2);
   const float* tr = p.target + trow * V;
   int out = -1;
-  if (L.Z > 0.0f && L.index >= 0) {
-    const float th = L.fallback ? INFINITY : (u * L.Z - L.P);
+  if (L.Z > 0.0f && L.seg >= 0) {
+    const float th = L.fallback ? INFINITY : L.rem;
     const int lg = lanes_log2(p.seg_rows);
-    const int v0 = L.index * p.seg_rows;
+    const int v0 = L.seg * p.seg_rows;
     const int i = tid >> lg;
     const int v = v0 + i;
     const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);

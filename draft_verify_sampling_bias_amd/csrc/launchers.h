@@ -32,12 +32,12 @@ struct TileParams {
   const float* U;        // [u_rows = R * gamma, V] (residual mode)
   const float* target;   // [t_rows = n_rows, V]    (residual mode)
   int64_t u_rows, t_rows;
-  float* part;           // [R][n_seg][kRecFloats]
+  float* part;           // [record_rows][n_seg][kRecFloats] segment records
 };
 
 // Per-position draft finish: turns the segment records into y / q_tok / q_stats.
 struct FinishParams {
-  const float* part;
+  const float* part;     // segment records of the fused bias kernel
   int seg_rows, n_seg, V, rank, R, gamma, k;
   const void* W1;
   const void* W2;
@@ -73,7 +73,7 @@ struct VerifyParams {
   float* vpart;      // [n_rows][n_chunks][kChunkFloats]
   int32_t* rs_info;  // [R][4]
   float* rs_stats;   // [R][4]
-  float* rpart;      // [R][n_seg][kRecFloats]
+  float* rpart;      // [record_rows][n_seg][kRecFloats] residual segment records
 };
 
 hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s);

@@ -33,9 +33,9 @@ int plan_draft(const dspark_draft_args* a, DraftPlan* plan) {
   if (st != DSPARK_OK) return st;
   plan->seg_rows = seg_rows_for(a->R, a->wdtype);
   plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
+  const std::size_t rows = static_cast<std::size_t>(record_rows(plan->seg_rows, a->R));
   plan->part_off = 0;
-  std::size_t part = static_cast<std::size_t>(a->R) * plan->n_seg * kRecFloats * sizeof(float);
-  plan->total = round_up(part, kWsAlign);
+  plan->total = round_up(rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
   return DSPARK_OK;
 }
 
@@ -73,8 +73,9 @@ int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
   off = round_up(off + static_cast<std::size_t>(a->R) * 4 * sizeof(int32_t), kWsAlign);
   plan->rsstats_off = off;
   off = round_up(off + static_cast<std::size_t>(a->R) * 4 * sizeof(float), kWsAlign);
+  const std::size_t rows = static_cast<std::size_t>(record_rows(plan->seg_rows, a->R));
   plan->rpart_off = off;
-  off = round_up(off + static_cast<std::size_t>(a->R) * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
+  off = round_up(off + rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
   plan->total = off;
   return DSPARK_OK;
 }

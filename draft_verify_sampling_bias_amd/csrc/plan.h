@@ -17,6 +17,24 @@ constexpr int kSegSmall = 16;
 constexpr int kSegLarge = 32;
 constexpr int kSmallMaxR = 64;               // requests held by the 16-row path
 constexpr int kRecFloats = 2;                // floats per (request, segment) record
+// Record arrays of the 16-row path hold kSmallMaxR request rows whatever R
+// is: every lane of the kernel stores its record unconditionally (rows of
+// absent requests are padding and never read), which keeps divergent
+// branches out of the kernel's streaming loop.
+inline int record_rows(int seg_rows, int R) { return seg_rows == kSegSmall ? kSmallMaxR : R; }
+
+#if defined(__HIPCC__)
+#define DSPARK_HD __host__ __device__
+#else
+#define DSPARK_HD
+#endif
+
+// Balanced partition of n items into n_ranges contiguous ranges (the first
+// n % n_ranges ranges one item longer): first item of range g.
+DSPARK_HD inline int range_start(int g, int n, int n_ranges) {
+  const int q = n / n_ranges, r = n % n_ranges;
+  return g * q + (g < r ? g : r);
+}
 // Target-row elements per workgroup of the verify statistics kernel.
 constexpr int kChunk = 4096;
 constexpr int kChunkFloats = 4;              // floats per (row, chunk) record
@@ -30,7 +48,7 @@ inline int seg_rows_for(int32_t R, int32_t wdtype) {
 struct DraftPlan {
   int seg_rows = 0;
   int n_seg = 0;
-  std::size_t part_off = 0;   // [R][n_seg][kRecFloats] float
+  std::size_t part_off = 0;  // [record_rows][n_seg][kRecFloats] float
   std::size_t total = 0;
 };
 
@@ -41,7 +59,7 @@ struct VerifyPlan {
   std::size_t vpart_off = 0;    // [n_rows][n_chunks][kChunkFloats] float
   std::size_t rsinfo_off = 0;   // [R][4] int32: flag, prev, U row, target row
   std::size_t rsstats_off = 0;  // [R][4] float: Mq, 1/Zq, Mp, 1/Zp
-  std::size_t rpart_off = 0;    // [R][n_seg][kRecFloats] float
+  std::size_t rpart_off = 0;    // [record_rows][n_seg][kRecFloats] float
   std::size_t total = 0;
 };
 

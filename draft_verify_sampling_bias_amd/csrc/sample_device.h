@@ -4,8 +4,8 @@
 // An inverse-CDF draw walks the vocabulary in index order and returns the
 // first entry whose inclusive cumulative mass exceeds u * Z.  The vocabulary
 // is covered by segments whose masses were reduced by an earlier kernel, so
-// the walk is done in two levels: a block-wide prefix over segment masses
-// picks the segment, and only that segment's 16 or 32 entries are recomputed
+// the walk is done in levels: block-wide prefixes over segment masses pick
+// the segment, and only that segment's 16 or 32 entries are recomputed
 // and scanned (a target row, which is an input, is rescanned in chunks of
 // 4096 entries instead).  Intervals of
 // consecutive threads meet exactly (block256_scan), so exactly one thread owns
@@ -48,6 +48,7 @@ __device__ Located locate_segments(int n, Mass mass, float u, LocScratch* sh) {
   const int t0 = min(tid * seg, n), t1 = min(t0 + seg, n);
   float ts = 0.0f;
   int lastpos = -1;
+#pragma unroll 4
   for (int t = t0; t < t1; ++t) {
     const float x = mass(t);
     ts += x;
@@ -101,6 +102,112 @@ __device__ Located locate_segments(int n, Mass mass, float u, LocScratch* sh) {
   }
   __syncthreads();
   return L;
+}
+
+// Two-level location over n segment masses mass(t) >= 0: thread i sums the
+// contiguous block i of a balanced 256-way partition, a block-wide scan
+// picks the block whose interval holds u * Z, and wavefront 0 scans that
+// block's masses 64 at a time to pick the segment.  Returns the segment and
+// the threshold left inside it (same units as the masses), or fallback =
+// true (threshold INFINITY: take the segment's last positive entry) when
+// rounding between the levels leaves the threshold past the block's last
+// positive segment, or when no block's interval holds it.  seg = -1 when
+// every mass is zero.  All threads get the result.
+struct Located2 {
+  int seg;
+  float rem;
+  float Z;
+  bool fallback;
+};
+
+struct Loc2Scratch {
+  float scan[4];
+  float fred[4];
+  int ired[4];
+  float P;
+  int sel;
+  float rem;
+  int fb;
+};
+
+template <class Mass>
+__device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
+  const int tid = threadIdx.x;
+  const int t0 = range_start(tid, n, 256), t1 = range_start(tid + 1, n, 256);
+  float ts = 0.0f;
+  int lastpos = -1;
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) {
+    const float x = mass(t);
+    ts += x;
+    lastpos = (x > 0.0f) ? t : lastpos;
+  }
+  float excl, Z;
+  const float incl = block256_scan(ts, sh->scan, &excl, &Z);
+  const float theta = u * Z;
+  const int first = block256_min_int((incl > theta) ? tid : 256, sh->ired);
+  const int glast = block256_max_int(lastpos, sh->ired);
+  if (tid == first) sh->P = excl;
+  __syncthreads();
+  int s0, s1;
+  float th;
+  bool fb;
+  if (first < 256) {
+    s0 = range_start(first, n, 256);
+    s1 = range_start(first + 1, n, 256);
+    th = theta - sh->P;
+    fb = false;
+  } else {
+    s0 = max(glast, 0);
+    s1 = glast + 1;
+    th = INFINITY;
+    fb = true;
+  }
+  if (tid < 64) {
+    const int lane = tid;
+    int sel = -1, lpos = -1;
+    float selP = 0.0f, lastP = 0.0f, base = 0.0f;
+    for (int c0 = s0; c0 < s1; c0 += 64) {
+      const int sidx = c0 + lane;
+      const float x = (sidx < s1) ? mass(sidx) : 0.0f;
+      const float cum = wave_incl_scan(x);
+      const float up = __shfl_up(cum, 1);
+      const float ex = (lane == 0) ? 0.0f : up;
+      const unsigned long long hit = __ballot(x > 0.0f && base + cum > th);
+      const unsigned long long pos = __ballot(x > 0.0f);
+      if (pos) {
+        const int lp = 63 - __clzll(static_cast<long long>(pos));
+        lpos = c0 + lp;
+        lastP = base + __shfl(ex, lp);
+      }
+      if (hit) {
+        const int fl = __ffsll(static_cast<long long>(hit)) - 1;
+        sel = c0 + fl;
+        selP = base + __shfl(ex, fl);
+        break;
+      }
+      base += __shfl(cum, 63);
+    }
+    bool f = fb;
+    if (sel < 0) {
+      sel = lpos;
+      selP = lastP;
+      f = true;
+    }
+    if (lane == 0) {
+      sh->sel = sel;
+      sh->rem = f ? INFINITY : th - selP;
+      sh->fb = f ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  Located2 out;
+  out.seg = sh->sel;
+  out.rem = sh->rem;
+  out.fallback = sh->fb != 0;
+  out.Z = Z;
+  __syncthreads();
+  return out;
 }
 
 // Wave 0: first of 32 weights whose inclusive prefix exceeds theta, else the

@@ -52,16 +52,20 @@ def test_schedule_rows():
 
 def test_workspace_sizes_match_struct_layout():
     # a struct_size mismatch would return DSPARK_ERR_ABI
-    # one (max, sum) record of two floats per (request, 16-row segment)
     def up(x):
         return (x + 255) // 256 * 256
 
+    # one (max, sum) record of two floats per (request row, 16-row segment);
+    # the 16-row path (bf16 weights, R <= 64) always holds 64 request rows
     assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1) == up(64 * 9496 * 8)
-    # 32-row segments above 64 requests and for fp32 weights
+    assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1) == up(64 * 63 * 8)
+    # 32-row segments, one row per request, above 64 requests and for fp32 weights
     assert ds.draft_workspace_bytes(65, 7, 151936, 512, 1) == up(65 * 4748 * 8)
     assert ds.draft_workspace_bytes(8, 7, 1024, 32, 0) == up(8 * 32 * 8)
+    # verify: chunk records (16 bytes per 4096-entry chunk of each target row),
+    # residual info/stats, then the residual segment records
     nb = ds.verify_workspace_bytes(64, 7, 151936, 512, 1, 512)
-    assert nb >= 512 * 38 * 16 + 64 * 9496 * 8
+    assert nb == up(512 * 38 * 16) + up(64 * 16) + up(64 * 16) + up(64 * 9496 * 8)
 
 
 def _draft_args(**kw):
