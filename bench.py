@@ -29,7 +29,6 @@ oracle on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -42,8 +41,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft+verify positions/sec (R×gamma) and achieved HBM GB/s at V=151936"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bias_tile_config3.json")
-KERNEL_SRC = os.path.join(ROOT, "draft_verify_sampling_bias_amd", "csrc", "bias_tile.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bias_seg16_config3_traffic.txt")
 
 
 def algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows):
@@ -54,19 +52,49 @@ def algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows):
     return step, per_pos_tile
 
 
-def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def load_traffic(per_launch_alg):
+def load_traffic():
+    """HBM bytes per launch of the fused bias kernel from the committed
+    counter summary, or None when it is missing or its kernel sources have
+    changed since the counters were taken."""
+    from draft_verify_sampling_bias_amd import profsum
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(TRAFFIC_FILE) as f:
-        t = json.load(f)
-    if t.get("kernel_sha256_16") != kernel_hash():
+    t = profsum.read_traffic(TRAFFIC_FILE)
+    if t.get("kernel_source_sha256_16") != profsum.tile_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return int(t["bytes_per_launch"])
+
+
+class HipTimingEvents:
+    """Raw HIP timing events created with hipEventDisableSystemFence: no
+    system-scope cache write-back / invalidate when they complete, so an
+    event pair attached to a kernel dispatch times the kernel alone."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        self._c = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self.handles = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            rc = self._hip.hipEventCreateWithFlags(ctypes.byref(ev), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.handles.append(ev.value)
+
+    def elapsed_ms(self, i, j):
+        ms = self._c.c_float()
+        rc = self._hip.hipEventElapsedTime(self._c.byref(ms), self._c.c_void_p(self.handles[i]),
+                                          self._c.c_void_p(self.handles[j]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(self._c.c_void_p(h))
+        self.handles = []
 
 
 def cpu_baseline(inp, n_sample, seed=0):
@@ -195,11 +223,7 @@ def main():
     K = args.steps
     positions = R * gamma * K
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * gamma)] for _ in range(K)]
-    for lst in kev:
-        for e in lst:
-            e.record(stream)  # creates the underlying hipEvent
-    torch.cuda.synchronize()
+    kev = HipTimingEvents(2 * gamma * K)
 
     # (1) the measured steps: cold caches, no events inside the step
     t0 = time.perf_counter()
@@ -214,14 +238,15 @@ def main():
     tot_ms = float(np.sum(step_ms))
     value = positions / (tot_ms / 1e3)
 
-    # (2) the dominant kernel alone: events recorded by the library around
-    # each fused bias launch (a separate pass: an event between launches
-    # adds a gap of several microseconds to the step)
+    # (2) the dominant kernel alone: the library attaches a start / stop event
+    # pair to each fused bias dispatch (hipExtLaunchKernel), so each interval
+    # is that kernel's execution time; same cache state as pass (1)
     for i in range(K):
         evict()
-        step(kev[i])
+        step(kev.handles[2 * gamma * i: 2 * gamma * (i + 1)])
     torch.cuda.synchronize()
-    tile_ms = [kev[i][2 * k].elapsed_time(kev[i][2 * k + 1]) for i in range(K) for k in range(gamma)]
+    tile_ms = [kev.elapsed_ms(2 * gamma * i + 2 * k, 2 * gamma * i + 2 * k + 1) for i in range(K) for k in range(gamma)]
+    kev.close()
 
     # (3) context: back-to-back steps with warm caches
     warm = None
@@ -277,7 +302,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(tile_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(bytes_tile),
+            "traffic": load_traffic(),
             "avg_launch_us": round(tile_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": int(bytes_tile),
         },

@@ -199,8 +199,10 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
     U [R, gamma, V] fp32; W1, W2 [V, rank] bf16 or fp32; anchor [R] int32;
     temp [R] fp32; u_draft [R, gamma] fp32.  Returns (y int32 [R, gamma],
     q_tok fp32 [R, gamma], q_stats fp32 [R, gamma, 2]).  ``out`` may supply
-    those three tensors; ``prof_events`` a list of 2*gamma torch.cuda.Event
-    (already recorded once) timed around each position's fused bias kernel."""
+    those three tensors; ``prof_events`` a list of 2*gamma timing events
+    (torch.cuda.Event already recorded once, or raw hipEvent_t handles)
+    attached to each position's fused bias kernel dispatch (start / stop of
+    that kernel alone)."""
     torch = _torch()
     dev = U.device
     R, gamma, V = U.shape
@@ -227,7 +229,9 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
     if prof_events is not None:
         if len(prof_events) != 2 * gamma:
             raise ValueError(f"prof_events needs {2 * gamma} events")
-        ev_arr = (ctypes.c_void_p * len(prof_events))(*[e.cuda_event for e in prof_events])
+        # torch.cuda.Event objects or raw hipEvent_t handles (int)
+        ev_arr = (ctypes.c_void_p * len(prof_events))(
+            *[e if isinstance(e, int) else e.cuda_event for e in prof_events])
     a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd,
                   U=_ptr(U), W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp),
                   u_draft=_ptr(u_draft), y=_ptr(y), q_tok=_ptr(q_tok), q_stats=_ptr(q_stats),

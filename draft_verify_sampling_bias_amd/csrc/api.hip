@@ -101,15 +101,10 @@ int dspark_draft_block(const dspark_draft_args* a) {
     tp.prev_base = (k == 0) ? a->anchor : a->y + (k - 1);
     tp.prev_stride = (k == 0) ? 1 : a->gamma;
     tp.U_base = a->U + static_cast<int64_t>(k) * a->V;
-    if (a->prof_events) {
-      if (hipEventRecord(static_cast<hipEvent_t>(a->prof_events[2 * k]), s) != hipSuccess) return DSPARK_ERR_HIP;
-    }
-    st = hip_status(launch_bias_tile(tp, a->wdtype, false, cu, s));
+    hipEvent_t e0 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k]) : nullptr;
+    hipEvent_t e1 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k + 1]) : nullptr;
+    st = hip_status(launch_bias_tile(tp, a->wdtype, false, cu, s, e0, e1));
     if (st != DSPARK_OK) return st;
-    if (a->prof_events) {
-      if (hipEventRecord(static_cast<hipEvent_t>(a->prof_events[2 * k + 1]), s) != hipSuccess)
-        return DSPARK_ERR_HIP;
-    }
     fp.prev_base = tp.prev_base;
     fp.prev_stride = tp.prev_stride;
     fp.U_base = tp.U_base;

@@ -31,6 +31,8 @@
 // (l & 31), 8 k at 8 * (l >> 5); accumulator i is row 8*(i/4) + 4*(l>>5) +
 // (i%4), column (l & 31).  Rows are vocabulary entries, columns requests.
 
+#include <hip/hip_ext.h>
+
 #include "dspark_device.h"
 #include "launchers.h"
 #include "plan.h"
@@ -47,11 +49,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ void amax_sel(float& m, int& i, float m2, int i2) {
-  const bool take = (m2 > m) | ((m2 == m) & (i2 < i));
-  m = take ? m2 : m;
-  i = take ? i2 : i;
-}
 
 // Per-request values staged in LDS.
 struct ReqInfo {
@@ -224,14 +221,12 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
         m = gt ? s[i] : m;
         im = gt ? vb + i : im;
       }
-      amax_sel(m, im, __shfl_xor(m, 16), __shfl_xor(im, 16));
-      amax_sel(m, im, __shfl_xor(m, 32), __shfl_xor(im, 32));
+      quad_amax(m, im);
       // exp2(-inf) = 0 for rows past V; a greedy request (c = 0) keeps im
       float e = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) e += exp2_hw((s[i] - m) * c);
-      e += __shfl_xor(e, 16);
-      e += __shfl_xor(e, 32);
+      for (int i = 0; i < 4; ++i) e += exp2_rel(s[i], m, c);
+      e = quad_sum(e);
       x = m;
       y = (c > 0.f) ? e : __int_as_float(im);
     } else {
@@ -244,8 +239,7 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
         const float d = fmaxf(pp - qq, 0.f);
         w += __int_as_float(__float_as_int(d) & -static_cast<int>(vb + i < V));
       }
-      w += __shfl_xor(w, 16);
-      w += __shfl_xor(w, 32);
+      w = quad_sum(w);
       x = 0.f;
       y = w;
     }
@@ -353,14 +347,12 @@ __device__ __forceinline__ void seg32_epilogue(const TileParams& p, const ReqInf
       m = gt ? s[i] : m;
       im = gt ? v : im;
     }
-    amax_sel(m, im, __shfl_xor(m, 32), __shfl_xor(im, 32));
+    half_amax(m, im);
+    // computed for greedy requests too (c = 0 gives 1s), then discarded
     float e = 0.f;
-    if (ci.c > 0.f) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) e += exp2_hw((s[i] - m) * ci.c);
-    }
-    const float eo = __shfl_xor(e, 32);
-    e = khalf ? (eo + e) : (e + eo);
+    for (int i = 0; i < 16; ++i) e += exp2_rel(s[i], m, ci.c);
+    e = half_sum(e);
     rx = m;
     ry = (ci.c > 0.f) ? e : __int_as_float(im);
   } else {
@@ -372,10 +364,11 @@ __device__ __forceinline__ void seg32_epilogue(const TileParams& p, const ReqInf
       const int v = vw + acc32_row(i, khalf);
       const float q = exp2_hw((acc[i] + x[i] - ci.Mq) * ci.c) * ci.iZq;
       const float pp = exp2_hw((t[i] - ci.Mp) * ci.c) * ci.iZp;
-      w += (okn && v < V) ? fmaxf(pp - q, 0.f) : 0.f;
+      // masked rows add +0 (a bit mask, not a branch around the exps)
+      const float d = fmaxf(pp - q, 0.f);
+      w += __int_as_float(__float_as_int(d) & -static_cast<int>(okn && v < V));
     }
-    const float wo = __shfl_xor(w, 32);
-    w = khalf ? (wo + w) : (w + wo);
+    w = half_sum(w);
     rx = 0.f;
     ry = w;
   }
@@ -512,10 +505,19 @@ __global__ void __launch_bounds__(256) bias_seg32_f32(TileParams p) {
   }
 }
 
+// One launch, with the optional timing events attached to the dispatch.
+template <typename K>
+void launch(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const TileParams& p) {
+  if (ev0 != nullptr || ev1 != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev0, ev1, 0, p);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, p);
+}
+
 template <bool RESID, bool VEC4>
-hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t s) {
+hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (wdtype == DSPARK_W_F32) {
-    hipLaunchKernelGGL((bias_seg32_f32<RESID, VEC4>), dim3((p.n_seg + 3) / 4), dim3(256), 0, s, p);
+    launch(bias_seg32_f32<RESID, VEC4>, dim3((p.n_seg + 3) / 4), dim3(256), s, e0, e1, p);
     return hipGetLastError();
   }
   if (p.seg_rows == kSegSmall) {
@@ -523,37 +525,41 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     const int blocks = max(1, min((p.n_seg + kSeg16Waves - 1) / kSeg16Waves, num_cu));
     const dim3 grid(blocks), block(kSeg16Waves * 64);
     if (p.rank <= 64)
-      hipLaunchKernelGGL((bias_seg16<2, RESID, VEC4>), grid, block, 0, s, p);
+      launch(bias_seg16<2, RESID, VEC4>, grid, block, s, e0, e1, p);
     else if (p.rank <= 128)
-      hipLaunchKernelGGL((bias_seg16<4, RESID, VEC4>), grid, block, 0, s, p);
+      launch(bias_seg16<4, RESID, VEC4>, grid, block, s, e0, e1, p);
     else if (p.rank <= 256)
-      hipLaunchKernelGGL((bias_seg16<8, RESID, VEC4>), grid, block, 0, s, p);
+      launch(bias_seg16<8, RESID, VEC4>, grid, block, s, e0, e1, p);
     else
-      hipLaunchKernelGGL((bias_seg16<16, RESID, VEC4>), grid, block, 0, s, p);
+      launch(bias_seg16<16, RESID, VEC4>, grid, block, s, e0, e1, p);
     return hipGetLastError();
   }
   const dim3 grid((p.n_seg + 3) / 4), block(256);
   if (p.rank <= 64)
-    hipLaunchKernelGGL((bias_seg32<4, RESID, VEC4>), grid, block, 0, s, p);
+    launch(bias_seg32<4, RESID, VEC4>, grid, block, s, e0, e1, p);
   else if (p.rank <= 128)
-    hipLaunchKernelGGL((bias_seg32<8, RESID, VEC4>), grid, block, 0, s, p);
+    launch(bias_seg32<8, RESID, VEC4>, grid, block, s, e0, e1, p);
   else if (p.rank <= 256)
-    hipLaunchKernelGGL((bias_seg32<16, RESID, VEC4>), grid, block, 0, s, p);
+    launch(bias_seg32<16, RESID, VEC4>, grid, block, s, e0, e1, p);
   else
-    hipLaunchKernelGGL((bias_seg32<32, RESID, VEC4>), grid, block, 0, s, p);
+    launch(bias_seg32<32, RESID, VEC4>, grid, block, s, e0, e1, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s) {
+hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s,
+                            hipEvent_t ev0, hipEvent_t ev1) {
   if (p.R == 0 || p.n_seg == 0) return hipSuccess;
   if (residual && (p.u_rows < 1 || p.t_rows < 1)) return hipErrorInvalidValue;
   // the 16-row path holds at most kSmallMaxR requests (LDS tile, record rows)
   if (p.seg_rows == kSegSmall && (p.R > kSmallMaxR || wdtype != DSPARK_W_BF16)) return hipErrorInvalidValue;
   const bool vec4 = (p.V % 4) == 0;
-  if (residual) return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s) : launch_mode<true, false>(p, wdtype, num_cu, s);
-  return vec4 ? launch_mode<false, true>(p, wdtype, num_cu, s) : launch_mode<false, false>(p, wdtype, num_cu, s);
+  if (residual)
+    return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s, ev0, ev1)
+                : launch_mode<true, false>(p, wdtype, num_cu, s, ev0, ev1);
+  return vec4 ? launch_mode<false, true>(p, wdtype, num_cu, s, ev0, ev1)
+              : launch_mode<false, false>(p, wdtype, num_cu, s, ev0, ev1);
 }
 
 }  // namespace dspark

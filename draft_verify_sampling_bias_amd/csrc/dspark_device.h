@@ -22,6 +22,70 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 // 2^x on the hardware transcendental unit (v_exp_f32, 1 ulp).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// (m2, i2) beats (m, i): larger value, or equal value and lower index
+// (evaluated without short-circuit branches)
+__device__ __forceinline__ bool amax_takes(float m2, int i2, float m, int i) {
+  return (static_cast<int>(m2 > m) | (static_cast<int>(m2 == m) & static_cast<int>(i2 < i))) != 0;
+}
+
+// Lane pairs (l, l ^ 16) and (l, l ^ 32) via the gfx950 permlane swaps (VALU,
+// no LDS round trip): both lanes of a pair receive (x[lower lane], x[upper
+// lane]) in that order, so a combine of the two is bit-identical in both.
+__device__ __forceinline__ void lane_pair16(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+__device__ __forceinline__ void lane_pair32(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  lo = r[0];
+  hi = r[1];
+}
+// sum / (max, lowest index) over the lane pair l, l ^ 32
+__device__ __forceinline__ float half_sum(float x) {
+  uint32_t lo, hi;
+  lane_pair32(__float_as_uint(x), lo, hi);
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+__device__ __forceinline__ void half_amax(float& m, int& i) {
+  uint32_t ml, mh, il, ih;
+  lane_pair32(__float_as_uint(m), ml, mh);
+  lane_pair32(static_cast<uint32_t>(i), il, ih);
+  const bool take =
+      amax_takes(__uint_as_float(mh), static_cast<int>(ih), __uint_as_float(ml), static_cast<int>(il));
+  m = __uint_as_float(take ? mh : ml);
+  i = static_cast<int>(take ? ih : il);
+}
+// sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float quad_sum(float x) {
+  uint32_t lo, hi;
+  lane_pair16(__float_as_uint(x), lo, hi);
+  x = __uint_as_float(lo) + __uint_as_float(hi);
+  lane_pair32(__float_as_uint(x), lo, hi);
+  return __uint_as_float(lo) + __uint_as_float(hi);
+}
+// (max, lowest index of the max) over the same four lanes
+__device__ __forceinline__ void quad_amax(float& m, int& i) {
+  uint32_t ml, mh, il, ih;
+  lane_pair16(__float_as_uint(m), ml, mh);
+  lane_pair16(static_cast<uint32_t>(i), il, ih);
+  bool take = amax_takes(__uint_as_float(mh), static_cast<int>(ih), __uint_as_float(ml), static_cast<int>(il));
+  m = __uint_as_float(take ? mh : ml);
+  i = static_cast<int>(take ? ih : il);
+  lane_pair32(__float_as_uint(m), ml, mh);
+  lane_pair32(static_cast<uint32_t>(i), il, ih);
+  take = amax_takes(__uint_as_float(mh), static_cast<int>(ih), __uint_as_float(ml), static_cast<int>(il));
+  m = __uint_as_float(take ? mh : ml);
+  i = static_cast<int>(take ? ih : il);
+}
+
+// 2^((x - m) c) for x <= m, with x == m giving 1 also when both are -inf (a
+// vocabulary masked with -inf logits): the weight of a masked entry relative
+// to a masked maximum stays finite, and relative to any finite maximum it is 0.
+__device__ __forceinline__ float exp2_rel(float x, float m, float c) {
+  return (x == m) ? 1.0f : __builtin_amdgcn_exp2f((x - m) * c);
+}
+
 // Scale that turns (logit - max) into a base-2 exponent at temperature T;
 // 0 marks a greedy request (T <= 0 or NaN).
 __device__ __forceinline__ float temp_scale(float T) { return (T > 0.0f) ? (kLog2e / T) : 0.0f; }

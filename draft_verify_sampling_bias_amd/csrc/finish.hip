@@ -23,36 +23,70 @@ namespace {
 // Rescan of one segment: thread group i (2^lpr_log2 lanes) owns row v0 + i.
 __device__ __forceinline__ int lanes_log2(int seg_rows) { return seg_rows == kSegSmall ? 4 : 3; }
 
-template <typename WT>
+// Segment records of one request staged in LDS (128 KiB: 16384 records, i.e.
+// V up to 262144 with 16-row or 524288 with 32-row segments); larger
+// vocabularies read the records from global memory instead.
+constexpr int kStageRecs = 16384;
+constexpr int kStageBatch = 40;  // loads in flight per thread while staging
+
+// Copies n records into LDS with every load of a batch issued before any is
+// used (one memory latency per 10240 records), folding each loaded record
+// into f(r) on the way.  No barrier.
+template <class F>
+__device__ __forceinline__ void stage_records(const float2* __restrict__ src, int n, float2* dst, F f) {
+  const int tid = threadIdx.x;
+  for (int base = 0; base < n; base += 256 * kStageBatch) {
+    float2 r[kStageBatch];
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int t = base + j * 256 + tid;
+      r[j] = src[min(t, n - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int t = base + j * 256 + tid;
+      if (t < n) {
+        dst[t] = r[j];
+        f(r[j]);
+      }
+    }
+  }
+}
+
+template <typename WT, bool STAGED>
 __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh;
   __shared__ float e32[32], s32[32];
+  __shared__ float2 srec[STAGED ? kStageRecs : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int V = p.V, n_seg = p.n_seg;
   const float c = temp_scale(p.temp[n]);
-  const float2* fine = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
+  const float2* gfine = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
+  const float2* fine = STAGED ? srec : gfine;
   const int64_t o = static_cast<int64_t>(n) * p.gamma + p.k;
   if (c > 0.0f) {
     const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
     load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
   }
+  // maximum (greedy: with the lowest argmax carried in the records' second
+  // word) over all records; order-independent, so taken while staging
   float m = -INFINITY;
   int im = kIntMax;
-  // coalesced pass over the segment records: maximum (and, greedy, the
-  // lowest argmax carried in the records' second word)
-  if (c == 0.0f) {
-#pragma unroll 8
-    for (int t = tid; t < n_seg; t += 256) {
-      const float2 r = fine[t];
+  auto fold = [&](float2 r) {
+    if (c == 0.0f)
       amax_merge(m, im, r.x, __float_as_int(r.y));
-    }
+    else
+      m = fmaxf(m, r.x);
+  };
+  if (STAGED) {
+    stage_records(gfine, n_seg, srec, fold);
   } else {
 #pragma unroll 8
-    for (int t = tid; t < n_seg; t += 256) m = fmaxf(m, fine[t].x);
-    im = 0;
+    for (int t = tid; t < n_seg; t += 256) fold(gfine[t]);
   }
-  block256_amax(m, im, sh.fred, sh.ired);
+  if (c != 0.0f) im = 0;
+  block256_amax(m, im, sh.fred, sh.ired);  // also orders the LDS stores before the reads below
   const float M = m;
   if (c == 0.0f) {
     if (tid == 0) {
@@ -64,6 +98,7 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
     return;
   }
   const float u = clamp_uniform(p.u_draft[o]);
+  // mass of segment t in units of 2^((. - M) c)
   auto mass = [&](int t) {
     const float2 r = fine[t];
     return r.y * exp2_hw((r.x - M) * c);
@@ -101,13 +136,14 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   }
 }
 
-template <typename WT>
+template <typename WT, bool STAGED>
 __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh2;
   __shared__ ChunkScratch sh;
   __shared__ float e32[32];
   __shared__ int s_out;
+  __shared__ float2 srec[STAGED ? kStageRecs : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int32_t* info = p.rs_info + 4 * static_cast<int64_t>(n);
   if (info[0] == 0) return;
@@ -120,7 +156,12 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   const float c = temp_scale(p.temp[n]);
   const float u = clamp_uniform(p.u_final[n]);
   load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
-  const float2* fine = reinterpret_cast<const float2*>(p.rpart) + static_cast<int64_t>(n) * p.n_seg;
+  const float2* gfine = reinterpret_cast<const float2*>(p.rpart) + static_cast<int64_t>(n) * p.n_seg;
+  const float2* fine = STAGED ? srec : gfine;
+  if (STAGED) {
+    stage_records(gfine, p.n_seg, srec, [](float2) {});
+    __syncthreads();
+  }
   auto mass = [&](int t) { return fine[t].y; };
   const Located2 L = locate_blocked(p.n_seg, mass, u, &sh2);
   const float* tr = p.target + trow * V;
@@ -162,19 +203,37 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
 
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  if (wdtype == DSPARK_W_BF16)
-    hipLaunchKernelGGL(draft_finish_kernel<uint16_t>, dim3(p.R), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(draft_finish_kernel<float>, dim3(p.R), dim3(256), 0, s, p);
+  const bool staged = p.n_seg <= kStageRecs;
+  const dim3 grid(p.R), block(256);
+  if (wdtype == DSPARK_W_BF16) {
+    if (staged)
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, false>), grid, block, 0, s, p);
+  } else {
+    if (staged)
+      hipLaunchKernelGGL((draft_finish_kernel<float, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((draft_finish_kernel<float, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  if (wdtype == DSPARK_W_BF16)
-    hipLaunchKernelGGL(residual_finish_kernel<uint16_t>, dim3(p.R), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(residual_finish_kernel<float>, dim3(p.R), dim3(256), 0, s, p);
+  const bool staged = p.n_seg <= kStageRecs;
+  const dim3 grid(p.R), block(256);
+  if (wdtype == DSPARK_W_BF16) {
+    if (staged)
+      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, false>), grid, block, 0, s, p);
+  } else {
+    if (staged)
+      hipLaunchKernelGGL((residual_finish_kernel<float, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((residual_finish_kernel<float, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -76,7 +76,10 @@ struct VerifyParams {
   float* rpart;      // [record_rows][n_seg][kRecFloats] residual segment records
 };
 
-hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s);
+// ev0 / ev1 (optional): events attached to the kernel's dispatch, recorded
+// when it starts and when it ends.
+hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s,
+                            hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s);
 hipError_t launch_verify_stats(const VerifyParams& p, hipStream_t s);
 hipError_t launch_verify_finish(const VerifyParams& p, hipStream_t s);

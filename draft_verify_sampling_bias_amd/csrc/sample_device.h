@@ -130,18 +130,14 @@ struct Loc2Scratch {
   int fb;
 };
 
+// First segment of thread block i of the 256-way partition.
+__device__ __forceinline__ int block_begin(int i, int n) { return range_start(i, n, 256); }
+
+// Second half of the location: ts is this thread's block sum (already in
+// the units of mass()), lastpos its last segment with positive mass (or -1).
 template <class Mass>
-__device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
+__device__ Located2 locate_from_block_sums(int n, float ts, int lastpos, Mass mass, float u, Loc2Scratch* sh) {
   const int tid = threadIdx.x;
-  const int t0 = range_start(tid, n, 256), t1 = range_start(tid + 1, n, 256);
-  float ts = 0.0f;
-  int lastpos = -1;
-#pragma unroll 8
-  for (int t = t0; t < t1; ++t) {
-    const float x = mass(t);
-    ts += x;
-    lastpos = (x > 0.0f) ? t : lastpos;
-  }
   float excl, Z;
   const float incl = block256_scan(ts, sh->scan, &excl, &Z);
   const float theta = u * Z;
@@ -153,8 +149,8 @@ __device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
   float th;
   bool fb;
   if (first < 256) {
-    s0 = range_start(first, n, 256);
-    s1 = range_start(first + 1, n, 256);
+    s0 = block_begin(first, n);
+    s1 = block_begin(first + 1, n);
     th = theta - sh->P;
     fb = false;
   } else {
@@ -208,6 +204,21 @@ __device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
   out.Z = Z;
   __syncthreads();
   return out;
+}
+
+template <class Mass>
+__device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
+  const int tid = threadIdx.x;
+  const int t0 = block_begin(tid, n), t1 = block_begin(tid + 1, n);
+  float ts = 0.0f;
+  int lastpos = -1;
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) {
+    const float x = mass(t);
+    ts += x;
+    lastpos = (x > 0.0f) ? t : lastpos;
+  }
+  return locate_from_block_sums(n, ts, lastpos, mass, u, sh);
 }
 
 // Wave 0: first of 32 weights whose inclusive prefix exceeds theta, else the

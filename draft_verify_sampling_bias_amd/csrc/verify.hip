@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(256) verify_stats_kernel(VerifyParams p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = base + (it * 256 + tid) * 4 + e;
-        if (v < V) e_loc += exp2_hw((x[4 * it + e] - m) * c);
+        if (v < V) e_loc += exp2_rel(x[4 * it + e], m, c);
       }
     e_loc = wave_sum(e_loc);
     if ((tid & 63) == 0) fred[tid >> 6] = e_loc;

@@ -1,0 +1,147 @@
+"""Summaries of rocprofv3 output for the kernels of libdspark.
+
+    python -m draft_verify_sampling_bias_amd.profsum stats KERNEL_STATS_CSV --command CMD > out.txt
+    python -m draft_verify_sampling_bias_amd.profsum traffic --kernel NAME \
+        --fetch CSV --write CSV --calib-fetch CSV --calib-write CSV --calib-bytes N \
+        --alg-bytes N --commands TEXT > out.txt
+
+`stats` condenses a `--kernel-trace --stats` kernel table (calls, total and
+average duration per kernel).  `traffic` turns two `--pmc FETCH_SIZE` /
+`--pmc WRITE_SIZE` runs (KiB per dispatch) into HBM bytes per launch of one
+kernel, each counter scaled by what it reads for a device copy of known size
+(the calibration runs), and records a SHA-256 over the fused bias kernel's
+source files so that a reader can tell when the figures are stale.  `read_traffic` parses
+such a file back.
+"""
+import argparse
+import csv
+import hashlib
+import os
+import sys
+from collections import defaultdict
+
+
+# files the fused bias kernel is compiled from (its figures go stale when any changes)
+TILE_SOURCES = ("bias_tile.hip", "dspark_device.h", "launchers.h", "plan.h")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def tile_source_hash():
+    return source_hash([os.path.join(CSRC, n) for n in TILE_SOURCES])
+
+
+def _short(name, width=100):
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def stats_text(csv_path, command):
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# rocprofv3 kernel statistics", f"# command: {command}",
+           f"# {'calls':>6} {'total_us':>10} {'avg_us':>9} {'min_us':>8} {'max_us':>8} {'pct':>6}  kernel"]
+    for r in rows:
+        out.append(f"  {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e3:10.1f} "
+                   f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:8.2f} "
+                   f"{float(r['MaxNs']) / 1e3:8.2f} {float(r['Percentage']):6.2f}  {_short(r['Name'])}")
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(csv_path, counter):
+    """{kernel name: [value per dispatch]} for one counter (KiB)."""
+    acc = defaultdict(lambda: defaultdict(float))
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in acc.items()}
+
+
+def _pick(table, pattern):
+    keys = [k for k in table if pattern in k]
+    if len(keys) != 1:
+        raise SystemExit(f"kernel pattern {pattern!r} matches {keys}")
+    return table[keys[0]]
+
+
+def _calib_factor(csv_path, counter, true_bytes):
+    """true bytes / counter bytes for the largest dispatch of the copy run."""
+    vals = [v for lst in _per_dispatch(csv_path, counter).values() for v in lst]
+    top = max(vals)
+    return true_bytes / (top * 1024.0), top
+
+
+def traffic_text(kernel, fetch_csv, write_csv, cfetch_csv, cwrite_csv, calib_bytes, alg_bytes, commands):
+    f = _pick(_per_dispatch(fetch_csv, "FETCH_SIZE"), kernel)
+    w = _pick(_per_dispatch(write_csv, "WRITE_SIZE"), kernel)
+    ff, ftop = _calib_factor(cfetch_csv, "FETCH_SIZE", calib_bytes)
+    wf, wtop = _calib_factor(cwrite_csv, "WRITE_SIZE", calib_bytes)
+    f_kib = sum(f) / len(f)
+    w_kib = sum(w) / len(w)
+    total = f_kib * 1024 * ff + w_kib * 1024 * wf
+    lines = [
+        "# HBM traffic per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch)",
+        *[f"# command: {c}" for c in commands],
+        f"kernel: {kernel}",
+        f"kernel_sources: {' '.join(TILE_SOURCES)}",
+        f"kernel_source_sha256_16: {tile_source_hash()}",
+        f"dispatches_fetch: {len(f)}",
+        f"dispatches_write: {len(w)}",
+        f"fetch_kib_per_dispatch: {f_kib:.1f}",
+        f"write_kib_per_dispatch: {w_kib:.1f}",
+        f"calib_copy_bytes: {calib_bytes}",
+        f"calib_fetch_kib: {ftop:.1f}",
+        f"calib_write_kib: {wtop:.1f}",
+        f"fetch_scale: {ff:.4f}",
+        f"write_scale: {wf:.4f}",
+        f"bytes_per_launch: {int(round(total))}",
+        f"algorithmic_bytes_per_launch: {alg_bytes}",
+        f"traffic_over_algorithmic: {total / alg_bytes:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(path):
+    """key: value pairs of a traffic summary (comments skipped)."""
+    out = {}
+    with open(path) as fh:
+        for ln in fh:
+            ln = ln.strip()
+            if not ln or ln.startswith("#") or ":" not in ln:
+                continue
+            k, v = ln.split(":", 1)
+            out[k.strip()] = v.strip()
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--kernel", required=True)
+    for k in ("fetch", "write", "calib-fetch", "calib-write"):
+        t.add_argument("--" + k, required=True)
+    t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--alg-bytes", type=int, required=True)
+    t.add_argument("--commands", action="append", default=[])
+    a = ap.parse_args(argv)
+    if a.mode == "stats":
+        sys.stdout.write(stats_text(a.csv, a.command))
+    else:
+        sys.stdout.write(traffic_text(a.kernel, a.fetch, a.write, a.calib_fetch, a.calib_write, a.calib_bytes,
+                                      a.alg_bytes, a.commands))
+
+
+if __name__ == "__main__":
+    main()

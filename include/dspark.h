@@ -116,9 +116,10 @@ typedef enum dspark_wdtype {
  *                                 256-byte aligned.
  *   stream   hipStream_t as void*.
  *   prof_events  optional (NULL normally): host array of 2*gamma hipEvent_t
- *                handles; event 2k / 2k+1 are recorded on `stream` just before
- *                / after the fused bias + softmax kernel of position k, for
- *                timing that kernel alone.
+ *                handles (created with timing enabled); events 2k / 2k+1 are
+ *                attached to the dispatch of the fused bias + softmax kernel
+ *                of position k (hipExtLaunchKernel start / stop events), so
+ *                their interval is that kernel's execution time alone.
  * -------------------------------------------------------------------------- */
 typedef struct dspark_draft_args {
   uint32_t struct_size;

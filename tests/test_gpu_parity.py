@@ -44,6 +44,8 @@ SMALL = [
     (17, 2, 1, 9000, 8, "bf16", "sampled", "fixed"),         # gamma = 1, minimum rank
     (18, 9, 16, 513, 128, "bf16", "temps", "uniformK"),      # maximum gamma
     (19, 4, 5, 5, 16, "bf16", "sampled", "fixed"),           # tiny vocabulary
+    (20, 3, 2, 300000, 64, "bf16", "mixed", "fixed"),        # > 16384 segment records: unstaged finish
+    (21, 2, 2, 600000, 8, "f32", "temps", "fixed"),          # same on the 32-row path, 147 chunks
 ]
 
 
@@ -83,6 +85,23 @@ def test_run_twice_bit_identical():
     g2 = gpu_step(d, inp.K, inp.gamma)
     for k in g1:
         np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
+
+
+@pytest.mark.parametrize("R", [20, 70], ids=["seg16", "seg32"])
+def test_masked_vocabulary(R):
+    """Logits of -inf (a vocabulary mask): whole 16/32-row segments and a
+    whole 4096-entry target chunk masked, plus scattered entries; the target
+    masks some entries the drafter allows, so p = 0 for some drafted tokens."""
+    inp = synth.make_custom(24 + R, R, 4, 9000, 64, policy="mixed", K_mode="uniformK", U_std=3.0, noise_std=1.0)
+    rng = np.random.default_rng(2024 + R)
+    mask = np.zeros(inp.V, bool)
+    mask[1000:1600] = True
+    mask[8192:] = True
+    mask |= rng.random(inp.V) < 0.2
+    inp.U[:, :, mask] = -np.inf
+    inp.target[:, :, mask | (rng.random(inp.V) < 0.1)] = -np.inf
+    g = _run(inp, label=f"masked-R{R}")
+    assert not np.isin(g["y"], np.flatnonzero(mask)).any()
 
 
 def _sample(R, n, seed):
