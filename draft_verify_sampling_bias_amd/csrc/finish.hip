@@ -20,8 +20,10 @@
 namespace dspark {
 namespace {
 
-// Rescan of one segment: thread group i (2^lpr_log2 lanes) owns row v0 + i.
+// Rescan of one record segment: thread group i (256 / seg_rows lanes) owns
+// row v0 + i (16-row segments: 16 lanes per row; 32-row: 8).
 __device__ __forceinline__ int lanes_log2(int seg_rows) { return seg_rows == kSegSmall ? 4 : 3; }
+constexpr int kMaxSegRows = 64;
 
 // Segment records of one request staged in LDS (128 KiB: 16384 records, i.e.
 // V up to 262144 with 16-row or 524288 with 32-row segments); larger
@@ -57,7 +59,7 @@ template <typename WT, bool STAGED>
 __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh;
-  __shared__ float e32[32], s32[32];
+  __shared__ float e64[kMaxSegRows], s64[kMaxSegRows];
   __shared__ float2 srec[STAGED ? kStageRecs : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int V = p.V, n_seg = p.n_seg;
@@ -118,16 +120,15 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
       s = p.U_base[static_cast<int64_t>(n) * p.U_stride + v] + b;
       e = exp2_hw((s - ms) * c);
     }
-    e32[i] = e;
-    s32[i] = s;
+    e64[i] = e;
+    s64[i] = s;
   }
-  if (tid >= p.seg_rows && tid < 32) e32[tid] = 0.0f;
   __syncthreads();
   if (tid < 64) {
-    const int pos = pick32(e32, th);
+    const int pos = pick64(e64, p.seg_rows, th);
     if (tid == 0) {
       const int yy = (pos >= 0) ? v0 + pos : min(v0, V - 1);
-      const float sy = (pos >= 0) ? s32[pos] : M;
+      const float sy = (pos >= 0) ? s64[pos] : M;
       p.y[o] = yy;
       p.q_tok[o] = exp2_hw((sy - M) * c) / L.Z;
       p.q_stats[2 * o] = M;
@@ -141,7 +142,7 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh2;
   __shared__ ChunkScratch sh;
-  __shared__ float e32[32];
+  __shared__ float e64[kMaxSegRows];
   __shared__ int s_out;
   __shared__ float2 srec[STAGED ? kStageRecs : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
@@ -181,12 +182,11 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
         const float pp = exp2_hw((tr[v] - Mp) * c) * iZp;
         w = fmaxf(pp - q, 0.0f);
       }
-      e32[i] = w;
+      e64[i] = w;
     }
-    if (tid >= p.seg_rows && tid < 32) e32[tid] = 0.0f;
     __syncthreads();
     if (tid < 64) {
-      const int pos = pick32(e32, th);
+      const int pos = pick64(e64, p.seg_rows, th);
       if (tid == 0) s_out = (pos >= 0) ? v0 + pos : -1;
     }
     __syncthreads();

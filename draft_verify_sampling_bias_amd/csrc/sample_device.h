@@ -221,59 +221,73 @@ __device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
   return locate_from_block_sums(n, ts, lastpos, mass, u, sh);
 }
 
-// Wave 0: first of 32 weights whose inclusive prefix exceeds theta, else the
-// last positive one, else -1.
-__device__ __forceinline__ int pick32(const float* e32, float theta) {
+// Wave 0: first of n <= 64 weights whose inclusive prefix exceeds theta,
+// else the last positive one, else -1.
+__device__ __forceinline__ int pick64(const float* e, int n, float theta) {
   const int lane = threadIdx.x & 63;
-  const float x = (lane < 32) ? e32[lane] : 0.0f;
+  const float x = (lane < n) ? e[lane] : 0.0f;
   const float cum = wave_incl_scan(x);
-  const unsigned long long hit = __ballot(lane < 32 && x > 0.0f && cum > theta);
+  const unsigned long long hit = __ballot(x > 0.0f && cum > theta);
   if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
-  const unsigned long long pos = __ballot(lane < 32 && x > 0.0f);
+  const unsigned long long pos = __ballot(x > 0.0f);
   return pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
 }
 
-// Eight consecutive weights of a row times h (fp32 accumulate, fixed order).
-__device__ __forceinline__ float dot8(const uint16_t* row, const float* h, int k) {
-  const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(row + k);
+// Eight consecutive weights of a row, loaded raw, and their product with h
+// (fp32 accumulate, fixed order).
+struct Raw8 {
+  u32x4_t a, b;  // bf16: 8 weights in a; fp32: 4 + 4
+};
+__device__ __forceinline__ Raw8 load8(const uint16_t* row, int k) {
+  return Raw8{*reinterpret_cast<const u32x4_t*>(row + k), u32x4_t{0u, 0u, 0u, 0u}};
+}
+__device__ __forceinline__ Raw8 load8(const float* row, int k) {
+  return Raw8{*reinterpret_cast<const u32x4_t*>(row + k), *reinterpret_cast<const u32x4_t*>(row + k + 4)};
+}
+__device__ __forceinline__ float dot8(const Raw8& r, const uint16_t*, const float* h, int k) {
   float acc = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    acc = fmaf(__uint_as_float(raw[q] << 16), h[k + 2 * q], acc);
-    acc = fmaf(__uint_as_float(raw[q] & 0xffff0000u), h[k + 2 * q + 1], acc);
+    acc = fmaf(__uint_as_float(r.a[q] << 16), h[k + 2 * q], acc);
+    acc = fmaf(__uint_as_float(r.a[q] & 0xffff0000u), h[k + 2 * q + 1], acc);
   }
   return acc;
 }
-
-__device__ __forceinline__ float dot8(const float* row, const float* h, int k) {
-  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(row + k);
-  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(row + k + 4);
+__device__ __forceinline__ float dot8(const Raw8& r, const float*, const float* h, int k) {
   float acc = 0.0f;
-  acc = fmaf(a[0], h[k + 0], acc);
-  acc = fmaf(a[1], h[k + 1], acc);
-  acc = fmaf(a[2], h[k + 2], acc);
-  acc = fmaf(a[3], h[k + 3], acc);
-  acc = fmaf(b[0], h[k + 4], acc);
-  acc = fmaf(b[1], h[k + 5], acc);
-  acc = fmaf(b[2], h[k + 6], acc);
-  acc = fmaf(b[3], h[k + 7], acc);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(r.a[q]), h[k + q], acc);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc = fmaf(__uint_as_float(r.b[q]), h[k + 4 + q], acc);
   return acc;
 }
 
 // Markov bias W2[v, :] . h for one vocabulary row per group of 2^lpr_log2
-// consecutive lanes (row index = threadIdx.x >> lpr_log2).  Every lane of the
-// group returns the same value.
+// consecutive lanes (row index = threadIdx.x >> lpr_log2, lpr_log2 >= 2).
+// Every lane of the group returns the same value.  A lane's weight loads are
+// all issued before any is used (at most DSPARK_MAX_RANK / 32 of them).
 template <typename WT>
 __device__ __forceinline__ float row_bias(const WT* W2, const float* hs, int rank, int v, int V, int lpr_log2) {
+  constexpr int kMaxChunks = DSPARK_MAX_RANK / 32;
   const int lpr = 1 << lpr_log2;
   const int part = threadIdx.x & (lpr - 1);
+  const WT* row = W2 + static_cast<int64_t>(min(v, V - 1)) * rank;
+  // chunk it exists for some lane of the group iff it * lpr * 8 < rank
+  // (wavefront-uniform: a scalar branch)
+  Raw8 r[kMaxChunks];
+#pragma unroll
+  for (int it = 0; it < kMaxChunks; ++it) {
+    const int k = (part + it * lpr) * 8;
+    if (it * lpr * 8 < rank) r[it] = load8(row, min(k, rank - 8));
+  }
   float acc = 0.0f;
-  if (v < V) {
-    const WT* row = W2 + static_cast<int64_t>(v) * rank;
-    for (int k = part * 8; k < rank; k += lpr * 8) acc += dot8(row, hs, k);
+#pragma unroll
+  for (int it = 0; it < kMaxChunks; ++it) {
+    const int k = (part + it * lpr) * 8;
+    if (it * lpr * 8 < rank && k < rank) acc += dot8(r[it], row, hs, k);
   }
   for (int d = 1; d < lpr; d <<= 1) acc += __shfl_xor(acc, d);
-  return acc;
+  return (v < V) ? acc : 0.0f;
 }
 
 template <typename WT>
