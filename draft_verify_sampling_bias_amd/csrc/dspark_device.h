@@ -92,10 +92,9 @@ __device__ __forceinline__ float temp_scale(float T) { return (T > 0.0f) ? (kLog
 
 // (m, i) <- better of (m, i) and (m2, i2): larger value, lower index on ties.
 __device__ __forceinline__ void amax_merge(float& m, int& i, float m2, int i2) {
-  if (m2 > m || (m2 == m && i2 < i)) {
-    m = m2;
-    i = i2;
-  }
+  const bool take = (static_cast<int>(m2 > m) | (static_cast<int>(m2 == m) & static_cast<int>(i2 < i))) != 0;
+  m = take ? m2 : m;
+  i = take ? i2 : i;
 }
 
 __device__ __forceinline__ void wave_amax(float& m, int& i) {

@@ -31,28 +31,66 @@ constexpr int kMaxSegRows = 64;
 constexpr int kStageRecs = 16384;
 constexpr int kStageBatch = 40;  // loads in flight per thread while staging
 
-// Copies n records into LDS with every load of a batch issued before any is
-// used (one memory latency per 10240 records), folding each loaded record
-// into f(r) on the way.  No barrier.
+// Records are copied into LDS in batches of 256 * kStageBatch, every load of
+// a batch issued before any is used (one memory latency per batch).
+struct StageBatch {
+  float2 r[kStageBatch];
+};
+
+__device__ __forceinline__ void stage_issue(const float2* __restrict__ src, int n, int base, StageBatch& b) {
+#pragma unroll
+  for (int j = 0; j < kStageBatch; ++j) b.r[j] = src[min(base + j * 256 + static_cast<int>(threadIdx.x), n - 1)];
+}
+
+// Stores a batch into LDS, folding each record into f(r).  No barrier.
 template <class F>
-__device__ __forceinline__ void stage_records(const float2* __restrict__ src, int n, float2* dst, F f) {
-  const int tid = threadIdx.x;
-  for (int base = 0; base < n; base += 256 * kStageBatch) {
-    float2 r[kStageBatch];
+__device__ __forceinline__ void stage_commit(int n, int base, const StageBatch& b, float2* dst, F f) {
 #pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int t = base + j * 256 + tid;
-      r[j] = src[min(t, n - 1)];
-    }
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int t = base + j * 256 + tid;
-      if (t < n) {
-        dst[t] = r[j];
-        f(r[j]);
-      }
+  for (int j = 0; j < kStageBatch; ++j) {
+    const int t = base + j * 256 + static_cast<int>(threadIdx.x);
+    if (t < n) {
+      dst[t] = b.r[j];
+      f(b.r[j]);
     }
   }
+}
+
+// h = W1[prev, :] as fp32, split so that its loads can be in flight with
+// the record loads: hold() issues them into registers, commit() stores to
+// LDS (no barrier).
+template <typename WT>
+struct HRow {
+  static constexpr int kPer = DSPARK_MAX_RANK / 256;
+  float v[kPer];
+  __device__ __forceinline__ void hold(const WT* W1, int prev, int rank) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = static_cast<int>(threadIdx.x) + j * 256;
+      v[j] = weight_at<WT>(W1, static_cast<int64_t>(prev) * rank + min(k, rank - 1));
+    }
+  }
+  __device__ __forceinline__ void commit(int rank, float* hs) const {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = static_cast<int>(threadIdx.x) + j * 256;
+      if (k < rank) hs[k] = v[j];
+    }
+  }
+};
+
+// Block-wide (max, lowest index) with one barrier; lm / li are used once.
+__device__ __forceinline__ void block_amax_once(float& m, int& i, float* lm, int* li) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  wave_amax(m, i);
+  if (lane == 0) {
+    lm[wave] = m;
+    li[wave] = i;
+  }
+  __syncthreads();
+  m = lm[0];
+  i = li[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) amax_merge(m, i, lm[w], li[w]);
 }
 
 template <typename WT, bool STAGED>
@@ -63,33 +101,37 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   __shared__ float2 srec[STAGED ? kStageRecs : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int V = p.V, n_seg = p.n_seg;
-  const float c = temp_scale(p.temp[n]);
   const float2* gfine = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
   const float2* fine = STAGED ? srec : gfine;
   const int64_t o = static_cast<int64_t>(n) * p.gamma + p.k;
-  if (c > 0.0f) {
-    const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
-    load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
-  }
+  // loads that depend on nothing go first; then the records, then W1[prev]
+  // (whose address waits only for prev), all in flight together
+  const float T = p.temp[n];
+  const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
+  const float u_raw = p.u_draft[o];
+  StageBatch sb;
+  if (STAGED) stage_issue(gfine, n_seg, 0, sb);
+  HRow<WT> hrow;
+  hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
   // maximum (greedy: with the lowest argmax carried in the records' second
-  // word) over all records; order-independent, so taken while staging
+  // word; sampled: the second word is ignored), taken while staging
   float m = -INFINITY;
   int im = kIntMax;
-  auto fold = [&](float2 r) {
-    if (c == 0.0f)
-      amax_merge(m, im, r.x, __float_as_int(r.y));
-    else
-      m = fmaxf(m, r.x);
-  };
+  auto fold = [&](float2 r) { amax_merge(m, im, r.x, __float_as_int(r.y)); };
   if (STAGED) {
-    stage_records(gfine, n_seg, srec, fold);
+    stage_commit(n_seg, 0, sb, srec, fold);
+    for (int base = 256 * kStageBatch; base < n_seg; base += 256 * kStageBatch) {
+      stage_issue(gfine, n_seg, base, sb);
+      stage_commit(n_seg, base, sb, srec, fold);
+    }
   } else {
 #pragma unroll 8
     for (int t = tid; t < n_seg; t += 256) fold(gfine[t]);
   }
-  if (c != 0.0f) im = 0;
-  block256_amax(m, im, sh.fred, sh.ired);  // also orders the LDS stores before the reads below
+  hrow.commit(p.rank, hs);
+  block_amax_once(m, im, sh.fred, sh.ired);  // also orders the LDS stores above before the reads below
   const float M = m;
+  const float c = temp_scale(T);
   if (c == 0.0f) {
     if (tid == 0) {
       p.y[o] = clampi(im, 0, V - 1);
@@ -99,7 +141,7 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
     }
     return;
   }
-  const float u = clamp_uniform(p.u_draft[o]);
+  const float u = clamp_uniform(u_raw);
   // mass of segment t in units of 2^((. - M) c)
   auto mass = [&](int t) {
     const float2 r = fine[t];
@@ -156,13 +198,22 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   const float Mq = st[0], iZq = 1.0f / st[1], Mp = st[2], iZp = 1.0f / st[3];
   const float c = temp_scale(p.temp[n]);
   const float u = clamp_uniform(p.u_final[n]);
-  load_h<WT>(static_cast<const WT*>(p.W1), prev, p.rank, hs);
   const float2* gfine = reinterpret_cast<const float2*>(p.rpart) + static_cast<int64_t>(n) * p.n_seg;
   const float2* fine = STAGED ? srec : gfine;
+  StageBatch sb;
+  if (STAGED) stage_issue(gfine, p.n_seg, 0, sb);
+  HRow<WT> hrow;
+  hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
   if (STAGED) {
-    stage_records(gfine, p.n_seg, srec, [](float2) {});
-    __syncthreads();
+    auto none = [](float2) {};
+    stage_commit(p.n_seg, 0, sb, srec, none);
+    for (int base = 256 * kStageBatch; base < p.n_seg; base += 256 * kStageBatch) {
+      stage_issue(gfine, p.n_seg, base, sb);
+      stage_commit(p.n_seg, base, sb, srec, none);
+    }
   }
+  hrow.commit(p.rank, hs);
+  __syncthreads();
   auto mass = [&](int t) { return fine[t].y; };
   const Located2 L = locate_blocked(p.n_seg, mass, u, &sh2);
   const float* tr = p.target + trow * V;

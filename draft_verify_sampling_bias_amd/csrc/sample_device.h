@@ -121,10 +121,12 @@ struct Located2 {
 };
 
 struct Loc2Scratch {
-  float scan[4];
-  float fred[4];
+  float wsum[4];   // per-wavefront totals of the block scan
+  float fred[4];   // per-wavefront maxima (finish kernels)
   int ired[4];
-  float P;
+  int cand[4];     // per-wavefront first thread whose interval holds u Z
+  float cexcl[4];  // and its exclusive prefix
+  int glast[4];    // per-wavefront last segment with positive mass
   int sel;
   float rem;
   int fb;
@@ -135,23 +137,52 @@ __device__ __forceinline__ int block_begin(int i, int n) { return range_start(i,
 
 // Second half of the location: ts is this thread's block sum (already in
 // the units of mass()), lastpos its last segment with positive mass (or -1).
+// Three workgroup barriers; every scratch slot is written once per call, so
+// no barrier is needed to protect reuse (callers must not call it twice
+// with the same scratch without a barrier in between).
 template <class Mass>
 __device__ Located2 locate_from_block_sums(int n, float ts, int lastpos, Mass mass, float u, Loc2Scratch* sh) {
-  const int tid = threadIdx.x;
-  float excl, Z;
-  const float incl = block256_scan(ts, sh->scan, &excl, &Z);
-  const float theta = u * Z;
-  const int first = block256_min_int((incl > theta) ? tid : 256, sh->ired);
-  const int glast = block256_max_int(lastpos, sh->ired);
-  if (tid == first) sh->P = excl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // block-wide scan: thread intervals [excl, incl) of consecutive threads
+  // meet exactly (incl of one thread is excl of the next, bit for bit)
+  const float v = wave_incl_scan(ts);
+  if (lane == 63) sh->wsum[wave] = v;
   __syncthreads();
+  const float w0 = sh->wsum[0], w1 = sh->wsum[1], w2 = sh->wsum[2], w3 = sh->wsum[3];
+  const float off = (wave == 0) ? 0.0f : (wave == 1) ? w0 : (wave == 2) ? (w0 + w1) : ((w0 + w1) + w2);
+  const float incl = off + v;
+  const float up = __shfl_up(incl, 1);
+  const float excl = (lane == 0) ? off : up;
+  const float Z = ((w0 + w1) + w2) + w3;
+  const float theta = u * Z;
+  // the first thread whose interval holds theta, with its exclusive prefix,
+  // and the last positive segment, in one barrier round
+  const unsigned long long hit = __ballot(incl > theta);
+  const int fl = hit ? (__ffsll(static_cast<long long>(hit)) - 1) : 0;
+  const float fex = __shfl(excl, fl);
+  const int wl = wave_max_int(lastpos);
+  if (lane == 0) {
+    sh->cand[wave] = hit ? (wave * 64 + fl) : 256;
+    sh->cexcl[wave] = fex;
+    sh->glast[wave] = wl;
+  }
+  __syncthreads();
+  int first = 256;
+  float P = 0.0f;
+#pragma unroll
+  for (int w = 3; w >= 0; --w) {
+    const bool has = sh->cand[w] < 256;
+    first = has ? sh->cand[w] : first;
+    P = has ? sh->cexcl[w] : P;
+  }
+  const int glast = max(max(sh->glast[0], sh->glast[1]), max(sh->glast[2], sh->glast[3]));
   int s0, s1;
   float th;
   bool fb;
   if (first < 256) {
     s0 = block_begin(first, n);
     s1 = block_begin(first + 1, n);
-    th = theta - sh->P;
+    th = theta - P;
     fb = false;
   } else {
     s0 = max(glast, 0);
@@ -160,26 +191,25 @@ __device__ Located2 locate_from_block_sums(int n, float ts, int lastpos, Mass ma
     fb = true;
   }
   if (tid < 64) {
-    const int lane = tid;
     int sel = -1, lpos = -1;
     float selP = 0.0f, lastP = 0.0f, base = 0.0f;
     for (int c0 = s0; c0 < s1; c0 += 64) {
       const int sidx = c0 + lane;
       const float x = (sidx < s1) ? mass(sidx) : 0.0f;
       const float cum = wave_incl_scan(x);
-      const float up = __shfl_up(cum, 1);
-      const float ex = (lane == 0) ? 0.0f : up;
-      const unsigned long long hit = __ballot(x > 0.0f && base + cum > th);
+      const float cup = __shfl_up(cum, 1);
+      const float ex = (lane == 0) ? 0.0f : cup;
+      const unsigned long long h2 = __ballot(x > 0.0f && base + cum > th);
       const unsigned long long pos = __ballot(x > 0.0f);
       if (pos) {
         const int lp = 63 - __clzll(static_cast<long long>(pos));
         lpos = c0 + lp;
         lastP = base + __shfl(ex, lp);
       }
-      if (hit) {
-        const int fl = __ffsll(static_cast<long long>(hit)) - 1;
-        sel = c0 + fl;
-        selP = base + __shfl(ex, fl);
+      if (h2) {
+        const int f2 = __ffsll(static_cast<long long>(h2)) - 1;
+        sel = c0 + f2;
+        selP = base + __shfl(ex, f2);
         break;
       }
       base += __shfl(cum, 63);
@@ -202,7 +232,6 @@ __device__ Located2 locate_from_block_sums(int n, float ts, int lastpos, Mass ma
   out.rem = sh->rem;
   out.fallback = sh->fb != 0;
   out.Z = Z;
-  __syncthreads();
   return out;
 }
 
