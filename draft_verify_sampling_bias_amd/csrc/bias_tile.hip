@@ -136,7 +136,10 @@ __device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s
   }
 }
 
-template <int KS>
+// B (H from LDS) is read one k-step ahead when DBUF, else just in time (the
+// draft kernel runs two wavefronts per SIMD, which cover the LDS latency,
+// and needs the registers).
+template <int KS, bool DBUF>
 __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
                                            f32x4_t (&acc)[4]) {
   constexpr int RS = KS * 32 + 8;
@@ -144,16 +147,23 @@ __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint16_t* h0 = Hs + l16 * RS + kq * 8;
-  u32x4_t b[2][4];
+  u32x4_t b[DBUF ? 2 : 1][4];
+  if (DBUF) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
+    for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
+  }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < KS) {
+    const int cur = DBUF ? (ks & 1) : 0;
+    if (DBUF) {
+      if (ks + 1 < KS) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
+        for (int nb = 0; nb < 4; ++nb)
+          b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
     }
     // the empty asm pins the zeroing here: hoisted next to the load (across
     // the loop's back edge) it would wait on the whole prefetch
@@ -248,17 +258,16 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
   }
 }
 
-constexpr int kSeg16Waves = 4;  // one wavefront per SIMD: the prefetched tile needs ~260 registers
+constexpr int kSeg16Waves = 4;  // wavefronts per workgroup, one per SIMD
 
 // Wavefront w of the grid handles segments w, w + W, w + 2W, ... (W = all
 // wavefronts), so at any moment the grid streams one contiguous stretch of
 // W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
 // each of 64 rows.
 template <int KS, bool RESID, bool VEC4>
-__global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16(TileParams p) {
+__device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci) {
   constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
-  __shared__ ReqInfo s_ci[kSmallMaxR];
+  constexpr bool DBUF = RESID;     // see seg16_mfma
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = p.R, rank = p.rank;
   const int n_seg = p.n_seg;
@@ -271,15 +280,25 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16(TileParams p) {
   if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, tid, RESID);
   lds_barrier();
   {
+    // H = W1[prev] for all requests: every 16-byte load of this thread is
+    // issued before any is stored, so the gather costs one memory latency
     constexpr int G = KS * 4;  // 16-byte groups per H row
+    constexpr int kPer = kSmallMaxR * G / (kSeg16Waves * 64);
     const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
-    for (int q = tid; q < kSmallMaxR * G; q += kSeg16Waves * 64) {
+    u32x4_t val[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = tid + j * kSeg16Waves * 64;
       const int nn = q / G, g = q - nn * G;
-      const ReqInfo& ci = s_ci[nn];
-      u32x4_t val = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(ci.prev) * rank +
-                                                       min(g * 8, rank - 8));
-      if (g * 8 >= rank || !ci.act) val = u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = val;
+      val[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank +
+                                                  min(g * 8, rank - 8));
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = tid + j * kSeg16Waves * 64;
+      const int nn = q / G, g = q - nn * G;
+      const u32x4_t v = (g * 8 >= rank || !s_ci[nn].act) ? u32x4_t{0u, 0u, 0u, 0u} : val[j];
+      *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
     }
   }
   // wavefront-uniform walk state (scalar registers, scalar branches)
@@ -298,16 +317,36 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16(TileParams p) {
     f32x4_t acc[4];
     const int s1 = sg + n_waves;
     seg16_load<KS, RESID, VEC4>(p, s_ci, min(s1, n_seg - 1) * kSegSmall, lane, fb);
-    seg16_mfma<KS>(fa.w, Hs, rank, lane, acc);
+    seg16_mfma<KS, DBUF>(fa.w, Hs, rank, lane, acc);
     seg16_epilogue<KS, RESID>(p, lq, sg, lane, fa, acc);
     if (s1 >= n_seg) break;
     const int s2 = s1 + n_waves;
     seg16_load<KS, RESID, VEC4>(p, s_ci, min(s2, n_seg - 1) * kSegSmall, lane, fa);
-    seg16_mfma<KS>(fb.w, Hs, rank, lane, acc);
+    seg16_mfma<KS, DBUF>(fb.w, Hs, rank, lane, acc);
     seg16_epilogue<KS, RESID>(p, lq, s1, lane, fb, acc);
     if (s2 >= n_seg) break;
     sg = s2;
   }
+}
+
+// Draft mode: two workgroups per CU (two wavefronts per SIMD) for latency
+// hiding; the kernel is compiled to fit 256 registers per wavefront.
+template <int KS, bool VEC4>
+__global__ void __launch_bounds__(kSeg16Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+bias_seg16(TileParams p) {
+  constexpr int RS = KS * 32 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
+  __shared__ ReqInfo s_ci[kSmallMaxR];
+  bias_seg16_body<KS, false, VEC4>(p, Hs, s_ci);
+}
+
+// Residual mode (holds the target values too): one wavefront per SIMD.
+template <int KS, bool VEC4>
+__global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p) {
+  constexpr int RS = KS * 32 + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
+  __shared__ ReqInfo s_ci[kSmallMaxR];
+  bias_seg16_body<KS, true, VEC4>(p, Hs, s_ci);
 }
 
 // ---------------------------------------------------------------------------
@@ -521,17 +560,30 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     return hipGetLastError();
   }
   if (p.seg_rows == kSegSmall) {
-    // persistent: at most one workgroup (four wavefronts, one per SIMD) per CU
-    const int blocks = max(1, min((p.n_seg + kSeg16Waves - 1) / kSeg16Waves, num_cu));
+    // persistent: two workgroups per CU in draft mode, one in residual mode
+    // (four wavefronts each, one per SIMD)
+    const int per_cu = RESID ? 1 : 2;
+    const int blocks = max(1, min((p.n_seg + kSeg16Waves - 1) / kSeg16Waves, per_cu * num_cu));
     const dim3 grid(blocks), block(kSeg16Waves * 64);
-    if (p.rank <= 64)
-      launch(bias_seg16<2, RESID, VEC4>, grid, block, s, e0, e1, p);
-    else if (p.rank <= 128)
-      launch(bias_seg16<4, RESID, VEC4>, grid, block, s, e0, e1, p);
-    else if (p.rank <= 256)
-      launch(bias_seg16<8, RESID, VEC4>, grid, block, s, e0, e1, p);
-    else
-      launch(bias_seg16<16, RESID, VEC4>, grid, block, s, e0, e1, p);
+    if (RESID) {
+      if (p.rank <= 64)
+        launch(bias_seg16_res<2, VEC4>, grid, block, s, e0, e1, p);
+      else if (p.rank <= 128)
+        launch(bias_seg16_res<4, VEC4>, grid, block, s, e0, e1, p);
+      else if (p.rank <= 256)
+        launch(bias_seg16_res<8, VEC4>, grid, block, s, e0, e1, p);
+      else
+        launch(bias_seg16_res<16, VEC4>, grid, block, s, e0, e1, p);
+    } else {
+      if (p.rank <= 64)
+        launch(bias_seg16<2, VEC4>, grid, block, s, e0, e1, p);
+      else if (p.rank <= 128)
+        launch(bias_seg16<4, VEC4>, grid, block, s, e0, e1, p);
+      else if (p.rank <= 256)
+        launch(bias_seg16<8, VEC4>, grid, block, s, e0, e1, p);
+      else
+        launch(bias_seg16<16, VEC4>, grid, block, s, e0, e1, p);
+    }
     return hipGetLastError();
   }
   const dim3 grid((p.n_seg + 3) / 4), block(256);
