@@ -1,10 +1,10 @@
 // Verify kernels ("DSpark" explainer sections 2-3; llama.cpp PR #25173,
 // "Losslessness").
 //
-// verify_stats: one workgroup per (target row, 4096-entry chunk); coalesced
-//   float4 sweep of the row giving the chunk's maximum, lowest argmax and, for
-//   a sampled request, sum of exp((t - max)/T).  This is the pass that reads
-//   every target logit once.
+// verify_stats: one wavefront per (target row, 4096-entry chunk), the
+//   request given by the grid; coalesced float4 sweep giving each (row,
+//   chunk) its maximum, lowest argmax and, for a sampled request, sum of
+//   exp((t - max)/T).  This is the pass that reads every target logit once.
 // verify_finish: one workgroup per request; combines its rows' chunk records
 //   into (max, argmax, Z) per row, runs the accept tests u < p/q left to
 //   right, finds the first rejection, and emits the greedy correction/bonus
@@ -20,100 +20,73 @@
 namespace dspark {
 namespace {
 
-constexpr int kOffLds = 4096;  // row_offsets entries staged in LDS
-
-// first index i in [0, n) with off[i] > key, or n
-__device__ __forceinline__ int upper_bound_i32(const int32_t* off, int n, int64_t key) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (static_cast<int64_t>(off[mid]) > key)
-      hi = mid;
-    else
-      lo = mid + 1;
-  }
-  return lo;
-}
-
-__global__ void __launch_bounds__(256) verify_stats_kernel(VerifyParams p) {
-  __shared__ int32_t s_off[kOffLds];
-  __shared__ float fred[4];
-  __shared__ int ired[4];
-  __shared__ int s_req;
-  const int tid = threadIdx.x;
-  const int64_t b = blockIdx.x;
-  const int64_t row = b / p.n_chunks;
-  const int ch = static_cast<int>(b - row * p.n_chunks);
-  const int V = p.V;
-  const float* tr = p.target + row * V;
-  const int base = ch * kChunk;
-  const bool vec4 = (V & 3) == 0;
-
-  float x[16];
+// verify_stats: workgroup (r, j, g) covers chunks 4g .. 4g + 3 of row j of
+// request r (row row_offsets[r] + j; workgroups past the request's last row
+// leave at once), one chunk per wavefront: 16 float4 loads per lane (1 KB
+// contiguous per instruction), then wavefront-level reductions only (no
+// workgroup barrier).
+template <bool VEC4>
+__device__ __forceinline__ void chunk_load(const float* row, int base, int V, int lane, float (&x)[64]) {
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int v = base + (it * 256 + tid) * 4;
-    if (vec4 && v < V) {
-      const f32x4_t t = *reinterpret_cast<const f32x4_t*>(tr + v);
-      x[4 * it + 0] = t[0];
-      x[4 * it + 1] = t[1];
-      x[4 * it + 2] = t[2];
-      x[4 * it + 3] = t[3];
+  for (int j = 0; j < 16; ++j) {
+    const int v = base + (j * 64 + lane) * 4;
+    if (VEC4) {
+      const f32x4_t t = *reinterpret_cast<const f32x4_t*>(row + min(v, V - 4));
+      x[4 * j + 0] = t[0];
+      x[4 * j + 1] = t[1];
+      x[4 * j + 2] = t[2];
+      x[4 * j + 3] = t[3];
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * it + e] = (v + e < V) ? tr[v + e] : -INFINITY;
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = row[min(v + e, V - 1)];
     }
   }
+}
 
-  // request owning this row
-  int r;
-  if (p.R + 1 <= kOffLds) {
-    for (int i = tid; i <= p.R; i += 256) s_off[i] = p.row_offsets[i];
-    __syncthreads();
-    r = upper_bound_i32(s_off, p.R + 1, row) - 1;
-  } else {
-    if (tid == 0) s_req = upper_bound_i32(p.row_offsets, p.R + 1, row) - 1;
-    __syncthreads();
-    r = s_req;
-  }
-  r = clampi(r, 0, p.R - 1);
+template <bool VEC4>
+__global__ void __launch_bounds__(256) verify_stats_kernel(VerifyParams p) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int ch = blockIdx.z * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  if (ch >= p.n_chunks) return;  // wavefront-uniform; no workgroup barrier follows
+  const int64_t lo = min(max(static_cast<int64_t>(p.row_offsets[r]), int64_t{0}), p.n_rows);
+  const int64_t hi = min(max(static_cast<int64_t>(p.row_offsets[r + 1]), lo), p.n_rows);
+  const int64_t row = lo + blockIdx.y;
+  if (row >= hi) return;
   const float c = temp_scale(p.temp[r]);
-
+  const int V = p.V;
+  const int base = ch * kChunk;
+  float x[64];
+  chunk_load<VEC4>(p.target + row * V, base, V, lane, x);
   float m = -INFINITY;
   int im = kIntMax;
 #pragma unroll
-  for (int it = 0; it < 4; ++it)
+  for (int j = 0; j < 16; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int v = base + (it * 256 + tid) * 4 + e;
-      if (v < V && x[4 * it + e] > m) {
-        m = x[4 * it + e];
-        im = v;
-      }
+      const int v = base + (j * 64 + lane) * 4 + e;
+      // lowest index of the maximum, also when every entry is -inf
+      const bool gt = (v < V) & amax_takes(x[4 * j + e], v, m, im);
+      m = gt ? x[4 * j + e] : m;
+      im = gt ? v : im;
     }
-  block256_amax(m, im, fred, ired);
-
+  wave_amax(m, im);
   float sum = 0.0f;
-  if (c > 0.0f) {
+  if (c > 0.0f) {  // workgroup-uniform (one request per workgroup)
     float e_loc = 0.0f;
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int j = 0; j < 16; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int v = base + (it * 256 + tid) * 4 + e;
-        if (v < V) e_loc += exp2_rel(x[4 * it + e], m, c);
+        const int v = base + (j * 64 + lane) * 4 + e;
+        const float w = exp2_rel(x[4 * j + e], m, c);
+        e_loc += (v < V) ? w : 0.0f;
       }
-    e_loc = wave_sum(e_loc);
-    if ((tid & 63) == 0) fred[tid >> 6] = e_loc;
-    __syncthreads();
-    sum = ((fred[0] + fred[1]) + fred[2]) + fred[3];
+    sum = wave_sum(e_loc);
   }
-  if (tid == 0) {
+  if (lane == 0) {
     float* rec = p.vpart + (row * p.n_chunks + ch) * kChunkFloats;
-    rec[0] = m;
-    rec[1] = __int_as_float(im);
-    rec[2] = sum;
-    rec[3] = 0.0f;
+    *reinterpret_cast<f32x4_t*>(rec) = f32x4_t{m, __int_as_float(im), sum, 0.0f};
   }
 }
 
@@ -233,8 +206,13 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
 
 hipError_t launch_verify_stats(const VerifyParams& p, hipStream_t s) {
   if (p.R == 0 || p.n_rows == 0) return hipSuccess;
-  const int64_t blocks = p.n_rows * p.n_chunks;
-  hipLaunchKernelGGL(verify_stats_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  // y: row index within the request (at most gamma + 1 rows)
+  const dim3 grid(static_cast<unsigned>(p.R), static_cast<unsigned>(p.gamma + 1),
+                  static_cast<unsigned>((p.n_chunks + 3) / 4));
+  if ((p.V & 3) == 0)
+    hipLaunchKernelGGL(verify_stats_kernel<true>, grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(verify_stats_kernel<false>, grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
