@@ -63,16 +63,28 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
 
   unsigned long long key[kSlots];
   bool valid[kSlots];
-  float run = 1.0f;
+  // the confidences and drafted tokens of this thread's slots are loaded up
+  // front, in one batch
+  float cv[kSlots];
+  int yv[kSlots];
 #pragma unroll
   for (int s = 0; s < kSlots; ++s) {
     const int j = s / gamma, k = s - j * gamma;
     const int r = j * kSchedThreads + tid;
     valid[s] = (s < used) && (r < R);
+    const int64_t o = valid[s] ? static_cast<int64_t>(r) * gamma + k : 0;
+    cv[s] = valid[s] ? a.c[o] : 0.0f;
+    yv[s] = valid[s] ? a.y[o] : 0;
+  }
+  float run = 1.0f;
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    const int j = s / gamma, k = s - j * gamma;
+    const int r = j * kSchedThreads + tid;
     key[s] = ~0ull;
     if (valid[s]) {
       const int64_t o = static_cast<int64_t>(r) * gamma + k;
-      float ck = fminf(fmaxf(a.c[o], 0.0f), 1.0f);  // NaN -> 0
+      float ck = fminf(fmaxf(cv[s], 0.0f), 1.0f);  // NaN -> 0
       run = (k == 0) ? ck : run * ck;
       const float av = (run == 0.0f) ? 0.0f : run;  // no -0
       a.a[o] = av;
@@ -150,17 +162,25 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
     if (j < JR) {
       const int r = j * kSchedThreads + tid;
       const int cnt = (r < R) ? lj[j] + 1 : 0;
+      const int anc = (r < R) ? a.anchor[r] : 0;  // in flight during the scan
       int tot;
       const int ex = block1024_excl_scan_int(cnt, s_i16, &tot);
       if (r < R) {
         const int off = carry + ex;
         a.l[r] = lj[j];
         a.row_offsets[r] = off;
-        const int anchor = a.anchor[r];
-        for (int pos = 0; pos <= lj[j]; ++pos) {
-          a.row_req[off + pos] = r;
-          a.row_pos[off + pos] = pos;
-          a.row_tok[off + pos] = (pos == 0) ? anchor : a.y[static_cast<int64_t>(r) * gamma + pos - 1];
+        // row pos of request r: the anchor for pos 0, else y[r, pos - 1]
+        // (slot j * gamma + pos - 1 of this thread)
+#pragma unroll
+        for (int q = 0; q <= kSlots; ++q) {
+          if (q <= lj[j]) {
+            int tok = anc;
+#pragma unroll
+            for (int s = 0; s < kSlots; ++s) tok = (q >= 1 && s == j * gamma + q - 1) ? yv[s] : tok;
+            a.row_req[off + q] = r;
+            a.row_pos[off + q] = q;
+            a.row_tok[off + q] = tok;
+          }
         }
       }
       carry += tot;

@@ -106,9 +106,24 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
   __shared__ ChunkScratch sh;
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = p.V, gamma = p.gamma;
-  const int64_t i0 = p.row_offsets[n], i1 = p.row_offsets[n + 1];
-  const int64_t nrows = i1 - i0;
   const int64_t og = static_cast<int64_t>(n) * gamma;
+  // every input that depends only on n is loaded first, in one batch; lane j
+  // of each wavefront holds position j's draft values
+  const int64_t i0 = p.row_offsets[n], i1 = p.row_offsets[n + 1];
+  const float T = p.temp[n];
+  const float uf = p.u_final[n];
+  const int anc = p.anchor[n];
+  int yv = 0;
+  float qt = 1.0f, ua = 0.0f, qs0 = 0.0f, qs1 = 1.0f;
+  if (lane < gamma) {
+    const int64_t o = og + lane;
+    yv = p.y[o];
+    qt = p.q_tok[o];
+    ua = p.u_accept[o];
+    qs0 = p.q_stats[2 * o];
+    qs1 = p.q_stats[2 * o + 1];
+  }
+  const int64_t nrows = i1 - i0;
   if (nrows < 1 || nrows > gamma + 1 || i0 < 0 || i1 > p.n_rows) {
     // inconsistent offsets: defined, in-bounds outputs
     if (tid < gamma) p.p_tok[og + tid] = 0.0f;
@@ -120,19 +135,28 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
     return;
   }
   const int l = static_cast<int>(nrows) - 1;
-  const float c = temp_scale(p.temp[n]);
+  const float c = temp_scale(T);
+  yv = clampi(yv, 0, V - 1);
+  // target logit of each drafted token (rows i0 + j, j < l), in flight while
+  // the chunk records below are combined
+  float tl = 0.0f;
+  if (wave == 0 && lane < l && c > 0.0f) tl = p.target[(i0 + lane) * V + yv];
 
   for (int j = wave; j <= l; j += 4) {
-    const float* rec = p.vpart + (i0 + j) * p.n_chunks * kChunkFloats;
+    const f32x4_t* rec = reinterpret_cast<const f32x4_t*>(p.vpart + (i0 + j) * p.n_chunks * kChunkFloats);
     float m = -INFINITY;
     int im = kIntMax;
-    for (int ch = lane; ch < p.n_chunks; ch += 64)
-      amax_merge(m, im, rec[ch * kChunkFloats], __float_as_int(rec[ch * kChunkFloats + 1]));
+    for (int ch = lane; ch < p.n_chunks; ch += 64) {
+      const f32x4_t r = rec[ch];
+      amax_merge(m, im, r[0], __float_as_int(r[1]));
+    }
     wave_amax(m, im);
     float z = 0.0f;
     if (c > 0.0f) {
-      for (int ch = lane; ch < p.n_chunks; ch += 64)
-        z += rec[ch * kChunkFloats + 2] * exp2_hw((rec[ch * kChunkFloats] - m) * c);
+      for (int ch = lane; ch < p.n_chunks; ch += 64) {
+        const f32x4_t r = rec[ch];
+        z += r[2] * exp2_hw((r[0] - m) * c);
+      }
       z = wave_sum(z);
     }
     if (lane == 0) {
@@ -147,25 +171,39 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
     bool rej = false;
     float pt = 0.0f;
     if (lane < l) {
-      const int64_t o = og + lane;
-      const int yj = clampi(p.y[o], 0, V - 1);
       if (c == 0.0f) {
-        const bool ok = (yj == rI[lane]);
+        const bool ok = (yv == rI[lane]);
         pt = ok ? 1.0f : 0.0f;
         rej = !ok;
       } else {
-        const float t = p.target[(i0 + lane) * V + yj];
-        pt = exp2_hw((t - rM[lane]) * c) / rZ[lane];
-        const float ratio = pt / p.q_tok[o];
-        rej = !(p.u_accept[o] < ratio);
+        pt = exp2_hw((tl - rM[lane]) * c) / rZ[lane];
+        const float ratio = pt / qt;
+        rej = !(ua < ratio);
       }
     }
     const unsigned long long mask = __ballot(rej);
     const int nacc = mask ? (__ffsll(static_cast<long long>(mask)) - 1) : l;
     if (lane < gamma) p.p_tok[og + lane] = (lane < l) ? pt : 0.0f;
+    // a sampled rejection: hand (prev, U row, target row, q and p statistics)
+    // to the residual pass; every value is already in this wavefront
+    const float q0 = __shfl(qs0, nacc & 63), q1 = __shfl(qs1, nacc & 63);
+    const int yprev = __shfl(yv, (nacc - 1) & 63);
     if (lane == 0) {
       p.n_accept[n] = nacc;
       s_nacc = nacc;
+      if (c != 0.0f && nacc < l) {
+        const int prev = (nacc == 0) ? anc : yprev;
+        int32_t* inf = p.rs_info + 4 * static_cast<int64_t>(n);
+        inf[0] = 1;
+        inf[1] = clampi(prev, 0, V - 1);
+        inf[2] = static_cast<int32_t>(og + nacc);
+        inf[3] = static_cast<int32_t>(i0 + nacc);
+        float* st = p.rs_stats + 4 * static_cast<int64_t>(n);
+        st[0] = q0;
+        st[1] = q1;
+        st[2] = rM[nacc];
+        st[3] = rZ[nacc];
+      }
     }
   }
   __syncthreads();
@@ -179,26 +217,13 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
     return;
   }
   if (nacc == l) {
-    const float u = clamp_uniform(p.u_final[n]);
+    const float u = clamp_uniform(uf);
     const int out = chunk_draw(p.vpart + (i0 + l) * p.n_chunks * kChunkFloats, p.n_chunks, p.target + (i0 + l) * V,
                                V, rM[l], c, u, &sh);
     if (tid == 0) {
       p.out_tok[n] = (out >= 0) ? out : rI[l];
       clear_residual(p, n);
     }
-  } else if (tid == 0) {
-    const int prev = (nacc == 0) ? p.anchor[n] : p.y[og + nacc - 1];
-    int32_t* inf = p.rs_info + 4 * static_cast<int64_t>(n);
-    inf[0] = 1;
-    inf[1] = clampi(prev, 0, V - 1);
-    inf[2] = static_cast<int32_t>(og + nacc);
-    inf[3] = static_cast<int32_t>(i0 + nacc);
-    const float* qs = p.q_stats + 2 * (og + nacc);
-    float* st = p.rs_stats + 4 * static_cast<int64_t>(n);
-    st[0] = qs[0];
-    st[1] = qs[1];
-    st[2] = rM[nacc];
-    st[3] = rZ[nacc];
   }
 }
 
