@@ -258,13 +258,14 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
   }
 }
 
-constexpr int kSeg16Waves = 4;  // wavefronts per workgroup, one per SIMD
+constexpr int kSeg16Waves = 4;     // residual mode: wavefronts per workgroup, one per SIMD
+constexpr int kSeg16DraftWaves = 8;  // draft mode: one workgroup per CU, two wavefronts per SIMD
 
 // Wavefront w of the grid handles segments w, w + W, w + 2W, ... (W = all
 // wavefronts), so at any moment the grid streams one contiguous stretch of
 // W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
 // each of 64 rows.
-template <int KS, bool RESID, bool VEC4>
+template <int KS, bool RESID, bool VEC4, int WPB>
 __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci) {
   constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
   constexpr bool DBUF = RESID;     // see seg16_mfma
@@ -274,7 +275,7 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
 
   if (RESID) {
     int any = 0;
-    for (int n = tid; n < R; n += kSeg16Waves * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
+    for (int n = tid; n < R; n += WPB * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
     if (!__syncthreads_or(any)) return;
   }
   if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, tid, RESID);
@@ -283,27 +284,27 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
     // H = W1[prev] for all requests: every 16-byte load of this thread is
     // issued before any is stored, so the gather costs one memory latency
     constexpr int G = KS * 4;  // 16-byte groups per H row
-    constexpr int kPer = kSmallMaxR * G / (kSeg16Waves * 64);
+    constexpr int kPer = kSmallMaxR * G / (WPB * 64);
     const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
     u32x4_t val[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int q = tid + j * kSeg16Waves * 64;
+      const int q = tid + j * WPB * 64;
       const int nn = q / G, g = q - nn * G;
       val[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank +
                                                   min(g * 8, rank - 8));
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int q = tid + j * kSeg16Waves * 64;
+      const int q = tid + j * WPB * 64;
       const int nn = q / G, g = q - nn * G;
       const u32x4_t v = (g * 8 >= rank || !s_ci[nn].act) ? u32x4_t{0u, 0u, 0u, 0u} : val[j];
       *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
     }
   }
   // wavefront-uniform walk state (scalar registers, scalar branches)
-  const int n_waves = gridDim.x * kSeg16Waves;
-  int sg = blockIdx.x * kSeg16Waves + __builtin_amdgcn_readfirstlane(wave);
+  const int n_waves = gridDim.x * WPB;
+  int sg = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(wave);
   Seg16Regs<KS, RESID> fa, fb;
   seg16_load<KS, RESID, VEC4>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
   lds_barrier();
@@ -329,15 +330,16 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
   }
 }
 
-// Draft mode: two workgroups per CU (two wavefronts per SIMD) for latency
-// hiding; the kernel is compiled to fit 256 registers per wavefront.
+// Draft mode: one workgroup of eight wavefronts per CU (two per SIMD, for
+// latency hiding, sharing one copy of H); compiled to fit 256 registers per
+// wavefront.
 template <int KS, bool VEC4>
-__global__ void __launch_bounds__(kSeg16Waves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kSeg16DraftWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bias_seg16(TileParams p) {
   constexpr int RS = KS * 32 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, false, VEC4>(p, Hs, s_ci);
+  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves>(p, Hs, s_ci);
 }
 
 // Residual mode (holds the target values too): one wavefront per SIMD.
@@ -346,7 +348,7 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p)
   constexpr int RS = KS * 32 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, true, VEC4>(p, Hs, s_ci);
+  bias_seg16_body<KS, true, VEC4, kSeg16Waves>(p, Hs, s_ci);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,11 +562,10 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     return hipGetLastError();
   }
   if (p.seg_rows == kSegSmall) {
-    // persistent: two workgroups per CU in draft mode, one in residual mode
-    // (four wavefronts each, one per SIMD)
-    const int per_cu = RESID ? 1 : 2;
-    const int blocks = max(1, min((p.n_seg + kSeg16Waves - 1) / kSeg16Waves, per_cu * num_cu));
-    const dim3 grid(blocks), block(kSeg16Waves * 64);
+    // persistent: one workgroup per CU (draft: eight wavefronts, residual: four)
+    const int wpb = RESID ? kSeg16Waves : kSeg16DraftWaves;
+    const int blocks = max(1, min((p.n_seg + wpb - 1) / wpb, num_cu));
+    const dim3 grid(blocks), block(wpb * 64);
     if (RESID) {
       if (p.rank <= 64)
         launch(bias_seg16_res<2, VEC4>, grid, block, s, e0, e1, p);
