@@ -31,14 +31,16 @@ __device__ __forceinline__ void chunk_load(const float* row, int base, int V, in
   for (int j = 0; j < 16; ++j) {
     const int v = base + (j * 64 + lane) * 4;
     if (VEC4) {
-      const f32x4_t t = *reinterpret_cast<const f32x4_t*>(row + min(v, V - 4));
+      // read once: non-temporal, so the stream does not displace the Markov
+      // weights that the residual pass reads next from the last-level cache
+      const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(row + min(v, V - 4)));
       x[4 * j + 0] = t[0];
       x[4 * j + 1] = t[1];
       x[4 * j + 2] = t[2];
       x[4 * j + 3] = t[3];
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * j + e] = row[min(v + e, V - 1)];
+      for (int e = 0; e < 4; ++e) x[4 * j + e] = __builtin_nontemporal_load(row + min(v + e, V - 1));
     }
   }
 }
