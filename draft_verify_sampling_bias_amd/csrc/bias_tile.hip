@@ -180,6 +180,64 @@ __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16
   }
 }
 
+// seg16_mfma with the next segment's loads interleaved: k-step ks issues
+// W2 fragment ks of segment [vw_next, vw_next + 16) (and, in the first
+// steps, its U / target values), so a load issue that stalls on a busy
+// memory pipeline holds up one k-step instead of a whole segment.
+template <int KS, bool RESID, bool VEC4, bool DBUF>
+__device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
+                                              f32x4_t (&acc)[4], const TileParams& p, const ReqInfo* s_ci,
+                                              int vw_next, Seg16Regs<KS, RESID>& nx) {
+  constexpr int RS = KS * 32 + 8;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int V = p.V;
+  const uint16_t* w2n =
+      static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(min(vw_next + l16, V - 1)) * rank;
+  const int vu = vw_next + kq * 4;
+  auto issue_u = [&](int nb) {
+    const int nn = nb * 16 + l16;
+    const ReqInfo& ci = s_ci[nn];
+    nx.u[nb] = load4<VEC4>(u_row(p, ci, nn < p.R ? nn : 0, RESID), vu, V);
+    if (RESID) nx.t[nb] = load4<VEC4>(p.target + static_cast<int64_t>(ci.trow) * V, vu, V);
+  };
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* h0 = Hs + l16 * RS + kq * 8;
+  u32x4_t b[DBUF ? 2 : 1][4];
+  if (DBUF) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    nx.w[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(w2n + min(ks * 32 + kq * 8, rank - 8)));
+    if (ks < 4) issue_u(ks);
+    const int cur = DBUF ? (ks & 1) : 0;
+    if (DBUF) {
+      if (ks + 1 < KS) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
+    }
+    // the empty asm pins the zeroing here: hoisted next to the load (across
+    // the loop's back edge) it would wait on the whole prefetch
+    bf16x8_t a = w[ks];
+    asm volatile("" : "+v"(a));
+    a = (ks * 32 + kq * 8 < rank) ? a : bf16x8_t{};
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb], 0, 0,
+                                                        0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int nb = KS; nb < 4; ++nb) issue_u(nb);  // fewer k-steps than U groups (rank <= 96)
+}
+
 // Per-lane copies of the request constants of the lane's four requests
 // (request 16 nb + (lane & 15)), kept in registers for the whole walk.
 template <bool RESID>
@@ -278,15 +336,26 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
     for (int n = tid; n < R; n += WPB * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
     if (!__syncthreads_or(any)) return;
   }
+  // H = W1[prev] for all requests.  Every 16-byte load of this thread is
+  // issued before any is stored.  From the second draft position on, the
+  // previous position's finish has left the rows in hbuf (contiguous, no
+  // dependence on prev), so they are loaded together with the request info.
+  constexpr int G = KS * 4;  // 16-byte groups per H row
+  constexpr int kPer = kSmallMaxR * G / (WPB * 64);
+  const bool from_buf = !RESID && p.hbuf != nullptr;  // uniform
+  u32x4_t val[kPer];
+  if (from_buf) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = tid + j * WPB * 64;
+      const int nn = q / G, g = q - nn * G;
+      val[j] = *reinterpret_cast<const u32x4_t*>(p.hbuf + static_cast<int64_t>(nn) * rank + min(g * 8, rank - 8));
+    }
+  }
   if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, tid, RESID);
   lds_barrier();
-  {
-    // H = W1[prev] for all requests: every 16-byte load of this thread is
-    // issued before any is stored, so the gather costs one memory latency
-    constexpr int G = KS * 4;  // 16-byte groups per H row
-    constexpr int kPer = kSmallMaxR * G / (WPB * 64);
+  if (!from_buf) {
     const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
-    u32x4_t val[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int q = tid + j * WPB * 64;
@@ -294,36 +363,39 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
       val[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank +
                                                   min(g * 8, rank - 8));
     }
+  }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int q = tid + j * WPB * 64;
-      const int nn = q / G, g = q - nn * G;
-      const u32x4_t v = (g * 8 >= rank || !s_ci[nn].act) ? u32x4_t{0u, 0u, 0u, 0u} : val[j];
-      *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
-    }
+  for (int j = 0; j < kPer; ++j) {
+    const int q = tid + j * WPB * 64;
+    const int nn = q / G, g = q - nn * G;
+    const u32x4_t v = (g * 8 >= rank || !s_ci[nn].act) ? u32x4_t{0u, 0u, 0u, 0u} : val[j];
+    *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
   }
   // wavefront-uniform walk state (scalar registers, scalar branches)
   const int n_waves = gridDim.x * WPB;
   int sg = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(wave);
-  Seg16Regs<KS, RESID> fa, fb;
-  seg16_load<KS, RESID, VEC4>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  // the barrier comes before the first segment's loads: their issue can
+  // stall on a memory pipeline that the whole grid floods at once, and no
+  // wavefront should wait for another's issue
   lds_barrier();
   if (sg >= n_seg) return;
   LaneReq<RESID> lq;
   lane_req<RESID>(s_ci, lane, lq);
-  // Ping-pong prefetch.  The prefetch issued on a wavefront's last segment
-  // re-reads segment n_seg - 1 (a cache hit, never used) so that the load
-  // stream, and with it the compiler's wait counts, is the same every trip.
+  Seg16Regs<KS, RESID> fa, fb;
+  seg16_load<KS, RESID, VEC4>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  // Ping-pong prefetch, the next segment's loads interleaved with the
+  // current one's k-steps.  The prefetch issued on a wavefront's last
+  // segment re-reads segment n_seg - 1 (a cache hit, never used) so that the
+  // load stream, and with it the compiler's wait counts, is the same every
+  // trip.
   while (true) {
     f32x4_t acc[4];
     const int s1 = sg + n_waves;
-    seg16_load<KS, RESID, VEC4>(p, s_ci, min(s1, n_seg - 1) * kSegSmall, lane, fb);
-    seg16_mfma<KS, DBUF>(fa.w, Hs, rank, lane, acc);
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF>(fa.w, Hs, rank, lane, acc, p, s_ci, min(s1, n_seg - 1) * kSegSmall, fb);
     seg16_epilogue<KS, RESID>(p, lq, sg, lane, fa, acc);
     if (s1 >= n_seg) break;
     const int s2 = s1 + n_waves;
-    seg16_load<KS, RESID, VEC4>(p, s_ci, min(s2, n_seg - 1) * kSegSmall, lane, fa);
-    seg16_mfma<KS, DBUF>(fb.w, Hs, rank, lane, acc);
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF>(fb.w, Hs, rank, lane, acc, p, s_ci, min(s2, n_seg - 1) * kSegSmall, fa);
     seg16_epilogue<KS, RESID>(p, lq, s1, lane, fb, acc);
     if (s2 >= n_seg) break;
     sg = s2;
