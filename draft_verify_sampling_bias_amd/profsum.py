@@ -6,7 +6,8 @@
         --alg-bytes N --commands TEXT > out.txt
 
 `stats` condenses a `--kernel-trace --stats` kernel table (calls, total and
-average duration per kernel).  `traffic` turns two `--pmc FETCH_SIZE` /
+average duration per kernel).  `mfma` reports a kernel's bf16 MFMA work and
+utilisation from SQ counters and its traced average duration.  `traffic` turns two `--pmc FETCH_SIZE` /
 `--pmc WRITE_SIZE` runs (KiB per dispatch) into HBM bytes per launch of one
 kernel, each counter scaled by what it reads for a device copy of known size
 (the calibration runs), and records a SHA-256 over the fused bias kernel's
@@ -109,6 +110,36 @@ def traffic_text(kernel, fetch_csv, write_csv, cfetch_csv, cwrite_csv, calib_byt
     return "\n".join(lines) + "\n"
 
 
+def mfma_text(kernel, counters_csv, stats_csv, flops_per_launch, peak_tflops, commands):
+    """MFMA work and utilisation of one kernel: bf16 MFMA MOPs per dispatch
+    (one MOP = 512 FLOPs), MFMA busy cycles, and the achieved rate over the
+    kernel's average duration from a kernel-trace run."""
+    table = {}
+    for cn in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES"):
+        vals = _pick(_per_dispatch(counters_csv, cn), kernel)
+        table[cn] = sum(vals) / len(vals)
+    rows = [r for r in csv.DictReader(open(stats_csv)) if kernel in r["Name"]]
+    if len(rows) != 1:
+        raise SystemExit(f"kernel pattern {kernel!r} matches {len(rows)} rows of {stats_csv}")
+    avg_ns = float(rows[0]["AverageNs"])
+    flops = table["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0
+    tflops = flops / (avg_ns * 1e-9) / 1e12
+    lines = [
+        "# MFMA work of one kernel from rocprofv3 --pmc (per dispatch) and its average duration",
+        *[f"# command: {c}" for c in commands],
+        f"kernel: {kernel}",
+        f"kernel_source_sha256_16: {tile_source_hash()}",
+        *[f"{k.lower()}_per_dispatch: {v:.1f}" for k, v in table.items()],
+        f"mfma_flops_per_dispatch: {flops:.0f}",
+        f"algorithmic_flops_per_launch: {flops_per_launch}",
+        f"avg_duration_us: {avg_ns / 1e3:.2f}",
+        f"achieved_tflops: {tflops:.1f}",
+        f"peak_tflops_bf16_dense: {peak_tflops}",
+        f"mfma_utilisation: {tflops / peak_tflops:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path):
     """key: value pairs of a traffic summary (comments skipped)."""
     out = {}
@@ -135,7 +166,17 @@ def main(argv=None):
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--alg-bytes", type=int, required=True)
     t.add_argument("--commands", action="append", default=[])
+    m = sub.add_parser("mfma")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--counters", required=True)
+    m.add_argument("--stats", required=True)
+    m.add_argument("--flops", type=int, required=True)
+    m.add_argument("--peak-tflops", type=float, default=2500.0)
+    m.add_argument("--commands", action="append", default=[])
     a = ap.parse_args(argv)
+    if a.mode == "mfma":
+        sys.stdout.write(mfma_text(a.kernel, a.counters, a.stats, a.flops, a.peak_tflops, a.commands))
+        return
     if a.mode == "stats":
         sys.stdout.write(stats_text(a.csv, a.command))
     else:
