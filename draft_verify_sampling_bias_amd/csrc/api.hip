@@ -159,6 +159,10 @@ int dspark_verify(const dspark_verify_args* a) {
   vp.rs_info = ws_at<int32_t>(a->workspace, plan.rsinfo_off);
   vp.rs_stats = ws_at<float>(a->workspace, plan.rsstats_off);
   vp.rpart = ws_at<float>(a->workspace, plan.rpart_off);
+  if (plan.seg_rows == kSegWide) {
+    vp.rs_count = ws_at<int32_t>(a->workspace, plan.rcount_off);
+    vp.rs_list = ws_at<ResidualEntry>(a->workspace, plan.rlist_off);
+  }
 
   st = hip_status(launch_verify_stats(vp, s));
   if (st != DSPARK_OK) return st;
@@ -177,6 +181,8 @@ int dspark_verify(const dspark_verify_args* a) {
   tp.temp = a->temp;
   tp.rs_info = vp.rs_info;
   tp.rs_stats = vp.rs_stats;
+  tp.rs_count = vp.rs_count;
+  tp.rs_list = vp.rs_list;
   tp.U = a->U;
   tp.target = a->target;
   tp.u_rows = static_cast<int64_t>(a->R) * a->gamma;

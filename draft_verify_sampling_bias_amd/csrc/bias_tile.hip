@@ -424,6 +424,459 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p)
 }
 
 // ---------------------------------------------------------------------------
+// 64-row path (bf16 weights, R > 64): the product is a real GEMM
+// ---------------------------------------------------------------------------
+// A workgroup of four wavefronts owns 256 vocabulary rows; wavefront w keeps
+// W2 rows [64 (4 blockIdx + w), +64) in registers for the whole launch, as
+// four 16-row MFMA A blocks, so that every B fragment read from LDS feeds
+// four MFMAs.  The requests stream through in chunks of 16 (one MFMA column
+// block): while chunk c computes, the W1 rows of chunk c + 2 and the U (and
+// target) values of chunk c + 2 are in flight in registers; H goes through a
+// two-stage LDS ring with one barrier per chunk.  Per-request values come
+// from an LDS window of 256 requests, loaded 16 chunks ahead.  Residual mode
+// visits only the requests listed by verify_finish.
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt not waited for
+constexpr int kVmcntZero = 0x0F70;
+constexpr int kWideWin = 256;                          // requests per window (one per thread)
+constexpr int kWideWinChunks = kWideWin / kWideChunk;  // chunks per window
+
+template <bool RESID>
+struct WideReq;
+template <>
+struct WideReq<false> {
+  int n, prev;  // record row, previous token
+  float c;      // log2(e) / T, 0 for greedy
+};
+template <>
+struct WideReq<true> {
+  int n, prev, urow, trow;
+  float c, Mq, iZq, Mp, iZp;
+};
+
+// A request's raw inputs, held in registers between the window's load and
+// its store into LDS (every derived value is computed at the store, so no
+// instruction touches the loads early).
+template <bool RESID>
+struct WideRaw;
+template <>
+struct WideRaw<false> {
+  int prev;
+  float T;
+};
+template <>
+struct WideRaw<true> {
+  u32x4_t a, b;  // (n, prev, U row, target row), (Mq, Zq, Mp, Zp) of one ResidualEntry
+  float T;
+};
+
+template <bool RESID>
+__device__ __forceinline__ void wide_raw_load(const TileParams& p, int i, int cnt, WideRaw<RESID>& r) {
+  const int j = min(i, cnt - 1);
+  if constexpr (!RESID) {
+    r.prev = p.prev_base[static_cast<int64_t>(j) * p.prev_stride];
+    r.T = p.temp[j];
+  } else {
+    const u32x4_t* e = reinterpret_cast<const u32x4_t*>(p.rs_list + j);
+    r.a = e[0];
+    r.b = e[1];
+    r.T = p.rs_list[j].T;
+  }
+}
+
+template <bool RESID>
+__device__ __forceinline__ void wide_raw_store(const TileParams& p, int i, int cnt, const WideRaw<RESID>& r,
+                                               WideReq<RESID>& q) {
+  // slots past the last request write their records into padding rows
+  const int pad_row = p.R + (i & (kWideChunk - 1));
+  if constexpr (!RESID) {
+    q.n = (i < cnt) ? i : pad_row;
+    q.prev = clampi(r.prev, 0, p.V - 1);
+    q.c = temp_scale(r.T);
+  } else {
+    q.n = (i < cnt) ? clampi(static_cast<int>(r.a[0]), 0, p.R - 1) : pad_row;
+    q.prev = clampi(static_cast<int>(r.a[1]), 0, p.V - 1);
+    q.urow = static_cast<int>(min(max(static_cast<int64_t>(static_cast<int>(r.a[2])), int64_t{0}), p.u_rows - 1));
+    q.trow = static_cast<int>(min(max(static_cast<int64_t>(static_cast<int>(r.a[3])), int64_t{0}), p.t_rows - 1));
+    q.c = temp_scale(r.T);
+    q.Mq = __uint_as_float(r.b[0]);
+    q.iZq = 1.0f / __uint_as_float(r.b[1]);
+    q.Mp = __uint_as_float(r.b[2]);
+    q.iZp = 1.0f / __uint_as_float(r.b[3]);
+  }
+}
+
+// W1 rows of one chunk in flight: 16-byte piece q = tid + 256 j is group
+// q % (4 KS) of row q / (4 KS); pieces past the 16 rows go to a dummy row.
+template <int KS>
+struct WideH {
+  static constexpr int kGroups = 4 * KS;  // 16-byte groups per LDS row
+  static constexpr int kPer = (kWideChunk * kGroups + 255) / 256;
+  u32x4_t v[kPer];
+};
+
+template <int KS, bool RESID>
+__device__ __forceinline__ void wide_h_issue(const TileParams& p, const WideReq<RESID>* win, int cw, WideH<KS>& h) {
+  constexpr int G = WideH<KS>::kGroups;
+  const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
+#pragma unroll
+  for (int j = 0; j < WideH<KS>::kPer; ++j) {
+    const int q = static_cast<int>(threadIdx.x) + j * 256;
+    const int r = min(q / G, kWideChunk - 1), g = q % G;
+    const int prev = win[cw * kWideChunk + r].prev;
+    h.v[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(prev) * p.rank + min(g * 8, p.rank - 8));
+  }
+}
+
+// Stores a chunk's W1 rows into an LDS stage; pieces past the 16 rows land
+// in row 16.  Groups past the rank hold the row's last real weights again
+// (clamped loads): the W2 fragments are zero there, so they add 0.
+template <int KS>
+__device__ __forceinline__ void wide_h_commit(const WideH<KS>& h, uint16_t* stage) {
+  constexpr int G = WideH<KS>::kGroups;
+  constexpr int RS = KS * 32 + 8;
+#pragma unroll
+  for (int j = 0; j < WideH<KS>::kPer; ++j) {
+    const int q = static_cast<int>(threadIdx.x) + j * 256;
+    const int r = min(q / G, kWideChunk), g = q % G;
+    *reinterpret_cast<u32x4_t*>(stage + r * RS + g * 8) = h.v[j];
+  }
+}
+
+// Epilogue inputs of one chunk for this lane's request (16 c + (lane & 15)):
+// U (and target) values of rows vw + 16 b + 4 (lane >> 4) .. +4, b < 4.
+template <bool RESID>
+struct WideU {
+  f32x4_t u[4];
+  f32x4_t t[RESID ? 4 : 1];
+  int n;
+  float c;
+  float Mq, iZq, Mp, iZp;  // residual mode
+};
+
+template <bool RESID, bool VEC4>
+__device__ __forceinline__ void wide_u_issue(const TileParams& p, const WideReq<RESID>* win, int chunk, int cw,
+                                             int vw, int lane, WideU<RESID>& f) {
+  const int l16 = lane & 15, kq = lane >> 4;
+  const WideReq<RESID>& q = win[cw * kWideChunk + l16];
+  f.n = q.n;
+  f.c = q.c;
+  const float* urow;
+  if constexpr (!RESID) {
+    urow = p.U_base + static_cast<int64_t>(min(chunk * kWideChunk + l16, p.R - 1)) * p.U_stride;
+  } else {
+    urow = p.U + static_cast<int64_t>(q.urow) * p.V;
+    f.Mq = q.Mq;
+    f.iZq = q.iZq;
+    f.Mp = q.Mp;
+    f.iZp = q.iZp;
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) f.u[b] = load4<VEC4>(urow, vw + 16 * b + 4 * kq, p.V);
+  if constexpr (RESID) {
+    const float* trow = p.target + static_cast<int64_t>(q.trow) * p.V;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f.t[b] = load4<VEC4>(trow, vw + 16 * b + 4 * kq, p.V);
+  }
+}
+
+// This wavefront's W2 rows vw + 16 b + (lane & 15), k = 32 ks + 8 (lane >> 4)
+// .. +8, the MFMA A fragments (addresses clamped into the row; the groups
+// past the rank are zeroed by wide_w2_ready).
+template <int KS>
+__device__ __forceinline__ void wide_w2_load(const TileParams& p, int vw, int lane, u32x4_t (&w)[4][KS]) {
+  const int l16 = lane & 15, kq = lane >> 4;
+  const uint16_t* w2 = static_cast<const uint16_t*>(p.W2);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int v = min(vw + 16 * b + l16, p.V - 1);
+      w[b][ks] = *reinterpret_cast<const u32x4_t*>(w2 + static_cast<int64_t>(v) * p.rank +
+                                                   min(ks * 32 + kq * 8, p.rank - 8));
+    }
+}
+
+// Called once the prologue's other loads are issued: zeroes the groups past
+// the rank (only the last k-step can hold any) and pins every fragment to the
+// accumulation registers, the operand form the MFMA reads directly, which
+// leaves the architectural registers to the stream.
+template <int KS>
+__device__ __forceinline__ void wide_w2_ready(int rank, int lane, u32x4_t (&w)[4][KS]) {
+  const bool past = (KS - 1) * 32 + (lane >> 4) * 8 >= rank;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) w[b][KS - 1] = past ? u32x4_t{0u, 0u, 0u, 0u} : w[b][KS - 1];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) asm volatile("" : "+a"(w[b][ks]));
+}
+
+// Base of the exponentials of a 64-row record: its maximum, or 0 when every
+// row is masked (-inf), so that no entry computes -inf - (-inf).  A wholly
+// masked segment then records the sum 0; its weight 2^((max - M) / T) in
+// any finite-maximum total is 0 either way.  (A greedy request's sum is
+// never used.)
+__device__ __forceinline__ float wide_exp_base(float m) { return (m == -INFINITY) ? 0.f : m; }
+
+// One chunk's record for this lane's request over the wavefront's 64 rows:
+// 16 values in the lane, then the four lanes (lane & 15) + 16 j.
+template <bool RESID>
+__device__ __forceinline__ void wide_epilogue(const TileParams& p, int seg, int lane, const WideU<RESID>& f,
+                                              const f32x4_t (&acc)[4], bool live) {
+  const int kq = lane >> 4;
+  const int V = p.V;
+  const int vb = seg * kSegWide + 4 * kq;
+  float x, y;
+  if constexpr (!RESID) {
+    float s[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[4 * b + i] = (vb + 16 * b + i < V) ? acc[b][i] + f.u[b][i] : -INFINITY;
+    float m = s[0];
+    int im = vb;
+#pragma unroll
+    for (int e = 1; e < 16; ++e) {
+      const bool gt = s[e] > m;
+      m = gt ? s[e] : m;
+      im = gt ? vb + 16 * (e >> 2) + (e & 3) : im;
+    }
+    quad_amax(m, im);
+    const float mg = wide_exp_base(m);
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) z += exp2_hw((s[e] - mg) * f.c);
+    z = quad_sum(z);
+    x = m;
+    y = (f.c > 0.f) ? z : __int_as_float(im);
+  } else {
+    float w = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float qq = exp2_hw((acc[b][i] + f.u[b][i] - f.Mq) * f.c) * f.iZq;
+        const float pp = exp2_hw((f.t[b][i] - f.Mp) * f.c) * f.iZp;
+        const float d = fmaxf(pp - qq, 0.f);
+        w += __int_as_float(__float_as_int(d) & -static_cast<int>(vb + 16 * b + i < V));
+      }
+    w = quad_sum(w);
+    x = 0.f;
+    y = w;
+  }
+  // segments past the vocabulary (last workgroup), and the pipeline's
+  // empty first slot, store into the dummy row
+  const bool in_v = live && seg < p.n_seg;
+  const int64_t row = in_v ? f.n : p.R + kWideChunk;
+  const int col = in_v ? seg : 0;
+  reinterpret_cast<float2*>(p.part)[row * p.n_seg + col] = make_float2(x, y);
+}
+
+// The same epilogue cut into small steps, so that its vector instructions
+// can be placed one step after each MFMA of the next chunk (step t is a
+// compile-time constant at every call).  Draft: steps 0-15 form logit k = t
+// (after step 15 the inputs may be overwritten), 16-31 fold entry t - 16
+// into the maximum and lowest argmax, 32 combines the four lanes, 33-48 add
+// exponential t - 33, 49 combines and stores.  Residual: step 3 k adds entry
+// k (the two steps after it are empty), step 48 combines and stores.  The
+// arithmetic, and its order, is that of wide_epilogue.
+constexpr int kEpiSteps = 50;
+
+template <bool RESID>
+struct WideEpi {
+  float s[RESID ? 1 : 16];
+  float m, mg, z, c;
+  int im, n;
+};
+
+template <bool RESID>
+__device__ __forceinline__ void wide_epi_step(int t, const TileParams& p, int seg, int lane, const WideU<RESID>& f,
+                                              const f32x4_t (&acc)[4], bool live, WideEpi<RESID>& e) {
+  const int V = p.V;
+  const int vb = seg * kSegWide + 4 * (lane >> 4);
+  auto store = [&](float x, float y) {
+    const bool in_v = live && seg < p.n_seg;
+    const int64_t row = in_v ? e.n : p.R + kWideChunk;
+    const int col = in_v ? seg : 0;
+    reinterpret_cast<float2*>(p.part)[row * p.n_seg + col] = make_float2(x, y);
+  };
+  if constexpr (!RESID) {
+    if (t < 16) {
+      if (t == 0) {
+        e.c = f.c;
+        e.n = f.n;
+      }
+      const int b = t >> 2, i = t & 3;
+      e.s[t] = (vb + 16 * b + i < V) ? acc[b][i] + f.u[b][i] : -INFINITY;
+    } else if (t < 32) {
+      const int k = t - 16;
+      if (k == 0) {
+        e.m = e.s[0];
+        e.im = vb;
+      } else {
+        const bool gt = e.s[k] > e.m;
+        e.m = gt ? e.s[k] : e.m;
+        e.im = gt ? vb + 16 * (k >> 2) + (k & 3) : e.im;
+      }
+    } else if (t == 32) {
+      quad_amax(e.m, e.im);
+      e.mg = wide_exp_base(e.m);
+      e.z = 0.f;
+    } else if (t < 49) {
+      e.z += exp2_hw((e.s[t - 33] - e.mg) * e.c);
+    } else if (t == 49) {
+      store(e.m, (e.c > 0.f) ? quad_sum(e.z) : __int_as_float(e.im));
+    }
+  } else {
+    if (t < 48 && t % 3 == 0) {
+      const int k = t / 3, b = k >> 2, i = k & 3;
+      if (k == 0) {
+        e.z = 0.f;
+        e.n = f.n;
+      }
+      const float qq = exp2_hw((acc[b][i] + f.u[b][i] - f.Mq) * f.c) * f.iZq;
+      const float pp = exp2_hw((f.t[b][i] - f.Mp) * f.c) * f.iZp;
+      const float d = fmaxf(pp - qq, 0.f);
+      e.z += __int_as_float(__float_as_int(d) & -static_cast<int>(vb + 16 * b + i < V));
+    } else if (t == 48) {
+      store(0.f, quad_sum(e.z));
+    }
+  }
+}
+
+template <int KS, bool RESID, bool VEC4>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) bias_seg64(TileParams p) {
+  constexpr int RS = KS * 32 + 8;
+  constexpr int kStage = (kWideChunk + 1) * RS;  // 16 rows + the dummy row
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[2 * kStage];
+  __shared__ WideReq<RESID> win[2][kWideWin];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cnt = RESID ? min(max(p.rs_count[0], 0), p.R) : p.R;
+  if (cnt == 0) return;
+  const int n_chunks = (cnt + kWideChunk - 1) / kWideChunk;
+  const int n_win = (n_chunks + kWideWinChunks - 1) / kWideWinChunks;
+  const int seg = blockIdx.x * 4 + wave;
+  const int vw = seg * kSegWide;
+  const int rank = p.rank;
+
+  // window 0 (its loads are waited for at once: nothing else is in flight yet)
+  WideRaw<RESID> raw;
+  wide_raw_load<RESID>(p, tid, cnt, raw);
+  wide_raw_store<RESID>(p, tid, cnt, raw, win[0][tid]);
+  lds_barrier();
+  // the first two chunks' W1 rows, then this wavefront's W2 rows, then the
+  // first chunk's U values (the first H wait does not wait for W2)
+  WideH<KS> h0, h1;
+  wide_h_issue<KS, RESID>(p, win[0], 0, h0);
+  wide_h_issue<KS, RESID>(p, win[0], min(1, n_chunks - 1), h1);
+  u32x4_t w[4][KS];
+  wide_w2_load<KS>(p, vw, lane, w);
+  // ua / ub: epilogue inputs of the odd / even chunks; ua starts empty (the
+  // first iteration's epilogue has no chunk: it stores into the dummy row)
+  WideU<RESID> ua, ub;
+  ua.n = 0;
+  ua.c = 0.f;
+  ua.Mq = ua.iZq = ua.Mp = ua.iZp = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) ua.u[b] = ua.t[RESID ? b : 0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  wide_u_issue<RESID, VEC4>(p, win[0], 0, 0, vw, lane, ub);
+  wide_h_commit<KS>(h0, Hs);
+  // every load of the prologue (W2 included) has landed before the loop:
+  // the loop's own waits then follow its steady state only
+  wide_w2_ready<KS>(rank, lane, w);
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);
+  lds_barrier();
+
+  // Iteration c (LDS stage c & 1) runs chunk c's MFMAs and, interleaved with
+  // them, chunk c - 1's epilogue (its accumulators and inputs are ready), so
+  // the matrix cores and the vector ALUs work at once.  ha receives chunk
+  // c + 2's W1 rows, hb holds chunk c + 1's (stored into stage (c + 1) & 1
+  // at the end); uf holds chunk c - 1's epilogue inputs and then receives
+  // chunk c + 1's.  Chunks past the last re-load the last one (never stored
+  // differently), so every trip issues the same loads.
+  //
+  // Work besides the MFMAs runs in 64 sub-slots: sub-slot j right after
+  // MFMA j * 4 KS / 64 of the iteration (one per MFMA at rank 512), so its
+  // vector instructions issue while that MFMA executes.
+  //   0        row indices of chunk c + 2 (LDS)    2   its W1 rows (loads)
+  //   4-53     epilogue steps 0-49 of chunk c - 1
+  //   kUSlot   chunk c + 1's epilogue inputs (after the steps that read the
+  //            previous ones)
+  //   60       chunk c + 1's W1 rows into LDS
+  constexpr int kUSlot = RESID ? 4 + 49 : 4 + 16;
+  constexpr int kPerH = WideH<KS>::kPer, kG = WideH<KS>::kGroups;
+  constexpr int kSubPerMfma = 64 / (4 * KS);
+  f32x4_t acc0[4], acc1[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc1[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto iter = [&](int c, int s, WideH<KS>& ha, WideH<KS>& hb, WideU<RESID>& uf, f32x4_t(&acc)[4],
+                  const f32x4_t(&acc_prev)[4]) {
+    const int c2 = min(c + 2, n_chunks - 1), c1 = min(c + 1, n_chunks - 1);
+    const WideReq<RESID>* win2 = win[(c2 / kWideWinChunks) & 1] + (c2 % kWideWinChunks) * kWideChunk;
+    const WideReq<RESID>* win1 = win[(c1 / kWideWinChunks) & 1];
+    const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
+    int hp[kPerH];
+    WideEpi<RESID> ep;
+    auto side = [&](int j) {
+      if (j == 0) {
+#pragma unroll
+        for (int q = 0; q < kPerH; ++q) hp[q] = win2[min((tid + q * 256) / kG, kWideChunk - 1)].prev;
+      } else if (j == 2) {
+#pragma unroll
+        for (int q = 0; q < kPerH; ++q) {
+          const int g = (tid + q * 256) % kG;
+          ha.v[q] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(hp[q]) * rank + min(g * 8, rank - 8));
+        }
+      }
+      if (j >= 4 && j < 4 + kEpiSteps) wide_epi_step<RESID>(j - 4, p, seg, lane, uf, acc_prev, c > 0, ep);
+      if (j == kUSlot) wide_u_issue<RESID, VEC4>(p, win1, c1, c1 % kWideWinChunks, vw, lane, uf);
+      if (j == 60) wide_h_commit<KS>(hb, Hs + (s ^ 1) * kStage);
+    };
+    const uint16_t* hbase = Hs + s * kStage + (lane & 15) * RS + (lane >> 4) * 8;
+    u32x4_t bq = *reinterpret_cast<const u32x4_t*>(hbase);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t bn = bq;
+      if (ks + 1 < KS) bn = *reinterpret_cast<const u32x4_t*>(hbase + (ks + 1) * 32);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[b][ks]),
+                                                         __builtin_bit_cast(bf16x8_t, bq), acc[b], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < kSubPerMfma; ++t) side((4 * ks + b) * kSubPerMfma + t);
+        // nothing moves across: each sub-slot's work issues behind its MFMA
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      bq = bn;
+    }
+    // window wn + 1 is loaded at the window's first chunk and stored at its
+    // ninth (its previous occupant, window wn - 1, is no longer read)
+    const int wn = c / kWideWinChunks, cw = c % kWideWinChunks;
+    if (wn + 1 < n_win) {
+      if (cw == 0) wide_raw_load<RESID>(p, (wn + 1) * kWideWin + tid, cnt, raw);
+      if (cw == kWideWinChunks / 2)
+        wide_raw_store<RESID>(p, (wn + 1) * kWideWin + tid, cnt, raw, win[(wn + 1) & 1][tid]);
+    }
+    lds_barrier();
+  };
+  // whole pairs only (a loop exit between the two halves would give the
+  // compiler a path that skips the second half's loads, and every wait in
+  // the loop would be computed for it); with an odd count the last trip's
+  // second half recomputes the last chunk, storing the same records again
+  int c = 0;
+  do {
+    iter(c, 0, h0, h1, ua, acc0, acc1);
+    iter(c + 1, 1, h1, h0, ub, acc1, acc0);
+    c += 2;
+  } while (c < n_chunks);
+  // the last trip's second chunk
+  wide_epilogue<RESID>(p, seg, lane, ua, acc1, true);
+}
+
+// ---------------------------------------------------------------------------
 // 32-row paths: one wavefront = one 32-row segment, requests in chunks
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int acc32_row(int i, int khalf) { return 8 * (i >> 2) + 4 * khalf + (i & 3); }
@@ -660,6 +1113,17 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     return hipGetLastError();
   }
   const dim3 grid((p.n_seg + 3) / 4), block(256);
+  if (p.seg_rows == kSegWide) {
+    if (p.rank <= 64)
+      launch(bias_seg64<2, RESID, VEC4>, grid, block, s, e0, e1, p);
+    else if (p.rank <= 128)
+      launch(bias_seg64<4, RESID, VEC4>, grid, block, s, e0, e1, p);
+    else if (p.rank <= 256)
+      launch(bias_seg64<8, RESID, VEC4>, grid, block, s, e0, e1, p);
+    else
+      launch(bias_seg64<16, RESID, VEC4>, grid, block, s, e0, e1, p);
+    return hipGetLastError();
+  }
   if (p.rank <= 64)
     launch(bias_seg32<4, RESID, VEC4>, grid, block, s, e0, e1, p);
   else if (p.rank <= 128)
@@ -679,6 +1143,10 @@ hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int 
   if (residual && (p.u_rows < 1 || p.t_rows < 1)) return hipErrorInvalidValue;
   // the 16-row path holds at most kSmallMaxR requests (LDS tile, record rows)
   if (p.seg_rows == kSegSmall && (p.R > kSmallMaxR || wdtype != DSPARK_W_BF16)) return hipErrorInvalidValue;
+  // the 64-row path: bf16 weights; residual mode walks the verify list
+  if (p.seg_rows == kSegWide &&
+      (wdtype != DSPARK_W_BF16 || (residual && (p.rs_count == nullptr || p.rs_list == nullptr))))
+    return hipErrorInvalidValue;
   const bool vec4 = (p.V % 4) == 0;
   if (residual)
     return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s, ev0, ev1)

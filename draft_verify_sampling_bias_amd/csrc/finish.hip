@@ -23,13 +23,17 @@ namespace dspark {
 namespace {
 
 // Rescan of one record segment: thread group i (256 / seg_rows lanes) owns
-// row v0 + i (16-row segments: 16 lanes per row; 32-row: 8).
-__device__ __forceinline__ int lanes_log2(int seg_rows) { return seg_rows == kSegSmall ? 4 : 3; }
+// row v0 + i (16-row segments: 16 lanes per row; 32-row: 8; 64-row: 4).
+__device__ __forceinline__ int lanes_log2(int seg_rows) {
+  return seg_rows == kSegSmall ? 4 : (seg_rows == kSegLarge ? 3 : 2);
+}
 constexpr int kMaxSegRows = 64;
 
-// Segment records of one request staged in LDS (128 KiB: 16384 records, i.e.
-// V up to 262144 with 16-row or 524288 with 32-row segments); larger
+// Segment records of one request staged in LDS: up to 2048 records (16 KiB,
+// several workgroups per CU) or 16384 (128 KiB, i.e. V up to 262144 with
+// 16-row, 524288 with 32-row or 1048576 with 64-row segments); larger
 // vocabularies read the records from global memory instead.
+constexpr int kStageSmall = 2048;
 constexpr int kStageRecs = 16384;
 constexpr int kStageBatch = 40;  // loads in flight per thread while staging
 
@@ -109,12 +113,13 @@ __device__ __forceinline__ void copy_next_h(const FinishParams& p, int n, int y)
   }
 }
 
-template <typename WT, bool STAGED>
+template <typename WT, int STAGE>
 __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
+  constexpr bool STAGED = STAGE > 0;
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh;
   __shared__ float e64[kMaxSegRows], s64[kMaxSegRows];
-  __shared__ float2 srec[STAGED ? kStageRecs : 1];
+  __shared__ float2 srec[STAGED ? STAGE : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int V = p.V, n_seg = p.n_seg;
   const float2* gfine = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
@@ -197,14 +202,15 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   }
 }
 
-template <typename WT, bool STAGED>
+template <typename WT, int STAGE>
 __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
+  constexpr bool STAGED = STAGE > 0;
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh2;
   __shared__ ChunkScratch sh;
   __shared__ float e64[kMaxSegRows];
   __shared__ int s_out;
-  __shared__ float2 srec[STAGED ? kStageRecs : 1];
+  __shared__ float2 srec[STAGED ? STAGE : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int32_t* info = p.rs_info + 4 * static_cast<int64_t>(n);
   if (info[0] == 0) return;
@@ -272,36 +278,44 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
 
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  const bool staged = p.n_seg <= kStageRecs;
   const dim3 grid(p.R), block(256);
+  const int stage = p.n_seg <= kStageSmall ? kStageSmall : (p.n_seg <= kStageRecs ? kStageRecs : 0);
   if (wdtype == DSPARK_W_BF16) {
-    if (staged)
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, true>), grid, block, 0, s, p);
+    if (stage == kStageSmall)
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageSmall>), grid, block, 0, s, p);
+    else if (stage == kStageRecs)
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageRecs>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, 0>), grid, block, 0, s, p);
   } else {
-    if (staged)
-      hipLaunchKernelGGL((draft_finish_kernel<float, true>), grid, block, 0, s, p);
+    if (stage == kStageSmall)
+      hipLaunchKernelGGL((draft_finish_kernel<float, kStageSmall>), grid, block, 0, s, p);
+    else if (stage == kStageRecs)
+      hipLaunchKernelGGL((draft_finish_kernel<float, kStageRecs>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((draft_finish_kernel<float, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<float, 0>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  const bool staged = p.n_seg <= kStageRecs;
   const dim3 grid(p.R), block(256);
+  const int stage = p.n_seg <= kStageSmall ? kStageSmall : (p.n_seg <= kStageRecs ? kStageRecs : 0);
   if (wdtype == DSPARK_W_BF16) {
-    if (staged)
-      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, true>), grid, block, 0, s, p);
+    if (stage == kStageSmall)
+      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, kStageSmall>), grid, block, 0, s, p);
+    else if (stage == kStageRecs)
+      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, kStageRecs>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, 0>), grid, block, 0, s, p);
   } else {
-    if (staged)
-      hipLaunchKernelGGL((residual_finish_kernel<float, true>), grid, block, 0, s, p);
+    if (stage == kStageSmall)
+      hipLaunchKernelGGL((residual_finish_kernel<float, kStageSmall>), grid, block, 0, s, p);
+    else if (stage == kStageRecs)
+      hipLaunchKernelGGL((residual_finish_kernel<float, kStageRecs>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((residual_finish_kernel<float, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((residual_finish_kernel<float, 0>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

@@ -9,6 +9,16 @@
 
 namespace dspark {
 
+// A request that rejected a sampled draft, as handed from verify_finish to
+// the residual pass of the 64-row path (which visits only these requests).
+struct ResidualEntry {
+  int32_t n, prev, urow, trow;   // request, previous token, U row, target row
+  float Mq, Zq, Mp, Zp;          // softmax statistics of q and p at that position
+  float T;                       // temperature
+  float pad[3];
+};
+static_assert(sizeof(ResidualEntry) == 48, "ResidualEntry layout");
+
 // One launch of the fused Markov-bias + softmax-statistics kernel.
 //   draft mode:    request n uses prev = prev_base[n * prev_stride] and the
 //                  base-logit row U_base + n * U_stride; writes per (n, segment)
@@ -17,6 +27,8 @@ namespace dspark {
 //   residual mode: request n takes (flag, prev, U row, target row) from
 //                  rs_info and (Mq, Zq, Mp, Zp) from rs_stats and writes
 //                  (0, sum of max(0, p - q)) per segment; flag 0 => skipped.
+//                  The 64-row path visits only the rs_count[0] entries of
+//                  rs_list instead.
 struct TileParams {
   const void* W1;
   const void* W2;
@@ -29,6 +41,8 @@ struct TileParams {
   const float* temp;
   const int32_t* rs_info;
   const float* rs_stats;
+  const int32_t* rs_count;          // 64-row path, residual mode
+  const ResidualEntry* rs_list;
   const float* U;        // [u_rows = R * gamma, V] (residual mode)
   const float* target;   // [t_rows = n_rows, V]    (residual mode)
   int64_t u_rows, t_rows;
@@ -79,6 +93,10 @@ struct VerifyParams {
   int32_t* rs_info;  // [R][4]
   float* rs_stats;   // [R][4]
   float* rpart;      // [record_rows][n_seg][kRecFloats] residual segment records
+  // 64-row path (else null): verify_stats zeroes the count, verify_finish
+  // appends every request that needs the residual pass
+  int32_t* rs_count;
+  ResidualEntry* rs_list;  // [R]
 };
 
 // ev0 / ev1 (optional): events attached to the kernel's dispatch, recorded

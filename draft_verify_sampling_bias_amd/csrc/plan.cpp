@@ -80,6 +80,12 @@ int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
   const std::size_t rows = static_cast<std::size_t>(record_rows(plan->seg_rows, a->R));
   plan->rpart_off = off;
   off = round_up(off + rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
+  if (plan->seg_rows == kSegWide) {
+    plan->rcount_off = off;
+    off = round_up(off + sizeof(int32_t), kWsAlign);
+    plan->rlist_off = off;
+    off = round_up(off + static_cast<std::size_t>(a->R) * kResidualEntryBytes, kWsAlign);
+  }
   plan->total = off;
   return DSPARK_OK;
 }

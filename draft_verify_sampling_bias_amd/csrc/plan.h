@@ -10,18 +10,27 @@
 namespace dspark {
 
 // The fused bias + softmax kernels reduce each request's logits over
-// vocabulary segments of 16 rows (bf16 weights, R <= 64: one 16x16x32 MFMA
-// row block per wavefront) or 32 rows (otherwise: 32x32 MFMA row blocks) to
-// one record of two floats per (request, segment).
+// vocabulary segments to one record of two floats per (request, segment):
+//   16 rows  bf16 weights, R <= 64 (one 16x16x32 MFMA row block per wavefront)
+//   64 rows  bf16 weights, R > 64 (four row blocks held by one wavefront)
+//   32 rows  fp32 weights (32x32x2 MFMA row blocks)
 constexpr int kSegSmall = 16;
 constexpr int kSegLarge = 32;
+constexpr int kSegWide = 64;
 constexpr int kSmallMaxR = 64;               // requests held by the 16-row path
+constexpr int kWideChunk = 16;               // requests per chunk of the 64-row path
 constexpr int kRecFloats = 2;                // floats per (request, segment) record
-// Record arrays of the 16-row path hold kSmallMaxR request rows whatever R
-// is: every lane of the kernel stores its record unconditionally (rows of
-// absent requests are padding and never read), which keeps divergent
-// branches out of the kernel's streaming loop.
-inline int record_rows(int seg_rows, int R) { return seg_rows == kSegSmall ? kSmallMaxR : R; }
+// Record arrays hold more rows than requests where the kernels store
+// unconditionally (which keeps divergent branches out of their streaming
+// loops; the extra rows are never read):
+//   16-row path: kSmallMaxR rows whatever R is;
+//   64-row path: R + 16 rows catch the requests past R of the last chunk,
+//                and row R + 16 the segments past the vocabulary of the
+//                last workgroup.
+constexpr int kWidePadRows = kWideChunk + 1;
+inline int record_rows(int seg_rows, int R) {
+  return seg_rows == kSegSmall ? kSmallMaxR : (seg_rows == kSegWide ? R + kWidePadRows : R);
+}
 
 #if defined(__HIPCC__)
 #define DSPARK_HD __host__ __device__
@@ -42,7 +51,8 @@ constexpr std::size_t kWsAlign = 256;
 
 // Rows per segment for a batch of R requests with weights of type wdtype.
 inline int seg_rows_for(int32_t R, int32_t wdtype) {
-  return (wdtype == DSPARK_W_BF16 && R <= kSmallMaxR) ? kSegSmall : kSegLarge;
+  if (wdtype != DSPARK_W_BF16) return kSegLarge;
+  return R <= kSmallMaxR ? kSegSmall : kSegWide;
 }
 
 struct DraftPlan {
@@ -61,8 +71,13 @@ struct VerifyPlan {
   std::size_t rsinfo_off = 0;   // [R][4] int32: flag, prev, U row, target row
   std::size_t rsstats_off = 0;  // [R][4] float: Mq, 1/Zq, Mp, 1/Zp
   std::size_t rpart_off = 0;    // [record_rows][n_seg][kRecFloats] float
+  // 64-row path: the requests that need the residual pass, compacted
+  std::size_t rcount_off = 0;   // int32 count
+  std::size_t rlist_off = 0;    // [R] ResidualEntry (48 bytes)
   std::size_t total = 0;
 };
+
+constexpr std::size_t kResidualEntryBytes = 48;
 
 // Size checks shared by draft and verify.  Returns a dspark_status.
 int check_dims(int32_t R, int32_t gamma, int32_t V, int32_t rank, int32_t wdtype);

@@ -49,6 +49,8 @@ template <bool VEC4>
 __global__ void __launch_bounds__(256) verify_stats_kernel(VerifyParams p) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63;
+  // the residual list is rebuilt by verify_finish, which runs after this kernel
+  if (p.rs_count != nullptr && (blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *p.rs_count = 0;
   const int ch = blockIdx.z * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   if (ch >= p.n_chunks) return;  // wavefront-uniform; no workgroup barrier follows
   const int64_t lo = min(max(static_cast<int64_t>(p.row_offsets[r]), int64_t{0}), p.n_rows);
@@ -205,6 +207,23 @@ __global__ void __launch_bounds__(256) verify_finish_kernel(VerifyParams p) {
         st[1] = q1;
         st[2] = rM[nacc];
         st[3] = rZ[nacc];
+        if (p.rs_list != nullptr) {
+          // slot order varies from run to run; each entry carries its request
+          // and the residual pass writes that request's records only
+          const int slot = atomicAdd(p.rs_count, 1);
+          ResidualEntry e;
+          e.n = n;
+          e.prev = inf[1];
+          e.urow = inf[2];
+          e.trow = inf[3];
+          e.Mq = q0;
+          e.Zq = q1;
+          e.Mp = rM[nacc];
+          e.Zp = rZ[nacc];
+          e.T = T;
+          e.pad[0] = e.pad[1] = e.pad[2] = 0.0f;
+          p.rs_list[slot] = e;
+        }
       }
     }
   }

@@ -60,13 +60,21 @@ def test_workspace_sizes_match_struct_layout():
     # plus, on that path, 64 rows of W1 (bf16) handed from one draft position to the next
     assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1) == up(64 * 9496 * 8) + up(64 * 512 * 2)
     assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1) == up(64 * 63 * 8) + up(64 * 64 * 2)
-    # 32-row segments, one row per request, above 64 requests and for fp32 weights
-    assert ds.draft_workspace_bytes(65, 7, 151936, 512, 1) == up(65 * 4748 * 8)
+    # 64-row segments above 64 requests (bf16): R + 17 record rows (padding
+    # requests of the last chunk, one dummy row)
+    assert ds.draft_workspace_bytes(65, 7, 151936, 512, 1) == up((65 + 17) * 2374 * 8)
+    # 32-row segments, one row per request, for fp32 weights
+    assert ds.draft_workspace_bytes(65, 7, 151936, 512, 0) == up(65 * 4748 * 8)
     assert ds.draft_workspace_bytes(8, 7, 1024, 32, 0) == up(8 * 32 * 8)
     # verify: chunk records (16 bytes per 4096-entry chunk of each target row),
     # residual info/stats, then the residual segment records
     nb = ds.verify_workspace_bytes(64, 7, 151936, 512, 1, 512)
     assert nb == up(512 * 38 * 16) + up(64 * 16) + up(64 * 16) + up(64 * 9496 * 8)
+    # 64-row path: plus the count and list (48 bytes per request) of the
+    # requests that need the residual pass
+    nb = ds.verify_workspace_bytes(256, 5, 129280, 512, 1, 768)
+    assert nb == (up(768 * 32 * 16) + up(256 * 16) + up(256 * 16) + up((256 + 17) * 2020 * 8) + up(4)
+                  + up(256 * 48))
 
 
 def _draft_args(**kw):

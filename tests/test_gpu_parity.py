@@ -46,6 +46,11 @@ SMALL = [
     (19, 4, 5, 5, 16, "bf16", "sampled", "fixed"),           # tiny vocabulary
     (20, 3, 2, 300000, 64, "bf16", "mixed", "fixed"),        # > 16384 segment records: unstaged finish
     (21, 2, 2, 600000, 8, "f32", "temps", "fixed"),          # same on the 32-row path, 147 chunks
+    # 64-row path (bf16, R > 64): request chunks of 16, info windows of 256
+    (25, 300, 3, 3001, 128, "bf16", "mixed", "uniformK"),    # 19 chunks (odd), 2 windows, V % 4 != 0
+    (26, 600, 2, 4160, 256, "bf16", "temps", "fixed"),       # 38 chunks, 3 windows, ragged last window
+    (27, 65, 3, 5000, 512, "bf16", "sampled", "uniformK"),   # one request in the last chunk
+    (28, 97, 2, 1000, 96, "bf16", "sampled", "fixed"),       # rank 96: zero k-groups in the last step
 ]
 
 
@@ -87,12 +92,13 @@ def test_run_twice_bit_identical():
         np.testing.assert_array_equal(g1[k], g2[k], err_msg=k)
 
 
-@pytest.mark.parametrize("R", [20, 70], ids=["seg16", "seg32"])
-def test_masked_vocabulary(R):
-    """Logits of -inf (a vocabulary mask): whole 16/32-row segments and a
+@pytest.mark.parametrize("R,wd", [(20, "bf16"), (70, "bf16"), (40, "f32")], ids=["seg16", "seg64", "seg32"])
+def test_masked_vocabulary(R, wd):
+    """Logits of -inf (a vocabulary mask): whole 16/32/64-row segments and a
     whole 4096-entry target chunk masked, plus scattered entries; the target
     masks some entries the drafter allows, so p = 0 for some drafted tokens."""
-    inp = synth.make_custom(24 + R, R, 4, 9000, 64, policy="mixed", K_mode="uniformK", U_std=3.0, noise_std=1.0)
+    inp = synth.make_custom(24 + R, R, 4, 9000, 64, wdtype=wd, policy="mixed", K_mode="uniformK", U_std=3.0,
+                            noise_std=1.0)
     rng = np.random.default_rng(2024 + R)
     mask = np.zeros(inp.V, bool)
     mask[1000:1600] = True
