@@ -22,7 +22,8 @@ dominant kernel with events around each launch, and a back-to-back loop
 gives the warm-cache rate for context.
 
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the fused Markov
-bias + softmax statistics kernel, bias_seg16), timed with HIP events
+bias + softmax statistics kernel: bias_seg16 for bf16 weights and R <= 64,
+bias_seg64 above, bias_seg32_f32 for fp32 weights), timed with HIP events
 recorded by the library around each launch; `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
 """
@@ -41,7 +42,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft+verify positions/sec (R×gamma) and achieved HBM GB/s at V=151936"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bias_seg16_config3_traffic.txt")
+# committed FETCH_SIZE / WRITE_SIZE summaries of the fused kernel, per workload
+TRAFFIC_FILES = {3: os.path.join(ROOT, "profiles", "bias_seg16_config3_traffic.txt"),
+                 5: os.path.join(ROOT, "profiles", "bias_seg64_config5_traffic.txt")}
+
+
+def tile_kernel(R, wdtype):
+    """Name of the fused bias kernel that a batch runs on."""
+    if wdtype != "bf16":
+        return "bias_seg32_f32"
+    return "bias_seg16" if R <= 64 else "bias_seg64"
 
 
 def algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows):
@@ -52,14 +62,18 @@ def algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows):
     return step, per_pos_tile
 
 
-def load_traffic():
+def load_traffic(config, kernel):
     """HBM bytes per launch of the fused bias kernel from the committed
-    counter summary, or None when it is missing or its kernel sources have
-    changed since the counters were taken."""
+    counter summary of this workload, or None when there is none, it covers
+    another kernel, or its kernel sources have changed since the counters
+    were taken."""
     from draft_verify_sampling_bias_amd import profsum
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get(config)
+    if path is None or not os.path.exists(path):
         return None
-    t = profsum.read_traffic(TRAFFIC_FILE)
+    t = profsum.read_traffic(path)
+    if not t.get("kernel", "").startswith(kernel + "<"):
+        return None
     if t.get("kernel_source_sha256_16") != profsum.tile_source_hash():
         return None
     return int(t["bytes_per_launch"])
@@ -260,6 +274,7 @@ def main():
         warm = dict(value=positions / wall_warm, ms_per_step=wall_warm / K * 1e3)
 
     bytes_step, bytes_tile = algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows)
+    kernel = tile_kernel(R, inp.wdtype)
     ms_per_step = tot_ms / K
     tile_avg_ms = float(np.mean(tile_ms))
     tile_gbps = bytes_tile / (tile_avg_ms / 1e3) / 1e9
@@ -296,13 +311,13 @@ def main():
         "step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(step_ms, [10, 50, 90])],
         "warm_back_to_back": None if warm is None else {k: round(v, 4) for k, v in warm.items()},
         "roofline": {
-            "kernel": "bias_seg16 (fused Markov bias GEMM + softmax statistics, one launch per draft position)",
+            "kernel": f"{kernel} (fused Markov bias GEMM + softmax statistics, one launch per draft position)",
             "bound": "hbm",
             "achieved": round(tile_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(tile_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(),
+            "traffic": load_traffic(args.config, kernel),
             "avg_launch_us": round(tile_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": int(bytes_tile),
         },

@@ -16,13 +16,13 @@
 //
 // Paths:
 //   bias_seg16      bf16 weights, R <= 64.  v_mfma_f32_16x16x32_bf16; each
-//                   wavefront owns 16-row segments; persistent workgroups of
-//                   4 wavefronts (one per CU) gather H once and prefetch the
-//                   next segment's W2 / U fragments while computing the
-//                   current one.
-//   bias_seg32      bf16 weights, R > 64.  v_mfma_f32_32x32x16_bf16; each
-//                   wavefront keeps its 32 rows of W2 in registers while the
-//                   request chunks (64 at a time) stream through LDS.
+//                   wavefront owns 16-row segments; persistent workgroups
+//                   (one per CU) gather H once and prefetch the next
+//                   segment's W2 / U fragments while computing the current
+//                   one.
+//   bias_seg64      bf16 weights, R > 64.  v_mfma_f32_16x16x32_bf16; each
+//                   wavefront keeps its 64 rows of W2 in registers while the
+//                   requests stream through in chunks of 16 (H via LDS).
 //   bias_seg32_f32  fp32 weights.  v_mfma_f32_32x32x2_f32.
 //
 // Operand layouts (wave64).  16x16x32: A lane l holds row (l & 15), 8 k at
@@ -877,7 +877,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 
 // ---------------------------------------------------------------------------
-// 32-row paths: one wavefront = one 32-row segment, requests in chunks
+// 32-row path (fp32 weights): one wavefront = one 32-row segment, requests
+// in chunks of 32
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int acc32_row(int i, int khalf) { return 8 * (i >> 2) + 4 * khalf + (i & 3); }
 
@@ -941,83 +942,6 @@ __device__ __forceinline__ void seg32_epilogue(const TileParams& p, const ReqInf
   if (khalf == 0 && okn) {
     float2* rec = reinterpret_cast<float2*>(p.part) + static_cast<int64_t>(n) * p.n_seg + seg;
     *rec = make_float2(rx, ry);
-  }
-}
-
-constexpr int kNch32 = 64;  // requests per chunk (two 32-wide column blocks)
-
-template <int KREG, bool RESID, bool VEC4>
-__global__ void __launch_bounds__(256) bias_seg32(TileParams p) {
-  constexpr int RS = KREG * 16 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[kNch32 * RS];
-  __shared__ ReqInfo s_ci[kNch32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lrow = lane & 31, khalf = lane >> 5;
-  const int seg = blockIdx.x * 4 + wave;
-  const int V = p.V, rank = p.rank, R = p.R;
-
-  if (RESID) {
-    int any = 0;
-    for (int n = tid; n < R; n += 256) any |= p.rs_info[4 * static_cast<int64_t>(n)];
-    if (!__syncthreads_or(any)) return;
-  }
-  bf16x8_t wf[KREG];
-  {
-    const int v = min(seg * kSegLarge + lrow, V - 1);
-    const uint16_t* w2 = static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(v) * rank;
-#pragma unroll
-    for (int ks = 0; ks < KREG; ++ks) {
-      const int k0 = ks * 16 + khalf * 8;
-      u32x4_t raw = *reinterpret_cast<const u32x4_t*>(w2 + min(k0, rank - 8));
-      if (k0 >= rank) raw = u32x4_t{0u, 0u, 0u, 0u};
-      wf[ks] = __builtin_bit_cast(bf16x8_t, raw);
-    }
-  }
-  for (int n0 = 0; n0 < R; n0 += kNch32) {
-    lds_barrier();  // previous chunk done with LDS
-    if (tid < kNch32) s_ci[tid] = fetch_info(p, n0 + tid, RESID);
-    lds_barrier();
-    {
-      constexpr int G = KREG * 2;
-      const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
-      for (int q = tid; q < kNch32 * G; q += 256) {
-        const int nn = q / G, g = q - nn * G;
-        const ReqInfo& ci = s_ci[nn];
-        u32x4_t val = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(ci.prev) * rank +
-                                                         min(g * 8, rank - 8));
-        if (g * 8 >= rank || !ci.act) val = u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = val;
-      }
-    }
-    float x[2][16];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int nn = nb * 32 + lrow, n = n0 + nn;
-      load16_32<VEC4>(u_row(p, s_ci[nn], n < R ? n : 0, RESID), seg * kSegLarge + 4 * khalf, V, x[nb]);
-    }
-    lds_barrier();  // H ready
-    f32x16_t acc[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      acc[nb] = f32x16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (n0 + nb * 32 < R) {
-        const uint16_t* hrow = &Hs[(nb * 32 + lrow) * RS + khalf * 8];
-#pragma unroll
-        for (int ks = 0; ks < KREG; ++ks) {
-          const u32x4_t braw = *reinterpret_cast<const u32x4_t*>(hrow + ks * 16);
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks], __builtin_bit_cast(bf16x8_t, braw), acc[nb], 0,
-                                                            0, 0);
-        }
-      }
-    }
-    if (seg < p.n_seg) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int nn = nb * 32 + lrow, n = n0 + nn;
-        const ReqInfo& ci = s_ci[nn];
-        seg32_epilogue<RESID, VEC4>(p, ci, (n < R) && ci.act, n, seg, khalf, acc[nb], x[nb]);
-      }
-    }
   }
 }
 
@@ -1112,26 +1036,16 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     }
     return hipGetLastError();
   }
+  // 64-row path: one workgroup per 256 vocabulary rows
   const dim3 grid((p.n_seg + 3) / 4), block(256);
-  if (p.seg_rows == kSegWide) {
-    if (p.rank <= 64)
-      launch(bias_seg64<2, RESID, VEC4>, grid, block, s, e0, e1, p);
-    else if (p.rank <= 128)
-      launch(bias_seg64<4, RESID, VEC4>, grid, block, s, e0, e1, p);
-    else if (p.rank <= 256)
-      launch(bias_seg64<8, RESID, VEC4>, grid, block, s, e0, e1, p);
-    else
-      launch(bias_seg64<16, RESID, VEC4>, grid, block, s, e0, e1, p);
-    return hipGetLastError();
-  }
   if (p.rank <= 64)
-    launch(bias_seg32<4, RESID, VEC4>, grid, block, s, e0, e1, p);
+    launch(bias_seg64<2, RESID, VEC4>, grid, block, s, e0, e1, p);
   else if (p.rank <= 128)
-    launch(bias_seg32<8, RESID, VEC4>, grid, block, s, e0, e1, p);
+    launch(bias_seg64<4, RESID, VEC4>, grid, block, s, e0, e1, p);
   else if (p.rank <= 256)
-    launch(bias_seg32<16, RESID, VEC4>, grid, block, s, e0, e1, p);
+    launch(bias_seg64<8, RESID, VEC4>, grid, block, s, e0, e1, p);
   else
-    launch(bias_seg32<32, RESID, VEC4>, grid, block, s, e0, e1, p);
+    launch(bias_seg64<16, RESID, VEC4>, grid, block, s, e0, e1, p);
   return hipGetLastError();
 }
 
@@ -1147,6 +1061,8 @@ hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int 
   if (p.seg_rows == kSegWide &&
       (wdtype != DSPARK_W_BF16 || (residual && (p.rs_count == nullptr || p.rs_list == nullptr))))
     return hipErrorInvalidValue;
+  // 32-row segments are the fp32-weight path only
+  if (p.seg_rows == kSegLarge && wdtype != DSPARK_W_F32) return hipErrorInvalidValue;
   const bool vec4 = (p.V % 4) == 0;
   if (residual)
     return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s, ev0, ev1)
