@@ -35,7 +35,10 @@ Readings of points the pages leave open (each also listed in the design notes):
     [0, 1] (NaN -> 0), so the schedule is reproducible bit for bit;
   * the scheduler ranks candidates by (a descending, k ascending, r ascending)
     and takes min(K, R*gamma) of them; each request keeps its anchor row, so
-    it owns l[r] + 1 verify rows.
+    it owns l[r] + 1 verify rows;
+  * the static confidence cutoff compares each position's own confidence c
+    (clamped as for survival) with conf_min, keeps the leading positions that
+    reach it (>=) and stops at the first that does not; no global capacity.
 """
 from __future__ import annotations
 
@@ -47,7 +50,7 @@ import numpy as np
 
 __all__ = [
     "NEAR", "widen", "markov_bias", "inverse_cdf", "draft_block", "survival",
-    "schedule", "verify", "step", "DraftResult", "ScheduleResult", "VerifyResult",
+    "schedule", "schedule_cutoff", "verify", "step", "DraftResult", "ScheduleResult", "VerifyResult",
 ]
 
 #: width of the band around a decision boundary inside which a flip caused by
@@ -222,8 +225,19 @@ def schedule(c, K: int, anchor, y) -> ScheduleResult:
     for negv, k, r in cand:
         l[r] += 1
         sel_a.append(-negv)
+    off, row_req, row_pos, row_tok = _flatten_rows(l, anchor, y)
+    return ScheduleResult(a=a, l=l.astype(np.int32), row_offsets=off,
+                          row_req=row_req, row_pos=row_pos, row_tok=row_tok,
+                          expected_tokens=R + math.fsum(sel_a), Kc=Kc)
+
+
+def _flatten_rows(l, anchor, y):
+    """Flattened verify rows of a schedule (explainer section 13): request r
+    owns rows off[r] .. off[r] + l[r]; row j of them is fed the anchor (j = 0)
+    or y[r, j - 1]."""
+    R = len(l)
     off = np.zeros(R + 1, dtype=np.int64)
-    off[1:] = np.cumsum(l + 1)
+    off[1:] = np.cumsum(np.asarray(l, dtype=np.int64) + 1)
     n_rows = int(off[-1])
     row_req = np.empty(n_rows, dtype=np.int32)
     row_pos = np.empty(n_rows, dtype=np.int32)
@@ -234,9 +248,37 @@ def schedule(c, K: int, anchor, y) -> ScheduleResult:
             row_req[i] = r
             row_pos[i] = j
             row_tok[i] = int(anchor[r]) if j == 0 else int(y[r, j - 1])
-    return ScheduleResult(a=a, l=l.astype(np.int32), row_offsets=off.astype(np.int32),
+    return off.astype(np.int32), row_req, row_pos, row_tok
+
+
+def schedule_cutoff(c, conf_min, anchor, y) -> ScheduleResult:
+    """Static confidence cutoff: the scheduling step the pages try first
+    (Strata plan, "Approach" step 5: evaluate a static confidence cutoff
+    before a load-aware scheduler; llama.cpp PR #25173, "Confidence
+    Evaluation": the conf_min setting, measured at 0.0, 0.3 and 0.6).
+
+    Request r verifies its leading drafted positions while each position's
+    confidence c[r, k] (clamped to [0, 1], NaN -> 0, as for survival) is at
+    least conf_min (an fp32 value), and stops at the first that is not:
+    per request, with no global capacity.  Survival, the flattened rows and
+    the expected token count are those of schedule() for the resulting l."""
+    a = survival(c)
+    R, gamma = a.shape
+    c32 = np.asarray(c, dtype=np.float32)
+    cc = np.where(np.isnan(c32), np.float32(0), np.clip(c32, np.float32(0), np.float32(1)))
+    thr = np.float32(conf_min)
+    l = np.zeros(R, dtype=np.int64)
+    sel_a = []
+    for r in range(R):
+        k = 0
+        while k < gamma and cc[r, k] >= thr:
+            sel_a.append(float(a[r, k]))
+            k += 1
+        l[r] = k
+    off, row_req, row_pos, row_tok = _flatten_rows(l, anchor, y)
+    return ScheduleResult(a=a, l=l.astype(np.int32), row_offsets=off,
                           row_req=row_req, row_pos=row_pos, row_tok=row_tok,
-                          expected_tokens=R + math.fsum(sel_a), Kc=Kc)
+                          expected_tokens=R + math.fsum(sel_a), Kc=int(l.sum()))
 
 
 @dataclass

@@ -480,6 +480,83 @@ def test_schedule_is_causal():
 
 
 # ---------------------------------------------------------------------------
+# static confidence cutoff (Strata plan "Approach" step 5; llama.cpp PR
+# "Confidence Evaluation", conf_min)
+# ---------------------------------------------------------------------------
+def _cutoff_brute(c, conf_min):
+    """Longest prefix length whose every position's clamped confidence
+    reaches conf_min, by enumerating all prefix lengths."""
+    R, gamma = c.shape
+    out = []
+    for r in range(R):
+        best = 0
+        for m in range(gamma + 1):
+            ok = True
+            for k in range(m):
+                v = float(c[r, k])
+                v = 0.0 if v != v else min(max(v, 0.0), 1.0)
+                if not v >= float(np.float32(conf_min)):
+                    ok = False
+            if ok:
+                best = m
+        out.append(best)
+    return out
+
+
+@pytest.mark.parametrize("R,gamma", [(1, 1), (4, 3), (9, 7)])
+def test_cutoff_by_brute_force(R, gamma):
+    rng = np.random.default_rng(100 + R * gamma)
+    c, anc, y = _rand_sched(rng, R, gamma)
+    c = c.copy()
+    c.flat[::5] = np.float32(0.5)                    # exact ties with conf_min = 0.5
+    c.flat[3::11] = np.nan
+    c.flat[4::13] = np.float32(1.5)
+    for conf_min in (0.0, 0.3, 0.5, 0.6, 0.999, 1.0):
+        s = oracle.schedule_cutoff(c, conf_min, anc, y)
+        assert list(s.l) == _cutoff_brute(c, conf_min)
+        assert (np.diff(s.row_offsets) == s.l + 1).all() and s.row_offsets[0] == 0
+        for i in range(len(s.row_req)):
+            r, j = s.row_req[i], s.row_pos[i]
+            assert s.row_offsets[r] + j == i
+            assert s.row_tok[i] == (anc[r] if j == 0 else y[r, j - 1])
+        sel_a = [float(s.a[r, k]) for r in range(R) for k in range(s.l[r])]
+        assert abs(s.expected_tokens - (R + sum(sel_a))) < 1e-9
+
+
+def test_cutoff_extremes_reduce_to_fixed_length_and_target_only():
+    """conf_min <= 0 keeps every position (the fixed-length schedule, K >=
+    R*gamma); conf_min above 1 keeps none (target-only, K = 0)."""
+    rng = np.random.default_rng(5)
+    R, gamma = 11, 6
+    c, anc, y = _rand_sched(rng, R, gamma)
+    for conf_min, K in ((0.0, R * gamma), (-2.0, R * gamma), (np.nextafter(np.float32(1), np.float32(2)), 0),
+                        (3.0, 0)):
+        s = oracle.schedule_cutoff(c, conf_min, anc, y)
+        t = oracle.schedule(c, K, anc, y)
+        for f in ("a", "l", "row_offsets", "row_req", "row_pos", "row_tok"):
+            np.testing.assert_array_equal(getattr(s, f), getattr(t, f), err_msg=f)
+        assert s.expected_tokens == pytest.approx(t.expected_tokens, rel=0, abs=1e-9)
+
+
+def test_cutoff_is_monotone_and_causal():
+    """A higher conf_min never verifies more; the drafted tokens never change
+    the lengths (explainer section 4)."""
+    rng = np.random.default_rng(6)
+    R, gamma = 20, 7
+    c, anc, y = _rand_sched(rng, R, gamma)
+    prev = None
+    for conf_min in np.linspace(0.0, 1.0, 21):
+        s = oracle.schedule_cutoff(c, conf_min, anc, y)
+        if prev is not None:
+            assert (s.l <= prev).all()
+        prev = s.l
+        y2 = rng.integers(0, 1000, size=y.shape).astype(np.int32)
+        s2 = oracle.schedule_cutoff(c, conf_min, anc, y2)
+        np.testing.assert_array_equal(s.l, s2.l)
+        np.testing.assert_array_equal(s.row_offsets, s2.row_offsets)
+
+
+# ---------------------------------------------------------------------------
 # bias and input conversion
 # ---------------------------------------------------------------------------
 def test_markov_bias_is_low_rank_product():
