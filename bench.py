@@ -111,8 +111,9 @@ class HipTimingEvents:
         self.handles = []
 
 
-def cpu_baseline(inp, n_sample, seed=0):
-    """The CPU oracle on a bounded sample of requests (single BLAS thread)."""
+def cpu_baseline(inp, n_sample, seed=0, conf_min=None):
+    """The CPU oracle on a bounded sample of requests (single BLAS thread),
+    with the same scheduler as the GPU step."""
     import oracle
     from threadpoolctl import threadpool_limits
     rng = np.random.default_rng(seed)
@@ -122,7 +123,10 @@ def cpu_baseline(inp, n_sample, seed=0):
         d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
                                requests=reqs)
         y = np.where(d.y < 0, 0, d.y)
-        s = oracle.schedule(inp.c, inp.K, inp.anchor, y)
+        if conf_min is None:
+            s = oracle.schedule(inp.c, inp.K, inp.anchor, y)
+        else:
+            s = oracle.schedule_cutoff(inp.c, conf_min, inp.anchor, y)
         t1 = time.perf_counter()
         # the row gather stands in for the target forward (not timed, as on the GPU)
         rows = inp.target[s.row_req.astype(np.int64), s.row_pos.astype(np.int64)]
@@ -146,6 +150,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=64)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the back-to-back warm loop")
+    ap.add_argument("--conf-min", type=float, default=None,
+                    help="schedule with the static confidence cutoff at this conf_min instead of the top-K "
+                         "scheduler with the configuration's capacity K")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -194,7 +201,8 @@ def main():
     q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
     wd = ds.W_BF16 if inp.wdtype == "bf16" else ds.W_F32
     ws_d = torch.empty(ds.draft_workspace_bytes(R, gamma, V, rank, wd), dtype=torch.uint8, device=dev)
-    n_rows = ds.dspark_schedule_rows(R, gamma, inp.K)
+    cutoff = args.conf_min is not None
+    n_rows = R * (gamma + 1) if cutoff else ds.dspark_schedule_rows(R, gamma, inp.K)
     sch = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
                l=torch.empty(R, dtype=torch.int32, device=dev),
                row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
@@ -202,22 +210,29 @@ def main():
                row_pos=torch.empty(n_rows, dtype=torch.int32, device=dev),
                row_tok=torch.empty(n_rows, dtype=torch.int32, device=dev),
                expected_tokens=torch.empty(1, dtype=torch.float32, device=dev))
-    ws_v = torch.empty(ds.verify_workspace_bytes(R, gamma, V, rank, wd, n_rows), dtype=torch.uint8, device=dev)
     n_acc = torch.empty(R, dtype=torch.int32, device=dev)
     out_tok = torch.empty(R, dtype=torch.int32, device=dev)
     p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
 
     # target rows of the (deterministic) schedule: the stand-in for the target forward
+    def schedule():
+        if cutoff:
+            ds.dspark_schedule_cutoff(c, args.conf_min, anchor, y, out=sch)
+        else:
+            ds.dspark_schedule(c, inp.K, anchor, y, out=sch)
+
     ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d)
-    ds.dspark_schedule(c, inp.K, anchor, y, out=sch)
-    rows = target_full[sch["row_req"].long(), sch["row_pos"].long()].contiguous()
+    schedule()
+    n_rows = int(sch["row_offsets"][R].item())
+    rows = target_full[sch["row_req"][:n_rows].long(), sch["row_pos"][:n_rows].long()].contiguous()
     del target_full
+    ws_v = torch.empty(ds.verify_workspace_bytes(R, gamma, V, rank, wd, n_rows), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(prof=None):
         ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d,
                               prof_events=prof)
-        ds.dspark_schedule(c, inp.K, anchor, y, out=sch)
+        schedule()
         ds.dspark_verify(rows, sch["row_offsets"], U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final,
                          out=(n_acc, out_tok, p_tok), workspace=ws_v)
 
@@ -282,7 +297,7 @@ def main():
 
     cpu = None
     if not args.skip_cpu:
-        cpu = cpu_baseline(inp, args.cpu_sample)
+        cpu = cpu_baseline(inp, args.cpu_sample, conf_min=args.conf_min)
 
     line = {
         "metric": METRIC,
@@ -299,7 +314,9 @@ def main():
         "data": "synthetic (seeded; logits, Markov factors, uniforms and confidences drawn by synth)",
         "config": {
             "workload": f"config{args.config}: R={R} gamma={gamma} V={V} r={rank} {inp.wdtype} W1/W2, fp32 logits, "
-                        f"{'fixed-length' if inp.K >= R * gamma else 'scheduled'} verify (K={inp.K}, {n_rows} rows)",
+                        + (f"static confidence cutoff conf_min={args.conf_min} ({n_rows} rows)" if cutoff else
+                           f"{'fixed-length' if inp.K >= R * gamma else 'scheduled'} verify "
+                           f"(K={inp.K}, {n_rows} rows)"),
             "R": R, "gamma": gamma, "V": V, "rank": rank, "weights": inp.wdtype, "K": inp.K,
             "verify_rows": n_rows, "parallelism": "single GPU",
         },

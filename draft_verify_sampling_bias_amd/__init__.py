@@ -16,9 +16,10 @@ from typing import Optional, Sequence
 
 __all__ = [
     "LIB_PATH", "get_lib", "Status", "DsparkError", "dspark_draft_block", "dspark_schedule",
+    "dspark_schedule_cutoff",
     "dspark_verify", "dspark_schedule_rows", "dspark_draft_workspace_size",
     "dspark_verify_workspace_size", "dspark_status_string", "dspark_abi_version",
-    "DraftArgs", "ScheduleArgs", "VerifyArgs", "EXPORTED_SYMBOLS",
+    "DraftArgs", "ScheduleArgs", "CutoffArgs", "VerifyArgs", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
@@ -27,8 +28,8 @@ W_F32, W_BF16 = 0, 1
 
 EXPORTED_SYMBOLS = (
     "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
-    "dspark_schedule", "dspark_verify", "dspark_schedule_rows", "dspark_status_string",
-    "dspark_abi_version",
+    "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_schedule_rows",
+    "dspark_status_string", "dspark_abi_version",
 )
 
 
@@ -60,6 +61,13 @@ class ScheduleArgs(ctypes.Structure):
                 ("expected_tokens", _p), ("stream", _p)]
 
 
+class CutoffArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("conf_min", ctypes.c_float), ("c", _p), ("anchor", _p), ("y", _p), ("a", _p), ("l", _p),
+                ("row_offsets", _p), ("row_req", _p), ("row_pos", _p), ("row_tok", _p),
+                ("expected_tokens", _p), ("stream", _p)]
+
+
 class VerifyArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
                 ("V", ctypes.c_int32), ("rank", ctypes.c_int32), ("wdtype", ctypes.c_int32),
@@ -79,9 +87,10 @@ def _load():
     L.dspark_verify_workspace_size.argtypes = [P(VerifyArgs), P(ctypes.c_size_t)]
     L.dspark_draft_block.argtypes = [P(DraftArgs)]
     L.dspark_schedule.argtypes = [P(ScheduleArgs)]
+    L.dspark_schedule_cutoff.argtypes = [P(CutoffArgs)]
     L.dspark_verify.argtypes = [P(VerifyArgs)]
     for f in ("dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
-              "dspark_schedule", "dspark_verify", "dspark_abi_version"):
+              "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_abi_version"):
         getattr(L, f).restype = ctypes.c_int
     L.dspark_schedule_rows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     L.dspark_schedule_rows.restype = ctypes.c_int64
@@ -276,6 +285,41 @@ def dspark_schedule(c, K: int, anchor, y, *, out=None, want_expected: bool = Tru
                      row_pos=_ptr(out["row_pos"]), row_tok=_ptr(out["row_tok"]),
                      expected_tokens=_ptr(out.get("expected_tokens")), stream=_stream(dev, stream))
     _check("dspark_schedule", get_lib().dspark_schedule(ctypes.byref(a)))
+    return out
+
+
+def dspark_schedule_cutoff(c, conf_min: float, anchor, y, *, out=None, want_expected: bool = True, stream=None):
+    """Survival + static confidence-cutoff schedule (include/dspark.h,
+    dspark_schedule_cutoff).  c [R, gamma] fp32; anchor [R] int32; y [R, gamma]
+    int32.  Returns a dict like dspark_schedule's; the row arrays have room
+    for R * (gamma + 1) rows, of which row_offsets[R] are written."""
+    torch = _torch()
+    dev = c.device
+    R, gamma = c.shape
+    _want(c, "c", torch.float32, (R, gamma), dev)
+    _want(anchor, "anchor", torch.int32, (R,), dev)
+    _want(y, "y", torch.int32, (R, gamma), dev)
+    cap = R * (gamma + 1)
+    if out is None:
+        out = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                   l=torch.empty(R, dtype=torch.int32, device=dev),
+                   row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
+                   row_req=torch.empty(cap, dtype=torch.int32, device=dev),
+                   row_pos=torch.empty(cap, dtype=torch.int32, device=dev),
+                   row_tok=torch.empty(cap, dtype=torch.int32, device=dev),
+                   expected_tokens=torch.empty(1, dtype=torch.float32, device=dev) if want_expected else None)
+    else:
+        _want(out["a"], "a", torch.float32, (R, gamma), dev)
+        _want(out["l"], "l", torch.int32, (R,), dev)
+        _want(out["row_offsets"], "row_offsets", torch.int32, (R + 1,), dev)
+        for f in ("row_req", "row_pos", "row_tok"):
+            _want(out[f], f, torch.int32, (cap,), dev)
+    a = CutoffArgs(struct_size=ctypes.sizeof(CutoffArgs), R=R, gamma=gamma, conf_min=float(conf_min), c=_ptr(c),
+                   anchor=_ptr(anchor), y=_ptr(y), a=_ptr(out["a"]), l=_ptr(out["l"]),
+                   row_offsets=_ptr(out["row_offsets"]), row_req=_ptr(out["row_req"]),
+                   row_pos=_ptr(out["row_pos"]), row_tok=_ptr(out["row_tok"]),
+                   expected_tokens=_ptr(out.get("expected_tokens")), stream=_stream(dev, stream))
+    _check("dspark_schedule_cutoff", get_lib().dspark_schedule_cutoff(ctypes.byref(a)))
     return out
 
 

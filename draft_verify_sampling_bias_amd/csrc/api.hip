@@ -125,6 +125,28 @@ int dspark_schedule(const dspark_schedule_args* a) {
   return hip_status(launch_schedule(*a, static_cast<hipStream_t>(a->stream)));
 }
 
+int dspark_schedule_cutoff(const dspark_cutoff_args* a) {
+  const int st = validate_cutoff(a);
+  if (st != DSPARK_OK || a->R == 0) return st;
+  dspark_schedule_args s{};
+  s.struct_size = sizeof(s);
+  s.R = a->R;
+  s.gamma = a->gamma;
+  s.K = 0;  // not read by the cutoff
+  s.c = a->c;
+  s.anchor = a->anchor;
+  s.y = a->y;
+  s.a = a->a;
+  s.l = a->l;
+  s.row_offsets = a->row_offsets;
+  s.row_req = a->row_req;
+  s.row_pos = a->row_pos;
+  s.row_tok = a->row_tok;
+  s.expected_tokens = a->expected_tokens;
+  s.stream = a->stream;
+  return hip_status(launch_schedule_cutoff(s, a->conf_min, static_cast<hipStream_t>(a->stream)));
+}
+
 int dspark_verify(const dspark_verify_args* a) {
   VerifyPlan plan;
   int st = validate_verify(a, &plan);

@@ -108,5 +108,7 @@ hipError_t launch_verify_stats(const VerifyParams& p, hipStream_t s);
 hipError_t launch_verify_finish(const VerifyParams& p, hipStream_t s);
 hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t s);
 hipError_t launch_schedule(const dspark_schedule_args& a, hipStream_t s);
+// the static confidence cutoff; a.K is not read
+hipError_t launch_schedule_cutoff(const dspark_schedule_args& a, float conf_min, hipStream_t s);
 
 }  // namespace dspark

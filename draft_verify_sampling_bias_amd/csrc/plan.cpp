@@ -129,6 +129,25 @@ int validate_schedule(const dspark_schedule_args* a) {
   return DSPARK_OK;
 }
 
+int validate_cutoff(const dspark_cutoff_args* a) {
+  if (a == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_cutoff_args)) return DSPARK_ERR_ABI;
+  if (a->R < 0 || a->gamma < 1 || a->conf_min != a->conf_min) return DSPARK_ERR_SHAPE;
+  if (a->gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
+  const int64_t per_thread = (static_cast<int64_t>(a->R) + 1023) / 1024 * a->gamma;
+  if (per_thread > DSPARK_SCHED_KEYS_PER_THREAD) return DSPARK_ERR_UNSUPPORTED;
+  if (a->R == 0) return DSPARK_OK;
+  if (!a->c || !a->anchor || !a->y || !a->a || !a->l || !a->row_offsets || !a->row_req || !a->row_pos ||
+      !a->row_tok)
+    return DSPARK_ERR_NULL;
+  if (!aligned(a->c, 4) || !aligned(a->anchor, 4) || !aligned(a->y, 4) || !aligned(a->a, 4) ||
+      !aligned(a->l, 4) || !aligned(a->row_offsets, 4) || !aligned(a->row_req, 4) ||
+      !aligned(a->row_pos, 4) || !aligned(a->row_tok, 4) ||
+      (a->expected_tokens && !aligned(a->expected_tokens, 4)))
+    return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
 int64_t schedule_rows(int32_t R, int32_t gamma, int64_t K) {
   if (R < 0 || gamma < 1) return -1;
   const int64_t n = static_cast<int64_t>(R) * gamma;

@@ -1,5 +1,8 @@
 // Causal prefix-closed global top-K verify scheduler ("DSpark" explainer
-// sections 4, 5, 8-10 and 13).
+// sections 4, 5, 8-10 and 13), and the static confidence cutoff (Strata
+// plan "Approach" step 5; llama.cpp PR #25173 "Confidence Evaluation",
+// conf_min), which replaces the top-K selection by a per-request rule: the
+// leading positions whose own clamped confidence is at least conf_min.
 //
 // One workgroup of 1024 threads.  Thread t owns requests t, t + 1024, ...;
 // their survival values a[r, k] (fp32 running product of the clamped c) live
@@ -50,7 +53,8 @@ __device__ __forceinline__ int block1024_excl_scan_int(int v, int* lds16, int* t
   return off + ex;
 }
 
-__global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule_args a) {
+template <bool CUTOFF>
+__global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule_args a, float conf_min) {
   __shared__ unsigned int hist[256];
   __shared__ unsigned long long s_prefix;
   __shared__ int s_rem;
@@ -63,6 +67,7 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
 
   unsigned long long key[kSlots];
   bool valid[kSlots];
+  bool keep[kSlots];  // static cutoff: position still inside the request's leading run
   // the confidences and drafted tokens of this thread's slots are loaded up
   // front, in one batch
   float cv[kSlots];
@@ -77,15 +82,19 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
     yv[s] = valid[s] ? a.y[o] : 0;
   }
   float run = 1.0f;
+  bool alive = true;
 #pragma unroll
   for (int s = 0; s < kSlots; ++s) {
     const int j = s / gamma, k = s - j * gamma;
     const int r = j * kSchedThreads + tid;
     key[s] = ~0ull;
+    keep[s] = false;
     if (valid[s]) {
       const int64_t o = static_cast<int64_t>(r) * gamma + k;
       float ck = fminf(fmaxf(cv[s], 0.0f), 1.0f);  // NaN -> 0
       run = (k == 0) ? ck : run * ck;
+      alive = ((k == 0) || alive) && (ck >= conf_min);
+      keep[s] = alive;
       const float av = (run == 0.0f) ? 0.0f : run;  // no -0
       a.a[o] = av;
       const unsigned int bits = __float_as_uint(av);
@@ -98,7 +107,7 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
   const int64_t Kc = a.K < 0 ? 0 : (a.K > n ? n : a.K);
   unsigned long long thr = 0;
   bool none = (Kc == 0), all = (Kc == n);
-  if (!none && !all) {
+  if (!CUTOFF && !none && !all) {
     unsigned long long prefix = 0;
     int rem = static_cast<int>(Kc);
     for (int pass = 0; pass < 8; ++pass) {
@@ -143,7 +152,7 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
 #pragma unroll
   for (int s = 0; s < kSlots; ++s) {
     if (valid[s]) {
-      const bool sel = all || (!none && key[s] <= thr);
+      const bool sel = CUTOFF ? keep[s] : (all || (!none && key[s] <= thr));
       if (sel) {
         const int j = s / gamma;
 #pragma unroll
@@ -204,7 +213,13 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
 
 hipError_t launch_schedule(const dspark_schedule_args& a, hipStream_t s) {
   if (a.R == 0) return hipSuccess;
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kSchedThreads), 0, s, a);
+  hipLaunchKernelGGL(schedule_kernel<false>, dim3(1), dim3(kSchedThreads), 0, s, a, 0.0f);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_cutoff(const dspark_schedule_args& a, float conf_min, hipStream_t s) {
+  if (a.R == 0) return hipSuccess;
+  hipLaunchKernelGGL(schedule_kernel<true>, dim3(1), dim3(kSchedThreads), 0, s, a, conf_min);
   return hipGetLastError();
 }
 

@@ -278,8 +278,54 @@ typedef struct dspark_verify_args {
 int dspark_draft_workspace_size(const dspark_draft_args* args, size_t* bytes);
 int dspark_verify_workspace_size(const dspark_verify_args* args, size_t* bytes);
 
+/* --------------------------------------------------------------------------
+ * dspark_schedule_cutoff: survival and the static confidence-cutoff schedule.
+ *
+ * [PLAN] "Approach", step 5: confidence scheduling first evaluates a static
+ * confidence cutoff, before any load-aware scheduler.  [LCPP] "Confidence
+ * Evaluation": the conf_min setting (measured at 0.0, 0.3 and 0.6).  Each
+ * request verifies its leading drafted positions while each position's own
+ * confidence reaches conf_min, and stops at the first that does not: a
+ * per-request rule, prefix-closed by construction, with no global capacity.
+ * Like dspark_schedule, the decision reads only c, never the drafted tokens
+ * ([EXP] section 4).
+ *
+ *   c'[r, k]  = c clamped to [0, 1] (NaN -> 0), as for survival;
+ *   l[r]      = the largest m in 0..gamma with c'[r, k] >= conf_min for
+ *               every k < m (fp32 comparison);
+ *   a, row_offsets, row_req, row_pos, row_tok and expected_tokens are then
+ *   defined exactly as by dspark_schedule for this l.
+ *
+ * conf_min <= 0 verifies every position (the fixed-length schedule);
+ * conf_min > 1 verifies none (target-only decoding).
+ *
+ * Arguments: as dspark_schedule_args, without K and with
+ *   conf_min   host float, not NaN (DSPARK_ERR_SHAPE otherwise).
+ *   row_req, row_pos, row_tok  int32 [R * (gamma + 1)] out: room for the
+ *              largest schedule (R + sum l[r] rows are written; the number is
+ *              row_offsets[R]).
+ * -------------------------------------------------------------------------- */
+typedef struct dspark_cutoff_args {
+  uint32_t struct_size;
+  int32_t R, gamma;
+  float conf_min;
+  const float* c;
+  const int32_t* anchor;
+  const int32_t* y;
+  float* a;
+  int32_t* l;
+  int32_t* row_offsets;
+  int32_t* row_req;
+  int32_t* row_pos;
+  int32_t* row_tok;
+  float* expected_tokens;
+  void* stream;
+} dspark_cutoff_args;
+
+
 int dspark_draft_block(const dspark_draft_args* args);
 int dspark_schedule(const dspark_schedule_args* args);
+int dspark_schedule_cutoff(const dspark_cutoff_args* args);
 int dspark_verify(const dspark_verify_args* args);
 
 /* Host-side: number of verify rows dspark_schedule emits,

@@ -42,12 +42,20 @@ def upload(inp: synth.StepInputs, device="cuda:0"):
                 u_accept=f(inp.u_accept), u_final=f(inp.u_final), c=f(inp.c), target=f(inp.target))
 
 
-def gpu_step(d, K, gamma):
-    """draft -> schedule -> gather rows -> verify on the GPU; returns numpy results."""
+def gpu_step(d, K, gamma, conf_min=None):
+    """draft -> schedule (top-K with capacity K, or the static confidence
+    cutoff when conf_min is given) -> gather rows -> verify on the GPU;
+    returns numpy results."""
     import draft_verify_sampling_bias_amd as ds
     torch = torch_mod()
     y, q_tok, q_stats = ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"])
-    sch = ds.dspark_schedule(d["c"], K, d["anchor"], y)
+    if conf_min is None:
+        sch = ds.dspark_schedule(d["c"], K, d["anchor"], y)
+    else:
+        sch = ds.dspark_schedule_cutoff(d["c"], conf_min, d["anchor"], y)
+        n = int(sch["row_offsets"][-1].item())
+        for f in ("row_req", "row_pos", "row_tok"):
+            sch[f] = sch[f][:n]
     rows = d["target"][sch["row_req"].long(), sch["row_pos"].long()].contiguous()
     n_acc, out_tok, p_tok = ds.dspark_verify(rows, sch["row_offsets"], d["U"], d["W1"], d["W2"], d["anchor"],
                                              d["temp"], y, q_tok, q_stats, d["u_accept"], d["u_final"])
@@ -107,8 +115,11 @@ def compare_draft(inp, g, reqs, tally: Tally):
     return d
 
 
-def compare_schedule(inp, g, K):
-    s = oracle.schedule(inp.c, K, inp.anchor, g["y"])
+def compare_schedule(inp, g, K, conf_min=None):
+    if conf_min is None:
+        s = oracle.schedule(inp.c, K, inp.anchor, g["y"])
+    else:
+        s = oracle.schedule_cutoff(inp.c, conf_min, inp.anchor, g["y"])
     np.testing.assert_array_equal(g["a"], s.a)
     np.testing.assert_array_equal(g["l"], s.l)
     np.testing.assert_array_equal(g["row_offsets"], s.row_offsets)

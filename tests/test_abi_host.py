@@ -157,8 +157,29 @@ def test_schedule_rejects_invalid_arguments(kw, status):
     assert _call("dspark_schedule", ds.ScheduleArgs(**base)) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=0), ds.Status.ERR_ABI),
+    (dict(gamma=0), ds.Status.ERR_SHAPE),
+    (dict(conf_min=float("nan")), ds.Status.ERR_SHAPE),
+    (dict(R=-2), ds.Status.ERR_SHAPE),
+    (dict(gamma=17), ds.Status.ERR_UNSUPPORTED),
+    (dict(R=1025, gamma=9), ds.Status.ERR_UNSUPPORTED),
+    (dict(y=None), ds.Status.ERR_NULL),
+    (dict(row_pos=FAKE + 2), ds.Status.ERR_ALIGN),
+])
+def test_cutoff_rejects_invalid_arguments(kw, status):
+    base = dict(struct_size=ctypes.sizeof(ds.CutoffArgs), R=8, gamma=4, conf_min=0.5)
+    for f in ("c", "anchor", "y", "a", "l", "row_offsets", "row_req", "row_pos", "row_tok"):
+        base[f] = FAKE
+    base.update(kw)
+    assert _call("dspark_schedule_cutoff", ds.CutoffArgs(**base)) == status
+    assert _call("dspark_schedule_cutoff", ds.CutoffArgs(struct_size=ctypes.sizeof(ds.CutoffArgs), R=0, gamma=3,
+                                                         conf_min=0.5)) == ds.Status.OK
+
+
 def test_null_args_pointer():
     lib = ds.get_lib()
     assert lib.dspark_draft_block(None) == ds.Status.ERR_NULL
     assert lib.dspark_verify(None) == ds.Status.ERR_NULL
     assert lib.dspark_schedule(None) == ds.Status.ERR_NULL
+    assert lib.dspark_schedule_cutoff(None) == ds.Status.ERR_NULL

@@ -110,6 +110,54 @@ def test_masked_vocabulary(R, wd):
     assert not np.isin(g["y"], np.flatnonzero(mask)).any()
 
 
+@pytest.mark.parametrize("R,gamma", [(1, 1), (37, 5), (64, 7), (1500, 3), (5000, 3)])
+def test_schedule_cutoff(R, gamma):
+    """Static confidence cutoff against the oracle, bit-exact, with exact ties
+    at conf_min, NaN and out-of-range confidences, and several 1024-request
+    rounds per thread."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    rng = np.random.default_rng(700 + R + gamma)
+    c = (1 / (1 + np.exp(-rng.normal(1, 1, (R, gamma))))).astype(np.float32)
+    c.flat[::7] = np.float32(0.5)
+    c.flat[::23] = np.float32(0.3)
+    c.flat[3::29] = np.nan
+    c.flat[5::31] = np.float32(1.25)
+    c.flat[6::37] = np.float32(-0.5)
+    anc = rng.integers(0, 100000, R).astype(np.int32)
+    y = rng.integers(0, 100000, (R, gamma)).astype(np.int32)
+    cd, ad, yd = (torch.from_numpy(x).cuda() for x in (c, anc, y))
+    for conf_min in (-1.0, 0.0, 0.3, 0.5, 0.6, 0.999, 1.0, 1.5):
+        g = {k: v.cpu().numpy() for k, v in ds.dspark_schedule_cutoff(cd, conf_min, ad, yd).items()}
+        o = oracle.schedule_cutoff(c, conf_min, anc, y)
+        n = int(o.row_offsets[-1])
+        np.testing.assert_array_equal(g["a"], o.a)
+        np.testing.assert_array_equal(g["l"], o.l, err_msg=f"conf_min={conf_min}")
+        np.testing.assert_array_equal(g["row_offsets"], o.row_offsets)
+        for f in ("row_req", "row_pos", "row_tok"):
+            np.testing.assert_array_equal(g[f][:n], getattr(o, f), err_msg=f)
+        assert abs(float(g["expected_tokens"][0]) - o.expected_tokens) <= 1e-5 * o.expected_tokens
+    print(f"[cutoff R={R} gamma={gamma}] ok", flush=True)
+
+
+@pytest.mark.parametrize("cfg,conf_min", [(3, 0.6), (4, 0.3)])
+def test_cutoff_step(cfg, conf_min):
+    """A full step with the static cutoff in place of the top-K scheduler:
+    draft, cutoff schedule, verify on the variable-length rows (sampled
+    requests compared against the oracle)."""
+    inp = synth.make_config(cfg)
+    reqs = _sample(inp.R, 4, cfg)
+    d = upload(inp)
+    g = gpu_step(d, None, inp.gamma, conf_min=conf_min)
+    t = Tally()
+    compare_draft(inp, g, reqs, t)
+    compare_schedule(inp, g, None, conf_min=conf_min)
+    compare_verify(inp, g, reqs, t)
+    print(f"[cutoff config{cfg} conf_min={conf_min}] rows={int(g['row_offsets'][-1])} {t.summary()}", flush=True)
+    t.check()
+
+
 def _sample(R, n, seed):
     rng = np.random.default_rng(seed)
     return sorted(rng.choice(R, size=min(n, R), replace=False).tolist())
