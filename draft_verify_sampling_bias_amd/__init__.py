@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 
 __all__ = [
     "LIB_PATH", "get_lib", "Status", "DsparkError", "dspark_draft_block", "dspark_schedule",
-    "dspark_schedule_cutoff",
+    "dspark_schedule_cutoff", "dspark_pack_w2", "dspark_w2_packed_bytes", "PackArgs",
     "dspark_verify", "dspark_schedule_rows", "dspark_draft_workspace_size",
     "dspark_verify_workspace_size", "dspark_status_string", "dspark_abi_version",
     "DraftArgs", "ScheduleArgs", "CutoffArgs", "VerifyArgs", "EXPORTED_SYMBOLS",
@@ -29,7 +29,7 @@ W_F32, W_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
     "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_schedule_rows",
-    "dspark_status_string", "dspark_abi_version",
+    "dspark_status_string", "dspark_abi_version", "dspark_pack_w2", "dspark_w2_packed_bytes",
 )
 
 
@@ -51,7 +51,7 @@ class DraftArgs(ctypes.Structure):
                 ("V", ctypes.c_int32), ("rank", ctypes.c_int32), ("wdtype", ctypes.c_int32),
                 ("U", _p), ("W1", _p), ("W2", _p), ("anchor", _p), ("temp", _p), ("u_draft", _p),
                 ("y", _p), ("q_tok", _p), ("q_stats", _p), ("workspace", _p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("prof_events", _p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("prof_events", _p), ("W2_packed", _p)]
 
 
 class ScheduleArgs(ctypes.Structure):
@@ -74,7 +74,12 @@ class VerifyArgs(ctypes.Structure):
                 ("n_rows", ctypes.c_int64), ("target", _p), ("row_offsets", _p), ("U", _p), ("W1", _p),
                 ("W2", _p), ("anchor", _p), ("temp", _p), ("y", _p), ("q_tok", _p), ("q_stats", _p),
                 ("u_accept", _p), ("u_final", _p), ("n_accept", _p), ("out_tok", _p), ("p_tok", _p),
-                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("stream", _p)]
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("W2_packed", _p)]
+
+
+class PackArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("V", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("W2", _p), ("W2_packed", _p), ("W2_packed_bytes", ctypes.c_size_t), ("stream", _p)]
 
 
 def _load():
@@ -88,9 +93,13 @@ def _load():
     L.dspark_draft_block.argtypes = [P(DraftArgs)]
     L.dspark_schedule.argtypes = [P(ScheduleArgs)]
     L.dspark_schedule_cutoff.argtypes = [P(CutoffArgs)]
+    L.dspark_pack_w2.argtypes = [P(PackArgs)]
+    L.dspark_w2_packed_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    L.dspark_w2_packed_bytes.restype = ctypes.c_size_t
     L.dspark_verify.argtypes = [P(VerifyArgs)]
     for f in ("dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
-              "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_abi_version"):
+              "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_abi_version",
+              "dspark_pack_w2"):
         getattr(L, f).restype = ctypes.c_int
     L.dspark_schedule_rows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     L.dspark_schedule_rows.restype = ctypes.c_int64
@@ -201,8 +210,31 @@ dspark_draft_workspace_size = draft_workspace_bytes
 dspark_verify_workspace_size = verify_workspace_bytes
 
 
+def dspark_w2_packed_bytes(V: int, rank: int) -> int:
+    return int(get_lib().dspark_w2_packed_bytes(int(V), int(rank)))
+
+
+def dspark_pack_w2(W2, *, out=None, stream=None):
+    """W2 [V, rank] bf16 in the fragment-packed layout of the 16-row fused
+    kernel (include/dspark.h, dspark_pack_w2): a uint8 tensor of
+    dspark_w2_packed_bytes(V, rank) bytes, to pass as W2_packed."""
+    torch = _torch()
+    dev = W2.device
+    V, rank = W2.shape
+    _want(W2, "W2", torch.bfloat16, (V, rank), dev)
+    nbytes = dspark_w2_packed_bytes(V, rank)
+    if nbytes == 0:
+        raise ValueError("invalid V / rank")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a = PackArgs(struct_size=ctypes.sizeof(PackArgs), V=V, rank=rank, W2=_ptr(W2), W2_packed=_ptr(out),
+                 W2_packed_bytes=out.numel() * out.element_size(), stream=_stream(dev, stream))
+    _check("dspark_pack_w2", get_lib().dspark_pack_w2(ctypes.byref(a)))
+    return out
+
+
 def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=None, stream=None,
-                       prof_events=None):
+                       prof_events=None, W2_packed=None):
     """Draft gamma tokens per request (include/dspark.h, dspark_draft_block).
 
     U [R, gamma, V] fp32; W1, W2 [V, rank] bf16 or fp32; anchor [R] int32;
@@ -211,7 +243,7 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
     those three tensors; ``prof_events`` a list of 2*gamma timing events
     (torch.cuda.Event already recorded once, or raw hipEvent_t handles)
     attached to each position's fused bias kernel dispatch (start / stop of
-    that kernel alone)."""
+    that kernel alone); ``W2_packed`` the output of dspark_pack_w2 for W2."""
     torch = _torch()
     dev = U.device
     R, gamma, V = U.shape
@@ -246,7 +278,8 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
                   u_draft=_ptr(u_draft), y=_ptr(y), q_tok=_ptr(q_tok), q_stats=_ptr(q_stats),
                   workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(),
                   stream=_stream(dev, stream),
-                  prof_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None)
+                  prof_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
+                  W2_packed=_ptr(W2_packed))
     _check("dspark_draft_block", get_lib().dspark_draft_block(ctypes.byref(a)))
     return y, q_tok, q_stats
 
@@ -324,7 +357,7 @@ def dspark_schedule_cutoff(c, conf_min: float, anchor, y, *, out=None, want_expe
 
 
 def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final, *,
-                  out=None, workspace=None, stream=None):
+                  out=None, workspace=None, stream=None, W2_packed=None):
     """Accept / reject against target logits (include/dspark.h, dspark_verify).
 
     target [n_rows, V] fp32; row_offsets [R+1] int32; the draft inputs and
@@ -364,6 +397,7 @@ def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stat
                    W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp), y=_ptr(y),
                    q_tok=_ptr(q_tok), q_stats=_ptr(q_stats), u_accept=_ptr(u_accept), u_final=_ptr(u_final),
                    n_accept=_ptr(n_accept), out_tok=_ptr(out_tok), p_tok=_ptr(p_tok), workspace=_ptr(ws),
-                   workspace_bytes=ws.numel() * ws.element_size(), stream=_stream(dev, stream))
+                   workspace_bytes=ws.numel() * ws.element_size(), stream=_stream(dev, stream),
+                   W2_packed=_ptr(W2_packed))
     _check("dspark_verify", get_lib().dspark_verify(ctypes.byref(a)))
     return n_accept, out_tok, p_tok

@@ -77,6 +77,8 @@ int dspark_draft_block(const dspark_draft_args* a) {
   tp.temp = a->temp;
   tp.U_stride = static_cast<int64_t>(a->gamma) * a->V;
   tp.part = ws_at<float>(a->workspace, plan.part_off);
+  // the fragment-packed W2 is the 16-row path's layout only
+  tp.w2p = (plan.seg_rows == kSegSmall) ? static_cast<const uint16_t*>(a->W2_packed) : nullptr;
 
   FinishParams fp{};
   fp.part = tp.part;
@@ -123,6 +125,17 @@ int dspark_schedule(const dspark_schedule_args* a) {
   const int st = validate_schedule(a);
   if (st != DSPARK_OK || a->R == 0) return st;
   return hip_status(launch_schedule(*a, static_cast<hipStream_t>(a->stream)));
+}
+
+size_t dspark_w2_packed_bytes(int32_t V, int32_t rank) {
+  if (check_dims(0, 1, V, rank, DSPARK_W_BF16) != DSPARK_OK) return 0;
+  return w2_packed_bytes(V, rank);
+}
+
+int dspark_pack_w2(const dspark_pack_w2_args* a) {
+  const int st = validate_pack_w2(a);
+  if (st != DSPARK_OK) return st;
+  return hip_status(launch_pack_w2(*a, static_cast<hipStream_t>(a->stream)));
 }
 
 int dspark_schedule_cutoff(const dspark_cutoff_args* a) {
@@ -210,6 +223,7 @@ int dspark_verify(const dspark_verify_args* a) {
   tp.u_rows = static_cast<int64_t>(a->R) * a->gamma;
   tp.t_rows = a->n_rows;
   tp.part = vp.rpart;
+  tp.w2p = (plan.seg_rows == kSegSmall) ? static_cast<const uint16_t*>(a->W2_packed) : nullptr;
   st = hip_status(launch_bias_tile(tp, a->wdtype, true, current_cu_count(), s));
   if (st != DSPARK_OK) return st;
   return hip_status(launch_residual_finish(vp, a->wdtype, s));

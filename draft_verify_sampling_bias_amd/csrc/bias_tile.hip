@@ -110,22 +110,33 @@ struct Seg16Regs {
   f32x4_t t[RESID ? 4 : 1];  // target values, residual mode
 };
 
-// Issues the loads of segment [vw, vw + 16).  Rows past V re-read row V - 1
-// and columns k >= rank re-read the row's last 8 weights; both are masked at
-// use, so no instruction touches the loaded registers before the MFMA or the
-// epilogue needs them.
-template <int KS, bool RESID, bool VEC4>
+// W2 fragment ks of segment [vw, vw + 16) for this lane: from the
+// fragment-packed copy (1 KiB contiguous per k-step and wavefront; zeros
+// past V and the rank), or from the row-major W2, where rows past V re-read
+// row V - 1 and columns k >= rank re-read the row's last 8 weights (both
+// masked at use).
+template <int KS, bool PACKED>
+__device__ __forceinline__ const uint16_t* seg16_w2(const TileParams& p, int vw, int lane) {
+  if (PACKED) return p.w2p + (static_cast<int64_t>(vw / kSegSmall) * KS * 64 + lane) * 8;
+  return static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(min(vw + (lane & 15), p.V - 1)) * p.rank;
+}
+template <int KS, bool PACKED>
+__device__ __forceinline__ bf16x8_t seg16_w2_frag(const uint16_t* w2, int ks, int lane, int rank) {
+  const uint16_t* a = PACKED ? w2 + ks * 512 : w2 + min(ks * 32 + (lane >> 4) * 8, rank - 8);
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(a));
+}
+
+// Issues the loads of segment [vw, vw + 16).  No instruction touches the
+// loaded registers before the MFMA or the epilogue needs them (the rank and
+// vocabulary masks are applied at use).
+template <int KS, bool RESID, bool VEC4, bool PACKED>
 __device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s_ci, int vw, int lane,
                                            Seg16Regs<KS, RESID>& f) {
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V, rank = p.rank;
-  const int v = min(vw + l16, V - 1);
-  const uint16_t* w2 = static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(v) * rank;
+  const uint16_t* w2 = seg16_w2<KS, PACKED>(p, vw, lane);
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int k = ks * 32 + kq * 8;
-    f.w[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(w2 + min(k, rank - 8)));
-  }
+  for (int ks = 0; ks < KS; ++ks) f.w[ks] = seg16_w2_frag<KS, PACKED>(w2, ks, lane, rank);
   const int vu = vw + kq * 4;
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
@@ -184,15 +195,14 @@ __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16
 // W2 fragment ks of segment [vw_next, vw_next + 16) (and, in the first
 // steps, its U / target values), so a load issue that stalls on a busy
 // memory pipeline holds up one k-step instead of a whole segment.
-template <int KS, bool RESID, bool VEC4, bool DBUF>
+template <int KS, bool RESID, bool VEC4, bool DBUF, bool PACKED>
 __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
                                               f32x4_t (&acc)[4], const TileParams& p, const ReqInfo* s_ci,
                                               int vw_next, Seg16Regs<KS, RESID>& nx) {
   constexpr int RS = KS * 32 + 8;
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V;
-  const uint16_t* w2n =
-      static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(min(vw_next + l16, V - 1)) * rank;
+  const uint16_t* w2n = seg16_w2<KS, PACKED>(p, vw_next, lane);
   const int vu = vw_next + kq * 4;
   auto issue_u = [&](int nb) {
     const int nn = nb * 16 + l16;
@@ -210,7 +220,7 @@ __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uin
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    nx.w[ks] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(w2n + min(ks * 32 + kq * 8, rank - 8)));
+    nx.w[ks] = seg16_w2_frag<KS, PACKED>(w2n, ks, lane, rank);
     if (ks < 4) issue_u(ks);
     const int cur = DBUF ? (ks & 1) : 0;
     if (DBUF) {
@@ -323,7 +333,7 @@ constexpr int kSeg16DraftWaves = 8;  // draft mode: one workgroup per CU, two wa
 // wavefronts), so at any moment the grid streams one contiguous stretch of
 // W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
 // each of 64 rows.
-template <int KS, bool RESID, bool VEC4, int WPB>
+template <int KS, bool RESID, bool VEC4, int WPB, bool PACKED>
 __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci) {
   constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
   constexpr bool DBUF = RESID;     // see seg16_mfma
@@ -382,7 +392,7 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
   LaneReq<RESID> lq;
   lane_req<RESID>(s_ci, lane, lq);
   Seg16Regs<KS, RESID> fa, fb;
-  seg16_load<KS, RESID, VEC4>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  seg16_load<KS, RESID, VEC4, PACKED>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
   // Ping-pong prefetch, the next segment's loads interleaved with the
   // current one's k-steps.  The prefetch issued on a wavefront's last
   // segment re-reads segment n_seg - 1 (a cache hit, never used) so that the
@@ -391,11 +401,13 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
   while (true) {
     f32x4_t acc[4];
     const int s1 = sg + n_waves;
-    seg16_mfma_pf<KS, RESID, VEC4, DBUF>(fa.w, Hs, rank, lane, acc, p, s_ci, min(s1, n_seg - 1) * kSegSmall, fb);
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED>(fa.w, Hs, rank, lane, acc, p, s_ci, min(s1, n_seg - 1) * kSegSmall,
+                                                 fb);
     seg16_epilogue<KS, RESID>(p, lq, sg, lane, fa, acc);
     if (s1 >= n_seg) break;
     const int s2 = s1 + n_waves;
-    seg16_mfma_pf<KS, RESID, VEC4, DBUF>(fb.w, Hs, rank, lane, acc, p, s_ci, min(s2, n_seg - 1) * kSegSmall, fa);
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED>(fb.w, Hs, rank, lane, acc, p, s_ci, min(s2, n_seg - 1) * kSegSmall,
+                                                 fa);
     seg16_epilogue<KS, RESID>(p, lq, s1, lane, fb, acc);
     if (s2 >= n_seg) break;
     sg = s2;
@@ -405,22 +417,22 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
 // Draft mode: one workgroup of eight wavefronts per CU (two per SIMD, for
 // latency hiding, sharing one copy of H); compiled to fit 256 registers per
 // wavefront.
-template <int KS, bool VEC4>
+template <int KS, bool VEC4, bool PACKED>
 __global__ void __launch_bounds__(kSeg16DraftWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bias_seg16(TileParams p) {
   constexpr int RS = KS * 32 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves>(p, Hs, s_ci);
+  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves, PACKED>(p, Hs, s_ci);
 }
 
 // Residual mode (holds the target values too): one wavefront per SIMD.
-template <int KS, bool VEC4>
+template <int KS, bool VEC4, bool PACKED>
 __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p) {
   constexpr int RS = KS * 32 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, true, VEC4, kSeg16Waves>(p, Hs, s_ci);
+  bias_seg16_body<KS, true, VEC4, kSeg16Waves, PACKED>(p, Hs, s_ci);
 }
 
 // ---------------------------------------------------------------------------
@@ -1004,6 +1016,29 @@ void launch(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hipE
     hipLaunchKernelGGL(kernel, grid, block, 0, s, p);
 }
 
+// KS = seg16_ksteps(rank): the packed W2 layout uses the same count
+template <bool RESID, bool VEC4, bool PACKED>
+void launch_seg16(const TileParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (seg16_ksteps(p.rank)) {
+    case 2:
+      if (RESID) launch(bias_seg16_res<2, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<2, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      break;
+    case 4:
+      if (RESID) launch(bias_seg16_res<4, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<4, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      break;
+    case 8:
+      if (RESID) launch(bias_seg16_res<8, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<8, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      break;
+    default:
+      if (RESID) launch(bias_seg16_res<16, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<16, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      break;
+  }
+}
+
 template <bool RESID, bool VEC4>
 hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (wdtype == DSPARK_W_F32) {
@@ -1015,25 +1050,10 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     const int wpb = RESID ? kSeg16Waves : kSeg16DraftWaves;
     const int blocks = max(1, min((p.n_seg + wpb - 1) / wpb, num_cu));
     const dim3 grid(blocks), block(wpb * 64);
-    if (RESID) {
-      if (p.rank <= 64)
-        launch(bias_seg16_res<2, VEC4>, grid, block, s, e0, e1, p);
-      else if (p.rank <= 128)
-        launch(bias_seg16_res<4, VEC4>, grid, block, s, e0, e1, p);
-      else if (p.rank <= 256)
-        launch(bias_seg16_res<8, VEC4>, grid, block, s, e0, e1, p);
-      else
-        launch(bias_seg16_res<16, VEC4>, grid, block, s, e0, e1, p);
-    } else {
-      if (p.rank <= 64)
-        launch(bias_seg16<2, VEC4>, grid, block, s, e0, e1, p);
-      else if (p.rank <= 128)
-        launch(bias_seg16<4, VEC4>, grid, block, s, e0, e1, p);
-      else if (p.rank <= 256)
-        launch(bias_seg16<8, VEC4>, grid, block, s, e0, e1, p);
-      else
-        launch(bias_seg16<16, VEC4>, grid, block, s, e0, e1, p);
-    }
+    if (p.w2p != nullptr)
+      launch_seg16<RESID, VEC4, true>(p, grid, block, s, e0, e1);
+    else
+      launch_seg16<RESID, VEC4, false>(p, grid, block, s, e0, e1);
     return hipGetLastError();
   }
   // 64-row path: one workgroup per 256 vocabulary rows

@@ -51,6 +51,9 @@ struct TileParams {
   // ([kSmallMaxR][rank] bf16, written by the previous position's finish)
   // instead of being gathered from W1 by prev
   const uint16_t* hbuf;
+  // 16-row path: when set, the W2 fragments are read from this
+  // fragment-packed copy (dspark_pack_w2) instead of W2
+  const uint16_t* w2p;
 };
 
 // Per-position draft finish: turns the segment records into y / q_tok / q_stats.
@@ -108,6 +111,7 @@ hipError_t launch_verify_stats(const VerifyParams& p, hipStream_t s);
 hipError_t launch_verify_finish(const VerifyParams& p, hipStream_t s);
 hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t s);
 hipError_t launch_schedule(const dspark_schedule_args& a, hipStream_t s);
+hipError_t launch_pack_w2(const dspark_pack_w2_args& a, hipStream_t s);
 // the static confidence cutoff; a.K is not read
 hipError_t launch_schedule_cutoff(const dspark_schedule_args& a, float conf_min, hipStream_t s);
 

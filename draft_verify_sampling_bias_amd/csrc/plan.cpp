@@ -54,6 +54,8 @@ int validate_draft(const dspark_draft_args* a, DraftPlan* plan) {
   if (!aligned(a->anchor, 4) || !aligned(a->temp, 4) || !aligned(a->u_draft, 4) ||
       !aligned(a->y, 4) || !aligned(a->q_tok, 4) || !aligned(a->q_stats, 8))
     return DSPARK_ERR_ALIGN;
+  if (a->W2_packed != nullptr && a->wdtype != DSPARK_W_BF16) return DSPARK_ERR_DTYPE;
+  if (!aligned(a->W2_packed, 16)) return DSPARK_ERR_ALIGN;
   if (a->workspace == nullptr || a->workspace_bytes < plan->total) return DSPARK_ERR_WORKSPACE;
   if (!aligned(a->workspace, kWsAlign)) return DSPARK_ERR_ALIGN;
   return DSPARK_OK;
@@ -105,8 +107,21 @@ int validate_verify(const dspark_verify_args* a, VerifyPlan* plan) {
       !aligned(a->u_accept, 4) || !aligned(a->u_final, 4) || !aligned(a->n_accept, 4) ||
       !aligned(a->out_tok, 4) || !aligned(a->p_tok, 4))
     return DSPARK_ERR_ALIGN;
+  if (a->W2_packed != nullptr && a->wdtype != DSPARK_W_BF16) return DSPARK_ERR_DTYPE;
+  if (!aligned(a->W2_packed, 16)) return DSPARK_ERR_ALIGN;
   if (a->workspace == nullptr || a->workspace_bytes < plan->total) return DSPARK_ERR_WORKSPACE;
   if (!aligned(a->workspace, kWsAlign)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+int validate_pack_w2(const dspark_pack_w2_args* a) {
+  if (a == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_pack_w2_args)) return DSPARK_ERR_ABI;
+  const int st = check_dims(0, 1, a->V, a->rank, DSPARK_W_BF16);
+  if (st != DSPARK_OK) return st;
+  if (!a->W2 || !a->W2_packed) return DSPARK_ERR_NULL;
+  if (!aligned(a->W2, 16) || !aligned(a->W2_packed, 16)) return DSPARK_ERR_ALIGN;
+  if (a->W2_packed_bytes < w2_packed_bytes(a->V, a->rank)) return DSPARK_ERR_WORKSPACE;
   return DSPARK_OK;
 }
 

@@ -49,6 +49,17 @@ constexpr int kChunk = 4096;
 constexpr int kChunkFloats = 4;              // floats per (row, chunk) record
 constexpr std::size_t kWsAlign = 256;
 
+// k-steps (32 ranks each) of the 16-row kernel for a rank: 2, 4, 8 or 16.
+// The fragment-packed W2 layout uses the same count.
+inline int seg16_ksteps(int rank) { return rank <= 64 ? 2 : (rank <= 128 ? 4 : (rank <= 256 ? 8 : 16)); }
+
+// Fragment-packed W2 (bf16): for each 16-row segment s and k-step ks, the
+// 64 lanes' 16-byte MFMA A fragments in lane order, 1 KiB contiguous; lane
+// L = 16 kq + l holds W2[16 s + l][32 ks + 8 kq .. +8] (zero past V or rank).
+inline std::size_t w2_packed_bytes(int V, int rank) {
+  return static_cast<std::size_t>((V + 15) / 16) * seg16_ksteps(rank) * 1024;
+}
+
 // Rows per segment for a batch of R requests with weights of type wdtype.
 inline int seg_rows_for(int32_t R, int32_t wdtype) {
   if (wdtype != DSPARK_W_BF16) return kSegLarge;
@@ -90,6 +101,7 @@ int validate_verify(const dspark_verify_args* a, VerifyPlan* plan);
 
 int validate_schedule(const dspark_schedule_args* a);
 int validate_cutoff(const dspark_cutoff_args* a);
+int validate_pack_w2(const dspark_pack_w2_args* a);
 
 int64_t schedule_rows(int32_t R, int32_t gamma, int64_t K);
 const char* status_string(int status);

@@ -120,6 +120,9 @@ typedef enum dspark_wdtype {
  *                attached to the dispatch of the fused bias + softmax kernel
  *                of position k (hipExtLaunchKernel start / stop events), so
  *                their interval is that kernel's execution time alone.
+ *   W2_packed    optional (NULL normally): the output of dspark_pack_w2 for
+ *                this W2, 16-byte aligned; read instead of W2 by the fused
+ *                kernel when the batch takes the 16-row path (bf16, R <= 64).
  * -------------------------------------------------------------------------- */
 typedef struct dspark_draft_args {
   uint32_t struct_size;
@@ -138,6 +141,7 @@ typedef struct dspark_draft_args {
   size_t workspace_bytes;
   void* stream;
   void* const* prof_events;
+  const void* W2_packed;
 } dspark_draft_args;
 
 /* --------------------------------------------------------------------------
@@ -246,6 +250,8 @@ typedef struct dspark_schedule_args {
  *   workspace, workspace_bytes    >= dspark_verify_workspace_size(); 256-byte
  *                                 aligned.
  *   stream     hipStream_t as void*.
+ *   W2_packed  optional, as for dspark_draft_block (read by the residual
+ *              pass of the 16-row path).
  * -------------------------------------------------------------------------- */
 typedef struct dspark_verify_args {
   uint32_t struct_size;
@@ -270,6 +276,7 @@ typedef struct dspark_verify_args {
   void* workspace;
   size_t workspace_bytes;
   void* stream;
+  const void* W2_packed;
 } dspark_verify_args;
 
 /* Workspace bytes needed by a call with these arguments (only the size
@@ -322,6 +329,45 @@ typedef struct dspark_cutoff_args {
   void* stream;
 } dspark_cutoff_args;
 
+
+/* --------------------------------------------------------------------------
+ * dspark_pack_w2: W2 rearranged once (at model load) into the layout the
+ * 16-row fused bias kernel reads, so that each of its load instructions
+ * reads 1 KiB contiguous instead of 64 bytes from each of 16 rows.
+ *
+ * For callers whose batches take the 16-row path (bf16 weights, R <= 64).
+ * The packed copy holds the same weights as W2; passed as W2_packed to
+ * dspark_draft_block and dspark_verify (which still need W2 itself for the
+ * finish kernels' one-segment rescans), it is read instead of W2 by the
+ * fused kernel.  It is not read on the other paths (R > 64, fp32 weights).
+ *
+ * Layout: KS = 2, 4, 8 or 16 for rank <= 64, 128, 256, 512; for segment
+ * s = 0 .. ceil(V / 16) - 1 and k-step ks = 0 .. KS - 1, 64 slots of 8 bf16
+ * (16 bytes) at byte offset ((s * KS + ks) * 64 + L) * 16, slot L = 16 q + i
+ * holding W2[16 s + i][32 ks + 8 q .. 32 ks + 8 q + 7], zero where the row
+ * is >= V or the column >= rank.
+ *
+ * Arguments:
+ *   V, rank    host ints (as for dspark_draft_block; bf16 weights only).
+ *   W2         bf16 [V, rank] device, 16-byte aligned.
+ *   W2_packed  device, 16-byte aligned, dspark_w2_packed_bytes(V, rank)
+ *              bytes, out; owned by the caller.
+ *   stream     hipStream_t as void*.
+ * -------------------------------------------------------------------------- */
+typedef struct dspark_pack_w2_args {
+  uint32_t struct_size;
+  int32_t V, rank;
+  const void* W2;
+  void* W2_packed;
+  size_t W2_packed_bytes;
+  void* stream;
+} dspark_pack_w2_args;
+
+int dspark_pack_w2(const dspark_pack_w2_args* args);
+
+/* Host-side: bytes of the packed W2 of dspark_pack_w2; 0 for an invalid
+ * V or rank. */
+size_t dspark_w2_packed_bytes(int32_t V, int32_t rank);
 
 int dspark_draft_block(const dspark_draft_args* args);
 int dspark_schedule(const dspark_schedule_args* args);

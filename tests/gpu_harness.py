@@ -42,13 +42,14 @@ def upload(inp: synth.StepInputs, device="cuda:0"):
                 u_accept=f(inp.u_accept), u_final=f(inp.u_final), c=f(inp.c), target=f(inp.target))
 
 
-def gpu_step(d, K, gamma, conf_min=None):
+def gpu_step(d, K, gamma, conf_min=None, W2_packed=None):
     """draft -> schedule (top-K with capacity K, or the static confidence
     cutoff when conf_min is given) -> gather rows -> verify on the GPU;
     returns numpy results."""
     import draft_verify_sampling_bias_amd as ds
     torch = torch_mod()
-    y, q_tok, q_stats = ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"])
+    y, q_tok, q_stats = ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"],
+                                              W2_packed=W2_packed)
     if conf_min is None:
         sch = ds.dspark_schedule(d["c"], K, d["anchor"], y)
     else:
@@ -58,7 +59,8 @@ def gpu_step(d, K, gamma, conf_min=None):
             sch[f] = sch[f][:n]
     rows = d["target"][sch["row_req"].long(), sch["row_pos"].long()].contiguous()
     n_acc, out_tok, p_tok = ds.dspark_verify(rows, sch["row_offsets"], d["U"], d["W1"], d["W2"], d["anchor"],
-                                             d["temp"], y, q_tok, q_stats, d["u_accept"], d["u_final"])
+                                             d["temp"], y, q_tok, q_stats, d["u_accept"], d["u_final"],
+                                             W2_packed=W2_packed)
     torch.cuda.synchronize()
     res = dict(y=y, q_tok=q_tok, q_stats=q_stats, n_accept=n_acc, out_tok=out_tok, p_tok=p_tok, rows=rows,
                **{k: v for k, v in sch.items() if v is not None})

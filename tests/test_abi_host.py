@@ -177,6 +177,37 @@ def test_cutoff_rejects_invalid_arguments(kw, status):
                                                          conf_min=0.5)) == ds.Status.OK
 
 
+def test_packed_w2_bytes():
+    # ceil(V/16) segments x k-steps (2/4/8/16 for rank <= 64/128/256/512) x 1 KiB
+    assert ds.dspark_w2_packed_bytes(151936, 512) == 9496 * 16 * 1024
+    assert ds.dspark_w2_packed_bytes(1000, 96) == 63 * 4 * 1024
+    assert ds.dspark_w2_packed_bytes(5, 8) == 1 * 2 * 1024
+    assert ds.dspark_w2_packed_bytes(0, 64) == 0
+    assert ds.dspark_w2_packed_bytes(100, 12) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=4), ds.Status.ERR_ABI),
+    (dict(rank=520), ds.Status.ERR_UNSUPPORTED),
+    (dict(V=0), ds.Status.ERR_SHAPE),
+    (dict(W2=None), ds.Status.ERR_NULL),
+    (dict(W2_packed=FAKE + 8), ds.Status.ERR_ALIGN),
+    (dict(W2_packed_bytes=63 * 4 * 1024 - 1), ds.Status.ERR_WORKSPACE),
+])
+def test_pack_rejects_invalid_arguments(kw, status):
+    base = dict(struct_size=ctypes.sizeof(ds.PackArgs), V=1000, rank=96, W2=FAKE, W2_packed=FAKE,
+                W2_packed_bytes=63 * 4 * 1024)
+    base.update(kw)
+    assert _call("dspark_pack_w2", ds.PackArgs(**base)) == status
+
+
+def test_packed_w2_needs_bf16_and_alignment():
+    big = dict(workspace=FAKE, workspace_bytes=1 << 30)
+    assert _call("dspark_draft_block", _draft_args(wdtype=0, W2_packed=FAKE, **big)) == ds.Status.ERR_DTYPE
+    assert _call("dspark_draft_block", _draft_args(W2_packed=FAKE + 4, **big)) == ds.Status.ERR_ALIGN
+    assert _call("dspark_verify", _verify_args(wdtype=0, W2_packed=FAKE, **big)) == ds.Status.ERR_DTYPE
+
+
 def test_null_args_pointer():
     lib = ds.get_lib()
     assert lib.dspark_draft_block(None) == ds.Status.ERR_NULL

@@ -158,6 +158,61 @@ def test_cutoff_step(cfg, conf_min):
     t.check()
 
 
+def _pack_reference(W2_bits, rank):
+    """The fragment-packed layout built with NumPy from its definition in
+    include/dspark.h (bf16 bit patterns)."""
+    V = W2_bits.shape[0]
+    KS = 2 if rank <= 64 else 4 if rank <= 128 else 8 if rank <= 256 else 16
+    n_seg = (V + 15) // 16
+    full = np.zeros((n_seg * 16, KS * 32), dtype=np.uint16)
+    full[:V, :rank] = W2_bits
+    # [s, i, ks, q, e] -> [s, ks, q, i, e]: slot L = 16 q + i of (s, ks)
+    return full.reshape(n_seg, 16, KS, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("V,rank", [(37, 8), (1000, 96), (4160, 512), (513, 128), (5, 16)])
+def test_pack_w2_layout(V, rank):
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    rng = np.random.default_rng(V + rank)
+    bits = rng.integers(0, 1 << 16, (V, rank), dtype=np.uint16)
+    W2 = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    got = ds.dspark_pack_w2(W2).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, _pack_reference(bits, rank))
+
+
+@pytest.mark.parametrize("case", [(11, 3, 4, 1000, 64, "sampled"), (13, 40, 3, 4099, 40, "temps"),
+                                  (18, 9, 16, 513, 128, "temps"), (19, 4, 5, 5, 16, "sampled"),
+                                  (29, 64, 2, 20000, 512, "mixed")], ids=["p11", "p13", "p18", "p19", "p29"])
+def test_packed_w2_identical(case):
+    """The fragment-packed W2 gives bit-identical results to W2 itself (the
+    same products in the same order), and those match the oracle."""
+    import draft_verify_sampling_bias_amd as ds
+    seed, R, gamma, V, rank, pol = case
+    inp = synth.make_custom(seed, R, gamma, V, rank, policy=pol, K_mode="uniformK", U_std=3.0, noise_std=1.0)
+    d = upload(inp)
+    g0 = gpu_step(d, inp.K, inp.gamma)
+    g1 = gpu_step(d, inp.K, inp.gamma, W2_packed=ds.dspark_pack_w2(d["W2"]))
+    for k in g0:
+        np.testing.assert_array_equal(g1[k], g0[k], err_msg=k)
+    t = Tally()
+    compare_draft(inp, g1, range(R), t)
+    compare_verify(inp, g1, range(R), t)
+    print(f"[packed {inp.name}] {t.summary()}", flush=True)
+    t.check()
+
+
+def test_packed_w2_config3():
+    import draft_verify_sampling_bias_amd as ds
+    inp = synth.make_config(3)
+    d = upload(inp)
+    g0 = gpu_step(d, inp.K, inp.gamma)
+    g1 = gpu_step(d, inp.K, inp.gamma, W2_packed=ds.dspark_pack_w2(d["W2"]))
+    for k in g0:
+        np.testing.assert_array_equal(g1[k], g0[k], err_msg=k)
+    print("[packed config3] identical", flush=True)
+
+
 def _sample(R, n, seed):
     rng = np.random.default_rng(seed)
     return sorted(rng.choice(R, size=min(n, R), replace=False).tolist())
