@@ -38,7 +38,12 @@ Readings of points the pages leave open (each also listed in the design notes):
     it owns l[r] + 1 verify rows;
   * the static confidence cutoff compares each position's own confidence c
     (clamped as for survival) with conf_min, keeps the leading positions that
-    reach it (>=) and stops at the first that does not; no global capacity.
+    reach it (>=) and stops at the first that does not; no global capacity;
+  * hardware-aware capacity: Theta(K) = E(K) * SPS(R + K) with E(K) = R +
+    the sum of the K largest survival values (the scheduler's expected token
+    count) and R + K verify rows; the causal greedy adds candidates while
+    Theta strictly improves and stops at the first K with Theta(K+1) <=
+    Theta(K); the throughput table and the (lagged) survival are inputs.
 """
 from __future__ import annotations
 
@@ -50,7 +55,8 @@ import numpy as np
 
 __all__ = [
     "NEAR", "widen", "markov_bias", "inverse_cdf", "draft_block", "survival",
-    "schedule", "schedule_cutoff", "verify", "step", "DraftResult", "ScheduleResult", "VerifyResult",
+    "schedule", "schedule_cutoff", "capacity", "verify", "step", "DraftResult", "ScheduleResult",
+    "VerifyResult", "CapacityResult",
 ]
 
 #: width of the band around a decision boundary inside which a flip caused by
@@ -279,6 +285,58 @@ def schedule_cutoff(c, conf_min, anchor, y) -> ScheduleResult:
     return ScheduleResult(a=a, l=l.astype(np.int32), row_offsets=off,
                           row_req=row_req, row_pos=row_pos, row_tok=row_tok,
                           expected_tokens=R + math.fsum(sel_a), Kc=int(l.sum()))
+
+
+@dataclass
+class CapacityResult:
+    K: int                   # capacity in draft positions
+    theta: float             # Theta(K)
+    expected: float          # E(K)
+    near_tie: bool           # the deciding comparison was within NEAR_THETA of a tie
+
+
+#: relative width of a Theta comparison treated as a near tie
+NEAR_THETA = 1e-9
+
+
+def capacity(a_lag, sps) -> CapacityResult:
+    """Hardware-aware capacity by the causal greedy (explainer section 9:
+    choose the prefix-closed work that maximises expected effective output
+    times the engine's measured step rate SPS(B) for B query tokens; add
+    candidates in order of cumulative survival and stop when Theta no longer
+    improves.  Section 10: the capacity for an upcoming step is predicted
+    from the confidence of an earlier step; the survival given here is that
+    earlier one).
+
+    a_lag [R, gamma]: survival values (clamped to [0, 1], NaN -> 0); sps
+    [B_max + 1]: steps per second for a verify batch of B rows.  Candidates
+    are taken largest survival first; their order among equal values does
+    not change any E.  E(K) = R + sum of the K largest values (exactly
+    rounded), Theta(K) = E(K) * sps[R + K], both in fp64; K runs up to
+    min(R * gamma, B_max - R)."""
+    a = np.asarray(a_lag, dtype=np.float32)
+    a = np.where(np.isnan(a), np.float32(0), np.clip(a, np.float32(0), np.float32(1)))
+    R, gamma = a.shape
+    sps = np.asarray(sps, dtype=np.float32)
+    vals = sorted((float(x) for x in a.ravel()), reverse=True)
+    kmax = max(0, min(R * gamma, len(sps) - 1 - R))
+    K = 0
+    near = False
+
+    def E(k):
+        return R + math.fsum(vals[:k])
+
+    # every comparison made decides the result; a near tie in any of them is
+    # reported
+    while K < kmax:
+        now = E(K) * float(sps[R + K])
+        nxt = E(K + 1) * float(sps[R + K + 1])
+        near = near or abs(nxt - now) <= NEAR_THETA * max(abs(now), abs(nxt))
+        if not nxt > now:
+            break
+        K += 1
+    return CapacityResult(K=K, theta=E(K) * float(sps[R + K]) if R + K < len(sps) else float("nan"),
+                          expected=E(K), near_tie=near)
 
 
 @dataclass

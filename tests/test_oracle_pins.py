@@ -557,6 +557,107 @@ def test_cutoff_is_monotone_and_causal():
 
 
 # ---------------------------------------------------------------------------
+# hardware-aware capacity (explainer sections 9-10: causal greedy on
+# Theta = expected tokens x SPS(B))
+# ---------------------------------------------------------------------------
+def _theta_all(a, sps):
+    """Theta(K) for every K, vectorised: values sorted descending, fp64
+    running sums (an implementation independent of the oracle's loop)."""
+    R, gamma = a.shape
+    v = np.sort(np.nan_to_num(np.clip(a.astype(np.float64), 0, 1), nan=0.0).ravel())[::-1]
+    kmax = max(0, min(R * gamma, len(sps) - 1 - R))
+    E = R + np.concatenate([[0.0], np.cumsum(v)])[:kmax + 1]
+    return E * sps[R:R + kmax + 1].astype(np.float64), v, kmax
+
+
+def _first_stop(theta):
+    for K in range(len(theta) - 1):
+        if not theta[K + 1] > theta[K]:
+            return K
+    return len(theta) - 1
+
+
+def test_capacity_constant_rate_takes_every_positive_candidate():
+    rng = np.random.default_rng(31)
+    for _ in range(20):
+        R, gamma = int(rng.integers(1, 9)), int(rng.integers(1, 6))
+        c, _, _ = _rand_sched(rng, R, gamma)
+        c.flat[::4] = 0.0                                  # some zero survival
+        a = oracle.survival(c)
+        sps = np.full(R * (gamma + 1) + 3, 7.0, np.float32)
+        r = oracle.capacity(a, sps)
+        assert r.K == int((a > 0).sum())
+
+
+def test_capacity_per_row_rate_closed_form():
+    """SPS(B) = 1 / B: (E + v) / (B + 1) > E / B iff v > E / B, so the greedy
+    stops at the first value not above the current mean E(K) / (R + K)."""
+    rng = np.random.default_rng(32)
+    checked = 0
+    for _ in range(40):
+        R, gamma = int(rng.integers(1, 12)), int(rng.integers(1, 8))
+        c, _, _ = _rand_sched(rng, R, gamma)
+        a = oracle.survival(c)
+        sps = np.array([1.0 / max(b, 1) for b in range(R * (gamma + 1) + 1)], np.float32)
+        r = oracle.capacity(a, sps)
+        v = np.sort(a.astype(np.float64).ravel())[::-1]
+        K, E, tie = 0, float(R), False
+        while K < R * gamma:
+            tie = tie or abs(v[K] * (R + K) - E) <= 1e-6 * E
+            if not v[K] > E / (R + K):
+                break
+            E += v[K]
+            K += 1
+        if not tie:
+            assert r.K == K
+            checked += 1
+    assert checked >= 30
+
+
+def test_capacity_step_table_by_brute_force():
+    rng = np.random.default_rng(33)
+    for trial in range(60):
+        R, gamma = int(rng.integers(1, 10)), int(rng.integers(1, 7))
+        c, _, _ = _rand_sched(rng, R, gamma)
+        a = oracle.survival(c)
+        n = R * (gamma + 1) + int(rng.integers(0, 4))
+        # a step-shaped rate (graph-capture buckets), falling with B
+        edges = np.sort(rng.choice(np.arange(1, n + 1), size=min(4, n), replace=False))
+        sps = np.empty(n + 1, np.float32)
+        level = 1000.0
+        for b in range(n + 1):
+            if b in edges:
+                level *= float(rng.uniform(0.5, 0.95))
+            sps[b] = level
+        r = oracle.capacity(a, sps)
+        theta, _, kmax = _theta_all(a, sps)
+        if not r.near_tie:
+            assert r.K == _first_stop(theta), (trial, r.K)
+            assert r.theta == pytest.approx(theta[r.K], rel=1e-12)
+
+
+def test_capacity_expected_tokens_match_the_schedule():
+    """E(K) is the scheduler's expected token count at capacity K."""
+    rng = np.random.default_rng(34)
+    R, gamma = 13, 5
+    c, anc, y = _rand_sched(rng, R, gamma)
+    sps = np.array([100.0 / (1 + 0.03 * b) for b in range(R * (gamma + 1) + 1)], np.float32)
+    r = oracle.capacity(oracle.survival(c), sps)
+    s = oracle.schedule(c, r.K, anc, y)
+    assert s.expected_tokens == pytest.approx(r.expected, rel=1e-12, abs=1e-12)
+    # scaling the rate table changes Theta, never K
+    r2 = oracle.capacity(oracle.survival(c), (sps * np.float32(4.0)).astype(np.float32))
+    assert r2.K == r.K
+
+
+def test_capacity_table_bound():
+    a = np.full((4, 3), 0.9, np.float32)
+    assert oracle.capacity(a, np.ones(5, np.float32)).K == 0        # only B = R fits
+    assert oracle.capacity(a, np.ones(9, np.float32)).K == 4        # B <= 8
+    assert oracle.capacity(a, np.ones(40, np.float32)).K == 12      # all R * gamma
+
+
+# ---------------------------------------------------------------------------
 # bias and input conversion
 # ---------------------------------------------------------------------------
 def test_markov_bias_is_low_rank_product():
