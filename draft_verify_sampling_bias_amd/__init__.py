@@ -20,6 +20,7 @@ __all__ = [
     "dspark_verify", "dspark_schedule_rows", "dspark_draft_workspace_size",
     "dspark_verify_workspace_size", "dspark_status_string", "dspark_abi_version",
     "DraftArgs", "ScheduleArgs", "CutoffArgs", "VerifyArgs", "EXPORTED_SYMBOLS",
+    "dspark_capacity", "CapacityArgs",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = (
     "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
     "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_schedule_rows",
     "dspark_status_string", "dspark_abi_version", "dspark_pack_w2", "dspark_w2_packed_bytes",
+    "dspark_capacity",
 )
 
 
@@ -77,6 +79,12 @@ class VerifyArgs(ctypes.Structure):
                 ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("W2_packed", _p)]
 
 
+class CapacityArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("n_sps", ctypes.c_int32), ("a_lag", _p), ("sps", _p), ("K", _p), ("expected", _p),
+                ("theta", _p), ("stream", _p)]
+
+
 class PackArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("V", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("W2", _p), ("W2_packed", _p), ("W2_packed_bytes", ctypes.c_size_t), ("stream", _p)]
@@ -97,9 +105,10 @@ def _load():
     L.dspark_w2_packed_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
     L.dspark_w2_packed_bytes.restype = ctypes.c_size_t
     L.dspark_verify.argtypes = [P(VerifyArgs)]
+    L.dspark_capacity.argtypes = [P(CapacityArgs)]
     for f in ("dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
               "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_abi_version",
-              "dspark_pack_w2"):
+              "dspark_pack_w2", "dspark_capacity"):
         getattr(L, f).restype = ctypes.c_int
     L.dspark_schedule_rows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     L.dspark_schedule_rows.restype = ctypes.c_int64
@@ -353,6 +362,35 @@ def dspark_schedule_cutoff(c, conf_min: float, anchor, y, *, out=None, want_expe
                    row_pos=_ptr(out["row_pos"]), row_tok=_ptr(out["row_tok"]),
                    expected_tokens=_ptr(out.get("expected_tokens")), stream=_stream(dev, stream))
     _check("dspark_schedule_cutoff", get_lib().dspark_schedule_cutoff(ctypes.byref(a)))
+    return out
+
+
+def dspark_capacity(a_lag, sps, *, out=None, stream=None):
+    """Hardware-aware capacity for a later step (include/dspark.h,
+    dspark_capacity).  a_lag [R, gamma] fp32: survival of an earlier step;
+    sps [n_sps] fp32: step rate of a verify batch of B rows, n_sps >= R + 1.
+    Returns a dict of device tensors: K int32 [1], expected float64 [1] (E(K))
+    and theta float64 [1] (Theta(K))."""
+    torch = _torch()
+    dev = sps.device
+    R, gamma = a_lag.shape
+    _want(a_lag, "a_lag", torch.float32, (R, gamma), dev)
+    (n_sps,) = sps.shape
+    _want(sps, "sps", torch.float32, (n_sps,), dev)
+    if out is None:
+        out = dict(K=torch.empty(1, dtype=torch.int32, device=dev),
+                   expected=torch.empty(1, dtype=torch.float64, device=dev),
+                   theta=torch.empty(1, dtype=torch.float64, device=dev))
+    else:
+        _want(out["K"], "K", torch.int32, (1,), dev)
+        for f in ("expected", "theta"):
+            if out.get(f) is not None:
+                _want(out[f], f, torch.float64, (1,), dev)
+    a = CapacityArgs(struct_size=ctypes.sizeof(CapacityArgs), R=R, gamma=gamma, n_sps=n_sps,
+                     a_lag=_ptr(a_lag) if R > 0 else None, sps=_ptr(sps), K=_ptr(out["K"]),
+                     expected=_ptr(out.get("expected")), theta=_ptr(out.get("theta")),
+                     stream=_stream(dev, stream))
+    _check("dspark_capacity", get_lib().dspark_capacity(ctypes.byref(a)))
     return out
 
 

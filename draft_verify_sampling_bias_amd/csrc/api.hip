@@ -160,6 +160,12 @@ int dspark_schedule_cutoff(const dspark_cutoff_args* a) {
   return hip_status(launch_schedule_cutoff(s, a->conf_min, static_cast<hipStream_t>(a->stream)));
 }
 
+int dspark_capacity(const dspark_capacity_args* a) {
+  const int st = validate_capacity(a);
+  if (st != DSPARK_OK) return st;
+  return hip_status(launch_capacity(*a, static_cast<hipStream_t>(a->stream)));
+}
+
 int dspark_verify(const dspark_verify_args* a) {
   VerifyPlan plan;
   int st = validate_verify(a, &plan);

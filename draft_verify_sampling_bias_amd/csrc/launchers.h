@@ -114,5 +114,7 @@ hipError_t launch_schedule(const dspark_schedule_args& a, hipStream_t s);
 hipError_t launch_pack_w2(const dspark_pack_w2_args& a, hipStream_t s);
 // the static confidence cutoff; a.K is not read
 hipError_t launch_schedule_cutoff(const dspark_schedule_args& a, float conf_min, hipStream_t s);
+// the hardware-aware capacity (one workgroup)
+hipError_t launch_capacity(const dspark_capacity_args& a, hipStream_t s);
 
 }  // namespace dspark

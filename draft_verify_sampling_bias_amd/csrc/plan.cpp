@@ -163,6 +163,20 @@ int validate_cutoff(const dspark_cutoff_args* a) {
   return DSPARK_OK;
 }
 
+int validate_capacity(const dspark_capacity_args* a) {
+  if (a == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_capacity_args)) return DSPARK_ERR_ABI;
+  if (a->R < 0 || a->gamma < 1) return DSPARK_ERR_SHAPE;
+  if (a->gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(a->R) * a->gamma > DSPARK_CAPACITY_MAX_CANDIDATES) return DSPARK_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(a->n_sps) < static_cast<int64_t>(a->R) + 1) return DSPARK_ERR_SHAPE;
+  if (!a->sps || !a->K || (a->R > 0 && !a->a_lag)) return DSPARK_ERR_NULL;
+  if (!aligned(a->sps, 4) || !aligned(a->K, 4) || (a->a_lag && !aligned(a->a_lag, 4)) ||
+      (a->expected && !aligned(a->expected, 8)) || (a->theta && !aligned(a->theta, 8)))
+    return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
 int64_t schedule_rows(int32_t R, int32_t gamma, int64_t K) {
   if (R < 0 || gamma < 1) return -1;
   const int64_t n = static_cast<int64_t>(R) * gamma;

@@ -53,6 +53,7 @@ extern "C" {
 #define DSPARK_MAX_RANK 512          /* Markov rank r in [8, 512], r % 8 == 0       */
 #define DSPARK_MAX_VOCAB (1 << 30)   /* V in [1, 2^30]                              */
 #define DSPARK_SCHED_KEYS_PER_THREAD 16  /* dspark_schedule: ceil(R/1024)*gamma <= 16 */
+#define DSPARK_CAPACITY_MAX_CANDIDATES 16384  /* dspark_capacity: R * gamma <= 16384 */
 
 typedef enum dspark_status {
   DSPARK_OK = 0,
@@ -329,6 +330,63 @@ typedef struct dspark_cutoff_args {
   void* stream;
 } dspark_cutoff_args;
 
+
+/* --------------------------------------------------------------------------
+ * dspark_capacity: hardware-aware capacity K for a later step.
+ *
+ * [EXP] section 9: the scheduler should pick the prefix-closed verify work
+ * that maximises the expected effective output times the engine's measured
+ * step rate SPS(B) for a batch of B query tokens (step-shaped over the
+ * graph-capture sizes); candidates are added in order of cumulative
+ * survival and the greedy stops when that product no longer improves.
+ * Section 10: so that the physical batch shape is known ahead and no host
+ * round trip stalls the step, the capacity for an upcoming step is predicted
+ * from the confidence of an earlier step (lagged); a_lag is that earlier
+ * step's survival (the a output of dspark_schedule), and the K written here
+ * is meant to be read back asynchronously and passed to dspark_schedule of a
+ * later step.
+ *
+ *   v_1 >= v_2 >= ...  the R * gamma values of a_lag clamped to [0, 1]
+ *                      (NaN -> 0), sorted descending;
+ *   E(K)     = R + fl64(v_1 + ... + v_K)    (the exact sum rounded once to
+ *              fp64, then an fp64 add; the expected tokens of the schedule
+ *              with capacity K: R bonus/correction tokens plus survival);
+ *   Theta(K) = E(K) * SPS[R + K]            (fp64 multiply; the batch has R
+ *              anchor rows and K draft rows);
+ *   kmax     = min(R * gamma, n_sps - 1 - R);
+ *   K        = the first K in 0 .. kmax-1 with NOT Theta(K+1) > Theta(K),
+ *              else kmax (greedy: add while Theta strictly improves).
+ * The result depends only on the multiset of values, not on their order.
+ *
+ * Arguments (device arrays unless stated):
+ *   R, gamma   host ints; R >= 0, gamma in [1, DSPARK_MAX_GAMMA],
+ *              R * gamma <= DSPARK_CAPACITY_MAX_CANDIDATES.
+ *   n_sps      host int: entries of sps; n_sps >= R + 1 (DSPARK_ERR_SHAPE
+ *              otherwise: the table must at least cover the anchor rows).
+ *   a_lag      float [R, gamma]  survival of an earlier step (may be NULL
+ *              when R == 0).
+ *   sps        float [n_sps]     steps per second of a verify batch of B
+ *              rows, B = 0 .. n_sps-1 (any positive unit; scaling the table
+ *              by a power of two never changes K).
+ *   K          int32 [1]   out.
+ *   expected   double [1]  optional out: E(K).
+ *   theta      double [1]  optional out: Theta(K).
+ *   stream     hipStream_t as void*.
+ * One workgroup; no workspace.
+ * -------------------------------------------------------------------------- */
+typedef struct dspark_capacity_args {
+  uint32_t struct_size;
+  int32_t R, gamma;
+  int32_t n_sps;
+  const float* a_lag;
+  const float* sps;
+  int32_t* K;
+  double* expected;
+  double* theta;
+  void* stream;
+} dspark_capacity_args;
+
+int dspark_capacity(const dspark_capacity_args* args);
 
 /* --------------------------------------------------------------------------
  * dspark_pack_w2: W2 rearranged once (at model load) into the layout the

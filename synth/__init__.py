@@ -38,6 +38,7 @@ import numpy as np
 __all__ = [
     "StepInputs", "CONFIGS", "make_config", "make_custom", "bf16_round_bits",
     "bf16_bits_to_f32", "weights_as_f32", "gather_rows", "fixed_offsets",
+    "sps_table", "random_sps_table",
 ]
 
 # stream order inside SeedSequence(seed).spawn(N_STREAMS)
@@ -232,3 +233,34 @@ def make_config(cfg: int, policy: Optional[str] = None, *, R: Optional[int] = No
                       zipf=spec.get("zipf"), policy=pol, K_mode=K_mode,
                       name=f"config{cfg}-{pol}")
     return inp
+
+
+# ---------------------------------------------------------------------------
+# step-rate tables for the hardware-aware capacity
+# ---------------------------------------------------------------------------
+def sps_table(n: int, *, t_fixed: float = 1.0, t_row: float = 1.0 / 8192, bucket: int = 16) -> np.ndarray:
+    """A synthetic verify step rate SPS(B) for B = 0 .. n-1 rows, fp32.
+
+    The pages give no measured table.  This one models a decode step whose
+    time is a fixed part (weights read once) plus a per-row part, with the
+    batch padded up to the next multiple of ``bucket`` (the graph-capture
+    sizes), so the rate is flat within a bucket and drops between buckets:
+    SPS(B) = 1 / (t_fixed + t_row * bucket * ceil(B / bucket))."""
+    B = np.arange(n, dtype=np.float64)
+    padded = np.ceil(B / bucket) * bucket
+    return (1.0 / (t_fixed + t_row * padded)).astype(np.float32)
+
+
+def random_sps_table(seed: int, n: int) -> np.ndarray:
+    """A seeded random step-shaped rate table of n entries, falling with B:
+    a few random bucket edges, each lowering the rate by 0.5 % to 10 %."""
+    rng = np.random.default_rng(seed)
+    sps = np.empty(n, np.float32)
+    n_edges = min(max(1, n // 8), 64)
+    edges = set(rng.choice(np.arange(1, max(n, 2)), size=min(n_edges, max(n - 1, 1)), replace=False).tolist())
+    level = 1000.0
+    for b in range(n):
+        if b in edges:
+            level *= float(rng.uniform(0.90, 0.995))
+        sps[b] = level
+    return sps

@@ -177,6 +177,34 @@ def test_cutoff_rejects_invalid_arguments(kw, status):
                                                          conf_min=0.5)) == ds.Status.OK
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), ds.Status.ERR_ABI),
+    (dict(gamma=0), ds.Status.ERR_SHAPE),
+    (dict(R=-1), ds.Status.ERR_SHAPE),
+    (dict(gamma=17), ds.Status.ERR_UNSUPPORTED),
+    (dict(R=1025, gamma=16), ds.Status.ERR_UNSUPPORTED),    # R * gamma > 16384
+    (dict(n_sps=8), ds.Status.ERR_SHAPE),                    # n_sps < R + 1
+    (dict(a_lag=None), ds.Status.ERR_NULL),
+    (dict(sps=None), ds.Status.ERR_NULL),
+    (dict(K=None), ds.Status.ERR_NULL),
+    (dict(sps=FAKE + 2), ds.Status.ERR_ALIGN),
+    (dict(expected=FAKE + 4), ds.Status.ERR_ALIGN),
+    (dict(theta=FAKE + 4), ds.Status.ERR_ALIGN),
+])
+def test_capacity_rejects_invalid_arguments(kw, status):
+    base = dict(struct_size=ctypes.sizeof(ds.CapacityArgs), R=8, gamma=4, n_sps=41, a_lag=FAKE, sps=FAKE, K=FAKE)
+    base.update(kw)
+    assert _call("dspark_capacity", ds.CapacityArgs(**base)) == status
+
+
+def test_capacity_largest_batch_passes_the_size_checks():
+    # R * gamma = 16384 exactly and n_sps = R + 1 are inside the limits: with a
+    # NULL K the call must fail on the pointer check, not on a size check
+    a = ds.CapacityArgs(struct_size=ctypes.sizeof(ds.CapacityArgs), R=1024, gamma=16, n_sps=1025,
+                        a_lag=FAKE, sps=FAKE, K=None)
+    assert _call("dspark_capacity", a) == ds.Status.ERR_NULL
+
+
 def test_packed_w2_bytes():
     # ceil(V/16) segments x k-steps (2/4/8/16 for rank <= 64/128/256/512) x 1 KiB
     assert ds.dspark_w2_packed_bytes(151936, 512) == 9496 * 16 * 1024
@@ -214,3 +242,4 @@ def test_null_args_pointer():
     assert lib.dspark_verify(None) == ds.Status.ERR_NULL
     assert lib.dspark_schedule(None) == ds.Status.ERR_NULL
     assert lib.dspark_schedule_cutoff(None) == ds.Status.ERR_NULL
+    assert lib.dspark_capacity(None) == ds.Status.ERR_NULL

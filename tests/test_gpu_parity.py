@@ -225,3 +225,102 @@ def test_full_size_configs(cfg, policy):
     if cfg == 5:  # include both greedy and sampled requests
         reqs = sorted(set(reqs) | {int(np.flatnonzero(inp.temp <= 0)[0]), int(np.flatnonzero(inp.temp > 0)[0])})
     _run(inp, reqs=reqs, label=f"config{cfg}-{policy or 'default'}")
+
+
+def _capacity_case(rng, R, gamma, kind):
+    c = (1 / (1 + np.exp(-rng.normal(1, 1, (R, gamma))))).astype(np.float32)
+    import oracle
+    a = oracle.survival(c) if R > 0 else np.zeros((0, gamma), np.float32)
+    if kind == "raw" and a.size:
+        # unsorted values with the clamping cases: NaN, negatives, -0, > 1,
+        # subnormals and exact duplicates
+        a = rng.random((R, gamma)).astype(np.float32)
+        a.flat[::11] = np.nan
+        a.flat[1::13] = np.float32(-0.25)
+        a.flat[2::17] = np.float32(-0.0)
+        a.flat[3::19] = np.float32(3.0)
+        a.flat[4::23] = np.float32(1e-40)
+        a.flat[5::7] = np.float32(0.5)
+    return a
+
+
+def _capacity_tables(rng, R, gamma):
+    n_full = R * (gamma + 1) + 1
+    yield "bucketed", synth.sps_table(n_full)
+    yield "bucketed-steep", synth.sps_table(n_full, t_row=1.0 / 1024)
+    yield "random-steps", synth.random_sps_table(int(rng.integers(1 << 30)), n_full)
+    yield "per-row", np.array([1.0 / max(b, 1) for b in range(n_full)], np.float32)
+    yield "constant", np.full(n_full, 3.0, np.float32)
+    yield "short", synth.sps_table(R + 1 + int(rng.integers(0, max(1, R * gamma // 2))))
+    yield "minimal", np.full(R + 1, 2.0, np.float32)
+    nan_t = synth.sps_table(n_full)
+    nan_t[R + (R * gamma) // 3] = np.nan
+    yield "with-nan", nan_t
+
+
+@pytest.mark.parametrize("R,gamma,kind", [(0, 3, "surv"), (1, 1, "surv"), (3, 5, "raw"), (64, 7, "surv"),
+                                          (64, 7, "raw"), (256, 5, "surv"), (1000, 3, "raw"),
+                                          (1024, 5, "surv")])
+def test_capacity(R, gamma, kind):
+    """Hardware-aware capacity against the oracle: K exact, E(K) and
+    Theta(K) bit-identical (both round the exact sum once to fp64), over
+    step-shaped, per-row, constant, short, minimal and NaN-holding tables."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    rng = np.random.default_rng(900 + 7 * R + gamma)
+    a = _capacity_case(rng, R, gamma, kind)
+    ad = torch.from_numpy(a).cuda()
+    for name, sps in _capacity_tables(rng, R, gamma):
+        g = {k: v.cpu().numpy() for k, v in ds.dspark_capacity(ad, torch.from_numpy(sps).cuda()).items()}
+        o = oracle.capacity(a, sps)
+        assert int(g["K"][0]) == o.K, (name, int(g["K"][0]), o.K)
+        assert float(g["expected"][0]) == o.expected, (name, float(g["expected"][0]), o.expected)
+        th = float(g["theta"][0])
+        assert th == o.theta or (np.isnan(th) and np.isnan(o.theta)), (name, th, o.theta)
+        print(f"[capacity R={R} gamma={gamma} {kind} {name}] K={o.K} E={o.expected:.6f}", flush=True)
+
+
+def test_capacity_largest_batch():
+    """R * gamma = 16384 candidates (the limit): a constant rate takes every
+    positive value, a bucketed rate stops inside the batch."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    rng = np.random.default_rng(990)
+    R, gamma = 1024, 16
+    a = _capacity_case(rng, R, gamma, "surv")
+    a.flat[::9] = np.float32(0.0)
+    ad = torch.from_numpy(a).cuda()
+    for sps in (np.full(R * (gamma + 1) + 1, 5.0, np.float32), synth.sps_table(R * (gamma + 1) + 1, t_row=1 / 65536)):
+        g = {k: v.cpu().numpy() for k, v in ds.dspark_capacity(ad, torch.from_numpy(sps).cuda()).items()}
+        o = oracle.capacity(a, sps)
+        assert int(g["K"][0]) == o.K
+        assert float(g["expected"][0]) == o.expected and float(g["theta"][0]) == o.theta
+        print(f"[capacity R={R} gamma={gamma}] K={o.K}", flush=True)
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_capacity_drives_the_schedule(cfg):
+    """The lagged pipeline on the GPU: survival from dspark_schedule, capacity
+    from that survival, then a schedule with that capacity; every result
+    against the oracle."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    inp = synth.make_config(cfg)
+    c = torch.from_numpy(inp.c).cuda()
+    anc = torch.from_numpy(inp.anchor).cuda()
+    y = torch.from_numpy(inp.anchor[:, None].repeat(inp.gamma, 1)).cuda()
+    s0 = ds.dspark_schedule(c, inp.R * inp.gamma, anc, y)
+    sps = synth.sps_table(inp.R * (inp.gamma + 1) + 1)
+    cap = ds.dspark_capacity(s0["a"], torch.from_numpy(sps).cuda())
+    K = int(cap["K"].cpu()[0])
+    o = oracle.capacity(oracle.survival(inp.c), sps)
+    assert K == o.K and float(cap["expected"].cpu()[0]) == o.expected
+    s1 = {k: v.cpu().numpy() for k, v in ds.dspark_schedule(c, K, anc, y).items()}
+    os_ = oracle.schedule(inp.c, K, inp.anchor, y.cpu().numpy())
+    np.testing.assert_array_equal(s1["l"], os_.l)
+    np.testing.assert_array_equal(s1["row_offsets"], os_.row_offsets)
+    assert abs(float(s1["expected_tokens"][0]) - o.expected) <= 1e-5 * o.expected
+    print(f"[capacity config{cfg}] K={K} rows={int(s1['row_offsets'][-1])} E={o.expected:.3f}", flush=True)
