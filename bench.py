@@ -111,9 +111,10 @@ class HipTimingEvents:
         self.handles = []
 
 
-def cpu_baseline(inp, n_sample, seed=0, conf_min=None):
+def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None):
     """The CPU oracle on a bounded sample of requests (single BLAS thread),
-    with the same scheduler as the GPU step."""
+    with the same scheduler as the GPU step (with capacity_sps: the capacity
+    from the survival, then the top-K schedule with it)."""
     import oracle
     from threadpoolctl import threadpool_limits
     rng = np.random.default_rng(seed)
@@ -123,7 +124,10 @@ def cpu_baseline(inp, n_sample, seed=0, conf_min=None):
         d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
                                requests=reqs)
         y = np.where(d.y < 0, 0, d.y)
-        if conf_min is None:
+        if capacity_sps is not None:
+            cap = oracle.capacity(oracle.survival(inp.c), capacity_sps)
+            s = oracle.schedule(inp.c, cap.K, inp.anchor, y)
+        elif conf_min is None:
             s = oracle.schedule(inp.c, inp.K, inp.anchor, y)
         else:
             s = oracle.schedule_cutoff(inp.c, conf_min, inp.anchor, y)
@@ -153,6 +157,10 @@ def main():
     ap.add_argument("--conf-min", type=float, default=None,
                     help="schedule with the static confidence cutoff at this conf_min instead of the top-K "
                          "scheduler with the configuration's capacity K")
+    ap.add_argument("--capacity", action="store_true",
+                    help="hardware-aware capacity: each step runs dspark_capacity on the previous step's "
+                         "survival with a synthetic bucketed step-rate table, and the schedule uses the "
+                         "capacity that call produced (the lag: K is known on the host ahead of the step)")
     ap.add_argument("--no-pack", action="store_true",
                     help="read W2 itself instead of its fragment-packed copy (dspark_pack_w2)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -208,8 +216,31 @@ def main():
     q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
     wd = ds.W_BF16 if inp.wdtype == "bf16" else ds.W_F32
     ws_d = torch.empty(ds.draft_workspace_bytes(R, gamma, V, rank, wd), dtype=torch.uint8, device=dev)
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev)
+    out_tok = torch.empty(R, dtype=torch.int32, device=dev)
+    p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+
     cutoff = args.conf_min is not None
-    n_rows = R * (gamma + 1) if cutoff else ds.dspark_schedule_rows(R, gamma, inp.K)
+    if cutoff and args.capacity:
+        raise SystemExit("--conf-min and --capacity are alternative schedulers")
+    # hardware-aware capacity: the step rate table and the capacity outputs;
+    # K_sched is the capacity the schedule uses
+    K_sched = inp.K
+    sps = cap_out = None
+    if args.capacity:
+        sps = up(synth.sps_table(R * (gamma + 1) + 1))
+        cap_out = dict(K=torch.empty(1, dtype=torch.int32, device=dev),
+                       expected=torch.empty(1, dtype=torch.float64, device=dev),
+                       theta=torch.empty(1, dtype=torch.float64, device=dev))
+        # an earlier step's survival (the inputs repeat, so every step has
+        # the same) gives the capacity of the steps that follow
+        ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d,
+                              W2_packed=W2p)
+        first = ds.dspark_schedule(c, R * gamma, anchor, y)
+        ds.dspark_capacity(first["a"], sps, out=cap_out)
+        K_sched = int(cap_out["K"].item())
+
+    n_rows = R * (gamma + 1) if cutoff else ds.dspark_schedule_rows(R, gamma, K_sched)
     sch = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
                l=torch.empty(R, dtype=torch.int32, device=dev),
                row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
@@ -217,16 +248,19 @@ def main():
                row_pos=torch.empty(n_rows, dtype=torch.int32, device=dev),
                row_tok=torch.empty(n_rows, dtype=torch.int32, device=dev),
                expected_tokens=torch.empty(1, dtype=torch.float32, device=dev))
-    n_acc = torch.empty(R, dtype=torch.int32, device=dev)
-    out_tok = torch.empty(R, dtype=torch.int32, device=dev)
-    p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    if args.capacity:
+        sch["a"].copy_(first["a"])
 
     # target rows of the (deterministic) schedule: the stand-in for the target forward
     def schedule():
         if cutoff:
             ds.dspark_schedule_cutoff(c, args.conf_min, anchor, y, out=sch)
         else:
-            ds.dspark_schedule(c, inp.K, anchor, y, out=sch)
+            if args.capacity:
+                # the capacity for a later step, from the survival the
+                # previous step left in sch["a"]; not read back in the step
+                ds.dspark_capacity(sch["a"], sps, out=cap_out)
+            ds.dspark_schedule(c, K_sched, anchor, y, out=sch)
 
     ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d, W2_packed=W2p)
     schedule()
@@ -304,7 +338,8 @@ def main():
 
     cpu = None
     if not args.skip_cpu:
-        cpu = cpu_baseline(inp, args.cpu_sample, conf_min=args.conf_min)
+        cpu = cpu_baseline(inp, args.cpu_sample, conf_min=args.conf_min,
+                           capacity_sps=synth.sps_table(R * (gamma + 1) + 1) if args.capacity else None)
 
     line = {
         "metric": METRIC,
@@ -322,9 +357,11 @@ def main():
         "config": {
             "workload": f"config{args.config}: R={R} gamma={gamma} V={V} r={rank} {inp.wdtype} W1/W2, fp32 logits, "
                         + (f"static confidence cutoff conf_min={args.conf_min} ({n_rows} rows)" if cutoff else
+                           f"hardware-aware capacity K={K_sched} from the previous step's survival and a "
+                           f"bucketed step-rate table ({n_rows} rows)" if args.capacity else
                            f"{'fixed-length' if inp.K >= R * gamma else 'scheduled'} verify "
                            f"(K={inp.K}, {n_rows} rows)"),
-            "R": R, "gamma": gamma, "V": V, "rank": rank, "weights": inp.wdtype, "K": inp.K,
+            "R": R, "gamma": gamma, "V": V, "rank": rank, "weights": inp.wdtype, "K": K_sched,
             "W2_layout": "fragment-packed copy (dspark_pack_w2, made once before timing)" if use_pack
             else "row-major",
             "verify_rows": n_rows, "parallelism": "single GPU",
