@@ -33,7 +33,6 @@ namespace dspark {
 namespace {
 
 constexpr int kCapThreads = 1024;
-constexpr int kCapMaxPer = DSPARK_CAPACITY_MAX_CANDIDATES / kCapThreads;  // 16
 
 struct U192 {
   unsigned long long w0, w1, w2;
@@ -116,61 +115,84 @@ __device__ __forceinline__ U192 u192_shfl_up(const U192& x, int d) {
   return r;
 }
 
-__global__ void __launch_bounds__(kCapThreads) capacity_kernel(dspark_capacity_args a, int N) {
-  __shared__ unsigned int keys[DSPARK_CAPACITY_MAX_CANDIDATES];  // sort buffer
+// Compare-exchange of element g with its bitonic partner value pv at
+// stride j of merge size k: keeps the larger value where g is the first of
+// its pair in a descending block or the second in an ascending one.
+__device__ __forceinline__ unsigned int bitonic_keep(unsigned int v, unsigned int pv, int g, int j, int k) {
+  const bool take_max = ((g & j) == 0) == ((g & k) == 0);
+  return take_max ? max(v, pv) : min(v, pv);
+}
+
+// E = sorted values per thread (2, 4, 8 or 16): N = 1024 * E entries.
+template <int E>
+__global__ void __launch_bounds__(kCapThreads) capacity_kernel(dspark_capacity_args a) {
+  constexpr int N = kCapThreads * E;
+  // exchange buffer of the cross-wavefront stages ([e][thread], so that a
+  // wavefront's lanes touch consecutive words), then the rates SPS[R + i]
+  __shared__ unsigned int xbuf[DSPARK_CAPACITY_MAX_CANDIDATES + 1];
   __shared__ unsigned long long wtot[16 * 3];  // wavefront totals of the scan
   __shared__ int s_kmin[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = a.R;
   const int n = R * a.gamma;
   const int kmax = min(n, a.n_sps - 1 - R);
-  const int c = N / kCapThreads;  // sorted positions per thread (2 .. 16)
-  const int base = tid * c;
+  const int base = tid * E;  // this thread holds entries base .. base + E - 1
 
   // load, clamp (NaN -> 0, -0 -> +0) and pad with +0
-  for (int p = tid; p < N; p += kCapThreads) {
-    float v = 0.0f;
-    if (p < n) {
-      v = fminf(fmaxf(a.a_lag[p], 0.0f), 1.0f);
-      if (v == 0.0f) v = 0.0f;
+  unsigned int v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float x = 0.0f;
+    if (base + e < n) {
+      x = fminf(fmaxf(a.a_lag[base + e], 0.0f), 1.0f);
+      if (x == 0.0f) x = 0.0f;
     }
-    keys[p] = __float_as_uint(v);
+    v[e] = __float_as_uint(x);
   }
-  __syncthreads();
 
-  // bitonic sort, descending
+  // bitonic sort, descending: strides below E inside the thread, below 64 E
+  // across the lanes of a wavefront, the rest through LDS
   for (int k = 2; k <= N; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int p = tid; p < (N >> 1); p += kCapThreads) {
-        const int i = ((p & ~(j - 1)) << 1) | (p & (j - 1));
-        const int l = i + j;
-        const unsigned int x = keys[i], y = keys[l];
-        const bool desc = (i & k) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          keys[i] = y;
-          keys[l] = x;
+      if (j >= 64 * E) {
+        const int m = j / E;  // partner thread tid ^ m, another wavefront
+#pragma unroll
+        for (int e = 0; e < E; ++e) xbuf[e * kCapThreads + tid] = v[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = bitonic_keep(v[e], xbuf[e * kCapThreads + (tid ^ m)], base + e, j, k);
+        __syncthreads();
+      } else if (j >= E) {
+        const int m = j / E;  // partner lane lane ^ m
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = bitonic_keep(v[e], __shfl_xor(v[e], m), base + e, j, k);
+      } else {
+#pragma unroll
+        for (int jj = E / 2; jj >= 1; jj >>= 1) {
+          if (jj == j) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              if ((e & jj) == 0) {
+                const unsigned int x = v[e], y = v[e | jj];
+                const bool desc = ((base + e) & k) == 0;
+                v[e] = desc ? max(x, y) : min(x, y);
+                v[e | jj] = desc ? min(x, y) : max(x, y);
+              }
+            }
+          }
         }
       }
-      __syncthreads();
     }
   }
 
-  // this thread's sorted values stay in keys[base .. base + c - 1]
-  U192 local = {0ull, 0ull, 0ull};
-#pragma unroll
-  for (int q = 0; q < kCapMaxPer; ++q)
-    if (q < c) local = u192_add(local, u192_from_f32_bits(keys[base + q]));
-
-  // the rates this thread's stop tests read: SPS[R + base + q], q = 0 .. c
-  // (in flight during the scan)
-  float sps_v[kCapMaxPer + 1];
-#pragma unroll
-  for (int q = 0; q <= kCapMaxPer; ++q) {
-    const int i = base + q;
-    sps_v[q] = (q <= c && i <= kmax) ? a.sps[R + i] : 0.0f;
-  }
+  // the rates the stop tests read, SPS[R + i] for i = 0 .. kmax, into LDS
+  float* sps_s = reinterpret_cast<float*>(xbuf);
+  for (int i = tid; i <= kmax; i += kCapThreads) sps_s[i] = a.sps[R + i];
 
   // block-wide exclusive scan of the exact partial sums
+  U192 local = {0ull, 0ull, 0ull};
+#pragma unroll
+  for (int e = 0; e < E; ++e) local = u192_add(local, u192_from_f32_bits(v[e]));
   U192 incl = local;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -182,7 +204,7 @@ __global__ void __launch_bounds__(kCapThreads) capacity_kernel(dspark_capacity_a
     wtot[3 * wave + 1] = incl.w1;
     wtot[3 * wave + 2] = incl.w2;
   }
-  __syncthreads();
+  __syncthreads();  // also orders the rate stores before the reads below
   U192 excl = {0ull, 0ull, 0ull};
   for (int w = 0; w < wave; ++w) {
     const U192 t = {wtot[3 * w], wtot[3 * w + 1], wtot[3 * w + 2]};
@@ -191,19 +213,19 @@ __global__ void __launch_bounds__(kCapThreads) capacity_kernel(dspark_capacity_a
   const U192 o = u192_shfl_up(incl, 1);
   if (lane > 0) excl = u192_add(excl, o);
 
-  // stop tests for the owned positions i = base + q < kmax
+  // stop tests for the owned positions i = base + e < kmax
   const double Rd = static_cast<double>(R);
   U192 S = excl;
   double E_now = __dadd_rn(Rd, u192_to_double(S));
   int kfirst = kmax;
 #pragma unroll
-  for (int q = 0; q < kCapMaxPer; ++q) {
-    const int i = base + q;
-    if (q < c && i < kmax) {
-      S = u192_add(S, u192_from_f32_bits(keys[i]));
+  for (int e = 0; e < E; ++e) {
+    const int i = base + e;
+    if (i < kmax) {
+      S = u192_add(S, u192_from_f32_bits(v[e]));
       const double E_next = __dadd_rn(Rd, u192_to_double(S));
-      const double th_now = __dmul_rn(E_now, static_cast<double>(sps_v[q]));
-      const double th_next = __dmul_rn(E_next, static_cast<double>(sps_v[q + 1]));
+      const double th_now = __dmul_rn(E_now, static_cast<double>(sps_s[i]));
+      const double th_next = __dmul_rn(E_next, static_cast<double>(sps_s[i + 1]));
       if (!(th_next > th_now) && i < kfirst) kfirst = i;
       E_now = E_next;
     }
@@ -217,30 +239,31 @@ __global__ void __launch_bounds__(kCapThreads) capacity_kernel(dspark_capacity_a
 
   // the thread owning position K (the last thread for K = N) writes E(K)
   // and Theta(K)
-  const int owner = min(K / c, kCapThreads - 1);
+  const int owner = min(K / E, kCapThreads - 1);
   if (tid == owner) {
     U192 SK = excl;
 #pragma unroll
-    for (int q = 0; q < kCapMaxPer; ++q)
-      if (q < c && base + q < K) SK = u192_add(SK, u192_from_f32_bits(keys[base + q]));
-    const double E = __dadd_rn(Rd, u192_to_double(SK));
+    for (int e = 0; e < E; ++e)
+      if (base + e < K) SK = u192_add(SK, u192_from_f32_bits(v[e]));
+    const double Ek = __dadd_rn(Rd, u192_to_double(SK));
     a.K[0] = K;
-    if (a.expected) a.expected[0] = E;
-    if (a.theta) a.theta[0] = __dmul_rn(E, static_cast<double>(a.sps[R + K]));
+    if (a.expected) a.expected[0] = Ek;
+    if (a.theta) a.theta[0] = __dmul_rn(Ek, static_cast<double>(sps_s[K]));
   }
 }
 
 }  // namespace
 
-int capacity_sort_size(int n) {
-  int N = 2048;
-  while (N < n) N <<= 1;
-  return N;
-}
-
 hipError_t launch_capacity(const dspark_capacity_args& a, hipStream_t s) {
-  const int N = capacity_sort_size(a.R * a.gamma);
-  hipLaunchKernelGGL(capacity_kernel, dim3(1), dim3(kCapThreads), 0, s, a, N);
+  const int n = a.R * a.gamma;
+  if (n <= 2 * kCapThreads)
+    hipLaunchKernelGGL(capacity_kernel<2>, dim3(1), dim3(kCapThreads), 0, s, a);
+  else if (n <= 4 * kCapThreads)
+    hipLaunchKernelGGL(capacity_kernel<4>, dim3(1), dim3(kCapThreads), 0, s, a);
+  else if (n <= 8 * kCapThreads)
+    hipLaunchKernelGGL(capacity_kernel<8>, dim3(1), dim3(kCapThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(capacity_kernel<16>, dim3(1), dim3(kCapThreads), 0, s, a);
   return hipGetLastError();
 }
 
