@@ -97,15 +97,11 @@ int dspark_draft_block(const dspark_draft_args* a) {
   fp.q_tok = a->q_tok;
   fp.q_stats = a->q_stats;
 
-  // 16-row path: each finish leaves W1[y] for the next position in hbuf
-  uint16_t* hbuf = (plan.seg_rows == kSegSmall) ? ws_at<uint16_t>(a->workspace, plan.hbuf_off) : nullptr;
   const int cu = current_cu_count();
   for (int k = 0; k < a->gamma; ++k) {
     // prev = anchor for the first position, the token drafted just before otherwise
     tp.prev_base = (k == 0) ? a->anchor : a->y + (k - 1);
     tp.prev_stride = (k == 0) ? 1 : a->gamma;
-    tp.hbuf = (k == 0) ? nullptr : hbuf;
-    fp.hbuf_out = (k + 1 < a->gamma) ? hbuf : nullptr;
     tp.U_base = a->U + static_cast<int64_t>(k) * a->V;
     hipEvent_t e0 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k]) : nullptr;
     hipEvent_t e1 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k + 1]) : nullptr;

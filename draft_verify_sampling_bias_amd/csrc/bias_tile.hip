@@ -346,33 +346,27 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
     for (int n = tid; n < R; n += WPB * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
     if (!__syncthreads_or(any)) return;
   }
-  // H = W1[prev] for all requests.  Every 16-byte load of this thread is
-  // issued before any is stored.  From the second draft position on, the
-  // previous position's finish has left the rows in hbuf (contiguous, no
-  // dependence on prev), so they are loaded together with the request info.
+  // H = W1[prev] for all requests, gathered once per workgroup.  Every
+  // 16-byte load of this thread is issued before any is stored.
   constexpr int G = KS * 4;  // 16-byte groups per H row
   constexpr int kPer = kSmallMaxR * G / (WPB * 64);
-  const bool from_buf = !RESID && p.hbuf != nullptr;  // uniform
-  u32x4_t val[kPer];
-  if (from_buf) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int q = tid + j * WPB * 64;
-      const int nn = q / G, g = q - nn * G;
-      val[j] = *reinterpret_cast<const u32x4_t*>(p.hbuf + static_cast<int64_t>(nn) * rank + min(g * 8, rank - 8));
-    }
-  }
+  // wavefront-uniform walk state (scalar registers, scalar branches)
+  const int n_waves = gridDim.x * WPB;
+  int sg = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(wave);
+  Seg16Regs<KS, RESID> fa, fb;
+  // draft mode: the first segment's W2 and U addresses depend on neither H
+  // nor the request info, so its loads go out first and are in flight
+  // while the request info and the H rows (prev -> W1[prev]) arrive
+  if (!RESID) seg16_load<KS, RESID, VEC4, PACKED>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
   if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, tid, RESID);
   lds_barrier();
-  if (!from_buf) {
-    const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
+  u32x4_t val[kPer];
+  const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int q = tid + j * WPB * 64;
-      const int nn = q / G, g = q - nn * G;
-      val[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank +
-                                                  min(g * 8, rank - 8));
-    }
+  for (int j = 0; j < kPer; ++j) {
+    const int q = tid + j * WPB * 64;
+    const int nn = q / G, g = q - nn * G;
+    val[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank + min(g * 8, rank - 8));
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -381,18 +375,13 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
     const u32x4_t v = (g * 8 >= rank || !s_ci[nn].act) ? u32x4_t{0u, 0u, 0u, 0u} : val[j];
     *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
   }
-  // wavefront-uniform walk state (scalar registers, scalar branches)
-  const int n_waves = gridDim.x * WPB;
-  int sg = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(wave);
-  // the barrier comes before the first segment's loads: their issue can
-  // stall on a memory pipeline that the whole grid floods at once, and no
-  // wavefront should wait for another's issue
+  // residual mode: the barrier comes before the first segment's loads
+  // (their U and target rows come from the request info)
   lds_barrier();
   if (sg >= n_seg) return;
   LaneReq<RESID> lq;
   lane_req<RESID>(s_ci, lane, lq);
-  Seg16Regs<KS, RESID> fa, fb;
-  seg16_load<KS, RESID, VEC4, PACKED>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  if (RESID) seg16_load<KS, RESID, VEC4, PACKED>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
   // Ping-pong prefetch, the next segment's loads interleaved with the
   // current one's k-steps.  The prefetch issued on a wavefront's last
   // segment re-reads segment n_seg - 1 (a cache hit, never used) so that the

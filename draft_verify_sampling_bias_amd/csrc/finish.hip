@@ -12,7 +12,6 @@
 // the segment sums written by the residual pass of the fused bias kernel; if
 // that residual has no mass it draws from p.
 
-#include <type_traits>
 
 #include "dspark_device.h"
 #include "launchers.h"
@@ -99,20 +98,6 @@ __device__ __forceinline__ void block_amax_once(float& m, int& i, float* lm, int
   for (int w = 1; w < 4; ++w) amax_merge(m, i, lm[w], li[w]);
 }
 
-// Wavefront 0: W1[y] (bf16) into row n of the next position's H buffer
-// (16-row path only; one 16-byte chunk per lane, rank <= 512).
-template <typename WT>
-__device__ __forceinline__ void copy_next_h(const FinishParams& p, int n, int y) {
-  if constexpr (std::is_same<WT, uint16_t>::value) {
-    const int lane = threadIdx.x & 63;
-    if (p.hbuf_out != nullptr && lane * 8 < p.rank) {
-      const uint16_t* src = static_cast<const uint16_t*>(p.W1) + static_cast<int64_t>(y) * p.rank + lane * 8;
-      *reinterpret_cast<u32x4_t*>(p.hbuf_out + static_cast<int64_t>(n) * p.rank + lane * 8) =
-          *reinterpret_cast<const u32x4_t*>(src);
-    }
-  }
-}
-
 template <typename WT, int STAGE>
 __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   constexpr bool STAGED = STAGE > 0;
@@ -160,7 +145,6 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
       p.q_stats[2 * o] = M;
       p.q_stats[2 * o + 1] = 1.0f;
     }
-    if (tid < 64) copy_next_h<WT>(p, n, clampi(im, 0, V - 1));
     return;
   }
   const float u = clamp_uniform(u_raw);
@@ -198,7 +182,6 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
       p.q_stats[2 * o] = M;
       p.q_stats[2 * o + 1] = L.Z;
     }
-    copy_next_h<WT>(p, n, (pos >= 0) ? v0 + pos : min(v0, V - 1));
   }
 }
 

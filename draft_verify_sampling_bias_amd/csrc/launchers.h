@@ -47,10 +47,6 @@ struct TileParams {
   const float* target;   // [t_rows = n_rows, V]    (residual mode)
   int64_t u_rows, t_rows;
   float* part;           // [record_rows][n_seg][kRecFloats] segment records
-  // draft mode, 16-row path: when set, H is read from these rows
-  // ([kSmallMaxR][rank] bf16, written by the previous position's finish)
-  // instead of being gathered from W1 by prev
-  const uint16_t* hbuf;
   // 16-row path: when set, the W2 fragments are read from this
   // fragment-packed copy (dspark_pack_w2) instead of W2
   const uint16_t* w2p;
@@ -71,7 +67,6 @@ struct FinishParams {
   int32_t* y;
   float* q_tok;
   float* q_stats;
-  uint16_t* hbuf_out;    // when set: row n receives W1[y_n] (bf16), H of the next position
 };
 
 struct VerifyParams {

@@ -35,11 +35,7 @@ int plan_draft(const dspark_draft_args* a, DraftPlan* plan) {
   plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
   const std::size_t rows = static_cast<std::size_t>(record_rows(plan->seg_rows, a->R));
   plan->part_off = 0;
-  std::size_t off = round_up(rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
-  plan->hbuf_off = off;
-  if (plan->seg_rows == kSegSmall)
-    off = round_up(off + static_cast<std::size_t>(kSmallMaxR) * a->rank * sizeof(uint16_t), kWsAlign);
-  plan->total = off;
+  plan->total = round_up(rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
   return DSPARK_OK;
 }
 

@@ -70,7 +70,6 @@ struct DraftPlan {
   int seg_rows = 0;
   int n_seg = 0;
   std::size_t part_off = 0;  // [record_rows][n_seg][kRecFloats] float
-  std::size_t hbuf_off = 0;  // 16-row path: [kSmallMaxR][rank] bf16, W1 rows of the next prev tokens
   std::size_t total = 0;
 };
 

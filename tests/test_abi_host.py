@@ -57,9 +57,8 @@ def test_workspace_sizes_match_struct_layout():
 
     # one (max, sum) record of two floats per (request row, 16-row segment);
     # the 16-row path (bf16 weights, R <= 64) always holds 64 request rows
-    # plus, on that path, 64 rows of W1 (bf16) handed from one draft position to the next
-    assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1) == up(64 * 9496 * 8) + up(64 * 512 * 2)
-    assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1) == up(64 * 63 * 8) + up(64 * 64 * 2)
+    assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1) == up(64 * 9496 * 8)
+    assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1) == up(64 * 63 * 8)
     # 64-row segments above 64 requests (bf16): R + 17 record rows (padding
     # requests of the last chunk, one dummy row)
     assert ds.draft_workspace_bytes(65, 7, 151936, 512, 1) == up((65 + 17) * 2374 * 8)
