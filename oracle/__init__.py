@@ -43,7 +43,15 @@ Readings of points the pages leave open (each also listed in the design notes):
     the sum of the K largest survival values (the scheduler's expected token
     count) and R + K verify rows; the causal greedy adds candidates while
     Theta strictly improves and stops at the first K with Theta(K+1) <=
-    Theta(K); the throughput table and the (lagged) survival are inputs.
+    Theta(K); the throughput table and the (lagged) survival are inputs;
+  * sequential temperature scaling: position k's temperature is the maximum-
+    likelihood one of the Bernoulli model P(accept k | reached k) =
+    sigmoid(z / tau_k) on the calibration blocks that reached k (every
+    earlier draft accepted), positions fitted left to right; 1 / tau_k is
+    searched in [2^-8, 2^8] and an end of that interval is taken when the
+    likelihood keeps rising past it; no information (no block reached k, or
+    all its logits are 0) gives tau_k = 1; logits are clamped to [-64, 64]
+    with NaN -> 0.
 """
 from __future__ import annotations
 
@@ -56,7 +64,8 @@ import numpy as np
 __all__ = [
     "NEAR", "widen", "markov_bias", "inverse_cdf", "draft_block", "survival",
     "schedule", "schedule_cutoff", "capacity", "verify", "step", "DraftResult", "ScheduleResult",
-    "VerifyResult", "CapacityResult",
+    "VerifyResult", "CapacityResult", "sts_fit", "sts_apply", "CalibrationResult",
+    "STS_BETA_MIN", "STS_BETA_MAX",
 ]
 
 #: width of the band around a decision boundary inside which a flip caused by
@@ -337,6 +346,85 @@ def capacity(a_lag, sps) -> CapacityResult:
         K += 1
     return CapacityResult(K=K, theta=E(K) * float(sps[R + K]) if R + K < len(sps) else float("nan"),
                           expected=E(K), near_tie=near)
+
+
+#: search interval of the inverse temperature 1 / tau of the calibration fit
+STS_BETA_MIN, STS_BETA_MAX = 2.0 ** -8, 2.0 ** 8
+#: confidence logits are clamped to this magnitude (the sigmoid is saturated
+#: far inside it)
+STS_ZMAX = 64.0
+
+
+@dataclass
+class CalibrationResult:
+    tau: np.ndarray        # float64 [gamma]
+    reached: np.ndarray    # int64 [gamma]: calibration blocks that reached each position
+    at_bound: np.ndarray   # bool [gamma]: interval end taken, or no information (tau = 1)
+
+
+def _sts_logits(z) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float32).astype(np.float64)
+    return np.clip(np.where(np.isnan(z), 0.0, z), -STS_ZMAX, STS_ZMAX)
+
+
+def sts_fit(z, n_acc) -> CalibrationResult:
+    """Sequential temperature scaling of the confidence head (explainer
+    section 8: a confidence that ranks well but is over-confident in absolute
+    value gives wrong capacity decisions, so the cumulative probabilities are
+    corrected by a posterior temperature calibration, position by position
+    from left to right).
+
+    Calibration data: N drafted blocks with confidence logits z [N, gamma]
+    and accepted draft counts n_acc [N] (0 .. gamma).  Block i reached
+    position k iff n_acc[i] >= k (every earlier draft accepted), and was
+    accepted there iff n_acc[i] > k.  For k = 0 .. gamma-1, with S_k the
+    blocks that reached k, tau_k = 1 / beta_k where beta_k maximises the
+    likelihood of those outcomes under P(accept) = sigmoid(beta z): the root
+    of the score g(beta) = sum_{i in S_k} z_ik (sigmoid(beta z_ik) - y_ik),
+    which is non-decreasing in beta.  Then survival = running product of
+    sigmoid(z_k / tau_k) estimates P(n_acc > k), the product of the
+    calibrated conditional rates."""
+    zz = _sts_logits(z)
+    N, gamma = zz.shape
+    n = np.clip(np.asarray(n_acc).astype(np.int64), 0, gamma)
+    tau = np.ones(gamma)
+    reached = np.zeros(gamma, np.int64)
+    at_bound = np.zeros(gamma, bool)
+    for k in range(gamma):                       # left to right
+        S = n >= k
+        zs = zz[S, k]
+        ys = (n[S] > k).astype(np.float64)
+        reached[k] = int(S.sum())
+        if zs.size == 0 or not np.any(zs != 0.0):
+            at_bound[k] = True                   # no information: identity calibration
+            continue
+
+        def score(beta):
+            return math.fsum((zs * (_expit(beta * zs) - ys)).tolist())
+
+        if score(STS_BETA_MIN) >= 0.0:
+            beta, at_bound[k] = STS_BETA_MIN, True
+        elif score(STS_BETA_MAX) <= 0.0:
+            beta, at_bound[k] = STS_BETA_MAX, True
+        else:
+            from scipy.optimize import brentq
+            beta = brentq(score, STS_BETA_MIN, STS_BETA_MAX, xtol=1e-300, rtol=4 * np.finfo(float).eps,
+                          maxiter=1000)
+        tau[k] = 1.0 / beta
+    return CalibrationResult(tau=tau, reached=reached, at_bound=at_bound)
+
+
+def _expit(x):
+    from scipy.special import expit
+    return expit(x)
+
+
+def sts_apply(z, tau) -> np.ndarray:
+    """Calibrated confidence c[r, k] = sigmoid(z[r, k] / tau[k]) (logits
+    clamped as for the fit), evaluated in fp64 and rounded once to fp32."""
+    zz = _sts_logits(z)
+    t = np.asarray(tau, dtype=np.float32).astype(np.float64)
+    return _expit(zz / t[None, :]).astype(np.float32)
 
 
 @dataclass

@@ -38,7 +38,7 @@ import numpy as np
 __all__ = [
     "StepInputs", "CONFIGS", "make_config", "make_custom", "bf16_round_bits",
     "bf16_bits_to_f32", "weights_as_f32", "gather_rows", "fixed_offsets",
-    "sps_table", "random_sps_table",
+    "sps_table", "random_sps_table", "make_calibration",
 ]
 
 # stream order inside SeedSequence(seed).spawn(N_STREAMS)
@@ -264,3 +264,27 @@ def random_sps_table(seed: int, n: int) -> np.ndarray:
             level *= float(rng.uniform(0.90, 0.995))
         sps[b] = level
     return sps
+
+
+# ---------------------------------------------------------------------------
+# calibration blocks for sequential temperature scaling
+# ---------------------------------------------------------------------------
+def make_calibration(seed: int, N: int, gamma: int, tau_true=None, *, loc: float = 1.5, scale: float = 2.0):
+    """N synthetic drafted blocks for fitting the confidence calibration.
+
+    Returns (z, n_acc, tau_true): confidence logits z [N, gamma] fp32 ~
+    N(loc, scale); accepted counts n_acc [N] int32.  The pages give no
+    calibration set; this one has a known ground truth: draft k of a block is
+    accepted with probability sigmoid(z / tau_true[k]) (drawn with seeded
+    uniforms), and n_acc is the number of leading accepted drafts.  A
+    tau_true above 1 makes the raw logits over-confident.  The default
+    tau_true rises along the block."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    if tau_true is None:
+        tau_true = np.linspace(1.2, 2.5, gamma)
+    tau_true = np.asarray(tau_true, dtype=np.float64)
+    z = rng.normal(loc, scale, (N, gamma)).astype(np.float32)
+    u = rng.random((N, gamma))
+    accept = u < 1.0 / (1.0 + np.exp(-z.astype(np.float64) / tau_true[None, :]))
+    n_acc = np.where(accept.all(axis=1), gamma, np.argmin(accept, axis=1)).astype(np.int32)
+    return z, n_acc, tau_true

@@ -17,6 +17,7 @@ import pytest
 from scipy.special import softmax, logsumexp
 
 import oracle
+import synth
 from measure import pieces, probs
 
 V8 = 8
@@ -681,3 +682,123 @@ def test_bf16_widening_exact():
     w = oracle.widen(bits, "bf16")
     np.testing.assert_array_equal(w, synth.bf16_bits_to_f32(bits).astype(np.float64))
     assert w[3] == -2.5
+
+
+# ---------------------------------------------------------------------------
+# sequential temperature scaling (explainer section 8: posterior temperature
+# calibration of the confidence, position by position from left to right)
+# ---------------------------------------------------------------------------
+def _nll(beta, z, y):
+    """Bernoulli negative log-likelihood of outcomes y under sigmoid(beta z),
+    written with log_expit (a formulation independent of the oracle's score
+    equation)."""
+    from scipy.special import log_expit
+    return -float(np.sum(y * log_expit(beta * z) + (1 - y) * log_expit(-beta * z)))
+
+
+def test_sts_constant_logit_closed_form():
+    """With one logit value z0 at position k among the blocks that reached it,
+    the likelihood is maximised where sigmoid(beta z0) equals the acceptance
+    frequency: tau = z0 / logit(mean y)."""
+    from scipy.special import logit
+    rng = np.random.default_rng(41)
+    gamma = 4
+    z = rng.normal(1.0, 2.0, (500, gamma)).astype(np.float32)
+    z0s = [1.5, -0.75, 3.0, 0.625]
+    for k in range(gamma):
+        z[:, k] = np.float32(z0s[k])
+    n_acc = rng.integers(0, gamma + 1, 500).astype(np.int32)
+    r = oracle.sts_fit(z, n_acc)
+    for k in range(gamma):
+        reached = n_acc >= k
+        ybar = float(np.mean(n_acc[reached] > k))
+        beta = logit(ybar) / z0s[k]
+        if oracle.STS_BETA_MIN < beta < oracle.STS_BETA_MAX:
+            assert r.tau[k] == pytest.approx(1.0 / beta, rel=1e-12), k
+            assert not r.at_bound[k]
+
+
+def test_sts_fit_minimises_the_likelihood():
+    rng = np.random.default_rng(42)
+    z, n_acc, _ = synth.make_calibration(42, 3000, 6)
+    r = oracle.sts_fit(z, n_acc)
+    for k in range(6):
+        S = n_acc >= k
+        zs, ys = z[S, k].astype(np.float64), (n_acc[S] > k).astype(np.float64)
+        b = 1.0 / r.tau[k]
+        f0 = _nll(b, zs, ys)
+        for d in (1e-3, -1e-3, 1e-2, -1e-2):
+            assert f0 < _nll(b * (1 + d), zs, ys), (k, d)
+
+
+def test_sts_recovers_the_generating_temperatures():
+    """Outcomes drawn from sigmoid(z / tau_true): the fit is consistent."""
+    tau_true = [0.8, 1.3, 2.0, 2.6, 1.0]
+    z, n_acc, _ = synth.make_calibration(43, 60000, 5, tau_true)
+    r = oracle.sts_fit(z, n_acc)
+    for k, t in enumerate(tau_true):
+        se = 4.0 * t / np.sqrt(r.reached[k])       # generous: a few standard errors
+        assert abs(r.tau[k] - t) < max(0.08 * t, se * 3), (k, r.tau[k], t)
+    # calibrated survival matches the empirical survival, position by position
+    c = oracle.sts_apply(z, r.tau.astype(np.float32))
+    a = np.cumprod(c.astype(np.float64), axis=1)
+    for k in range(5):
+        assert a[:, k].mean() == pytest.approx(float(np.mean(n_acc > k)), abs=0.01), k
+
+
+def test_sts_conditions_on_reaching_the_position():
+    """Position k is fitted on the blocks that reached it only: logits at k of
+    blocks that stopped earlier do not move tau_k, those of blocks that
+    reached it do."""
+    z, n_acc, _ = synth.make_calibration(44, 2000, 5)
+    r = oracle.sts_fit(z, n_acc)
+    for k in range(1, 5):
+        z2 = z.copy()
+        early = n_acc < k
+        z2[early, k] = -z2[early, k] * 3 + 7      # arbitrary change on unreached blocks
+        assert oracle.sts_fit(z2, n_acc).tau[k] == r.tau[k]
+        z3 = z.copy()
+        z3[~early, k] *= np.float32(1.5)
+        assert oracle.sts_fit(z3, n_acc).tau[k] != pytest.approx(r.tau[k], rel=1e-6)
+
+
+def test_sts_scale_equivariance():
+    z, n_acc, _ = synth.make_calibration(45, 2000, 4)
+    r = oracle.sts_fit(z, n_acc)
+    for lam in (2.0, 0.5):
+        r2 = oracle.sts_fit((z * np.float32(lam)).astype(np.float32), n_acc)
+        np.testing.assert_allclose(r2.tau, lam * r.tau, rtol=1e-12)
+
+
+def test_sts_degenerate_cases():
+    z = np.array([[2.0, 1.0], [-1.0, 0.5], [3.0, -2.0]], np.float32)
+    # separable at position 0 (accepted exactly where z > 0): the likelihood
+    # keeps rising with beta, so the largest inverse temperature is taken
+    r = oracle.sts_fit(z, np.array([2, 0, 1], np.int32))
+    assert r.tau[0] == 1.0 / oracle.STS_BETA_MAX and r.at_bound[0]
+    # anti-separable (accepted exactly where z < 0): the smallest
+    r = oracle.sts_fit(z, np.array([0, 1, 0], np.int32))
+    assert r.tau[0] == 1.0 / oracle.STS_BETA_MIN and r.at_bound[0]
+    # no block reached position 1: tau = 1
+    r = oracle.sts_fit(z, np.array([0, 0, 0], np.int32))
+    assert r.tau[1] == 1.0 and r.reached[1] == 0 and r.at_bound[1]
+    # all logits zero: no information
+    r = oracle.sts_fit(np.zeros((5, 2), np.float32), np.array([2, 1, 0, 2, 1], np.int32))
+    assert (r.tau == 1.0).all()
+    # NaN logits count as 0, huge ones are clamped
+    zn = np.array([[np.nan, 1.0], [1e30, 1.0], [-1.0, 1.0]], np.float32)
+    r1 = oracle.sts_fit(zn, np.array([1, 2, 0], np.int32))
+    r2 = oracle.sts_fit(np.array([[0.0, 1.0], [64.0, 1.0], [-1.0, 1.0]], np.float32), np.array([1, 2, 0], np.int32))
+    np.testing.assert_array_equal(r1.tau, r2.tau)
+
+
+def test_sts_apply_is_the_sigmoid_of_the_scaled_logit():
+    from scipy.special import expit
+    rng = np.random.default_rng(46)
+    z = rng.normal(0, 4, (50, 3)).astype(np.float32)
+    tau = np.array([0.5, 1.0, 3.0], np.float32)
+    c = oracle.sts_apply(z, tau)
+    assert c.dtype == np.float32
+    np.testing.assert_allclose(c, expit(z.astype(np.float64) / tau.astype(np.float64)), rtol=1e-7)
+    # tau = 1 leaves the head's own probability
+    np.testing.assert_allclose(oracle.sts_apply(z, np.ones(3, np.float32)), expit(z.astype(np.float64)), rtol=1e-7)
