@@ -20,7 +20,7 @@ __all__ = [
     "dspark_verify", "dspark_schedule_rows", "dspark_draft_workspace_size",
     "dspark_verify_workspace_size", "dspark_status_string", "dspark_abi_version",
     "DraftArgs", "ScheduleArgs", "CutoffArgs", "VerifyArgs", "EXPORTED_SYMBOLS",
-    "dspark_capacity", "CapacityArgs",
+    "dspark_capacity", "CapacityArgs", "dspark_sts_fit", "dspark_sts_apply", "StsFitArgs", "StsApplyArgs",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
     "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_schedule_rows",
     "dspark_status_string", "dspark_abi_version", "dspark_pack_w2", "dspark_w2_packed_bytes",
-    "dspark_capacity",
+    "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply",
 )
 
 
@@ -85,6 +85,16 @@ class CapacityArgs(ctypes.Structure):
                 ("theta", _p), ("stream", _p)]
 
 
+class StsFitArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("N", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("z", _p), ("n_acc", _p), ("tau", _p), ("stream", _p)]
+
+
+class StsApplyArgs(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
+                ("z", _p), ("tau", _p), ("c", _p), ("stream", _p)]
+
+
 class PackArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("V", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("W2", _p), ("W2_packed", _p), ("W2_packed_bytes", ctypes.c_size_t), ("stream", _p)]
@@ -106,9 +116,11 @@ def _load():
     L.dspark_w2_packed_bytes.restype = ctypes.c_size_t
     L.dspark_verify.argtypes = [P(VerifyArgs)]
     L.dspark_capacity.argtypes = [P(CapacityArgs)]
+    L.dspark_sts_fit.argtypes = [P(StsFitArgs)]
+    L.dspark_sts_apply.argtypes = [P(StsApplyArgs)]
     for f in ("dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
               "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_abi_version",
-              "dspark_pack_w2", "dspark_capacity"):
+              "dspark_pack_w2", "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply"):
         getattr(L, f).restype = ctypes.c_int
     L.dspark_schedule_rows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     L.dspark_schedule_rows.restype = ctypes.c_int64
@@ -392,6 +404,40 @@ def dspark_capacity(a_lag, sps, *, out=None, stream=None):
                      stream=_stream(dev, stream))
     _check("dspark_capacity", get_lib().dspark_capacity(ctypes.byref(a)))
     return out
+
+
+def dspark_sts_fit(z, n_acc, *, out=None, stream=None):
+    """Sequential temperature scaling fit (include/dspark.h, dspark_sts_fit).
+    z [N, gamma] fp32 confidence logits of calibration blocks; n_acc [N]
+    int32 accepted counts.  Returns tau [gamma] fp32 (device)."""
+    torch = _torch()
+    dev = z.device
+    N, gamma = z.shape
+    _want(z, "z", torch.float32, (N, gamma), dev)
+    _want(n_acc, "n_acc", torch.int32, (N,), dev)
+    tau = torch.empty(gamma, dtype=torch.float32, device=dev) if out is None else out
+    _want(tau, "tau", torch.float32, (gamma,), dev)
+    a = StsFitArgs(struct_size=ctypes.sizeof(StsFitArgs), N=N, gamma=gamma, z=_ptr(z) if N else None,
+                   n_acc=_ptr(n_acc) if N else None, tau=_ptr(tau), stream=_stream(dev, stream))
+    _check("dspark_sts_fit", get_lib().dspark_sts_fit(ctypes.byref(a)))
+    return tau
+
+
+def dspark_sts_apply(z, tau, *, out=None, stream=None):
+    """Calibrated confidence c = sigmoid(z / tau) (include/dspark.h,
+    dspark_sts_apply).  z [R, gamma] fp32, tau [gamma] fp32; returns c
+    [R, gamma] fp32 (device)."""
+    torch = _torch()
+    dev = z.device
+    R, gamma = z.shape
+    _want(z, "z", torch.float32, (R, gamma), dev)
+    _want(tau, "tau", torch.float32, (gamma,), dev)
+    c = torch.empty((R, gamma), dtype=torch.float32, device=dev) if out is None else out
+    _want(c, "c", torch.float32, (R, gamma), dev)
+    a = StsApplyArgs(struct_size=ctypes.sizeof(StsApplyArgs), R=R, gamma=gamma, z=_ptr(z), tau=_ptr(tau),
+                     c=_ptr(c), stream=_stream(dev, stream))
+    _check("dspark_sts_apply", get_lib().dspark_sts_apply(ctypes.byref(a)))
+    return c
 
 
 def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final, *,

@@ -29,7 +29,8 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
-SOURCES = ["plan.cpp", "api.hip", "bias_tile.hip", "finish.hip", "verify.hip", "schedule.hip", "pack.hip", "capacity.hip"]
+SOURCES = ["plan.cpp", "api.hip", "bias_tile.hip", "finish.hip", "verify.hip", "schedule.hip", "pack.hip", "capacity.hip",
+           "calibrate.hip"]
 
 
 def _compile(src: str, extra) -> str:

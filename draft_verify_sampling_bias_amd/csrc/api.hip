@@ -162,6 +162,18 @@ int dspark_capacity(const dspark_capacity_args* a) {
   return hip_status(launch_capacity(*a, static_cast<hipStream_t>(a->stream)));
 }
 
+int dspark_sts_fit(const dspark_sts_fit_args* a) {
+  const int st = validate_sts_fit(a);
+  if (st != DSPARK_OK) return st;
+  return hip_status(launch_sts_fit(*a, static_cast<hipStream_t>(a->stream)));
+}
+
+int dspark_sts_apply(const dspark_sts_apply_args* a) {
+  const int st = validate_sts_apply(a);
+  if (st != DSPARK_OK || a->R == 0) return st;
+  return hip_status(launch_sts_apply(*a, static_cast<hipStream_t>(a->stream)));
+}
+
 int dspark_verify(const dspark_verify_args* a) {
   VerifyPlan plan;
   int st = validate_verify(a, &plan);

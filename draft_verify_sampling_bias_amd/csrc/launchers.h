@@ -111,5 +111,9 @@ hipError_t launch_pack_w2(const dspark_pack_w2_args& a, hipStream_t s);
 hipError_t launch_schedule_cutoff(const dspark_schedule_args& a, float conf_min, hipStream_t s);
 // the hardware-aware capacity (one workgroup)
 hipError_t launch_capacity(const dspark_capacity_args& a, hipStream_t s);
+// sequential temperature scaling: the fit (one workgroup per position) and
+// the calibrated confidence
+hipError_t launch_sts_fit(const dspark_sts_fit_args& a, hipStream_t s);
+hipError_t launch_sts_apply(const dspark_sts_apply_args& a, hipStream_t s);
 
 }  // namespace dspark

@@ -173,6 +173,28 @@ int validate_capacity(const dspark_capacity_args* a) {
   return DSPARK_OK;
 }
 
+int validate_sts_fit(const dspark_sts_fit_args* a) {
+  if (a == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_sts_fit_args)) return DSPARK_ERR_ABI;
+  if (a->N < 0 || a->gamma < 1) return DSPARK_ERR_SHAPE;
+  if (a->gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
+  if (!a->tau || (a->N > 0 && (!a->z || !a->n_acc))) return DSPARK_ERR_NULL;
+  if (!aligned(a->tau, 4) || (a->z && !aligned(a->z, 4)) || (a->n_acc && !aligned(a->n_acc, 4)))
+    return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+int validate_sts_apply(const dspark_sts_apply_args* a) {
+  if (a == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_sts_apply_args)) return DSPARK_ERR_ABI;
+  if (a->R < 0 || a->gamma < 1) return DSPARK_ERR_SHAPE;
+  if (a->gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
+  if (a->R == 0) return DSPARK_OK;
+  if (!a->z || !a->tau || !a->c) return DSPARK_ERR_NULL;
+  if (!aligned(a->z, 4) || !aligned(a->tau, 4) || !aligned(a->c, 4)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
 int64_t schedule_rows(int32_t R, int32_t gamma, int64_t K) {
   if (R < 0 || gamma < 1) return -1;
   const int64_t n = static_cast<int64_t>(R) * gamma;

@@ -102,6 +102,8 @@ int validate_schedule(const dspark_schedule_args* a);
 int validate_cutoff(const dspark_cutoff_args* a);
 int validate_pack_w2(const dspark_pack_w2_args* a);
 int validate_capacity(const dspark_capacity_args* a);
+int validate_sts_fit(const dspark_sts_fit_args* a);
+int validate_sts_apply(const dspark_sts_apply_args* a);
 
 int64_t schedule_rows(int32_t R, int32_t gamma, int64_t K);
 const char* status_string(int status);

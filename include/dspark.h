@@ -389,6 +389,61 @@ typedef struct dspark_capacity_args {
 int dspark_capacity(const dspark_capacity_args* args);
 
 /* --------------------------------------------------------------------------
+ * Sequential temperature scaling of the confidence head ("STS").
+ *
+ * [EXP] section 8: the scheduler multiplies survival by the hardware
+ * throughput curve, so a confidence head that ranks well but is
+ * over-confident in absolute value makes wrong capacity decisions; the
+ * cumulative probabilities are therefore corrected by a posterior
+ * temperature calibration, position by position from left to right.
+ *
+ * dspark_sts_fit: one temperature per block position from calibration data.
+ *   Calibration block i (of N) has confidence logits z[i, 0..gamma-1] and
+ *   n_acc[i] accepted drafts (clamped to [0, gamma]).  It reached position k
+ *   iff n_acc[i] >= k (every earlier draft accepted) and was accepted there
+ *   iff n_acc[i] > k.  For each k, over the blocks that reached k:
+ *     beta_k = the root of g(beta) = sum z_ik (sigmoid(beta z_ik) - y_ik)
+ *              (the maximum-likelihood inverse temperature of
+ *              P(accept k | reached k) = sigmoid(beta z); g is
+ *              non-decreasing in beta), in [2^-8, 2^8]: 2^-8 if
+ *              g(2^-8) >= 0, 2^8 if g(2^8) <= 0 (no sign change);
+ *     beta_k = 1 when no block reached k or all its logits are 0;
+ *     tau[k] = fp32(1 / beta_k).
+ *   Logits are clamped to [-64, 64], NaN -> 0.  Each position's fit uses
+ *   only the blocks that reached it, so the product of the calibrated
+ *   conditional rates estimates the survival P(n_acc > k).
+ *   Arguments: N >= 0 host int; gamma in [1, DSPARK_MAX_GAMMA];
+ *   z float [N, gamma]; n_acc int32 [N]; tau float [gamma] out.
+ *   One workgroup per position; calibration is an offline step.
+ *
+ * dspark_sts_apply: calibrated confidence for a batch,
+ *   c[r, k] = fp32(sigmoid(z[r, k] / tau[k])) evaluated in fp64 (logits
+ *   clamped as above), the c input of dspark_schedule.
+ *   Arguments: R >= 0 host int; gamma in [1, DSPARK_MAX_GAMMA];
+ *   z float [R, gamma]; tau float [gamma] (> 0); c float [R, gamma] out.
+ * -------------------------------------------------------------------------- */
+typedef struct dspark_sts_fit_args {
+  uint32_t struct_size;
+  int32_t N, gamma;
+  const float* z;
+  const int32_t* n_acc;
+  float* tau;
+  void* stream;
+} dspark_sts_fit_args;
+
+typedef struct dspark_sts_apply_args {
+  uint32_t struct_size;
+  int32_t R, gamma;
+  const float* z;
+  const float* tau;
+  float* c;
+  void* stream;
+} dspark_sts_apply_args;
+
+int dspark_sts_fit(const dspark_sts_fit_args* args);
+int dspark_sts_apply(const dspark_sts_apply_args* args);
+
+/* --------------------------------------------------------------------------
  * dspark_pack_w2: W2 rearranged once (at model load) into the layout the
  * 16-row fused bias kernel reads, so that each of its load instructions
  * reads 1 KiB contiguous instead of 64 bytes from each of 16 rows.

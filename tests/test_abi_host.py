@@ -204,6 +204,40 @@ def test_capacity_largest_batch_passes_the_size_checks():
     assert _call("dspark_capacity", a) == ds.Status.ERR_NULL
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=4), ds.Status.ERR_ABI),
+    (dict(N=-1), ds.Status.ERR_SHAPE),
+    (dict(gamma=0), ds.Status.ERR_SHAPE),
+    (dict(gamma=17), ds.Status.ERR_UNSUPPORTED),
+    (dict(z=None), ds.Status.ERR_NULL),
+    (dict(n_acc=None), ds.Status.ERR_NULL),
+    (dict(tau=None), ds.Status.ERR_NULL),
+    (dict(tau=FAKE + 1), ds.Status.ERR_ALIGN),
+])
+def test_sts_fit_rejects_invalid_arguments(kw, status):
+    base = dict(struct_size=ctypes.sizeof(ds.StsFitArgs), N=100, gamma=5, z=FAKE, n_acc=FAKE, tau=FAKE)
+    base.update(kw)
+    assert _call("dspark_sts_fit", ds.StsFitArgs(**base)) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=4), ds.Status.ERR_ABI),
+    (dict(R=-1), ds.Status.ERR_SHAPE),
+    (dict(gamma=0), ds.Status.ERR_SHAPE),
+    (dict(gamma=17), ds.Status.ERR_UNSUPPORTED),
+    (dict(z=None), ds.Status.ERR_NULL),
+    (dict(c=None), ds.Status.ERR_NULL),
+    (dict(c=FAKE + 2), ds.Status.ERR_ALIGN),
+])
+def test_sts_apply_rejects_invalid_arguments(kw, status):
+    base = dict(struct_size=ctypes.sizeof(ds.StsApplyArgs), R=8, gamma=5, z=FAKE, tau=FAKE, c=FAKE)
+    base.update(kw)
+    assert _call("dspark_sts_apply", ds.StsApplyArgs(**base)) == status
+    # nothing to do for an empty batch
+    assert _call("dspark_sts_apply", ds.StsApplyArgs(struct_size=ctypes.sizeof(ds.StsApplyArgs), R=0,
+                                                     gamma=5)) == ds.Status.OK
+
+
 def test_packed_w2_bytes():
     # ceil(V/16) segments x k-steps (2/4/8/16 for rank <= 64/128/256/512) x 1 KiB
     assert ds.dspark_w2_packed_bytes(151936, 512) == 9496 * 16 * 1024
@@ -242,3 +276,5 @@ def test_null_args_pointer():
     assert lib.dspark_schedule(None) == ds.Status.ERR_NULL
     assert lib.dspark_schedule_cutoff(None) == ds.Status.ERR_NULL
     assert lib.dspark_capacity(None) == ds.Status.ERR_NULL
+    assert lib.dspark_sts_fit(None) == ds.Status.ERR_NULL
+    assert lib.dspark_sts_apply(None) == ds.Status.ERR_NULL

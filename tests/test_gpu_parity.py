@@ -324,3 +324,59 @@ def test_capacity_drives_the_schedule(cfg):
     np.testing.assert_array_equal(s1["row_offsets"], os_.row_offsets)
     assert abs(float(s1["expected_tokens"][0]) - o.expected) <= 1e-5 * o.expected
     print(f"[capacity config{cfg}] K={K} rows={int(s1['row_offsets'][-1])} E={o.expected:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("N,gamma,kind", [(1, 1, "model"), (37, 5, "model"), (2000, 7, "model"),
+                                          (8192, 5, "model"), (8193, 5, "model"), (40000, 16, "model"),
+                                          (3000, 4, "special"), (0, 3, "model")])
+def test_sts_fit(N, gamma, kind):
+    """Sequential temperature scaling fit against the oracle (tau within
+    1e-6 relative: both solve the same score equation to fp64 precision,
+    the GPU returns fp32), on both the register (N <= 8192) and streaming
+    paths, with the degenerate positions (unreached, all-zero logits,
+    separable) and clamped logits."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    z, n_acc, _ = synth.make_calibration(800 + N + gamma, N, gamma)
+    if kind == "special":
+        z[:, 0] = np.float32(0.0)                        # no information at position 0
+        z[:, 1] = np.where(n_acc > 1, 2.0, -2.0)         # separable at position 1
+        z[::5, 2] = np.nan                               # NaN -> 0
+        z[1::7, 3] = np.float32(1e30)                    # clamped
+        n_acc = np.minimum(n_acc, 3).astype(np.int32)    # position 3 reached, never passed
+    zd, nd = torch.from_numpy(z).cuda(), torch.from_numpy(n_acc).cuda()
+    tau = ds.dspark_sts_fit(zd, nd).cpu().numpy()
+    o = oracle.sts_fit(z, n_acc)
+    np.testing.assert_allclose(tau, o.tau.astype(np.float32), rtol=1e-6, err_msg=f"{o.tau}")
+    print(f"[sts fit N={N} gamma={gamma} {kind}] tau={np.round(tau, 4).tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("R,gamma", [(1, 1), (64, 7), (1000, 16), (5000, 3)])
+def test_sts_apply_and_schedule(R, gamma):
+    """Calibrated confidence against the oracle, then the schedule on it."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    rng = np.random.default_rng(850 + R)
+    z = rng.normal(1.5, 2.5, (R, gamma)).astype(np.float32)
+    z.flat[::13] = np.nan
+    z.flat[1::17] = np.float32(-300.0)
+    z.flat[2::19] = np.float32(300.0)
+    tau = rng.uniform(0.3, 3.0, gamma).astype(np.float32)
+    c = ds.dspark_sts_apply(torch.from_numpy(z).cuda(), torch.from_numpy(tau).cuda())
+    o = oracle.sts_apply(z, tau)
+    g = c.cpu().numpy()
+    tiny = np.finfo(np.float32).tiny
+    big = o >= tiny
+    np.testing.assert_allclose(g[big], o[big], rtol=1e-6)
+    assert (g[~big] < 2 * tiny).all()
+    exact = float(np.mean(g == o))
+    anc = torch.zeros(R, dtype=torch.int32, device="cuda")
+    y = torch.zeros((R, gamma), dtype=torch.int32, device="cuda")
+    K = (R * gamma) // 3
+    s = {k: v.cpu().numpy() for k, v in ds.dspark_schedule(c, K, anc, y).items()}
+    os_ = oracle.schedule(g, K, np.zeros(R, np.int32), np.zeros((R, gamma), np.int32))
+    np.testing.assert_array_equal(s["l"], os_.l)
+    np.testing.assert_array_equal(s["a"], os_.a)
+    print(f"[sts apply R={R} gamma={gamma}] bit-identical fraction {exact:.4f}", flush=True)
