@@ -111,26 +111,32 @@ class HipTimingEvents:
         self.handles = []
 
 
-def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None):
+def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=None):
     """The CPU oracle on a bounded sample of requests (single BLAS thread),
     with the same scheduler as the GPU step (with capacity_sps: the capacity
-    from the survival, then the top-K schedule with it)."""
+    from the survival, then the top-K schedule with it; with sts = (logits,
+    calibration logits, calibration counts): the temperatures fitted once
+    outside the timing, then the calibrated confidence in each step)."""
     import oracle
     from threadpoolctl import threadpool_limits
     rng = np.random.default_rng(seed)
     reqs = sorted(rng.choice(inp.R, size=min(n_sample, inp.R), replace=False).tolist())
+    conf = inp.c
     with threadpool_limits(limits=1):
+        tau = oracle.sts_fit(sts[1], sts[2]).tau if sts is not None else None
         t0 = time.perf_counter()
+        if sts is not None:
+            conf = oracle.sts_apply(sts[0], tau)
         d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
                                requests=reqs)
         y = np.where(d.y < 0, 0, d.y)
         if capacity_sps is not None:
-            cap = oracle.capacity(oracle.survival(inp.c), capacity_sps)
-            s = oracle.schedule(inp.c, cap.K, inp.anchor, y)
+            cap = oracle.capacity(oracle.survival(conf), capacity_sps)
+            s = oracle.schedule(conf, cap.K, inp.anchor, y)
         elif conf_min is None:
-            s = oracle.schedule(inp.c, inp.K, inp.anchor, y)
+            s = oracle.schedule(conf, inp.K, inp.anchor, y)
         else:
-            s = oracle.schedule_cutoff(inp.c, conf_min, inp.anchor, y)
+            s = oracle.schedule_cutoff(conf, conf_min, inp.anchor, y)
         t1 = time.perf_counter()
         # the row gather stands in for the target forward (not timed, as on the GPU)
         rows = inp.target[s.row_req.astype(np.int64), s.row_pos.astype(np.int64)]
@@ -161,6 +167,10 @@ def main():
                     help="hardware-aware capacity: each step runs dspark_capacity on the previous step's "
                          "survival with a synthetic bucketed step-rate table, and the schedule uses the "
                          "capacity that call produced (the lag: K is known on the host ahead of the step)")
+    ap.add_argument("--sts", action="store_true",
+                    help="sequential temperature scaling: each step calibrates the confidence logits with "
+                         "temperatures fitted once (dspark_sts_fit on synthetic calibration blocks, before "
+                         "timing) and schedules on the calibrated confidence (dspark_sts_apply)")
     ap.add_argument("--no-pack", action="store_true",
                     help="read W2 itself instead of its fragment-packed copy (dspark_pack_w2)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -223,6 +233,14 @@ def main():
     cutoff = args.conf_min is not None
     if cutoff and args.capacity:
         raise SystemExit("--conf-min and --capacity are alternative schedulers")
+    # sequential temperature scaling: confidence logits of this batch, and the
+    # temperatures fitted once on calibration blocks (an offline step)
+    z_step = tau = None
+    if args.sts:
+        z_step = up(synth.make_calibration(7000 + args.config, R, gamma)[0])
+        zc, nc, _ = synth.make_calibration(7100 + args.config, 20000, gamma)
+        tau = ds.dspark_sts_fit(up(zc), up(nc))
+        c = ds.dspark_sts_apply(z_step, tau)
     # hardware-aware capacity: the step rate table and the capacity outputs;
     # K_sched is the capacity the schedule uses
     K_sched = inp.K
@@ -253,6 +271,8 @@ def main():
 
     # target rows of the (deterministic) schedule: the stand-in for the target forward
     def schedule():
+        if args.sts:
+            ds.dspark_sts_apply(z_step, tau, out=c)
         if cutoff:
             ds.dspark_schedule_cutoff(c, args.conf_min, anchor, y, out=sch)
         else:
@@ -339,7 +359,9 @@ def main():
     cpu = None
     if not args.skip_cpu:
         cpu = cpu_baseline(inp, args.cpu_sample, conf_min=args.conf_min,
-                           capacity_sps=synth.sps_table(R * (gamma + 1) + 1) if args.capacity else None)
+                           capacity_sps=synth.sps_table(R * (gamma + 1) + 1) if args.capacity else None,
+                           sts=(synth.make_calibration(7000 + args.config, R, gamma)[0],
+                                *synth.make_calibration(7100 + args.config, 20000, gamma)[:2]) if args.sts else None)
 
     line = {
         "metric": METRIC,
@@ -356,6 +378,7 @@ def main():
         "data": "synthetic (seeded; logits, Markov factors, uniforms and confidences drawn by synth)",
         "config": {
             "workload": f"config{args.config}: R={R} gamma={gamma} V={V} r={rank} {inp.wdtype} W1/W2, fp32 logits, "
+                        + ("confidence calibrated by sequential temperature scaling, " if args.sts else "")
                         + (f"static confidence cutoff conf_min={args.conf_min} ({n_rows} rows)" if cutoff else
                            f"hardware-aware capacity K={K_sched} from the previous step's survival and a "
                            f"bucketed step-rate table ({n_rows} rows)" if args.capacity else
