@@ -380,3 +380,48 @@ def test_sts_apply_and_schedule(R, gamma):
     np.testing.assert_array_equal(s["l"], os_.l)
     np.testing.assert_array_equal(s["a"], os_.a)
     print(f"[sts apply R={R} gamma={gamma}] bit-identical fraction {exact:.4f}", flush=True)
+
+
+def test_lagged_pipeline_over_steps():
+    """The serving loop the pages describe, over five steps with fresh inputs
+    each step: the confidence calibrated with temperatures fitted once
+    (sequential temperature scaling), the capacity of step t taken from the
+    survival of step t - 2 (fixed-length verify before that), then draft,
+    schedule, verify.  Every stage is compared with the oracle on the same
+    inputs the GPU stage received."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    R, gamma, V, rank = 24, 5, 3000, 64
+    zc, nc, _ = synth.make_calibration(960, 6000, gamma)
+    tau = ds.dspark_sts_fit(torch.from_numpy(zc).cuda(), torch.from_numpy(nc).cuda())
+    tau_np = tau.cpu().numpy()
+    np.testing.assert_allclose(tau_np, oracle.sts_fit(zc, nc).tau.astype(np.float32), rtol=1e-6)
+    sps = synth.sps_table(R * (gamma + 1) + 1, t_row=1.0 / 2048)
+    sps_d = torch.from_numpy(sps).cuda()
+    survival = {}
+    for t in range(5):
+        inp = synth.make_custom(970 + t, R, gamma, V, rank, policy="temps", name=f"loop{t}")
+        z = synth.make_calibration(980 + t, R, gamma)[0]
+        c = ds.dspark_sts_apply(torch.from_numpy(z).cuda(), tau)
+        c_np = c.cpu().numpy()
+        o_c = oracle.sts_apply(z, tau_np)
+        np.testing.assert_allclose(c_np, o_c, rtol=1e-6, atol=2 * np.finfo(np.float32).tiny)
+        inp.c = c_np                                  # the oracle schedules on the same confidence
+        if t >= 2:
+            cap = ds.dspark_capacity(torch.from_numpy(survival[t - 2]).cuda(), sps_d)
+            K = int(cap["K"].cpu()[0])
+            assert K == oracle.capacity(survival[t - 2], sps).K
+        else:
+            K = R * gamma
+        d = upload(inp)
+        g = gpu_step(d, K, gamma)
+        tally = Tally()
+        reqs = list(range(R))
+        compare_draft(inp, g, reqs, tally)
+        compare_schedule(inp, g, K)
+        compare_verify(inp, g, reqs, tally)
+        tally.check()
+        survival[t] = g["a"]
+        print(f"[loop step {t}] K={K} rows={int(g['row_offsets'][-1])} accepted={int(g['n_accept'].sum())} "
+              f"{tally.summary()}", flush=True)
