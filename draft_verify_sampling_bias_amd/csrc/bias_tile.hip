@@ -1037,7 +1037,10 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
   if (p.seg_rows == kSegSmall) {
     // persistent: one workgroup per CU (draft: eight wavefronts, residual: four)
     const int wpb = RESID ? kSeg16Waves : kSeg16DraftWaves;
-    const int blocks = max(1, min((p.n_seg + wpb - 1) / wpb, num_cu));
+    // as many rounds of segments as one workgroup per CU needs, spread
+    // evenly: every wavefront gets the same count, or one fewer
+    const int rounds = max(1, (p.n_seg + wpb * num_cu - 1) / (wpb * num_cu));
+    const int blocks = max(1, min((p.n_seg + wpb * rounds - 1) / (wpb * rounds), num_cu));
     const dim3 grid(blocks), block(wpb * 64);
     if (p.w2p != nullptr)
       launch_seg16<RESID, VEC4, true>(p, grid, block, s, e0, e1);
