@@ -10,8 +10,10 @@
 // order is (a descending, k ascending, r ascending).  The Kc-th smallest key is
 // found by an 8-pass radix select (8-bit digits, LDS histograms); a candidate
 // is selected iff its key is <= that threshold, which gives exactly Kc
-// selections.  Then l[r], an exclusive scan of l[r] + 1 for the row offsets,
-// and the flattened rows.  Nothing here reads the drafted tokens except the
+// selections.  The last four passes (the (k, r) tie-break) are skipped when
+// the survival bits alone leave a bucket whose members are all selected.
+// Then l[r], an exclusive scan of l[r] + 1 for the row offsets, and the
+// flattened rows.  Nothing here reads the drafted tokens except the
 // copy into row_tok.
 
 #include "dspark_device.h"
@@ -58,6 +60,7 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
   __shared__ unsigned int hist[256];
   __shared__ unsigned long long s_prefix;
   __shared__ int s_rem;
+  __shared__ int s_all;
   __shared__ int s_i16[16];
   __shared__ float s_f16[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -110,7 +113,8 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
   if (!CUTOFF && !none && !all) {
     unsigned long long prefix = 0;
     int rem = static_cast<int>(Kc);
-    for (int pass = 0; pass < 8; ++pass) {
+    int pass = 0;
+    for (; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       if (tid < 256) hist[tid] = 0u;
       __syncthreads();
@@ -131,6 +135,7 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
             if (rem <= cb + hs[q]) {
               s_prefix = prefix | (static_cast<unsigned long long>(4 * lane + q) << shift);
               s_rem = rem - cb;
+              s_all = (rem - cb == hs[q]) ? 1 : 0;
               break;
             }
             cb += hs[q];
@@ -140,8 +145,12 @@ __global__ void __launch_bounds__(kSchedThreads) schedule_kernel(dspark_schedule
       __syncthreads();
       prefix = s_prefix;
       rem = s_rem;
+      // once the survival bits are fixed (the upper 32), a threshold bucket
+      // whose every member is selected needs no tie-break by (k, r): all
+      // keys up to the bucket's largest are taken (uniform: read from LDS)
+      if (pass == 3 && s_all) break;
     }
-    thr = prefix;
+    thr = (pass < 8) ? (prefix | 0xFFFFFFFFull) : prefix;
   }
 
   // l[r] and this thread's contribution to the expected token count

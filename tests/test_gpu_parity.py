@@ -425,3 +425,27 @@ def test_lagged_pipeline_over_steps():
         survival[t] = g["a"]
         print(f"[loop step {t}] K={K} rows={int(g['row_offsets'][-1])} accepted={int(g['n_accept'].sum())} "
               f"{tally.summary()}", flush=True)
+
+
+@pytest.mark.parametrize("R,gamma", [(5, 3), (64, 7), (300, 5), (1024, 16), (3000, 5)])
+def test_schedule_ties(R, gamma):
+    """Top-K schedule bit-exact against the oracle when survival values tie
+    heavily (confidences from a small set, exact 0 and 1), at every capacity
+    from none to all: the selection then depends on the (k, r) tie-break."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import oracle
+    rng = np.random.default_rng(1100 + R + gamma)
+    c = rng.choice(np.array([1.0, 1.0, 0.5, 0.25, 0.0], np.float32), (R, gamma))
+    anc = rng.integers(0, 50000, R).astype(np.int32)
+    y = rng.integers(0, 50000, (R, gamma)).astype(np.int32)
+    cd, ad, yd = (torch.from_numpy(x).cuda() for x in (c, anc, y))
+    n = R * gamma
+    Ks = sorted({0, 1, R, n // 3, n // 2, n - 1, n, int(rng.integers(0, n + 1)), int(rng.integers(0, n + 1))})
+    for K in Ks:
+        g = {k: v.cpu().numpy() for k, v in ds.dspark_schedule(cd, K, ad, yd).items()}
+        o = oracle.schedule(c, K, anc, y)
+        np.testing.assert_array_equal(g["l"], o.l, err_msg=f"K={K}")
+        np.testing.assert_array_equal(g["row_offsets"], o.row_offsets)
+        for f in ("row_req", "row_pos", "row_tok"):
+            np.testing.assert_array_equal(g[f], getattr(o, f), err_msg=f)
