@@ -21,12 +21,19 @@
 namespace dspark {
 namespace {
 
-// Rescan of one record segment: thread group i (256 / seg_rows lanes) owns
-// row v0 + i (16-row segments: 16 lanes per row; 32-row: 8; 64-row: 4).
+// Rescan of one record segment: thread group i (NT / seg_rows lanes) owns
+// row v0 + i (256 threads: 16 lanes per row for 16-row segments, 8 for
+// 32-row, 4 for 64-row; 1024 threads: four times as many).
+template <int NT = 256>
 __device__ __forceinline__ int lanes_log2(int seg_rows) {
-  return seg_rows == kSegSmall ? 4 : (seg_rows == kSegLarge ? 3 : 2);
+  constexpr int extra = NT == 1024 ? 2 : 0;
+  return (seg_rows == kSegSmall ? 4 : (seg_rows == kSegLarge ? 3 : 2)) + extra;
 }
 constexpr int kMaxSegRows = 64;
+// threads per workgroup of the draft finish (bf16 weights): its per-thread
+// share of the record pass (n_seg / NT records, read one after another)
+// sets the location's latency
+constexpr int kDraftFinishThreads = 1024;
 
 // Segment records of one request staged in LDS: up to 2048 records (16 KiB,
 // several workgroups per CU) or 16384 (128 KiB, i.e. V up to 262144 with
@@ -34,25 +41,30 @@ constexpr int kMaxSegRows = 64;
 // vocabularies read the records from global memory instead.
 constexpr int kStageSmall = 2048;
 constexpr int kStageRecs = 16384;
-constexpr int kStageBatch = 40;  // loads in flight per thread while staging
+constexpr int kStageBatchRecs = 10240;  // records in flight per workgroup while staging
 
-// Records are copied into LDS in batches of 256 * kStageBatch, every load of
-// a batch issued before any is used (one memory latency per batch).
+// Records are copied into LDS in batches of kStageBatchRecs (kStageBatchRecs
+// / NT loads per thread), every load of a batch issued before any is used
+// (one memory latency per batch).
+template <int NT = 256>
 struct StageBatch {
-  float2 r[kStageBatch];
+  static constexpr int kLoads = kStageBatchRecs / NT;
+  float2 r[kLoads];
 };
 
-__device__ __forceinline__ void stage_issue(const float2* __restrict__ src, int n, int base, StageBatch& b) {
+template <int NT = 256>
+__device__ __forceinline__ void stage_issue(const float2* __restrict__ src, int n, int base, StageBatch<NT>& b) {
 #pragma unroll
-  for (int j = 0; j < kStageBatch; ++j) b.r[j] = src[min(base + j * 256 + static_cast<int>(threadIdx.x), n - 1)];
+  for (int j = 0; j < StageBatch<NT>::kLoads; ++j)
+    b.r[j] = src[min(base + j * NT + static_cast<int>(threadIdx.x), n - 1)];
 }
 
 // Stores a batch into LDS, folding each record into f(r).  No barrier.
-template <class F>
-__device__ __forceinline__ void stage_commit(int n, int base, const StageBatch& b, float2* dst, F f) {
+template <int NT = 256, class F>
+__device__ __forceinline__ void stage_commit(int n, int base, const StageBatch<NT>& b, float2* dst, F f) {
 #pragma unroll
-  for (int j = 0; j < kStageBatch; ++j) {
-    const int t = base + j * 256 + static_cast<int>(threadIdx.x);
+  for (int j = 0; j < StageBatch<NT>::kLoads; ++j) {
+    const int t = base + j * NT + static_cast<int>(threadIdx.x);
     if (t < n) {
       dst[t] = b.r[j];
       f(b.r[j]);
@@ -63,27 +75,28 @@ __device__ __forceinline__ void stage_commit(int n, int base, const StageBatch& 
 // h = W1[prev, :] as fp32, split so that its loads can be in flight with
 // the record loads: hold() issues them into registers, commit() stores to
 // LDS (no barrier).
-template <typename WT>
+template <typename WT, int NT = 256>
 struct HRow {
-  static constexpr int kPer = DSPARK_MAX_RANK / 256;
+  static constexpr int kPer = (DSPARK_MAX_RANK + NT - 1) / NT;
   float v[kPer];
   __device__ __forceinline__ void hold(const WT* W1, int prev, int rank) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int k = static_cast<int>(threadIdx.x) + j * 256;
+      const int k = static_cast<int>(threadIdx.x) + j * NT;
       v[j] = weight_at<WT>(W1, static_cast<int64_t>(prev) * rank + min(k, rank - 1));
     }
   }
   __device__ __forceinline__ void commit(int rank, float* hs) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int k = static_cast<int>(threadIdx.x) + j * 256;
+      const int k = static_cast<int>(threadIdx.x) + j * NT;
       if (k < rank) hs[k] = v[j];
     }
   }
 };
 
 // Block-wide (max, lowest index) with one barrier; lm / li are used once.
+template <int NT = 256>
 __device__ __forceinline__ void block_amax_once(float& m, int& i, float* lm, int* li) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   wave_amax(m, i);
@@ -95,11 +108,11 @@ __device__ __forceinline__ void block_amax_once(float& m, int& i, float* lm, int
   m = lm[0];
   i = li[0];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) amax_merge(m, i, lm[w], li[w]);
+  for (int w = 1; w < NT / 64; ++w) amax_merge(m, i, lm[w], li[w]);
 }
 
-template <typename WT, int STAGE>
-__global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
+template <typename WT, int STAGE, int NT>
+__global__ void __launch_bounds__(NT) draft_finish_kernel(FinishParams p) {
   constexpr bool STAGED = STAGE > 0;
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh;
@@ -115,9 +128,9 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   const float T = p.temp[n];
   const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
   const float u_raw = p.u_draft[o];
-  StageBatch sb;
-  if (STAGED) stage_issue(gfine, n_seg, 0, sb);
-  HRow<WT> hrow;
+  StageBatch<NT> sb;
+  if (STAGED) stage_issue<NT>(gfine, n_seg, 0, sb);
+  HRow<WT, NT> hrow;
   hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
   // maximum (greedy: with the lowest argmax carried in the records' second
   // word; sampled: the second word is ignored), taken while staging
@@ -125,17 +138,17 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
   int im = kIntMax;
   auto fold = [&](float2 r) { amax_merge(m, im, r.x, __float_as_int(r.y)); };
   if (STAGED) {
-    stage_commit(n_seg, 0, sb, srec, fold);
-    for (int base = 256 * kStageBatch; base < n_seg; base += 256 * kStageBatch) {
-      stage_issue(gfine, n_seg, base, sb);
-      stage_commit(n_seg, base, sb, srec, fold);
+    stage_commit<NT>(n_seg, 0, sb, srec, fold);
+    for (int base = kStageBatchRecs; base < n_seg; base += kStageBatchRecs) {
+      stage_issue<NT>(gfine, n_seg, base, sb);
+      stage_commit<NT>(n_seg, base, sb, srec, fold);
     }
   } else {
 #pragma unroll 8
-    for (int t = tid; t < n_seg; t += 256) fold(gfine[t]);
+    for (int t = tid; t < n_seg; t += NT) fold(gfine[t]);
   }
   hrow.commit(p.rank, hs);
-  block_amax_once(m, im, sh.fred, sh.ired);  // also orders the LDS stores above before the reads below
+  block_amax_once<NT>(m, im, sh.fred, sh.ired);  // also orders the LDS stores above before the reads below
   const float M = m;
   const float c = temp_scale(T);
   if (c == 0.0f) {
@@ -153,11 +166,11 @@ __global__ void __launch_bounds__(256) draft_finish_kernel(FinishParams p) {
     const float2 r = fine[t];
     return r.y * exp2_hw((r.x - M) * c);
   };
-  const Located2 L = locate_blocked(n_seg, mass, u, &sh);
+  const Located2 L = locate_blocked<NT>(n_seg, mass, u, &sh);
   const int seg = L.seg < 0 ? 0 : L.seg;
   const float ms = fine[seg].x;
   const float th = L.fallback ? INFINITY : L.rem / exp2_hw((ms - M) * c);
-  const int lg = lanes_log2(p.seg_rows);
+  const int lg = lanes_log2<NT>(p.seg_rows);
   const int v0 = seg * p.seg_rows;
   const int i = tid >> lg;
   const int v = v0 + i;
@@ -207,16 +220,16 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   const float u = clamp_uniform(p.u_final[n]);
   const float2* gfine = reinterpret_cast<const float2*>(p.rpart) + static_cast<int64_t>(n) * p.n_seg;
   const float2* fine = STAGED ? srec : gfine;
-  StageBatch sb;
-  if (STAGED) stage_issue(gfine, p.n_seg, 0, sb);
-  HRow<WT> hrow;
+  StageBatch<256> sb;
+  if (STAGED) stage_issue<256>(gfine, p.n_seg, 0, sb);
+  HRow<WT, 256> hrow;
   hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
   if (STAGED) {
     auto none = [](float2) {};
-    stage_commit(p.n_seg, 0, sb, srec, none);
-    for (int base = 256 * kStageBatch; base < p.n_seg; base += 256 * kStageBatch) {
-      stage_issue(gfine, p.n_seg, base, sb);
-      stage_commit(p.n_seg, base, sb, srec, none);
+    stage_commit<256>(p.n_seg, 0, sb, srec, none);
+    for (int base = kStageBatchRecs; base < p.n_seg; base += kStageBatchRecs) {
+      stage_issue<256>(gfine, p.n_seg, base, sb);
+      stage_commit<256>(p.n_seg, base, sb, srec, none);
     }
   }
   hrow.commit(p.rank, hs);
@@ -227,7 +240,7 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   int out = -1;
   if (L.Z > 0.0f && L.seg >= 0) {
     const float th = L.fallback ? INFINITY : L.rem;
-    const int lg = lanes_log2(p.seg_rows);
+    const int lg = lanes_log2<256>(p.seg_rows);
     const int v0 = L.seg * p.seg_rows;
     const int i = tid >> lg;
     const int v = v0 + i;
@@ -261,22 +274,26 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
 
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  const dim3 grid(p.R), block(256);
+  const dim3 grid(p.R);
   const int stage = p.n_seg <= kStageSmall ? kStageSmall : (p.n_seg <= kStageRecs ? kStageRecs : 0);
   if (wdtype == DSPARK_W_BF16) {
+    constexpr int NT = kDraftFinishThreads;
+    const dim3 block(NT);
     if (stage == kStageSmall)
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageSmall>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageSmall, NT>), grid, block, 0, s, p);
     else if (stage == kStageRecs)
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageRecs>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageRecs, NT>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, 0>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, 0, NT>), grid, block, 0, s, p);
   } else {
+    // fp32 weights: the 32-row rescan's registers fit 256 threads per workgroup
+    const dim3 block(256);
     if (stage == kStageSmall)
-      hipLaunchKernelGGL((draft_finish_kernel<float, kStageSmall>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<float, kStageSmall, 256>), grid, block, 0, s, p);
     else if (stage == kStageRecs)
-      hipLaunchKernelGGL((draft_finish_kernel<float, kStageRecs>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<float, kStageRecs, 256>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((draft_finish_kernel<float, 0>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((draft_finish_kernel<float, 0, 256>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

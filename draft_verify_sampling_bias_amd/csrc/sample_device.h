@@ -120,40 +120,48 @@ struct Located2 {
   bool fallback;
 };
 
+constexpr int kLocMaxWaves = 16;  // workgroups of up to 1024 threads
 struct Loc2Scratch {
-  float wsum[4];   // per-wavefront totals of the block scan
-  float fred[4];   // per-wavefront maxima (finish kernels)
-  int ired[4];
-  int cand[4];     // per-wavefront first thread whose interval holds u Z
-  float cexcl[4];  // and its exclusive prefix
-  int glast[4];    // per-wavefront last segment with positive mass
+  float wsum[kLocMaxWaves];   // per-wavefront totals of the block scan
+  float fred[kLocMaxWaves];   // per-wavefront maxima (finish kernels)
+  int ired[kLocMaxWaves];
+  int cand[kLocMaxWaves];     // per-wavefront first thread whose interval holds u Z
+  float cexcl[kLocMaxWaves];  // and its exclusive prefix
+  int glast[kLocMaxWaves];    // per-wavefront last segment with positive mass
   int sel;
   float rem;
   int fb;
 };
 
-// First segment of thread block i of the 256-way partition.
-__device__ __forceinline__ int block_begin(int i, int n) { return range_start(i, n, 256); }
+// First segment of thread block i of the NT-way partition.
+template <int NT = 256>
+__device__ __forceinline__ int block_begin(int i, int n) { return range_start(i, n, NT); }
 
 // Second half of the location: ts is this thread's block sum (already in
 // the units of mass()), lastpos its last segment with positive mass (or -1).
 // Three workgroup barriers; every scratch slot is written once per call, so
 // no barrier is needed to protect reuse (callers must not call it twice
 // with the same scratch without a barrier in between).
-template <class Mass>
+template <int NT = 256, class Mass>
 __device__ Located2 locate_from_block_sums(int n, float ts, int lastpos, Mass mass, float u, Loc2Scratch* sh) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // block-wide scan: thread intervals [excl, incl) of consecutive threads
-  // meet exactly (incl of one thread is excl of the next, bit for bit)
+  // meet exactly (incl of one thread is excl of the next, bit for bit: every
+  // wavefront offset is the same left-to-right sum of the totals before it)
   const float v = wave_incl_scan(ts);
   if (lane == 63) sh->wsum[wave] = v;
   __syncthreads();
-  const float w0 = sh->wsum[0], w1 = sh->wsum[1], w2 = sh->wsum[2], w3 = sh->wsum[3];
-  const float off = (wave == 0) ? 0.0f : (wave == 1) ? w0 : (wave == 2) ? (w0 + w1) : ((w0 + w1) + w2);
+  float off = 0.0f, Z = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float x = sh->wsum[w];
+    off = (w < wave) ? Z + x : off;
+    Z += x;
+  }
   const float incl = off + v;
   const float up = __shfl_up(incl, 1);
   const float excl = (lane == 0) ? off : up;
-  const float Z = ((w0 + w1) + w2) + w3;
   const float theta = u * Z;
   // the first thread whose interval holds theta, with its exclusive prefix,
   // and the last positive segment, in one barrier round
@@ -162,26 +170,27 @@ __device__ Located2 locate_from_block_sums(int n, float ts, int lastpos, Mass ma
   const float fex = __shfl(excl, fl);
   const int wl = wave_max_int(lastpos);
   if (lane == 0) {
-    sh->cand[wave] = hit ? (wave * 64 + fl) : 256;
+    sh->cand[wave] = hit ? (wave * 64 + fl) : NT;
     sh->cexcl[wave] = fex;
     sh->glast[wave] = wl;
   }
   __syncthreads();
-  int first = 256;
+  int first = NT;
   float P = 0.0f;
+  int glast = -1;
 #pragma unroll
-  for (int w = 3; w >= 0; --w) {
-    const bool has = sh->cand[w] < 256;
+  for (int w = NW - 1; w >= 0; --w) {
+    const bool has = sh->cand[w] < NT;
     first = has ? sh->cand[w] : first;
     P = has ? sh->cexcl[w] : P;
+    glast = max(glast, sh->glast[w]);
   }
-  const int glast = max(max(sh->glast[0], sh->glast[1]), max(sh->glast[2], sh->glast[3]));
   int s0, s1;
   float th;
   bool fb;
-  if (first < 256) {
-    s0 = block_begin(first, n);
-    s1 = block_begin(first + 1, n);
+  if (first < NT) {
+    s0 = block_begin<NT>(first, n);
+    s1 = block_begin<NT>(first + 1, n);
     th = theta - P;
     fb = false;
   } else {
@@ -235,10 +244,10 @@ __device__ Located2 locate_from_block_sums(int n, float ts, int lastpos, Mass ma
   return out;
 }
 
-template <class Mass>
+template <int NT = 256, class Mass>
 __device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
   const int tid = threadIdx.x;
-  const int t0 = block_begin(tid, n), t1 = block_begin(tid + 1, n);
+  const int t0 = block_begin<NT>(tid, n), t1 = block_begin<NT>(tid + 1, n);
   float ts = 0.0f;
   int lastpos = -1;
 #pragma unroll 8
@@ -247,7 +256,7 @@ __device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
     ts += x;
     lastpos = (x > 0.0f) ? t : lastpos;
   }
-  return locate_from_block_sums(n, ts, lastpos, mass, u, sh);
+  return locate_from_block_sums<NT>(n, ts, lastpos, mass, u, sh);
 }
 
 // Wave 0: first of n <= 64 weights whose inclusive prefix exceeds theta,
