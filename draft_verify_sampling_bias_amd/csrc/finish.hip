@@ -30,9 +30,9 @@ __device__ __forceinline__ int lanes_log2(int seg_rows) {
   return (seg_rows == kSegSmall ? 4 : (seg_rows == kSegLarge ? 3 : 2)) + extra;
 }
 constexpr int kMaxSegRows = 64;
-// threads per workgroup of the draft finish (bf16 weights): its per-thread
-// share of the record pass (n_seg / NT records, read one after another)
-// sets the location's latency
+// threads per workgroup of the draft finish (bf16 weights, at most one
+// request per CU): its per-thread share of the record pass (n_seg / NT
+// records, read one after another) sets the location's latency
 constexpr int kDraftFinishThreads = 1024;
 
 // Segment records of one request staged in LDS: up to 2048 records (16 KiB,
@@ -272,29 +272,44 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
 
 }  // namespace
 
+template <typename WT, int NT>
+void launch_draft_finish_nt(const FinishParams& p, int stage, hipStream_t s) {
+  const dim3 grid(p.R), block(NT);
+  if (stage == kStageSmall)
+    hipLaunchKernelGGL((draft_finish_kernel<WT, kStageSmall, NT>), grid, block, 0, s, p);
+  else if (stage == kStageRecs)
+    hipLaunchKernelGGL((draft_finish_kernel<WT, kStageRecs, NT>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((draft_finish_kernel<WT, 0, NT>), grid, block, 0, s, p);
+}
+
+// Compute units of the current device, cached per device (256 if the query
+// fails).
+static int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  const dim3 grid(p.R);
+  const int num_cu = device_cu_count();
   const int stage = p.n_seg <= kStageSmall ? kStageSmall : (p.n_seg <= kStageRecs ? kStageRecs : 0);
-  if (wdtype == DSPARK_W_BF16) {
-    constexpr int NT = kDraftFinishThreads;
-    const dim3 block(NT);
-    if (stage == kStageSmall)
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageSmall, NT>), grid, block, 0, s, p);
-    else if (stage == kStageRecs)
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, kStageRecs, NT>), grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL((draft_finish_kernel<uint16_t, 0, NT>), grid, block, 0, s, p);
-  } else {
-    // fp32 weights: the 32-row rescan's registers fit 256 threads per workgroup
-    const dim3 block(256);
-    if (stage == kStageSmall)
-      hipLaunchKernelGGL((draft_finish_kernel<float, kStageSmall, 256>), grid, block, 0, s, p);
-    else if (stage == kStageRecs)
-      hipLaunchKernelGGL((draft_finish_kernel<float, kStageRecs, 256>), grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL((draft_finish_kernel<float, 0, 256>), grid, block, 0, s, p);
-  }
+  // 1024 threads while every request's workgroup gets a CU of its own; more
+  // requests than CUs run as several smaller workgroups per CU instead.  fp32
+  // weights: the 32-row rescan's registers fit 256 threads per workgroup.
+  if (wdtype == DSPARK_W_BF16 && p.R <= num_cu)
+    launch_draft_finish_nt<uint16_t, kDraftFinishThreads>(p, stage, s);
+  else if (wdtype == DSPARK_W_BF16)
+    launch_draft_finish_nt<uint16_t, 256>(p, stage, s);
+  else
+    launch_draft_finish_nt<float, 256>(p, stage, s);
   return hipGetLastError();
 }
 
