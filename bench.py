@@ -171,6 +171,9 @@ def main():
                     help="sequential temperature scaling: each step calibrates the confidence logits with "
                          "temperatures fitted once (dspark_sts_fit on synthetic calibration blocks, before "
                          "timing) and schedules on the calibrated confidence (dspark_sts_apply)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step once in a HIP graph (torch.cuda.CUDAGraph) and time its replays; "
+                         "every shape is fixed ahead, so the captured step needs no host work")
     ap.add_argument("--no-pack", action="store_true",
                     help="read W2 itself instead of its fragment-packed copy (dspark_pack_w2)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -310,6 +313,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # the measured step: the eager calls, or the replay of their capture
+    run = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                step()
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        run = graph.replay
+        for _ in range(args.warmup):
+            evict()
+            run()
+        torch.cuda.synchronize()
+
     K = args.steps
     positions = R * gamma * K
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
@@ -320,7 +342,7 @@ def main():
     for i in range(K):
         evict()
         ev[i][0].record(stream)
-        step()
+        run()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall_cold = time.perf_counter() - t0
@@ -344,7 +366,7 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(K):
-            step()
+            run()
         torch.cuda.synchronize()
         wall_warm = time.perf_counter() - t1
         warm = dict(value=positions / wall_warm, ms_per_step=wall_warm / K * 1e3)
@@ -392,7 +414,8 @@ def main():
         "hbm_gbps": round(step_gbps, 1),
         "hbm_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": int(bytes_step),
-        "timing": "sum of per-step HIP-event intervals; caches evicted by a 1 GiB read before each step (excluded)",
+        "timing": "sum of per-step HIP-event intervals; caches evicted by a 1 GiB read before each step (excluded)"
+                  + ("; the step is the replay of its HIP-graph capture" if args.graph else ""),
         "wall_s_timed_loop": round(wall_cold, 4),
         "step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(step_ms, [10, 50, 90])],
         "warm_back_to_back": None if warm is None else {k: round(v, 4) for k, v in warm.items()},

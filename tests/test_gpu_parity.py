@@ -449,3 +449,89 @@ def test_schedule_ties(R, gamma):
         np.testing.assert_array_equal(g["row_offsets"], o.row_offsets)
         for f in ("row_req", "row_pos", "row_tok"):
             np.testing.assert_array_equal(g[f], getattr(o, f), err_msg=f)
+
+
+def test_step_graph_capture_replays():
+    """A whole step (draft, schedule, verify) captured once in a HIP graph.
+    Every buffer is allocated before the capture and every call has a shape
+    known on the host (the capacity is fixed ahead), so the captured step
+    replays without host work.  The graph is replayed several times, with
+    eager work and synchronisations in between, with new inputs copied in
+    before each replay, and every replay must equal the eager step on the
+    same inputs bit for bit."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    R, gamma, V, rank = 64, 5, 20000, 128
+    inps = [synth.make_custom(1200 + i, R, gamma, V, rank, policy="temps", name=f"graph{i}") for i in range(3)]
+    K = (R * gamma) // 2
+    d = upload(inps[0])
+    # the schedule of these inputs decides which target rows the verify reads;
+    # the rows buffer is refilled (eagerly) before each replay
+    n_rows = ds.dspark_schedule_rows(R, gamma, K)
+    dev = torch.device("cuda:0")
+    y = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+    q_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(ds.draft_workspace_bytes(R, gamma, V, rank, ds.W_BF16), dtype=torch.uint8, device=dev)
+    sch = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+               l=torch.empty(R, dtype=torch.int32, device=dev),
+               row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
+               row_req=torch.empty(n_rows, dtype=torch.int32, device=dev),
+               row_pos=torch.empty(n_rows, dtype=torch.int32, device=dev),
+               row_tok=torch.empty(n_rows, dtype=torch.int32, device=dev),
+               expected_tokens=torch.empty(1, dtype=torch.float32, device=dev))
+    rows = torch.empty((n_rows, V), dtype=torch.float32, device=dev)
+    n_acc = torch.empty(R, dtype=torch.int32, device=dev)
+    out_tok = torch.empty(R, dtype=torch.int32, device=dev)
+    p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    ws_v = torch.empty(ds.verify_workspace_bytes(R, gamma, V, rank, ds.W_BF16, n_rows), dtype=torch.uint8,
+                       device=dev)
+
+    def step():
+        ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"],
+                              out=(y, q_tok, q_stats), workspace=ws_d)
+        ds.dspark_schedule(d["c"], K, d["anchor"], y, out=sch)
+        ds.dspark_verify(rows, sch["row_offsets"], d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], y, q_tok,
+                         q_stats, d["u_accept"], d["u_final"], out=(n_acc, out_tok, p_tok), workspace=ws_v)
+
+    def load(inp):
+        nd = upload(inp)
+        for k in d:
+            d[k].copy_(nd[k])
+        # the target rows of this input's schedule (stand-in for the target forward)
+        ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"],
+                              out=(y, q_tok, q_stats), workspace=ws_d)
+        ds.dspark_schedule(d["c"], K, d["anchor"], y, out=sch)
+        rows.copy_(d["target"][sch["row_req"].long(), sch["row_pos"].long()])
+        torch.cuda.synchronize()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {k: v.clone() for k, v in dict(y=y, q_tok=q_tok, q_stats=q_stats, n_acc=n_acc, out_tok=out_tok,
+                                               p_tok=p_tok, **sch).items()}
+
+    load(inps[0])
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()  # warm the stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        inp = inps[rep % 3]
+        load(inp)
+        step()
+        eager = snapshot()
+        torch.sum(rows, dim=0)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        replay = snapshot()
+        for k in eager:
+            assert torch.equal(eager[k], replay[k]), (rep, k)
+        print(f"[graph replay {rep}] input {rep % 3}: identical to eager; accepted {int(n_acc.sum())}", flush=True)
