@@ -174,11 +174,14 @@ __global__ void __launch_bounds__(NT) draft_finish_kernel(FinishParams p) {
   const int v0 = seg * p.seg_rows;
   const int i = tid >> lg;
   const int v = v0 + i;
+  // the row's base logit is loaded before the W2 row, so both are in flight
+  // together (clamped address; rows past V are masked below)
+  const float uv = p.U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
   const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);
   if ((tid & ((1 << lg) - 1)) == 0) {
     float s = -INFINITY, e = 0.0f;
     if (v < V) {
-      s = p.U_base[static_cast<int64_t>(n) * p.U_stride + v] + b;
+      s = uv + b;
       e = exp2_hw((s - ms) * c);
     }
     e64[i] = e;
@@ -244,13 +247,17 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
     const int v0 = L.seg * p.seg_rows;
     const int i = tid >> lg;
     const int v = v0 + i;
+    // the row's base and target logits are loaded before the W2 row, so all
+    // are in flight together (clamped addresses; rows past V are masked below)
+    const int vc = min(v, V - 1);
+    const float uv = p.U[urow * V + vc], tv = tr[vc];
     const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);
     if ((tid & ((1 << lg) - 1)) == 0) {
       float w = 0.0f;
       if (v < V) {
-        const float s = p.U[urow * V + v] + b;
+        const float s = uv + b;
         const float q = exp2_hw((s - Mq) * c) * iZq;
-        const float pp = exp2_hw((tr[v] - Mp) * c) * iZp;
+        const float pp = exp2_hw((tv - Mp) * c) * iZp;
         w = fmaxf(pp - q, 0.0f);
       }
       e64[i] = w;
