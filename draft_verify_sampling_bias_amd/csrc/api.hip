@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "device_info.h"
 #include "dspark.h"
 #include "launchers.h"
 #include "plan.h"
@@ -16,20 +17,6 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPAR
 template <typename T>
 inline T* ws_at(void* ws, std::size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
-}
-
-// Compute units of the current device (persistent-grid sizing), cached per
-// device; 256 if the query fails.
-int current_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cu = 0;
-    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
-    cached[dev] = cu;
-  }
-  return cached[dev];
 }
 
 }  // namespace

@@ -13,6 +13,7 @@
 // that residual has no mass it draws from p.
 
 
+#include "device_info.h"
 #include "dspark_device.h"
 #include "launchers.h"
 #include "plan.h"
@@ -290,23 +291,9 @@ void launch_draft_finish_nt(const FinishParams& p, int stage, hipStream_t s) {
     hipLaunchKernelGGL((draft_finish_kernel<WT, 0, NT>), grid, block, 0, s, p);
 }
 
-// Compute units of the current device, cached per device (256 if the query
-// fails).
-static int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int cu = 0;
-    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
-    cached[dev] = cu;
-  }
-  return cached[dev];
-}
-
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  const int num_cu = device_cu_count();
+  const int num_cu = current_cu_count();
   const int stage = p.n_seg <= kStageSmall ? kStageSmall : (p.n_seg <= kStageRecs ? kStageRecs : 0);
   // 1024 threads while every request's workgroup gets a CU of its own; more
   // requests than CUs run as several smaller workgroups per CU instead.  fp32
