@@ -10,15 +10,17 @@
 //   K           the first K < kmax with Theta(K + 1) <= Theta(K) (or NaN),
 //               else kmax = min(R * gamma, n_sps - 1 - R).
 //
-// One workgroup of 1024 threads:
+// One workgroup of 1024 threads, each holding E = 2, 4, 8 or 16 entries
+// (N = 1024 E >= R * gamma, padded with +0):
 //   1. the values' fp32 bit patterns (non-negative, so their unsigned order
-//      is the value order) are sorted descending by a bitonic network in LDS,
-//      padded with +0 to N = max(2048, next power of two) entries;
-//   2. thread t owns sorted positions t*c .. t*c + c - 1 (c = N / 1024) and
-//      sums them exactly in a 192-bit fixed-point integer (unit 2^-149, the
-//      smallest fp32 subnormal; a value <= 1 is below 2^150 and at most 2^14
-//      of them are summed); a block-wide exclusive scan of those integers
-//      gives every exact prefix sum;
+//      is the value order) are sorted descending by a bitonic network: strides
+//      below E inside a thread's registers, below 64 E by lane shuffles, the
+//      ten cross-wavefront stages through LDS;
+//   2. thread t then owns sorted positions t*E .. t*E + E - 1 and sums them
+//      exactly in a 192-bit fixed-point integer (unit 2^-149, the smallest
+//      fp32 subnormal; a value <= 1 is below 2^150 and at most 2^14 of them
+//      are summed); a block-wide exclusive scan of those integers gives every
+//      exact prefix sum;
 //   3. each prefix sum is rounded to fp64 (round to nearest even), R is added
 //      and the stop test is evaluated for each owned position; a block
 //      minimum gives K.
