@@ -278,3 +278,26 @@ def test_null_args_pointer():
     assert lib.dspark_capacity(None) == ds.Status.ERR_NULL
     assert lib.dspark_sts_fit(None) == ds.Status.ERR_NULL
     assert lib.dspark_sts_apply(None) == ds.Status.ERR_NULL
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: with libdspark.so absent, the binding's first use raises
+    ImportError (run in a child process against a copy of the package whose
+    library is missing, so the loaded library of this process is untouched)."""
+    import shutil
+    import sys
+    pkg = os.path.join(ROOT, "draft_verify_sampling_bias_amd")
+    dst = tmp_path / "draft_verify_sampling_bias_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import draft_verify_sampling_bias_amd as ds\n"
+            "assert not ds.LIB_PATH.startswith(%r)\n"
+            "try:\n"
+            "    ds.dspark_abi_version()\n"
+            "except ImportError as e:\n"
+            "    print('raised', e)\n"
+            "else:\n"
+            "    raise SystemExit('no error')\n") % (str(tmp_path), ROOT + os.sep)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=str(tmp_path))
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "raised" in r.stdout and "libdspark.so" in r.stdout
