@@ -6,7 +6,8 @@
         --alg-bytes N --commands TEXT > out.txt
 
 `stats` condenses a `--kernel-trace --stats` kernel table (calls, total and
-average duration per kernel).  `mfma` reports a kernel's bf16 MFMA work and
+average duration per kernel).  `calls` lists one kernel's durations from a
+`--kernel-trace` table in call order, grouped per size of a sweep.  `mfma` reports a kernel's bf16 MFMA work and
 utilisation from SQ counters and its traced average duration.  `traffic` turns two `--pmc FETCH_SIZE` /
 `--pmc WRITE_SIZE` runs (KiB per dispatch) into HBM bytes per launch of one
 kernel, each counter scaled by what it reads for a device copy of known size
@@ -53,6 +54,24 @@ def stats_text(csv_path, command):
         out.append(f"  {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e3:10.1f} "
                    f"{float(r['AverageNs']) / 1e3:9.2f} {float(r['MinNs']) / 1e3:8.2f} "
                    f"{float(r['MaxNs']) / 1e3:8.2f} {float(r['Percentage']):6.2f}  {_short(r['Name'])}")
+    return "\n".join(out) + "\n"
+
+
+def calls_text(trace_csv, kernel, group, labels, command):
+    """Durations of the dispatches of one kernel (name substring) in call
+    order, grouped: one line per group of `group` calls with its label."""
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    names = [_short(r["Kernel_Name"], 60) for r in rows]
+    if len(dur) != group * len(labels):
+        raise SystemExit(f"{len(dur)} dispatches of {kernel!r}, expected {group} x {len(labels)}")
+    out = [f"# kernel durations by call group (rocprofv3 --kernel-trace), {group} calls per size",
+           f"# command: {command}",
+           f"# {'median_us':>10} {'min_us':>8}  size / kernel"]
+    for i, lab in enumerate(labels):
+        d = sorted(dur[i * group:(i + 1) * group])
+        out.append(f"  {d[len(d) // 2]:10.2f} {d[0]:8.2f}  {lab}  [{names[i * group]}]")
     return "\n".join(out) + "\n"
 
 
@@ -166,6 +185,12 @@ def main(argv=None):
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--alg-bytes", type=int, required=True)
     t.add_argument("--commands", action="append", default=[])
+    c = sub.add_parser("calls")
+    c.add_argument("trace_csv")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--group", type=int, required=True)
+    c.add_argument("--labels", required=True, help="comma-separated, one per group")
+    c.add_argument("--command", required=True)
     m = sub.add_parser("mfma")
     m.add_argument("--kernel", required=True)
     m.add_argument("--counters", required=True)
@@ -174,6 +199,9 @@ def main(argv=None):
     m.add_argument("--peak-tflops", type=float, default=2500.0)
     m.add_argument("--commands", action="append", default=[])
     a = ap.parse_args(argv)
+    if a.mode == "calls":
+        sys.stdout.write(calls_text(a.trace_csv, a.kernel, a.group, a.labels.split(","), a.command))
+        return
     if a.mode == "mfma":
         sys.stdout.write(mfma_text(a.kernel, a.counters, a.stats, a.flops, a.peak_tflops, a.commands))
         return
