@@ -529,17 +529,34 @@ __device__ __forceinline__ void wide_h_issue(const TileParams& p, const WideReq<
 }
 
 // Stores a chunk's W1 rows into an LDS stage; pieces past the 16 rows land
-// in row 16.  Groups past the rank hold the row's last real weights again
-// (clamped loads): the W2 fragments are zero there, so they add 0.
+// in row 16.  Groups past the rank are not stored: wide_h_zero_tail clears
+// them once in both stages, and they stay zero.  Their loads were clamped to
+// the row's last real weights, and so were those of the W2 fragments, which
+// are zeroed (wide_w2_ready) only in the last k-step, while a rank whose
+// next-to-last k-step is not full (e.g. 72, 200 or 384) has such groups in
+// earlier k-steps too.
 template <int KS>
-__device__ __forceinline__ void wide_h_commit(const WideH<KS>& h, uint16_t* stage) {
+__device__ __forceinline__ void wide_h_commit(const WideH<KS>& h, int rank, uint16_t* stage) {
   constexpr int G = WideH<KS>::kGroups;
   constexpr int RS = KS * 32 + 8;
 #pragma unroll
   for (int j = 0; j < WideH<KS>::kPer; ++j) {
     const int q = static_cast<int>(threadIdx.x) + j * 256;
     const int r = min(q / G, kWideChunk), g = q % G;
-    *reinterpret_cast<u32x4_t*>(stage + r * RS + g * 8) = h.v[j];
+    if (g * 8 < rank) *reinterpret_cast<u32x4_t*>(stage + r * RS + g * 8) = h.v[j];
+  }
+}
+
+// Zeroes the groups past the rank in every row of the nst LDS stages of
+// kStage elements (no barrier).
+template <int KS>
+__device__ __forceinline__ void wide_h_zero_tail(int rank, uint16_t* Hs, int nst) {
+  constexpr int G = WideH<KS>::kGroups;
+  constexpr int RS = KS * 32 + 8;
+  constexpr int kRows = kWideChunk + 1;
+  for (int q = static_cast<int>(threadIdx.x); q < nst * kRows * G; q += 256) {
+    const int row = q / G, g = q % G;  // row counts over the stages: stage st holds rows st * kRows ..
+    if (g * 8 >= rank) *reinterpret_cast<u32x4_t*>(Hs + row * RS + g * 8) = u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
@@ -598,7 +615,8 @@ __device__ __forceinline__ void wide_w2_load(const TileParams& p, int vw, int la
 }
 
 // Called once the prologue's other loads are issued: zeroes the groups past
-// the rank (only the last k-step can hold any) and pins every fragment to the
+// the rank in the last k-step (the H rows are zero in every group past the
+// rank, wide_h_commit) and pins every fragment to the
 // accumulation registers, the operand form the MFMA reads directly, which
 // leaves the architectural registers to the stream.
 template <int KS>
@@ -782,7 +800,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
   for (int b = 0; b < 4; ++b) ua.u[b] = ua.t[RESID ? b : 0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   wide_u_issue<RESID, VEC4>(p, win[0], 0, 0, vw, lane, ub);
-  wide_h_commit<KS>(h0, Hs);
+  wide_h_zero_tail<KS>(rank, Hs, 2);
+  wide_h_commit<KS>(h0, rank, Hs);
   // every load of the prologue (W2 included) has landed before the loop:
   // the loop's own waits then follow its steady state only
   wide_w2_ready<KS>(rank, lane, w);
@@ -832,7 +851,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
       if (j >= 4 && j < 4 + kEpiSteps) wide_epi_step<RESID>(j - 4, p, seg, lane, uf, acc_prev, c > 0, ep);
       if (j == kUSlot) wide_u_issue<RESID, VEC4>(p, win1, c1, c1 % kWideWinChunks, vw, lane, uf);
-      if (j == 60) wide_h_commit<KS>(hb, Hs + (s ^ 1) * kStage);
+      if (j == 60) wide_h_commit<KS>(hb, rank, Hs + (s ^ 1) * kStage);
     };
     const uint16_t* hbase = Hs + s * kStage + (lane & 15) * RS + (lane >> 4) * 8;
     u32x4_t bq = *reinterpret_cast<const u32x4_t*>(hbase);

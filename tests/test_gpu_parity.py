@@ -51,6 +51,13 @@ SMALL = [
     (26, 600, 2, 4160, 256, "bf16", "temps", "fixed"),       # 38 chunks, 3 windows, ragged last window
     (27, 65, 3, 5000, 512, "bf16", "sampled", "uniformK"),   # one request in the last chunk
     (28, 97, 2, 1000, 96, "bf16", "sampled", "fixed"),       # rank 96: zero k-groups in the last step
+    # ranks whose next-to-last k-step is not full: k-groups past the rank
+    # before the last k-step
+    (29, 70, 3, 1000, 24, "bf16", "mixed", "uniformK"),      # rank 24: one such group in the first step
+    (30, 80, 2, 777, 8, "bf16", "sampled", "fixed"),         # rank 8: one real k-group
+    (31, 66, 2, 2000, 72, "bf16", "temps", "fixed"),         # rank 72: 4 k-steps, the third partial
+    (32, 90, 2, 1500, 200, "bf16", "mixed", "uniformK"),     # rank 200: 8 k-steps, the seventh partial
+    (33, 67, 2, 1200, 384, "bf16", "sampled", "fixed"),      # rank 384: 16 k-steps, the last four empty
 ]
 
 
