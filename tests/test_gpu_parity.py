@@ -58,6 +58,9 @@ SMALL = [
     (31, 66, 2, 2000, 72, "bf16", "temps", "fixed"),         # rank 72: 4 k-steps, the third partial
     (32, 90, 2, 1500, 200, "bf16", "mixed", "uniformK"),     # rank 200: 8 k-steps, the seventh partial
     (33, 67, 2, 1200, 384, "bf16", "sampled", "fixed"),      # rank 384: 16 k-steps, the last four empty
+    (34, 40, 3, 3000, 200, "bf16", "mixed", "uniformK"),     # the same ranks on the 16-row path
+    (35, 64, 2, 2000, 384, "bf16", "sampled", "fixed"),
+    (36, 10, 2, 1000, 200, "f32", "temps", "fixed"),         # and on the fp32 path
 ]
 
 
