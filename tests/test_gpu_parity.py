@@ -61,6 +61,9 @@ SMALL = [
     (34, 40, 3, 3000, 200, "bf16", "mixed", "uniformK"),     # the same ranks on the 16-row path
     (35, 64, 2, 2000, 384, "bf16", "sampled", "fixed"),
     (36, 10, 2, 1000, 200, "f32", "temps", "fixed"),         # and on the fp32 path
+    (37, 70, 3, 5, 16, "bf16", "mixed", "uniformK"),         # tiny vocabularies on the 64-row path
+    (38, 66, 2, 4, 8, "bf16", "sampled", "fixed"),           # (one segment, V % 4 == 0)
+    (39, 3, 2, 4, 8, "f32", "sampled", "fixed"),             # and on the fp32 path
 ]
 
 
