@@ -64,6 +64,9 @@ SMALL = [
     (37, 70, 3, 5, 16, "bf16", "mixed", "uniformK"),         # tiny vocabularies on the 64-row path
     (38, 66, 2, 4, 8, "bf16", "sampled", "fixed"),           # (one segment, V % 4 == 0)
     (39, 3, 2, 4, 8, "f32", "sampled", "fixed"),             # and on the fp32 path
+    (40, 2, 2, 200000, 16, "bf16", "mixed", "fixed"),        # 12500 records: staged in two batches
+    (41, 3, 2, 32768, 64, "bf16", "sampled", "fixed"),       # 2048 records: the small stage, full
+    (42, 3, 2, 32784, 64, "bf16", "sampled", "fixed"),       # 2049 records: the large stage
 ]
 
 
