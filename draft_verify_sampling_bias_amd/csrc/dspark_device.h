@@ -87,8 +87,14 @@ __device__ __forceinline__ float exp2_rel(float x, float m, float c) {
 }
 
 // Scale that turns (logit - max) into a base-2 exponent at temperature T;
-// 0 marks a greedy request (T <= 0 or NaN).
-__device__ __forceinline__ float temp_scale(float T) { return (T > 0.0f) ? (kLog2e / T) : 0.0f; }
+// 0 marks a greedy request (T <= 0 or NaN).  A positive T is used clamped
+// to [1e-30, 1e30], so the scale stays finite and positive for a subnormal
+// T and for T = +inf (at either end the fp32 softmax is already one-hot or
+// uniform).
+constexpr float kTempMin = 1e-30f, kTempMax = 1e30f;
+__device__ __forceinline__ float temp_scale(float T) {
+  return (T > 0.0f) ? (kLog2e / fminf(fmaxf(T, kTempMin), kTempMax)) : 0.0f;
+}
 
 // (m, i) <- better of (m, i) and (m2, i2): larger value, lower index on ties.
 __device__ __forceinline__ void amax_merge(float& m, int& i, float m2, int i2) {

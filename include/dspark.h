@@ -91,7 +91,8 @@ typedef enum dspark_wdtype {
  *   greedy (temp[r] <= 0 or NaN):
  *     y[r, k] = lowest index v with maximal s[r, v]; q_tok = 1;
  *     q_stats = (max_v s, 1)
- *   sampled (temp[r] = T > 0):
+ *   sampled (temp[r] = T > 0; T is used clamped to [1e-30, 1e30], so
+ *   T = +inf samples uniformly over the entries that are not -inf):
  *     x = s / T, m = max x, Z = sum_v exp(x_v - m);
  *     y[r, k] = first v (in index order) whose inclusive cumulative sum of
  *               exp(x - m) exceeds u_draft[r, k] * Z (never a zero-mass entry);
@@ -222,7 +223,7 @@ typedef struct dspark_schedule_args {
  *   greedy (temp[r] <= 0 or NaN):
  *     accept y_j iff y_j is the lowest-index argmax of t_j; p_tok = 1 or 0;
  *     n = first rejected j (else l); out_tok = lowest-index argmax of t_n.
- *   sampled (T = temp[r] > 0):
+ *   sampled (T = temp[r] > 0, clamped as in dspark_draft_block):
  *     p_j = softmax(t_j / T); p_tok[r, j] = p_j(y_j);
  *     accept iff u_accept[r, j] < p_tok[r, j] / q_tok[r, j];
  *     n = first rejected j, else l;

@@ -22,7 +22,9 @@ Readings of points the pages leave open (each also listed in the design notes):
   * position 0 is biased with prev = anchor (anchor-first block);
   * the bias is added to the logits before the temperature: q = softmax((U+B)/T);
   * draft and target use the same per-request temperature; T <= 0 (or NaN)
-    means greedy for both;
+    means greedy for both; a positive T is used clamped to [1e-30, 1e30]
+    (T = +inf samples uniformly over the entries that are not -inf, a
+    subnormal T samples the argmax);
   * inverse-CDF sampling walks the vocabulary in index order and returns the
     first index whose inclusive cumulative mass exceeds u * Z (strict); if
     rounding leaves none, the last index with positive mass;
@@ -117,6 +119,17 @@ def _is_greedy(T: float) -> bool:
     return not (T > 0.0)
 
 
+TEMP_MIN, TEMP_MAX = 1e-30, 1e30
+
+
+def _sample_T(T: float) -> float:
+    """The temperature a sampled request uses: T clamped to [1e-30, 1e30].
+    Inside that range the softmax is the plain definition; beyond it, it is
+    already uniform (T -> +inf) or one-hot (T -> 0) at any working
+    precision, and s / T stays defined for s = -inf and T = +inf."""
+    return min(max(T, TEMP_MIN), TEMP_MAX)
+
+
 def _argmax_with_gap(s: np.ndarray):
     """Lowest-index argmax and whether the runner-up is within the near-tie band."""
     y = int(np.argmax(s))
@@ -178,7 +191,7 @@ def draft_block(U, W1, W2, wdtype, anchor, temp, u_draft, *,
                 if near:
                     flags[(r, k)] = "draft-near-tie"
             else:
-                x = s / T
+                x = s / _sample_T(T)
                 w = np.exp(x - x.max())
                 yk, Z, near = inverse_cdf(w, float(u_draft[r, k]))
                 y[r, k] = yk
@@ -440,7 +453,7 @@ class VerifyResult:
 
 
 def _softmax_T(row: np.ndarray, T: float) -> np.ndarray:
-    x = np.asarray(row, dtype=np.float64) / T
+    x = np.asarray(row, dtype=np.float64) / _sample_T(T)
     e = np.exp(x - x.max())
     return e / math.fsum(e)
 
@@ -521,7 +534,7 @@ def verify(target_rows, row_offsets, U, W1, W2, wdtype, anchor, y, q_tok, temp,
             if greedy:
                 out_tok[r] = int(np.argmax(t))
             else:
-                x = np.asarray(t, dtype=np.float64) / T
+                x = np.asarray(t, dtype=np.float64) / _sample_T(T)
                 out, _, near = inverse_cdf(np.exp(x - x.max()), float(u_final[r]))
                 out_tok[r] = out
                 if near:

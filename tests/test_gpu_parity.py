@@ -85,6 +85,23 @@ def test_target_only_fallback_K0():
     assert (g["l"] == 0).all() and (g["n_accept"] == 0).all()
 
 
+@pytest.mark.parametrize("R,wd", [(10, "bf16"), (70, "bf16"), (10, "f32")], ids=["seg16", "seg64", "seg32"])
+def test_extreme_temperatures(R, wd):
+    """Temperatures at and past the ends of the clamp [1e-30, 1e30]: +inf and
+    1e35 sample uniformly over the entries that are not -inf, a subnormal and
+    1e-30 sample the argmax, NaN and a negative value are greedy; some
+    entries are masked (-inf) in U and in the target."""
+    inp = synth.make_custom(60 + R, R, 3, 3000, 64, wdtype=wd, policy="temps", K_mode="fixed", U_std=3.0,
+                            noise_std=1.0)
+    extremes = np.array([np.inf, 1e35, 1e30, 1e-40, 1e-30, 1e-3, np.nan, -1.0, 50.0, 1.0], np.float32)
+    inp.temp[:] = extremes[np.arange(R) % len(extremes)]
+    rng = np.random.default_rng(90 + R)
+    mask = rng.random(inp.V) < 0.3
+    inp.U[:, :, mask] = -np.inf
+    inp.target[:, :, mask | (rng.random(inp.V) < 0.1)] = -np.inf
+    _run(inp, label=f"extreme-T-{wd}-R{R}")
+
+
 def test_high_acceptance_and_greedy_identity():
     """Target = drafter base logits with small noise and no Markov bias: most
     drafts are accepted; greedy requests emit the target argmax chain."""

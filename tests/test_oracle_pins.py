@@ -802,3 +802,27 @@ def test_sts_apply_is_the_sigmoid_of_the_scaled_logit():
     np.testing.assert_allclose(c, expit(z.astype(np.float64) / tau.astype(np.float64)), rtol=1e-7)
     # tau = 1 leaves the head's own probability
     np.testing.assert_allclose(oracle.sts_apply(z, np.ones(3, np.float32)), expit(z.astype(np.float64)), rtol=1e-7)
+
+
+def test_extreme_temperatures():
+    """A positive temperature is used clamped to [1e-30, 1e30] (the reading
+    the oracle header states). Closed forms at both ends, with the bias zero
+    so that s = U: T = +inf, or any T >= 1e30, samples uniformly over the
+    entries that are not -inf (the draw is live entry floor(u n), q_tok =
+    1 / n); a subnormal or tiny T samples the argmax with q_tok = 1."""
+    V, rank = 10, 8
+    rng = np.random.default_rng(7)
+    U = rng.normal(0, 2, (1, 1, V)).astype(np.float32)
+    U[0, 0, [1, 4, 8]] = -np.inf
+    W = np.zeros((V, rank), np.float32)
+    anc = np.array([0], np.int32)
+    live = np.flatnonzero(np.isfinite(U[0, 0]))
+    for T in (np.inf, 1e35, 1e30):
+        for u in (0.0, 0.35, 0.6, 0.999):
+            d = oracle.draft_block(U, W, W, "f32", anc, np.array([T], np.float32), np.array([[u]], np.float32))
+            assert d.y[0, 0] == live[int(np.floor(u * len(live)))]
+            assert d.q_tok[0, 0] == pytest.approx(1.0 / len(live), rel=1e-12)
+    for T in (1e-40, 1e-30, 1e-20):
+        d = oracle.draft_block(U, W, W, "f32", anc, np.array([T], np.float32), np.array([[0.5]], np.float32))
+        assert d.y[0, 0] == int(np.argmax(U[0, 0]))
+        assert d.q_tok[0, 0] == 1.0
