@@ -103,9 +103,13 @@ typedef enum dspark_wdtype {
  *                       [1, DSPARK_MAX_GAMMA], V in [1, DSPARK_MAX_VOCAB],
  *                       rank in [8, DSPARK_MAX_RANK] with rank % 8 == 0.
  *   wdtype              dspark_wdtype of W1 and W2.
- *   U        float [R, gamma, V]  base logits; 16-byte aligned.
+ *   U        float [R, gamma, V]  base logits; 16-byte aligned.  Each entry
+ *                                 is finite or -inf (a masked token), and
+ *                                 every row of U + B has a finite entry;
+ *                                 +inf and NaN logits are outside this
+ *                                 contract (results are then undefined).
  *   W1, W2   wdtype [V, rank]     Markov factors (markov_w1, markov_w2);
- *                                 16-byte aligned.
+ *                                 16-byte aligned; finite.
  *   anchor   int32 [R]            last committed token (prev for k = 0).
  *   temp     float [R]            per-request temperature; <= 0 => greedy.
  *   u_draft  float [R, gamma]     uniforms in [0, 1) (read by sampled rows).
@@ -239,7 +243,9 @@ typedef struct dspark_schedule_args {
  *   R, gamma, V, rank, wdtype  as for dspark_draft_block.
  *   n_rows     host int64: total rows = row_offsets[R]; R <= n_rows <=
  *              R * (gamma + 1).
- *   target     float [n_rows, V]  target logits; 16-byte aligned.
+ *   target     float [n_rows, V]  target logits; 16-byte aligned; finite or
+ *                                 -inf, with a finite entry in every row
+ *                                 (as for U).
  *   row_offsets int32 [R + 1]     (from dspark_schedule, or r*(gamma+1) for
  *                                  fixed-length verify).
  *   U, W1, W2, anchor, temp       the inputs given to dspark_draft_block.
