@@ -110,7 +110,9 @@ typedef enum dspark_wdtype {
  *                                 contract (results are then undefined).
  *   W1, W2   wdtype [V, rank]     Markov factors (markov_w1, markov_w2);
  *                                 16-byte aligned; finite.
- *   anchor   int32 [R]            last committed token (prev for k = 0).
+ *   anchor   int32 [R]            last committed token (prev for k = 0), in
+ *                                 [0, V); the kernels clamp a token index
+ *                                 into that range before any use.
  *   temp     float [R]            per-request temperature; <= 0 => greedy.
  *   u_draft  float [R, gamma]     uniforms in [0, 1) (read by sampled rows).
  *   y        int32 [R, gamma]     out: drafted tokens.
