@@ -216,7 +216,9 @@ def test_pack_w2_layout(V, rank):
 
 @pytest.mark.parametrize("case", [(11, 3, 4, 1000, 64, "sampled"), (13, 40, 3, 4099, 40, "temps"),
                                   (18, 9, 16, 513, 128, "temps"), (19, 4, 5, 5, 16, "sampled"),
-                                  (29, 64, 2, 20000, 512, "mixed")], ids=["p11", "p13", "p18", "p19", "p29"])
+                                  (29, 64, 2, 20000, 512, "mixed"), (34, 40, 3, 3000, 200, "mixed"),
+                                  (35, 20, 2, 2000, 384, "sampled")],
+                         ids=["p11", "p13", "p18", "p19", "p29", "p34", "p35"])
 def test_packed_w2_identical(case):
     """The fragment-packed W2 gives bit-identical results to W2 itself (the
     same products in the same order), and those match the oracle."""
