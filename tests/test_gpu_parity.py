@@ -67,6 +67,8 @@ SMALL = [
     (40, 2, 2, 200000, 16, "bf16", "mixed", "fixed"),        # 12500 records: staged in two batches
     (41, 3, 2, 32768, 64, "bf16", "sampled", "fixed"),       # 2048 records: the small stage, full
     (42, 3, 2, 32784, 64, "bf16", "sampled", "fixed"),       # 2049 records: the large stage
+    (43, 70, 16, 1000, 64, "bf16", "temps", "uniformK"),     # maximum gamma on the 64-row path
+    (44, 33, 16, 1000, 96, "f32", "mixed", "uniformK"),      # and on the fp32 path
 ]
 
 
