@@ -826,3 +826,32 @@ def test_extreme_temperatures():
         d = oracle.draft_block(U, W, W, "f32", anc, np.array([T], np.float32), np.array([[0.5]], np.float32))
         assert d.y[0, 0] == int(np.argmax(U[0, 0]))
         assert d.q_tok[0, 0] == 1.0
+
+
+def test_extreme_temperatures_verify():
+    """The same clamp on the target side: at T = +inf the target
+    distribution is uniform over the target row's entries that are not
+    -inf, so a live drafted token has p_tok = 1 / n_target; with the drafter
+    uniform over its own n_draft live entries, p/q = n_draft / n_target and
+    a draft in both live sets is accepted for every u (here n_draft >=
+    n_target); the bonus after a fully accepted block is live entry
+    floor(u n) of the bonus row (closed forms)."""
+    V, rank, gamma = 12, 8, 2
+    rng = np.random.default_rng(11)
+    U = rng.normal(0, 2, (1, gamma, V)).astype(np.float32)
+    U[0, :, [2, 7]] = -np.inf
+    target = rng.normal(0, 2, (gamma + 1, V)).astype(np.float32)
+    target[:, [2, 7, 9]] = -np.inf
+    W = np.zeros((V, rank), np.float32)
+    anc = np.array([0], np.int32)
+    T = np.array([np.inf], np.float32)
+    live_t = np.flatnonzero(np.isfinite(target[0]))
+    n_d, n_t = V - 2, len(live_t)
+    for u_fin in (0.1, 0.55, 0.93):
+        y = np.array([[int(live_t[0]), int(live_t[3])]], np.int32)   # drafts live on both sides
+        q_tok = np.full((1, gamma), 1.0 / n_d, np.float32)
+        v = oracle.verify(target, np.array([0, gamma + 1], np.int32), U, W, W, "f32", anc, y, q_tok, T,
+                          np.array([[0.999, 0.999]], np.float32), np.array([u_fin], np.float32))
+        assert v.p_tok[0].tolist() == pytest.approx([1.0 / n_t] * gamma, rel=1e-12)
+        assert v.n_accept[0] == gamma
+        assert v.out_tok[0] == live_t[int(np.floor(u_fin * n_t))]
