@@ -301,3 +301,18 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=str(tmp_path))
     assert r.returncode == 0, r.stdout + r.stderr
     assert "raised" in r.stdout and "libdspark.so" in r.stdout
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/dspark.h is a C header: it compiles as C99 with -pedantic and
+    as C++17, with no warnings."""
+    import shutil
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    for compiler, lang, std in (("gcc", "c", "c99"), ("g++", "c++", "c++17")):
+        if shutil.which(compiler) is None:
+            pytest.skip(f"{compiler} not installed")
+        src = tmp_path / f"t.{lang}"
+        src.write_text('#include "dspark.h"\nint main(void) { return 0; }\n')
+        r = subprocess.run([compiler, "-x", lang, f"-std={std}", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                            "-fsyntax-only", "-I", inc, str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
