@@ -65,7 +65,7 @@ import numpy as np
 
 __all__ = [
     "NEAR", "widen", "markov_bias", "inverse_cdf", "draft_block", "survival",
-    "schedule", "schedule_cutoff", "capacity", "verify", "step", "DraftResult", "ScheduleResult",
+    "schedule", "schedule_cutoff", "capacity", "verify", "DraftResult", "ScheduleResult",
     "VerifyResult", "CapacityResult", "sts_fit", "sts_apply", "CalibrationResult",
     "STS_BETA_MIN", "STS_BETA_MAX",
 ]
@@ -540,17 +540,3 @@ def verify(target_rows, row_offsets, U, W1, W2, wdtype, anchor, y, q_tok, temp,
                 if near:
                     flags[("final", r, l)] = "bonus-cdf-boundary"
     return VerifyResult(n_accept=n_accept, out_tok=out_tok, p_tok=p_tok, flags=flags)
-
-
-def step(inp, *, K: Optional[int] = None, requests: Optional[Sequence[int]] = None):
-    """One whole oracle step on a ``synth.StepInputs``-like object:
-    draft -> schedule -> gather the scheduled target rows -> verify.
-    Returns (DraftResult, ScheduleResult, target_rows, VerifyResult)."""
-    d = draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
-                    requests=requests)
-    y = d.y
-    sch = schedule(inp.c, inp.K if K is None else K, inp.anchor, np.where(y < 0, 0, y))
-    rows = np.asarray(inp.target)[sch.row_req.astype(np.int64), sch.row_pos.astype(np.int64)]
-    v = verify(rows, sch.row_offsets, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, y,
-               d.q_tok, inp.temp, inp.u_accept, inp.u_final, requests=requests)
-    return d, sch, rows, v

@@ -7,7 +7,11 @@ Comparison rules (decisions are compared, values within tolerance):
     argmax, CDF edge, u within 1e-6 of p/q); such flips are counted;
   * the oracle is teacher-forced with the GPU's drafted prefix, so a flagged
     flip does not cascade into later positions;
-  * probabilities (q_tok, p_tok, Z) and survival within 1e-5 relative.
+  * probabilities (q_tok, p_tok, Z) and survival within 1e-5 relative;
+  * every accept decision is also re-taken by the oracle with its own
+    teacher-forced q_tok (not the GPU's): a decision that then differs from
+    the GPU's is allowed only where u lies within 1e-5 * p/q of p/q (the
+    two q_tok may differ by the 1e-5 tolerance), and is counted.
 """
 from __future__ import annotations
 
@@ -81,6 +85,8 @@ class Tally:
     decisions: int = 0
     flagged: int = 0
     flagged_flips: int = 0
+    own_q_decisions: int = 0     # accept decisions re-taken with the oracle's own q_tok
+    own_q_flips: int = 0         # of those, differing from the GPU inside the 1e-5 band
     failures: list = field(default_factory=list)
 
     def check(self):
@@ -88,7 +94,8 @@ class Tally:
 
     def summary(self):
         return (f"decisions={self.decisions} flagged={self.flagged} "
-                f"flagged_flips={self.flagged_flips} unflagged_mismatches={len(self.failures)}")
+                f"flagged_flips={self.flagged_flips} own_q_decisions={self.own_q_decisions} "
+                f"own_q_flips={self.own_q_flips} unflagged_mismatches={len(self.failures)}")
 
 
 def compare_draft(inp, g, reqs, tally: Tally):
@@ -133,11 +140,40 @@ def compare_schedule(inp, g, K, conf_min=None):
     return s
 
 
-def compare_verify(inp, g, reqs, tally: Tally):
-    """Oracle verify on the GPU's drafted tokens and q_tok, the GPU's rows."""
+#: band around p/q (relative) inside which the accept decision re-taken with
+#: the oracle's own q_tok may differ from the GPU's: each side's q_tok is
+#: within 1e-5 of the other's
+OWN_Q_BAND = 1e-5
+
+
+def compare_verify(inp, g, reqs, tally: Tally, d=None):
+    """Oracle verify on the GPU's drafted tokens and q_tok, the GPU's rows.
+
+    With ``d`` (the DraftResult of compare_draft, teacher-forced on the GPU's
+    tokens), the oracle also verifies with its own q_tok: only the accept
+    decisions depend on q_tok (the residual rebuilds q from U and the
+    weights), so the accepted counts must agree, except where the first
+    differing decision has u within OWN_Q_BAND * p/q of p/q."""
     v = oracle.verify(g["rows"], g["row_offsets"], inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"],
                       g["q_tok"], inp.temp, inp.u_accept, inp.u_final, requests=reqs)
     off = g["row_offsets"]
+    if d is not None:
+        v2 = oracle.verify(g["rows"], off, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"], d.q_tok,
+                           inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+        for r in reqs:
+            l = int(off[r + 1] - off[r] - 1)
+            tally.own_q_decisions += l
+            ng, n2 = int(g["n_accept"][r]), int(v2.n_accept[r])
+            if ng == n2:
+                continue
+            j = min(ng, n2)
+            ratio = float(v2.p_tok[r, j]) / float(d.q_tok[r, j])
+            u = float(inp.u_accept[r, j])
+            if inp.temp[r] > 0 and abs(u - ratio) <= OWN_Q_BAND * ratio:
+                tally.own_q_flips += 1
+            else:
+                tally.failures.append(f"verify with the oracle's q_tok r={r}: gpu n_accept {ng} oracle {n2} "
+                                      f"(u={u}, p/q={ratio}, T={inp.temp[r]})")
     for r in reqs:
         l = int(off[r + 1] - off[r] - 1)
         tally.decisions += l + 1

@@ -1,8 +1,11 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Small cases are compared in full; the full-size configurations are compared
-exactly on the schedule and on a seeded sample of requests for draft and
-verify (every request's draft and verify are independent of the others).
+Small cases are compared in full.  The full-size configurations are compared
+exactly on the schedule; draft and verify are compared on every request at
+R <= 64 and, above that, on 64 requests spread evenly over the batch (one per
+stratum of R / 64 consecutive requests, so every 16-request chunk window and
+every 256-request window of the large-batch kernels is visited).  Every
+request's draft and verify are independent of the others.
 """
 import numpy as np
 import pytest
@@ -20,9 +23,9 @@ def _run(inp, K=None, reqs=None, label=""):
     g = gpu_step(d, K, inp.gamma)
     reqs = list(range(inp.R)) if reqs is None else list(reqs)
     t = Tally()
-    compare_draft(inp, g, reqs, t)
+    dr = compare_draft(inp, g, reqs, t)
     compare_schedule(inp, g, K)
-    compare_verify(inp, g, reqs, t)
+    compare_verify(inp, g, reqs, t, dr)
     print(f"[{label or inp.name}] K={K} {t.summary()}", flush=True)
     t.check()
     return g
@@ -182,13 +185,13 @@ def test_cutoff_step(cfg, conf_min):
     draft, cutoff schedule, verify on the variable-length rows (sampled
     requests compared against the oracle)."""
     inp = synth.make_config(cfg)
-    reqs = _sample(inp.R, 4, cfg)
+    reqs = _spread(inp.R, 64, cfg)
     d = upload(inp)
     g = gpu_step(d, None, inp.gamma, conf_min=conf_min)
     t = Tally()
-    compare_draft(inp, g, reqs, t)
+    dr = compare_draft(inp, g, reqs, t)
     compare_schedule(inp, g, None, conf_min=conf_min)
-    compare_verify(inp, g, reqs, t)
+    compare_verify(inp, g, reqs, t, dr)
     print(f"[cutoff config{cfg} conf_min={conf_min}] rows={int(g['row_offsets'][-1])} {t.summary()}", flush=True)
     t.check()
 
@@ -233,8 +236,8 @@ def test_packed_w2_identical(case):
     for k in g0:
         np.testing.assert_array_equal(g1[k], g0[k], err_msg=k)
     t = Tally()
-    compare_draft(inp, g1, range(R), t)
-    compare_verify(inp, g1, range(R), t)
+    dr = compare_draft(inp, g1, range(R), t)
+    compare_verify(inp, g1, range(R), t, dr)
     print(f"[packed {inp.name}] {t.summary()}", flush=True)
     t.check()
 
@@ -250,17 +253,23 @@ def test_packed_w2_config3():
     print("[packed config3] identical", flush=True)
 
 
-def _sample(R, n, seed):
+def _spread(R, n, seed):
+    """Every request when R <= n; otherwise one seeded request from each of
+    n equal strata of consecutive requests (so the whole batch is visited)."""
+    if R <= n:
+        return list(range(R))
     rng = np.random.default_rng(seed)
-    return sorted(rng.choice(R, size=min(n, R), replace=False).tolist())
+    edges = [(i * R) // n for i in range(n + 1)]
+    return [int(rng.integers(edges[i], edges[i + 1])) for i in range(n)]
 
 
 @pytest.mark.parametrize("cfg,policy", [(2, "greedy"), (2, "sampled"), (3, None), (4, None), (5, None)])
 def test_full_size_configs(cfg, policy):
     inp = synth.make_config(cfg, policy)
-    reqs = _sample(inp.R, 4, cfg)
-    if cfg == 5:  # include both greedy and sampled requests
-        reqs = sorted(set(reqs) | {int(np.flatnonzero(inp.temp <= 0)[0]), int(np.flatnonzero(inp.temp > 0)[0])})
+    reqs = _spread(inp.R, 64, cfg)
+    if cfg == 5:
+        assert (inp.temp[reqs] <= 0).any() and (inp.temp[reqs] > 0).any()
+        assert len({r // 256 for r in reqs}) == 4
     _run(inp, reqs=reqs, label=f"config{cfg}-{policy or 'default'}")
 
 
@@ -455,9 +464,9 @@ def test_lagged_pipeline_over_steps():
         g = gpu_step(d, K, gamma)
         tally = Tally()
         reqs = list(range(R))
-        compare_draft(inp, g, reqs, tally)
+        dr = compare_draft(inp, g, reqs, tally)
         compare_schedule(inp, g, K)
-        compare_verify(inp, g, reqs, tally)
+        compare_verify(inp, g, reqs, tally, dr)
         tally.check()
         survival[t] = g["a"]
         print(f"[loop step {t}] K={K} rows={int(g['row_offsets'][-1])} accepted={int(g['n_accept'].sum())} "
