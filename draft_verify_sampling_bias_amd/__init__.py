@@ -2,14 +2,18 @@
 on MI355X / gfx950).
 
 Argument marshalling only: tensors are checked for device, dtype and layout,
-outputs and workspaces are allocated with torch on the inputs' device, and
+outputs and workspaces are allocated with torch on the inputs' device (from
+the pool of the stream the call is launched on, so a buffer freed after the
+call is not handed to other work while the call's kernels still use it), and
 the C entry points of ``libdspark.so`` (declared in include/dspark.h) are
-called on the current torch stream.  Every step of the computation runs in the
-library's HIP kernels; there is no other implementation to fall back to, and
-the first call fails loudly (ImportError) if the library has not been built.
+called on that stream (the current torch stream unless ``stream`` is given).
+Every step of the computation runs in the library's HIP kernels; there is no
+other implementation to fall back to, and the first call fails loudly
+(ImportError) if the library has not been built.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Sequence
@@ -21,22 +25,31 @@ __all__ = [
     "dspark_verify_workspace_size", "dspark_status_string", "dspark_abi_version",
     "DraftArgs", "ScheduleArgs", "CutoffArgs", "VerifyArgs", "EXPORTED_SYMBOLS",
     "dspark_capacity", "CapacityArgs", "dspark_sts_fit", "dspark_sts_apply", "StsFitArgs", "StsApplyArgs",
+    "dspark_check", "InputCheckError", "CHECK_INPUTS", "BAD_TOKEN", "BAD_UNIFORM", "BAD_LENGTH",
+    "BAD_CONFIDENCE", "WORKSPACE_HEADER", "dspark_schedule_workspace_size", "dspark_cutoff_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
 
 W_F32, W_BF16 = 0, 1
 
+# flags and input-check bits (include/dspark.h)
+CHECK_INPUTS = 1
+BAD_TOKEN, BAD_UNIFORM, BAD_LENGTH, BAD_CONFIDENCE = 1, 2, 4, 8
+WORKSPACE_HEADER = 256
+
 EXPORTED_SYMBOLS = (
     "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
     "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_schedule_rows",
     "dspark_status_string", "dspark_abi_version", "dspark_pack_w2", "dspark_w2_packed_bytes",
-    "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply",
+    "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply", "dspark_schedule_workspace_size",
+    "dspark_cutoff_workspace_size", "dspark_check",
 )
 
 
 class Status:
-    OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_ABI, ERR_HIP = range(9)
+    (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_ABI, ERR_HIP,
+     ERR_INPUT) = range(10)
 
 
 class DsparkError(RuntimeError):
@@ -45,38 +58,56 @@ class DsparkError(RuntimeError):
         super().__init__(f"{fn} failed: status {status} ({dspark_status_string(status)})")
 
 
+class InputCheckError(DsparkError):
+    """The device input checks (check_inputs=True) found values outside the
+    contract; ``bits`` holds the BAD_* bits.  The call's outputs were still
+    written (with clamped inputs), but are unspecified."""
+
+    def __init__(self, fn: str, bits: int):
+        self.bits = bits
+        names = [n for n, b in (("BAD_TOKEN", BAD_TOKEN), ("BAD_UNIFORM", BAD_UNIFORM), ("BAD_LENGTH", BAD_LENGTH),
+                                ("BAD_CONFIDENCE", BAD_CONFIDENCE)) if bits & b]
+        super().__init__(fn, Status.ERR_INPUT)
+        self.args = (f"{fn}: device input check failed: {' | '.join(names) or hex(bits)}",)
+
+
 _p = ctypes.c_void_p
 
 
 class DraftArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
                 ("V", ctypes.c_int32), ("rank", ctypes.c_int32), ("wdtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32),
                 ("U", _p), ("W1", _p), ("W2", _p), ("anchor", _p), ("temp", _p), ("u_draft", _p),
                 ("y", _p), ("q_tok", _p), ("q_stats", _p), ("workspace", _p),
-                ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("prof_events", _p), ("W2_packed", _p)]
+                ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("prof_events", _p), ("W2_packed", _p),
+                ("W2_packed_bytes", ctypes.c_size_t)]
 
 
 class ScheduleArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
-                ("K", ctypes.c_int64), ("c", _p), ("anchor", _p), ("y", _p), ("a", _p), ("l", _p),
-                ("row_offsets", _p), ("row_req", _p), ("row_pos", _p), ("row_tok", _p),
-                ("expected_tokens", _p), ("stream", _p)]
+                ("K", ctypes.c_int64), ("flags", ctypes.c_uint32), ("c", _p), ("anchor", _p), ("y", _p),
+                ("a", _p), ("l", _p), ("row_offsets", _p), ("row_req", _p), ("row_pos", _p), ("row_tok", _p),
+                ("expected_tokens", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t),
+                ("stream", _p)]
 
 
 class CutoffArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
-                ("conf_min", ctypes.c_float), ("c", _p), ("anchor", _p), ("y", _p), ("a", _p), ("l", _p),
-                ("row_offsets", _p), ("row_req", _p), ("row_pos", _p), ("row_tok", _p),
-                ("expected_tokens", _p), ("stream", _p)]
+                ("conf_min", ctypes.c_float), ("flags", ctypes.c_uint32), ("c", _p), ("anchor", _p),
+                ("y", _p), ("a", _p), ("l", _p), ("row_offsets", _p), ("row_req", _p), ("row_pos", _p),
+                ("row_tok", _p), ("expected_tokens", _p), ("workspace", _p),
+                ("workspace_bytes", ctypes.c_size_t), ("stream", _p)]
 
 
 class VerifyArgs(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("R", ctypes.c_int32), ("gamma", ctypes.c_int32),
                 ("V", ctypes.c_int32), ("rank", ctypes.c_int32), ("wdtype", ctypes.c_int32),
-                ("n_rows", ctypes.c_int64), ("target", _p), ("row_offsets", _p), ("U", _p), ("W1", _p),
-                ("W2", _p), ("anchor", _p), ("temp", _p), ("y", _p), ("q_tok", _p), ("q_stats", _p),
-                ("u_accept", _p), ("u_final", _p), ("n_accept", _p), ("out_tok", _p), ("p_tok", _p),
-                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("W2_packed", _p)]
+                ("flags", ctypes.c_uint32), ("n_rows", ctypes.c_int64), ("target", _p), ("row_offsets", _p),
+                ("U", _p), ("W1", _p), ("W2", _p), ("anchor", _p), ("temp", _p), ("y", _p), ("q_tok", _p),
+                ("q_stats", _p), ("u_accept", _p), ("u_final", _p), ("n_accept", _p), ("out_tok", _p),
+                ("p_tok", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("stream", _p),
+                ("W2_packed", _p), ("W2_packed_bytes", ctypes.c_size_t)]
 
 
 class CapacityArgs(ctypes.Structure):
@@ -108,6 +139,9 @@ def _load():
     P = ctypes.POINTER
     L.dspark_draft_workspace_size.argtypes = [P(DraftArgs), P(ctypes.c_size_t)]
     L.dspark_verify_workspace_size.argtypes = [P(VerifyArgs), P(ctypes.c_size_t)]
+    L.dspark_schedule_workspace_size.argtypes = [P(ScheduleArgs), P(ctypes.c_size_t)]
+    L.dspark_cutoff_workspace_size.argtypes = [P(CutoffArgs), P(ctypes.c_size_t)]
+    L.dspark_check.argtypes = [_p, _p, P(ctypes.c_uint32)]
     L.dspark_draft_block.argtypes = [P(DraftArgs)]
     L.dspark_schedule.argtypes = [P(ScheduleArgs)]
     L.dspark_schedule_cutoff.argtypes = [P(CutoffArgs)]
@@ -120,7 +154,8 @@ def _load():
     L.dspark_sts_apply.argtypes = [P(StsApplyArgs)]
     for f in ("dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
               "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_abi_version",
-              "dspark_pack_w2", "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply"):
+              "dspark_pack_w2", "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply",
+              "dspark_schedule_workspace_size", "dspark_cutoff_workspace_size", "dspark_check"):
         getattr(L, f).restype = ctypes.c_int
     L.dspark_schedule_rows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     L.dspark_schedule_rows.restype = ctypes.c_int64
@@ -203,25 +238,80 @@ def _stream(device, stream):
     return s.cuda_stream
 
 
+def _alloc_on(stream):
+    """Allocation context for a call's outputs and workspace: the pool of the
+    stream the call runs on (a given side stream), so that freeing a buffer
+    after the call waits for that stream's work in torch's caching
+    allocator."""
+    torch = _torch()
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _workspace(nbytes: int, device, workspace):
     torch = _torch()
     if workspace is not None:
-        if workspace.device != device or workspace.numel() * workspace.element_size() < nbytes:
-            raise ValueError(f"workspace must hold {nbytes} bytes on {device}")
+        if (workspace.device != device or workspace.numel() * workspace.element_size() < nbytes
+                or not workspace.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous buffer of {nbytes} bytes on {device}")
         return workspace
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def draft_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int) -> int:
-    a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wdtype)
+def _w2_packed(W2_packed, device, V: int, rank: int):
+    """(pointer, bytes) of an optional fragment-packed W2: a contiguous uint8
+    tensor on the inputs' device holding at least dspark_w2_packed_bytes."""
+    torch = _torch()
+    if W2_packed is None:
+        return None, 0
+    need = dspark_w2_packed_bytes(V, rank)
+    if not isinstance(W2_packed, torch.Tensor) or W2_packed.dtype != torch.uint8:
+        raise TypeError("W2_packed must be the uint8 tensor made by dspark_pack_w2")
+    if W2_packed.device != device or not W2_packed.is_contiguous():
+        raise ValueError(f"W2_packed must be contiguous on {device}")
+    if W2_packed.numel() < need:
+        raise ValueError(f"W2_packed holds {W2_packed.numel()} bytes, V={V} rank={rank} needs {need}")
+    return W2_packed.data_ptr(), W2_packed.numel()
+
+
+def dspark_check(workspace, stream=None) -> int:
+    """Error word of the device input checks of the last call on this
+    workspace (include/dspark.h, dspark_check): waits for the stream and
+    returns the BAD_* bits (0 when every checked input is inside the
+    contract)."""
+    bits = ctypes.c_uint32(0)
+    st = get_lib().dspark_check(ctypes.c_void_p(workspace.data_ptr()), _stream(workspace.device, stream),
+                                ctypes.byref(bits))
+    if st not in (Status.OK, Status.ERR_INPUT):
+        raise DsparkError("dspark_check", st)
+    return int(bits.value)
+
+
+def _raise_on_check(fn: str, ws, stream):
+    bits = dspark_check(ws, stream)
+    if bits:
+        raise InputCheckError(fn, bits)
+
+
+def _sched_workspace(fn: str, args, device, workspace):
+    n = ctypes.c_size_t(0)
+    _check(fn, getattr(get_lib(), fn)(ctypes.byref(args), ctypes.byref(n)))
+    if n.value == 0:
+        return None
+    return _workspace(int(n.value), device, workspace)
+
+
+def draft_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, flags: int = 0) -> int:
+    a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wdtype,
+                  flags=flags)
     n = ctypes.c_size_t(0)
     _check("dspark_draft_workspace_size", get_lib().dspark_draft_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
 
 
-def verify_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, n_rows: int) -> int:
+def verify_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, n_rows: int,
+                           flags: int = 0) -> int:
     a = VerifyArgs(struct_size=ctypes.sizeof(VerifyArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wdtype,
-                   n_rows=n_rows)
+                   n_rows=n_rows, flags=flags)
     n = ctypes.c_size_t(0)
     _check("dspark_verify_workspace_size", get_lib().dspark_verify_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
@@ -229,6 +319,22 @@ def verify_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, n
 
 dspark_draft_workspace_size = draft_workspace_bytes
 dspark_verify_workspace_size = verify_workspace_bytes
+
+
+def dspark_schedule_workspace_size(R: int, gamma: int, flags: int = 0) -> int:
+    a = ScheduleArgs(struct_size=ctypes.sizeof(ScheduleArgs), R=R, gamma=gamma, flags=flags)
+    n = ctypes.c_size_t(0)
+    _check("dspark_schedule_workspace_size", get_lib().dspark_schedule_workspace_size(ctypes.byref(a),
+                                                                                      ctypes.byref(n)))
+    return int(n.value)
+
+
+def dspark_cutoff_workspace_size(R: int, gamma: int, flags: int = 0) -> int:
+    a = CutoffArgs(struct_size=ctypes.sizeof(CutoffArgs), R=R, gamma=gamma, flags=flags)
+    n = ctypes.c_size_t(0)
+    _check("dspark_cutoff_workspace_size", get_lib().dspark_cutoff_workspace_size(ctypes.byref(a),
+                                                                                  ctypes.byref(n)))
+    return int(n.value)
 
 
 def dspark_w2_packed_bytes(V: int, rank: int) -> int:
@@ -247,7 +353,8 @@ def dspark_pack_w2(W2, *, out=None, stream=None):
     if nbytes == 0:
         raise ValueError("invalid V / rank")
     if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        with _alloc_on(stream):
+            out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     a = PackArgs(struct_size=ctypes.sizeof(PackArgs), V=V, rank=rank, W2=_ptr(W2), W2_packed=_ptr(out),
                  W2_packed_bytes=out.numel() * out.element_size(), stream=_stream(dev, stream))
     _check("dspark_pack_w2", get_lib().dspark_pack_w2(ctypes.byref(a)))
@@ -255,7 +362,7 @@ def dspark_pack_w2(W2, *, out=None, stream=None):
 
 
 def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=None, stream=None,
-                       prof_events=None, W2_packed=None):
+                       prof_events=None, W2_packed=None, check_inputs: bool = False):
     """Draft gamma tokens per request (include/dspark.h, dspark_draft_block).
 
     U [R, gamma, V] fp32; W1, W2 [V, rank] bf16 or fp32; anchor [R] int32;
@@ -264,7 +371,10 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
     those three tensors; ``prof_events`` a list of 2*gamma timing events
     (torch.cuda.Event already recorded once, or raw hipEvent_t handles)
     attached to each position's fused bias kernel dispatch (start / stop of
-    that kernel alone); ``W2_packed`` the output of dspark_pack_w2 for W2."""
+    that kernel alone); ``W2_packed`` the output of dspark_pack_w2 for W2.
+    ``check_inputs`` runs the device input checks (DSPARK_CHECK_INPUTS) and
+    then waits for them: InputCheckError if an input is outside the
+    contract (debug only: it synchronises)."""
     torch = _torch()
     dev = U.device
     R, gamma, V = U.shape
@@ -276,17 +386,20 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
     _want(anchor, "anchor", torch.int32, (R,), dev)
     _want(temp, "temp", torch.float32, (R,), dev)
     _want(u_draft, "u_draft", torch.float32, (R, gamma), dev)
-    if out is None:
-        y = torch.empty((R, gamma), dtype=torch.int32, device=dev)
-        q_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
-        q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
-    else:
-        y, q_tok, q_stats = out
-        _want(y, "y", torch.int32, (R, gamma), dev)
-        _want(q_tok, "q_tok", torch.float32, (R, gamma), dev)
-        _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
-    nbytes = draft_workspace_bytes(R, gamma, V, rank, wd)
-    ws = _workspace(nbytes, dev, workspace)
+    w2p, w2p_bytes = _w2_packed(W2_packed, dev, V, rank)
+    flags = CHECK_INPUTS if check_inputs else 0
+    with _alloc_on(stream):
+        if out is None:
+            y = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+            q_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+            q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
+        else:
+            y, q_tok, q_stats = out
+            _want(y, "y", torch.int32, (R, gamma), dev)
+            _want(q_tok, "q_tok", torch.float32, (R, gamma), dev)
+            _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
+        nbytes = draft_workspace_bytes(R, gamma, V, rank, wd, flags)
+        ws = _workspace(nbytes, dev, workspace)
     ev_arr = None
     if prof_events is not None:
         if len(prof_events) != 2 * gamma:
@@ -294,18 +407,21 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
         # torch.cuda.Event objects or raw hipEvent_t handles (int)
         ev_arr = (ctypes.c_void_p * len(prof_events))(
             *[e if isinstance(e, int) else e.cuda_event for e in prof_events])
-    a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd,
+    a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd, flags=flags,
                   U=_ptr(U), W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp),
                   u_draft=_ptr(u_draft), y=_ptr(y), q_tok=_ptr(q_tok), q_stats=_ptr(q_stats),
                   workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(),
                   stream=_stream(dev, stream),
                   prof_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
-                  W2_packed=_ptr(W2_packed))
+                  W2_packed=w2p, W2_packed_bytes=w2p_bytes)
     _check("dspark_draft_block", get_lib().dspark_draft_block(ctypes.byref(a)))
+    if check_inputs and R > 0:
+        _raise_on_check("dspark_draft_block", ws, stream)
     return y, q_tok, q_stats
 
 
-def dspark_schedule(c, K: int, anchor, y, *, out=None, want_expected: bool = True, stream=None):
+def dspark_schedule(c, K: int, anchor, y, *, out=None, want_expected: bool = True, stream=None,
+                    check_inputs: bool = False, workspace=None):
     """Survival + causal prefix-closed top-K schedule (include/dspark.h,
     dspark_schedule).  c [R, gamma] fp32; anchor [R] int32; y [R, gamma] int32.
     Returns a dict with a, l, row_offsets, row_req, row_pos, row_tok and
@@ -319,30 +435,39 @@ def dspark_schedule(c, K: int, anchor, y, *, out=None, want_expected: bool = Tru
     n_rows = dspark_schedule_rows(R, gamma, K)
     if n_rows < 0:
         raise ValueError("invalid R / gamma")
-    if out is None:
-        out = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
-                   l=torch.empty(R, dtype=torch.int32, device=dev),
-                   row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
-                   row_req=torch.empty(n_rows, dtype=torch.int32, device=dev),
-                   row_pos=torch.empty(n_rows, dtype=torch.int32, device=dev),
-                   row_tok=torch.empty(n_rows, dtype=torch.int32, device=dev),
-                   expected_tokens=torch.empty(1, dtype=torch.float32, device=dev) if want_expected else None)
-    else:
+    flags = CHECK_INPUTS if check_inputs else 0
+    given = out is not None
+    a = ScheduleArgs(struct_size=ctypes.sizeof(ScheduleArgs), R=R, gamma=gamma, K=int(K), flags=flags)
+    with _alloc_on(stream):
+        ws = _sched_workspace("dspark_schedule_workspace_size", a, dev, workspace)
+        if out is None:
+            out = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                       l=torch.empty(R, dtype=torch.int32, device=dev),
+                       row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
+                       row_req=torch.empty(n_rows, dtype=torch.int32, device=dev),
+                       row_pos=torch.empty(n_rows, dtype=torch.int32, device=dev),
+                       row_tok=torch.empty(n_rows, dtype=torch.int32, device=dev),
+                       expected_tokens=torch.empty(1, dtype=torch.float32, device=dev) if want_expected else None)
+    if given:
         _want(out["a"], "a", torch.float32, (R, gamma), dev)
         _want(out["l"], "l", torch.int32, (R,), dev)
         _want(out["row_offsets"], "row_offsets", torch.int32, (R + 1,), dev)
         for f in ("row_req", "row_pos", "row_tok"):
             _want(out[f], f, torch.int32, (n_rows,), dev)
-    a = ScheduleArgs(struct_size=ctypes.sizeof(ScheduleArgs), R=R, gamma=gamma, K=int(K), c=_ptr(c),
+    a = ScheduleArgs(struct_size=ctypes.sizeof(ScheduleArgs), R=R, gamma=gamma, K=int(K), flags=flags, c=_ptr(c),
                      anchor=_ptr(anchor), y=_ptr(y), a=_ptr(out["a"]), l=_ptr(out["l"]),
                      row_offsets=_ptr(out["row_offsets"]), row_req=_ptr(out["row_req"]),
                      row_pos=_ptr(out["row_pos"]), row_tok=_ptr(out["row_tok"]),
-                     expected_tokens=_ptr(out.get("expected_tokens")), stream=_stream(dev, stream))
+                     expected_tokens=_ptr(out.get("expected_tokens")), workspace=_ptr(ws),
+                     workspace_bytes=0 if ws is None else ws.numel(), stream=_stream(dev, stream))
     _check("dspark_schedule", get_lib().dspark_schedule(ctypes.byref(a)))
+    if check_inputs and R > 0:
+        _raise_on_check("dspark_schedule", ws, stream)
     return out
 
 
-def dspark_schedule_cutoff(c, conf_min: float, anchor, y, *, out=None, want_expected: bool = True, stream=None):
+def dspark_schedule_cutoff(c, conf_min: float, anchor, y, *, out=None, want_expected: bool = True, stream=None,
+                           check_inputs: bool = False, workspace=None):
     """Survival + static confidence-cutoff schedule (include/dspark.h,
     dspark_schedule_cutoff).  c [R, gamma] fp32; anchor [R] int32; y [R, gamma]
     int32.  Returns a dict like dspark_schedule's; the row arrays have room
@@ -354,26 +479,34 @@ def dspark_schedule_cutoff(c, conf_min: float, anchor, y, *, out=None, want_expe
     _want(anchor, "anchor", torch.int32, (R,), dev)
     _want(y, "y", torch.int32, (R, gamma), dev)
     cap = R * (gamma + 1)
-    if out is None:
-        out = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
-                   l=torch.empty(R, dtype=torch.int32, device=dev),
-                   row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
-                   row_req=torch.empty(cap, dtype=torch.int32, device=dev),
-                   row_pos=torch.empty(cap, dtype=torch.int32, device=dev),
-                   row_tok=torch.empty(cap, dtype=torch.int32, device=dev),
-                   expected_tokens=torch.empty(1, dtype=torch.float32, device=dev) if want_expected else None)
-    else:
+    flags = CHECK_INPUTS if check_inputs else 0
+    given = out is not None
+    a = CutoffArgs(struct_size=ctypes.sizeof(CutoffArgs), R=R, gamma=gamma, conf_min=float(conf_min), flags=flags)
+    with _alloc_on(stream):
+        ws = _sched_workspace("dspark_cutoff_workspace_size", a, dev, workspace)
+        if out is None:
+            out = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+                       l=torch.empty(R, dtype=torch.int32, device=dev),
+                       row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
+                       row_req=torch.empty(cap, dtype=torch.int32, device=dev),
+                       row_pos=torch.empty(cap, dtype=torch.int32, device=dev),
+                       row_tok=torch.empty(cap, dtype=torch.int32, device=dev),
+                       expected_tokens=torch.empty(1, dtype=torch.float32, device=dev) if want_expected else None)
+    if given:
         _want(out["a"], "a", torch.float32, (R, gamma), dev)
         _want(out["l"], "l", torch.int32, (R,), dev)
         _want(out["row_offsets"], "row_offsets", torch.int32, (R + 1,), dev)
         for f in ("row_req", "row_pos", "row_tok"):
             _want(out[f], f, torch.int32, (cap,), dev)
-    a = CutoffArgs(struct_size=ctypes.sizeof(CutoffArgs), R=R, gamma=gamma, conf_min=float(conf_min), c=_ptr(c),
-                   anchor=_ptr(anchor), y=_ptr(y), a=_ptr(out["a"]), l=_ptr(out["l"]),
+    a = CutoffArgs(struct_size=ctypes.sizeof(CutoffArgs), R=R, gamma=gamma, conf_min=float(conf_min), flags=flags,
+                   c=_ptr(c), anchor=_ptr(anchor), y=_ptr(y), a=_ptr(out["a"]), l=_ptr(out["l"]),
                    row_offsets=_ptr(out["row_offsets"]), row_req=_ptr(out["row_req"]),
                    row_pos=_ptr(out["row_pos"]), row_tok=_ptr(out["row_tok"]),
-                   expected_tokens=_ptr(out.get("expected_tokens")), stream=_stream(dev, stream))
+                   expected_tokens=_ptr(out.get("expected_tokens")), workspace=_ptr(ws),
+                   workspace_bytes=0 if ws is None else ws.numel(), stream=_stream(dev, stream))
     _check("dspark_schedule_cutoff", get_lib().dspark_schedule_cutoff(ctypes.byref(a)))
+    if check_inputs and R > 0:
+        _raise_on_check("dspark_schedule_cutoff", ws, stream)
     return out
 
 
@@ -390,9 +523,10 @@ def dspark_capacity(a_lag, sps, *, out=None, stream=None):
     (n_sps,) = sps.shape
     _want(sps, "sps", torch.float32, (n_sps,), dev)
     if out is None:
-        out = dict(K=torch.empty(1, dtype=torch.int32, device=dev),
-                   expected=torch.empty(1, dtype=torch.float64, device=dev),
-                   theta=torch.empty(1, dtype=torch.float64, device=dev))
+        with _alloc_on(stream):
+            out = dict(K=torch.empty(1, dtype=torch.int32, device=dev),
+                       expected=torch.empty(1, dtype=torch.float64, device=dev),
+                       theta=torch.empty(1, dtype=torch.float64, device=dev))
     else:
         _want(out["K"], "K", torch.int32, (1,), dev)
         for f in ("expected", "theta"):
@@ -415,7 +549,8 @@ def dspark_sts_fit(z, n_acc, *, out=None, stream=None):
     N, gamma = z.shape
     _want(z, "z", torch.float32, (N, gamma), dev)
     _want(n_acc, "n_acc", torch.int32, (N,), dev)
-    tau = torch.empty(gamma, dtype=torch.float32, device=dev) if out is None else out
+    with _alloc_on(stream):
+        tau = torch.empty(gamma, dtype=torch.float32, device=dev) if out is None else out
     _want(tau, "tau", torch.float32, (gamma,), dev)
     a = StsFitArgs(struct_size=ctypes.sizeof(StsFitArgs), N=N, gamma=gamma, z=_ptr(z) if N else None,
                    n_acc=_ptr(n_acc) if N else None, tau=_ptr(tau), stream=_stream(dev, stream))
@@ -432,7 +567,8 @@ def dspark_sts_apply(z, tau, *, out=None, stream=None):
     R, gamma = z.shape
     _want(z, "z", torch.float32, (R, gamma), dev)
     _want(tau, "tau", torch.float32, (gamma,), dev)
-    c = torch.empty((R, gamma), dtype=torch.float32, device=dev) if out is None else out
+    with _alloc_on(stream):
+        c = torch.empty((R, gamma), dtype=torch.float32, device=dev) if out is None else out
     _want(c, "c", torch.float32, (R, gamma), dev)
     a = StsApplyArgs(struct_size=ctypes.sizeof(StsApplyArgs), R=R, gamma=gamma, z=_ptr(z), tau=_ptr(tau),
                      c=_ptr(c), stream=_stream(dev, stream))
@@ -441,7 +577,7 @@ def dspark_sts_apply(z, tau, *, out=None, stream=None):
 
 
 def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final, *,
-                  out=None, workspace=None, stream=None, W2_packed=None):
+                  out=None, workspace=None, stream=None, W2_packed=None, check_inputs: bool = False):
     """Accept / reject against target logits (include/dspark.h, dspark_verify).
 
     target [n_rows, V] fp32; row_offsets [R+1] int32; the draft inputs and
@@ -465,23 +601,28 @@ def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stat
     _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
     _want(u_accept, "u_accept", torch.float32, (R, gamma), dev)
     _want(u_final, "u_final", torch.float32, (R,), dev)
-    if out is None:
-        n_accept = torch.empty(R, dtype=torch.int32, device=dev)
-        out_tok = torch.empty(R, dtype=torch.int32, device=dev)
-        p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
-    else:
-        n_accept, out_tok, p_tok = out
-        _want(n_accept, "n_accept", torch.int32, (R,), dev)
-        _want(out_tok, "out_tok", torch.int32, (R,), dev)
-        _want(p_tok, "p_tok", torch.float32, (R, gamma), dev)
-    nbytes = verify_workspace_bytes(R, gamma, V, rank, wd, n_rows)
-    ws = _workspace(nbytes, dev, workspace)
-    a = VerifyArgs(struct_size=ctypes.sizeof(VerifyArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd,
+    w2p, w2p_bytes = _w2_packed(W2_packed, dev, V, rank)
+    flags = CHECK_INPUTS if check_inputs else 0
+    with _alloc_on(stream):
+        if out is None:
+            n_accept = torch.empty(R, dtype=torch.int32, device=dev)
+            out_tok = torch.empty(R, dtype=torch.int32, device=dev)
+            p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+        else:
+            n_accept, out_tok, p_tok = out
+            _want(n_accept, "n_accept", torch.int32, (R,), dev)
+            _want(out_tok, "out_tok", torch.int32, (R,), dev)
+            _want(p_tok, "p_tok", torch.float32, (R, gamma), dev)
+        nbytes = verify_workspace_bytes(R, gamma, V, rank, wd, n_rows, flags)
+        ws = _workspace(nbytes, dev, workspace)
+    a = VerifyArgs(struct_size=ctypes.sizeof(VerifyArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd, flags=flags,
                    n_rows=n_rows, target=_ptr(target), row_offsets=_ptr(row_offsets), U=_ptr(U),
                    W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp), y=_ptr(y),
                    q_tok=_ptr(q_tok), q_stats=_ptr(q_stats), u_accept=_ptr(u_accept), u_final=_ptr(u_final),
                    n_accept=_ptr(n_accept), out_tok=_ptr(out_tok), p_tok=_ptr(p_tok), workspace=_ptr(ws),
                    workspace_bytes=ws.numel() * ws.element_size(), stream=_stream(dev, stream),
-                   W2_packed=_ptr(W2_packed))
+                   W2_packed=w2p, W2_packed_bytes=w2p_bytes)
     _check("dspark_verify", get_lib().dspark_verify(ctypes.byref(a)))
+    if check_inputs and R > 0:
+        _raise_on_check("dspark_verify", ws, stream)
     return n_accept, out_tok, p_tok

@@ -19,6 +19,29 @@ inline T* ws_at(void* ws, std::size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
+// The input-check pass of a call made with DSPARK_CHECK_INPUTS: writes the
+// error word at the start of the workspace.
+inline CheckParams check_params(void* ws) {
+  CheckParams c{};
+  c.err = ws_at<uint32_t>(ws, 0);
+  return c;
+}
+
+// Schedule calls: the check of c (confidence) and of the token ids copied
+// into the verify rows.
+template <typename A>
+int schedule_check(const A* a, hipStream_t s) {
+  CheckParams c = check_params(a->workspace);
+  c.ids[0] = a->anchor;
+  c.n_ids[0] = a->R;
+  c.ids[1] = a->y;
+  c.n_ids[1] = static_cast<int64_t>(a->R) * a->gamma;
+  c.V = 0x7fffffff;  // the schedule knows no vocabulary size: ids are checked for >= 0 only
+  c.conf = a->c;
+  c.n_conf = static_cast<int64_t>(a->R) * a->gamma;
+  return hip_status(launch_input_check(c, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -45,6 +68,25 @@ int dspark_verify_workspace_size(const dspark_verify_args* args, size_t* bytes) 
   if (st != DSPARK_OK) return st;
   *bytes = plan.total;
   return DSPARK_OK;
+}
+
+int dspark_schedule_workspace_size(const dspark_schedule_args* args, size_t* bytes) {
+  return plan_schedule(args, bytes);
+}
+
+int dspark_cutoff_workspace_size(const dspark_cutoff_args* args, size_t* bytes) {
+  return plan_cutoff(args, bytes);
+}
+
+int dspark_check(const void* workspace, void* stream, uint32_t* bits) {
+  if (workspace == nullptr) return DSPARK_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  // enqueued behind the calls that wrote the word, then waited for
+  if (hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess) return DSPARK_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return DSPARK_ERR_HIP;
+  if (bits != nullptr) *bits = word;
+  return word == 0 ? DSPARK_OK : DSPARK_ERR_INPUT;
 }
 
 int dspark_draft_block(const dspark_draft_args* a) {
@@ -84,6 +126,18 @@ int dspark_draft_block(const dspark_draft_args* a) {
   fp.q_tok = a->q_tok;
   fp.q_stats = a->q_stats;
 
+  uint32_t* err = ws_at<uint32_t>(a->workspace, 0);
+  if (plan.check) {
+    CheckParams c = check_params(a->workspace);
+    c.ids[0] = a->anchor;
+    c.n_ids[0] = a->R;
+    c.V = a->V;
+    c.unif[0] = a->u_draft;
+    c.n_unif[0] = static_cast<int64_t>(a->R) * a->gamma;
+    st = hip_status(launch_input_check(c, s));
+    if (st != DSPARK_OK) return st;
+  }
+
   const int cu = current_cu_count();
   for (int k = 0; k < a->gamma; ++k) {
     // prev = anchor for the first position, the token drafted just before otherwise
@@ -98,6 +152,8 @@ int dspark_draft_block(const dspark_draft_args* a) {
     fp.prev_stride = tp.prev_stride;
     fp.U_base = tp.U_base;
     fp.k = k;
+    // a call without the checks still rewrites the error word (first finish)
+    fp.err_clear = (k == 0 && !plan.check) ? err : nullptr;
     st = hip_status(launch_draft_finish(fp, a->wdtype, s));
     if (st != DSPARK_OK) return st;
   }
@@ -105,9 +161,14 @@ int dspark_draft_block(const dspark_draft_args* a) {
 }
 
 int dspark_schedule(const dspark_schedule_args* a) {
-  const int st = validate_schedule(a);
+  int st = validate_schedule(a);
   if (st != DSPARK_OK || a->R == 0) return st;
-  return hip_status(launch_schedule(*a, static_cast<hipStream_t>(a->stream)));
+  hipStream_t s = static_cast<hipStream_t>(a->stream);
+  if (a->flags & DSPARK_CHECK_INPUTS) {
+    st = schedule_check(a, s);
+    if (st != DSPARK_OK) return st;
+  }
+  return hip_status(launch_schedule(*a, s));
 }
 
 size_t dspark_w2_packed_bytes(int32_t V, int32_t rank) {
@@ -122,8 +183,12 @@ int dspark_pack_w2(const dspark_pack_w2_args* a) {
 }
 
 int dspark_schedule_cutoff(const dspark_cutoff_args* a) {
-  const int st = validate_cutoff(a);
+  int st = validate_cutoff(a);
   if (st != DSPARK_OK || a->R == 0) return st;
+  if (a->flags & DSPARK_CHECK_INPUTS) {
+    st = schedule_check(a, static_cast<hipStream_t>(a->stream));
+    if (st != DSPARK_OK) return st;
+  }
   dspark_schedule_args s{};
   s.struct_size = sizeof(s);
   s.R = a->R;
@@ -198,6 +263,26 @@ int dspark_verify(const dspark_verify_args* a) {
   if (plan.seg_rows == kSegWide) {
     vp.rs_count = ws_at<int32_t>(a->workspace, plan.rcount_off);
     vp.rs_list = ws_at<ResidualEntry>(a->workspace, plan.rlist_off);
+  }
+  if (plan.check) {
+    CheckParams c = check_params(a->workspace);
+    c.ids[0] = a->anchor;
+    c.n_ids[0] = a->R;
+    c.ids[1] = a->y;
+    c.n_ids[1] = static_cast<int64_t>(a->R) * a->gamma;
+    c.V = a->V;
+    c.unif[0] = a->u_accept;
+    c.n_unif[0] = static_cast<int64_t>(a->R) * a->gamma;
+    c.unif[1] = a->u_final;
+    c.n_unif[1] = a->R;
+    c.offsets = a->row_offsets;
+    c.R = a->R;
+    c.gamma = a->gamma;
+    c.n_rows = a->n_rows;
+    st = hip_status(launch_input_check(c, s));
+    if (st != DSPARK_OK) return st;
+  } else {
+    vp.err_clear = ws_at<uint32_t>(a->workspace, 0);
   }
 
   st = hip_status(launch_verify_stats(vp, s));

@@ -121,6 +121,7 @@ __global__ void __launch_bounds__(NT) draft_finish_kernel(FinishParams p) {
   __shared__ float2 srec[STAGED ? STAGE : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
   const int V = p.V, n_seg = p.n_seg;
+  if (p.err_clear != nullptr && (n | tid) == 0) *p.err_clear = 0u;
   const float2* gfine = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
   const float2* fine = STAGED ? srec : gfine;
   const int64_t o = static_cast<int64_t>(n) * p.gamma + p.k;

@@ -67,6 +67,9 @@ struct FinishParams {
   int32_t* y;
   float* q_tok;
   float* q_stats;
+  // when set, block 0 writes 0 to this error word (a call made without the
+  // input checks still rewrites the word of its workspace)
+  uint32_t* err_clear;
 };
 
 struct VerifyParams {
@@ -95,7 +98,30 @@ struct VerifyParams {
   // appends every request that needs the residual pass
   int32_t* rs_count;
   ResidualEntry* rs_list;  // [R]
+  // when set, verify_stats writes 0 to this error word (as FinishParams)
+  uint32_t* err_clear;
 };
+
+// The device input checks of one call (DSPARK_CHECK_INPUTS): token arrays
+// must hold ids in [0, V), uniform arrays values in [0, 1), the confidence
+// values in [0, 1], and the verify row offsets 1 .. gamma + 1 rows per
+// request inside [0, n_rows].  Unused entries are NULL.  The bits found are
+// written to *err (the first word of the call's workspace).
+constexpr int kCheckMaxArrays = 2;
+struct CheckParams {
+  uint32_t* err;
+  const int32_t* ids[kCheckMaxArrays];
+  int64_t n_ids[kCheckMaxArrays];
+  int V;
+  const float* unif[kCheckMaxArrays];
+  int64_t n_unif[kCheckMaxArrays];
+  const float* conf;
+  int64_t n_conf;
+  const int32_t* offsets;  // [R + 1]
+  int R, gamma;
+  int64_t n_rows;
+};
+hipError_t launch_input_check(const CheckParams& p, hipStream_t s);
 
 // ev0 / ev1 (optional): events attached to the kernel's dispatch, recorded
 // when it starts and when it ends.

@@ -12,6 +12,35 @@ inline bool aligned(const void* p, std::size_t a) {
 
 inline std::size_t round_up(std::size_t x, std::size_t a) { return (x + a - 1) / a * a; }
 
+constexpr uint32_t kKnownFlags = DSPARK_CHECK_INPUTS;
+
+// A workspace given to a call: present, large enough, 256-byte aligned.
+inline int check_workspace(const void* ws, std::size_t have, std::size_t need) {
+  if (need == 0) return DSPARK_OK;
+  if (ws == nullptr || have < need) return DSPARK_ERR_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return DSPARK_ERR_ALIGN;
+  return DSPARK_OK;
+}
+
+// The optional fragment-packed W2: bf16 weights only, 16-byte aligned, at
+// least as large as the layout for (V, rank).
+inline int check_w2_packed(const void* w2p, std::size_t bytes, int32_t wdtype, int32_t V, int32_t rank) {
+  if (w2p == nullptr) return DSPARK_OK;
+  if (wdtype != DSPARK_W_BF16) return DSPARK_ERR_DTYPE;
+  if (!aligned(w2p, 16)) return DSPARK_ERR_ALIGN;
+  if (bytes < w2_packed_bytes(V, rank)) return DSPARK_ERR_WORKSPACE;
+  return DSPARK_OK;
+}
+
+// Schedule-side shape checks shared by the top-K schedule and the cutoff.
+inline int check_schedule_dims(int32_t R, int32_t gamma) {
+  if (R < 0 || gamma < 1) return DSPARK_ERR_SHAPE;
+  if (gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
+  const int64_t per_thread = (static_cast<int64_t>(R) + 1023) / 1024 * gamma;
+  if (per_thread > DSPARK_SCHED_KEYS_PER_THREAD) return DSPARK_ERR_UNSUPPORTED;
+  return DSPARK_OK;
+}
+
 
 }  // namespace
 
@@ -31,11 +60,13 @@ int plan_draft(const dspark_draft_args* a, DraftPlan* plan) {
   if (a->struct_size != sizeof(dspark_draft_args)) return DSPARK_ERR_ABI;
   int st = check_dims(a->R, a->gamma, a->V, a->rank, a->wdtype);
   if (st != DSPARK_OK) return st;
+  if ((a->flags & ~kKnownFlags) != 0) return DSPARK_ERR_UNSUPPORTED;
+  plan->check = (a->flags & DSPARK_CHECK_INPUTS) != 0;
   plan->seg_rows = seg_rows_for(a->R, a->wdtype);
   plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
   const std::size_t rows = static_cast<std::size_t>(record_rows(plan->seg_rows, a->R));
-  plan->part_off = 0;
-  plan->total = round_up(rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
+  plan->part_off = kHeaderBytes;
+  plan->total = kHeaderBytes + round_up(rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
   return DSPARK_OK;
 }
 
@@ -50,11 +81,9 @@ int validate_draft(const dspark_draft_args* a, DraftPlan* plan) {
   if (!aligned(a->anchor, 4) || !aligned(a->temp, 4) || !aligned(a->u_draft, 4) ||
       !aligned(a->y, 4) || !aligned(a->q_tok, 4) || !aligned(a->q_stats, 8))
     return DSPARK_ERR_ALIGN;
-  if (a->W2_packed != nullptr && a->wdtype != DSPARK_W_BF16) return DSPARK_ERR_DTYPE;
-  if (!aligned(a->W2_packed, 16)) return DSPARK_ERR_ALIGN;
-  if (a->workspace == nullptr || a->workspace_bytes < plan->total) return DSPARK_ERR_WORKSPACE;
-  if (!aligned(a->workspace, kWsAlign)) return DSPARK_ERR_ALIGN;
-  return DSPARK_OK;
+  st = check_w2_packed(a->W2_packed, a->W2_packed_bytes, a->wdtype, a->V, a->rank);
+  if (st != DSPARK_OK) return st;
+  return check_workspace(a->workspace, a->workspace_bytes, plan->total);
 }
 
 int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
@@ -64,10 +93,12 @@ int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
   if (st != DSPARK_OK) return st;
   const int64_t max_rows = static_cast<int64_t>(a->R) * (a->gamma + 1);
   if (a->n_rows < a->R || a->n_rows > max_rows) return DSPARK_ERR_SHAPE;
+  if ((a->flags & ~kKnownFlags) != 0) return DSPARK_ERR_UNSUPPORTED;
+  plan->check = (a->flags & DSPARK_CHECK_INPUTS) != 0;
   plan->seg_rows = seg_rows_for(a->R, a->wdtype);
   plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
   plan->n_chunks = (a->V + kChunk - 1) / kChunk;
-  std::size_t off = 0;
+  std::size_t off = kHeaderBytes;
   plan->vpart_off = off;
   off = round_up(off + static_cast<std::size_t>(a->n_rows) * plan->n_chunks * kChunkFloats * sizeof(float),
                  kWsAlign);
@@ -103,11 +134,9 @@ int validate_verify(const dspark_verify_args* a, VerifyPlan* plan) {
       !aligned(a->u_accept, 4) || !aligned(a->u_final, 4) || !aligned(a->n_accept, 4) ||
       !aligned(a->out_tok, 4) || !aligned(a->p_tok, 4))
     return DSPARK_ERR_ALIGN;
-  if (a->W2_packed != nullptr && a->wdtype != DSPARK_W_BF16) return DSPARK_ERR_DTYPE;
-  if (!aligned(a->W2_packed, 16)) return DSPARK_ERR_ALIGN;
-  if (a->workspace == nullptr || a->workspace_bytes < plan->total) return DSPARK_ERR_WORKSPACE;
-  if (!aligned(a->workspace, kWsAlign)) return DSPARK_ERR_ALIGN;
-  return DSPARK_OK;
+  st = check_w2_packed(a->W2_packed, a->W2_packed_bytes, a->wdtype, a->V, a->rank);
+  if (st != DSPARK_OK) return st;
+  return check_workspace(a->workspace, a->workspace_bytes, plan->total);
 }
 
 int validate_pack_w2(const dspark_pack_w2_args* a) {
@@ -121,13 +150,31 @@ int validate_pack_w2(const dspark_pack_w2_args* a) {
   return DSPARK_OK;
 }
 
-int validate_schedule(const dspark_schedule_args* a) {
-  if (a == nullptr) return DSPARK_ERR_NULL;
+int plan_schedule(const dspark_schedule_args* a, std::size_t* bytes) {
+  if (a == nullptr || bytes == nullptr) return DSPARK_ERR_NULL;
   if (a->struct_size != sizeof(dspark_schedule_args)) return DSPARK_ERR_ABI;
-  if (a->R < 0 || a->gamma < 1) return DSPARK_ERR_SHAPE;
-  if (a->gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
-  const int64_t per_thread = (static_cast<int64_t>(a->R) + 1023) / 1024 * a->gamma;
-  if (per_thread > DSPARK_SCHED_KEYS_PER_THREAD) return DSPARK_ERR_UNSUPPORTED;
+  const int st = check_schedule_dims(a->R, a->gamma);
+  if (st != DSPARK_OK) return st;
+  if ((a->flags & ~kKnownFlags) != 0) return DSPARK_ERR_UNSUPPORTED;
+  *bytes = (a->flags & DSPARK_CHECK_INPUTS) ? kHeaderBytes : 0;
+  return DSPARK_OK;
+}
+
+int plan_cutoff(const dspark_cutoff_args* a, std::size_t* bytes) {
+  if (a == nullptr || bytes == nullptr) return DSPARK_ERR_NULL;
+  if (a->struct_size != sizeof(dspark_cutoff_args)) return DSPARK_ERR_ABI;
+  if (a->conf_min != a->conf_min) return DSPARK_ERR_SHAPE;
+  const int st = check_schedule_dims(a->R, a->gamma);
+  if (st != DSPARK_OK) return st;
+  if ((a->flags & ~kKnownFlags) != 0) return DSPARK_ERR_UNSUPPORTED;
+  *bytes = (a->flags & DSPARK_CHECK_INPUTS) ? kHeaderBytes : 0;
+  return DSPARK_OK;
+}
+
+int validate_schedule(const dspark_schedule_args* a) {
+  std::size_t need = 0;
+  const int st = plan_schedule(a, &need);
+  if (st != DSPARK_OK) return st;
   if (a->R == 0) return DSPARK_OK;
   if (!a->c || !a->anchor || !a->y || !a->a || !a->l || !a->row_offsets || !a->row_req ||
       !a->row_pos || !a->row_tok)
@@ -137,16 +184,13 @@ int validate_schedule(const dspark_schedule_args* a) {
       !aligned(a->row_pos, 4) || !aligned(a->row_tok, 4) ||
       (a->expected_tokens && !aligned(a->expected_tokens, 4)))
     return DSPARK_ERR_ALIGN;
-  return DSPARK_OK;
+  return check_workspace(a->workspace, a->workspace_bytes, need);
 }
 
 int validate_cutoff(const dspark_cutoff_args* a) {
-  if (a == nullptr) return DSPARK_ERR_NULL;
-  if (a->struct_size != sizeof(dspark_cutoff_args)) return DSPARK_ERR_ABI;
-  if (a->R < 0 || a->gamma < 1 || a->conf_min != a->conf_min) return DSPARK_ERR_SHAPE;
-  if (a->gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_UNSUPPORTED;
-  const int64_t per_thread = (static_cast<int64_t>(a->R) + 1023) / 1024 * a->gamma;
-  if (per_thread > DSPARK_SCHED_KEYS_PER_THREAD) return DSPARK_ERR_UNSUPPORTED;
+  std::size_t need = 0;
+  const int st = plan_cutoff(a, &need);
+  if (st != DSPARK_OK) return st;
   if (a->R == 0) return DSPARK_OK;
   if (!a->c || !a->anchor || !a->y || !a->a || !a->l || !a->row_offsets || !a->row_req || !a->row_pos ||
       !a->row_tok)
@@ -156,7 +200,7 @@ int validate_cutoff(const dspark_cutoff_args* a) {
       !aligned(a->row_pos, 4) || !aligned(a->row_tok, 4) ||
       (a->expected_tokens && !aligned(a->expected_tokens, 4)))
     return DSPARK_ERR_ALIGN;
-  return DSPARK_OK;
+  return check_workspace(a->workspace, a->workspace_bytes, need);
 }
 
 int validate_capacity(const dspark_capacity_args* a) {
@@ -214,6 +258,7 @@ const char* status_string(int status) {
     case DSPARK_ERR_UNSUPPORTED: return "arguments outside the library's supported limits";
     case DSPARK_ERR_ABI: return "struct_size does not match this library's ABI";
     case DSPARK_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case DSPARK_ERR_INPUT: return "a device input check found a value outside the contract";
     default: return "unknown status";
   }
 }

@@ -48,6 +48,14 @@ DSPARK_HD inline int range_start(int g, int n, int n_ranges) {
 constexpr int kChunk = 4096;
 constexpr int kChunkFloats = 4;              // floats per (row, chunk) record
 constexpr std::size_t kWsAlign = 256;
+// Every draft and verify workspace (and a schedule workspace, which exists
+// only for the input checks) starts with a header: the error word of the
+// device input checks at byte 0, then per-launch arrival counters of the
+// kernels that combine their workgroups' results in the same launch.
+constexpr std::size_t kHeaderBytes = DSPARK_WORKSPACE_HEADER;
+constexpr std::size_t kCounterOff = 64;  // first arrival counter (uint32)
+constexpr int kMaxCounters = (DSPARK_WORKSPACE_HEADER - 64) / 4;
+static_assert(DSPARK_WORKSPACE_HEADER % 256 == 0, "header keeps the workspace 256-byte aligned");
 
 // k-steps (32 ranks each) of the 16-row kernel for a rank: 2, 4, 8 or 16.
 // The fragment-packed W2 layout uses the same count.
@@ -57,7 +65,8 @@ inline int seg16_ksteps(int rank) { return rank <= 64 ? 2 : (rank <= 128 ? 4 : (
 // 64 lanes' 16-byte MFMA A fragments in lane order, 1 KiB contiguous; lane
 // L = 16 kq + l holds W2[16 s + l][32 ks + 8 kq .. +8] (zero past V or rank).
 inline std::size_t w2_packed_bytes(int V, int rank) {
-  return static_cast<std::size_t>((V + 15) / 16) * seg16_ksteps(rank) * 1024;
+  if (V < 1) return 0;
+  return (static_cast<std::size_t>(V) + 15) / 16 * static_cast<std::size_t>(seg16_ksteps(rank)) * 1024;
 }
 
 // Rows per segment for a batch of R requests with weights of type wdtype.
@@ -71,6 +80,7 @@ struct DraftPlan {
   int n_seg = 0;
   std::size_t part_off = 0;  // [record_rows][n_seg][kRecFloats] float
   std::size_t total = 0;
+  bool check = false;        // DSPARK_CHECK_INPUTS
 };
 
 struct VerifyPlan {
@@ -85,6 +95,7 @@ struct VerifyPlan {
   std::size_t rcount_off = 0;   // int32 count
   std::size_t rlist_off = 0;    // [R] ResidualEntry (48 bytes)
   std::size_t total = 0;
+  bool check = false;           // DSPARK_CHECK_INPUTS
 };
 
 constexpr std::size_t kResidualEntryBytes = 48;
@@ -98,6 +109,9 @@ int validate_draft(const dspark_draft_args* a, DraftPlan* plan);  // sizes + poi
 int plan_verify(const dspark_verify_args* a, VerifyPlan* plan);
 int validate_verify(const dspark_verify_args* a, VerifyPlan* plan);
 
+// Schedule calls: workspace bytes (the header with DSPARK_CHECK_INPUTS, else 0).
+int plan_schedule(const dspark_schedule_args* a, std::size_t* bytes);
+int plan_cutoff(const dspark_cutoff_args* a, std::size_t* bytes);
 int validate_schedule(const dspark_schedule_args* a);
 int validate_cutoff(const dspark_cutoff_args* a);
 int validate_pack_w2(const dspark_pack_w2_args* a);

@@ -50,7 +50,10 @@ __global__ void __launch_bounds__(256) verify_stats_kernel(VerifyParams p) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63;
   // the residual list is rebuilt by verify_finish, which runs after this kernel
-  if (p.rs_count != nullptr && (blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *p.rs_count = 0;
+  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) {
+    if (p.rs_count != nullptr) *p.rs_count = 0;
+    if (p.err_clear != nullptr) *p.err_clear = 0u;
+  }
   const int ch = blockIdx.z * 4 + __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   if (ch >= p.n_chunks) return;  // wavefront-uniform; no workgroup barrier follows
   const int64_t lo = min(max(static_cast<int64_t>(p.row_offsets[r]), int64_t{0}), p.n_rows);

@@ -32,6 +32,16 @@
  *     (token ids, logits, offsets, probabilities) is not inspected on the
  *     host; out-of-range ids and offsets are clamped inside the kernels so no
  *     access leaves its buffer, but the results are then unspecified.
+ *   - Device input checks (debug): with DSPARK_CHECK_INPUTS in `flags`, a
+ *     call first runs a small kernel that inspects its device inputs (token
+ *     ids, uniforms, confidences, verify row offsets) and writes what it
+ *     found as DSPARK_BAD_* bits into the error word at the start of the
+ *     call's workspace; the call's other kernels run as usual.
+ *     dspark_check() synchronises the stream and reads that word back.  A
+ *     block size or verify length that does not match the call is thereby
+ *     reported instead of silently changing the results ([PR] automated
+ *     review: a non-uniform block must not be inferred silently, a degraded
+ *     result must not be silent, a missing input must be an error).
  *   - No C++ exception crosses this interface and nothing is printed.
  *   - Calls that share a workspace must not overlap in time.
  *   - Argument structs are versioned: set struct_size = sizeof(the struct).
@@ -46,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 1
+#define DSPARK_ABI_VERSION 2
 
 /* limits checked on the host */
 #define DSPARK_MAX_GAMMA 16          /* block size gamma in [1, 16]                 */
@@ -64,8 +74,25 @@ typedef enum dspark_status {
   DSPARK_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required        */
   DSPARK_ERR_UNSUPPORTED = 6, /* valid but outside this library's limits           */
   DSPARK_ERR_ABI = 7,         /* struct_size does not match this library          */
-  DSPARK_ERR_HIP = 8          /* a HIP runtime call or kernel launch failed        */
+  DSPARK_ERR_HIP = 8,         /* a HIP runtime call or kernel launch failed        */
+  DSPARK_ERR_INPUT = 9        /* dspark_check: a device input check failed         */
 } dspark_status;
+
+/* Bits of the `flags` field of the argument structs. */
+#define DSPARK_CHECK_INPUTS 1u       /* run the device input checks (debug)          */
+
+/* Bits of the error word that dspark_check() returns (the start of the
+ * workspace of a call made with DSPARK_CHECK_INPUTS). */
+#define DSPARK_BAD_TOKEN (1u << 0)      /* an anchor or drafted token outside [0, V)  */
+#define DSPARK_BAD_UNIFORM (1u << 1)    /* a uniform outside [0, 1), or NaN          */
+#define DSPARK_BAD_LENGTH (1u << 2)     /* verify rows: a request owns fewer than 1 or
+                                           more than gamma + 1 rows (l outside
+                                           [0, gamma]), or the offsets leave
+                                           [0, n_rows]                               */
+#define DSPARK_BAD_CONFIDENCE (1u << 3) /* a confidence outside [0, 1], or NaN       */
+/* Size of the header that holds the error word at the start of every
+ * workspace (the rest of the workspace follows it). */
+#define DSPARK_WORKSPACE_HEADER 256
 
 /* Element type of the Markov factors W1, W2. */
 typedef enum dspark_wdtype {
@@ -103,6 +130,7 @@ typedef enum dspark_wdtype {
  *                       [1, DSPARK_MAX_GAMMA], V in [1, DSPARK_MAX_VOCAB],
  *                       rank in [8, DSPARK_MAX_RANK] with rank % 8 == 0.
  *   wdtype              dspark_wdtype of W1 and W2.
+ *   flags               0, or DSPARK_CHECK_INPUTS (checks anchor and u_draft).
  *   U        float [R, gamma, V]  base logits; 16-byte aligned.  Each entry
  *                                 is finite or -inf (a masked token), and
  *                                 every row of U + B has a finite entry;
@@ -131,11 +159,15 @@ typedef enum dspark_wdtype {
  *   W2_packed    optional (NULL normally): the output of dspark_pack_w2 for
  *                this W2, 16-byte aligned; read instead of W2 by the fused
  *                kernel when the batch takes the 16-row path (bf16, R <= 64).
+ *   W2_packed_bytes  size of the W2_packed buffer; at least
+ *                dspark_w2_packed_bytes(V, rank) when W2_packed is given
+ *                (DSPARK_ERR_WORKSPACE otherwise).
  * -------------------------------------------------------------------------- */
 typedef struct dspark_draft_args {
   uint32_t struct_size;
   int32_t R, gamma, V, rank;
   int32_t wdtype;
+  uint32_t flags;
   const float* U;
   const void* W1;
   const void* W2;
@@ -150,6 +182,7 @@ typedef struct dspark_draft_args {
   void* stream;
   void* const* prof_events;
   const void* W2_packed;
+  size_t W2_packed_bytes;
 } dspark_draft_args;
 
 /* --------------------------------------------------------------------------
@@ -183,6 +216,8 @@ typedef struct dspark_draft_args {
  *   R, gamma   host ints; R >= 0, gamma in [1, DSPARK_MAX_GAMMA],
  *              ceil(R / 1024) * gamma <= DSPARK_SCHED_KEYS_PER_THREAD.
  *   K          host int64 capacity in draft positions (any value; clamped).
+ *   flags      0, or DSPARK_CHECK_INPUTS (checks that c is in [0, 1] and that
+ *              anchor and y are not negative; this call knows no V).
  *   c          float [R, gamma]  per-position acceptance estimates.
  *   anchor     int32 [R]; y int32 [R, gamma] (drafted tokens; only copied
  *              into row_tok, never read by the decision).
@@ -191,12 +226,16 @@ typedef struct dspark_draft_args {
  *   row_offsets int32 [R + 1]    out.
  *   row_req, row_pos, row_tok  int32 [dspark_schedule_rows(R, gamma, K)] out.
  *   expected_tokens  float [1]   optional out (may be NULL).
+ *   workspace, workspace_bytes  dspark_schedule_workspace_size() bytes,
+ *              256-byte aligned: none (NULL, 0) without DSPARK_CHECK_INPUTS,
+ *              the error-word header with it.
  *   stream     hipStream_t as void*.
  * -------------------------------------------------------------------------- */
 typedef struct dspark_schedule_args {
   uint32_t struct_size;
   int32_t R, gamma;
   int64_t K;
+  uint32_t flags;
   const float* c;
   const int32_t* anchor;
   const int32_t* y;
@@ -207,6 +246,8 @@ typedef struct dspark_schedule_args {
   int32_t* row_pos;
   int32_t* row_tok;
   float* expected_tokens;
+  void* workspace;
+  size_t workspace_bytes;
   void* stream;
 } dspark_schedule_args;
 
@@ -243,6 +284,8 @@ typedef struct dspark_schedule_args {
  *
  * Arguments (device arrays unless stated):
  *   R, gamma, V, rank, wdtype  as for dspark_draft_block.
+ *   flags      0, or DSPARK_CHECK_INPUTS (checks row_offsets, anchor, y,
+ *              u_accept and u_final).
  *   n_rows     host int64: total rows = row_offsets[R]; R <= n_rows <=
  *              R * (gamma + 1).
  *   target     float [n_rows, V]  target logits; 16-byte aligned; finite or
@@ -260,13 +303,14 @@ typedef struct dspark_schedule_args {
  *   workspace, workspace_bytes    >= dspark_verify_workspace_size(); 256-byte
  *                                 aligned.
  *   stream     hipStream_t as void*.
- *   W2_packed  optional, as for dspark_draft_block (read by the residual
- *              pass of the 16-row path).
+ *   W2_packed, W2_packed_bytes  optional, as for dspark_draft_block (read by
+ *              the residual pass of the 16-row path).
  * -------------------------------------------------------------------------- */
 typedef struct dspark_verify_args {
   uint32_t struct_size;
   int32_t R, gamma, V, rank;
   int32_t wdtype;
+  uint32_t flags;
   int64_t n_rows;
   const float* target;
   const int32_t* row_offsets;
@@ -287,13 +331,32 @@ typedef struct dspark_verify_args {
   size_t workspace_bytes;
   void* stream;
   const void* W2_packed;
+  size_t W2_packed_bytes;
 } dspark_verify_args;
 
 /* Workspace bytes needed by a call with these arguments (only the size
- * fields are read).  Returns DSPARK_OK and writes *bytes, or an error status
- * for invalid sizes. */
+ * fields and flags are read).  Returns DSPARK_OK and writes *bytes, or an
+ * error status for invalid sizes.  Draft and verify workspaces start with
+ * the DSPARK_WORKSPACE_HEADER bytes of the error word; the schedule calls
+ * need a workspace (that header alone) only with DSPARK_CHECK_INPUTS, and
+ * report 0 bytes otherwise. */
 int dspark_draft_workspace_size(const dspark_draft_args* args, size_t* bytes);
 int dspark_verify_workspace_size(const dspark_verify_args* args, size_t* bytes);
+int dspark_schedule_workspace_size(const dspark_schedule_args* args, size_t* bytes);
+
+/* --------------------------------------------------------------------------
+ * dspark_check: result of the device input checks of the last call that
+ * used `workspace` with DSPARK_CHECK_INPUTS (debug only: it synchronises).
+ *
+ * Waits for `stream` (hipStream_t as void*), then copies the error word at
+ * the start of the workspace to the host.  Returns DSPARK_OK when it is 0,
+ * DSPARK_ERR_INPUT when some DSPARK_BAD_* bit is set, DSPARK_ERR_NULL for a
+ * NULL workspace, DSPARK_ERR_HIP if the wait or the copy fails.  *bits (may
+ * be NULL) receives the word.  Every call that uses a draft or verify
+ * workspace rewrites the word (0 when it was made without the flag), so a
+ * check reports the call that ran last on that workspace.
+ * -------------------------------------------------------------------------- */
+int dspark_check(const void* workspace, void* stream, uint32_t* bits);
 
 /* --------------------------------------------------------------------------
  * dspark_schedule_cutoff: survival and the static confidence-cutoff schedule.
@@ -316,7 +379,8 @@ int dspark_verify_workspace_size(const dspark_verify_args* args, size_t* bytes);
  * conf_min <= 0 verifies every position (the fixed-length schedule);
  * conf_min > 1 verifies none (target-only decoding).
  *
- * Arguments: as dspark_schedule_args, without K and with
+ * Arguments: as dspark_schedule_args (flags and workspace included),
+ * without K and with
  *   conf_min   host float, not NaN (DSPARK_ERR_SHAPE otherwise).
  *   row_req, row_pos, row_tok  int32 [R * (gamma + 1)] out: room for the
  *              largest schedule (R + sum l[r] rows are written; the number is
@@ -326,6 +390,7 @@ typedef struct dspark_cutoff_args {
   uint32_t struct_size;
   int32_t R, gamma;
   float conf_min;
+  uint32_t flags;
   const float* c;
   const int32_t* anchor;
   const int32_t* y;
@@ -336,8 +401,14 @@ typedef struct dspark_cutoff_args {
   int32_t* row_pos;
   int32_t* row_tok;
   float* expected_tokens;
+  void* workspace;
+  size_t workspace_bytes;
   void* stream;
 } dspark_cutoff_args;
+
+/* Workspace bytes of dspark_schedule_cutoff: 0, or the error-word header with
+ * DSPARK_CHECK_INPUTS (as dspark_schedule_workspace_size). */
+int dspark_cutoff_workspace_size(const dspark_cutoff_args* args, size_t* bytes);
 
 
 /* --------------------------------------------------------------------------

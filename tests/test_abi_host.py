@@ -34,9 +34,10 @@ def test_header_declares_and_library_exports_everything():
 
 
 def test_abi_version_and_strings():
-    assert ds.dspark_abi_version() == 1
-    for s in range(9):
-        assert ds.dspark_status_string(s)
+    assert ds.dspark_abi_version() == 2
+    strings = [ds.dspark_status_string(s) for s in range(10)]
+    assert all(strings) and len(set(strings)) == 10
+    assert "unknown status" not in strings
     assert ds.dspark_status_string(123) == "unknown status"
 
 
@@ -55,25 +56,34 @@ def test_workspace_sizes_match_struct_layout():
     def up(x):
         return (x + 255) // 256 * 256
 
+    H = ds.WORKSPACE_HEADER  # the error word (and arrival counters) come first
+    assert H == 256
     # one (max, sum) record of two floats per (request row, 16-row segment);
     # the 16-row path (bf16 weights, R <= 64) always holds 64 request rows
-    assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1) == up(64 * 9496 * 8)
-    assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1) == up(64 * 63 * 8)
+    assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1) == H + up(64 * 9496 * 8)
+    assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1) == H + up(64 * 63 * 8)
+    # the input checks need no more room than the header
+    assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1, ds.CHECK_INPUTS) == H + up(64 * 63 * 8)
     # 64-row segments above 64 requests (bf16): R + 17 record rows (padding
     # requests of the last chunk, one dummy row)
-    assert ds.draft_workspace_bytes(65, 7, 151936, 512, 1) == up((65 + 17) * 2374 * 8)
+    assert ds.draft_workspace_bytes(65, 7, 151936, 512, 1) == H + up((65 + 17) * 2374 * 8)
     # 32-row segments, one row per request, for fp32 weights
-    assert ds.draft_workspace_bytes(65, 7, 151936, 512, 0) == up(65 * 4748 * 8)
-    assert ds.draft_workspace_bytes(8, 7, 1024, 32, 0) == up(8 * 32 * 8)
+    assert ds.draft_workspace_bytes(65, 7, 151936, 512, 0) == H + up(65 * 4748 * 8)
+    assert ds.draft_workspace_bytes(8, 7, 1024, 32, 0) == H + up(8 * 32 * 8)
     # verify: chunk records (16 bytes per 4096-entry chunk of each target row),
     # residual info/stats, then the residual segment records
     nb = ds.verify_workspace_bytes(64, 7, 151936, 512, 1, 512)
-    assert nb == up(512 * 38 * 16) + up(64 * 16) + up(64 * 16) + up(64 * 9496 * 8)
+    assert nb == H + up(512 * 38 * 16) + up(64 * 16) + up(64 * 16) + up(64 * 9496 * 8)
     # 64-row path: plus the count and list (48 bytes per request) of the
     # requests that need the residual pass
     nb = ds.verify_workspace_bytes(256, 5, 129280, 512, 1, 768)
-    assert nb == (up(768 * 32 * 16) + up(256 * 16) + up(256 * 16) + up((256 + 17) * 2020 * 8) + up(4)
+    assert nb == (H + up(768 * 32 * 16) + up(256 * 16) + up(256 * 16) + up((256 + 17) * 2020 * 8) + up(4)
                   + up(256 * 48))
+    # the schedule calls need a workspace (the header) only for the checks
+    assert ds.dspark_schedule_workspace_size(64, 7) == 0
+    assert ds.dspark_schedule_workspace_size(64, 7, ds.CHECK_INPUTS) == H
+    assert ds.dspark_cutoff_workspace_size(1024, 16) == 0
+    assert ds.dspark_cutoff_workspace_size(1024, 16, ds.CHECK_INPUTS) == H
 
 
 def _draft_args(**kw):
@@ -104,6 +114,8 @@ def _call(fn, args):
     (dict(), ds.Status.ERR_WORKSPACE),
     (dict(workspace=FAKE, workspace_bytes=100), ds.Status.ERR_WORKSPACE),
     (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), ds.Status.ERR_ALIGN),
+    (dict(flags=2), ds.Status.ERR_UNSUPPORTED),            # unknown flag bit
+    (dict(flags=1 << 31), ds.Status.ERR_UNSUPPORTED),
 ])
 def test_draft_rejects_invalid_arguments(kw, status):
     assert _call("dspark_draft_block", _draft_args(**kw)) == status
@@ -136,6 +148,7 @@ def _verify_args(**kw):
     (dict(target=FAKE + 4), ds.Status.ERR_ALIGN),
     (dict(q_stats=FAKE + 4), ds.Status.ERR_ALIGN),
     (dict(), ds.Status.ERR_WORKSPACE),
+    (dict(flags=4), ds.Status.ERR_UNSUPPORTED),
 ])
 def test_verify_rejects_invalid_arguments(kw, status):
     assert _call("dspark_verify", _verify_args(**kw)) == status
@@ -147,6 +160,11 @@ def test_verify_rejects_invalid_arguments(kw, status):
     (dict(R=1025, gamma=9), ds.Status.ERR_UNSUPPORTED),   # ceil(R/1024) * gamma > 16
     (dict(c=None), ds.Status.ERR_NULL),
     (dict(row_tok=FAKE + 2), ds.Status.ERR_ALIGN),
+    (dict(flags=2), ds.Status.ERR_UNSUPPORTED),
+    # the input checks write their error word into a workspace
+    (dict(flags=1), ds.Status.ERR_WORKSPACE),
+    (dict(flags=1, workspace=FAKE, workspace_bytes=255), ds.Status.ERR_WORKSPACE),
+    (dict(flags=1, workspace=FAKE + 128, workspace_bytes=256), ds.Status.ERR_ALIGN),
 ])
 def test_schedule_rejects_invalid_arguments(kw, status):
     base = dict(struct_size=ctypes.sizeof(ds.ScheduleArgs), R=8, gamma=4, K=10)
@@ -165,6 +183,8 @@ def test_schedule_rejects_invalid_arguments(kw, status):
     (dict(R=1025, gamma=9), ds.Status.ERR_UNSUPPORTED),
     (dict(y=None), ds.Status.ERR_NULL),
     (dict(row_pos=FAKE + 2), ds.Status.ERR_ALIGN),
+    (dict(flags=8), ds.Status.ERR_UNSUPPORTED),
+    (dict(flags=1), ds.Status.ERR_WORKSPACE),
 ])
 def test_cutoff_rejects_invalid_arguments(kw, status):
     base = dict(struct_size=ctypes.sizeof(ds.CutoffArgs), R=8, gamma=4, conf_min=0.5)
@@ -262,15 +282,53 @@ def test_pack_rejects_invalid_arguments(kw, status):
     assert _call("dspark_pack_w2", ds.PackArgs(**base)) == status
 
 
-def test_packed_w2_needs_bf16_and_alignment():
+def test_packed_w2_needs_bf16_alignment_and_size():
     big = dict(workspace=FAKE, workspace_bytes=1 << 30)
-    assert _call("dspark_draft_block", _draft_args(wdtype=0, W2_packed=FAKE, **big)) == ds.Status.ERR_DTYPE
-    assert _call("dspark_draft_block", _draft_args(W2_packed=FAKE + 4, **big)) == ds.Status.ERR_ALIGN
-    assert _call("dspark_verify", _verify_args(wdtype=0, W2_packed=FAKE, **big)) == ds.Status.ERR_DTYPE
+    need = ds.dspark_w2_packed_bytes(1000, 64)
+    assert _call("dspark_draft_block", _draft_args(wdtype=0, W2_packed=FAKE, W2_packed_bytes=need,
+                                                   **big)) == ds.Status.ERR_DTYPE
+    assert _call("dspark_draft_block", _draft_args(W2_packed=FAKE + 4, W2_packed_bytes=need,
+                                                   **big)) == ds.Status.ERR_ALIGN
+    assert _call("dspark_verify", _verify_args(wdtype=0, W2_packed=FAKE, W2_packed_bytes=need,
+                                               **big)) == ds.Status.ERR_DTYPE
+    # a packed copy smaller than the layout of (V, rank) is rejected: made for
+    # a smaller V or rank, it would be read past its end
+    for fn, mk in (("dspark_draft_block", _draft_args), ("dspark_verify", _verify_args)):
+        assert _call(fn, mk(W2_packed=FAKE, W2_packed_bytes=need - 1, **big)) == ds.Status.ERR_WORKSPACE
+        assert _call(fn, mk(W2_packed=FAKE, W2_packed_bytes=0, **big)) == ds.Status.ERR_WORKSPACE
+        assert _call(fn, mk(W2_packed=FAKE, W2_packed_bytes=ds.dspark_w2_packed_bytes(900, 64),
+                            **big)) == ds.Status.ERR_WORKSPACE
+
+
+def test_check_needs_a_workspace():
+    lib = ds.get_lib()
+    bits = ctypes.c_uint32(7)
+    assert lib.dspark_check(None, None, ctypes.byref(bits)) == ds.Status.ERR_NULL
+    assert bits.value == 7  # untouched on error
+
+
+def test_binding_checks_the_packed_copy():
+    """The binding refuses a packed copy of the wrong type, device, layout or
+    size before calling the library (CPU tensors: nothing is launched)."""
+    import torch
+    dev = torch.device("cpu")
+    need = ds.dspark_w2_packed_bytes(1000, 64)
+    assert ds._w2_packed(None, dev, 1000, 64) == (None, 0)
+    with pytest.raises(TypeError):
+        ds._w2_packed(torch.zeros(need, dtype=torch.int16), dev, 1000, 64)
+    with pytest.raises(ValueError):
+        ds._w2_packed(torch.zeros(need - 1, dtype=torch.uint8), dev, 1000, 64)
+    with pytest.raises(ValueError):
+        ds._w2_packed(torch.zeros(2 * need, dtype=torch.uint8)[::2], dev, 1000, 64)
+    ptr, nbytes = ds._w2_packed(torch.zeros(need, dtype=torch.uint8), dev, 1000, 64)
+    assert nbytes == need and ptr
 
 
 def test_null_args_pointer():
     lib = ds.get_lib()
+    n = ctypes.c_size_t(0)
+    assert lib.dspark_schedule_workspace_size(None, ctypes.byref(n)) == ds.Status.ERR_NULL
+    assert lib.dspark_cutoff_workspace_size(None, ctypes.byref(n)) == ds.Status.ERR_NULL
     assert lib.dspark_draft_block(None) == ds.Status.ERR_NULL
     assert lib.dspark_verify(None) == ds.Status.ERR_NULL
     assert lib.dspark_schedule(None) == ds.Status.ERR_NULL
