@@ -1,6 +1,7 @@
 """Benchmark of one DSpark draft -> schedule -> verify step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--policy greedy|sampled]
+    python bench.py --sweep capacity|sts     (size sweeps of the off-step kernels, for a kernel trace)
 
 Workload (default): R = 64 requests, block gamma = 7, vocabulary V = 151936,
 Markov rank r = 512, bf16 Markov factors, fp32 logits, per-request
@@ -24,8 +25,12 @@ gives the warm-cache rate for context.
 Prints ONE JSON line.  `roofline` is for the dominant kernel (the fused Markov
 bias + softmax statistics kernel: bias_seg16 for bf16 weights and R <= 64,
 bias_seg64 above, bias_seg32_f32 for fp32 weights), timed with HIP events
-recorded by the library around each launch; `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+recorded by the library around each launch; `calls_us` gives each call's
+time per step (a separate pass with events between the calls);
+`acceptance` the accept rate by draft position and the tokens emitted per
+request and verify pass; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload, on one host core and on all of them (processes
+over request chunks, the schedule in the parent), before the GPU is used.
 """
 from __future__ import annotations
 
@@ -111,44 +116,172 @@ class HipTimingEvents:
         self.handles = []
 
 
-def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=None):
-    """The CPU oracle on a bounded sample of requests (single BLAS thread),
-    with the same scheduler as the GPU step (with capacity_sps: the capacity
-    from the survival, then the top-K schedule with it; with sts = (logits,
-    calibration logits, calibration counts): the temperatures fitted once
-    outside the timing, then the calibrated confidence in each step)."""
+# inputs of the all-cores oracle leg, set in the parent before its worker
+# processes are forked (copy-on-write; the workers read them, never write)
+_POOL = {}
+
+
+def _oracle_draft_chunk(reqs):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    P = _POOL
+    inp = P["inp"]
+    with threadpool_limits(limits=1):
+        d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft, requests=reqs)
+    return reqs, d.y[reqs], d.q_tok[reqs], len(d.flags)
+
+
+def _oracle_verify_chunk(job):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    reqs, y, q_tok = job
+    P = _POOL
+    inp = P["inp"]
+    with threadpool_limits(limits=1):
+        v = oracle.verify(P["rows"], P["row_offsets"], inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, y, q_tok,
+                          inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+    return len(v.flags)
+
+
+def _host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count() or 1
+    return dict(cpu_count=os.cpu_count(), allowed=allowed, model=model)
+
+
+def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=None, max_procs=16):
+    """The CPU oracle, unmodified, on a bounded sample of requests of the same
+    workload, timed twice: on one host core (BLAS on one thread, the process
+    pinned to one core) and on all allowed cores (up to max_procs worker
+    processes over request chunks, BLAS on one thread each; the schedule in
+    the parent, as the global top-K needs every request's survival).  The
+    scheduler is the GPU step's (with capacity_sps: the capacity from the
+    survival, then the top-K schedule with it; with sts = (logits,
+    calibration logits, calibration counts): temperatures fitted once outside
+    the timing, then the calibrated confidence in each step).  The row gather
+    stands in for the target forward and is not timed, as on the GPU.  Must
+    run before this process touches the GPU (the workers are forked)."""
+    import multiprocessing as mp
+
     import oracle
     from threadpoolctl import threadpool_limits
     rng = np.random.default_rng(seed)
     reqs = sorted(rng.choice(inp.R, size=min(n_sample, inp.R), replace=False).tolist())
-    conf = inp.c
-    with threadpool_limits(limits=1):
-        tau = oracle.sts_fit(sts[1], sts[2]).tau if sts is not None else None
-        t0 = time.perf_counter()
-        if sts is not None:
-            conf = oracle.sts_apply(sts[0], tau)
-        d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
-                               requests=reqs)
-        y = np.where(d.y < 0, 0, d.y)
+    host = _host_cpu()
+
+    def sched(conf, y):
         if capacity_sps is not None:
             cap = oracle.capacity(oracle.survival(conf), capacity_sps)
-            s = oracle.schedule(conf, cap.K, inp.anchor, y)
-        elif conf_min is None:
-            s = oracle.schedule(conf, inp.K, inp.anchor, y)
-        else:
-            s = oracle.schedule_cutoff(conf, conf_min, inp.anchor, y)
+            return oracle.schedule(conf, cap.K, inp.anchor, y)
+        if conf_min is None:
+            return oracle.schedule(conf, inp.K, inp.anchor, y)
+        return oracle.schedule_cutoff(conf, conf_min, inp.anchor, y)
+
+    tau = None
+    if sts is not None:
+        with threadpool_limits(limits=1):
+            tau = oracle.sts_fit(sts[1], sts[2]).tau
+
+    # (1) one core
+    old_aff = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if old_aff:
+        os.sched_setaffinity(0, {min(old_aff)})
+    try:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            conf = oracle.sts_apply(sts[0], tau) if sts is not None else inp.c
+            d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
+                                   requests=reqs)
+            y = np.where(d.y < 0, 0, d.y)
+            sch = sched(conf, y)
+            t1 = time.perf_counter()
+            rows = inp.target[sch.row_req.astype(np.int64), sch.row_pos.astype(np.int64)]
+            t2 = time.perf_counter()
+            v = oracle.verify(rows, sch.row_offsets, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, y, d.q_tok,
+                              inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+            t3 = time.perf_counter()
+    finally:
+        if old_aff:
+            os.sched_setaffinity(0, old_aff)
+    el1 = (t1 - t0) + (t3 - t2)
+    flags = dict(draft=len(d.flags), verify=len(v.flags))
+
+    # (2) all allowed cores: the same sample split into one chunk per process
+    n_proc = max(1, min(host["allowed"], max_procs, len(reqs)))
+    chunks = [c.tolist() for c in np.array_split(np.asarray(reqs), n_proc) if len(c)]
+    _POOL.clear()
+    _POOL.update(inp=inp, rows=rows, row_offsets=sch.row_offsets)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(n_proc) as pool:
+        pool.map(abs, range(n_proc))  # workers up before timing
+        t0 = time.perf_counter()
+        conf = oracle.sts_apply(sts[0], tau) if sts is not None else inp.c
+        y_all = np.zeros((inp.R, inp.gamma), np.int32)
+        q_all = np.full((inp.R, inp.gamma), np.nan)
+        for rq, yy, qq, _ in pool.map(_oracle_draft_chunk, chunks):
+            y_all[rq] = yy
+            q_all[rq] = qq
+        sch2 = sched(conf, y_all)
         t1 = time.perf_counter()
-        # the row gather stands in for the target forward (not timed, as on the GPU)
-        rows = inp.target[s.row_req.astype(np.int64), s.row_pos.astype(np.int64)]
+        # the rows were gathered above (row_req / row_pos do not depend on y)
+        assert np.array_equal(sch2.row_offsets, sch.row_offsets)
         t2 = time.perf_counter()
-        oracle.verify(rows, s.row_offsets, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, y, d.q_tok,
-                      inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+        pool.map(_oracle_verify_chunk, [(c, y_all, q_all) for c in chunks])
         t3 = time.perf_counter()
-    el = (t1 - t0) + (t3 - t2)
-    return dict(value=len(reqs) * inp.gamma / el, unit="positions/s", cores=1, kind="oracle",
+    _POOL.clear()
+    eln = (t1 - t0) + (t3 - t2)
+    pos = len(reqs) * inp.gamma
+    return dict(value=pos / eln, unit="positions/s", cores=n_proc, kind="oracle",
                 sample=f"{len(reqs)} of {inp.R} requests (all {inp.gamma} positions, full V) plus the "
-                       f"full-batch schedule; fp64 NumPy, 1 BLAS thread; {el:.1f} s",
-                seconds=round(el, 2))
+                       f"full-batch schedule; fp64 NumPy, 1 BLAS thread per process; {n_proc} processes over "
+                       f"request chunks: {eln:.2f} s; one core: {el1:.2f} s",
+                seconds=round(eln, 2),
+                single_core=dict(value=pos / el1, cores=1, seconds=round(el1, 2)),
+                host=host, oracle_flags=flags)
+
+
+CAPACITY_SIZES = [(1, 1), (64, 7), (256, 5), (1024, 5), (1024, 16)]
+STS_SIZES = [(2000, 7), (8192, 7), (8193, 7), (20000, 1), (20000, 7), (24576, 7), (40000, 7)]
+SWEEP_REPEATS = 3
+
+
+def sweep(which):
+    """Size sweep of an off-step kernel (dspark_capacity or dspark_sts_fit):
+    each size is called SWEEP_REPEATS times on seeded synthetic inputs and one
+    line per size is printed, so that a kernel trace (rocprofv3
+    --kernel-trace) can be matched to its sizes by call order."""
+    import torch
+    import draft_verify_sampling_bias_amd as ds
+    import synth
+    if which == "capacity":
+        for R, gamma in CAPACITY_SIZES:
+            rng = np.random.default_rng(R * 31 + gamma)
+            c = (1 / (1 + np.exp(-rng.normal(1, 1, (R, gamma))))).astype(np.float32)
+            a = torch.from_numpy(np.cumprod(c, axis=1).astype(np.float32)).cuda()
+            sps = torch.from_numpy(synth.sps_table(R * (gamma + 1) + 1)).cuda()
+            for _ in range(SWEEP_REPEATS):
+                out = ds.dspark_capacity(a, sps)
+            torch.cuda.synchronize()
+            print(f"capacity R={R} gamma={gamma} candidates={R * gamma} K={int(out['K'].item())}", flush=True)
+    else:
+        for N, gamma in STS_SIZES:
+            z, n_acc, _ = synth.make_calibration(5, N, gamma)
+            zd, nd = torch.from_numpy(z).cuda(), torch.from_numpy(n_acc).cuda()
+            for _ in range(SWEEP_REPEATS):
+                tau = ds.dspark_sts_fit(zd, nd)
+            torch.cuda.synchronize()
+            print(f"sts_fit N={N} gamma={gamma} tau={np.round(tau.cpu().numpy(), 4).tolist()}", flush=True)
 
 
 def main():
@@ -157,6 +290,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--policy", default=None, choices=["greedy", "sampled"],
+                    help="the greedy or the sampled run of configs 1 and 2 (default: the configuration's first)")
+    ap.add_argument("--sweep", default=None, choices=["capacity", "sts"],
+                    help="only run a size sweep of dspark_capacity or dspark_sts_fit (durations from a kernel "
+                         "trace: one line is printed per size, in call order)")
     ap.add_argument("--cpu-sample", type=int, default=64)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the back-to-back warm loop")
@@ -186,9 +324,27 @@ def main():
                                    "(request sharding across GPUs is a design note, not built)"}))
         sys.exit(2)
 
+    import synth
+
+    if args.sweep:
+        sweep(args.sweep)
+        return
+    inp = None
+    cpu = None
+    if not args.copy_calib:
+        inp = synth.make_config(args.config, args.policy)
+        # the CPU oracle runs first: its all-cores leg forks worker
+        # processes, which must happen before this process uses the GPU
+        if not args.skip_cpu:
+            R_, g_ = inp.R, inp.gamma
+            cpu = cpu_baseline(inp, args.cpu_sample, conf_min=args.conf_min,
+                               capacity_sps=synth.sps_table(R_ * (g_ + 1) + 1) if args.capacity else None,
+                               sts=(synth.make_calibration(7000 + args.config, R_, g_)[0],
+                                    *synth.make_calibration(7100 + args.config, 20000, g_)[:2])
+                               if args.sts else None)
+
     import torch
     import draft_verify_sampling_bias_amd as ds
-    import synth
 
     dev = torch.device("cuda:0")
     if args.copy_calib:
@@ -201,7 +357,6 @@ def main():
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
         return
 
-    inp = synth.make_config(args.config)
     R, gamma, V, rank = inp.R, inp.gamma, inp.V, inp.rank
     wbytes = 2 if inp.wdtype == "bf16" else 4
 
@@ -360,7 +515,41 @@ def main():
     tile_ms = [kev.elapsed_ms(2 * gamma * i + 2 * k, 2 * gamma * i + 2 * k + 1) for i in range(K) for k in range(gamma)]
     kev.close()
 
-    # (3) context: back-to-back steps with warm caches
+    # (3) each call's time: events between the calls of the step (a pass of
+    # its own, as the events add a little to the step); eager calls only
+    cev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        evict()
+        cev[i][0].record(stream)
+        ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d,
+                              W2_packed=W2p)
+        cev[i][1].record(stream)
+        schedule()
+        cev[i][2].record(stream)
+        ds.dspark_verify(rows, sch["row_offsets"], U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final,
+                         out=(n_acc, out_tok, p_tok), workspace=ws_v, W2_packed=W2p)
+        cev[i][3].record(stream)
+    torch.cuda.synchronize()
+    calls_us = {name: round(float(np.mean([cev[i][j].elapsed_time(cev[i][j + 1]) for i in range(K)])) * 1e3, 2)
+                for j, name in enumerate(("draft", "schedule", "verify"))}
+
+    # acceptance of the step (the inputs are the same every step): rate by
+    # draft position among the requests that verified it and reached it
+    # (every earlier draft accepted), and tokens emitted per request and
+    # verify pass (accepted drafts + the correction or bonus)
+    n_acc_h = n_acc.cpu().numpy().astype(np.int64)
+    l_h = sch["l"].cpu().numpy().astype(np.int64)
+    by_pos = []
+    for k in range(gamma):
+        reached = int(np.sum((l_h > k) & (n_acc_h >= k)))
+        acc = int(np.sum((l_h > k) & (n_acc_h > k)))
+        by_pos.append(dict(position=k, reached=reached, accepted=acc,
+                           rate=round(acc / reached, 4) if reached else None))
+    acceptance = dict(by_position=by_pos, tokens_per_request_per_pass=round(float(np.mean(n_acc_h + 1)), 4),
+                      accepted_drafts=int(n_acc_h.sum()), verified_drafts=int(l_h.sum()),
+                      greedy_requests=int(np.sum(inp.temp <= 0)))
+
+    # (4) context: back-to-back steps with warm caches
     warm = None
     if not args.no_warm:
         torch.cuda.synchronize()
@@ -378,13 +567,6 @@ def main():
     tile_gbps = bytes_tile / (tile_avg_ms / 1e3) / 1e9
     step_gbps = bytes_step / (ms_per_step / 1e3) / 1e9
 
-    cpu = None
-    if not args.skip_cpu:
-        cpu = cpu_baseline(inp, args.cpu_sample, conf_min=args.conf_min,
-                           capacity_sps=synth.sps_table(R * (gamma + 1) + 1) if args.capacity else None,
-                           sts=(synth.make_calibration(7000 + args.config, R, gamma)[0],
-                                *synth.make_calibration(7100 + args.config, 20000, gamma)[:2]) if args.sts else None)
-
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -400,6 +582,7 @@ def main():
         "data": "synthetic (seeded; logits, Markov factors, uniforms and confidences drawn by synth)",
         "config": {
             "workload": f"config{args.config}: R={R} gamma={gamma} V={V} r={rank} {inp.wdtype} W1/W2, fp32 logits, "
+                        + (f"{args.policy} requests, " if args.policy else "")
                         + ("confidence calibrated by sequential temperature scaling, " if args.sts else "")
                         + (f"static confidence cutoff conf_min={args.conf_min} ({n_rows} rows)" if cutoff else
                            f"hardware-aware capacity K={K_sched} from the previous step's survival and a "
@@ -419,6 +602,8 @@ def main():
         "wall_s_timed_loop": round(wall_cold, 4),
         "step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(step_ms, [10, 50, 90])],
         "warm_back_to_back": None if warm is None else {k: round(v, 4) for k, v in warm.items()},
+        "calls_us": calls_us,
+        "acceptance": acceptance,
         "roofline": {
             "kernel": f"{kernel} (fused Markov bias GEMM + softmax statistics, one launch per draft position)",
             "bound": "hbm",
