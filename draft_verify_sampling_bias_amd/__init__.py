@@ -27,6 +27,7 @@ __all__ = [
     "dspark_capacity", "CapacityArgs", "dspark_sts_fit", "dspark_sts_apply", "StsFitArgs", "StsApplyArgs",
     "dspark_check", "InputCheckError", "CHECK_INPUTS", "BAD_TOKEN", "BAD_UNIFORM", "BAD_LENGTH",
     "BAD_CONFIDENCE", "WORKSPACE_HEADER", "dspark_schedule_workspace_size", "dspark_cutoff_workspace_size",
+    "dspark_draft_block_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
@@ -37,13 +38,14 @@ W_F32, W_BF16 = 0, 1
 CHECK_INPUTS = 1
 BAD_TOKEN, BAD_UNIFORM, BAD_LENGTH, BAD_CONFIDENCE = 1, 2, 4, 8
 WORKSPACE_HEADER = 256
+NOALLOC_SCRATCH_BYTES = 32 << 20   # the static workspace of dspark_draft_block_noalloc
 
 EXPORTED_SYMBOLS = (
     "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
     "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_schedule_rows",
     "dspark_status_string", "dspark_abi_version", "dspark_pack_w2", "dspark_w2_packed_bytes",
     "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply", "dspark_schedule_workspace_size",
-    "dspark_cutoff_workspace_size", "dspark_check",
+    "dspark_cutoff_workspace_size", "dspark_check", "dspark_draft_block_noalloc",
 )
 
 
@@ -143,6 +145,7 @@ def _load():
     L.dspark_cutoff_workspace_size.argtypes = [P(CutoffArgs), P(ctypes.c_size_t)]
     L.dspark_check.argtypes = [_p, _p, P(ctypes.c_uint32)]
     L.dspark_draft_block.argtypes = [P(DraftArgs)]
+    L.dspark_draft_block_noalloc.argtypes = [P(DraftArgs)]
     L.dspark_schedule.argtypes = [P(ScheduleArgs)]
     L.dspark_schedule_cutoff.argtypes = [P(CutoffArgs)]
     L.dspark_pack_w2.argtypes = [P(PackArgs)]
@@ -155,7 +158,8 @@ def _load():
     for f in ("dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",
               "dspark_schedule", "dspark_schedule_cutoff", "dspark_verify", "dspark_abi_version",
               "dspark_pack_w2", "dspark_capacity", "dspark_sts_fit", "dspark_sts_apply",
-              "dspark_schedule_workspace_size", "dspark_cutoff_workspace_size", "dspark_check"):
+              "dspark_schedule_workspace_size", "dspark_cutoff_workspace_size", "dspark_check",
+              "dspark_draft_block_noalloc"):
         getattr(L, f).restype = ctypes.c_int
     L.dspark_schedule_rows.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
     L.dspark_schedule_rows.restype = ctypes.c_int64
@@ -417,6 +421,35 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
     _check("dspark_draft_block", get_lib().dspark_draft_block(ctypes.byref(a)))
     if check_inputs and R > 0:
         _raise_on_check("dspark_draft_block", ws, stream)
+    return y, q_tok, q_stats
+
+
+def dspark_draft_block_noalloc(U, W1, W2, anchor, temp, u_draft, *, out, stream=None, W2_packed=None):
+    """dspark_draft_block with the library's static device workspace
+    (include/dspark.h, dspark_draft_block_noalloc): nothing is allocated, so
+    ``out`` = (y, q_tok, q_stats) must be given.  Calls that overlap in time
+    on one device share that workspace and race."""
+    torch = _torch()
+    dev = U.device
+    R, gamma, V = U.shape
+    rank = W1.shape[1]
+    wd = _wdtype(W1, W2)
+    _want(U, "U", torch.float32, (R, gamma, V), dev)
+    _want(W1, "W1", W1.dtype, (V, rank), dev)
+    _want(W2, "W2", W1.dtype, (V, rank), dev)
+    _want(anchor, "anchor", torch.int32, (R,), dev)
+    _want(temp, "temp", torch.float32, (R,), dev)
+    _want(u_draft, "u_draft", torch.float32, (R, gamma), dev)
+    y, q_tok, q_stats = out
+    _want(y, "y", torch.int32, (R, gamma), dev)
+    _want(q_tok, "q_tok", torch.float32, (R, gamma), dev)
+    _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
+    w2p, w2p_bytes = _w2_packed(W2_packed, dev, V, rank)
+    a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd,
+                  U=_ptr(U), W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp),
+                  u_draft=_ptr(u_draft), y=_ptr(y), q_tok=_ptr(q_tok), q_stats=_ptr(q_stats),
+                  stream=_stream(dev, stream), W2_packed=w2p, W2_packed_bytes=w2p_bytes)
+    _check("dspark_draft_block_noalloc", get_lib().dspark_draft_block_noalloc(ctypes.byref(a)))
     return y, q_tok, q_stats
 
 
