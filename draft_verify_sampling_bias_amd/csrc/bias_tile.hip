@@ -40,6 +40,9 @@
 namespace dspark {
 namespace {
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt not waited for
+constexpr int kVmcntZero = 0x0F70;
+
 // LDS-only workgroup barrier: orders LDS traffic without draining the
 // wavefront's outstanding global loads (a full __syncthreads() waits for
 // every in-flight prefetch).
@@ -56,13 +59,22 @@ struct ReqInfo {
   float c, Mq, iZq, Mp, iZp;
 };
 
-__device__ __forceinline__ ReqInfo fetch_info(const TileParams& p, int n, bool resid) {
+// The rows a draft position reads: request n's previous token at
+// prev_base[n * prev_stride], its base logits at U_base + n * U_stride.
+struct Pos {
+  const int32_t* prev_base;
+  int prev_stride;
+  const float* U_base;
+};
+__device__ __forceinline__ Pos pos_of(const TileParams& p) { return Pos{p.prev_base, p.prev_stride, p.U_base}; }
+
+__device__ __forceinline__ ReqInfo fetch_info(const TileParams& p, const Pos& ps, int n, bool resid) {
   ReqInfo ci{0, 0, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (n >= p.R) return ci;
   ci.c = temp_scale(p.temp[n]);
   if (!resid) {
     ci.act = 1;
-    ci.prev = p.prev_base[static_cast<int64_t>(n) * p.prev_stride];
+    ci.prev = ps.prev_base[static_cast<int64_t>(n) * ps.prev_stride];
   } else {
     const int32_t* inf = p.rs_info + 4 * static_cast<int64_t>(n);
     ci.act = inf[0];
@@ -83,8 +95,9 @@ __device__ __forceinline__ ReqInfo fetch_info(const TileParams& p, int n, bool r
   return ci;
 }
 
-__device__ __forceinline__ const float* u_row(const TileParams& p, const ReqInfo& ci, int n, bool resid) {
-  return resid ? p.U + static_cast<int64_t>(ci.urow) * p.V : p.U_base + static_cast<int64_t>(n) * p.U_stride;
+__device__ __forceinline__ const float* u_row(const TileParams& p, const Pos& ps, const ReqInfo& ci, int n,
+                                             bool resid) {
+  return resid ? p.U + static_cast<int64_t>(ci.urow) * p.V : ps.U_base + static_cast<int64_t>(n) * p.U_stride;
 }
 
 // Four consecutive logits starting at v (clamped addresses; the caller masks).
@@ -103,11 +116,13 @@ __device__ __forceinline__ f32x4_t load4(const float* row, int v, int V) {
 // ---------------------------------------------------------------------------
 // 16-row path
 // ---------------------------------------------------------------------------
-template <int KS, bool RESID>
+// NB: request column blocks of 16 (1, 2 or 4: R <= 16, 32 or 64); the
+// columns past the batch are not computed.
+template <int KS, bool RESID, int NB>
 struct Seg16Regs {
   bf16x8_t w[KS];     // W2 rows vw + (lane & 15), k = 32 ks + 8 (lane >> 4) .. +8
-  f32x4_t u[4];       // U[request 16 nb + (lane & 15)][vw + 4 (lane >> 4) .. +4]
-  f32x4_t t[RESID ? 4 : 1];  // target values, residual mode
+  f32x4_t u[NB];      // U[request 16 nb + (lane & 15)][vw + 4 (lane >> 4) .. +4]
+  f32x4_t t[RESID ? NB : 1];  // target values, residual mode
 };
 
 // W2 fragment ks of segment [vw, vw + 16) for this lane: from the
@@ -129,9 +144,9 @@ __device__ __forceinline__ bf16x8_t seg16_w2_frag(const uint16_t* w2, int ks, in
 // Issues the loads of segment [vw, vw + 16).  No instruction touches the
 // loaded registers before the MFMA or the epilogue needs them (the rank and
 // vocabulary masks are applied at use).
-template <int KS, bool RESID, bool VEC4, bool PACKED>
-__device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s_ci, int vw, int lane,
-                                           Seg16Regs<KS, RESID>& f) {
+template <int KS, bool RESID, bool VEC4, bool PACKED, int NB>
+__device__ __forceinline__ void seg16_load(const TileParams& p, const Pos& ps, const ReqInfo* s_ci, int vw, int lane,
+                                           Seg16Regs<KS, RESID, NB>& f) {
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V, rank = p.rank;
   const uint16_t* w2 = seg16_w2<KS, PACKED>(p, vw, lane);
@@ -139,10 +154,10 @@ __device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s
   for (int ks = 0; ks < KS; ++ks) f.w[ks] = seg16_w2_frag<KS, PACKED>(w2, ks, lane, rank);
   const int vu = vw + kq * 4;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int nn = nb * 16 + l16;
     const ReqInfo& ci = s_ci[nn];
-    f.u[nb] = load4<VEC4>(u_row(p, ci, nn < p.R ? nn : 0, RESID), vu, V);
+    f.u[nb] = load4<VEC4>(u_row(p, ps, ci, nn < p.R ? nn : 0, RESID), vu, V);
     if (RESID) f.t[nb] = load4<VEC4>(p.target + static_cast<int64_t>(ci.trow) * V, vu, V);
   }
 }
@@ -150,31 +165,31 @@ __device__ __forceinline__ void seg16_load(const TileParams& p, const ReqInfo* s
 // B (H from LDS) is read one k-step ahead when DBUF, else just in time (the
 // draft kernel runs two wavefronts per SIMD, which cover the LDS latency,
 // and needs the registers).
-template <int KS, bool DBUF>
+template <int KS, bool DBUF, int NB>
 __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
-                                           f32x4_t (&acc)[4]) {
+                                           f32x4_t (&acc)[NB]) {
   constexpr int RS = KS * 32 + 8;
   const int l16 = lane & 15, kq = lane >> 4;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint16_t* h0 = Hs + l16 * RS + kq * 8;
-  u32x4_t b[DBUF ? 2 : 1][4];
-  if (DBUF) {
+  u32x4_t b[DBUF ? 2 : 1][NB];
+  if constexpr (DBUF) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
+    for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int cur = DBUF ? (ks & 1) : 0;
-    if (DBUF) {
+    if constexpr (DBUF) {
       if (ks + 1 < KS) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
       }
     } else {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
+      for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
     }
     // the empty asm pins the zeroing here: hoisted next to the load (across
     // the loop's back edge) it would wait on the whole prefetch
@@ -182,7 +197,7 @@ __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16
     asm volatile("" : "+v"(a));
     a = (ks * 32 + kq * 8 < rank) ? a : bf16x8_t{};
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb], 0, 0,
                                                         0);
     // keep the B reads one step ahead only: unrestricted hoisting of all of
@@ -195,10 +210,10 @@ __device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16
 // W2 fragment ks of segment [vw_next, vw_next + 16) (and, in the first
 // steps, its U / target values), so a load issue that stalls on a busy
 // memory pipeline holds up one k-step instead of a whole segment.
-template <int KS, bool RESID, bool VEC4, bool DBUF, bool PACKED>
+template <int KS, bool RESID, bool VEC4, bool DBUF, bool PACKED, int NB>
 __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
-                                              f32x4_t (&acc)[4], const TileParams& p, const ReqInfo* s_ci,
-                                              int vw_next, Seg16Regs<KS, RESID>& nx) {
+                                              f32x4_t (&acc)[NB], const TileParams& p, const Pos& ps,
+                                              const ReqInfo* s_ci, int vw_next, Seg16Regs<KS, RESID, NB>& nx) {
   constexpr int RS = KS * 32 + 8;
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V;
@@ -207,31 +222,31 @@ __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uin
   auto issue_u = [&](int nb) {
     const int nn = nb * 16 + l16;
     const ReqInfo& ci = s_ci[nn];
-    nx.u[nb] = load4<VEC4>(u_row(p, ci, nn < p.R ? nn : 0, RESID), vu, V);
+    nx.u[nb] = load4<VEC4>(u_row(p, ps, ci, nn < p.R ? nn : 0, RESID), vu, V);
     if (RESID) nx.t[nb] = load4<VEC4>(p.target + static_cast<int64_t>(ci.trow) * V, vu, V);
   };
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint16_t* h0 = Hs + l16 * RS + kq * 8;
-  u32x4_t b[DBUF ? 2 : 1][4];
-  if (DBUF) {
+  u32x4_t b[DBUF ? 2 : 1][NB];
+  if constexpr (DBUF) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
+    for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     nx.w[ks] = seg16_w2_frag<KS, PACKED>(w2n, ks, lane, rank);
-    if (ks < 4) issue_u(ks);
+    if (ks < NB) issue_u(ks);
     const int cur = DBUF ? (ks & 1) : 0;
-    if (DBUF) {
+    if constexpr (DBUF) {
       if (ks + 1 < KS) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
       }
     } else {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
+      for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
     }
     // the empty asm pins the zeroing here: hoisted next to the load (across
     // the loop's back edge) it would wait on the whole prefetch
@@ -239,27 +254,27 @@ __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uin
     asm volatile("" : "+v"(a));
     a = (ks * 32 + kq * 8 < rank) ? a : bf16x8_t{};
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
       acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb], 0, 0,
                                                         0);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int nb = KS; nb < 4; ++nb) issue_u(nb);  // fewer k-steps than U groups (rank <= 96)
+  for (int nb = KS; nb < NB; ++nb) issue_u(nb);  // fewer k-steps than U groups (rank <= 96)
 }
 
-// Per-lane copies of the request constants of the lane's four requests
+// Per-lane copies of the request constants of the lane's NB requests
 // (request 16 nb + (lane & 15)), kept in registers for the whole walk.
-template <bool RESID>
+template <bool RESID, int NB>
 struct LaneReq {
-  float c[4];  // log2(e) / T, 0 for greedy
-  float Mq[RESID ? 4 : 1], iZq[RESID ? 4 : 1], Mp[RESID ? 4 : 1], iZp[RESID ? 4 : 1];
+  float c[NB];  // log2(e) / T, 0 for greedy
+  float Mq[RESID ? NB : 1], iZq[RESID ? NB : 1], Mp[RESID ? NB : 1], iZp[RESID ? NB : 1];
 };
 
-template <bool RESID>
-__device__ __forceinline__ void lane_req(const ReqInfo* s_ci, int lane, LaneReq<RESID>& q) {
+template <bool RESID, int NB>
+__device__ __forceinline__ void lane_req(const ReqInfo* s_ci, int lane, LaneReq<RESID, NB>& q) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const ReqInfo ci = s_ci[nb * 16 + (lane & 15)];
     q.c[nb] = ci.c;
     if (RESID) {
@@ -276,14 +291,14 @@ __device__ __forceinline__ void lane_req(const ReqInfo* s_ci, int lane, LaneReq<
 // segment's record.  All four lanes hold the reduced record and all store it
 // (same value, same address); records of absent requests land in padding
 // rows of the workspace and are never read.
-template <int KS, bool RESID>
-__device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneReq<RESID>& q, int wt, int lane,
-                                               const Seg16Regs<KS, RESID>& f, const f32x4_t (&acc)[4]) {
+template <int KS, bool RESID, int NB>
+__device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneReq<RESID, NB>& q, int wt, int lane,
+                                               const Seg16Regs<KS, RESID, NB>& f, const f32x4_t (&acc)[NB]) {
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V;
   const int vb = wt * kSegSmall + kq * 4;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int nn = nb * 16 + l16;
     const float c = q.c[nb];
     f32x4_t s = acc[nb] + f.u[nb];
@@ -329,42 +344,24 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
 constexpr int kSeg16Waves = 4;     // residual mode: wavefronts per workgroup, one per SIMD
 constexpr int kSeg16DraftWaves = 8;  // draft mode: one workgroup per CU, two wavefronts per SIMD
 
-// Wavefront w of the grid handles segments w, w + W, w + 2W, ... (W = all
-// wavefronts), so at any moment the grid streams one contiguous stretch of
-// W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
-// each of 64 rows.
-template <int KS, bool RESID, bool VEC4, int WPB, bool PACKED>
-__device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci) {
+// Request info and H = W1[prev] for all requests of the 16-row path, into
+// LDS (the workgroup's first barrier comes after the info, the second after
+// H).  Every 16-byte load of this thread is issued before any is stored.
+template <int KS, bool RESID, int WPB, int NB>
+__device__ __forceinline__ void seg16_info_h(const TileParams& p, const Pos& ps, uint16_t* Hs, ReqInfo* s_ci) {
   constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
-  constexpr bool DBUF = RESID;     // see seg16_mfma
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int R = p.R, rank = p.rank;
-  const int n_seg = p.n_seg;
-
-  if (RESID) {
-    int any = 0;
-    for (int n = tid; n < R; n += WPB * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
-    if (!__syncthreads_or(any)) return;
-  }
-  // H = W1[prev] for all requests, gathered once per workgroup.  Every
-  // 16-byte load of this thread is issued before any is stored.
-  constexpr int G = KS * 4;  // 16-byte groups per H row
-  constexpr int kPer = kSmallMaxR * G / (WPB * 64);
-  // wavefront-uniform walk state (scalar registers, scalar branches)
-  const int n_waves = gridDim.x * WPB;
-  int sg = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(wave);
-  Seg16Regs<KS, RESID> fa, fb;
-  // draft mode: the first segment's W2 and U addresses depend on neither H
-  // nor the request info, so its loads go out first and are in flight
-  // while the request info and the H rows (prev -> W1[prev]) arrive
-  if (!RESID) seg16_load<KS, RESID, VEC4, PACKED>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
-  if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, tid, RESID);
+  constexpr int G = KS * 4;        // 16-byte groups per H row
+  constexpr int kPieces = NB * 16 * G;  // 16-byte pieces of the NB * 16 H rows
+  constexpr int kPer = (kPieces + WPB * 64 - 1) / (WPB * 64);
+  const int tid = threadIdx.x;
+  const int rank = p.rank;
+  if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, ps, tid, RESID);
   lds_barrier();
   u32x4_t val[kPer];
   const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int q = tid + j * WPB * 64;
+    const int q = min(tid + j * WPB * 64, kPieces - 1);
     const int nn = q / G, g = q - nn * G;
     val[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank + min(g * 8, rank - 8));
   }
@@ -373,55 +370,91 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
     const int q = tid + j * WPB * 64;
     const int nn = q / G, g = q - nn * G;
     const u32x4_t v = (g * 8 >= rank || !s_ci[nn].act) ? u32x4_t{0u, 0u, 0u, 0u} : val[j];
-    *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
+    if (kPieces % (WPB * 64) == 0 || q < kPieces) *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
   }
-  // residual mode: the barrier comes before the first segment's loads
-  // (their U and target rows come from the request info)
   lds_barrier();
+}
+
+// Wavefront w of the grid handles segments w, w + W, w + 2W, ... (W = all
+// wavefronts), so at any moment the grid streams one contiguous stretch of
+// W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
+// each of 64 rows.  `fa` holds the loads of the wavefront's first segment
+// sg, already issued; H and the request info are in LDS.
+template <int KS, bool RESID, bool VEC4, bool PACKED, int NB>
+__device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, const uint16_t* Hs,
+                                           const ReqInfo* s_ci, int sg, Seg16Regs<KS, RESID, NB>& fa,
+                                           Seg16Regs<KS, RESID, NB>& fb) {
+  constexpr bool DBUF = RESID;  // see seg16_mfma
+  const int lane = threadIdx.x & 63;
+  const int rank = p.rank, n_seg = p.n_seg;
+  const int n_waves = gridDim.x * (blockDim.x >> 6);
   if (sg >= n_seg) return;
-  LaneReq<RESID> lq;
-  lane_req<RESID>(s_ci, lane, lq);
-  if (RESID) seg16_load<KS, RESID, VEC4, PACKED>(p, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  LaneReq<RESID, NB> lq;
+  lane_req<RESID, NB>(s_ci, lane, lq);
   // Ping-pong prefetch, the next segment's loads interleaved with the
   // current one's k-steps.  The prefetch issued on a wavefront's last
   // segment re-reads segment n_seg - 1 (a cache hit, never used) so that the
   // load stream, and with it the compiler's wait counts, is the same every
   // trip.
   while (true) {
-    f32x4_t acc[4];
+    f32x4_t acc[NB];
     const int s1 = sg + n_waves;
-    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED>(fa.w, Hs, rank, lane, acc, p, s_ci, min(s1, n_seg - 1) * kSegSmall,
-                                                 fb);
-    seg16_epilogue<KS, RESID>(p, lq, sg, lane, fa, acc);
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB>(fa.w, Hs, rank, lane, acc, p, ps, s_ci,
+                                                 min(s1, n_seg - 1) * kSegSmall, fb);
+    seg16_epilogue<KS, RESID, NB>(p, lq, sg, lane, fa, acc);
     if (s1 >= n_seg) break;
     const int s2 = s1 + n_waves;
-    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED>(fb.w, Hs, rank, lane, acc, p, s_ci, min(s2, n_seg - 1) * kSegSmall,
-                                                 fa);
-    seg16_epilogue<KS, RESID>(p, lq, s1, lane, fb, acc);
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB>(fb.w, Hs, rank, lane, acc, p, ps, s_ci,
+                                                 min(s2, n_seg - 1) * kSegSmall, fa);
+    seg16_epilogue<KS, RESID, NB>(p, lq, s1, lane, fb, acc);
     if (s2 >= n_seg) break;
     sg = s2;
   }
 }
 
+template <int KS, bool RESID, bool VEC4, int WPB, bool PACKED, int NB>
+__device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = p.R, n_seg = p.n_seg;
+  if (RESID) {
+    int any = 0;
+    for (int n = tid; n < R; n += WPB * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
+    if (!__syncthreads_or(any)) return;
+  }
+  // wavefront-uniform walk state (scalar registers, scalar branches)
+  const int sg = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(wave);
+  Seg16Regs<KS, RESID, NB> fa, fb;
+  const Pos ps = pos_of(p);
+  // draft mode: the first segment's W2 and U addresses depend on neither H
+  // nor the request info, so its loads go out first and are in flight
+  // while the request info and the H rows (prev -> W1[prev]) arrive
+  if (!RESID) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  seg16_info_h<KS, RESID, WPB, NB>(p, ps, Hs, s_ci);
+  // residual mode: the first segment's loads come after the barrier (their
+  // U and target rows come from the request info)
+  if (RESID) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  seg16_walk<KS, RESID, VEC4, PACKED, NB>(p, ps, Hs, s_ci, sg, fa, fb);
+}
+
 // Draft mode: one workgroup of eight wavefronts per CU (two per SIMD, for
 // latency hiding, sharing one copy of H); compiled to fit 256 registers per
 // wavefront.
-template <int KS, bool VEC4, bool PACKED>
+template <int KS, bool VEC4, bool PACKED, int NB>
 __global__ void __launch_bounds__(kSeg16DraftWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bias_seg16(TileParams p) {
   constexpr int RS = KS * 32 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[NB * 16 * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves, PACKED>(p, Hs, s_ci);
+  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves, PACKED, NB>(p, Hs, s_ci);
 }
 
 // Residual mode (holds the target values too): one wavefront per SIMD.
-template <int KS, bool VEC4, bool PACKED>
+template <int KS, bool VEC4, bool PACKED, int NB>
 __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p) {
   constexpr int RS = KS * 32 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[kSmallMaxR * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[NB * 16 * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, true, VEC4, kSeg16Waves, PACKED>(p, Hs, s_ci);
+  bias_seg16_body<KS, true, VEC4, kSeg16Waves, PACKED, NB>(p, Hs, s_ci);
 }
 
 // ---------------------------------------------------------------------------
@@ -436,8 +469,6 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p)
 // two-stage LDS ring with one barrier per chunk.  Per-request values come
 // from an LDS window of 256 requests, loaded 16 chunks ahead.  Residual mode
 // visits only the requests listed by verify_finish.
-// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt not waited for
-constexpr int kVmcntZero = 0x0F70;
 constexpr int kWideWin = 256;                          // requests per window (one per thread)
 constexpr int kWideWinChunks = kWideWin / kWideChunk;  // chunks per window
 
@@ -985,7 +1016,7 @@ __global__ void __launch_bounds__(256) bias_seg32_f32(TileParams p) {
   const float* w2row = static_cast<const float*>(p.W2) + static_cast<int64_t>(min(v_a, V - 1)) * rank;
   for (int n0 = 0; n0 < R; n0 += NCH) {
     lds_barrier();
-    if (tid < NCH) s_ci[tid] = fetch_info(p, n0 + tid, RESID);
+    if (tid < NCH) s_ci[tid] = fetch_info(p, pos_of(p), n0 + tid, RESID);
     lds_barrier();
     {
       const float* w1 = static_cast<const float*>(p.W1);
@@ -998,7 +1029,7 @@ __global__ void __launch_bounds__(256) bias_seg32_f32(TileParams p) {
     float x[16];
     {
       const int n = n0 + lrow;
-      load16_32<VEC4>(u_row(p, s_ci[lrow], n < R ? n : 0, RESID), seg * kSegLarge + 4 * khalf, V, x);
+      load16_32<VEC4>(u_row(p, pos_of(p), s_ci[lrow], n < R ? n : 0, RESID), seg * kSegLarge + 4 * khalf, V, x);
     }
     lds_barrier();
     f32x16_t acc = f32x16_t{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1025,26 +1056,37 @@ void launch(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hipE
 }
 
 // KS = seg16_ksteps(rank): the packed W2 layout uses the same count
-template <bool RESID, bool VEC4, bool PACKED>
-void launch_seg16(const TileParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <bool RESID, bool VEC4, bool PACKED, int NB>
+void launch_seg16_nb(const TileParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (seg16_ksteps(p.rank)) {
     case 2:
-      if (RESID) launch(bias_seg16_res<2, VEC4, PACKED>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<2, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<2, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<2, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
       break;
     case 4:
-      if (RESID) launch(bias_seg16_res<4, VEC4, PACKED>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<4, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<4, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<4, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
       break;
     case 8:
-      if (RESID) launch(bias_seg16_res<8, VEC4, PACKED>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<8, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<8, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<8, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
       break;
     default:
-      if (RESID) launch(bias_seg16_res<16, VEC4, PACKED>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<16, VEC4, PACKED>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<16, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<16, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
       break;
   }
+}
+
+// request column blocks: as many as the batch needs (1, 2 or 4)
+template <bool RESID, bool VEC4, bool PACKED>
+void launch_seg16(const TileParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.R <= 16)
+    launch_seg16_nb<RESID, VEC4, PACKED, 1>(p, grid, block, s, e0, e1);
+  else if (p.R <= 32)
+    launch_seg16_nb<RESID, VEC4, PACKED, 2>(p, grid, block, s, e0, e1);
+  else
+    launch_seg16_nb<RESID, VEC4, PACKED, 4>(p, grid, block, s, e0, e1);
 }
 
 template <bool RESID, bool VEC4>

@@ -1,0 +1,224 @@
+// Device code of the per-request draft finish (finish.hip), written as one
+// request's finish by one workgroup so that any kernel can run it.
+//
+// The finish combines the segment records of the fused bias kernel into the
+// position's maximum, lowest argmax and normaliser Z, and for a sampled
+// request draws the token by inverse CDF with its uniform ("DSpark"
+// explainer sections 2 and 7: the block is drafted left to right from
+// q = softmax((U_k + B_k)/T); llama.cpp PR #25173: anchor-first,
+// bias(prev) = markov_w2 . markov_w1[prev]).
+#pragma once
+
+#include "dspark_device.h"
+#include "launchers.h"
+#include "plan.h"
+#include "sample_device.h"
+
+namespace dspark {
+
+// Rescan of one record segment: thread group i (NT / seg_rows lanes) owns
+// row v0 + i (256 threads: 16 lanes per row for 16-row segments, 8 for
+// 32-row, 4 for 64-row; 512 and 1024 threads: two and four times as many).
+template <int NT = 256>
+__device__ __forceinline__ int lanes_log2(int seg_rows) {
+  static_assert(NT == 256 || NT == 512 || NT == 1024, "finish workgroups of 256, 512 or 1024 threads");
+  constexpr int extra = NT == 1024 ? 2 : (NT == 512 ? 1 : 0);
+  return (seg_rows == kSegSmall ? 4 : (seg_rows == kSegLarge ? 3 : 2)) + extra;
+}
+constexpr int kMaxSegRows = 64;
+// threads per workgroup of the draft finish (bf16 weights, at most one
+// request per CU): its per-thread share of the record pass (n_seg / NT
+// records, read one after another) sets the location's latency
+constexpr int kDraftFinishThreads = 1024;
+
+// Segment records of one request staged in LDS: up to 2048 records (16 KiB,
+// several workgroups per CU) or 16384 (128 KiB, i.e. V up to 262144 with
+// 16-row, 524288 with 32-row or 1048576 with 64-row segments); larger
+// vocabularies read the records from global memory instead.
+constexpr int kStageSmall = 2048;
+constexpr int kStageRecs = 16384;
+constexpr int kStageBatchRecs = 10240;  // records in flight per workgroup while staging
+
+// Records are copied into LDS in batches of kStageBatchRecs (kStageBatchRecs
+// / NT loads per thread), every load of a batch issued before any is used
+// (one memory latency per batch).
+template <int NT = 256, int BATCH = kStageBatchRecs>
+struct StageBatch {
+  static constexpr int kLoads = BATCH / NT;
+  float2 r[kLoads];
+};
+
+template <int NT = 256, int BATCH = kStageBatchRecs>
+__device__ __forceinline__ void stage_issue(const float2* __restrict__ src, int n, int base,
+                                            StageBatch<NT, BATCH>& b) {
+#pragma unroll
+  for (int j = 0; j < StageBatch<NT, BATCH>::kLoads; ++j)
+    b.r[j] = src[min(base + j * NT + static_cast<int>(threadIdx.x), n - 1)];
+}
+
+// Stores a batch into LDS, folding each record into f(r).  No barrier.
+template <int NT = 256, int BATCH = kStageBatchRecs, class F>
+__device__ __forceinline__ void stage_commit(int n, int base, const StageBatch<NT, BATCH>& b, float2* dst, F f) {
+#pragma unroll
+  for (int j = 0; j < StageBatch<NT, BATCH>::kLoads; ++j) {
+    const int t = base + j * NT + static_cast<int>(threadIdx.x);
+    if (t < n) {
+      dst[t] = b.r[j];
+      f(b.r[j]);
+    }
+  }
+}
+
+// h = W1[prev, :] as fp32, split so that its loads can be in flight with
+// the record loads: hold() issues them into registers, commit() stores to
+// LDS (no barrier).
+template <typename WT, int NT = 256>
+struct HRow {
+  static constexpr int kPer = (DSPARK_MAX_RANK + NT - 1) / NT;
+  float v[kPer];
+  __device__ __forceinline__ void hold(const WT* W1, int prev, int rank) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = static_cast<int>(threadIdx.x) + j * NT;
+      v[j] = weight_at<WT>(W1, static_cast<int64_t>(prev) * rank + min(k, rank - 1));
+    }
+  }
+  __device__ __forceinline__ void commit(int rank, float* hs) const {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = static_cast<int>(threadIdx.x) + j * NT;
+      if (k < rank) hs[k] = v[j];
+    }
+  }
+};
+
+// Block-wide (max, lowest index) with one barrier; lm / li are used once.
+template <int NT = 256>
+__device__ __forceinline__ void block_amax_once(float& m, int& i, float* lm, int* li) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  wave_amax(m, i);
+  if (lane == 0) {
+    lm[wave] = m;
+    li[wave] = i;
+  }
+  __syncthreads();
+  m = lm[0];
+  i = li[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) amax_merge(m, i, lm[w], li[w]);
+}
+
+// LDS of one draft finish, besides the record staging buffer.
+struct FinishSmem {
+  float hs[DSPARK_MAX_RANK];
+  Loc2Scratch sh;
+  float e64[kMaxSegRows], s64[kMaxSegRows];
+};
+
+// The draft finish of request n at position p.k, by one workgroup of NT
+// threads: the position's maximum, lowest argmax and normaliser Z from the
+// segment records, and for a sampled request the inverse-CDF draw of its
+// uniform (two levels over the records, then a rescan of the chosen
+// segment).  Writes y, q_tok and q_stats of (n, k).  The caller separates
+// two calls on the same scratch with a workgroup barrier.
+// SEG: the segment rows when known at compile time (0: p.seg_rows).
+// Position k reads request n's previous token at prev_base[n * prev_stride]
+// and its base logits at U_base + n * p.U_stride.  With STAGE > 0 the
+// request's records (at most STAGE of them) are staged in srec (LDS), BATCH
+// records in flight at a time.
+template <typename WT, int STAGE, int NT, int SEG = 0, int BATCH = kStageBatchRecs>
+__device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, int k, const int32_t* prev_base,
+                                                 int prev_stride, const float* U_base, FinishSmem& sm,
+                                                 float2* srec) {
+  constexpr bool STAGED = STAGE > 0;
+  float* hs = sm.hs;
+  Loc2Scratch& sh = sm.sh;
+  float* e64 = sm.e64;
+  float* s64 = sm.s64;
+  const int tid = threadIdx.x;
+  const int V = p.V, n_seg = p.n_seg;
+  const float2* gfine = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
+  const float2* fine = STAGED ? srec : gfine;
+  const int64_t o = static_cast<int64_t>(n) * p.gamma + k;
+  // loads that depend on nothing go first; then the records, then W1[prev]
+  // (whose address waits only for prev), all in flight together
+  const float T = p.temp[n];
+  const int prev = clampi(prev_base[static_cast<int64_t>(n) * prev_stride], 0, V - 1);
+  const float u_raw = p.u_draft[o];
+  StageBatch<NT, BATCH> sb;
+  if (STAGED) stage_issue<NT, BATCH>(gfine, n_seg, 0, sb);
+  HRow<WT, NT> hrow;
+  hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
+  // maximum (greedy: with the lowest argmax carried in the records' second
+  // word; sampled: the second word is ignored), taken while staging
+  float m = -INFINITY;
+  int im = kIntMax;
+  auto fold = [&](float2 r) { amax_merge(m, im, r.x, __float_as_int(r.y)); };
+  if (STAGED) {
+    stage_commit<NT, BATCH>(n_seg, 0, sb, srec, fold);
+    for (int base = BATCH; base < n_seg; base += BATCH) {
+      stage_issue<NT, BATCH>(gfine, n_seg, base, sb);
+      stage_commit<NT, BATCH>(n_seg, base, sb, srec, fold);
+    }
+  } else {
+#pragma unroll 8
+    for (int t = tid; t < n_seg; t += NT) fold(gfine[t]);
+  }
+  hrow.commit(p.rank, hs);
+  block_amax_once<NT>(m, im, sh.fred, sh.ired);  // also orders the LDS stores above before the reads below
+  const float M = m;
+  const float c = temp_scale(T);
+  if (c == 0.0f) {
+    if (tid == 0) {
+      p.y[o] = clampi(im, 0, V - 1);
+      p.q_tok[o] = 1.0f;
+      p.q_stats[2 * o] = M;
+      p.q_stats[2 * o + 1] = 1.0f;
+    }
+    return;
+  }
+  const float u = clamp_uniform(u_raw);
+  // mass of segment t in units of 2^((. - M) c)
+  auto mass = [&](int t) {
+    const float2 r = fine[t];
+    return r.y * exp2_hw((r.x - M) * c);
+  };
+  const Located2 L = locate_blocked<NT>(n_seg, mass, u, &sh);
+  const int seg = L.seg < 0 ? 0 : L.seg;
+  const float ms = fine[seg].x;
+  const float th = L.fallback ? INFINITY : L.rem / exp2_hw((ms - M) * c);
+  const int seg_rows = SEG > 0 ? SEG : p.seg_rows;
+  const int lg = lanes_log2<NT>(seg_rows);
+  const int v0 = seg * seg_rows;
+  const int i = tid >> lg;
+  const int v = v0 + i;
+  // the row's base logit is loaded before the W2 row, so both are in flight
+  // together (clamped address; rows past V are masked below)
+  const float uv = U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
+  // lanes per row known at compile time when SEG is: fewer weight chunks per lane
+  constexpr int kMinLg = SEG > 0 ? (SEG == kSegSmall ? 4 : (SEG == kSegLarge ? 3 : 2)) + (NT == 1024 ? 2 : (NT == 512 ? 1 : 0)) : 2;
+  const float b = row_bias<WT, kMinLg>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);
+  if ((tid & ((1 << lg) - 1)) == 0) {
+    float s = -INFINITY, e = 0.0f;
+    if (v < V) {
+      s = uv + b;
+      e = exp2_hw((s - ms) * c);
+    }
+    e64[i] = e;
+    s64[i] = s;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int pos = pick64(e64, seg_rows, th);
+    if (tid == 0) {
+      const int yy = (pos >= 0) ? v0 + pos : min(v0, V - 1);
+      const float sy = (pos >= 0) ? s64[pos] : M;
+      p.y[o] = yy;
+      p.q_tok[o] = exp2_hw((sy - M) * c) / L.Z;
+      p.q_stats[2 * o] = M;
+      p.q_stats[2 * o + 1] = L.Z;
+    }
+  }
+}
+
+}  // namespace dspark

@@ -49,12 +49,9 @@ constexpr int kChunk = 4096;
 constexpr int kChunkFloats = 4;              // floats per (row, chunk) record
 constexpr std::size_t kWsAlign = 256;
 // Every draft and verify workspace (and a schedule workspace, which exists
-// only for the input checks) starts with a header: the error word of the
-// device input checks at byte 0, then per-launch arrival counters of the
-// kernels that combine their workgroups' results in the same launch.
+// only for the input checks) starts with a header holding the error word of
+// the device input checks at byte 0.
 constexpr std::size_t kHeaderBytes = DSPARK_WORKSPACE_HEADER;
-constexpr std::size_t kCounterOff = 64;  // first arrival counter (uint32)
-constexpr int kMaxCounters = (DSPARK_WORKSPACE_HEADER - 64) / 4;
 static_assert(DSPARK_WORKSPACE_HEADER % 256 == 0, "header keeps the workspace 256-byte aligned");
 
 // k-steps (32 ranks each) of the 16-row kernel for a rank: 2, 4, 8 or 16.

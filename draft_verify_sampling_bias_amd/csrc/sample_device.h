@@ -304,9 +304,11 @@ __device__ __forceinline__ float dot8(const Raw8& r, const float*, const float* 
 // consecutive lanes (row index = threadIdx.x >> lpr_log2, lpr_log2 >= 2).
 // Every lane of the group returns the same value.  A lane's weight loads are
 // all issued before any is used (at most DSPARK_MAX_RANK / 32 of them).
-template <typename WT>
+// MIN_LG: a lower bound of lpr_log2 known at compile time (bounds the
+// number of weight chunks a lane can hold, and so its registers).
+template <typename WT, int MIN_LG = 2>
 __device__ __forceinline__ float row_bias(const WT* W2, const float* hs, int rank, int v, int V, int lpr_log2) {
-  constexpr int kMaxChunks = DSPARK_MAX_RANK / 32;
+  constexpr int kMaxChunks = DSPARK_MAX_RANK / (8 << MIN_LG);
   const int lpr = 1 << lpr_log2;
   const int part = threadIdx.x & (lpr - 1);
   const WT* row = W2 + static_cast<int64_t>(min(v, V - 1)) * rank;
