@@ -46,6 +46,11 @@ Readings of points the pages leave open (each also listed in the design notes):
     count) and R + K verify rows; the causal greedy adds candidates while
     Theta strictly improves and stops at the first K with Theta(K+1) <=
     Theta(K); the throughput table and the (lagged) survival are inputs;
+  * the RNN head (the explainer names it beside the Markov head, without
+    equations): an Elman recurrence h_k = act(A h_{k-1} + W1[prev_k]) from
+    h_{-1} = 0, with the bias W2 h_k and act the identity or tanh; A = 0 with
+    the identity is exactly the Markov head.  A verify rebuilds q at a
+    rejected position from the draft's state there;
   * sequential temperature scaling: position k's temperature is the maximum-
     likelihood one of the Bernoulli model P(accept k | reached k) =
     sigmoid(z / tau_k) on the calibration blocks that reached k (every
@@ -66,6 +71,7 @@ import numpy as np
 __all__ = [
     "NEAR", "widen", "markov_bias", "inverse_cdf", "draft_block", "survival",
     "schedule", "schedule_cutoff", "capacity", "verify", "DraftResult", "ScheduleResult",
+    "rnn_state", "rnn_draft_block", "ACT_IDENTITY", "ACT_TANH",
     "VerifyResult", "CapacityResult", "sts_fit", "sts_apply", "CalibrationResult",
     "STS_BETA_MIN", "STS_BETA_MAX",
 ]
@@ -148,6 +154,21 @@ class DraftResult:
     q_stats: np.ndarray      # fp64 [R, gamma, 2]  (max s, Z)
     flags: dict = field(default_factory=dict)   # (r, k) -> kind
     s: Optional[dict] = None                    # (r, k) -> fp64 biased logits, if kept
+    h: Optional[np.ndarray] = None              # fp64 [R, gamma, rank]: RNN head states
+
+
+def _draw_position(s, T, u):
+    """The draft decision of one position from its biased logits s: greedy
+    takes the lowest-index argmax; sampled draws by inverse CDF from
+    exp(s/T - max) with uniform u.  Returns (y, q_tok, (max s, Z), flag)."""
+    Ms = float(s.max())
+    if _is_greedy(T):
+        yk, near = _argmax_with_gap(s)
+        return yk, 1.0, (Ms, 1.0), ("draft-near-tie" if near else None)
+    x = s / _sample_T(T)
+    w = np.exp(x - x.max())
+    yk, Z, near = inverse_cdf(w, float(u))
+    return yk, float(w[yk]) / Z, (Ms, Z), ("draft-cdf-boundary" if near else None)
 
 
 def draft_block(U, W1, W2, wdtype, anchor, temp, u_draft, *,
@@ -181,25 +202,74 @@ def draft_block(U, W1, W2, wdtype, anchor, temp, u_draft, *,
             s = U[r, k].astype(np.float64) + B[i]
             if keep_s:
                 kept[(r, k)] = s
-            T = float(temp[r])
-            Ms = float(s.max())
-            if _is_greedy(T):
-                yk, near = _argmax_with_gap(s)
-                y[r, k] = yk
-                q_tok[r, k] = 1.0
-                q_stats[r, k] = (Ms, 1.0)
-                if near:
-                    flags[(r, k)] = "draft-near-tie"
-            else:
-                x = s / _sample_T(T)
-                w = np.exp(x - x.max())
-                yk, Z, near = inverse_cdf(w, float(u_draft[r, k]))
-                y[r, k] = yk
-                q_tok[r, k] = float(w[yk]) / Z
-                q_stats[r, k] = (Ms, Z)
-                if near:
-                    flags[(r, k)] = "draft-cdf-boundary"
+            y[r, k], q_tok[r, k], q_stats[r, k], flag = _draw_position(s, float(temp[r]), u_draft[r, k])
+            if flag:
+                flags[(r, k)] = flag
     return DraftResult(y=y, q_tok=q_tok, q_stats=q_stats, flags=flags, s=kept)
+
+
+#: activations of the RNN head's state update
+ACT_IDENTITY, ACT_TANH = 0, 1
+
+
+def rnn_state(A_64: np.ndarray, h_prev: np.ndarray, w1_row: np.ndarray, act: int) -> np.ndarray:
+    """One step of the RNN head's in-block state: act(A h_prev + W1[prev]).
+
+    The explainer (section 7) names an RNN head beside the Markov head: it
+    carries a longer in-block state through the sampled prefix instead of
+    conditioning on the previous token alone.  The pages give no equations;
+    this is the plain Elman recurrence with the Markov head's embedding W1 as
+    input weights and a recurrence matrix A (rank x rank), the state starting
+    at zero, so that A = 0 with the identity activation is exactly the Markov
+    head (h = W1[prev])."""
+    z = A_64 @ h_prev + w1_row
+    if act == ACT_TANH:
+        return np.tanh(z)
+    if act == ACT_IDENTITY:
+        return z
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def rnn_draft_block(U, W1, W2, A, wdtype, act, anchor, temp, u_draft, *,
+                    requests: Optional[Sequence[int]] = None,
+                    prev_override: Optional[np.ndarray] = None,
+                    keep_s: bool = False) -> DraftResult:
+    """Draft one block left to right with the RNN head.
+
+    For each request the state starts at h = 0; at k = 0 .. gamma-1:
+    prev = anchor at k = 0, else the token drafted at k-1 (or
+    prev_override[r, k-1]); h = act(A h + W1[prev]); s = U_k + W2 h; then
+    the same draw as the Markov head (explainer section 7: the sequential
+    head corrects the parallel backbone's base logits position by position
+    with a prefix-dependent bias).  The states are returned in .h [R, gamma,
+    rank] (the verify rebuilds q at a rejected position from them)."""
+    U = np.asarray(U)
+    R, gamma, V = U.shape
+    reqs = list(range(R)) if requests is None else [int(r) for r in requests]
+    W1_64, W2_64, A_64 = widen(W1, wdtype), widen(W2, wdtype), widen(A, wdtype)
+    rank = W1_64.shape[1]
+    y = np.full((R, gamma), -1, dtype=np.int32)
+    q_tok = np.full((R, gamma), np.nan)
+    q_stats = np.full((R, gamma, 2), np.nan)
+    hs = np.full((R, gamma, rank), np.nan)
+    flags = {}
+    kept = {} if keep_s else None
+    for r in reqs:
+        h = np.zeros(rank)
+        for k in range(gamma):
+            if k == 0:
+                prev = int(anchor[r])
+            else:
+                prev = int(prev_override[r, k - 1]) if prev_override is not None else int(y[r, k - 1])
+            h = rnn_state(A_64, h, W1_64[prev], act)
+            hs[r, k] = h
+            s = U[r, k].astype(np.float64) + W2_64 @ h
+            if keep_s:
+                kept[(r, k)] = s
+            y[r, k], q_tok[r, k], q_stats[r, k], flag = _draw_position(s, float(temp[r]), u_draft[r, k])
+            if flag:
+                flags[(r, k)] = flag
+    return DraftResult(y=y, q_tok=q_tok, q_stats=q_stats, flags=flags, s=kept, h=hs)
 
 
 def survival(c) -> np.ndarray:
@@ -459,7 +529,8 @@ def _softmax_T(row: np.ndarray, T: float) -> np.ndarray:
 
 
 def verify(target_rows, row_offsets, U, W1, W2, wdtype, anchor, y, q_tok, temp,
-           u_accept, u_final, *, requests: Optional[Sequence[int]] = None) -> VerifyResult:
+           u_accept, u_final, *, requests: Optional[Sequence[int]] = None,
+           h_states: Optional[np.ndarray] = None) -> VerifyResult:
     """Verify drafted blocks against target logits.
 
     Request r owns target rows off[r] .. off[r+1]-1; its verify length is
@@ -474,7 +545,9 @@ def verify(target_rows, row_offsets, U, W1, W2, wdtype, anchor, y, q_tok, temp,
     prev = anchor (j = 0) or y_{j-1}.  Greedy requests accept iff the draft is
     the target argmax, and emit the argmax as correction or bonus, which makes
     the output identical to target-only greedy decoding (llama.cpp PR,
-    "Losslessness")."""
+    "Losslessness").  With ``h_states`` (the RNN head's states of the
+    draft, [R, gamma, rank]) the drafter's bias at position n is W2 h_n
+    instead of the Markov bias of prev."""
     target_rows = np.asarray(target_rows)
     off = np.asarray(row_offsets, dtype=np.int64)
     R = len(off) - 1
@@ -517,8 +590,12 @@ def verify(target_rows, row_offsets, U, W1, W2, wdtype, anchor, y, q_tok, temp,
             else:
                 if W1_64 is None:
                     W1_64, W2_64 = widen(W1, wdtype), widen(W2, wdtype)
-                prev = int(anchor[r]) if n == 0 else int(y[r, n - 1])
-                s = np.asarray(U[r, n], dtype=np.float64) + markov_bias(W1_64, W2_64, [prev])[0]
+                if h_states is not None:
+                    B = W2_64 @ np.asarray(h_states[r, n], dtype=np.float64)
+                else:
+                    prev = int(anchor[r]) if n == 0 else int(y[r, n - 1])
+                    B = markov_bias(W1_64, W2_64, [prev])[0]
+                s = np.asarray(U[r, n], dtype=np.float64) + B
                 q = _softmax_T(s, T)
                 p = _softmax_T(t, T)
                 w = np.maximum(0.0, p - q)
