@@ -233,6 +233,7 @@ def rnn_state(A_64: np.ndarray, h_prev: np.ndarray, w1_row: np.ndarray, act: int
 def rnn_draft_block(U, W1, W2, A, wdtype, act, anchor, temp, u_draft, *,
                     requests: Optional[Sequence[int]] = None,
                     prev_override: Optional[np.ndarray] = None,
+                    state_override: Optional[np.ndarray] = None,
                     keep_s: bool = False) -> DraftResult:
     """Draft one block left to right with the RNN head.
 
@@ -242,7 +243,12 @@ def rnn_draft_block(U, W1, W2, A, wdtype, act, anchor, temp, u_draft, *,
     the same draw as the Markov head (explainer section 7: the sequential
     head corrects the parallel backbone's base logits position by position
     with a prefix-dependent bias).  The states are returned in .h [R, gamma,
-    rank] (the verify rebuilds q at a rejected position from them)."""
+    rank] (the verify rebuilds q at a rejected position from them).
+
+    state_override [R, gamma, rank] teacher-forces the state as prev_override
+    does the tokens: position k then steps from state_override[r, k-1]
+    (.h[r, k] is that one step) and draws from s = U_k + W2
+    state_override[r, k]."""
     U = np.asarray(U)
     R, gamma, V = U.shape
     reqs = list(range(R)) if requests is None else [int(r) for r in requests]
@@ -261,9 +267,12 @@ def rnn_draft_block(U, W1, W2, A, wdtype, act, anchor, temp, u_draft, *,
                 prev = int(anchor[r])
             else:
                 prev = int(prev_override[r, k - 1]) if prev_override is not None else int(y[r, k - 1])
+                if state_override is not None:
+                    h = np.asarray(state_override[r, k - 1], dtype=np.float64)
             h = rnn_state(A_64, h, W1_64[prev], act)
             hs[r, k] = h
-            s = U[r, k].astype(np.float64) + W2_64 @ h
+            h_draw = h if state_override is None else np.asarray(state_override[r, k], dtype=np.float64)
+            s = U[r, k].astype(np.float64) + W2_64 @ h_draw
             if keep_s:
                 kept[(r, k)] = s
             y[r, k], q_tok[r, k], q_stats[r, k], flag = _draw_position(s, float(temp[r]), u_draft[r, k])

@@ -211,3 +211,39 @@ def test_exhaustive_v8_lossless_rnn_head():
                 for t, ln in probs(pc).items():
                     z[t] += qv * (1.0 - tau) * ln
         np.testing.assert_allclose(z, p, atol=1e-9)
+
+
+def test_state_override_teacher_forces_one_step():
+    """state_override: given the oracle's own states it changes nothing; given
+    other states, each .h[r, k] is one recurrence step (tanh written out per
+    entry) from the forced state at k-1, and the draw at k is that of the
+    Markov-style bias W2 . forced state (a Markov draw with W1 replaced by the
+    forced states as embedding rows)."""
+    U, W1, W2, A, anc, temp, ud = _rand(4, 3, 4, 120, 8)
+    d = oracle.rnn_draft_block(U, W1, W2, A, "f32", oracle.ACT_TANH, anc, temp, ud)
+    same = oracle.rnn_draft_block(U, W1, W2, A, "f32", oracle.ACT_TANH, anc, temp, ud,
+                                  prev_override=d.y, state_override=d.h)
+    np.testing.assert_array_equal(same.y, d.y)
+    np.testing.assert_allclose(same.h, d.h, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(same.q_tok, d.q_tok, rtol=1e-13)
+    # fp32 values, so that the Markov draft below (whose "f32" weights are
+    # taken as fp32) sees the same rows
+    forced = np.random.default_rng(9).uniform(-1, 1, d.h.shape).astype(np.float32).astype(np.float64)
+    f = oracle.rnn_draft_block(U, W1, W2, A, "f32", oracle.ACT_TANH, anc, temp, ud,
+                               prev_override=d.y, state_override=forced)
+    A64, W164, W264 = (x.astype(np.float64) for x in (A, W1, W2))
+    for r in range(3):
+        for k in range(4):
+            prev = anc[r] if k == 0 else d.y[r, k - 1]
+            hp = np.zeros(8) if k == 0 else forced[r, k - 1]
+            want = [math.tanh(sum(A64[j, i] * hp[i] for i in range(8)) + W164[prev, j]) for j in range(8)]
+            np.testing.assert_allclose(f.h[r, k], want, rtol=0, atol=1e-14)
+            # the draw at k: a one-position Markov draft whose embedding row
+            # for the anchor is the forced state
+            emb = np.zeros((120, 8))
+            emb[0] = forced[r, k]
+            m = oracle.draft_block(U[r:r + 1, k:k + 1], emb, W264, "f32", np.array([0], np.int32),
+                                   temp[r:r + 1], ud[r:r + 1, k:k + 1])
+            assert f.y[r, k] == m.y[0, 0]
+            np.testing.assert_allclose(f.q_tok[r, k], m.q_tok[0, 0], rtol=1e-13)
+            np.testing.assert_allclose(f.q_stats[r, k], m.q_stats[0, 0], rtol=1e-13)
