@@ -27,12 +27,16 @@ __all__ = [
     "dspark_capacity", "CapacityArgs", "dspark_sts_fit", "dspark_sts_apply", "StsFitArgs", "StsApplyArgs",
     "dspark_check", "InputCheckError", "CHECK_INPUTS", "BAD_TOKEN", "BAD_UNIFORM", "BAD_LENGTH",
     "BAD_CONFIDENCE", "WORKSPACE_HEADER", "dspark_schedule_workspace_size", "dspark_cutoff_workspace_size",
-    "dspark_draft_block_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "dspark_draft_block_noalloc", "NOALLOC_SCRATCH_BYTES", "HEAD_MARKOV", "HEAD_RNN", "ACT_IDENTITY",
+    "ACT_TANH", "ABI_VERSION",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdspark.so")
 
 W_F32, W_BF16 = 0, 1
+HEAD_MARKOV, HEAD_RNN = 0, 1      # dspark_head
+ACT_IDENTITY, ACT_TANH = 0, 1     # dspark_act
+ABI_VERSION = 3                   # DSPARK_ABI_VERSION these structs follow
 
 # flags and input-check bits (include/dspark.h)
 CHECK_INPUTS = 1
@@ -83,7 +87,8 @@ class DraftArgs(ctypes.Structure):
                 ("U", _p), ("W1", _p), ("W2", _p), ("anchor", _p), ("temp", _p), ("u_draft", _p),
                 ("y", _p), ("q_tok", _p), ("q_stats", _p), ("workspace", _p),
                 ("workspace_bytes", ctypes.c_size_t), ("stream", _p), ("prof_events", _p), ("W2_packed", _p),
-                ("W2_packed_bytes", ctypes.c_size_t)]
+                ("W2_packed_bytes", ctypes.c_size_t), ("head", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("A", _p), ("h", _p)]
 
 
 class ScheduleArgs(ctypes.Structure):
@@ -109,7 +114,8 @@ class VerifyArgs(ctypes.Structure):
                 ("U", _p), ("W1", _p), ("W2", _p), ("anchor", _p), ("temp", _p), ("y", _p), ("q_tok", _p),
                 ("q_stats", _p), ("u_accept", _p), ("u_final", _p), ("n_accept", _p), ("out_tok", _p),
                 ("p_tok", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t), ("stream", _p),
-                ("W2_packed", _p), ("W2_packed_bytes", ctypes.c_size_t)]
+                ("W2_packed", _p), ("W2_packed_bytes", ctypes.c_size_t), ("head", ctypes.c_int32),
+                ("h", _p)]
 
 
 class CapacityArgs(ctypes.Structure):
@@ -166,6 +172,9 @@ def _load():
     L.dspark_status_string.argtypes = [ctypes.c_int]
     L.dspark_status_string.restype = ctypes.c_char_p
     L.dspark_abi_version.argtypes = []
+    got = L.dspark_abi_version()
+    if got != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has C ABI version {got}, these bindings follow {ABI_VERSION}: rebuild it")
     return L
 
 
@@ -304,18 +313,19 @@ def _sched_workspace(fn: str, args, device, workspace):
     return _workspace(int(n.value), device, workspace)
 
 
-def draft_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, flags: int = 0) -> int:
+def draft_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, flags: int = 0, *,
+                          head: int = 0, act: int = 0) -> int:
     a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wdtype,
-                  flags=flags)
+                  flags=flags, head=head, act=act)
     n = ctypes.c_size_t(0)
     _check("dspark_draft_workspace_size", get_lib().dspark_draft_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
 
 
 def verify_workspace_bytes(R: int, gamma: int, V: int, rank: int, wdtype: int, n_rows: int,
-                           flags: int = 0) -> int:
+                           flags: int = 0, *, head: int = 0) -> int:
     a = VerifyArgs(struct_size=ctypes.sizeof(VerifyArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wdtype,
-                   n_rows=n_rows, flags=flags)
+                   n_rows=n_rows, flags=flags, head=head)
     n = ctypes.c_size_t(0)
     _check("dspark_verify_workspace_size", get_lib().dspark_verify_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
@@ -365,8 +375,28 @@ def dspark_pack_w2(W2, *, out=None, stream=None):
     return out
 
 
+def _rnn_head(A, act, h, dev, R, gamma, rank, wd, *, alloc: bool):
+    """(head, act, A ptr, h tensor) of a draft call: the Markov head when A
+    is None, else the RNN head with recurrence A [rank, rank] (the weights'
+    dtype) and state output h [R, gamma, rank] fp32 (allocated if None and
+    ``alloc``)."""
+    torch = _torch()
+    if A is None:
+        if h is not None:
+            raise ValueError("h is the RNN head's state output: give A too")
+        return HEAD_MARKOV, ACT_IDENTITY, None, None
+    _want(A, "A", torch.bfloat16 if wd == W_BF16 else torch.float32, (rank, rank), dev)
+    if h is None:
+        if not alloc:
+            raise ValueError("the RNN head needs h (the state output) here")
+        h = torch.empty((R, gamma, rank), dtype=torch.float32, device=dev)
+    _want(h, "h", torch.float32, (R, gamma, rank), dev)
+    return HEAD_RNN, int(act), _ptr(A), h
+
+
 def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=None, stream=None,
-                       prof_events=None, W2_packed=None, check_inputs: bool = False):
+                       prof_events=None, W2_packed=None, check_inputs: bool = False, A=None, act: int = 1,
+                       h=None):
     """Draft gamma tokens per request (include/dspark.h, dspark_draft_block).
 
     U [R, gamma, V] fp32; W1, W2 [V, rank] bf16 or fp32; anchor [R] int32;
@@ -378,7 +408,10 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
     that kernel alone); ``W2_packed`` the output of dspark_pack_w2 for W2.
     ``check_inputs`` runs the device input checks (DSPARK_CHECK_INPUTS) and
     then waits for them: InputCheckError if an input is outside the
-    contract (debug only: it synchronises)."""
+    contract (debug only: it synchronises).  ``A`` selects the RNN head
+    (DSPARK_HEAD_RNN) with recurrence A [rank, rank] and activation ``act``
+    (ACT_IDENTITY / ACT_TANH); the call then returns the states h [R, gamma,
+    rank] fp32 as a fourth value (written into ``h`` if given)."""
     torch = _torch()
     dev = U.device
     R, gamma, V = U.shape
@@ -402,7 +435,8 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
             _want(y, "y", torch.int32, (R, gamma), dev)
             _want(q_tok, "q_tok", torch.float32, (R, gamma), dev)
             _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
-        nbytes = draft_workspace_bytes(R, gamma, V, rank, wd, flags)
+        head, act_v, a_ptr, h = _rnn_head(A, act, h, dev, R, gamma, rank, wd, alloc=True)
+        nbytes = draft_workspace_bytes(R, gamma, V, rank, wd, flags, head=head, act=act_v)
         ws = _workspace(nbytes, dev, workspace)
     ev_arr = None
     if prof_events is not None:
@@ -417,18 +451,23 @@ def dspark_draft_block(U, W1, W2, anchor, temp, u_draft, *, out=None, workspace=
                   workspace=_ptr(ws), workspace_bytes=ws.numel() * ws.element_size(),
                   stream=_stream(dev, stream),
                   prof_events=ctypes.cast(ev_arr, ctypes.c_void_p) if ev_arr is not None else None,
-                  W2_packed=w2p, W2_packed_bytes=w2p_bytes)
+                  W2_packed=w2p, W2_packed_bytes=w2p_bytes, head=head, act=act_v, A=a_ptr,
+                  h=_ptr(h) if h is not None else None)
     _check("dspark_draft_block", get_lib().dspark_draft_block(ctypes.byref(a)))
     if check_inputs and R > 0:
         _raise_on_check("dspark_draft_block", ws, stream)
+    if head == HEAD_RNN:
+        return y, q_tok, q_stats, h
     return y, q_tok, q_stats
 
 
-def dspark_draft_block_noalloc(U, W1, W2, anchor, temp, u_draft, *, out, stream=None, W2_packed=None):
+def dspark_draft_block_noalloc(U, W1, W2, anchor, temp, u_draft, *, out, stream=None, W2_packed=None, A=None,
+                               act: int = 1, h=None):
     """dspark_draft_block with the library's static device workspace
     (include/dspark.h, dspark_draft_block_noalloc): nothing is allocated, so
-    ``out`` = (y, q_tok, q_stats) must be given.  Calls that overlap in time
-    on one device share that workspace and race."""
+    ``out`` = (y, q_tok, q_stats) must be given (and ``h`` with the RNN
+    head).  Calls that overlap in time on one device share that workspace
+    and race."""
     torch = _torch()
     dev = U.device
     R, gamma, V = U.shape
@@ -445,11 +484,15 @@ def dspark_draft_block_noalloc(U, W1, W2, anchor, temp, u_draft, *, out, stream=
     _want(q_tok, "q_tok", torch.float32, (R, gamma), dev)
     _want(q_stats, "q_stats", torch.float32, (R, gamma, 2), dev)
     w2p, w2p_bytes = _w2_packed(W2_packed, dev, V, rank)
+    head, act_v, a_ptr, h = _rnn_head(A, act, h, dev, R, gamma, rank, wd, alloc=False)
     a = DraftArgs(struct_size=ctypes.sizeof(DraftArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd,
                   U=_ptr(U), W1=_ptr(W1), W2=_ptr(W2), anchor=_ptr(anchor), temp=_ptr(temp),
                   u_draft=_ptr(u_draft), y=_ptr(y), q_tok=_ptr(q_tok), q_stats=_ptr(q_stats),
-                  stream=_stream(dev, stream), W2_packed=w2p, W2_packed_bytes=w2p_bytes)
+                  stream=_stream(dev, stream), W2_packed=w2p, W2_packed_bytes=w2p_bytes, head=head, act=act_v,
+                  A=a_ptr, h=_ptr(h) if h is not None else None)
     _check("dspark_draft_block_noalloc", get_lib().dspark_draft_block_noalloc(ctypes.byref(a)))
+    if head == HEAD_RNN:
+        return y, q_tok, q_stats, h
     return y, q_tok, q_stats
 
 
@@ -610,11 +653,12 @@ def dspark_sts_apply(z, tau, *, out=None, stream=None):
 
 
 def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final, *,
-                  out=None, workspace=None, stream=None, W2_packed=None, check_inputs: bool = False):
+                  out=None, workspace=None, stream=None, W2_packed=None, check_inputs: bool = False, h=None):
     """Accept / reject against target logits (include/dspark.h, dspark_verify).
 
     target [n_rows, V] fp32; row_offsets [R+1] int32; the draft inputs and
-    outputs; u_accept [R, gamma] fp32; u_final [R] fp32.  Returns
+    outputs; u_accept [R, gamma] fp32; u_final [R] fp32; ``h`` the RNN
+    head's states from dspark_draft_block (None: Markov head).  Returns
     (n_accept int32 [R], out_tok int32 [R], p_tok fp32 [R, gamma])."""
     torch = _torch()
     dev = target.device
@@ -636,6 +680,10 @@ def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stat
     _want(u_final, "u_final", torch.float32, (R,), dev)
     w2p, w2p_bytes = _w2_packed(W2_packed, dev, V, rank)
     flags = CHECK_INPUTS if check_inputs else 0
+    head = HEAD_MARKOV
+    if h is not None:
+        _want(h, "h", torch.float32, (R, gamma, rank), dev)
+        head = HEAD_RNN
     with _alloc_on(stream):
         if out is None:
             n_accept = torch.empty(R, dtype=torch.int32, device=dev)
@@ -646,7 +694,7 @@ def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stat
             _want(n_accept, "n_accept", torch.int32, (R,), dev)
             _want(out_tok, "out_tok", torch.int32, (R,), dev)
             _want(p_tok, "p_tok", torch.float32, (R, gamma), dev)
-        nbytes = verify_workspace_bytes(R, gamma, V, rank, wd, n_rows, flags)
+        nbytes = verify_workspace_bytes(R, gamma, V, rank, wd, n_rows, flags, head=head)
         ws = _workspace(nbytes, dev, workspace)
     a = VerifyArgs(struct_size=ctypes.sizeof(VerifyArgs), R=R, gamma=gamma, V=V, rank=rank, wdtype=wd, flags=flags,
                    n_rows=n_rows, target=_ptr(target), row_offsets=_ptr(row_offsets), U=_ptr(U),
@@ -654,7 +702,7 @@ def dspark_verify(target, row_offsets, U, W1, W2, anchor, temp, y, q_tok, q_stat
                    q_tok=_ptr(q_tok), q_stats=_ptr(q_stats), u_accept=_ptr(u_accept), u_final=_ptr(u_final),
                    n_accept=_ptr(n_accept), out_tok=_ptr(out_tok), p_tok=_ptr(p_tok), workspace=_ptr(ws),
                    workspace_bytes=ws.numel() * ws.element_size(), stream=_stream(dev, stream),
-                   W2_packed=w2p, W2_packed_bytes=w2p_bytes)
+                   W2_packed=w2p, W2_packed_bytes=w2p_bytes, head=head, h=_ptr(h) if h is not None else None)
     _check("dspark_verify", get_lib().dspark_verify(ctypes.byref(a)))
     if check_inputs and R > 0:
         _raise_on_check("dspark_verify", ws, stream)

@@ -30,7 +30,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
 SOURCES = ["plan.cpp", "api.hip", "bias_tile.hip", "finish.hip", "verify.hip", "schedule.hip", "pack.hip", "capacity.hip",
-           "calibrate.hip", "check.hip", "noalloc.hip"]
+           "calibrate.hip", "check.hip", "noalloc.hip", "rnn.hip"]
 
 
 def _compile(src: str, extra) -> str:

@@ -138,12 +138,37 @@ int dspark_draft_block(const dspark_draft_args* a) {
     if (st != DSPARK_OK) return st;
   }
 
+  // RNN head: the state of each position is computed first; the fused bias
+  // kernel and the finish then read it instead of W1[prev]
+  const bool rnn = a->head == DSPARK_HEAD_RNN;
+  RnnStateParams rp{};
+  if (rnn) {
+    rp.R = a->R;
+    rp.gamma = a->gamma;
+    rp.V = a->V;
+    rp.rank = a->rank;
+    rp.act = a->act;
+    rp.W1 = static_cast<const uint16_t*>(a->W1);
+    rp.A = static_cast<const uint16_t*>(a->A);
+    rp.anchor = a->anchor;
+    rp.y = a->y;
+    rp.h = a->h;
+    tp.h_stride = static_cast<int64_t>(a->gamma) * a->rank;
+    fp.hstate = a->h;
+  }
+
   const int cu = current_cu_count();
   for (int k = 0; k < a->gamma; ++k) {
     // prev = anchor for the first position, the token drafted just before otherwise
     tp.prev_base = (k == 0) ? a->anchor : a->y + (k - 1);
     tp.prev_stride = (k == 0) ? 1 : a->gamma;
     tp.U_base = a->U + static_cast<int64_t>(k) * a->V;
+    if (rnn) {
+      rp.k = k;
+      st = hip_status(launch_rnn_state(rp, s));
+      if (st != DSPARK_OK) return st;
+      tp.h_base = a->h + static_cast<int64_t>(k) * a->rank;
+    }
     hipEvent_t e0 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k]) : nullptr;
     hipEvent_t e1 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k + 1]) : nullptr;
     st = hip_status(launch_bias_tile(tp, a->wdtype, false, cu, s, e0, e1));
@@ -260,6 +285,7 @@ int dspark_verify(const dspark_verify_args* a) {
   vp.rs_info = ws_at<int32_t>(a->workspace, plan.rsinfo_off);
   vp.rs_stats = ws_at<float>(a->workspace, plan.rsstats_off);
   vp.rpart = ws_at<float>(a->workspace, plan.rpart_off);
+  if (a->head == DSPARK_HEAD_RNN) vp.hstate = a->h;
   if (plan.seg_rows == kSegWide) {
     vp.rs_count = ws_at<int32_t>(a->workspace, plan.rcount_off);
     vp.rs_list = ws_at<ResidualEntry>(a->workspace, plan.rlist_off);
@@ -310,6 +336,7 @@ int dspark_verify(const dspark_verify_args* a) {
   tp.t_rows = a->n_rows;
   tp.part = vp.rpart;
   tp.w2p = (plan.seg_rows == kSegSmall) ? static_cast<const uint16_t*>(a->W2_packed) : nullptr;
+  tp.h_base = vp.hstate;  // residual mode: row urow of the states
   st = hip_status(launch_bias_tile(tp, a->wdtype, true, current_cu_count(), s));
   if (st != DSPARK_OK) return st;
   return hip_status(launch_residual_finish(vp, a->wdtype, s));

@@ -65,8 +65,14 @@ struct Pos {
   const int32_t* prev_base;
   int prev_stride;
   const float* U_base;
+  // RNN head: the fp32 states (draft: request n's row at h_base + n *
+  // h_stride; residual: row urow of h_base)
+  const float* h_base;
+  int64_t h_stride;
 };
-__device__ __forceinline__ Pos pos_of(const TileParams& p) { return Pos{p.prev_base, p.prev_stride, p.U_base}; }
+__device__ __forceinline__ Pos pos_of(const TileParams& p) {
+  return Pos{p.prev_base, p.prev_stride, p.U_base, p.h_base, p.h_stride};
+}
 
 __device__ __forceinline__ ReqInfo fetch_info(const TileParams& p, const Pos& ps, int n, bool resid) {
   ReqInfo ci{0, 0, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -162,59 +168,21 @@ __device__ __forceinline__ void seg16_load(const TileParams& p, const Pos& ps, c
   }
 }
 
-// B (H from LDS) is read one k-step ahead when DBUF, else just in time (the
-// draft kernel runs two wavefronts per SIMD, which cover the LDS latency,
-// and needs the registers).
-template <int KS, bool DBUF, int NB>
-__device__ __forceinline__ void seg16_mfma(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
-                                           f32x4_t (&acc)[NB]) {
-  constexpr int RS = KS * 32 + 8;
-  const int l16 = lane & 15, kq = lane >> 4;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* h0 = Hs + l16 * RS + kq * 8;
-  u32x4_t b[DBUF ? 2 : 1][NB];
-  if constexpr (DBUF) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
-  }
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int cur = DBUF ? (ks & 1) : 0;
-    if constexpr (DBUF) {
-      if (ks + 1 < KS) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
-      }
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
-    }
-    // the empty asm pins the zeroing here: hoisted next to the load (across
-    // the loop's back edge) it would wait on the whole prefetch
-    bf16x8_t a = w[ks];
-    asm volatile("" : "+v"(a));
-    a = (ks * 32 + kq * 8 < rank) ? a : bf16x8_t{};
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb], 0, 0,
-                                                        0);
-    // keep the B reads one step ahead only: unrestricted hoisting of all of
-    // them exhausts the register file
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// seg16_mfma with the next segment's loads interleaved: k-step ks issues
-// W2 fragment ks of segment [vw_next, vw_next + 16) (and, in the first
-// steps, its U / target values), so a load issue that stalls on a busy
-// memory pipeline holds up one k-step instead of a whole segment.
-template <int KS, bool RESID, bool VEC4, bool DBUF, bool PACKED, int NB>
+// The segment's MFMAs (H from LDS), with the next segment's loads
+// interleaved: k-step ks issues W2 fragment ks of segment [vw_next,
+// vw_next + 16) (and, in the first steps, its U / target values), so a load
+// issue that stalls on a busy memory pipeline holds up one k-step instead of
+// a whole segment.  B (H) is read one k-step ahead when DBUF, else just in
+// time (the draft kernel runs two wavefronts per SIMD, which cover the LDS
+// latency, and needs the registers).  SPLIT: H is two bf16 planes (hi, lo:
+// an fp32 state), and each k-step runs one MFMA per plane.
+template <int KS, bool RESID, bool VEC4, bool DBUF, bool PACKED, int NB, bool SPLIT>
 __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uint16_t* Hs, int rank, int lane,
                                               f32x4_t (&acc)[NB], const TileParams& p, const Pos& ps,
                                               const ReqInfo* s_ci, int vw_next, Seg16Regs<KS, RESID, NB>& nx) {
   constexpr int RS = KS * 32 + 8;
+  constexpr int kPlane = NB * 16 * RS;  // offset of the lo plane (SPLIT)
+  constexpr int NP = SPLIT ? 2 : 1;
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V;
   const uint16_t* w2n = seg16_w2<KS, PACKED>(p, vw_next, lane);
@@ -228,10 +196,13 @@ __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uin
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint16_t* h0 = Hs + l16 * RS + kq * 8;
-  u32x4_t b[DBUF ? 2 : 1][NB];
+  u32x4_t b[DBUF ? 2 : 1][NP][NB];
   if constexpr (DBUF) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS);
+    for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        b[0][pl][nb] = *reinterpret_cast<const u32x4_t*>(h0 + pl * kPlane + nb * 16 * RS);
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -241,12 +212,18 @@ __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uin
     if constexpr (DBUF) {
       if (ks + 1 < KS) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          b[cur ^ 1][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + (ks + 1) * 32);
+        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            b[cur ^ 1][pl][nb] =
+                *reinterpret_cast<const u32x4_t*>(h0 + pl * kPlane + nb * 16 * RS + (ks + 1) * 32);
       }
     } else {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4_t*>(h0 + nb * 16 * RS + ks * 32);
+      for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          b[0][pl][nb] = *reinterpret_cast<const u32x4_t*>(h0 + pl * kPlane + nb * 16 * RS + ks * 32);
     }
     // the empty asm pins the zeroing here: hoisted next to the load (across
     // the loop's back edge) it would wait on the whole prefetch
@@ -254,9 +231,11 @@ __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uin
     asm volatile("" : "+v"(a));
     a = (ks * 32 + kq * 8 < rank) ? a : bf16x8_t{};
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[cur][nb]), acc[nb], 0, 0,
-                                                        0);
+    for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[cur][pl][nb]), acc[nb],
+                                                          0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
@@ -344,10 +323,62 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
 constexpr int kSeg16Waves = 4;     // residual mode: wavefronts per workgroup, one per SIMD
 constexpr int kSeg16DraftWaves = 8;  // draft mode: one workgroup per CU, two wavefronts per SIMD
 
+// H of the RNN head: request nn's fp32 state row (draft mode: h_base +
+// nn * h_stride; residual mode: row urow of h_base, stride rank) split into
+// a hi plane bf16(h) and a lo plane bf16(h - hi).  The states are stored as
+// double-bf16 values (rnn.hip), so hi + lo == h exactly and the two MFMAs
+// per k-step compute W2 h with exact products.
+// Rows of inactive requests and groups past the rank are zero.  The caller
+// has stored the request info (s_ci) and passed a barrier.
+template <int KS, bool RESID, int WPB, int NB>
+__device__ __forceinline__ void seg16_state_h(const TileParams& p, const Pos& ps, uint16_t* Hs,
+                                              const ReqInfo* s_ci) {
+  constexpr int RS = KS * 32 + 8;
+  constexpr int G = KS * 4;
+  constexpr int kPieces = NB * 16 * G;
+  constexpr int kPer = (kPieces + WPB * 64 - 1) / (WPB * 64);
+  constexpr int kPlane = NB * 16 * RS;
+  const int tid = threadIdx.x;
+  const int rank = p.rank;
+  f32x4_t va[kPer], vb[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = min(tid + j * WPB * 64, kPieces - 1);
+    const int nn = q / G, g = q - nn * G;
+    const int64_t row = RESID ? static_cast<int64_t>(s_ci[nn].urow) * rank
+                              : static_cast<int64_t>(nn < p.R ? nn : 0) * ps.h_stride;
+    const float* h = ps.h_base + row + min(g * 8, rank - 8);
+    va[j] = *reinterpret_cast<const f32x4_t*>(h);
+    vb[j] = *reinterpret_cast<const f32x4_t*>(h + 4);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = tid + j * WPB * 64;
+    const int nn = q / G, g = q - nn * G;
+    const bool zero = g * 8 >= rank || !s_ci[nn].act;
+    u32x4_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = e < 2 ? va[j][2 * e] : vb[j][2 * e - 4];
+      const float x1 = e < 2 ? va[j][2 * e + 1] : vb[j][2 * e - 3];
+      const uint32_t h0 = bf16_rne_bits(x0), h1 = bf16_rne_bits(x1);
+      const uint32_t l0 = bf16_rne_bits(x0 - __uint_as_float(h0 << 16));
+      const uint32_t l1 = bf16_rne_bits(x1 - __uint_as_float(h1 << 16));
+      hi[e] = zero ? 0u : (h0 | (h1 << 16));
+      lo[e] = zero ? 0u : (l0 | (l1 << 16));
+    }
+    if (kPieces % (WPB * 64) == 0 || q < kPieces) {
+      *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = hi;
+      *reinterpret_cast<u32x4_t*>(&Hs[kPlane + nn * RS + g * 8]) = lo;
+    }
+  }
+  lds_barrier();
+}
+
 // Request info and H = W1[prev] for all requests of the 16-row path, into
 // LDS (the workgroup's first barrier comes after the info, the second after
 // H).  Every 16-byte load of this thread is issued before any is stored.
-template <int KS, bool RESID, int WPB, int NB>
+template <int KS, bool RESID, int WPB, int NB, bool SPLIT>
 __device__ __forceinline__ void seg16_info_h(const TileParams& p, const Pos& ps, uint16_t* Hs, ReqInfo* s_ci) {
   constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
   constexpr int G = KS * 4;        // 16-byte groups per H row
@@ -357,6 +388,10 @@ __device__ __forceinline__ void seg16_info_h(const TileParams& p, const Pos& ps,
   const int rank = p.rank;
   if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, ps, tid, RESID);
   lds_barrier();
+  if constexpr (SPLIT) {
+    seg16_state_h<KS, RESID, WPB, NB>(p, ps, Hs, s_ci);
+    return;
+  }
   u32x4_t val[kPer];
   const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
 #pragma unroll
@@ -380,7 +415,7 @@ __device__ __forceinline__ void seg16_info_h(const TileParams& p, const Pos& ps,
 // W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
 // each of 64 rows.  `fa` holds the loads of the wavefront's first segment
 // sg, already issued; H and the request info are in LDS.
-template <int KS, bool RESID, bool VEC4, bool PACKED, int NB>
+template <int KS, bool RESID, bool VEC4, bool PACKED, int NB, bool SPLIT>
 __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, const uint16_t* Hs,
                                            const ReqInfo* s_ci, int sg, Seg16Regs<KS, RESID, NB>& fa,
                                            Seg16Regs<KS, RESID, NB>& fb) {
@@ -399,12 +434,12 @@ __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, c
   while (true) {
     f32x4_t acc[NB];
     const int s1 = sg + n_waves;
-    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB>(fa.w, Hs, rank, lane, acc, p, ps, s_ci,
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB, SPLIT>(fa.w, Hs, rank, lane, acc, p, ps, s_ci,
                                                  min(s1, n_seg - 1) * kSegSmall, fb);
     seg16_epilogue<KS, RESID, NB>(p, lq, sg, lane, fa, acc);
     if (s1 >= n_seg) break;
     const int s2 = s1 + n_waves;
-    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB>(fb.w, Hs, rank, lane, acc, p, ps, s_ci,
+    seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB, SPLIT>(fb.w, Hs, rank, lane, acc, p, ps, s_ci,
                                                  min(s2, n_seg - 1) * kSegSmall, fa);
     seg16_epilogue<KS, RESID, NB>(p, lq, s1, lane, fb, acc);
     if (s2 >= n_seg) break;
@@ -412,7 +447,7 @@ __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, c
   }
 }
 
-template <int KS, bool RESID, bool VEC4, int WPB, bool PACKED, int NB>
+template <int KS, bool RESID, bool VEC4, int WPB, bool PACKED, int NB, bool SPLIT>
 __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = p.R, n_seg = p.n_seg;
@@ -429,32 +464,32 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
   // nor the request info, so its loads go out first and are in flight
   // while the request info and the H rows (prev -> W1[prev]) arrive
   if (!RESID) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
-  seg16_info_h<KS, RESID, WPB, NB>(p, ps, Hs, s_ci);
+  seg16_info_h<KS, RESID, WPB, NB, SPLIT>(p, ps, Hs, s_ci);
   // residual mode: the first segment's loads come after the barrier (their
   // U and target rows come from the request info)
   if (RESID) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
-  seg16_walk<KS, RESID, VEC4, PACKED, NB>(p, ps, Hs, s_ci, sg, fa, fb);
+  seg16_walk<KS, RESID, VEC4, PACKED, NB, SPLIT>(p, ps, Hs, s_ci, sg, fa, fb);
 }
 
 // Draft mode: one workgroup of eight wavefronts per CU (two per SIMD, for
 // latency hiding, sharing one copy of H); compiled to fit 256 registers per
 // wavefront.
-template <int KS, bool VEC4, bool PACKED, int NB>
+template <int KS, bool VEC4, bool PACKED, int NB, bool SPLIT>
 __global__ void __launch_bounds__(kSeg16DraftWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bias_seg16(TileParams p) {
   constexpr int RS = KS * 32 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[NB * 16 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[(SPLIT ? 2 : 1) * NB * 16 * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves, PACKED, NB>(p, Hs, s_ci);
+  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves, PACKED, NB, SPLIT>(p, Hs, s_ci);
 }
 
 // Residual mode (holds the target values too): one wavefront per SIMD.
-template <int KS, bool VEC4, bool PACKED, int NB>
+template <int KS, bool VEC4, bool PACKED, int NB, bool SPLIT>
 __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p) {
   constexpr int RS = KS * 32 + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Hs[NB * 16 * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t Hs[(SPLIT ? 2 : 1) * NB * 16 * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, true, VEC4, kSeg16Waves, PACKED, NB>(p, Hs, s_ci);
+  bias_seg16_body<KS, true, VEC4, kSeg16Waves, PACKED, NB, SPLIT>(p, Hs, s_ci);
 }
 
 // ---------------------------------------------------------------------------
@@ -1056,37 +1091,46 @@ void launch(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEvent_t ev0, hipE
 }
 
 // KS = seg16_ksteps(rank): the packed W2 layout uses the same count
-template <bool RESID, bool VEC4, bool PACKED, int NB>
+template <bool RESID, bool VEC4, bool PACKED, int NB, bool SPLIT>
 void launch_seg16_nb(const TileParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (seg16_ksteps(p.rank)) {
     case 2:
-      if (RESID) launch(bias_seg16_res<2, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<2, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<2, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<2, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
       break;
     case 4:
-      if (RESID) launch(bias_seg16_res<4, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<4, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<4, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<4, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
       break;
     case 8:
-      if (RESID) launch(bias_seg16_res<8, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<8, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<8, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<8, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
       break;
     default:
-      if (RESID) launch(bias_seg16_res<16, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
-      else launch(bias_seg16<16, VEC4, PACKED, NB>, grid, block, s, e0, e1, p);
+      if (RESID) launch(bias_seg16_res<16, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
+      else launch(bias_seg16<16, VEC4, PACKED, NB, SPLIT>, grid, block, s, e0, e1, p);
       break;
   }
 }
 
-// request column blocks: as many as the batch needs (1, 2 or 4)
+// request column blocks: as many as the batch needs (1, 2 or 4); H from
+// W1[prev] (Markov head) or split from the fp32 states (RNN head)
+template <bool RESID, bool VEC4, bool PACKED, bool SPLIT>
+void launch_seg16_h(const TileParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.R <= 16)
+    launch_seg16_nb<RESID, VEC4, PACKED, 1, SPLIT>(p, grid, block, s, e0, e1);
+  else if (p.R <= 32)
+    launch_seg16_nb<RESID, VEC4, PACKED, 2, SPLIT>(p, grid, block, s, e0, e1);
+  else
+    launch_seg16_nb<RESID, VEC4, PACKED, 4, SPLIT>(p, grid, block, s, e0, e1);
+}
+
 template <bool RESID, bool VEC4, bool PACKED>
 void launch_seg16(const TileParams& p, dim3 grid, dim3 block, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (p.R <= 16)
-    launch_seg16_nb<RESID, VEC4, PACKED, 1>(p, grid, block, s, e0, e1);
-  else if (p.R <= 32)
-    launch_seg16_nb<RESID, VEC4, PACKED, 2>(p, grid, block, s, e0, e1);
+  if (p.h_base != nullptr)
+    launch_seg16_h<RESID, VEC4, PACKED, true>(p, grid, block, s, e0, e1);
   else
-    launch_seg16_nb<RESID, VEC4, PACKED, 4>(p, grid, block, s, e0, e1);
+    launch_seg16_h<RESID, VEC4, PACKED, false>(p, grid, block, s, e0, e1);
 }
 
 template <bool RESID, bool VEC4>
@@ -1136,6 +1180,8 @@ hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int 
     return hipErrorInvalidValue;
   // 32-row segments are the fp32-weight path only
   if (p.seg_rows == kSegLarge && wdtype != DSPARK_W_F32) return hipErrorInvalidValue;
+  // H from the RNN head's states: the 16-row path only
+  if (p.h_base != nullptr && p.seg_rows != kSegSmall) return hipErrorInvalidValue;
   const bool vec4 = (p.V % 4) == 0;
   if (residual)
     return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s, ev0, ev1)

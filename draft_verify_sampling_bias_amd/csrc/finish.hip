@@ -56,7 +56,10 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   StageBatch<256> sb;
   if (STAGED) stage_issue<256>(gfine, p.n_seg, 0, sb);
   HRow<WT, 256> hrow;
-  hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
+  if (p.hstate != nullptr)
+    hrow.hold_state(p.hstate + urow * p.rank, p.rank);
+  else
+    hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
   if (STAGED) {
     auto none = [](float2) {};
     stage_commit<256>(p.n_seg, 0, sb, srec, none);

@@ -83,6 +83,14 @@ struct HRow {
       v[j] = weight_at<WT>(W1, static_cast<int64_t>(prev) * rank + min(k, rank - 1));
     }
   }
+  // the RNN head's fp32 state row instead
+  __device__ __forceinline__ void hold_state(const float* h, int rank) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int k = static_cast<int>(threadIdx.x) + j * NT;
+      v[j] = h[min(k, rank - 1)];
+    }
+  }
   __device__ __forceinline__ void commit(int rank, float* hs) const {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -148,7 +156,10 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
   StageBatch<NT, BATCH> sb;
   if (STAGED) stage_issue<NT, BATCH>(gfine, n_seg, 0, sb);
   HRow<WT, NT> hrow;
-  hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
+  if (p.hstate != nullptr)
+    hrow.hold_state(p.hstate + o * p.rank, p.rank);
+  else
+    hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
   // maximum (greedy: with the lowest argmax carried in the records' second
   // word; sampled: the second word is ignored), taken while staging
   float m = -INFINITY;

@@ -50,6 +50,11 @@ struct TileParams {
   // 16-row path: when set, the W2 fragments are read from this
   // fragment-packed copy (dspark_pack_w2) instead of W2
   const uint16_t* w2p;
+  // RNN head (16-row path), else null: H is the fp32 state instead of
+  // W1[prev]; draft mode: request n's row at h_base + n * h_stride;
+  // residual mode: row urow (U row index n * gamma + position) of h_base
+  const float* h_base;
+  int64_t h_stride;
 };
 
 // Per-position draft finish: turns the segment records into y / q_tok / q_stats.
@@ -67,6 +72,9 @@ struct FinishParams {
   int32_t* y;
   float* q_tok;
   float* q_stats;
+  // RNN head, else null: h for (n, k) is the fp32 row hstate + (n * gamma + k)
+  // * rank instead of W1[prev]
+  const float* hstate;
   // when set, block 0 writes 0 to this error word (a call made without the
   // input checks still rewrites the word of its workspace)
   uint32_t* err_clear;
@@ -98,6 +106,9 @@ struct VerifyParams {
   // appends every request that needs the residual pass
   int32_t* rs_count;
   ResidualEntry* rs_list;  // [R]
+  // RNN head, else null: the draft's fp32 states [R * gamma, rank]; the
+  // residual of request n at position j uses row n * gamma + j
+  const float* hstate;
   // when set, verify_stats writes 0 to this error word (as FinishParams)
   uint32_t* err_clear;
 };
@@ -128,6 +139,18 @@ hipError_t launch_input_check(const CheckParams& p, hipStream_t s);
 hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s);
+
+// The RNN head's state of position k for every request:
+// h[n, k] = act(A h[n, k-1] + W1[prev]) (h[n, -1] = 0), fp32.
+struct RnnStateParams {
+  int R, gamma, V, rank, k, act;
+  const uint16_t* W1;      // [V, rank] bf16
+  const uint16_t* A;       // [rank, rank] bf16
+  const int32_t* anchor;   // [R]
+  const int32_t* y;        // [R, gamma] (prev of k > 0)
+  float* h;                // [R, gamma, rank]: row k - 1 read, row k written
+};
+hipError_t launch_rnn_state(const RnnStateParams& p, hipStream_t s);
 hipError_t launch_verify_stats(const VerifyParams& p, hipStream_t s);
 hipError_t launch_verify_finish(const VerifyParams& p, hipStream_t s);
 hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t s);

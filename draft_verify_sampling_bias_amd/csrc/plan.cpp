@@ -41,6 +41,15 @@ inline int check_schedule_dims(int32_t R, int32_t gamma) {
   return DSPARK_OK;
 }
 
+// The head of a draft or verify call: the RNN head runs on the 16-row path
+// only (bf16 weights, R <= 64).
+inline int check_head(int32_t head, int32_t act, int32_t R, int32_t wdtype) {
+  if (head == DSPARK_HEAD_MARKOV) return DSPARK_OK;
+  if (head != DSPARK_HEAD_RNN) return DSPARK_ERR_UNSUPPORTED;
+  if (act != DSPARK_ACT_IDENTITY && act != DSPARK_ACT_TANH) return DSPARK_ERR_UNSUPPORTED;
+  if (seg_rows_for(R, wdtype) != kSegSmall) return DSPARK_ERR_UNSUPPORTED;
+  return DSPARK_OK;
+}
 
 }  // namespace
 
@@ -61,6 +70,8 @@ int plan_draft(const dspark_draft_args* a, DraftPlan* plan) {
   int st = check_dims(a->R, a->gamma, a->V, a->rank, a->wdtype);
   if (st != DSPARK_OK) return st;
   if ((a->flags & ~kKnownFlags) != 0) return DSPARK_ERR_UNSUPPORTED;
+  st = check_head(a->head, a->act, a->R, a->wdtype);
+  if (st != DSPARK_OK) return st;
   plan->check = (a->flags & DSPARK_CHECK_INPUTS) != 0;
   plan->seg_rows = seg_rows_for(a->R, a->wdtype);
   plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
@@ -83,6 +94,10 @@ int validate_draft(const dspark_draft_args* a, DraftPlan* plan) {
     return DSPARK_ERR_ALIGN;
   st = check_w2_packed(a->W2_packed, a->W2_packed_bytes, a->wdtype, a->V, a->rank);
   if (st != DSPARK_OK) return st;
+  if (a->head == DSPARK_HEAD_RNN) {
+    if (!a->A || !a->h) return DSPARK_ERR_NULL;
+    if (!aligned(a->A, 16) || !aligned(a->h, 16)) return DSPARK_ERR_ALIGN;
+  }
   return check_workspace(a->workspace, a->workspace_bytes, plan->total);
 }
 
@@ -94,6 +109,8 @@ int plan_verify(const dspark_verify_args* a, VerifyPlan* plan) {
   const int64_t max_rows = static_cast<int64_t>(a->R) * (a->gamma + 1);
   if (a->n_rows < a->R || a->n_rows > max_rows) return DSPARK_ERR_SHAPE;
   if ((a->flags & ~kKnownFlags) != 0) return DSPARK_ERR_UNSUPPORTED;
+  st = check_head(a->head, DSPARK_ACT_IDENTITY, a->R, a->wdtype);
+  if (st != DSPARK_OK) return st;
   plan->check = (a->flags & DSPARK_CHECK_INPUTS) != 0;
   plan->seg_rows = seg_rows_for(a->R, a->wdtype);
   plan->n_seg = (a->V + plan->seg_rows - 1) / plan->seg_rows;
@@ -136,6 +153,10 @@ int validate_verify(const dspark_verify_args* a, VerifyPlan* plan) {
     return DSPARK_ERR_ALIGN;
   st = check_w2_packed(a->W2_packed, a->W2_packed_bytes, a->wdtype, a->V, a->rank);
   if (st != DSPARK_OK) return st;
+  if (a->head == DSPARK_HEAD_RNN) {
+    if (!a->h) return DSPARK_ERR_NULL;
+    if (!aligned(a->h, 16)) return DSPARK_ERR_ALIGN;
+  }
   return check_workspace(a->workspace, a->workspace_bytes, plan->total);
 }
 

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DSPARK_ABI_VERSION 2
+#define DSPARK_ABI_VERSION 3
 
 /* limits checked on the host */
 #define DSPARK_MAX_GAMMA 16          /* block size gamma in [1, 16]                 */
@@ -100,6 +100,20 @@ typedef enum dspark_wdtype {
   DSPARK_W_BF16 = 1           /* bfloat16 bit patterns (uint16)                    */
 } dspark_wdtype;
 
+/* The drafter's sequential head ([EXP] section 7 names a Markov head and an
+ * RNN head that carries a longer in-block state; the pages give the RNN
+ * head no equations, and this library takes the Elman recurrence below). */
+typedef enum dspark_head {
+  DSPARK_HEAD_MARKOV = 0,     /* h_k = W1[prev_k]                                  */
+  DSPARK_HEAD_RNN = 1         /* h_k = act(A h_{k-1} + W1[prev_k]), h_{-1} = 0     */
+} dspark_head;
+
+/* Activation of the RNN head. */
+typedef enum dspark_act {
+  DSPARK_ACT_IDENTITY = 0,
+  DSPARK_ACT_TANH = 1
+} dspark_act;
+
 /* --------------------------------------------------------------------------
  * dspark_draft_block: draft one block of gamma tokens per request.
  *
@@ -114,7 +128,9 @@ typedef enum dspark_wdtype {
  *
  * For k = 0 .. gamma-1, sequentially (y[:, k-1] feeds position k):
  *   prev[r]  = anchor[r] if k == 0 else y[r, k-1]
- *   s[r, v]  = U[r, k, v] + sum_j W2[v, j] * W1[prev[r], j]
+ *   h[r, k]  = W1[prev[r]]                            (DSPARK_HEAD_MARKOV)
+ *              act(A h[r, k-1] + W1[prev[r]]), h[r, -1] = 0  (DSPARK_HEAD_RNN)
+ *   s[r, v]  = U[r, k, v] + sum_j W2[v, j] * h[r, k, j]
  *   greedy (temp[r] <= 0 or NaN):
  *     y[r, k] = lowest index v with maximal s[r, v]; q_tok = 1;
  *     q_stats = (max_v s, 1)
@@ -162,6 +178,18 @@ typedef enum dspark_wdtype {
  *   W2_packed_bytes  size of the W2_packed buffer; at least
  *                dspark_w2_packed_bytes(V, rank) when W2_packed is given
  *                (DSPARK_ERR_WORKSPACE otherwise).
+ *   head     dspark_head.  DSPARK_HEAD_RNN needs bf16 weights and R <= 64
+ *            (the 16-row path; DSPARK_ERR_UNSUPPORTED otherwise); an unknown
+ *            head or act is DSPARK_ERR_UNSUPPORTED.
+ *   act      dspark_act of the RNN head (ignored by the Markov head).
+ *   A        RNN head: wdtype [rank, rank] recurrence matrix, row j gives
+ *            output j (z_j = sum_i A[j, i] h_i); 16-byte aligned.  Else NULL.
+ *   h        RNN head: float [R, gamma, rank] out, 16-byte aligned: the
+ *            states h[r, k], which dspark_verify reads back.  They are
+ *            computed in fp32 and stored as double-bf16 values (the sum of
+ *            two bf16 numbers, 16 significant bits), the form in which the
+ *            fused bias kernel feeds them to the bf16 matrix cores exactly.
+ *            Else NULL.
  * -------------------------------------------------------------------------- */
 typedef struct dspark_draft_args {
   uint32_t struct_size;
@@ -183,6 +211,10 @@ typedef struct dspark_draft_args {
   void* const* prof_events;
   const void* W2_packed;
   size_t W2_packed_bytes;
+  int32_t head;
+  int32_t act;
+  const void* A;
+  float* h;
 } dspark_draft_args;
 
 /* --------------------------------------------------------------------------
@@ -274,8 +306,9 @@ typedef struct dspark_schedule_args {
  *     p_j = softmax(t_j / T); p_tok[r, j] = p_j(y_j);
  *     accept iff u_accept[r, j] < p_tok[r, j] / q_tok[r, j];
  *     n = first rejected j, else l;
- *     n < l: q_n = softmax((U[r, n] + W2 . W1[prev]) / T) rebuilt with
- *            prev = anchor (n = 0) or y[r, n-1] and q_stats[r, n];
+ *     n < l: q_n = softmax((U[r, n] + W2 . h[r, n]) / T) rebuilt with the
+ *            draft's h (Markov head: W1[prev], prev = anchor (n = 0) or
+ *            y[r, n-1]; RNN head: the state array) and q_stats[r, n];
  *            out_tok = inverse-CDF draw with u_final[r] from max(0, p_n - q_n)
  *            (from p_n if that has no mass);
  *     n = l: out_tok = inverse-CDF draw with u_final[r] from p_l (bonus).
@@ -305,6 +338,9 @@ typedef struct dspark_schedule_args {
  *   stream     hipStream_t as void*.
  *   W2_packed, W2_packed_bytes  optional, as for dspark_draft_block (read by
  *              the residual pass of the 16-row path).
+ *   head       the head the block was drafted with (same limits).
+ *   h          RNN head: the float [R, gamma, rank] states written by
+ *              dspark_draft_block, 16-byte aligned.  Else NULL.
  * -------------------------------------------------------------------------- */
 typedef struct dspark_verify_args {
   uint32_t struct_size;
@@ -332,6 +368,8 @@ typedef struct dspark_verify_args {
   void* stream;
   const void* W2_packed;
   size_t W2_packed_bytes;
+  int32_t head;
+  const float* h;
 } dspark_verify_args;
 
 /* Workspace bytes needed by a call with these arguments (only the size

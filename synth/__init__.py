@@ -23,6 +23,9 @@ stand in for them):
 * temperature per request; T <= 0 marks a greedy request.
 * confidence c = fp32(sigmoid(N(1, 1))), shape [R, gamma].
 * capacity K (number of draft positions to verify in the whole batch).
+* RNN head recurrence A, shape [rank, rank], drawn N(0, (scale/sqrt(rank))^2)
+  (spectral radius about ``scale``), bf16-rounded like W1, W2; from a stream
+  of its own (make_rnn_A), so the other arrays do not change with it.
 
 Every array comes from its own child stream of ``SeedSequence(seed)`` in a
 fixed order, and per-request arrays from per-request grandchildren, so any
@@ -38,7 +41,7 @@ import numpy as np
 __all__ = [
     "StepInputs", "CONFIGS", "make_config", "make_custom", "bf16_round_bits",
     "bf16_bits_to_f32", "weights_as_f32", "gather_rows", "fixed_offsets",
-    "sps_table", "random_sps_table", "make_calibration",
+    "sps_table", "random_sps_table", "make_calibration", "make_rnn_A",
 ]
 
 # stream order inside SeedSequence(seed).spawn(N_STREAMS)
@@ -101,6 +104,19 @@ def gather_rows(target: np.ndarray, row_req: np.ndarray, row_pos: np.ndarray) ->
     This stands in for the target model's forward over the scheduled rows."""
     return np.ascontiguousarray(target[np.asarray(row_req, dtype=np.int64),
                                        np.asarray(row_pos, dtype=np.int64)])
+
+
+def make_rnn_A(seed: int, rank: int, *, scale: float = 0.8, wdtype: str = "bf16") -> np.ndarray:
+    """Recurrence matrix of the RNN head for the inputs of ``seed``: entries
+    N(0, (scale / sqrt(rank))^2), bf16 bit patterns (uint16) or fp32.  Drawn
+    from child N_STREAMS of SeedSequence(seed), which no other array uses."""
+    ss = np.random.SeedSequence(seed).spawn(N_STREAMS + 1)[N_STREAMS]
+    A = _rng(ss).standard_normal((rank, rank), dtype=np.float32) * np.float32(scale / np.sqrt(rank))
+    if wdtype == "bf16":
+        return bf16_round_bits(A)
+    if wdtype != "f32":
+        raise ValueError(f"unknown wdtype {wdtype!r}")
+    return A
 
 
 # ---------------------------------------------------------------------------

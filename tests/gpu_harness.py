@@ -46,14 +46,25 @@ def upload(inp: synth.StepInputs, device="cuda:0"):
                 u_accept=f(inp.u_accept), u_final=f(inp.u_final), c=f(inp.c), target=f(inp.target))
 
 
-def gpu_step(d, K, gamma, conf_min=None, W2_packed=None):
+def upload_A(A: np.ndarray, wdtype: str, device="cuda:0"):
+    """The RNN head's recurrence matrix (synth.make_rnn_A) on the device."""
+    torch = torch_mod()
+    if wdtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(A).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(A)).to(device)
+
+
+def gpu_step(d, K, gamma, conf_min=None, W2_packed=None, A=None, act=1):
     """draft -> schedule (top-K with capacity K, or the static confidence
     cutoff when conf_min is given) -> gather rows -> verify on the GPU;
-    returns numpy results."""
+    returns numpy results.  ``A`` (a device tensor) selects the RNN head with
+    activation ``act``; the states come back as "h"."""
     import draft_verify_sampling_bias_amd as ds
     torch = torch_mod()
-    y, q_tok, q_stats = ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"],
-                                              W2_packed=W2_packed)
+    res = ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"],
+                                W2_packed=W2_packed, A=A, act=act)
+    y, q_tok, q_stats = res[:3]
+    h = res[3] if A is not None else None
     if conf_min is None:
         sch = ds.dspark_schedule(d["c"], K, d["anchor"], y)
     else:
@@ -64,10 +75,12 @@ def gpu_step(d, K, gamma, conf_min=None, W2_packed=None):
     rows = d["target"][sch["row_req"].long(), sch["row_pos"].long()].contiguous()
     n_acc, out_tok, p_tok = ds.dspark_verify(rows, sch["row_offsets"], d["U"], d["W1"], d["W2"], d["anchor"],
                                              d["temp"], y, q_tok, q_stats, d["u_accept"], d["u_final"],
-                                             W2_packed=W2_packed)
+                                             W2_packed=W2_packed, h=h)
     torch.cuda.synchronize()
     res = dict(y=y, q_tok=q_tok, q_stats=q_stats, n_accept=n_acc, out_tok=out_tok, p_tok=p_tok, rows=rows,
                **{k: v for k, v in sch.items() if v is not None})
+    if h is not None:
+        res["h"] = h
     return {k: v.cpu().numpy() for k, v in res.items()}
 
 
@@ -98,11 +111,58 @@ class Tally:
                 f"own_q_flips={self.own_q_flips} unflagged_mismatches={len(self.failures)}")
 
 
-def compare_draft(inp, g, reqs, tally: Tally):
-    """Teacher-forced comparison of the drafted ids, q_tok and q_stats."""
+#: unit roundoff of fp32 and the double-bf16 rounding of the RNN state
+#: (hi = bf16(x), lo = bf16(x - hi): |hi + lo - x| <= 2^-16 |x|)
+U32 = 2.0 ** -24
+DBF16 = 2.0 ** -16
+
+
+def rnn_state_bound(A64, W1_64, hp, prev, h_o):
+    """Bound on |h_gpu - h_oracle| for one RNN state step from the same
+    previous state hp and token prev: the fp32 dot product of rank terms
+    plus the input row (at most gamma_{rank+1} times the sum of magnitudes,
+    gamma_n = n u / (1 - n u)), carried through the activation (1-Lipschitz),
+    the activation's own rounding (tanhf within 2 ulp), and the double-bf16
+    rounding of the stored state."""
+    n = A64.shape[1] + 1
+    gam = n * U32 / (1 - n * U32)
+    mag = np.abs(A64) @ np.abs(hp) + np.abs(W1_64[prev])
+    return gam * mag + (DBF16 + 4 * U32) * np.abs(h_o) * (1 + DBF16) + 1e-30
+
+
+def compare_rnn_states(inp, g, A, act, reqs, tally: Tally):
+    """The RNN head teacher-forced on the GPU's tokens and states: every
+    state must be within rnn_state_bound of the oracle's one step from the
+    GPU's previous state.  Returns the oracle's DraftResult, whose draws use
+    the GPU's states (for compare_draft)."""
+    y_g, h_g = g["y"], g["h"]
+    d = oracle.rnn_draft_block(inp.U, inp.W1, inp.W2, A, inp.wdtype, act, inp.anchor, inp.temp, inp.u_draft,
+                               requests=reqs, prev_override=y_g, state_override=h_g)
+    A64 = synth.bf16_bits_to_f32(A).astype(np.float64) if inp.wdtype == "bf16" else A.astype(np.float64)
+    W1_64 = synth.weights_as_f32(inp)[0].astype(np.float64)
+    rank = A64.shape[0]
+    for r in reqs:
+        for k in range(inp.gamma):
+            prev = int(inp.anchor[r]) if k == 0 else int(y_g[r, k - 1])
+            hp = np.zeros(rank) if k == 0 else h_g[r, k - 1].astype(np.float64)
+            bound = rnn_state_bound(A64, W1_64, hp, prev, d.h[r, k])
+            err = np.abs(h_g[r, k].astype(np.float64) - d.h[r, k])
+            bad = np.nonzero(err > bound)[0]
+            if bad.size:
+                j = int(bad[0])
+                tally.failures.append(f"rnn state r={r} k={k} j={j}: gpu {h_g[r, k, j]} oracle {d.h[r, k, j]} "
+                                      f"(bound {bound[j]:.3g}, {bad.size} entries over)")
+    return d
+
+
+def compare_draft(inp, g, reqs, tally: Tally, d=None):
+    """Teacher-forced comparison of the drafted ids, q_tok and q_stats (``d``:
+    the oracle's teacher-forced DraftResult if already computed, else the
+    Markov head's)."""
     y_g = g["y"]
-    d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
-                           requests=reqs, prev_override=y_g)
+    if d is None:
+        d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
+                               requests=reqs, prev_override=y_g)
     for r in reqs:
         for k in range(inp.gamma):
             tally.decisions += 1
@@ -154,12 +214,13 @@ def compare_verify(inp, g, reqs, tally: Tally, d=None):
     decisions depend on q_tok (the residual rebuilds q from U and the
     weights), so the accepted counts must agree, except where the first
     differing decision has u within OWN_Q_BAND * p/q of p/q."""
+    hs = g.get("h")  # the RNN head's states (the verify's input), else None
     v = oracle.verify(g["rows"], g["row_offsets"], inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"],
-                      g["q_tok"], inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+                      g["q_tok"], inp.temp, inp.u_accept, inp.u_final, requests=reqs, h_states=hs)
     off = g["row_offsets"]
     if d is not None:
         v2 = oracle.verify(g["rows"], off, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"], d.q_tok,
-                           inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+                           inp.temp, inp.u_accept, inp.u_final, requests=reqs, h_states=hs)
         for r in reqs:
             l = int(off[r + 1] - off[r] - 1)
             tally.own_q_decisions += l

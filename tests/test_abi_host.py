@@ -34,7 +34,7 @@ def test_header_declares_and_library_exports_everything():
 
 
 def test_abi_version_and_strings():
-    assert ds.dspark_abi_version() == 2
+    assert ds.dspark_abi_version() == ds.ABI_VERSION == 3
     strings = [ds.dspark_status_string(s) for s in range(10)]
     assert all(strings) and len(set(strings)) == 10
     assert "unknown status" not in strings
@@ -116,6 +116,16 @@ def _call(fn, args):
     (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), ds.Status.ERR_ALIGN),
     (dict(flags=2), ds.Status.ERR_UNSUPPORTED),            # unknown flag bit
     (dict(flags=1 << 31), ds.Status.ERR_UNSUPPORTED),
+    # the RNN head: known head and activation, the 16-row path only
+    (dict(head=2), ds.Status.ERR_UNSUPPORTED),
+    (dict(head=1, act=2, A=FAKE, h=FAKE), ds.Status.ERR_UNSUPPORTED),
+    (dict(head=1, A=FAKE, h=FAKE, R=65), ds.Status.ERR_UNSUPPORTED),      # 64-row path
+    (dict(head=1, A=FAKE, h=FAKE, wdtype=0), ds.Status.ERR_UNSUPPORTED),  # fp32 path
+    (dict(head=1, A=None, h=FAKE), ds.Status.ERR_NULL),
+    (dict(head=1, A=FAKE, h=None), ds.Status.ERR_NULL),
+    (dict(head=1, A=FAKE + 8, h=FAKE), ds.Status.ERR_ALIGN),
+    (dict(head=1, A=FAKE, h=FAKE + 4), ds.Status.ERR_ALIGN),
+    (dict(head=1, A=FAKE, h=FAKE), ds.Status.ERR_WORKSPACE),  # valid RNN arguments up to the workspace
 ])
 def test_draft_rejects_invalid_arguments(kw, status):
     assert _call("dspark_draft_block", _draft_args(**kw)) == status
@@ -149,6 +159,12 @@ def _verify_args(**kw):
     (dict(q_stats=FAKE + 4), ds.Status.ERR_ALIGN),
     (dict(), ds.Status.ERR_WORKSPACE),
     (dict(flags=4), ds.Status.ERR_UNSUPPORTED),
+    (dict(head=3), ds.Status.ERR_UNSUPPORTED),
+    (dict(head=1, h=FAKE, R=65, n_rows=65), ds.Status.ERR_UNSUPPORTED),
+    (dict(head=1, h=FAKE, wdtype=0), ds.Status.ERR_UNSUPPORTED),
+    (dict(head=1, h=None), ds.Status.ERR_NULL),
+    (dict(head=1, h=FAKE + 4), ds.Status.ERR_ALIGN),
+    (dict(head=1, h=FAKE), ds.Status.ERR_WORKSPACE),
 ])
 def test_verify_rejects_invalid_arguments(kw, status):
     assert _call("dspark_verify", _verify_args(**kw)) == status
