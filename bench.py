@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--policy greedy|sampled]
     python bench.py --sweep capacity|sts     (size sweeps of the off-step kernels, for a kernel trace)
+    python bench.py --head rnn               (the RNN sequential head instead of the Markov head)
 
 Workload (default): R = 64 requests, block gamma = 7, vocabulary V = 151936,
 Markov rank r = 512, bf16 Markov factors, fp32 logits, per-request
@@ -59,11 +60,15 @@ def tile_kernel(R, wdtype):
     return "bias_seg16" if R <= 64 else "bias_seg64"
 
 
-def algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows):
+def algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows, rnn=False):
     """Bytes the method must move per step: U once, the verify target rows
-    once, W2 once per draft position, and the gathered W1 rows."""
-    per_pos_tile = wbytes * V * rank + 4 * R * V + wbytes * R * rank
-    step = gamma * per_pos_tile + 4 * n_rows * V
+    once, W2 once per draft position, and the gathered W1 rows (RNN head:
+    the fp32 states instead; the state update's own reads of A, rank x rank,
+    and of W1 rows are counted per position as well)."""
+    h_bytes = 4 * R * rank if rnn else wbytes * R * rank
+    per_pos_tile = wbytes * V * rank + 4 * R * V + h_bytes
+    state = (wbytes * rank * rank + wbytes * R * rank + 8 * R * rank) if rnn else 0
+    step = gamma * (per_pos_tile + state) + 4 * n_rows * V
     return step, per_pos_tile
 
 
@@ -121,25 +126,32 @@ class HipTimingEvents:
 _POOL = {}
 
 
-def _oracle_draft_chunk(reqs):
+def _oracle_draft(inp, reqs, rnn):
     import oracle
+    if rnn is None:
+        return oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
+                                  requests=reqs)
+    return oracle.rnn_draft_block(inp.U, inp.W1, inp.W2, rnn[0], inp.wdtype, rnn[1], inp.anchor, inp.temp,
+                                  inp.u_draft, requests=reqs)
+
+
+def _oracle_draft_chunk(reqs):
     from threadpoolctl import threadpool_limits
     P = _POOL
-    inp = P["inp"]
     with threadpool_limits(limits=1):
-        d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft, requests=reqs)
-    return reqs, d.y[reqs], d.q_tok[reqs], len(d.flags)
+        d = _oracle_draft(P["inp"], reqs, P["rnn"])
+    return reqs, d.y[reqs], d.q_tok[reqs], (d.h[reqs] if d.h is not None else None), len(d.flags)
 
 
 def _oracle_verify_chunk(job):
     import oracle
     from threadpoolctl import threadpool_limits
-    reqs, y, q_tok = job
+    reqs, y, q_tok, h = job
     P = _POOL
     inp = P["inp"]
     with threadpool_limits(limits=1):
         v = oracle.verify(P["rows"], P["row_offsets"], inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, y, q_tok,
-                          inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+                          inp.temp, inp.u_accept, inp.u_final, requests=reqs, h_states=h)
     return len(v.flags)
 
 
@@ -160,7 +172,7 @@ def _host_cpu():
     return dict(cpu_count=os.cpu_count(), allowed=allowed, model=model)
 
 
-def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=None, max_procs=16):
+def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=None, max_procs=16, rnn=None):
     """The CPU oracle, unmodified, on a bounded sample of requests of the same
     workload, timed twice: on one host core (BLAS on one thread, the process
     pinned to one core) and on all allowed cores (up to max_procs worker
@@ -171,7 +183,8 @@ def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=No
     calibration logits, calibration counts): temperatures fitted once outside
     the timing, then the calibrated confidence in each step).  The row gather
     stands in for the target forward and is not timed, as on the GPU.  Must
-    run before this process touches the GPU (the workers are forked)."""
+    run before this process touches the GPU (the workers are forked).  With
+    rnn = (A, act) the drafter is the RNN head."""
     import multiprocessing as mp
 
     import oracle
@@ -201,15 +214,14 @@ def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=No
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
             conf = oracle.sts_apply(sts[0], tau) if sts is not None else inp.c
-            d = oracle.draft_block(inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, inp.temp, inp.u_draft,
-                                   requests=reqs)
+            d = _oracle_draft(inp, reqs, rnn)
             y = np.where(d.y < 0, 0, d.y)
             sch = sched(conf, y)
             t1 = time.perf_counter()
             rows = inp.target[sch.row_req.astype(np.int64), sch.row_pos.astype(np.int64)]
             t2 = time.perf_counter()
             v = oracle.verify(rows, sch.row_offsets, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, y, d.q_tok,
-                              inp.temp, inp.u_accept, inp.u_final, requests=reqs)
+                              inp.temp, inp.u_accept, inp.u_final, requests=reqs, h_states=d.h)
             t3 = time.perf_counter()
     finally:
         if old_aff:
@@ -221,7 +233,7 @@ def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=No
     n_proc = max(1, min(host["allowed"], max_procs, len(reqs)))
     chunks = [c.tolist() for c in np.array_split(np.asarray(reqs), n_proc) if len(c)]
     _POOL.clear()
-    _POOL.update(inp=inp, rows=rows, row_offsets=sch.row_offsets)
+    _POOL.update(inp=inp, rows=rows, row_offsets=sch.row_offsets, rnn=rnn)
     ctx = mp.get_context("fork")
     with ctx.Pool(n_proc) as pool:
         pool.map(abs, range(n_proc))  # workers up before timing
@@ -229,15 +241,18 @@ def cpu_baseline(inp, n_sample, seed=0, conf_min=None, capacity_sps=None, sts=No
         conf = oracle.sts_apply(sts[0], tau) if sts is not None else inp.c
         y_all = np.zeros((inp.R, inp.gamma), np.int32)
         q_all = np.full((inp.R, inp.gamma), np.nan)
-        for rq, yy, qq, _ in pool.map(_oracle_draft_chunk, chunks):
+        h_all = np.zeros((inp.R, inp.gamma, inp.rank)) if rnn is not None else None
+        for rq, yy, qq, hh, _ in pool.map(_oracle_draft_chunk, chunks):
             y_all[rq] = yy
             q_all[rq] = qq
+            if hh is not None:
+                h_all[rq] = hh
         sch2 = sched(conf, y_all)
         t1 = time.perf_counter()
         # the rows were gathered above (row_req / row_pos do not depend on y)
         assert np.array_equal(sch2.row_offsets, sch.row_offsets)
         t2 = time.perf_counter()
-        pool.map(_oracle_verify_chunk, [(c, y_all, q_all) for c in chunks])
+        pool.map(_oracle_verify_chunk, [(c, y_all, q_all, h_all) for c in chunks])
         t3 = time.perf_counter()
     _POOL.clear()
     eln = (t1 - t0) + (t3 - t2)
@@ -314,6 +329,9 @@ def main():
                          "every shape is fixed ahead, so the captured step needs no host work")
     ap.add_argument("--no-pack", action="store_true",
                     help="read W2 itself instead of its fragment-packed copy (dspark_pack_w2)")
+    ap.add_argument("--head", default="markov", choices=["markov", "rnn"],
+                    help="the drafter's sequential head: Markov (bias W2 . W1[prev]) or RNN (bias W2 h_k, "
+                         "h_k = tanh(A h_{k-1} + W1[prev]), A from synth.make_rnn_A; bf16 with R <= 64 only)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
@@ -331,8 +349,13 @@ def main():
         return
     inp = None
     cpu = None
+    rnn = None
     if not args.copy_calib:
         inp = synth.make_config(args.config, args.policy)
+        if args.head == "rnn":
+            if inp.wdtype != "bf16" or inp.R > 64:
+                raise SystemExit("--head rnn runs on the 16-row path only (bf16 weights, R <= 64)")
+            rnn = (synth.make_rnn_A(1000 + args.config, inp.rank), 1)
         # the CPU oracle runs first: its all-cores leg forks worker
         # processes, which must happen before this process uses the GPU
         if not args.skip_cpu:
@@ -341,7 +364,7 @@ def main():
                                capacity_sps=synth.sps_table(R_ * (g_ + 1) + 1) if args.capacity else None,
                                sts=(synth.make_calibration(7000 + args.config, R_, g_)[0],
                                     *synth.make_calibration(7100 + args.config, 20000, g_)[:2])
-                               if args.sts else None)
+                               if args.sts else None, rnn=rnn)
 
     import torch
     import draft_verify_sampling_bias_amd as ds
@@ -371,6 +394,13 @@ def main():
     U, anchor, temp = up(inp.U), up(inp.anchor), up(inp.temp)
     u_draft, u_accept, u_final, c = up(inp.u_draft), up(inp.u_accept), up(inp.u_final), up(inp.c)
     target_full = up(inp.target)
+    # RNN head: the recurrence matrix and the state buffer (written by the
+    # draft, read by the verify)
+    A_d = h_buf = None
+    if rnn is not None:
+        A_d = torch.from_numpy(rnn[0].view(np.int16)).to(dev).view(torch.bfloat16)
+        h_buf = torch.empty((R, gamma, rank), dtype=torch.float32, device=dev)
+    rk = dict(A=A_d, act=rnn[1], h=h_buf) if rnn is not None else {}
 
     # the fragment-packed copy of W2 that the 16-row path reads, made once as
     # at model load (before and outside any timing)
@@ -383,7 +413,8 @@ def main():
     q_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
     q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
     wd = ds.W_BF16 if inp.wdtype == "bf16" else ds.W_F32
-    ws_d = torch.empty(ds.draft_workspace_bytes(R, gamma, V, rank, wd), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(ds.draft_workspace_bytes(R, gamma, V, rank, wd, head=ds.HEAD_RNN if rnn else ds.HEAD_MARKOV,
+                                                act=rnn[1] if rnn else 0), dtype=torch.uint8, device=dev)
     n_acc = torch.empty(R, dtype=torch.int32, device=dev)
     out_tok = torch.empty(R, dtype=torch.int32, device=dev)
     p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
@@ -411,7 +442,7 @@ def main():
         # an earlier step's survival (the inputs repeat, so every step has
         # the same) gives the capacity of the steps that follow
         ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d,
-                              W2_packed=W2p)
+                              W2_packed=W2p, **rk)
         first = ds.dspark_schedule(c, R * gamma, anchor, y)
         ds.dspark_capacity(first["a"], sps, out=cap_out)
         K_sched = int(cap_out["K"].item())
@@ -440,20 +471,23 @@ def main():
                 ds.dspark_capacity(sch["a"], sps, out=cap_out)
             ds.dspark_schedule(c, K_sched, anchor, y, out=sch)
 
-    ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d, W2_packed=W2p)
+    ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d, W2_packed=W2p,
+                          **rk)
     schedule()
     n_rows = int(sch["row_offsets"][R].item())
     rows = target_full[sch["row_req"][:n_rows].long(), sch["row_pos"][:n_rows].long()].contiguous()
     del target_full
-    ws_v = torch.empty(ds.verify_workspace_bytes(R, gamma, V, rank, wd, n_rows), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty(ds.verify_workspace_bytes(R, gamma, V, rank, wd, n_rows,
+                                                 head=ds.HEAD_RNN if rnn else ds.HEAD_MARKOV),
+                       dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(prof=None):
         ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d,
-                              prof_events=prof, W2_packed=W2p)
+                              prof_events=prof, W2_packed=W2p, **rk)
         schedule()
         ds.dspark_verify(rows, sch["row_offsets"], U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final,
-                         out=(n_acc, out_tok, p_tok), workspace=ws_v, W2_packed=W2p)
+                         out=(n_acc, out_tok, p_tok), workspace=ws_v, W2_packed=W2p, h=h_buf)
 
     # cache eviction between steps: READ 1 GiB of unrelated data (a write
     # would leave dirty lines whose write-back lands in the next kernel)
@@ -522,12 +556,12 @@ def main():
         evict()
         cev[i][0].record(stream)
         ds.dspark_draft_block(U, W1, W2, anchor, temp, u_draft, out=(y, q_tok, q_stats), workspace=ws_d,
-                              W2_packed=W2p)
+                              W2_packed=W2p, **rk)
         cev[i][1].record(stream)
         schedule()
         cev[i][2].record(stream)
         ds.dspark_verify(rows, sch["row_offsets"], U, W1, W2, anchor, temp, y, q_tok, q_stats, u_accept, u_final,
-                         out=(n_acc, out_tok, p_tok), workspace=ws_v, W2_packed=W2p)
+                         out=(n_acc, out_tok, p_tok), workspace=ws_v, W2_packed=W2p, h=h_buf)
         cev[i][3].record(stream)
     torch.cuda.synchronize()
     calls_us = {name: round(float(np.mean([cev[i][j].elapsed_time(cev[i][j + 1]) for i in range(K)])) * 1e3, 2)
@@ -560,7 +594,7 @@ def main():
         wall_warm = time.perf_counter() - t1
         warm = dict(value=positions / wall_warm, ms_per_step=wall_warm / K * 1e3)
 
-    bytes_step, bytes_tile = algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows)
+    bytes_step, bytes_tile = algorithmic_bytes(R, gamma, V, rank, wbytes, n_rows, rnn=rnn is not None)
     kernel = tile_kernel(R, inp.wdtype)
     ms_per_step = tot_ms / K
     tile_avg_ms = float(np.mean(tile_ms))
@@ -582,6 +616,7 @@ def main():
         "data": "synthetic (seeded; logits, Markov factors, uniforms and confidences drawn by synth)",
         "config": {
             "workload": f"config{args.config}: R={R} gamma={gamma} V={V} r={rank} {inp.wdtype} W1/W2, fp32 logits, "
+                        + ("RNN head (tanh, A from synth.make_rnn_A), " if rnn else "")
                         + (f"{args.policy} requests, " if args.policy else "")
                         + ("confidence calibrated by sequential temperature scaling, " if args.sts else "")
                         + (f"static confidence cutoff conf_min={args.conf_min} ({n_rows} rows)" if cutoff else
@@ -589,7 +624,7 @@ def main():
                            f"bucketed step-rate table ({n_rows} rows)" if args.capacity else
                            f"{'fixed-length' if inp.K >= R * gamma else 'scheduled'} verify "
                            f"(K={inp.K}, {n_rows} rows)"),
-            "R": R, "gamma": gamma, "V": V, "rank": rank, "weights": inp.wdtype, "K": K_sched,
+            "R": R, "gamma": gamma, "V": V, "rank": rank, "weights": inp.wdtype, "K": K_sched, "head": args.head,
             "W2_layout": "fragment-packed copy (dspark_pack_w2, made once before timing)" if use_pack
             else "row-major",
             "verify_rows": n_rows, "parallelism": "single GPU",
@@ -605,13 +640,14 @@ def main():
         "calls_us": calls_us,
         "acceptance": acceptance,
         "roofline": {
-            "kernel": f"{kernel} (fused Markov bias GEMM + softmax statistics, one launch per draft position)",
+            "kernel": f"{kernel} (fused Markov bias GEMM + softmax statistics, one launch per draft position"
+                      + ("; RNN state as two bf16 planes, two MFMAs per k-step)" if rnn else ")"),
             "bound": "hbm",
             "achieved": round(tile_gbps, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(tile_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(args.config, kernel),
+            "traffic": None if rnn else load_traffic(args.config, kernel),
             "avg_launch_us": round(tile_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": int(bytes_tile),
         },
