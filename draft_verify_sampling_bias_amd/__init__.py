@@ -42,7 +42,7 @@ ABI_VERSION = 3                   # DSPARK_ABI_VERSION these structs follow
 CHECK_INPUTS = 1
 BAD_TOKEN, BAD_UNIFORM, BAD_LENGTH, BAD_CONFIDENCE = 1, 2, 4, 8
 WORKSPACE_HEADER = 256
-NOALLOC_SCRATCH_BYTES = 32 << 20   # the static workspace of dspark_draft_block_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the static workspace of dspark_draft_block_noalloc
 
 EXPORTED_SYMBOLS = (
     "dspark_draft_workspace_size", "dspark_verify_workspace_size", "dspark_draft_block",

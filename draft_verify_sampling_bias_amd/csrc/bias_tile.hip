@@ -663,6 +663,20 @@ __device__ __forceinline__ void wide_u_issue(const TileParams& p, const WideReq<
   }
 }
 
+// Rows past the vocabulary become -inf (in U, and in the target values in
+// residual mode), so that the logits and the exponentials of those rows
+// need no per-row test.  `full` (the segment lies inside the vocabulary)
+// is wavefront-uniform: only the wavefront whose segment holds row V - 1
+// (or lies past it) runs the selects.
+__device__ __forceinline__ void wide_mask(bool full, int vw, int lane, int V, f32x4_t (&x)[4]) {
+  if (full) return;
+  const int vb = vw + 4 * (lane >> 4);
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[b][i] = (vb + 16 * b + i < V) ? x[b][i] : -INFINITY;
+}
+
 // This wavefront's W2 rows vw + 16 b + (lane & 15), k = 32 ks + 8 (lane >> 4)
 // .. +8, the MFMA A fragments (addresses clamped into the row; the groups
 // past the rank are zeroed by wide_w2_ready).
@@ -703,68 +717,23 @@ __device__ __forceinline__ void wide_w2_ready(int rank, int lane, u32x4_t (&w)[4
 // never used.)
 __device__ __forceinline__ float wide_exp_base(float m) { return (m == -INFINITY) ? 0.f : m; }
 
-// One chunk's record for this lane's request over the wavefront's 64 rows:
-// 16 values in the lane, then the four lanes (lane & 15) + 16 j.
-template <bool RESID>
-__device__ __forceinline__ void wide_epilogue(const TileParams& p, int seg, int lane, const WideU<RESID>& f,
-                                              const f32x4_t (&acc)[4], bool live) {
-  const int kq = lane >> 4;
-  const int V = p.V;
-  const int vb = seg * kSegWide + 4 * kq;
-  float x, y;
-  if constexpr (!RESID) {
-    float s[16];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[4 * b + i] = (vb + 16 * b + i < V) ? acc[b][i] + f.u[b][i] : -INFINITY;
-    float m = s[0];
-    int im = vb;
-#pragma unroll
-    for (int e = 1; e < 16; ++e) {
-      const bool gt = s[e] > m;
-      m = gt ? s[e] : m;
-      im = gt ? vb + 16 * (e >> 2) + (e & 3) : im;
-    }
-    quad_amax(m, im);
-    const float mg = wide_exp_base(m);
-    float z = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) z += exp2_hw((s[e] - mg) * f.c);
-    z = quad_sum(z);
-    x = m;
-    y = (f.c > 0.f) ? z : __int_as_float(im);
-  } else {
-    float w = 0.f;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float qq = exp2_hw((acc[b][i] + f.u[b][i] - f.Mq) * f.c) * f.iZq;
-        const float pp = exp2_hw((f.t[b][i] - f.Mp) * f.c) * f.iZp;
-        const float d = fmaxf(pp - qq, 0.f);
-        w += __int_as_float(__float_as_int(d) & -static_cast<int>(vb + 16 * b + i < V));
-      }
-    w = quad_sum(w);
-    x = 0.f;
-    y = w;
-  }
-  // segments past the vocabulary (last workgroup), and the pipeline's
-  // empty first slot, store into the dummy row
-  const bool in_v = live && seg < p.n_seg;
-  const int64_t row = in_v ? f.n : p.R + kWideChunk;
-  const int col = in_v ? seg : 0;
-  reinterpret_cast<float2*>(p.part)[row * p.n_seg + col] = make_float2(x, y);
-}
-
-// The same epilogue cut into small steps, so that its vector instructions
-// can be placed one step after each MFMA of the next chunk (step t is a
-// compile-time constant at every call).  Draft: steps 0-15 form logit k = t
-// (after step 15 the inputs may be overwritten), 16-31 fold entry t - 16
-// into the maximum and lowest argmax, 32 combines the four lanes, 33-48 add
-// exponential t - 33, 49 combines and stores.  Residual: step 3 k adds entry
-// k (the two steps after it are empty), step 48 combines and stores.  The
-// arithmetic, and its order, is that of wide_epilogue.
+// One chunk's record for this lane's request over the wavefront's 64 rows,
+// cut into small steps so that its vector instructions can be placed one
+// step after each MFMA of the next chunk (step t is a compile-time constant
+// at every call).  The accumulators start at zero: the bf16 products are
+// exact in fp32 and their partial sums stay exactly representable, so the
+// bias W2 h comes out exact in any summation order, and s = bias + U is the
+// value that the finish's rescan of a segment recomputes bit for bit (which
+// extreme temperatures, c ~ 1e30, need).
+// Draft: steps 0-15 form logit t (rows past V are -inf through U) and fold
+// them into the lane's maximum with 3-input maxima (after step 15 the
+// inputs may be overwritten); 16-31, only if a request of the wavefront is
+// greedy, find the lowest index of that maximum (scanning down); 32
+// combines the four lanes (lane & 15) + 16 j; 33-48, only if a request is
+// sampled, add the exponentials 2^((s - max) c); 49 combines and stores
+// (max, sum) or, for a greedy request, (max, argmax).  Residual: step 3 k
+// adds entry k of max(0, p - q) (the two steps after it are empty), step 48
+// combines and stores.
 constexpr int kEpiSteps = 50;
 
 template <bool RESID>
@@ -772,12 +741,13 @@ struct WideEpi {
   float s[RESID ? 1 : 16];
   float m, mg, z, c;
   int im, n;
+  bool greedy, sampled;  // wavefront-uniform: a request of the chunk is greedy / sampled
 };
 
 template <bool RESID>
-__device__ __forceinline__ void wide_epi_step(int t, const TileParams& p, int seg, int lane, const WideU<RESID>& f,
-                                              const f32x4_t (&acc)[4], bool live, WideEpi<RESID>& e) {
-  const int V = p.V;
+__device__ __forceinline__ void wide_epi_step(int t, const TileParams& p, int seg, bool full, int lane,
+                                              WideU<RESID>& f, const f32x4_t (&acc)[4], bool live,
+                                              WideEpi<RESID>& e) {
   const int vb = seg * kSegWide + 4 * (lane >> 4);
   auto store = [&](float x, float y) {
     const bool in_v = live && seg < p.n_seg;
@@ -790,25 +760,30 @@ __device__ __forceinline__ void wide_epi_step(int t, const TileParams& p, int se
       if (t == 0) {
         e.c = f.c;
         e.n = f.n;
+        e.im = 0;
+        e.greedy = __ballot(f.c == 0.f) != 0;
+        e.sampled = __ballot(f.c != 0.f) != 0;
+        wide_mask(full, seg * kSegWide, lane, p.V, f.u);
       }
-      const int b = t >> 2, i = t & 3;
-      e.s[t] = (vb + 16 * b + i < V) ? acc[b][i] + f.u[b][i] : -INFINITY;
+      e.s[t] = acc[t >> 2][t & 3] + f.u[t >> 2][t & 3];
+      if (t == 0) e.m = e.s[0];
+      if (t >= 2 && t % 2 == 0) e.m = fmaxf(fmaxf(e.m, e.s[t - 1]), e.s[t]);
+      if (t == 15) e.m = fmaxf(e.m, e.s[15]);
     } else if (t < 32) {
-      const int k = t - 16;
-      if (k == 0) {
-        e.m = e.s[0];
-        e.im = vb;
-      } else {
-        const bool gt = e.s[k] > e.m;
-        e.m = gt ? e.s[k] : e.m;
-        e.im = gt ? vb + 16 * (k >> 2) + (k & 3) : e.im;
+      if (e.greedy) {
+        const int k = 31 - t;  // 15 .. 0
+        if (k == 15) e.im = kIntMax;
+        e.im = (e.s[k] == e.m) ? vb + 16 * (k >> 2) + (k & 3) : e.im;
       }
     } else if (t == 32) {
-      quad_amax(e.m, e.im);
+      if (e.greedy)
+        quad_amax(e.m, e.im);
+      else
+        e.m = quad_max(e.m);
       e.mg = wide_exp_base(e.m);
       e.z = 0.f;
     } else if (t < 49) {
-      e.z += exp2_hw((e.s[t - 33] - e.mg) * e.c);
+      if (e.sampled) e.z += exp2_hw((e.s[t - 33] - e.mg) * e.c);
     } else if (t == 49) {
       store(e.m, (e.c > 0.f) ? quad_sum(e.z) : __int_as_float(e.im));
     }
@@ -818,15 +793,25 @@ __device__ __forceinline__ void wide_epi_step(int t, const TileParams& p, int se
       if (k == 0) {
         e.z = 0.f;
         e.n = f.n;
+        wide_mask(full, seg * kSegWide, lane, p.V, f.u);
+        wide_mask(full, seg * kSegWide, lane, p.V, f.t);
       }
       const float qq = exp2_hw((acc[b][i] + f.u[b][i] - f.Mq) * f.c) * f.iZq;
       const float pp = exp2_hw((f.t[b][i] - f.Mp) * f.c) * f.iZp;
-      const float d = fmaxf(pp - qq, 0.f);
-      e.z += __int_as_float(__float_as_int(d) & -static_cast<int>(vb + 16 * b + i < V));
+      e.z += fmaxf(pp - qq, 0.f);
     } else if (t == 48) {
       store(0.f, quad_sum(e.z));
     }
   }
+}
+
+// The whole epilogue of one chunk at once (the last chunk of the launch).
+template <bool RESID>
+__device__ __forceinline__ void wide_epilogue(const TileParams& p, int seg, bool full, int lane, WideU<RESID>& f,
+                                              const f32x4_t (&acc)[4]) {
+  WideEpi<RESID> e;
+#pragma unroll
+  for (int t = 0; t < kEpiSteps; ++t) wide_epi_step<RESID>(t, p, seg, full, lane, f, acc, true, e);
 }
 
 template <int KS, bool RESID, bool VEC4>
@@ -843,6 +828,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int n_win = (n_chunks + kWideWinChunks - 1) / kWideWinChunks;
   const int seg = blockIdx.x * 4 + wave;
   const int vw = seg * kSegWide;
+  const bool full = vw + kSegWide <= p.V;  // wavefront-uniform
   const int rank = p.rank;
 
   // window 0 (its loads are waited for at once: nothing else is in flight yet)
@@ -915,7 +901,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
           ha.v[q] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(hp[q]) * rank + min(g * 8, rank - 8));
         }
       }
-      if (j >= 4 && j < 4 + kEpiSteps) wide_epi_step<RESID>(j - 4, p, seg, lane, uf, acc_prev, c > 0, ep);
+      if (j >= 4 && j < 4 + kEpiSteps) wide_epi_step<RESID>(j - 4, p, seg, full, lane, uf, acc_prev, c > 0, ep);
       if (j == kUSlot) wide_u_issue<RESID, VEC4>(p, win1, c1, c1 % kWideWinChunks, vw, lane, uf);
       if (j == 60) wide_h_commit<KS>(hb, rank, Hs + (s ^ 1) * kStage);
     };
@@ -959,7 +945,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     c += 2;
   } while (c < n_chunks);
   // the last trip's second chunk
-  wide_epilogue<RESID>(p, seg, lane, ua, acc1, true);
+  wide_epilogue<RESID>(p, seg, full, lane, ua, acc1);
 }
 
 // ---------------------------------------------------------------------------

@@ -70,6 +70,14 @@ __device__ __forceinline__ float quad_sum(float x) {
   lane_pair32(__float_as_uint(x), lo, hi);
   return __uint_as_float(lo) + __uint_as_float(hi);
 }
+// maximum over the same four lanes
+__device__ __forceinline__ float quad_max(float x) {
+  uint32_t lo, hi;
+  lane_pair16(__float_as_uint(x), lo, hi);
+  x = fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+  lane_pair32(__float_as_uint(x), lo, hi);
+  return fmaxf(__uint_as_float(lo), __uint_as_float(hi));
+}
 // (max, lowest index of the max) over the same four lanes
 __device__ __forceinline__ void quad_amax(float& m, int& i) {
   uint32_t ml, mh, il, ih;

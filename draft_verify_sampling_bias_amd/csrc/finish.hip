@@ -117,6 +117,10 @@ void launch_draft_finish_nt(const FinishParams& p, int stage, hipStream_t s) {
   const dim3 grid(p.R), block(NT);
   if (stage == kStageSmall)
     hipLaunchKernelGGL((draft_finish_kernel<WT, kStageSmall, NT>), grid, block, 0, s, p);
+  else if (stage == kStageMid)
+    hipLaunchKernelGGL((draft_finish_kernel<WT, kStageMid, NT>), grid, block, 0, s, p);
+  else if (stage == kStageMid2)
+    hipLaunchKernelGGL((draft_finish_kernel<WT, kStageMid2, NT>), grid, block, 0, s, p);
   else if (stage == kStageRecs)
     hipLaunchKernelGGL((draft_finish_kernel<WT, kStageRecs, NT>), grid, block, 0, s, p);
   else
@@ -126,7 +130,7 @@ void launch_draft_finish_nt(const FinishParams& p, int stage, hipStream_t s) {
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
   const int num_cu = current_cu_count();
-  const int stage = p.n_seg <= kStageSmall ? kStageSmall : (p.n_seg <= kStageRecs ? kStageRecs : 0);
+  const int stage = stage_for(p.n_seg);
   // 1024 threads while every request's workgroup gets a CU of its own; more
   // requests than CUs run as several smaller workgroups per CU instead.  fp32
   // weights: the 32-row rescan's registers fit 256 threads per workgroup.
@@ -142,10 +146,14 @@ hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s)
 hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
   const dim3 grid(p.R), block(256);
-  const int stage = p.n_seg <= kStageSmall ? kStageSmall : (p.n_seg <= kStageRecs ? kStageRecs : 0);
+  const int stage = stage_for(p.n_seg);
   if (wdtype == DSPARK_W_BF16) {
     if (stage == kStageSmall)
       hipLaunchKernelGGL((residual_finish_kernel<uint16_t, kStageSmall>), grid, block, 0, s, p);
+    else if (stage == kStageMid)
+      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, kStageMid>), grid, block, 0, s, p);
+    else if (stage == kStageMid2)
+      hipLaunchKernelGGL((residual_finish_kernel<uint16_t, kStageMid2>), grid, block, 0, s, p);
     else if (stage == kStageRecs)
       hipLaunchKernelGGL((residual_finish_kernel<uint16_t, kStageRecs>), grid, block, 0, s, p);
     else
@@ -153,6 +161,10 @@ hipError_t launch_residual_finish(const VerifyParams& p, int wdtype, hipStream_t
   } else {
     if (stage == kStageSmall)
       hipLaunchKernelGGL((residual_finish_kernel<float, kStageSmall>), grid, block, 0, s, p);
+    else if (stage == kStageMid)
+      hipLaunchKernelGGL((residual_finish_kernel<float, kStageMid>), grid, block, 0, s, p);
+    else if (stage == kStageMid2)
+      hipLaunchKernelGGL((residual_finish_kernel<float, kStageMid2>), grid, block, 0, s, p);
     else if (stage == kStageRecs)
       hipLaunchKernelGGL((residual_finish_kernel<float, kStageRecs>), grid, block, 0, s, p);
     else

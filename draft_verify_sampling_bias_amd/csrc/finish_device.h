@@ -18,7 +18,7 @@ namespace dspark {
 
 // Rescan of one record segment: thread group i (NT / seg_rows lanes) owns
 // row v0 + i (256 threads: 16 lanes per row for 16-row segments, 8 for
-// 32-row, 4 for 64-row; 512 and 1024 threads: two and four times as many).
+// 32-row; 512 and 1024 threads: two and four times as many).
 template <int NT = 256>
 __device__ __forceinline__ int lanes_log2(int seg_rows) {
   static_assert(NT == 256 || NT == 512 || NT == 1024, "finish workgroups of 256, 512 or 1024 threads");
@@ -31,12 +31,21 @@ constexpr int kMaxSegRows = 64;
 // records, read one after another) sets the location's latency
 constexpr int kDraftFinishThreads = 1024;
 
-// Segment records of one request staged in LDS: up to 2048 records (16 KiB,
-// several workgroups per CU) or 16384 (128 KiB, i.e. V up to 262144 with
-// 16-row, 524288 with 32-row or 1048576 with 64-row segments); larger
+// Segment records of one request staged in LDS: up to 2048, 4096 or 8192
+// records (16, 32 or 64 KiB: several workgroups per CU) or 16384 (128 KiB,
+// i.e. V up to 262144 with 16-row or 524288 with 32-row segments); larger
 // vocabularies read the records from global memory instead.
 constexpr int kStageSmall = 2048;
+constexpr int kStageMid = 4096;
+constexpr int kStageMid2 = 8192;
 constexpr int kStageRecs = 16384;
+// the smallest stage that holds n_seg records, or 0 (read from global memory)
+inline int stage_for(int n_seg) {
+  return n_seg <= kStageSmall ? kStageSmall
+                              : (n_seg <= kStageMid ? kStageMid
+                                                    : (n_seg <= kStageMid2 ? kStageMid2
+                                                                           : (n_seg <= kStageRecs ? kStageRecs : 0)));
+}
 constexpr int kStageBatchRecs = 10240;  // records in flight per workgroup while staging
 
 // Records are copied into LDS in batches of kStageBatchRecs (kStageBatchRecs

@@ -613,15 +613,15 @@ int dspark_draft_block(const dspark_draft_args* args);
  * holds on each device it runs on until the process ends (its address is
  * looked up once per device; nothing is allocated or freed by the call).  A
  * call whose dspark_draft_workspace_size() exceeds that size returns
- * DSPARK_ERR_WORKSPACE and enqueues nothing (32 MiB holds, e.g., R = 1024 at
- * V = 129280 with 64-row segments, or R <= 64 at V up to 1048560 with 16-row
+ * DSPARK_ERR_WORKSPACE and enqueues nothing (64 MiB holds, e.g., R = 1024 at
+ * V = 129280 with 64-row segments, or R <= 64 at V up to 2097136 with 16-row
  * segments).  DSPARK_CHECK_INPUTS is refused (DSPARK_ERR_UNSUPPORTED): the
  * checks report through a caller's workspace.  Every call on one device
  * shares the array, and a call leaves its contents behind: calls that
  * overlap in time on one device (another stream, another host thread) race
  * and must be serialised by the caller.
  * -------------------------------------------------------------------------- */
-#define DSPARK_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define DSPARK_NOALLOC_SCRATCH_BYTES (64u << 20)
 int dspark_draft_block_noalloc(const dspark_draft_args* args);
 int dspark_schedule(const dspark_schedule_args* args);
 int dspark_schedule_cutoff(const dspark_cutoff_args* args);

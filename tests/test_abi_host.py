@@ -396,19 +396,19 @@ def test_noalloc_draft_refuses_before_enqueuing():
     """dspark_draft_block_noalloc: the size checks of dspark_draft_block, then
     the static workspace's limit and the refusal of the input checks, all on
     the host (fake pointers: none of these calls may reach a launch)."""
-    assert ds.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert ds.NOALLOC_SCRATCH_BYTES == 64 << 20
     fn = "dspark_draft_block_noalloc"
     assert _call(fn, _draft_args(struct_size=8)) == ds.Status.ERR_ABI
     assert _call(fn, _draft_args(gamma=0)) == ds.Status.ERR_SHAPE
     assert _call(fn, _draft_args(R=0)) == ds.Status.OK
     assert _call(fn, _draft_args(flags=ds.CHECK_INPUTS)) == ds.Status.ERR_UNSUPPORTED
     # 16-row path: 512 bytes of records per 16 vocabulary entries + the header
-    assert ds.draft_workspace_bytes(64, 7, 1048560, 512, 1) <= ds.NOALLOC_SCRATCH_BYTES
-    big = 1048576
+    assert ds.draft_workspace_bytes(64, 7, 2097136, 512, 1) <= ds.NOALLOC_SCRATCH_BYTES
+    big = 2097152
     assert ds.draft_workspace_bytes(64, 7, big, 512, 1) > ds.NOALLOC_SCRATCH_BYTES
     assert _call(fn, _draft_args(R=64, gamma=7, V=big, rank=512)) == ds.Status.ERR_WORKSPACE
-    # 64-row path: R = 1024 at V = 129280 fits, R = 4096 does not
+    # 64-row path: R = 1024 at V = 129280 fits, R = 8192 does not
     assert ds.draft_workspace_bytes(1024, 5, 129280, 512, 1) <= ds.NOALLOC_SCRATCH_BYTES
-    assert ds.draft_workspace_bytes(4096, 5, 129280, 512, 1) > ds.NOALLOC_SCRATCH_BYTES
-    assert _call(fn, _draft_args(R=4096, gamma=5, V=129280, rank=512)) == ds.Status.ERR_WORKSPACE
+    assert ds.draft_workspace_bytes(8192, 5, 129280, 512, 1) > ds.NOALLOC_SCRATCH_BYTES
+    assert _call(fn, _draft_args(R=8192, gamma=5, V=129280, rank=512)) == ds.Status.ERR_WORKSPACE
     assert ds.get_lib().dspark_draft_block_noalloc(None) == ds.Status.ERR_NULL
