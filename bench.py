@@ -49,7 +49,8 @@ sys.path.insert(0, ROOT)
 METRIC = "draft+verify positions/sec (R×gamma) and achieved HBM GB/s at V=151936"
 HBM_PEAK_GBPS = 8000.0
 # committed FETCH_SIZE / WRITE_SIZE summaries of the fused kernel, per workload
-TRAFFIC_FILES = {3: os.path.join(ROOT, "profiles", "bias_seg16_config3_traffic.txt"),
+TRAFFIC_FILES = {2: os.path.join(ROOT, "profiles", "bias_seg16_config2_traffic.txt"),
+                 3: os.path.join(ROOT, "profiles", "bias_seg16_config3_traffic.txt"),
                  5: os.path.join(ROOT, "profiles", "bias_seg64_config5_traffic.txt")}
 
 

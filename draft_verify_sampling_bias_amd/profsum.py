@@ -8,7 +8,9 @@
 `stats` condenses a `--kernel-trace --stats` kernel table (calls, total and
 average duration per kernel).  `calls` lists one kernel's durations from a
 `--kernel-trace` table in call order, grouped per size of a sweep.  `mfma` reports a kernel's bf16 MFMA work and
-utilisation from SQ counters and its traced average duration.  `traffic` turns two `--pmc FETCH_SIZE` /
+utilisation from SQ counters and its traced average duration.  `sq` averages
+any SQ counters of one kernel per dispatch over several `--pmc` runs and
+derives the shares of wave cycles.  `traffic` turns two `--pmc FETCH_SIZE` /
 `--pmc WRITE_SIZE` runs (KiB per dispatch) into HBM bytes per launch of one
 kernel, each counter scaled by what it reads for a device copy of known size
 (the calibration runs), and records a SHA-256 over the fused bias kernel's
@@ -159,6 +161,41 @@ def mfma_text(kernel, counters_csv, stats_csv, flops_per_launch, peak_tflops, co
     return "\n".join(lines) + "\n"
 
 
+def sq_text(kernel, csvs, commands):
+    """Per-dispatch averages (summed over the chip) of every counter found for
+    one kernel in the given counter CSVs, with the shares of wave cycles."""
+    table = {}
+    n_disp = {}
+    for path in csvs:
+        names = {r["Counter_Name"] for r in csv.DictReader(open(path))}
+        for cn in sorted(names):
+            vals = _pick(_per_dispatch(path, cn), kernel)
+            table[cn] = sum(vals) / len(vals)
+            n_disp[cn] = len(vals)
+    lines = ["# SQ counters per dispatch of one kernel (summed over the chip, averaged over its dispatches)",
+             *[f"# command: {c}" for c in commands],
+             f"kernel: {kernel}",
+             f"kernel_source_sha256_16: {tile_source_hash()}",
+             f"dispatches: {min(n_disp.values())}"]
+    lines += [f"{k}: {v:.0f}" for k, v in sorted(table.items())]
+    wc = table.get("SQ_WAVE_CYCLES")
+    waves = table.get("SQ_WAVES")
+    if wc:
+        lines.append("# derived (SQ_WAVE_CYCLES and the active / wait counters count in the same units)")
+        for k in ("SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_VMEM",
+                  "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_LDS"):
+            if k in table:
+                lines.append(f"share_of_wave_cycles_{k[3:].lower()}: {table[k] / wc:.3f}")
+    if waves:
+        for k in ("SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD"):
+            if k in table:
+                lines.append(f"per_wavefront_{k[3:].lower()}: {table[k] / waves:.0f}")
+    if "SQ_LDS_BANK_CONFLICT" in table and "SQ_INSTS_LDS" in table:
+        lines.append(f"lds_bank_conflict_cycles_per_lds_instruction: "
+                     f"{table['SQ_LDS_BANK_CONFLICT'] / table['SQ_INSTS_LDS']:.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path):
     """key: value pairs of a traffic summary (comments skipped)."""
     out = {}
@@ -198,7 +235,14 @@ def main(argv=None):
     m.add_argument("--flops", type=int, required=True)
     m.add_argument("--peak-tflops", type=float, default=2500.0)
     m.add_argument("--commands", action="append", default=[])
+    q = sub.add_parser("sq")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--counters", action="append", required=True)
+    q.add_argument("--commands", action="append", default=[])
     a = ap.parse_args(argv)
+    if a.mode == "sq":
+        sys.stdout.write(sq_text(a.kernel, a.counters, a.commands))
+        return
     if a.mode == "calls":
         sys.stdout.write(calls_text(a.trace_csv, a.kernel, a.group, a.labels.split(","), a.command))
         return
