@@ -115,15 +115,23 @@ def test_exact_cells_gamma1_lossless(T):
     uf = np.array([c[3] for c in cells], np.float32)
     for c, a, b, f in zip(cells, ud[:, 0], ua[:, 0], uf):
         assert emitted(float(a), float(b), float(f)) == c[4], "an fp32 representative left its cell"
-    outs = _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf)
-    dist1 = np.zeros(V)
-    for c, o in zip(cells, outs):
-        dist1[o[0]] += c[0]
-        assert tuple(o) == c[4], f"GPU output {o} differs from the oracle's {c[4]} inside a cell"
+    assert len(cells) > 64  # one batch takes the 64-row path
     p0 = _softmax(target[0] / T)
-    dev = np.abs(dist1 - p0).max()
-    print(f"[exact T={T}] {len(cells)} cells, first-token distribution = p_0 within {dev:.3g}", flush=True)
-    assert dev < 3 * 16 * 2.0 ** -24, (dist1, p0)
+    # all cells in one batch (64-row path), then in batches of at most 64
+    # requests (16-row path)
+    for batch, path in ((len(cells), "64-row"), (64, "16-row")):
+        outs = []
+        for i in range(0, len(cells), batch):
+            sl = slice(i, i + batch)
+            outs += _gpu_rounds(U, target, W1, W2, anchor, T, ud[sl], ua[sl], uf[sl])
+        dist1 = np.zeros(V)
+        for c, o in zip(cells, outs):
+            dist1[o[0]] += c[0]
+            assert tuple(o) == c[4], f"{path}: GPU output {o} differs from the oracle's {c[4]} inside a cell"
+        dev = np.abs(dist1 - p0).max()
+        print(f"[exact T={T} {path}] {len(cells)} cells, first-token distribution = p_0 within {dev:.3g}",
+              flush=True)
+        assert dev < 3 * 16 * 2.0 ** -24, (dist1, p0)
 
 
 @pytest.mark.parametrize("R,calls", [(8192, 64), (64, 1024)], ids=["wide", "seg16"])
