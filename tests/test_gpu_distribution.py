@@ -15,14 +15,15 @@ k-th emitted token must follow p_{k-1} (given that it is emitted).
   u_accept at p/q, then u_final into the CDF intervals of the residual or
   the bonus), found by bisection on the oracle; the GPU runs once at every
   cell's midpoint, in one batch, and the distribution it induces (cell
-  lengths times its outputs) must equal p_0.  The uniforms are fp32, so
+  lengths times its outputs) must equal p_0; on each of the three paths.  The uniforms are fp32, so
   every cell boundary the bisection finds is the real one moved by at most
   half an fp32 ulp (2^-25 below 1): with at most 16 boundaries in each of
   the three uniforms a token's mass is off by at most 3 * 16 * 2^-24 < 3e-6,
   the tolerance used.  (A GPU boundary that moved by less than the fp32
   rounding of the CDF would not show.)
-* Monte Carlo: gamma = 2, 2^19 trials on the 64-row path (R = 8192 per call)
-  and 2^16 on the 16-row path (R = 64 per call), each emitted position
+* Monte Carlo: gamma = 2, 2^19 trials on the 64-row path (R = 8192 per call),
+  2^16 on the 16-row path (R = 64 per call) and 2^17 on the fp32 path
+  (R = 4096 per call), each emitted position
   against its p by a chi-square test (fixed seeds; a p-value above 1e-4)
   and every frequency within 5 standard errors.
 """
@@ -58,10 +59,11 @@ def _round(seed, gamma):
     return U, target, W1, W2, 3
 
 
-def _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf):
+def _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf, f32=False):
     """Run draft -> fixed-length schedule -> verify for R = len(uf) copies of
     the round with the given uniforms; returns the emitted tokens per request
-    (a list of lists)."""
+    (a list of lists).  f32: the same (bf16-exact) weights as fp32 arrays,
+    which takes the fp32 path."""
     import draft_verify_sampling_bias_amd as ds
     dev = "cuda:0"
     R, gamma = ud.shape
@@ -70,8 +72,11 @@ def _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     Ud = t(np.broadcast_to(U, (R, gamma, V)))
-    W1d = torch.from_numpy(W1.view(np.int16)).to(dev).view(torch.bfloat16)
-    W2d = torch.from_numpy(W2.view(np.int16)).to(dev).view(torch.bfloat16)
+    if f32:
+        W1d, W2d = t(synth.bf16_bits_to_f32(W1)), t(synth.bf16_bits_to_f32(W2))
+    else:
+        W1d = torch.from_numpy(W1.view(np.int16)).to(dev).view(torch.bfloat16)
+        W2d = torch.from_numpy(W2.view(np.int16)).to(dev).view(torch.bfloat16)
     anc = t(np.full(R, anchor, np.int32))
     temp = t(np.full(R, T, np.float32))
     y, q_tok, q_stats = ds.dspark_draft_block(Ud, W1d, W2d, anc, temp, t(ud))
@@ -117,13 +122,13 @@ def test_exact_cells_gamma1_lossless(T):
         assert emitted(float(a), float(b), float(f)) == c[4], "an fp32 representative left its cell"
     assert len(cells) > 64  # one batch takes the 64-row path
     p0 = _softmax(target[0] / T)
-    # all cells in one batch (64-row path), then in batches of at most 64
-    # requests (16-row path)
-    for batch, path in ((len(cells), "64-row"), (64, "16-row")):
+    # all cells in one batch (64-row path), in batches of at most 64
+    # requests (16-row path), and with fp32 weights (32-row path)
+    for batch, path, f32 in ((len(cells), "64-row", False), (64, "16-row", False), (len(cells), "fp32", True)):
         outs = []
         for i in range(0, len(cells), batch):
             sl = slice(i, i + batch)
-            outs += _gpu_rounds(U, target, W1, W2, anchor, T, ud[sl], ua[sl], uf[sl])
+            outs += _gpu_rounds(U, target, W1, W2, anchor, T, ud[sl], ua[sl], uf[sl], f32=f32)
         dist1 = np.zeros(V)
         for c, o in zip(cells, outs):
             dist1[o[0]] += c[0]
@@ -134,8 +139,9 @@ def test_exact_cells_gamma1_lossless(T):
         assert dev < 3 * 16 * 2.0 ** -24, (dist1, p0)
 
 
-@pytest.mark.parametrize("R,calls", [(8192, 64), (64, 1024)], ids=["wide", "seg16"])
-def test_monte_carlo_emitted_tokens_follow_p(R, calls):
+@pytest.mark.parametrize("R,calls,f32", [(8192, 64, False), (64, 1024, False), (4096, 32, True)],
+                         ids=["wide", "seg16", "fp32"])
+def test_monte_carlo_emitted_tokens_follow_p(R, calls, f32):
     gamma, T = 2, 0.8
     U, target, W1, W2, anchor = _round(12, gamma)
     p = [_softmax(target[j] / T) for j in range(gamma + 1)]
@@ -145,7 +151,7 @@ def test_monte_carlo_emitted_tokens_follow_p(R, calls):
         ud = rng.random((R, gamma), dtype=np.float32)
         ua = rng.random((R, gamma), dtype=np.float32)
         uf = rng.random(R, dtype=np.float32)
-        for toks in _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf):
+        for toks in _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf, f32=f32):
             for j, tok in enumerate(toks):
                 counts[j, tok] += 1
     n_trials = R * calls
