@@ -23,7 +23,7 @@ k-th emitted token must follow p_{k-1} (given that it is emitted).
   rounding of the CDF would not show.)
 * Monte Carlo: gamma = 2, 2^19 trials on the 64-row path (R = 8192 per call),
   2^16 on the 16-row path (R = 64 per call) and 2^17 on the fp32 path
-  (R = 4096 per call), each emitted position
+  (R = 4096 per call), and 2^16 with the RNN head, each emitted position
   against its p by a chi-square test (fixed seeds; a p-value above 1e-4)
   and every frequency within 5 standard errors.
 """
@@ -59,11 +59,12 @@ def _round(seed, gamma):
     return U, target, W1, W2, 3
 
 
-def _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf, f32=False):
+def _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf, f32=False, A=None):
     """Run draft -> fixed-length schedule -> verify for R = len(uf) copies of
     the round with the given uniforms; returns the emitted tokens per request
     (a list of lists).  f32: the same (bf16-exact) weights as fp32 arrays,
-    which takes the fp32 path."""
+    which takes the fp32 path.  A: the RNN head's recurrence (bf16 bits),
+    tanh; None for the Markov head."""
     import draft_verify_sampling_bias_amd as ds
     dev = "cuda:0"
     R, gamma = ud.shape
@@ -79,11 +80,16 @@ def _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf, f32=False):
         W2d = torch.from_numpy(W2.view(np.int16)).to(dev).view(torch.bfloat16)
     anc = t(np.full(R, anchor, np.int32))
     temp = t(np.full(R, T, np.float32))
-    y, q_tok, q_stats = ds.dspark_draft_block(Ud, W1d, W2d, anc, temp, t(ud))
+    h = None
+    if A is None:
+        y, q_tok, q_stats = ds.dspark_draft_block(Ud, W1d, W2d, anc, temp, t(ud))
+    else:
+        Ad = torch.from_numpy(A.view(np.int16)).to(dev).view(torch.bfloat16)
+        y, q_tok, q_stats, h = ds.dspark_draft_block(Ud, W1d, W2d, anc, temp, t(ud), A=Ad, act=1)
     sch = ds.dspark_schedule(t(np.ones((R, gamma), np.float32)), R * gamma, anc, y)
     rows = t(np.tile(target, (R, 1)))  # every request verifies gamma positions: gamma + 1 rows each
     n_acc, out_tok, _ = ds.dspark_verify(rows, sch["row_offsets"], Ud, W1d, W2d, anc, temp, y, q_tok, q_stats,
-                                         t(ua), t(uf))
+                                         t(ua), t(uf), h=h)
     torch.cuda.synchronize()
     y, n_acc, out_tok = y.cpu().numpy(), n_acc.cpu().numpy(), out_tok.cpu().numpy()
     assert (sch["l"].cpu().numpy() == gamma).all()
@@ -139,11 +145,13 @@ def test_exact_cells_gamma1_lossless(T):
         assert dev < 3 * 16 * 2.0 ** -24, (dist1, p0)
 
 
-@pytest.mark.parametrize("R,calls,f32", [(8192, 64, False), (64, 1024, False), (4096, 32, True)],
-                         ids=["wide", "seg16", "fp32"])
-def test_monte_carlo_emitted_tokens_follow_p(R, calls, f32):
+@pytest.mark.parametrize("R,calls,f32,rnn", [(8192, 64, False, False), (64, 1024, False, False),
+                                             (4096, 32, True, False), (64, 1024, False, True)],
+                         ids=["wide", "seg16", "fp32", "seg16-rnn"])
+def test_monte_carlo_emitted_tokens_follow_p(R, calls, f32, rnn):
     gamma, T = 2, 0.8
     U, target, W1, W2, anchor = _round(12, gamma)
+    A = synth.make_rnn_A(12, RANK, scale=1.2) if rnn else None
     p = [_softmax(target[j] / T) for j in range(gamma + 1)]
     counts = np.zeros((gamma + 1, V), np.int64)
     rng = np.random.default_rng(1234 + R)
@@ -151,7 +159,7 @@ def test_monte_carlo_emitted_tokens_follow_p(R, calls, f32):
         ud = rng.random((R, gamma), dtype=np.float32)
         ua = rng.random((R, gamma), dtype=np.float32)
         uf = rng.random(R, dtype=np.float32)
-        for toks in _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf, f32=f32):
+        for toks in _gpu_rounds(U, target, W1, W2, anchor, T, ud, ua, uf, f32=f32, A=A):
             for j, tok in enumerate(toks):
                 counts[j, tok] += 1
     n_trials = R * calls
