@@ -410,22 +410,36 @@ __device__ __forceinline__ void seg16_info_h(const TileParams& p, const Pos& ps,
   lds_barrier();
 }
 
-// Wavefront w of the grid handles segments w, w + W, w + 2W, ... (W = all
-// wavefronts), so at any moment the grid streams one contiguous stretch of
-// W2 and of every U row: DRAM pages are read whole instead of 64 bytes from
-// each of 64 rows.  `fa` holds the loads of the wavefront's first segment
-// sg, already issued; H and the request info are in LDS.
-template <int KS, bool RESID, bool VEC4, bool PACKED, int NB, bool SPLIT>
+// The segments are dealt out in rounds of W = all wavefronts: round j is the
+// contiguous stretch [j W, (j + 1) W), so at any moment the grid streams one
+// stretch of W2 and of every U row (DRAM pages are read whole instead of 64
+// bytes from each of 64 rows).  Workgroup b owns the WPB segments
+// j W + b WPB + [0, WPB) of every round, in ticket order t = j WPB + i.  Its
+// wavefront i starts on ticket i and then takes the next free ticket of the
+// workgroup from an LDS counter, so a wavefront that streams faster takes
+// more of its workgroup's segments instead of waiting at the end.  `fa`
+// holds the loads of the wavefront's first segment sg, already issued; H
+// and the request info are in LDS, and *ctr (LDS) was set to WPB before the
+// last barrier.
+template <int KS, bool RESID, bool VEC4, bool PACKED, int NB, bool SPLIT, int WPB>
 __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, const uint16_t* Hs,
                                            const ReqInfo* s_ci, int sg, Seg16Regs<KS, RESID, NB>& fa,
-                                           Seg16Regs<KS, RESID, NB>& fb) {
+                                           Seg16Regs<KS, RESID, NB>& fb, int* ctr) {
   constexpr bool DBUF = RESID;  // see seg16_mfma
   const int lane = threadIdx.x & 63;
   const int rank = p.rank, n_seg = p.n_seg;
-  const int n_waves = gridDim.x * (blockDim.x >> 6);
+  const int n_waves = gridDim.x * WPB;
   if (sg >= n_seg) return;
   LaneReq<RESID, NB> lq;
   lane_req<RESID, NB>(s_ci, lane, lq);
+  // the segment of the workgroup's next free ticket (segments grow with the
+  // ticket, so once one is past n_seg every later one is too)
+  auto take = [&]() {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(ctr, 1);
+    t = __builtin_amdgcn_readfirstlane(t);
+    return static_cast<int>(blockIdx.x) * WPB + (t % WPB) + (t / WPB) * n_waves;
+  };
   // Ping-pong prefetch, the next segment's loads interleaved with the
   // current one's k-steps.  The prefetch issued on a wavefront's last
   // segment re-reads segment n_seg - 1 (a cache hit, never used) so that the
@@ -433,12 +447,12 @@ __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, c
   // trip.
   while (true) {
     f32x4_t acc[NB];
-    const int s1 = sg + n_waves;
+    const int s1 = take();
     seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB, SPLIT>(fa.w, Hs, rank, lane, acc, p, ps, s_ci,
                                                  min(s1, n_seg - 1) * kSegSmall, fb);
     seg16_epilogue<KS, RESID, NB>(p, lq, sg, lane, fa, acc);
     if (s1 >= n_seg) break;
-    const int s2 = s1 + n_waves;
+    const int s2 = take();
     seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB, SPLIT>(fb.w, Hs, rank, lane, acc, p, ps, s_ci,
                                                  min(s2, n_seg - 1) * kSegSmall, fa);
     seg16_epilogue<KS, RESID, NB>(p, lq, s1, lane, fb, acc);
@@ -448,9 +462,10 @@ __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, c
 }
 
 template <int KS, bool RESID, bool VEC4, int WPB, bool PACKED, int NB, bool SPLIT>
-__device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci) {
+__device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* Hs, ReqInfo* s_ci, int* ctr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int R = p.R, n_seg = p.n_seg;
+  if (tid == 0) *ctr = WPB;  // published by the barriers of seg16_info_h
   if (RESID) {
     int any = 0;
     for (int n = tid; n < R; n += WPB * 64) any |= p.rs_info[4 * static_cast<int64_t>(n)];
@@ -468,7 +483,7 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
   // residual mode: the first segment's loads come after the barrier (their
   // U and target rows come from the request info)
   if (RESID) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
-  seg16_walk<KS, RESID, VEC4, PACKED, NB, SPLIT>(p, ps, Hs, s_ci, sg, fa, fb);
+  seg16_walk<KS, RESID, VEC4, PACKED, NB, SPLIT, WPB>(p, ps, Hs, s_ci, sg, fa, fb, ctr);
 }
 
 // Draft mode: one workgroup of eight wavefronts per CU (two per SIMD, for
@@ -480,7 +495,8 @@ bias_seg16(TileParams p) {
   constexpr int RS = KS * 32 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Hs[(SPLIT ? 2 : 1) * NB * 16 * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves, PACKED, NB, SPLIT>(p, Hs, s_ci);
+  __shared__ int ctr;
+  bias_seg16_body<KS, false, VEC4, kSeg16DraftWaves, PACKED, NB, SPLIT>(p, Hs, s_ci, &ctr);
 }
 
 // Residual mode (holds the target values too): one wavefront per SIMD.
@@ -489,7 +505,8 @@ __global__ void __launch_bounds__(kSeg16Waves * 64) bias_seg16_res(TileParams p)
   constexpr int RS = KS * 32 + 8;
   __shared__ __attribute__((aligned(16))) uint16_t Hs[(SPLIT ? 2 : 1) * NB * 16 * RS];
   __shared__ ReqInfo s_ci[kSmallMaxR];
-  bias_seg16_body<KS, true, VEC4, kSeg16Waves, PACKED, NB, SPLIT>(p, Hs, s_ci);
+  __shared__ int ctr;
+  bias_seg16_body<KS, true, VEC4, kSeg16Waves, PACKED, NB, SPLIT>(p, Hs, s_ci, &ctr);
 }
 
 // ---------------------------------------------------------------------------
