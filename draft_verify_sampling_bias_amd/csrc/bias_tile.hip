@@ -74,10 +74,12 @@ __device__ __forceinline__ Pos pos_of(const TileParams& p) {
   return Pos{p.prev_base, p.prev_stride, p.U_base, p.h_base, p.h_stride};
 }
 
+// Every load is issued before the first value is used (the temperature's
+// scale, computed under a branch, would otherwise hold back the others).
 __device__ __forceinline__ ReqInfo fetch_info(const TileParams& p, const Pos& ps, int n, bool resid) {
   ReqInfo ci{0, 0, 0, 0, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (n >= p.R) return ci;
-  ci.c = temp_scale(p.temp[n]);
+  const float T = p.temp[n];
   if (!resid) {
     ci.act = 1;
     ci.prev = ps.prev_base[static_cast<int64_t>(n) * ps.prev_stride];
@@ -93,6 +95,7 @@ __device__ __forceinline__ ReqInfo fetch_info(const TileParams& p, const Pos& ps
     ci.Mp = st[2];
     ci.iZp = 1.0f / st[3];
   }
+  ci.c = temp_scale(T);
   ci.prev = clampi(ci.prev, 0, p.V - 1);
   // rows of inactive requests are never used, but their loads are still
   // issued: keep every row index inside its buffer
@@ -322,6 +325,7 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
 
 constexpr int kSeg16Waves = 4;     // residual mode: wavefronts per workgroup, one per SIMD
 constexpr int kSeg16DraftWaves = 8;  // draft mode: one workgroup per CU, two wavefronts per SIMD
+constexpr int kSeg16GatherWaves = 4;  // draft mode: wavefronts that gather H
 
 // H of the RNN head: request nn's fp32 state row (draft mode: h_base +
 // nn * h_stride; residual mode: row urow of h_base, stride rank) split into
@@ -330,20 +334,24 @@ constexpr int kSeg16DraftWaves = 8;  // draft mode: one workgroup per CU, two wa
 // per k-step compute W2 h with exact products.
 // Rows of inactive requests and groups past the rank are zero.  The caller
 // has stored the request info (s_ci) and passed a barrier.
-template <int KS, bool RESID, int WPB, int NB>
+template <int KS, bool RESID, int GW, int NB>
 __device__ __forceinline__ void seg16_state_h(const TileParams& p, const Pos& ps, uint16_t* Hs,
                                               const ReqInfo* s_ci) {
   constexpr int RS = KS * 32 + 8;
   constexpr int G = KS * 4;
   constexpr int kPieces = NB * 16 * G;
-  constexpr int kPer = (kPieces + WPB * 64 - 1) / (WPB * 64);
+  constexpr int kPer = (kPieces + GW * 64 - 1) / (GW * 64);
   constexpr int kPlane = NB * 16 * RS;
   const int tid = threadIdx.x;
   const int rank = p.rank;
+  if (tid >= GW * 64) {
+    lds_barrier();
+    return;
+  }
   f32x4_t va[kPer], vb[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int q = min(tid + j * WPB * 64, kPieces - 1);
+    const int q = min(tid + j * GW * 64, kPieces - 1);
     const int nn = q / G, g = q - nn * G;
     const int64_t row = RESID ? static_cast<int64_t>(s_ci[nn].urow) * rank
                               : static_cast<int64_t>(nn < p.R ? nn : 0) * ps.h_stride;
@@ -353,7 +361,7 @@ __device__ __forceinline__ void seg16_state_h(const TileParams& p, const Pos& ps
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int q = tid + j * WPB * 64;
+    const int q = tid + j * GW * 64;
     const int nn = q / G, g = q - nn * G;
     const bool zero = g * 8 >= rank || !s_ci[nn].act;
     u32x4_t hi, lo;
@@ -367,7 +375,7 @@ __device__ __forceinline__ void seg16_state_h(const TileParams& p, const Pos& ps
       hi[e] = zero ? 0u : (h0 | (h1 << 16));
       lo[e] = zero ? 0u : (l0 | (l1 << 16));
     }
-    if (kPieces % (WPB * 64) == 0 || q < kPieces) {
+    if (kPieces % (GW * 64) == 0 || q < kPieces) {
       *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = hi;
       *reinterpret_cast<u32x4_t*>(&Hs[kPlane + nn * RS + g * 8]) = lo;
     }
@@ -377,35 +385,40 @@ __device__ __forceinline__ void seg16_state_h(const TileParams& p, const Pos& ps
 
 // Request info and H = W1[prev] for all requests of the 16-row path, into
 // LDS (the workgroup's first barrier comes after the info, the second after
-// H).  Every 16-byte load of this thread is issued before any is stored.
-template <int KS, bool RESID, int WPB, int NB, bool SPLIT>
+// H).  The info is read by wavefront 0 and H by the first GW wavefronts;
+// every 16-byte load of a thread is issued before any is stored.
+template <int KS, bool RESID, int GW, int NB, bool SPLIT>
 __device__ __forceinline__ void seg16_info_h(const TileParams& p, const Pos& ps, uint16_t* Hs, ReqInfo* s_ci) {
   constexpr int RS = KS * 32 + 8;  // LDS row stride of H (bf16): 16-byte pad vs bank conflicts
   constexpr int G = KS * 4;        // 16-byte groups per H row
   constexpr int kPieces = NB * 16 * G;  // 16-byte pieces of the NB * 16 H rows
-  constexpr int kPer = (kPieces + WPB * 64 - 1) / (WPB * 64);
+  constexpr int kPer = (kPieces + GW * 64 - 1) / (GW * 64);
   const int tid = threadIdx.x;
   const int rank = p.rank;
   if (tid < kSmallMaxR) s_ci[tid] = fetch_info(p, ps, tid, RESID);
   lds_barrier();
   if constexpr (SPLIT) {
-    seg16_state_h<KS, RESID, WPB, NB>(p, ps, Hs, s_ci);
+    seg16_state_h<KS, RESID, GW, NB>(p, ps, Hs, s_ci);
+    return;
+  }
+  if (tid >= GW * 64) {
+    lds_barrier();
     return;
   }
   u32x4_t val[kPer];
   const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int q = min(tid + j * WPB * 64, kPieces - 1);
+    const int q = min(tid + j * GW * 64, kPieces - 1);
     const int nn = q / G, g = q - nn * G;
     val[j] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(s_ci[nn].prev) * rank + min(g * 8, rank - 8));
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int q = tid + j * WPB * 64;
+    const int q = tid + j * GW * 64;
     const int nn = q / G, g = q - nn * G;
     const u32x4_t v = (g * 8 >= rank || !s_ci[nn].act) ? u32x4_t{0u, 0u, 0u, 0u} : val[j];
-    if (kPieces % (WPB * 64) == 0 || q < kPieces) *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
+    if (kPieces % (GW * 64) == 0 || q < kPieces) *reinterpret_cast<u32x4_t*>(&Hs[nn * RS + g * 8]) = v;
   }
   lds_barrier();
 }
@@ -472,17 +485,24 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
     if (!__syncthreads_or(any)) return;
   }
   // wavefront-uniform walk state (scalar registers, scalar branches)
-  const int sg = blockIdx.x * WPB + __builtin_amdgcn_readfirstlane(wave);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int sg = blockIdx.x * WPB + wv;
   Seg16Regs<KS, RESID, NB> fa, fb;
   const Pos ps = pos_of(p);
   // draft mode: the first segment's W2 and U addresses depend on neither H
-  // nor the request info, so its loads go out first and are in flight
-  // while the request info and the H rows (prev -> W1[prev]) arrive
-  if (!RESID) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
-  seg16_info_h<KS, RESID, WPB, NB, SPLIT>(p, ps, Hs, s_ci);
+  // nor the request info, so the wavefronts that do not gather H issue its
+  // loads first, and they are in flight while the request info and the H
+  // rows (prev -> W1[prev]) arrive.  The gathering wavefronts issue theirs
+  // after H: a wavefront's loads complete in issue order, so H loads queued
+  // behind a segment's would wait for the segment.  The RNN head's fp32
+  // states (twice the bytes of W1 rows) are gathered by every wavefront.
+  constexpr int GW = (RESID || SPLIT) ? WPB : kSeg16GatherWaves;
+  const bool early = !RESID && wv >= GW;
+  if (early) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  seg16_info_h<KS, RESID, GW, NB, SPLIT>(p, ps, Hs, s_ci);
   // residual mode: the first segment's loads come after the barrier (their
   // U and target rows come from the request info)
-  if (RESID) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  if (!early) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
   seg16_walk<KS, RESID, VEC4, PACKED, NB, SPLIT, WPB>(p, ps, Hs, s_ci, sg, fa, fb, ctr);
 }
 
