@@ -31,6 +31,13 @@ __global__ void __launch_bounds__(NT) draft_finish_kernel(FinishParams p) {
   draft_finish_one<WT, STAGE, NT>(p, blockIdx.x, p.k, p.prev_base, p.prev_stride, p.U_base, sm, srec);
 }
 
+template <typename WT, int NT, int J>
+__global__ void __launch_bounds__(NT) draft_finish_waves_kernel(FinishParams p) {
+  __shared__ WaveFinishSmem<NT> sm;
+  if (p.err_clear != nullptr && (blockIdx.x | threadIdx.x) == 0) *p.err_clear = 0u;
+  draft_finish_waves<WT, NT, J>(p, sm);
+}
+
 template <typename WT, int STAGE>
 __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   constexpr bool STAGED = STAGE > 0;
@@ -134,7 +141,19 @@ hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s)
   // 1024 threads while every request's workgroup gets a CU of its own; more
   // requests than CUs run as several smaller workgroups per CU instead.  fp32
   // weights: the 32-row rescan's registers fit 256 threads per workgroup.
-  if (wdtype == DSPARK_W_BF16 && p.R <= num_cu)
+  // 16-row segments: the wave-range finish, its records in registers
+  if (wdtype == DSPARK_W_BF16 && p.seg_rows == kSegSmall && p.n_seg <= kDraftFinishThreads * kWaveFinishJ) {
+    const dim3 grid(p.R), block(kDraftFinishThreads);
+    if (p.n_seg <= kDraftFinishThreads * 4)
+      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, 4>), grid, block, 0, s, p);
+    else if (p.n_seg <= kDraftFinishThreads * 8)
+      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, 8>), grid, block, 0, s, p);
+    else if (p.n_seg <= kDraftFinishThreads * 12)
+      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, 12>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, kWaveFinishJ>), grid, block, 0,
+                         s, p);
+  } else if (wdtype == DSPARK_W_BF16 && p.R <= num_cu)
     launch_draft_finish_nt<uint16_t, kDraftFinishThreads>(p, stage, s);
   else if (wdtype == DSPARK_W_BF16)
     launch_draft_finish_nt<uint16_t, 256>(p, stage, s);

@@ -241,4 +241,240 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wave-range draft finish (16-row segments, n_seg <= NT * kWaveFinishJ)
+// ---------------------------------------------------------------------------
+// Wavefront w owns the contiguous records [w P, w P + n_w) (P = ceil(n_seg /
+// NW)); lane l holds records w P + 64 j + l (j < L = ceil(n_w / 64)) in
+// registers, read with coalesced loads.  Each wavefront publishes one pair,
+// (max, lowest argmax) for a greedy request or (max m_w, mass sum s_w in
+// units of 2^((. - m_w) c)) for a sampled one, and the workgroup meets at
+// its only barrier.  Every wavefront then combines the NW pairs, one per
+// lane, in the same order, so all agree on M, Z and on the wavefront whose
+// range holds u Z.  That wavefront alone finds the record: it transposes its
+// masses through LDS so that lane l holds the run [l L, l L + L) of its
+// range, scans the lanes' run sums, walks the chosen lane's run, and
+// rescans the segment's 16 rows, four lanes per row.
+constexpr int kWaveFinishJ = 16;  // records per lane at most (n_seg <= 16384 with 1024 threads)
+template <int NT>
+struct WaveFinishSmem {
+  float hs[DSPARK_MAX_RANK];
+  float wm[NT / 64];
+  float ws[NT / 64];
+  int wi[NT / 64];
+  float tx[64 * kWaveFinishJ];  // the chosen wavefront's masses, then its record maxima
+};
+
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+template <typename WT, int NT, int J>
+__device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFinishSmem<NT>& sm) {
+  constexpr int NW = NT / 64;
+  static_assert(NW <= 64, "one wavefront pair per lane");
+  const int n = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int V = p.V, n_seg = p.n_seg;
+  const float2* rec = reinterpret_cast<const float2*>(p.part) + static_cast<int64_t>(n) * n_seg;
+  const int64_t o = static_cast<int64_t>(n) * p.gamma + p.k;
+  // loads that depend on nothing first, then the records, then h (whose
+  // address waits only for prev), all in flight together
+  const float T = p.temp[n];
+  const int prev = clampi(p.prev_base[static_cast<int64_t>(n) * p.prev_stride], 0, V - 1);
+  const float u_raw = p.u_draft[o];
+  const int per_w = (n_seg + NW - 1) / NW;
+  const int w0 = wave * per_w;
+  const int n_w = max(0, min(per_w, n_seg - w0));
+  const int L = (n_w + 63) >> 6;  // wavefront-uniform, <= J
+  float2 r[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j < L) r[j] = rec[w0 + min(j * 64 + lane, n_w - 1)];
+  HRow<WT, NT> hrow;
+  if (p.hstate != nullptr)
+    hrow.hold_state(p.hstate + o * p.rank, p.rank);
+  else
+    hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
+  const float c = temp_scale(T);  // the same for the whole workgroup
+  const bool greedy = c == 0.0f;
+  // records past the wavefront's range: no mass, never the maximum
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < L) {
+      const bool in = j * 64 + lane < n_w;
+      r[j].x = in ? r[j].x : -INFINITY;
+      r[j].y = in ? r[j].y : (greedy ? __int_as_float(kIntMax) : 0.0f);
+    }
+  }
+  if (greedy) {
+    // the records carry their lowest argmax in the second word
+    float m = -INFINITY;
+    int im = kIntMax;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (j < L) amax_merge(m, im, r[j].x, __float_as_int(r[j].y));
+    wave_amax(m, im);
+    if (lane == 0) {
+      sm.wm[wave] = m;
+      sm.wi[wave] = im;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      m = lane < NW ? sm.wm[lane] : -INFINITY;
+      im = lane < NW ? sm.wi[lane] : kIntMax;
+      wave_amax(m, im);
+      if (lane == 0) {
+        p.y[o] = clampi(im, 0, V - 1);
+        p.q_tok[o] = 1.0f;
+        p.q_stats[2 * o] = m;
+        p.q_stats[2 * o + 1] = 1.0f;
+      }
+    }
+    return;
+  }
+  // sampled: the wavefront's maximum and its mass sum relative to it
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j < L) m = fmaxf(m, r[j].x);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j < L) s += r[j].y * exp2_rel(r[j].x, m, c);
+  s = wave_sum(s);
+  hrow.commit(p.rank, sm.hs);
+  if (lane == 0) {
+    sm.wm[wave] = m;
+    sm.ws[wave] = s;
+  }
+  __syncthreads();
+  // every wavefront, lane w holding wavefront w's pair: M, the masses in
+  // units of 2^((. - M) c), their inclusive prefix and Z; the wavefront
+  // whose interval holds theta = u Z, else the last one with mass (the
+  // fallback that takes the last positive entry)
+  const float mw = lane < NW ? sm.wm[lane] : -INFINITY;
+  const float sw = lane < NW ? sm.ws[lane] : 0.0f;
+  float M = mw;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) M = fmaxf(M, __shfl_xor(M, d));
+  const float S = sw * exp2_rel(mw, M, c);
+  const float incl = wave_incl_scan(S);
+  const float iup = __shfl_up(incl, 1);
+  const float excl = (lane == 0) ? 0.0f : iup;  // [excl, incl) of consecutive lanes meet exactly
+  const float Z = readlane_f(incl, 63);
+  const float theta = clamp_uniform(u_raw) * Z;
+  const unsigned long long whit = __ballot(S > 0.0f && incl > theta);
+  const unsigned long long wpos = __ballot(S > 0.0f);
+  bool fb = whit == 0;
+  const int wfin = whit ? (__ffsll(static_cast<long long>(whit)) - 1)
+                        : (wpos ? 63 - __clzll(static_cast<long long>(wpos)) : 0);
+  if (wave != wfin) return;
+  // second level: the masses of this wavefront's records (position q =
+  // 64 j + lane of its range) through LDS to lane q / L, so that each lane
+  // holds a run of consecutive records; the lane whose run holds th = theta
+  // - P, then the first record of that run whose running mass passes it
+  const float th = fb ? INFINITY : theta - readlane_f(excl, wfin);
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j < L) sm.tx[j * 64 + lane] = r[j].y * exp2_rel(r[j].x, M, c);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const int l0 = lane * L;
+  float x[J];
+  float tot = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    x[j] = (j < L) ? sm.tx[l0 + j] : 0.0f;
+    tot += x[j];
+  }
+  const float cum = wave_incl_scan(tot);
+  const float cup = __shfl_up(cum, 1);
+  const float ex = (lane == 0) ? 0.0f : cup;
+  // each lane walks its own run from its exclusive prefix: the first record
+  // past th, and the last record with mass
+  int jsel = -1, jlast = -1;
+  float psel = 0.0f, plast = 0.0f, run = ex;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < L) {
+      const float nxt = run + x[j];
+      const bool pos = x[j] > 0.0f;
+      const bool take = jsel < 0 && pos && nxt > th;
+      psel = take ? run : psel;
+      jsel = take ? j : jsel;
+      plast = pos ? run : plast;
+      jlast = pos ? j : jlast;
+      run = nxt;
+    }
+  }
+  const unsigned long long hit = __ballot(tot > 0.0f && cum > th);
+  const unsigned long long any = __ballot(tot > 0.0f);
+  int q = -1;  // position of the chosen record in the wavefront's range
+  float selP = 0.0f;
+  if (hit) {
+    // the lane whose interval [ex, cum) holds th; if its own walk stops
+    // short of th by rounding, its last record with mass is taken
+    const int ls = __ffsll(static_cast<long long>(hit)) - 1;
+    const int js = __builtin_amdgcn_readlane(jsel, ls);
+    const bool found = js >= 0;
+    q = ls * L + (found ? js : __builtin_amdgcn_readlane(jlast, ls));
+    selP = readlane_f(found ? psel : plast, ls);
+    fb = fb || !found;
+  } else if (any) {
+    const int ll = 63 - __clzll(static_cast<long long>(any));
+    q = ll * L + __builtin_amdgcn_readlane(jlast, ll);
+    selP = readlane_f(plast, ll);
+    fb = true;
+  } else {
+    fb = true;
+  }
+  // the chosen record's maximum, through the same LDS (every lane has read
+  // its masses above)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j < L && j * 64 + lane == q) sm.tx[0] = r[j].x;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const float ms = q >= 0 ? sm.tx[0] : M;
+  const int seg = q >= 0 ? w0 + q : 0;
+  const float ths = fb ? INFINITY : (th - selP) / exp2_rel(ms, M, c);
+  // rescan of the segment's 16 rows: four lanes per row
+  const int v0 = seg * kSegSmall;
+  const int i = lane >> 2;
+  const int v = v0 + i;
+  const float uv = p.U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
+  const float b = row_bias<WT, 2>(static_cast<const WT*>(p.W2), sm.hs, p.rank, v, V, 2);
+  float sv = -INFINITY, e = 0.0f;
+  if (v < V) {
+    sv = uv + b;
+    e = exp2_rel(sv, ms, c);
+  }
+  // row i's weight and logit to lane i, then the inverse-CDF pick in the row
+  const float el = __shfl(e, (lane & 15) * 4);
+  const float sl = __shfl(sv, (lane & 15) * 4);
+  const float xl = lane < kSegSmall ? el : 0.0f;
+  const float cl = wave_incl_scan(xl);
+  const unsigned long long rhit = __ballot(xl > 0.0f && cl > ths);
+  const unsigned long long rpos = __ballot(xl > 0.0f);
+  const int pk = rhit ? (__ffsll(static_cast<long long>(rhit)) - 1)
+                      : (rpos ? 63 - __clzll(static_cast<long long>(rpos)) : -1);
+  if (lane == 0) {
+    const int yy = (pk >= 0) ? v0 + pk : min(v0, V - 1);
+    const float sy = (pk >= 0) ? readlane_f(sl, pk) : M;
+    p.y[o] = yy;
+    p.q_tok[o] = exp2_hw((sy - M) * c) / Z;
+    p.q_stats[2 * o] = M;
+    p.q_stats[2 * o + 1] = Z;
+  }
+}
+
 }  // namespace dspark
