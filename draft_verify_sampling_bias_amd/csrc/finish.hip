@@ -31,11 +31,25 @@ __global__ void __launch_bounds__(NT) draft_finish_kernel(FinishParams p) {
   draft_finish_one<WT, STAGE, NT>(p, blockIdx.x, p.k, p.prev_base, p.prev_stride, p.U_base, sm, srec);
 }
 
-template <typename WT, int NT, int J>
+template <typename WT, int NT, int J, int SEG>
 __global__ void __launch_bounds__(NT) draft_finish_waves_kernel(FinishParams p) {
   __shared__ WaveFinishSmem<NT> sm;
   if (p.err_clear != nullptr && (blockIdx.x | threadIdx.x) == 0) *p.err_clear = 0u;
-  draft_finish_waves<WT, NT, J>(p, sm);
+  draft_finish_waves<WT, NT, J, SEG>(p, sm);
+}
+
+// the wave-range finish with records per lane J chosen from n_seg
+template <int NT, int SEG>
+void launch_draft_finish_waves(const FinishParams& p, hipStream_t s) {
+  const dim3 grid(p.R), block(NT);
+  if (p.n_seg <= NT * 4)
+    hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, 4, SEG>), grid, block, 0, s, p);
+  else if (p.n_seg <= NT * 8)
+    hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, 8, SEG>), grid, block, 0, s, p);
+  else if (p.n_seg <= NT * 12)
+    hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, 12, SEG>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, kWaveFinishJ, SEG>), grid, block, 0, s, p);
 }
 
 template <typename WT, int STAGE>
@@ -139,20 +153,19 @@ hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s)
   const int num_cu = current_cu_count();
   const int stage = stage_for(p.n_seg);
   // 1024 threads while every request's workgroup gets a CU of its own; more
-  // requests than CUs run as several smaller workgroups per CU instead.  fp32
-  // weights: the 32-row rescan's registers fit 256 threads per workgroup.
-  // 16-row segments: the wave-range finish, its records in registers
-  if (wdtype == DSPARK_W_BF16 && p.seg_rows == kSegSmall && p.n_seg <= kDraftFinishThreads * kWaveFinishJ) {
-    const dim3 grid(p.R), block(kDraftFinishThreads);
-    if (p.n_seg <= kDraftFinishThreads * 4)
-      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, 4>), grid, block, 0, s, p);
-    else if (p.n_seg <= kDraftFinishThreads * 8)
-      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, 8>), grid, block, 0, s, p);
-    else if (p.n_seg <= kDraftFinishThreads * 12)
-      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, 12>), grid, block, 0, s, p);
+  // requests than CUs run as several smaller workgroups per CU instead.  bf16
+  // weights with 16- or 64-row segments take the wave-range finish (records
+  // in registers) up to kWaveFinishJ records per lane, the staged-record
+  // finish beyond.  fp32 weights: the 32-row rescan's registers fit 256
+  // threads per workgroup.
+  const bool waves = wdtype == DSPARK_W_BF16 && (p.seg_rows == kSegSmall || p.seg_rows == kSegWide);
+  if (waves && p.R <= num_cu && p.n_seg <= kDraftFinishThreads * kWaveFinishJ) {
+    if (p.seg_rows == kSegSmall)
+      launch_draft_finish_waves<kDraftFinishThreads, kSegSmall>(p, s);
     else
-      hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, kDraftFinishThreads, kWaveFinishJ>), grid, block, 0,
-                         s, p);
+      launch_draft_finish_waves<kDraftFinishThreads, kSegWide>(p, s);
+  } else if (waves && p.seg_rows == kSegWide && p.n_seg <= 256 * kWaveFinishJ) {
+    launch_draft_finish_waves<256, kSegWide>(p, s);
   } else if (wdtype == DSPARK_W_BF16 && p.R <= num_cu)
     launch_draft_finish_nt<uint16_t, kDraftFinishThreads>(p, stage, s);
   else if (wdtype == DSPARK_W_BF16)

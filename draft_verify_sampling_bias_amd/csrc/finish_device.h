@@ -242,7 +242,8 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
 }
 
 // ---------------------------------------------------------------------------
-// Wave-range draft finish (16-row segments, n_seg <= NT * kWaveFinishJ)
+// Wave-range draft finish (bf16 weights, 16- or 64-row segments, n_seg <=
+// NT * kWaveFinishJ)
 // ---------------------------------------------------------------------------
 // Wavefront w owns the contiguous records [w P, w P + n_w) (P = ceil(n_seg /
 // NW)); lane l holds records w P + 64 j + l (j < L = ceil(n_w / 64)) in
@@ -253,8 +254,11 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
 // lane, in the same order, so all agree on M, Z and on the wavefront whose
 // range holds u Z.  That wavefront alone finds the record: it transposes its
 // masses through LDS so that lane l holds the run [l L, l L + L) of its
-// range, scans the lanes' run sums, walks the chosen lane's run, and
-// rescans the segment's 16 rows, four lanes per row.
+// range, scans the lanes' run sums and walks the chosen lane's run.  A
+// 16-row segment it then rescans alone, four lanes per row; a 64-row one it
+// hands to the whole workgroup through LDS (a second barrier), which
+// rescans it with NT / 64 lanes per row before wavefront 0 picks the entry
+// (a third).
 constexpr int kWaveFinishJ = 16;  // records per lane at most (n_seg <= 16384 with 1024 threads)
 template <int NT>
 struct WaveFinishSmem {
@@ -263,14 +267,179 @@ struct WaveFinishSmem {
   float ws[NT / 64];
   int wi[NT / 64];
   float tx[64 * kWaveFinishJ];  // the chosen wavefront's masses, then its record maxima
+  // 64-row segments: the chosen segment, its threshold and maximum, and the
+  // rescanned rows' weights and logits
+  int hseg;
+  float hths, hms;
+  float e64[kMaxSegRows], s64[kMaxSegRows];
 };
 
 __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-template <typename WT, int NT, int J>
+// The chosen wavefront's second level (see draft_finish_waves) and, for a
+// 16-row segment, its rescan and the stores; for a 64-row segment the
+// hand-over of (segment, threshold, maximum) through LDS.
+template <typename WT, int NT, int J, int SEG>
+__device__ __forceinline__ void draft_finish_waves_pick(const FinishParams& p, WaveFinishSmem<NT>& sm,
+                                                        const float2 (&r)[J], int n, int64_t o, int w0, int L,
+                                                        float M, float Z, float c, float theta, float P, bool fb) {
+  const int lane = threadIdx.x & 63;
+  const int V = p.V;
+  // second level: the masses of this wavefront's records (position q =
+  // 64 j + lane of its range) through LDS to lane q / L, so that each lane
+  // holds a run of consecutive records; the lane whose run holds th = theta
+  // - P, then the first record of that run whose running mass passes it
+  const float th = fb ? INFINITY : theta - P;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j < L) sm.tx[j * 64 + lane] = r[j].y * exp2_rel(r[j].x, M, c);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const int l0 = lane * L;
+  float x[J];
+  float tot = 0.0f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    x[j] = (j < L) ? sm.tx[l0 + j] : 0.0f;
+    tot += x[j];
+  }
+  const float cum = wave_incl_scan(tot);
+  const float cup = __shfl_up(cum, 1);
+  const float ex = (lane == 0) ? 0.0f : cup;
+  // each lane walks its own run from its exclusive prefix: the first record
+  // past th, and the last record with mass
+  int jsel = -1, jlast = -1;
+  float psel = 0.0f, plast = 0.0f, run = ex;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (j < L) {
+      const float nxt = run + x[j];
+      const bool pos = x[j] > 0.0f;
+      const bool take = jsel < 0 && pos && nxt > th;
+      psel = take ? run : psel;
+      jsel = take ? j : jsel;
+      plast = pos ? run : plast;
+      jlast = pos ? j : jlast;
+      run = nxt;
+    }
+  }
+  const unsigned long long hit = __ballot(tot > 0.0f && cum > th);
+  const unsigned long long any = __ballot(tot > 0.0f);
+  int q = -1;  // position of the chosen record in the wavefront's range
+  float selP = 0.0f;
+  if (hit) {
+    // the lane whose interval [ex, cum) holds th; if its own walk stops
+    // short of th by rounding, its last record with mass is taken
+    const int ls = __ffsll(static_cast<long long>(hit)) - 1;
+    const int js = __builtin_amdgcn_readlane(jsel, ls);
+    const bool found = js >= 0;
+    q = ls * L + (found ? js : __builtin_amdgcn_readlane(jlast, ls));
+    selP = readlane_f(found ? psel : plast, ls);
+    fb = fb || !found;
+  } else if (any) {
+    const int ll = 63 - __clzll(static_cast<long long>(any));
+    q = ll * L + __builtin_amdgcn_readlane(jlast, ll);
+    selP = readlane_f(plast, ll);
+    fb = true;
+  } else {
+    fb = true;
+  }
+  // the chosen record's maximum, through the same LDS (every lane has read
+  // its masses above)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    if (j < L && j * 64 + lane == q) sm.tx[0] = r[j].x;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const float ms = q >= 0 ? sm.tx[0] : M;
+  const int seg = q >= 0 ? w0 + q : 0;
+  const float ths = fb ? INFINITY : (th - selP) / exp2_rel(ms, M, c);
+  if constexpr (SEG == kSegWide) {
+    if (lane == 0) {
+      sm.hseg = seg;
+      sm.hths = ths;
+      sm.hms = ms;
+    }
+    return;
+  }
+  // rescan of the segment's 16 rows: four lanes per row
+  const int v0 = seg * kSegSmall;
+  const int i = lane >> 2;
+  const int v = v0 + i;
+  const float uv = p.U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
+  const float b = row_bias<WT, 2>(static_cast<const WT*>(p.W2), sm.hs, p.rank, v, V, 2);
+  float sv = -INFINITY, e = 0.0f;
+  if (v < V) {
+    sv = uv + b;
+    e = exp2_rel(sv, ms, c);
+  }
+  // row i's weight and logit to lane i, then the inverse-CDF pick in the row
+  const float el = __shfl(e, (lane & 15) * 4);
+  const float sl = __shfl(sv, (lane & 15) * 4);
+  const float xl = lane < kSegSmall ? el : 0.0f;
+  const float cl = wave_incl_scan(xl);
+  const unsigned long long rhit = __ballot(xl > 0.0f && cl > ths);
+  const unsigned long long rpos = __ballot(xl > 0.0f);
+  const int pk = rhit ? (__ffsll(static_cast<long long>(rhit)) - 1)
+                      : (rpos ? 63 - __clzll(static_cast<long long>(rpos)) : -1);
+  if (lane == 0) {
+    const int yy = (pk >= 0) ? v0 + pk : min(v0, V - 1);
+    const float sy = (pk >= 0) ? readlane_f(sl, pk) : M;
+    p.y[o] = yy;
+    p.q_tok[o] = exp2_hw((sy - M) * c) / Z;
+    p.q_stats[2 * o] = M;
+    p.q_stats[2 * o + 1] = Z;
+  }
+}
+
+// Rescan of the handed-over 64-row segment by the whole workgroup (NT / 64
+// lanes per row), then wavefront 0's pick and the stores.
+template <typename WT, int NT>
+__device__ __forceinline__ void draft_finish_rescan64(const FinishParams& p, WaveFinishSmem<NT>& sm, int n, int64_t o,
+                                                      float M, float Z, float c) {
+  const int tid = threadIdx.x;
+  const int V = p.V;
+  const int seg = sm.hseg;
+  const float ths = sm.hths, ms = sm.hms;
+  constexpr int kLg = NT == 1024 ? 4 : (NT == 512 ? 3 : 2);  // log2 of the lanes per row
+  const int v0 = seg * kSegWide;
+  const int i = tid >> kLg;
+  const int v = v0 + i;
+  const float uv = p.U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
+  const float b = row_bias<WT, kLg>(static_cast<const WT*>(p.W2), sm.hs, p.rank, v, V, kLg);
+  if ((tid & ((1 << kLg) - 1)) == 0) {
+    float sv = -INFINITY, e = 0.0f;
+    if (v < V) {
+      sv = uv + b;
+      e = exp2_rel(sv, ms, c);
+    }
+    sm.e64[i] = e;
+    sm.s64[i] = sv;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int pos = pick64(sm.e64, kSegWide, ths);
+    if (tid == 0) {
+      const int yy = (pos >= 0) ? v0 + pos : min(v0, V - 1);
+      const float sy = (pos >= 0) ? sm.s64[pos] : M;
+      p.y[o] = yy;
+      p.q_tok[o] = exp2_hw((sy - M) * c) / Z;
+      p.q_stats[2 * o] = M;
+      p.q_stats[2 * o + 1] = Z;
+    }
+  }
+}
+
+template <typename WT, int NT, int J, int SEG>
 __device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFinishSmem<NT>& sm) {
+  static_assert(SEG == kSegSmall || SEG == kSegWide, "16- or 64-row segments");
   constexpr int NW = NT / 64;
   static_assert(NW <= 64, "one wavefront pair per lane");
   const int n = blockIdx.x;
@@ -372,108 +541,11 @@ __device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFi
   bool fb = whit == 0;
   const int wfin = whit ? (__ffsll(static_cast<long long>(whit)) - 1)
                         : (wpos ? 63 - __clzll(static_cast<long long>(wpos)) : 0);
-  if (wave != wfin) return;
-  // second level: the masses of this wavefront's records (position q =
-  // 64 j + lane of its range) through LDS to lane q / L, so that each lane
-  // holds a run of consecutive records; the lane whose run holds th = theta
-  // - P, then the first record of that run whose running mass passes it
-  const float th = fb ? INFINITY : theta - readlane_f(excl, wfin);
-#pragma unroll
-  for (int j = 0; j < J; ++j)
-    if (j < L) sm.tx[j * 64 + lane] = r[j].y * exp2_rel(r[j].x, M, c);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  const int l0 = lane * L;
-  float x[J];
-  float tot = 0.0f;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    x[j] = (j < L) ? sm.tx[l0 + j] : 0.0f;
-    tot += x[j];
-  }
-  const float cum = wave_incl_scan(tot);
-  const float cup = __shfl_up(cum, 1);
-  const float ex = (lane == 0) ? 0.0f : cup;
-  // each lane walks its own run from its exclusive prefix: the first record
-  // past th, and the last record with mass
-  int jsel = -1, jlast = -1;
-  float psel = 0.0f, plast = 0.0f, run = ex;
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    if (j < L) {
-      const float nxt = run + x[j];
-      const bool pos = x[j] > 0.0f;
-      const bool take = jsel < 0 && pos && nxt > th;
-      psel = take ? run : psel;
-      jsel = take ? j : jsel;
-      plast = pos ? run : plast;
-      jlast = pos ? j : jlast;
-      run = nxt;
-    }
-  }
-  const unsigned long long hit = __ballot(tot > 0.0f && cum > th);
-  const unsigned long long any = __ballot(tot > 0.0f);
-  int q = -1;  // position of the chosen record in the wavefront's range
-  float selP = 0.0f;
-  if (hit) {
-    // the lane whose interval [ex, cum) holds th; if its own walk stops
-    // short of th by rounding, its last record with mass is taken
-    const int ls = __ffsll(static_cast<long long>(hit)) - 1;
-    const int js = __builtin_amdgcn_readlane(jsel, ls);
-    const bool found = js >= 0;
-    q = ls * L + (found ? js : __builtin_amdgcn_readlane(jlast, ls));
-    selP = readlane_f(found ? psel : plast, ls);
-    fb = fb || !found;
-  } else if (any) {
-    const int ll = 63 - __clzll(static_cast<long long>(any));
-    q = ll * L + __builtin_amdgcn_readlane(jlast, ll);
-    selP = readlane_f(plast, ll);
-    fb = true;
-  } else {
-    fb = true;
-  }
-  // the chosen record's maximum, through the same LDS (every lane has read
-  // its masses above)
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-#pragma unroll
-  for (int j = 0; j < J; ++j)
-    if (j < L && j * 64 + lane == q) sm.tx[0] = r[j].x;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  const float ms = q >= 0 ? sm.tx[0] : M;
-  const int seg = q >= 0 ? w0 + q : 0;
-  const float ths = fb ? INFINITY : (th - selP) / exp2_rel(ms, M, c);
-  // rescan of the segment's 16 rows: four lanes per row
-  const int v0 = seg * kSegSmall;
-  const int i = lane >> 2;
-  const int v = v0 + i;
-  const float uv = p.U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
-  const float b = row_bias<WT, 2>(static_cast<const WT*>(p.W2), sm.hs, p.rank, v, V, 2);
-  float sv = -INFINITY, e = 0.0f;
-  if (v < V) {
-    sv = uv + b;
-    e = exp2_rel(sv, ms, c);
-  }
-  // row i's weight and logit to lane i, then the inverse-CDF pick in the row
-  const float el = __shfl(e, (lane & 15) * 4);
-  const float sl = __shfl(sv, (lane & 15) * 4);
-  const float xl = lane < kSegSmall ? el : 0.0f;
-  const float cl = wave_incl_scan(xl);
-  const unsigned long long rhit = __ballot(xl > 0.0f && cl > ths);
-  const unsigned long long rpos = __ballot(xl > 0.0f);
-  const int pk = rhit ? (__ffsll(static_cast<long long>(rhit)) - 1)
-                      : (rpos ? 63 - __clzll(static_cast<long long>(rpos)) : -1);
-  if (lane == 0) {
-    const int yy = (pk >= 0) ? v0 + pk : min(v0, V - 1);
-    const float sy = (pk >= 0) ? readlane_f(sl, pk) : M;
-    p.y[o] = yy;
-    p.q_tok[o] = exp2_hw((sy - M) * c) / Z;
-    p.q_stats[2 * o] = M;
-    p.q_stats[2 * o + 1] = Z;
+  if (wave == wfin) draft_finish_waves_pick<WT, NT, J, SEG>(p, sm, r, n, o, w0, L, M, Z, c, theta,
+                                                             readlane_f(excl, wfin), fb);
+  if constexpr (SEG == kSegWide) {
+    __syncthreads();
+    draft_finish_rescan64<WT, NT>(p, sm, n, o, M, Z, c);
   }
 }
 
