@@ -157,6 +157,29 @@ int dspark_draft_block(const dspark_draft_args* a) {
     fp.hstate = a->h;
   }
 
+  // the RNN head's state of position k + 1: z = A h_k by the fused bias
+  // kernel of position k (as extra segments of its walk), act(z + W1[y_k])
+  // by the finish of position k, when that finish can (the state kernel then
+  // runs for k = 0 only)
+  const bool fused = rnn && draft_finish_fuses_state(fp, a->wdtype);
+  if (fused) {
+    fp.A = static_cast<const uint16_t*>(a->A);
+    fp.act = a->act;
+    if (tp.w2p != nullptr) {
+      // A in the fused kernel's fragment-packed layout, like W2
+      dspark_pack_w2_args pk{};
+      pk.struct_size = sizeof(pk);
+      pk.W2 = a->A;
+      pk.V = a->rank;
+      pk.rank = a->rank;
+      pk.W2_packed = ws_at<uint16_t>(a->workspace, plan.ap_off);
+      pk.W2_packed_bytes = w2_packed_bytes(a->rank, a->rank);
+      pk.stream = a->stream;
+      st = hip_status(launch_pack_w2(pk, s));
+      if (st != DSPARK_OK) return st;
+      tp.ap = static_cast<const uint16_t*>(pk.W2_packed);
+    }
+  }
   const int cu = current_cu_count();
   for (int k = 0; k < a->gamma; ++k) {
     // prev = anchor for the first position, the token drafted just before otherwise
@@ -165,9 +188,16 @@ int dspark_draft_block(const dspark_draft_args* a) {
     tp.U_base = a->U + static_cast<int64_t>(k) * a->V;
     if (rnn) {
       rp.k = k;
-      st = hip_status(launch_rnn_state(rp, s));
-      if (st != DSPARK_OK) return st;
+      if (k == 0 || !fused) {
+        st = hip_status(launch_rnn_state(rp, s));
+        if (st != DSPARK_OK) return st;
+      }
       tp.h_base = a->h + static_cast<int64_t>(k) * a->rank;
+      // fused: this position's kernel also computes A h into the next state row
+      const bool next = fused && k + 1 < a->gamma;
+      tp.n_seg_a = next ? (a->rank + kSegSmall - 1) / kSegSmall : 0;
+      tp.A = static_cast<const uint16_t*>(a->A);
+      tp.z_out = next ? a->h + static_cast<int64_t>(k + 1) * a->rank : nullptr;
     }
     hipEvent_t e0 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k]) : nullptr;
     hipEvent_t e1 = a->prof_events ? static_cast<hipEvent_t>(a->prof_events[2 * k + 1]) : nullptr;

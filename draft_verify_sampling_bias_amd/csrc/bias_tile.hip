@@ -139,8 +139,16 @@ struct Seg16Regs {
 // past V and the rank), or from the row-major W2, where rows past V re-read
 // row V - 1 and columns k >= rank re-read the row's last 8 weights (both
 // masked at use).
-template <int KS, bool PACKED>
+// ASEG (the RNN head's draft mode): a segment past the vocabulary's holds
+// rows vw - 16 n_seg .. +16 of A instead, in the same layout (rows past the
+// rank re-read row rank - 1, or are zero in the packed copy; never stored).
+template <int KS, bool PACKED, bool ASEG = false>
 __device__ __forceinline__ const uint16_t* seg16_w2(const TileParams& p, int vw, int lane) {
+  if (ASEG && vw >= p.n_seg * kSegSmall) {
+    const int va = vw - p.n_seg * kSegSmall;
+    if (PACKED) return p.ap + (static_cast<int64_t>(va / kSegSmall) * KS * 64 + lane) * 8;
+    return p.A + static_cast<int64_t>(min(va + (lane & 15), p.rank - 1)) * p.rank;
+  }
   if (PACKED) return p.w2p + (static_cast<int64_t>(vw / kSegSmall) * KS * 64 + lane) * 8;
   return static_cast<const uint16_t*>(p.W2) + static_cast<int64_t>(min(vw + (lane & 15), p.V - 1)) * p.rank;
 }
@@ -153,12 +161,12 @@ __device__ __forceinline__ bf16x8_t seg16_w2_frag(const uint16_t* w2, int ks, in
 // Issues the loads of segment [vw, vw + 16).  No instruction touches the
 // loaded registers before the MFMA or the epilogue needs them (the rank and
 // vocabulary masks are applied at use).
-template <int KS, bool RESID, bool VEC4, bool PACKED, int NB>
+template <int KS, bool RESID, bool VEC4, bool PACKED, int NB, bool ASEG = false>
 __device__ __forceinline__ void seg16_load(const TileParams& p, const Pos& ps, const ReqInfo* s_ci, int vw, int lane,
                                            Seg16Regs<KS, RESID, NB>& f) {
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V, rank = p.rank;
-  const uint16_t* w2 = seg16_w2<KS, PACKED>(p, vw, lane);
+  const uint16_t* w2 = seg16_w2<KS, PACKED, ASEG>(p, vw, lane);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) f.w[ks] = seg16_w2_frag<KS, PACKED>(w2, ks, lane, rank);
   const int vu = vw + kq * 4;
@@ -188,7 +196,7 @@ __device__ __forceinline__ void seg16_mfma_pf(const bf16x8_t (&w)[KS], const uin
   constexpr int NP = SPLIT ? 2 : 1;
   const int l16 = lane & 15, kq = lane >> 4;
   const int V = p.V;
-  const uint16_t* w2n = seg16_w2<KS, PACKED>(p, vw_next, lane);
+  const uint16_t* w2n = seg16_w2<KS, PACKED, SPLIT && !RESID>(p, vw_next, lane);
   const int vu = vw_next + kq * 4;
   auto issue_u = [&](int nb) {
     const int nn = nb * 16 + l16;
@@ -323,6 +331,26 @@ __device__ __forceinline__ void seg16_epilogue(const TileParams& p, const LaneRe
   }
 }
 
+// RNN head, draft mode: the segment wt >= n_seg holds rows (wt - n_seg) * 16
+// .. +16 of A; z = A h of request 16 nb + (lane & 15), rows 4 (lane >> 4)
+// .. +4 of the segment, stored as fp32 for the next state (rows past the
+// rank and absent requests are not stored).
+template <int NB>
+__device__ __forceinline__ void seg16_store_z(const TileParams& p, int wt, int lane, const f32x4_t (&acc)[NB]) {
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int j0 = (wt - p.n_seg) * kSegSmall + kq * 4;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int nn = nb * 16 + l16;
+    if (nn < p.R) {
+      float* z = p.z_out + static_cast<int64_t>(nn) * p.h_stride;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j0 + i < p.rank) z[j0 + i] = acc[nb][i];
+    }
+  }
+}
+
 constexpr int kSeg16Waves = 4;     // residual mode: wavefronts per workgroup, one per SIMD
 constexpr int kSeg16DraftWaves = 8;  // draft mode: one workgroup per CU, two wavefronts per SIMD
 constexpr int kSeg16GatherWaves = 4;  // draft mode: wavefronts that gather H
@@ -439,10 +467,12 @@ __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, c
                                            const ReqInfo* s_ci, int sg, Seg16Regs<KS, RESID, NB>& fa,
                                            Seg16Regs<KS, RESID, NB>& fb, int* ctr) {
   constexpr bool DBUF = RESID;  // see seg16_mfma
+  constexpr bool ASEG = SPLIT && !RESID;
   const int lane = threadIdx.x & 63;
   const int rank = p.rank, n_seg = p.n_seg;
+  const int n_walk = ASEG ? n_seg + p.n_seg_a : n_seg;  // with the RNN head's A segments
   const int n_waves = gridDim.x * WPB;
-  if (sg >= n_seg) return;
+  if (sg >= n_walk) return;
   LaneReq<RESID, NB> lq;
   lane_req<RESID, NB>(s_ci, lane, lq);
   // the segment of the workgroup's next free ticket (segments grow with the
@@ -458,18 +488,24 @@ __device__ __forceinline__ void seg16_walk(const TileParams& p, const Pos& ps, c
   // segment re-reads segment n_seg - 1 (a cache hit, never used) so that the
   // load stream, and with it the compiler's wait counts, is the same every
   // trip.
+  auto finish = [&](int wt, const Seg16Regs<KS, RESID, NB>& f, const f32x4_t (&acc)[NB]) {
+    if (ASEG && wt >= n_seg)
+      seg16_store_z<NB>(p, wt, lane, acc);
+    else
+      seg16_epilogue<KS, RESID, NB>(p, lq, wt, lane, f, acc);
+  };
   while (true) {
     f32x4_t acc[NB];
     const int s1 = take();
     seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB, SPLIT>(fa.w, Hs, rank, lane, acc, p, ps, s_ci,
-                                                 min(s1, n_seg - 1) * kSegSmall, fb);
-    seg16_epilogue<KS, RESID, NB>(p, lq, sg, lane, fa, acc);
-    if (s1 >= n_seg) break;
+                                                 min(s1, n_walk - 1) * kSegSmall, fb);
+    finish(sg, fa, acc);
+    if (s1 >= n_walk) break;
     const int s2 = take();
     seg16_mfma_pf<KS, RESID, VEC4, DBUF, PACKED, NB, SPLIT>(fb.w, Hs, rank, lane, acc, p, ps, s_ci,
-                                                 min(s2, n_seg - 1) * kSegSmall, fa);
-    seg16_epilogue<KS, RESID, NB>(p, lq, s1, lane, fb, acc);
-    if (s2 >= n_seg) break;
+                                                 min(s2, n_walk - 1) * kSegSmall, fa);
+    finish(s1, fb, acc);
+    if (s2 >= n_walk) break;
     sg = s2;
   }
 }
@@ -498,11 +534,13 @@ __device__ __forceinline__ void bias_seg16_body(const TileParams& p, uint16_t* H
   // states (twice the bytes of W1 rows) are gathered by every wavefront.
   constexpr int GW = (RESID || SPLIT) ? WPB : kSeg16GatherWaves;
   const bool early = !RESID && wv >= GW;
-  if (early) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  constexpr bool ASEG = SPLIT && !RESID;
+  const int vw0 = min(sg, n_seg + (ASEG ? p.n_seg_a : 0) - 1) * kSegSmall;
+  if (early) seg16_load<KS, RESID, VEC4, PACKED, NB, ASEG>(p, ps, s_ci, vw0, lane, fa);
   seg16_info_h<KS, RESID, GW, NB, SPLIT>(p, ps, Hs, s_ci);
   // residual mode: the first segment's loads come after the barrier (their
   // U and target rows come from the request info)
-  if (!early) seg16_load<KS, RESID, VEC4, PACKED, NB>(p, ps, s_ci, min(sg, n_seg - 1) * kSegSmall, lane, fa);
+  if (!early) seg16_load<KS, RESID, VEC4, PACKED, NB, ASEG>(p, ps, s_ci, vw0, lane, fa);
   seg16_walk<KS, RESID, VEC4, PACKED, NB, SPLIT, WPB>(p, ps, Hs, s_ci, sg, fa, fb, ctr);
 }
 
@@ -1167,8 +1205,9 @@ hipError_t launch_mode(const TileParams& p, int wdtype, int num_cu, hipStream_t 
     const int wpb = RESID ? kSeg16Waves : kSeg16DraftWaves;
     // as many rounds of segments as one workgroup per CU needs, spread
     // evenly: every wavefront gets the same count, or one fewer
-    const int rounds = max(1, (p.n_seg + wpb * num_cu - 1) / (wpb * num_cu));
-    const int blocks = max(1, min((p.n_seg + wpb * rounds - 1) / (wpb * rounds), num_cu));
+    const int n_walk = p.n_seg + p.n_seg_a;  // with the RNN head's A segments (draft mode)
+    const int rounds = max(1, (n_walk + wpb * num_cu - 1) / (wpb * num_cu));
+    const int blocks = max(1, min((n_walk + wpb * rounds - 1) / (wpb * rounds), num_cu));
     const dim3 grid(blocks), block(wpb * 64);
     if (p.w2p != nullptr)
       launch_seg16<RESID, VEC4, true>(p, grid, block, s, e0, e1);
@@ -1203,8 +1242,13 @@ hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int 
     return hipErrorInvalidValue;
   // 32-row segments are the fp32-weight path only
   if (p.seg_rows == kSegLarge && wdtype != DSPARK_W_F32) return hipErrorInvalidValue;
-  // H from the RNN head's states: the 16-row path only
+  // H from the RNN head's states: the 16-row path only; A segments in its
+  // draft mode only, with A (and with the packed W2, A's packed copy)
   if (p.h_base != nullptr && p.seg_rows != kSegSmall) return hipErrorInvalidValue;
+  if (p.n_seg_a != 0 && (residual || p.h_base == nullptr || p.A == nullptr || p.z_out == nullptr ||
+                         (p.w2p != nullptr && p.ap == nullptr) || p.n_seg_a < 0 ||
+                         p.n_seg_a > (p.rank + kSegSmall - 1) / kSegSmall))
+    return hipErrorInvalidValue;
   const bool vec4 = (p.V % 4) == 0;
   if (residual)
     return vec4 ? launch_mode<true, true>(p, wdtype, num_cu, s, ev0, ev1)

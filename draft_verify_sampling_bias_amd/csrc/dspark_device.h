@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "dspark.h"
+
 namespace dspark {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -23,6 +25,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   const uint32_t b = __float_as_uint(x);
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// The RNN head's activation, and a state rounded to the nearest double-bf16
+// value (hi = bf16(h), lo = bf16(h - hi), h = hi + lo: 16 significant bits),
+// the form in which every consumer of the state reads it.
+__device__ __forceinline__ float rnn_act(float z, int act) { return act == DSPARK_ACT_TANH ? tanhf(z) : z; }
+__device__ __forceinline__ float double_bf16(float h) {
+  const float hi = __uint_as_float(bf16_rne_bits(h) << 16);
+  const float lo = __uint_as_float(bf16_rne_bits(h - hi) << 16);
+  return hi + lo;
 }
 
 // 2^x on the hardware transcendental unit (v_exp_f32, 1 ulp).

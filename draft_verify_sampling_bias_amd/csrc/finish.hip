@@ -46,8 +46,6 @@ void launch_draft_finish_waves(const FinishParams& p, hipStream_t s) {
     hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, 4, SEG>), grid, block, 0, s, p);
   else if (p.n_seg <= NT * 8)
     hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, 8, SEG>), grid, block, 0, s, p);
-  else if (p.n_seg <= NT * 12)
-    hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, 12, SEG>), grid, block, 0, s, p);
   else
     hipLaunchKernelGGL((draft_finish_waves_kernel<uint16_t, NT, kWaveFinishJ, SEG>), grid, block, 0, s, p);
 }
@@ -146,6 +144,11 @@ void launch_draft_finish_nt(const FinishParams& p, int stage, hipStream_t s) {
     hipLaunchKernelGGL((draft_finish_kernel<WT, kStageRecs, NT>), grid, block, 0, s, p);
   else
     hipLaunchKernelGGL((draft_finish_kernel<WT, 0, NT>), grid, block, 0, s, p);
+}
+
+bool draft_finish_fuses_state(const FinishParams& p, int wdtype) {
+  return wdtype == DSPARK_W_BF16 && p.seg_rows == kSegSmall && p.R <= current_cu_count() &&
+         p.n_seg <= kDraftFinishThreads * kWaveFinishJ;
 }
 
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s) {

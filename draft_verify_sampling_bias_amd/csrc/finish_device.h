@@ -259,7 +259,7 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
 // hands to the whole workgroup through LDS (a second barrier), which
 // rescans it with NT / 64 lanes per row before wavefront 0 picks the entry
 // (a third).
-constexpr int kWaveFinishJ = 16;  // records per lane at most (n_seg <= 16384 with 1024 threads)
+constexpr int kWaveFinishJ = 12;  // records per lane at most (n_seg <= 12288 with 1024 threads)
 template <int NT>
 struct WaveFinishSmem {
   float hs[DSPARK_MAX_RANK];
@@ -272,7 +272,22 @@ struct WaveFinishSmem {
   int hseg;
   float hths, hms;
   float e64[kMaxSegRows], s64[kMaxSegRows];
+  // RNN head, next state fused: the drafted token
+  int ynext;
 };
+
+// The RNN head's next state, fused into the finish of (n, k < gamma - 1):
+// the fused bias kernel has stored z = A h in the state row of (n, k + 1);
+// this finish turns it into h = act(z + W1[y]), rounded to double-bf16 as
+// the state kernel rounds it (thread j < rank holds z_j from its entry).
+template <int NT>
+__device__ __forceinline__ void fused_state_store(const FinishParams& p, float zj, int y, int64_t o) {
+  const int j = static_cast<int>(threadIdx.x);
+  if (j < p.rank) {
+    const uint16_t* w1 = static_cast<const uint16_t*>(p.W1) + static_cast<int64_t>(clampi(y, 0, p.V - 1)) * p.rank;
+    p.hstate[(o + 1) * p.rank + j] = double_bf16(rnn_act(zj + bf16_to_f32(w1[j]), p.act));
+  }
+}
 
 __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
@@ -392,6 +407,7 @@ __device__ __forceinline__ void draft_finish_waves_pick(const FinishParams& p, W
   if (lane == 0) {
     const int yy = (pk >= 0) ? v0 + pk : min(v0, V - 1);
     const float sy = (pk >= 0) ? readlane_f(sl, pk) : M;
+    sm.ynext = yy;
     p.y[o] = yy;
     p.q_tok[o] = exp2_hw((sy - M) * c) / Z;
     p.q_stats[2 * o] = M;
@@ -466,6 +482,11 @@ __device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFi
     hrow.hold_state(p.hstate + o * p.rank, p.rank);
   else
     hrow.hold(static_cast<const WT*>(p.W1), prev, p.rank);
+  // the RNN head's next state in this finish (workgroup-uniform): its z
+  // (rank <= DSPARK_MAX_RANK <= NT values), loaded with the records
+  const bool fuse = SEG == kSegSmall && p.A != nullptr && p.k + 1 < p.gamma;
+  static_assert(DSPARK_MAX_RANK <= NT || SEG != kSegSmall, "one state value per thread");
+  const float zj = (fuse && tid < p.rank) ? p.hstate[(o + 1) * p.rank + tid] : 0.0f;
   const float c = temp_scale(T);  // the same for the whole workgroup
   const bool greedy = c == 0.0f;
   // records past the wavefront's range: no mass, never the maximum
@@ -490,16 +511,18 @@ __device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFi
       sm.wi[wave] = im;
     }
     __syncthreads();
-    if (wave == 0) {
+    // wavefront 0 (with the fused state, every wavefront) combines the pairs
+    if (wave == 0 || fuse) {
       m = lane < NW ? sm.wm[lane] : -INFINITY;
       im = lane < NW ? sm.wi[lane] : kIntMax;
       wave_amax(m, im);
-      if (lane == 0) {
+      if (wave == 0 && lane == 0) {
         p.y[o] = clampi(im, 0, V - 1);
         p.q_tok[o] = 1.0f;
         p.q_stats[2 * o] = m;
         p.q_stats[2 * o + 1] = 1.0f;
       }
+      if (fuse) fused_state_store<NT>(p, zj, im, o);
     }
     return;
   }
@@ -543,6 +566,10 @@ __device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFi
                         : (wpos ? 63 - __clzll(static_cast<long long>(wpos)) : 0);
   if (wave == wfin) draft_finish_waves_pick<WT, NT, J, SEG>(p, sm, r, n, o, w0, L, M, Z, c, theta,
                                                              readlane_f(excl, wfin), fb);
+  if (fuse) {
+    __syncthreads();  // the chosen wavefront's token
+    fused_state_store<NT>(p, zj, sm.ynext, o);
+  }
   if constexpr (SEG == kSegWide) {
     __syncthreads();
     draft_finish_rescan64<WT, NT>(p, sm, n, o, M, Z, c);

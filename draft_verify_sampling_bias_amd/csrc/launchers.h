@@ -55,6 +55,16 @@ struct TileParams {
   // residual mode: row urow (U row index n * gamma + position) of h_base
   const float* h_base;
   int64_t h_stride;
+  // RNN head, draft mode: when n_seg_a > 0 the walk also covers n_seg_a =
+  // ceil(rank / 16) segments of the recurrence matrix A (rank x rank, bf16)
+  // after the n_seg vocabulary segments, read from A (row-major, like W2)
+  // or, when w2p is set, from its fragment-packed copy ap; for them it
+  // stores z = A h of request n (fp32, rank values) at z_out + n * h_stride
+  // instead of records
+  int n_seg_a;
+  const uint16_t* A;
+  const uint16_t* ap;
+  float* z_out;
 };
 
 // Per-position draft finish: turns the segment records into y / q_tok / q_stats.
@@ -74,7 +84,13 @@ struct FinishParams {
   float* q_stats;
   // RNN head, else null: h for (n, k) is the fp32 row hstate + (n * gamma + k)
   // * rank instead of W1[prev]
-  const float* hstate;
+  float* hstate;
+  // RNN head with the next state fused into this finish (else null): the
+  // fused bias kernel stored z = A h in the state row of (n, k + 1); the
+  // finish of (n, k < gamma - 1) turns it into act(z + W1[y]) with this
+  // activation (A itself is not read here)
+  const uint16_t* A;
+  int act;
   // when set, block 0 writes 0 to this error word (a call made without the
   // input checks still rewrites the word of its workspace)
   uint32_t* err_clear;
@@ -139,6 +155,9 @@ hipError_t launch_input_check(const CheckParams& p, hipStream_t s);
 hipError_t launch_bias_tile(const TileParams& p, int wdtype, bool residual, int num_cu, hipStream_t s,
                             hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 hipError_t launch_draft_finish(const FinishParams& p, int wdtype, hipStream_t s);
+// whether launch_draft_finish takes the finish that can fuse the RNN head's
+// next state (p.A)
+bool draft_finish_fuses_state(const FinishParams& p, int wdtype);
 
 // The RNN head's state of position k for every request:
 // h[n, k] = act(A h[n, k-1] + W1[prev]) (h[n, -1] = 0), fp32.

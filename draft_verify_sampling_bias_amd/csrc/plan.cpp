@@ -78,6 +78,10 @@ int plan_draft(const dspark_draft_args* a, DraftPlan* plan) {
   const std::size_t rows = static_cast<std::size_t>(record_rows(plan->seg_rows, a->R));
   plan->part_off = kHeaderBytes;
   plan->total = kHeaderBytes + round_up(rows * plan->n_seg * kRecFloats * sizeof(float), kWsAlign);
+  if (a->head == DSPARK_HEAD_RNN && plan->seg_rows == kSegSmall) {
+    plan->ap_off = plan->total;
+    plan->total += round_up(w2_packed_bytes(a->rank, a->rank), kWsAlign);
+  }
   return DSPARK_OK;
 }
 

@@ -76,6 +76,9 @@ struct DraftPlan {
   int seg_rows = 0;
   int n_seg = 0;
   std::size_t part_off = 0;  // [record_rows][n_seg][kRecFloats] float
+  // RNN head on the 16-row path: the fragment-packed copy of A (rank rows,
+  // w2_packed_bytes(rank, rank)), made by the call when W2_packed is given
+  std::size_t ap_off = 0;
   std::size_t total = 0;
   bool check = false;        // DSPARK_CHECK_INPUTS
 };

@@ -30,15 +30,6 @@ constexpr int kLanesPerOut = 8;
 constexpr int kOutsPerGroup = kRnnThreads / kLanesPerOut;               // 32
 constexpr int kMaxPieces = DSPARK_MAX_RANK / 8 / kLanesPerOut;          // 8 per lane
 
-__device__ __forceinline__ float rnn_act(float z, int act) { return act == DSPARK_ACT_TANH ? tanhf(z) : z; }
-
-// h rounded to the nearest double-bf16 value (16 significant bits)
-__device__ __forceinline__ float double_bf16(float h) {
-  const float hi = __uint_as_float(bf16_rne_bits(h) << 16);
-  const float lo = __uint_as_float(bf16_rne_bits(h - hi) << 16);
-  return hi + lo;
-}
-
 __global__ void __launch_bounds__(kRnnThreads) rnn_state_kernel(RnnStateParams p) {
   __shared__ __attribute__((aligned(16))) float hp[DSPARK_MAX_RANK];
   const int n = blockIdx.x, tid = threadIdx.x;

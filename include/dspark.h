@@ -165,7 +165,10 @@ typedef enum dspark_act {
  *                                 dspark_verify to rebuild q on a rejection.
  *   workspace, workspace_bytes    scratch of at least
  *                                 dspark_draft_workspace_size() bytes,
- *                                 256-byte aligned.
+ *                                 256-byte aligned (the segment records; with
+ *                                 the RNN head on the 16-row path also a
+ *                                 fragment-packed copy of A, made by the
+ *                                 call when W2_packed is given).
  *   stream   hipStream_t as void*.
  *   prof_events  optional (NULL normally): host array of 2*gamma hipEvent_t
  *                handles (created with timing enabled); events 2k / 2k+1 are
@@ -615,7 +618,8 @@ int dspark_draft_block(const dspark_draft_args* args);
  * call whose dspark_draft_workspace_size() exceeds that size returns
  * DSPARK_ERR_WORKSPACE and enqueues nothing (64 MiB holds, e.g., R = 1024 at
  * V = 129280 with 64-row segments, or R <= 64 at V up to 2097136 with 16-row
- * segments).  DSPARK_CHECK_INPUTS is refused (DSPARK_ERR_UNSUPPORTED): the
+ * segments and the Markov head; the RNN head's packed A takes
+ * dspark_w2_packed_bytes(rank, rank) more).  DSPARK_CHECK_INPUTS is refused (DSPARK_ERR_UNSUPPORTED): the
  * checks report through a caller's workspace.  Every call on one device
  * shares the array, and a call leaves its contents behind: calls that
  * overlap in time on one device (another stream, another host thread) race
