@@ -70,6 +70,12 @@ def test_workspace_sizes_match_struct_layout():
     # 32-row segments, one row per request, for fp32 weights
     assert ds.draft_workspace_bytes(65, 7, 151936, 512, 0) == H + up(65 * 4748 * 8)
     assert ds.draft_workspace_bytes(8, 7, 1024, 32, 0) == H + up(8 * 32 * 8)
+    # the RNN head (16-row path) also holds A in the fragment-packed layout:
+    # ceil(rank / 16) segments x rank / 32 k-steps x 1 KiB (rank 64: 2 k-steps)
+    assert ds.draft_workspace_bytes(64, 7, 151936, 512, 1, head=ds.HEAD_RNN, act=1) == \
+        H + up(64 * 9496 * 8) + 32 * 16 * 1024
+    assert ds.draft_workspace_bytes(3, 7, 1000, 64, 1, head=ds.HEAD_RNN, act=0) == H + up(64 * 63 * 8) + 4 * 2 * 1024
+    assert ds.dspark_w2_packed_bytes(512, 512) == 32 * 16 * 1024
     # verify: chunk records (16 bytes per 4096-entry chunk of each target row),
     # residual info/stats, then the residual segment records
     nb = ds.verify_workspace_bytes(64, 7, 151936, 512, 1, 512)
