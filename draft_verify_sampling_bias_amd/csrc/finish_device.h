@@ -266,7 +266,7 @@ struct WaveFinishSmem {
   float wm[NT / 64];
   float ws[NT / 64];
   int wi[NT / 64];
-  float tx[64 * kWaveFinishJ];  // the chosen wavefront's masses, then its record maxima
+  float tx[64 * kWaveFinishJ];  // the chosen wavefront's masses, then the chosen record's maximum
   // 64-row segments: the chosen segment, its threshold and maximum, and the
   // rescanned rows' weights and logits
   int hseg;
@@ -280,7 +280,6 @@ struct WaveFinishSmem {
 // the fused bias kernel has stored z = A h in the state row of (n, k + 1);
 // this finish turns it into h = act(z + W1[y]), rounded to double-bf16 as
 // the state kernel rounds it (thread j < rank holds z_j from its entry).
-template <int NT>
 __device__ __forceinline__ void fused_state_store(const FinishParams& p, float zj, int y, int64_t o) {
   const int j = static_cast<int>(threadIdx.x);
   if (j < p.rank) {
@@ -522,7 +521,7 @@ __device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFi
         p.q_stats[2 * o] = m;
         p.q_stats[2 * o + 1] = 1.0f;
       }
-      if (fuse) fused_state_store<NT>(p, zj, im, o);
+      if (fuse) fused_state_store(p, zj, im, o);
     }
     return;
   }
@@ -568,7 +567,7 @@ __device__ __forceinline__ void draft_finish_waves(const FinishParams& p, WaveFi
                                                              readlane_f(excl, wfin), fb);
   if (fuse) {
     __syncthreads();  // the chosen wavefront's token
-    fused_state_store<NT>(p, zj, sm.ynext, o);
+    fused_state_store(p, zj, sm.ynext, o);
   }
   if constexpr (SEG == kSegWide) {
     __syncthreads();
