@@ -72,6 +72,15 @@ SMALL = [
     (42, 3, 2, 32784, 64, "bf16", "sampled", "fixed"),       # 2049 records: the large stage
     (43, 70, 16, 1000, 64, "bf16", "temps", "uniformK"),     # maximum gamma on the 64-row path
     (44, 33, 16, 1000, 96, "f32", "mixed", "uniformK"),      # and on the fp32 path
+    # the wave-range draft finish (1024 threads: 4, 8 or 12 records per lane,
+    # 256 threads above 256 requests) at the edges of each size
+    (50, 2, 2, 65536, 16, "bf16", "sampled", "fixed"),       # 4096 records: 4 per lane, full
+    (51, 2, 2, 65552, 16, "bf16", "mixed", "fixed"),         # 4097: 8 per lane
+    (52, 3, 2, 131088, 16, "bf16", "temps", "fixed"),        # 8193: 12 per lane
+    (53, 2, 2, 196608, 8, "bf16", "sampled", "fixed"),       # 12288: 12 per lane, full
+    (54, 2, 2, 196624, 8, "bf16", "sampled", "fixed"),       # 12289: the staged finish
+    (55, 70, 2, 262208, 8, "bf16", "mixed", "fixed"),        # 64-row segments, 4097 records: 8 per lane
+    (56, 260, 2, 65600, 8, "bf16", "sampled", "fixed"),      # 256 threads, 1025 records: 8 per lane
 ]
 
 
