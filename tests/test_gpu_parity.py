@@ -12,7 +12,7 @@ import pytest
 import torch  # noqa: F401  (first import is slow on a fresh box: pay it at collection)
 
 import synth
-from gpu_harness import Tally, compare_draft, compare_schedule, compare_verify, gpu_step, upload
+from gpu_harness import Tally, compare_draft, compare_schedule, compare_verify, gpu_step, upload, upload_A
 
 pytestmark = pytest.mark.gpu
 
@@ -506,20 +506,30 @@ def test_schedule_ties(R, gamma):
             np.testing.assert_array_equal(g[f], getattr(o, f), err_msg=f)
 
 
-def test_step_graph_capture_replays():
+@pytest.mark.parametrize("head", ["markov", "rnn"])
+def test_step_graph_capture_replays(head):
     """A whole step (draft, schedule, verify) captured once in a HIP graph.
     Every buffer is allocated before the capture and every call has a shape
     known on the host (the capacity is fixed ahead), so the captured step
     replays without host work.  The graph is replayed several times, with
     eager work and synchronisations in between, with new inputs copied in
     before each replay, and every replay must equal the eager step on the
-    same inputs bit for bit."""
+    same inputs bit for bit.  With the RNN head (and the packed W2) the
+    captured draft also packs A, runs the state kernel once and writes the
+    states, which the verify reads."""
     import torch
     import draft_verify_sampling_bias_amd as ds
     R, gamma, V, rank = 64, 5, 20000, 128
     inps = [synth.make_custom(1200 + i, R, gamma, V, rank, policy="temps", name=f"graph{i}") for i in range(3)]
     K = (R * gamma) // 2
     d = upload(inps[0])
+    rnn = head == "rnn"
+    rk, vk = {}, {}
+    if rnn:
+        h_buf = torch.empty((R, gamma, rank), dtype=torch.float32, device="cuda:0")
+        rk = dict(A=upload_A(synth.make_rnn_A(1200, rank), "bf16"), act=1, h=h_buf,
+                  W2_packed=ds.dspark_pack_w2(d["W2"]))
+        vk = dict(h=h_buf)
     # the schedule of these inputs decides which target rows the verify reads;
     # the rows buffer is refilled (eagerly) before each replay
     n_rows = ds.dspark_schedule_rows(R, gamma, K)
@@ -527,7 +537,8 @@ def test_step_graph_capture_replays():
     y = torch.empty((R, gamma), dtype=torch.int32, device=dev)
     q_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
     q_stats = torch.empty((R, gamma, 2), dtype=torch.float32, device=dev)
-    ws_d = torch.empty(ds.draft_workspace_bytes(R, gamma, V, rank, ds.W_BF16), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(ds.draft_workspace_bytes(R, gamma, V, rank, ds.W_BF16, head=ds.HEAD_RNN if rnn else 0,
+                                                act=1 if rnn else 0), dtype=torch.uint8, device=dev)
     sch = dict(a=torch.empty((R, gamma), dtype=torch.float32, device=dev),
                l=torch.empty(R, dtype=torch.int32, device=dev),
                row_offsets=torch.empty(R + 1, dtype=torch.int32, device=dev),
@@ -539,15 +550,15 @@ def test_step_graph_capture_replays():
     n_acc = torch.empty(R, dtype=torch.int32, device=dev)
     out_tok = torch.empty(R, dtype=torch.int32, device=dev)
     p_tok = torch.empty((R, gamma), dtype=torch.float32, device=dev)
-    ws_v = torch.empty(ds.verify_workspace_bytes(R, gamma, V, rank, ds.W_BF16, n_rows), dtype=torch.uint8,
-                       device=dev)
+    ws_v = torch.empty(ds.verify_workspace_bytes(R, gamma, V, rank, ds.W_BF16, n_rows,
+                                                 head=ds.HEAD_RNN if rnn else 0), dtype=torch.uint8, device=dev)
 
     def step():
         ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"],
-                              out=(y, q_tok, q_stats), workspace=ws_d)
+                              out=(y, q_tok, q_stats), workspace=ws_d, **rk)
         ds.dspark_schedule(d["c"], K, d["anchor"], y, out=sch)
         ds.dspark_verify(rows, sch["row_offsets"], d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], y, q_tok,
-                         q_stats, d["u_accept"], d["u_final"], out=(n_acc, out_tok, p_tok), workspace=ws_v)
+                         q_stats, d["u_accept"], d["u_final"], out=(n_acc, out_tok, p_tok), workspace=ws_v, **vk)
 
     def load(inp):
         nd = upload(inp)
@@ -555,7 +566,7 @@ def test_step_graph_capture_replays():
             d[k].copy_(nd[k])
         # the target rows of this input's schedule (stand-in for the target forward)
         ds.dspark_draft_block(d["U"], d["W1"], d["W2"], d["anchor"], d["temp"], d["u_draft"],
-                              out=(y, q_tok, q_stats), workspace=ws_d)
+                              out=(y, q_tok, q_stats), workspace=ws_d, **rk)
         ds.dspark_schedule(d["c"], K, d["anchor"], y, out=sch)
         rows.copy_(d["target"][sch["row_req"].long(), sch["row_pos"].long()])
         torch.cuda.synchronize()
@@ -563,7 +574,7 @@ def test_step_graph_capture_replays():
     def snapshot():
         torch.cuda.synchronize()
         return {k: v.clone() for k, v in dict(y=y, q_tok=q_tok, q_stats=q_stats, n_acc=n_acc, out_tok=out_tok,
-                                               p_tok=p_tok, **sch).items()}
+                                               p_tok=p_tok, **sch, **vk).items()}
 
     load(inps[0])
     step()
@@ -589,4 +600,5 @@ def test_step_graph_capture_replays():
         replay = snapshot()
         for k in eager:
             assert torch.equal(eager[k], replay[k]), (rep, k)
-        print(f"[graph replay {rep}] input {rep % 3}: identical to eager; accepted {int(n_acc.sum())}", flush=True)
+        print(f"[graph replay {rep} {head}] input {rep % 3}: identical to eager; accepted {int(n_acc.sum())}",
+              flush=True)
