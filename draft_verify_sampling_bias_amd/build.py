@@ -29,6 +29,12 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 
+# bias_tile.hip: MFMA results in architectural registers (the 64-row kernel
+# keeps its W2 fragments in all 256 accumulation registers; with accumulation-
+# register results the compiler moves some fragments out and back and reads
+# every result through v_accvgpr_read)
+PER_SOURCE = {"bias_tile.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 SOURCES = ["plan.cpp", "api.hip", "bias_tile.hip", "finish.hip", "verify.hip", "schedule.hip", "pack.hip", "capacity.hip",
            "calibrate.hip", "check.hip", "noalloc.hip", "rnn.hip"]
 
@@ -36,7 +42,7 @@ SOURCES = ["plan.cpp", "api.hip", "bias_tile.hip", "finish.hip", "verify.hip", "
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_SOURCE.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

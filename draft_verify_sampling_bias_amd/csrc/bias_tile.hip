@@ -792,101 +792,143 @@ __device__ __forceinline__ void wide_w2_ready(int rank, int lane, u32x4_t (&w)[4
 // never used.)
 __device__ __forceinline__ float wide_exp_base(float m) { return (m == -INFINITY) ? 0.f : m; }
 
-// One chunk's record for this lane's request over the wavefront's 64 rows,
-// cut into small steps so that its vector instructions can be placed one
-// step after each MFMA of the next chunk (step t is a compile-time constant
-// at every call).  The accumulators start at zero: the bf16 products are
-// exact in fp32 and their partial sums stay exactly representable, so the
-// bias W2 h comes out exact in any summation order, and s = bias + U is the
-// value that the finish's rescan of a segment recomputes bit for bit (which
-// extreme temperatures, c ~ 1e30, need).
-// Draft: steps 0-15 form logit t (rows past V are -inf through U) and fold
-// them into the lane's maximum with 3-input maxima (after step 15 the
-// inputs may be overwritten); 16-31, only if a request of the wavefront is
-// greedy, find the lowest index of that maximum (scanning down); 32
-// combines the four lanes (lane & 15) + 16 j; 33-48, only if a request is
-// sampled, add the exponentials 2^((s - max) c); 49 combines and stores
-// (max, sum) or, for a greedy request, (max, argmax).  Residual: step 3 k
+// Residual-mode record of one chunk for this lane's request over the
+// wavefront's 64 rows, cut into small steps placed between the MFMAs of the
+// next chunk (step t is a compile-time constant at every call): step 3 k
 // adds entry k of max(0, p - q) (the two steps after it are empty), step 48
-// combines and stores.
-constexpr int kEpiSteps = 50;
+// combines the four lanes (lane & 15) + 16 j and stores.  The accumulators
+// start at zero: the bf16 products are exact in fp32 and their partial sums
+// stay exactly representable, so the bias W2 h comes out exact in any
+// summation order, and s = bias + U is the value every other pass over the
+// same row computes bit for bit.
+constexpr int kEpiSteps = 49;
 
-template <bool RESID>
 struct WideEpi {
-  float s[RESID ? 1 : 16];
-  float m, mg, z, c;
-  int im, n;
-  bool greedy, sampled;  // wavefront-uniform: a request of the chunk is greedy / sampled
+  float z;
+  int n;
 };
 
-template <bool RESID>
-__device__ __forceinline__ void wide_epi_step(int t, const TileParams& p, int seg, bool full, int lane,
-                                              WideU<RESID>& f, const f32x4_t (&acc)[4], bool live,
-                                              WideEpi<RESID>& e) {
-  const int vb = seg * kSegWide + 4 * (lane >> 4);
-  auto store = [&](float x, float y) {
+__device__ __forceinline__ void wide_resid_step(int t, const TileParams& p, int seg, bool full, int lane,
+                                                WideU<true>& f, const f32x4_t (&acc)[4], bool live, WideEpi& e) {
+  if (t < 48 && t % 3 == 0) {
+    const int k = t / 3, b = k >> 2, i = k & 3;
+    if (k == 0) {
+      e.z = 0.f;
+      e.n = f.n;
+      wide_mask(full, seg * kSegWide, lane, p.V, f.u);
+      wide_mask(full, seg * kSegWide, lane, p.V, f.t);
+    }
+    const float qq = exp2_hw((acc[b][i] + f.u[b][i] - f.Mq) * f.c) * f.iZq;
+    const float pp = exp2_hw((f.t[b][i] - f.Mp) * f.c) * f.iZp;
+    e.z += fmaxf(pp - qq, 0.f);
+  } else if (t == 48) {
+    const float z = quad_sum(e.z);
     const bool in_v = live && seg < p.n_seg;
     const int64_t row = in_v ? e.n : p.R + kWideChunk;
     const int col = in_v ? seg : 0;
-    reinterpret_cast<float2*>(p.part)[row * p.n_seg + col] = make_float2(x, y);
-  };
-  if constexpr (!RESID) {
-    if (t < 16) {
-      if (t == 0) {
-        e.c = f.c;
-        e.n = f.n;
-        e.im = 0;
-        e.greedy = __ballot(f.c == 0.f) != 0;
-        e.sampled = __ballot(f.c != 0.f) != 0;
-        wide_mask(full, seg * kSegWide, lane, p.V, f.u);
-      }
-      e.s[t] = acc[t >> 2][t & 3] + f.u[t >> 2][t & 3];
-      if (t == 0) e.m = e.s[0];
-      if (t >= 2 && t % 2 == 0) e.m = fmaxf(fmaxf(e.m, e.s[t - 1]), e.s[t]);
-      if (t == 15) e.m = fmaxf(e.m, e.s[15]);
-    } else if (t < 32) {
-      if (e.greedy) {
-        const int k = 31 - t;  // 15 .. 0
-        if (k == 15) e.im = kIntMax;
-        e.im = (e.s[k] == e.m) ? vb + 16 * (k >> 2) + (k & 3) : e.im;
-      }
-    } else if (t == 32) {
-      if (e.greedy)
-        quad_amax(e.m, e.im);
-      else
-        e.m = quad_max(e.m);
-      e.mg = wide_exp_base(e.m);
-      e.z = 0.f;
-    } else if (t < 49) {
-      if (e.sampled) e.z += exp2_hw((e.s[t - 33] - e.mg) * e.c);
-    } else if (t == 49) {
-      store(e.m, (e.c > 0.f) ? quad_sum(e.z) : __int_as_float(e.im));
-    }
-  } else {
-    if (t < 48 && t % 3 == 0) {
-      const int k = t / 3, b = k >> 2, i = k & 3;
-      if (k == 0) {
-        e.z = 0.f;
-        e.n = f.n;
-        wide_mask(full, seg * kSegWide, lane, p.V, f.u);
-        wide_mask(full, seg * kSegWide, lane, p.V, f.t);
-      }
-      const float qq = exp2_hw((acc[b][i] + f.u[b][i] - f.Mq) * f.c) * f.iZq;
-      const float pp = exp2_hw((f.t[b][i] - f.Mp) * f.c) * f.iZp;
-      e.z += fmaxf(pp - qq, 0.f);
-    } else if (t == 48) {
-      store(0.f, quad_sum(e.z));
-    }
+    reinterpret_cast<float2*>(p.part)[row * p.n_seg + col] = make_float2(0.f, z);
   }
 }
 
-// The whole epilogue of one chunk at once (the last chunk of the launch).
-template <bool RESID>
-__device__ __forceinline__ void wide_epilogue(const TileParams& p, int seg, bool full, int lane, WideU<RESID>& f,
-                                              const f32x4_t (&acc)[4]) {
-  WideEpi<RESID> e;
-#pragma unroll
-  for (int t = 0; t < kEpiSteps; ++t) wide_epi_step<RESID>(t, p, seg, full, lane, f, acc, true, e);
+// Draft-mode record of one chunk (the maximum over the wavefront's 64 rows
+// for this lane's request, and its lowest argmax or the sum of
+// 2^((s - max) c)) as fixed work per sub-slot: sub-slot j runs right after
+// MFMA j of the next chunk (one sub-slot per MFMA at rank 512), with no
+// branch besides the rare vocabulary mask, so that the scheduler keeps every
+// piece where it is put.  Rows past V are -inf through U; the exponentials
+// use the maximum as base (0 when all 64 rows are masked, wide_exp_base).
+// One wavefront per SIMD does not overlap its own vector work with its
+// MFMAs, but work spread this way waits on no result of the last few
+// instructions, while the same work gathered into runs stalls on each
+// dependent step.  Every lane computes both the lowest argmax and the
+// exponential sum (a chunk's requests may be greedy and sampled at once).
+// Each piece reads only results of earlier sub-slots:
+//   3-10   logits s_k = acc + U, two per sub-slot; 4-11 the lane maximum
+//   12-20  lowest index of the maximum, scanning down: compares one sub-slot
+//          ahead of their selects
+//   21-26  (max, lowest argmax) over the four lanes (lane & 15) + 16 j
+//   27-45  z = sum of 2^((s_k - max) c), in index order (sub-slot n + 28
+//          forms exponent k = n, n + 29 takes its power, n + 30 adds it)
+//   46-49  sum over the four lanes; 50 stores (max, sum) or (max, argmax)
+// The epilogue inputs are free after sub-slot 11 (the next chunk's may be
+// loaded into them from sub-slot 12 on).
+constexpr int kDraftUFree = 12;
+constexpr int kDraftEpiEnd = 51;
+
+struct WideDraftEpi {
+  float s[16];
+  float m, mg, z, c, tt[2], ee[2];
+  uint32_t ml, mh, il, ih;
+  int im, n;
+  bool eq0, eq1, take;
+};
+
+__device__ __forceinline__ void wide_draft_slot(int j, const TileParams& p, int seg, bool full, int lane,
+                                                WideU<false>& f, const f32x4_t (&acc)[4], bool live,
+                                                WideDraftEpi& e) {
+  const int vb = seg * kSegWide + 4 * (lane >> 4);
+  auto row = [&](int k) { return vb + 16 * (k >> 2) + (k & 3); };
+  if (j == 3) {
+    e.c = f.c;
+    e.n = f.n;
+    wide_mask(full, seg * kSegWide, lane, p.V, f.u);
+  }
+  if (j >= 3 && j <= 10) {
+    const int k = 2 * (j - 3);
+    e.s[k] = acc[k >> 2][k & 3] + f.u[k >> 2][k & 3];
+    e.s[k + 1] = acc[(k + 1) >> 2][(k + 1) & 3] + f.u[(k + 1) >> 2][(k + 1) & 3];
+  }
+  if (j == 4) e.m = fmaxf(e.s[0], e.s[1]);
+  if (j >= 5 && j <= 11) {
+    const int k = 2 * (j - 4);
+    e.m = fmaxf(fmaxf(e.m, e.s[k]), e.s[k + 1]);
+  }
+  if (j >= 13 && j <= 20) {
+    const int k = 15 - 2 * (j - 13);
+    e.im = e.eq0 ? row(k) : e.im;
+    e.im = e.eq1 ? row(k - 1) : e.im;
+  }
+  if (j == 12) e.im = kIntMax;
+  if (j >= 12 && j <= 19) {
+    const int k = 15 - 2 * (j - 12);
+    e.eq0 = e.s[k] == e.m;
+    e.eq1 = e.s[k - 1] == e.m;
+  }
+  if (j == 21 || j == 24) {
+    if (j == 21) {
+      lane_pair16(__float_as_uint(e.m), e.ml, e.mh);
+      lane_pair16(static_cast<uint32_t>(e.im), e.il, e.ih);
+    } else {
+      lane_pair32(__float_as_uint(e.m), e.ml, e.mh);
+      lane_pair32(static_cast<uint32_t>(e.im), e.il, e.ih);
+    }
+  }
+  if (j == 22 || j == 25)
+    e.take = amax_takes(__uint_as_float(e.mh), static_cast<int>(e.ih), __uint_as_float(e.ml), static_cast<int>(e.il));
+  if (j == 23 || j == 26) {
+    e.m = __uint_as_float(e.take ? e.mh : e.ml);
+    e.im = static_cast<int>(e.take ? e.ih : e.il);
+  }
+  if (j == 27) {
+    e.mg = wide_exp_base(e.m);
+    e.z = 0.f;
+  }
+  if (j >= 28 && j <= 45) {
+    const int n = j - 28;
+    if (n >= 2) e.z += e.ee[n & 1];
+    if (n >= 1 && n <= 16) e.ee[(n - 1) & 1] = exp2_hw(e.tt[(n - 1) & 1]);
+    if (n < 16) e.tt[n & 1] = (e.s[n] - e.mg) * e.c;
+  }
+  if (j == 46) lane_pair16(__float_as_uint(e.z), e.ml, e.mh);
+  if (j == 48) lane_pair32(__float_as_uint(e.z), e.ml, e.mh);
+  if (j == 47 || j == 49) e.z = __uint_as_float(e.ml) + __uint_as_float(e.mh);
+  if (j == 50) {
+    const bool in_v = live && seg < p.n_seg;
+    const int64_t r = in_v ? e.n : p.R + kWideChunk;
+    const int col = in_v ? seg : 0;
+    reinterpret_cast<float2*>(p.part)[r * p.n_seg + col] =
+        make_float2(e.m, (e.c > 0.f) ? e.z : __int_as_float(e.im));
+  }
 }
 
 template <int KS, bool RESID, bool VEC4>
@@ -944,14 +986,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
   // differently), so every trip issues the same loads.
   //
   // Work besides the MFMAs runs in 64 sub-slots: sub-slot j right after
-  // MFMA j * 4 KS / 64 of the iteration (one per MFMA at rank 512), so its
-  // vector instructions issue while that MFMA executes.
+  // MFMA j * 4 KS / 64 of the iteration (one per MFMA at rank 512).
   //   0        row indices of chunk c + 2 (LDS)    2   its W1 rows (loads)
-  //   4-53     epilogue steps 0-49 of chunk c - 1
-  //   kUSlot   chunk c + 1's epilogue inputs (after the steps that read the
-  //            previous ones)
+  //   3-50     draft: chunk c - 1's record (wide_draft_slot)
+  //   4-52     residual: its epilogue steps 0-48 (wide_resid_step)
+  //   kUSlot   chunk c + 1's epilogue inputs (after the pieces that read
+  //            the previous ones)
   //   60       chunk c + 1's W1 rows into LDS
-  constexpr int kUSlot = RESID ? 4 + 49 : 4 + 16;
+  constexpr int kUSlot = RESID ? 4 + kEpiSteps : kDraftUFree;
   constexpr int kPerH = WideH<KS>::kPer, kG = WideH<KS>::kGroups;
   constexpr int kSubPerMfma = 64 / (4 * KS);
   f32x4_t acc0[4], acc1[4];
@@ -964,7 +1006,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     const WideReq<RESID>* win1 = win[(c1 / kWideWinChunks) & 1];
     const uint16_t* w1 = static_cast<const uint16_t*>(p.W1);
     int hp[kPerH];
-    WideEpi<RESID> ep;
+    WideEpi ep;
+    WideDraftEpi dp;
     auto side = [&](int j) {
       if (j == 0) {
 #pragma unroll
@@ -976,7 +1019,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
           ha.v[q] = *reinterpret_cast<const u32x4_t*>(w1 + static_cast<int64_t>(hp[q]) * rank + min(g * 8, rank - 8));
         }
       }
-      if (j >= 4 && j < 4 + kEpiSteps) wide_epi_step<RESID>(j - 4, p, seg, full, lane, uf, acc_prev, c > 0, ep);
+      if constexpr (RESID) {
+        if (j >= 4 && j < 4 + kEpiSteps) wide_resid_step(j - 4, p, seg, full, lane, uf, acc_prev, c > 0, ep);
+      } else {
+        if (j < kDraftEpiEnd) wide_draft_slot(j, p, seg, full, lane, uf, acc_prev, c > 0, dp);
+      }
       if (j == kUSlot) wide_u_issue<RESID, VEC4>(p, win1, c1, c1 % kWideWinChunks, vw, lane, uf);
       if (j == 60) wide_h_commit<KS>(hb, rank, Hs + (s ^ 1) * kStage);
     };
@@ -1020,7 +1067,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
     c += 2;
   } while (c < n_chunks);
   // the last trip's second chunk
-  wide_epilogue<RESID>(p, seg, full, lane, ua, acc1);
+  if constexpr (RESID) {
+    WideEpi ep;
+#pragma unroll
+    for (int t = 0; t < kEpiSteps; ++t) wide_resid_step(t, p, seg, full, lane, ua, acc1, true, ep);
+  } else {
+    WideDraftEpi dp;
+#pragma unroll
+    for (int j = 0; j < kDraftEpiEnd; ++j) wide_draft_slot(j, p, seg, full, lane, ua, acc1, true, dp);
+  }
 }
 
 // ---------------------------------------------------------------------------
