@@ -42,8 +42,15 @@ SOURCES = ["plan.cpp", "api.hip", "bias_tile.hip", "finish.hip", "verify.hip", "
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *PER_SOURCE.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    per = PER_SOURCE.get(src, [])
+    cmd = [HIPCC, *COMMON, *per, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0 and per and "Unknown command line argument" in r.stderr:
+        # a compiler without that backend option: the same code, a few
+        # instructions per chunk slower
+        sys.stderr.write(f"[{src}] {' '.join(per)} not known to this compiler; building without it\n")
+        cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
