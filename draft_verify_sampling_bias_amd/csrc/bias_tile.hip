@@ -979,7 +979,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   // Iteration c (LDS stage c & 1) runs chunk c's MFMAs and, interleaved with
   // them, chunk c - 1's epilogue (its accumulators and inputs are ready), so
-  // the matrix cores and the vector ALUs work at once.  ha receives chunk
+  // that no vector instruction waits on a result of the instructions just
+  // before it (a SIMD does not run them under the MFMAs).  ha receives chunk
   // c + 2's W1 rows, hb holds chunk c + 1's (stored into stage (c + 1) & 1
   // at the end); uf holds chunk c - 1's epilogue inputs and then receives
   // chunk c + 1's.  Chunks past the last re-load the last one (never stored
