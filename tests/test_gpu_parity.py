@@ -81,6 +81,10 @@ SMALL = [
     (54, 2, 2, 196624, 8, "bf16", "sampled", "fixed"),       # 12289: the staged finish
     (55, 70, 2, 262208, 8, "bf16", "mixed", "fixed"),        # 64-row segments, 4097 records: 8 per lane
     (56, 260, 2, 65600, 8, "bf16", "sampled", "fixed"),      # 256 threads, 1025 records: 8 per lane
+    # many request windows on the 64-row path (each window: 256 requests,
+    # loaded one window ahead into the other LDS half)
+    (57, 2990, 2, 1000, 32, "bf16", "mixed", "uniformK"),    # 187 chunks (odd), 12 windows, ragged last
+    (58, 5000, 3, 600, 64, "bf16", "temps", "uniformK"),     # 313 chunks, 20 windows
 ]
 
 
