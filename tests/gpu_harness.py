@@ -8,8 +8,8 @@ Comparison rules (decisions are compared, values within tolerance):
   * the oracle is teacher-forced with the GPU's drafted prefix, so a flagged
     flip does not cascade into later positions;
   * probabilities (q_tok, p_tok, Z) and survival within 1e-5 relative;
-  * every accept decision is also re-taken by the oracle with its own
-    teacher-forced q_tok (not the GPU's): a decision that then differs from
+  * every accept decision is also re-taken by the oracle with its own q of
+    the GPU's drafted tokens (not the GPU's q_tok): a decision that then differs from
     the GPU's is allowed only where u lies within 1e-5 * p/q of p/q (the
     two q_tok may differ by the 1e-5 tolerance), and is counted.
 """
@@ -206,20 +206,54 @@ def compare_schedule(inp, g, K, conf_min=None):
 OWN_Q_BAND = 1e-5
 
 
+def own_q_of_gpu_tokens(inp, g, d, reqs):
+    """The oracle's probability of each token the GPU drafted: d.q_tok, except
+    where the GPU's token differs from the oracle's own draw (a flip at a
+    flagged CDF boundary), where d.q_tok is the probability of the oracle's
+    token.  There it is rebuilt from the oracle's (max s, Z) of that position
+    and the logit of the GPU's token (U plus the bias from the GPU's previous
+    token, or from the GPU's state for the RNN head, as the teacher-forced
+    draw used)."""
+    q = d.q_tok.copy()
+    y_g = g["y"]
+    W1_64 = W2_64 = None
+    for r in reqs:
+        T = float(inp.temp[r])
+        if not T > 0:
+            continue
+        for k in range(inp.gamma):
+            t = int(y_g[r, k])
+            if t == int(d.y[r, k]):
+                continue
+            if W2_64 is None:
+                W1_64, W2_64 = oracle.widen(inp.W1, inp.wdtype), oracle.widen(inp.W2, inp.wdtype)
+            if "h" in g:
+                bias_t = float(W2_64[t] @ g["h"][r, k].astype(np.float64))
+            else:
+                prev = int(inp.anchor[r]) if k == 0 else int(y_g[r, k - 1])
+                bias_t = float(W2_64[t] @ W1_64[prev])
+            Tc = oracle._sample_T(T)
+            Ms, Z = float(d.q_stats[r, k, 0]), float(d.q_stats[r, k, 1])
+            q[r, k] = np.exp((float(inp.U[r, k, t]) + bias_t) / Tc - Ms / Tc) / Z
+    return q
+
+
 def compare_verify(inp, g, reqs, tally: Tally, d=None):
     """Oracle verify on the GPU's drafted tokens and q_tok, the GPU's rows.
 
     With ``d`` (the DraftResult of compare_draft, teacher-forced on the GPU's
-    tokens), the oracle also verifies with its own q_tok: only the accept
-    decisions depend on q_tok (the residual rebuilds q from U and the
-    weights), so the accepted counts must agree, except where the first
-    differing decision has u within OWN_Q_BAND * p/q of p/q."""
+    tokens), the oracle also verifies with its own q of the GPU's tokens
+    (own_q_of_gpu_tokens): only the accept decisions depend on q_tok (the
+    residual rebuilds q from U and the weights), so the accepted counts must
+    agree, except where the first differing decision has u within
+    OWN_Q_BAND * p/q of p/q."""
     hs = g.get("h")  # the RNN head's states (the verify's input), else None
     v = oracle.verify(g["rows"], g["row_offsets"], inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"],
                       g["q_tok"], inp.temp, inp.u_accept, inp.u_final, requests=reqs, h_states=hs)
     off = g["row_offsets"]
     if d is not None:
-        v2 = oracle.verify(g["rows"], off, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"], d.q_tok,
+        q_own = own_q_of_gpu_tokens(inp, g, d, reqs)
+        v2 = oracle.verify(g["rows"], off, inp.U, inp.W1, inp.W2, inp.wdtype, inp.anchor, g["y"], q_own,
                            inp.temp, inp.u_accept, inp.u_final, requests=reqs, h_states=hs)
         for r in reqs:
             l = int(off[r + 1] - off[r] - 1)
@@ -228,7 +262,7 @@ def compare_verify(inp, g, reqs, tally: Tally, d=None):
             if ng == n2:
                 continue
             j = min(ng, n2)
-            ratio = float(v2.p_tok[r, j]) / float(d.q_tok[r, j])
+            ratio = float(v2.p_tok[r, j]) / float(q_own[r, j])
             u = float(inp.u_accept[r, j])
             if inp.temp[r] > 0 and abs(u - ratio) <= OWN_Q_BAND * ratio:
                 tally.own_q_flips += 1
