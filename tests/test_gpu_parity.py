@@ -95,6 +95,47 @@ def test_small_shapes(case):
     _run(inp)
 
 
+def random_shapes(n, seed):
+    """n seeded random step shapes inside the library's limits, over every
+    path (16-row and 64-row bf16, fp32 weights), every policy and capacity
+    mode, Zipf-shaped or normal base logits, sized so that the oracle takes
+    about a second for each."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        wd = "f32" if rng.random() < 0.2 else "bf16"
+        wide = wd == "bf16" and rng.random() < 0.5
+        R = (int(rng.choice([65, 66, 79, 80, 95, 96, 97, 128, 129, 255, 256, 257, 300, 511, 513, 700, 1024, 1100]))
+             if wide else int(rng.integers(1, 65)))
+        gamma = int(rng.integers(1, 17))
+        rank = int(8 * rng.integers(1, 65))
+        V = int(rng.choice([int(rng.integers(2, 200)), int(rng.integers(200, 5000)), int(rng.integers(5000, 70000))]))
+        pol = str(rng.choice(["greedy", "sampled", "temps", "mixed"]))
+        km = str(rng.choice(["fixed", "uniformK", "2R"]))
+        seed_i = int(rng.integers(1, 1 << 30))
+        zipf = float(rng.choice([0.0, 1.1])) or None
+        noise = float(rng.choice([0.5, 1.0]))
+        if R * gamma * V * rank > 2.5e10 or R * V > 4e7 or (R + 1023) // 1024 * gamma > 16:
+            continue
+        out.append((seed_i, R, gamma, V, rank, wd, pol, km, zipf, noise))
+    return out
+
+
+# a flagged CDF-boundary flip at a draft position, where the re-verification
+# must take the oracle's q of the GPU's token
+RANDOM = [(648926920, 256, 3, 29075, 224, "bf16", "mixed", "uniformK", None, 1.0)] + random_shapes(40, 20240)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[f"rnd{i}" for i in range(len(RANDOM))])
+def test_random_shapes(case):
+    seed, R, gamma, V, rank, wd, pol, km, zipf, noise = case
+    name = f"random seed={seed} R={R} gamma={gamma} V={V} rank={rank} {wd} {pol} {km} zipf={zipf} noise={noise}"
+    print(name, flush=True)
+    inp = synth.make_custom(seed, R, gamma, V, rank, wdtype=wd, policy=pol, K_mode=km, zipf=zipf,
+                            U_std=None if zipf else 3.0, noise_std=noise, name=name)
+    _run(inp)
+
+
 def test_target_only_fallback_K0():
     """K = 0: nothing is verified, one row per request, the emitted token is
     the bonus draw from row 0 (target-only decoding)."""
