@@ -117,6 +117,8 @@ def random_shapes(n, seed):
         noise = float(rng.choice([0.5, 1.0]))
         if R * gamma * V * rank > 2.5e10 or R * V > 4e7 or (R + 1023) // 1024 * gamma > 16:
             continue
+        if km == "uniformK" and gamma < 2:  # K ~ U{R .. R gamma / 2} needs gamma >= 2
+            km = "fixed"
         out.append((seed_i, R, gamma, V, rank, wd, pol, km, zipf, noise))
     return out
 
@@ -134,6 +136,36 @@ def test_random_shapes(case):
     inp = synth.make_custom(seed, R, gamma, V, rank, wdtype=wd, policy=pol, K_mode=km, zipf=zipf,
                             U_std=None if zipf else 3.0, noise_std=noise, name=name)
     _run(inp)
+
+
+@pytest.mark.parametrize("case", random_shapes(12, 4242), ids=[f"rndp{i}" for i in range(12)])
+def test_random_shapes_packed_or_cutoff(case):
+    """Random shapes again, half with the fragment-packed W2 and the top-K
+    schedule (bf16, R <= 64: the layout of the 16-row kernel), the rest with
+    the static cutoff schedule at a random confidence threshold."""
+    seed, R, gamma, V, rank, wd, pol, km, zipf, noise = case
+    use_pack = wd == "bf16" and R <= 64 and seed % 2 == 0
+    conf_min = (0.05, 0.3, 0.6, 0.9)[seed % 4]
+    name = f"random seed={seed} R={R} gamma={gamma} V={V} rank={rank} {wd} {pol} {km} zipf={zipf} noise={noise}"
+    name += " packed" if use_pack else f" cutoff {conf_min}"
+    print(name, flush=True)
+    inp = synth.make_custom(seed, R, gamma, V, rank, wdtype=wd, policy=pol, K_mode=km, zipf=zipf,
+                            U_std=None if zipf else 3.0, noise_std=noise, name=name)
+    d = upload(inp)
+    reqs = list(range(R))
+    t = Tally()
+    if use_pack:
+        import draft_verify_sampling_bias_amd as ds
+        g = gpu_step(d, inp.K, gamma, W2_packed=ds.dspark_pack_w2(d["W2"]))
+        dr = compare_draft(inp, g, reqs, t)
+        compare_schedule(inp, g, inp.K)
+    else:
+        g = gpu_step(d, None, gamma, conf_min=conf_min)
+        dr = compare_draft(inp, g, reqs, t)
+        compare_schedule(inp, g, None, conf_min=conf_min)
+    compare_verify(inp, g, reqs, t, dr)
+    print(f"[{name}] {t.summary()}", flush=True)
+    t.check()
 
 
 def test_target_only_fallback_K0():

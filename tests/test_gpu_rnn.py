@@ -57,6 +57,40 @@ def test_rnn_small_shapes(case):
     _run_rnn(inp, A, act)
 
 
+def _random_rnn_cases(n, seed):
+    """Seeded random RNN-head shapes (bf16, R <= 64), both activations, three
+    recurrence scales, with and without the packed W2."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        R, gamma, rank = int(rng.integers(1, 65)), int(rng.integers(1, 17)), int(8 * rng.integers(1, 65))
+        V = int(rng.choice([int(rng.integers(2, 200)), int(rng.integers(200, 5000)), int(rng.integers(5000, 70000))]))
+        pol = str(rng.choice(["greedy", "sampled", "temps", "mixed"]))
+        km = str(rng.choice(["fixed", "uniformK", "2R"]))
+        s, act, scale = int(rng.integers(1, 1 << 30)), int(rng.integers(0, 2)), float(rng.choice([0.5, 0.9, 1.3]))
+        packed = bool(rng.random() < 0.5)
+        if R * gamma * V * rank > 2.5e10:
+            continue
+        if km == "uniformK" and gamma < 2:
+            km = "fixed"
+        out.append((s, R, gamma, V, rank, pol, km, act, scale, packed))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_rnn_cases(12, 777), ids=[f"rrnd{i}" for i in range(12)])
+def test_rnn_random_shapes(case):
+    seed, R, gamma, V, rank, pol, km, act, scale, packed = case
+    print(f"rnn random seed={seed} R={R} gamma={gamma} V={V} rank={rank} {pol} {km} act={act} scale={scale} "
+          f"packed={packed}", flush=True)
+    inp = synth.make_custom(seed, R, gamma, V, rank, policy=pol, K_mode=km, U_std=3.0, noise_std=1.0)
+    A = synth.make_rnn_A(seed, rank, scale=scale)
+    W2p = None
+    if packed:
+        import draft_verify_sampling_bias_amd as ds
+        W2p = ds.dspark_pack_w2(upload(inp)["W2"])
+    _run_rnn(inp, A, act, W2_packed=W2p)
+
+
 def test_rnn_packed_w2():
     """The fragment-packed W2 gives the same results as W2 itself."""
     import draft_verify_sampling_bias_amd as ds
