@@ -23,6 +23,11 @@
 namespace dspark {
 namespace {
 
+// Relative distance within which the residual rescan's recomputed segment
+// maximum counts as the draft's maximum (rounding of fp32 dot products of
+// up to 512 terms in two summation orders stays far below it).
+constexpr float kRoundSnap = 0x1p-16f;
+
 template <typename WT, int STAGE, int NT>
 __global__ void __launch_bounds__(NT) draft_finish_kernel(FinishParams p) {
   __shared__ FinishSmem sm;
@@ -56,7 +61,7 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
   __shared__ float hs[DSPARK_MAX_RANK];
   __shared__ Loc2Scratch sh2;
   __shared__ ChunkScratch sh;
-  __shared__ float e64[kMaxSegRows];
+  __shared__ float s64[kMaxSegRows], t64[kMaxSegRows];
   __shared__ int s_out;
   __shared__ float2 srec[STAGED ? STAGE : 1];
   const int n = blockIdx.x, tid = threadIdx.x;
@@ -105,18 +110,27 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
     const float uv = p.U[urow * V + vc], tv = tr[vc];
     const float b = row_bias<WT>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);
     if ((tid & ((1 << lg) - 1)) == 0) {
-      float w = 0.0f;
-      if (v < V) {
-        const float s = uv + b;
-        const float q = exp2_hw((s - Mq) * c) * iZq;
-        const float pp = exp2_hw((tv - Mp) * c) * iZp;
-        w = fmaxf(pp - q, 0.0f);
-      }
-      e64[i] = w;
+      s64[i] = (v < V) ? uv + b : -INFINITY;
+      t64[i] = (v < V) ? tv : -INFINITY;
     }
     __syncthreads();
     if (tid < 64) {
-      const int pos = pick64(e64, p.seg_rows, th);
+      const int ns = p.seg_rows;
+      const float sv = tid < ns ? s64[tid] : -INFINITY, tl = tid < ns ? t64[tid] : -INFINITY;
+      // q relative to the draft's maximum Mq.  The rescanned logits can
+      // differ from the records' by rounding (fp32 weights summed in another
+      // order than the fused kernel's, which gave the top row exactly Mq);
+      // when the segment's own maximum lies within that rounding of Mq and
+      // c would still magnify the difference beyond a factor of 2, the
+      // segment holds the top row and its own maximum is the reference.
+      float mr = sv;
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mr = fmaxf(mr, __shfl_xor(mr, d));
+      const float dq = mr - Mq;
+      const float ref = (fabsf(dq) <= kRoundSnap * fabsf(Mq) && fabsf(dq * c) > 1.0f) ? mr : Mq;
+      const float q = (sv == -INFINITY) ? 0.0f : exp2_rel(sv, ref, c) * iZq;
+      const float pp = exp2_hw((tl - Mp) * c) * iZp;
+      const int pos = pick64_reg(tid < ns ? fmaxf(pp - q, 0.0f) : 0.0f, th);
       if (tid == 0) s_out = (pos >= 0) ? v0 + pos : -1;
     }
     __syncthreads();

@@ -129,7 +129,7 @@ __device__ __forceinline__ void block_amax_once(float& m, int& i, float* lm, int
 struct FinishSmem {
   float hs[DSPARK_MAX_RANK];
   Loc2Scratch sh;
-  float e64[kMaxSegRows], s64[kMaxSegRows];
+  float s64[kMaxSegRows];
 };
 
 // The draft finish of request n at position p.k, by one workgroup of NT
@@ -150,7 +150,6 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
   constexpr bool STAGED = STAGE > 0;
   float* hs = sm.hs;
   Loc2Scratch& sh = sm.sh;
-  float* e64 = sm.e64;
   float* s64 = sm.s64;
   const int tid = threadIdx.x;
   const int V = p.V, n_seg = p.n_seg;
@@ -206,7 +205,11 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
   const Located2 L = locate_blocked<NT>(n_seg, mass, u, &sh);
   const int seg = L.seg < 0 ? 0 : L.seg;
   const float ms = fine[seg].x;
+  // the chosen segment's mass relative to its record maximum, and the
+  // fraction of it left over by the search over the records
+  const float rec = fine[seg].y;
   const float th = L.fallback ? INFINITY : L.rem / exp2_hw((ms - M) * c);
+  const float frac = L.fallback ? INFINITY : (rec > 0.0f ? th / rec : 0.0f);
   const int seg_rows = SEG > 0 ? SEG : p.seg_rows;
   const int lg = lanes_log2<NT>(seg_rows);
   const int v0 = seg * seg_rows;
@@ -218,23 +221,16 @@ __device__ __forceinline__ void draft_finish_one(const FinishParams& p, int n, i
   // lanes per row known at compile time when SEG is: fewer weight chunks per lane
   constexpr int kMinLg = SEG > 0 ? (SEG == kSegSmall ? 4 : (SEG == kSegLarge ? 3 : 2)) + (NT == 1024 ? 2 : (NT == 512 ? 1 : 0)) : 2;
   const float b = row_bias<WT, kMinLg>(static_cast<const WT*>(p.W2), hs, p.rank, v, V, lg);
-  if ((tid & ((1 << lg) - 1)) == 0) {
-    float s = -INFINITY, e = 0.0f;
-    if (v < V) {
-      s = uv + b;
-      e = exp2_hw((s - ms) * c);
-    }
-    e64[i] = e;
-    s64[i] = s;
-  }
+  if ((tid & ((1 << lg) - 1)) == 0) s64[i] = (v < V) ? uv + b : -INFINITY;
   __syncthreads();
   if (tid < 64) {
-    const int pos = pick64(e64, seg_rows, th);
+    // weights relative to the rescan's own maximum (seg_pick_own_max); q of
+    // the drawn row = its share of the segment times the segment's share of Z
+    const SegPick sp = seg_pick_own_max(tid < seg_rows ? s64[tid] : -INFINITY, seg_rows, c, frac);
     if (tid == 0) {
-      const int yy = (pos >= 0) ? v0 + pos : min(v0, V - 1);
-      const float sy = (pos >= 0) ? s64[pos] : M;
+      const int yy = (sp.pos >= 0) ? v0 + sp.pos : min(v0, V - 1);
       p.y[o] = yy;
-      p.q_tok[o] = exp2_hw((sy - M) * c) / L.Z;
+      p.q_tok[o] = (sp.pos >= 0) ? sp.qin * (rec * exp2_rel(ms, M, c) / L.Z) : 1.0f / L.Z;
       p.q_stats[2 * o] = M;
       p.q_stats[2 * o + 1] = L.Z;
     }
@@ -266,12 +262,13 @@ struct WaveFinishSmem {
   float wm[NT / 64];
   float ws[NT / 64];
   int wi[NT / 64];
-  float tx[64 * kWaveFinishJ];  // the chosen wavefront's masses, then the chosen record's maximum
-  // 64-row segments: the chosen segment, its threshold and maximum, and the
-  // rescanned rows' weights and logits
+  float tx[64 * kWaveFinishJ];  // the chosen wavefront's masses, then the chosen record (max, mass)
+  // 64-row segments: the chosen segment, the fraction of its mass left over
+  // by the search, its record's maximum and mass, and the rescanned rows'
+  // logits
   int hseg;
-  float hths, hms;
-  float e64[kMaxSegRows], s64[kMaxSegRows];
+  float hfrac, hms, hrec;
+  float s64[kMaxSegRows];
   // RNN head, next state fused: the drafted token
   int ynext;
 };
@@ -368,18 +365,24 @@ __device__ __forceinline__ void draft_finish_waves_pick(const FinishParams& p, W
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
   for (int j = 0; j < J; ++j)
-    if (j < L && j * 64 + lane == q) sm.tx[0] = r[j].x;
+    if (j < L && j * 64 + lane == q) {
+      sm.tx[0] = r[j].x;
+      sm.tx[1] = r[j].y;
+    }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   const float ms = q >= 0 ? sm.tx[0] : M;
+  const float rec = q >= 0 ? sm.tx[1] : 0.0f;  // its mass relative to ms
   const int seg = q >= 0 ? w0 + q : 0;
   const float ths = fb ? INFINITY : (th - selP) / exp2_rel(ms, M, c);
+  const float frac = fb ? INFINITY : (rec > 0.0f ? ths / rec : 0.0f);
   if constexpr (SEG == kSegWide) {
     if (lane == 0) {
       sm.hseg = seg;
-      sm.hths = ths;
+      sm.hfrac = frac;
       sm.hms = ms;
+      sm.hrec = rec;
     }
     return;
   }
@@ -389,26 +392,16 @@ __device__ __forceinline__ void draft_finish_waves_pick(const FinishParams& p, W
   const int v = v0 + i;
   const float uv = p.U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
   const float b = row_bias<WT, 2>(static_cast<const WT*>(p.W2), sm.hs, p.rank, v, V, 2);
-  float sv = -INFINITY, e = 0.0f;
-  if (v < V) {
-    sv = uv + b;
-    e = exp2_rel(sv, ms, c);
-  }
-  // row i's weight and logit to lane i, then the inverse-CDF pick in the row
-  const float el = __shfl(e, (lane & 15) * 4);
+  const float sv = (v < V) ? uv + b : -INFINITY;
+  // row i's logit to lane i, then the pick in the segment with weights
+  // relative to the rescan's own maximum (seg_pick_own_max)
   const float sl = __shfl(sv, (lane & 15) * 4);
-  const float xl = lane < kSegSmall ? el : 0.0f;
-  const float cl = wave_incl_scan(xl);
-  const unsigned long long rhit = __ballot(xl > 0.0f && cl > ths);
-  const unsigned long long rpos = __ballot(xl > 0.0f);
-  const int pk = rhit ? (__ffsll(static_cast<long long>(rhit)) - 1)
-                      : (rpos ? 63 - __clzll(static_cast<long long>(rpos)) : -1);
+  const SegPick sp = seg_pick_own_max(sl, kSegSmall, c, frac);
   if (lane == 0) {
-    const int yy = (pk >= 0) ? v0 + pk : min(v0, V - 1);
-    const float sy = (pk >= 0) ? readlane_f(sl, pk) : M;
+    const int yy = (sp.pos >= 0) ? v0 + sp.pos : min(v0, V - 1);
     sm.ynext = yy;
     p.y[o] = yy;
-    p.q_tok[o] = exp2_hw((sy - M) * c) / Z;
+    p.q_tok[o] = (sp.pos >= 0) ? sp.qin * (rec * exp2_rel(ms, M, c) / Z) : 1.0f / Z;
     p.q_stats[2 * o] = M;
     p.q_stats[2 * o + 1] = Z;
   }
@@ -422,30 +415,22 @@ __device__ __forceinline__ void draft_finish_rescan64(const FinishParams& p, Wav
   const int tid = threadIdx.x;
   const int V = p.V;
   const int seg = sm.hseg;
-  const float ths = sm.hths, ms = sm.hms;
+  const float frac = sm.hfrac, ms = sm.hms, rec = sm.hrec;
   constexpr int kLg = NT == 1024 ? 4 : (NT == 512 ? 3 : 2);  // log2 of the lanes per row
   const int v0 = seg * kSegWide;
   const int i = tid >> kLg;
   const int v = v0 + i;
   const float uv = p.U_base[static_cast<int64_t>(n) * p.U_stride + min(v, V - 1)];
   const float b = row_bias<WT, kLg>(static_cast<const WT*>(p.W2), sm.hs, p.rank, v, V, kLg);
-  if ((tid & ((1 << kLg) - 1)) == 0) {
-    float sv = -INFINITY, e = 0.0f;
-    if (v < V) {
-      sv = uv + b;
-      e = exp2_rel(sv, ms, c);
-    }
-    sm.e64[i] = e;
-    sm.s64[i] = sv;
-  }
+  if ((tid & ((1 << kLg) - 1)) == 0) sm.s64[i] = (v < V) ? uv + b : -INFINITY;
   __syncthreads();
   if (tid < 64) {
-    const int pos = pick64(sm.e64, kSegWide, ths);
+    // weights relative to the rescan's own maximum (seg_pick_own_max)
+    const SegPick sp = seg_pick_own_max(sm.s64[tid], kSegWide, c, frac);
     if (tid == 0) {
-      const int yy = (pos >= 0) ? v0 + pos : min(v0, V - 1);
-      const float sy = (pos >= 0) ? sm.s64[pos] : M;
+      const int yy = (sp.pos >= 0) ? v0 + sp.pos : min(v0, V - 1);
       p.y[o] = yy;
-      p.q_tok[o] = exp2_hw((sy - M) * c) / Z;
+      p.q_tok[o] = (sp.pos >= 0) ? sp.qin * (rec * exp2_rel(ms, M, c) / Z) : 1.0f / Z;
       p.q_stats[2 * o] = M;
       p.q_stats[2 * o + 1] = Z;
     }

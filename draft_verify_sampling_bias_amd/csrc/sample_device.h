@@ -261,14 +261,47 @@ __device__ Located2 locate_blocked(int n, Mass mass, float u, Loc2Scratch* sh) {
 
 // Wave 0: first of n <= 64 weights whose inclusive prefix exceeds theta,
 // else the last positive one, else -1.
-__device__ __forceinline__ int pick64(const float* e, int n, float theta) {
-  const int lane = threadIdx.x & 63;
-  const float x = (lane < n) ? e[lane] : 0.0f;
+__device__ __forceinline__ int pick64_reg(float x, float theta) {
   const float cum = wave_incl_scan(x);
   const unsigned long long hit = __ballot(x > 0.0f && cum > theta);
   if (hit) return __ffsll(static_cast<long long>(hit)) - 1;
   const unsigned long long pos = __ballot(x > 0.0f);
   return pos ? 63 - __clzll(static_cast<long long>(pos)) : -1;
+}
+__device__ __forceinline__ int pick64(const float* e, int n, float theta) {
+  const int lane = threadIdx.x & 63;
+  return pick64_reg((lane < n) ? e[lane] : 0.0f, theta);
+}
+
+// The draw inside the chosen segment from the rows' logits as a rescan
+// recomputes them (lane i: row i of n <= 64, -inf where masked), by a whole
+// wavefront.  Those logits can differ from the ones the segment records were
+// built from by rounding (fp32 weights summed in another order than the
+// fused kernel's), and a large scale c (a tiny temperature) turns such a
+// difference into 2^(+-huge) when it is measured against the record's
+// maximum.  The weights are therefore taken relative to the rescan's own
+// maximum, where the top row weighs exactly 1, and the draw uses the rescan's
+// own total with the fraction frac of the segment's mass that the search over
+// the records left over.  With logits identical to the records' the draw is
+// the one against the records.  Returns the row (-1: no positive weight) and
+// its probability within the segment.
+struct SegPick {
+  int pos;
+  float qin;
+};
+__device__ __forceinline__ SegPick seg_pick_own_max(float sv, int n, float c, float frac) {
+  const int lane = threadIdx.x & 63;
+  if (lane >= n) sv = -INFINITY;
+  float mr = sv;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) mr = fmaxf(mr, __shfl_xor(mr, d));
+  const float e = (sv == -INFINITY) ? 0.0f : exp2_rel(sv, mr, c);
+  float tot = e;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) tot += __shfl_xor(tot, d);
+  const int pos = pick64_reg(e, frac * tot);
+  const float ey = __shfl(e, pos < 0 ? 0 : pos);
+  return SegPick{pos, (pos >= 0 && tot > 0.0f) ? ey / tot : 0.0f};
 }
 
 // Eight consecutive weights of a row, loaded raw, and their product with h
