@@ -7,11 +7,14 @@ Comparison rules (decisions are compared, values within tolerance):
     argmax, CDF edge, u within 1e-6 of p/q); such flips are counted;
   * the oracle is teacher-forced with the GPU's drafted prefix, so a flagged
     flip does not cascade into later positions;
-  * probabilities (q_tok, p_tok, Z) and survival within 1e-5 relative;
+  * probabilities (q_tok, p_tok, Z) and survival within 1e-5 relative; for a
+    sampled request's q_tok and Z, within the rounding of its fp32 logits
+    magnified by 1/T where that is larger (q_rel_tol);
   * every accept decision is also re-taken by the oracle with its own q of
     the GPU's drafted tokens (not the GPU's q_tok): a decision that then differs from
     the GPU's is allowed only where u lies within 1e-5 * p/q of p/q (the
-    two q_tok may differ by the 1e-5 tolerance), and is counted.
+    two q_tok may differ by their tolerance, q_rel_tol where larger), and
+    is counted.
 """
 from __future__ import annotations
 
@@ -82,6 +85,20 @@ def gpu_step(d, K, gamma, conf_min=None, W2_packed=None, A=None, act=1):
     if h is not None:
         res["h"] = h
     return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def q_rel_tol(T, Ms):
+    """Relative tolerance of a draw's q_tok and Z: REL, or, for a sampled
+    request, the rounding of its fp32 logits (2^-21 max(|max s|, 1), a few
+    ulps of the largest logit) carried through 2^((s - max) c) with
+    c = log2(e) / T, i.e. times ln(2) c = 1 / T, where that is larger; at
+    most 0.5, so that a probability of 0 or infinity against 1 still fails.
+    At T = 1 and |max s| ~ 10 it is 5e-6, below REL; a temperature of 1e-3
+    magnifies one ulp of the logits to ~1e-3 of a weight near the maximum."""
+    T = float(T)
+    if not T > 0 or not np.isfinite(Ms):
+        return REL
+    return min(max(REL, 2.0 ** -21 * max(abs(float(Ms)), 1.0) / oracle._sample_T(T)), 0.5)
 
 
 def rel_ok(g, o, rel=REL, abs_floor=0.0):
@@ -175,11 +192,12 @@ def compare_draft(inp, g, reqs, tally: Tally, d=None):
                     tally.failures.append(f"draft r={r} k={k}: gpu y={y_g[r, k]} oracle y={d.y[r, k]} "
                                           f"(T={inp.temp[r]})")
                     continue
-            elif not rel_ok(g["q_tok"][r, k], d.q_tok[r, k]):
+            qt = q_rel_tol(inp.temp[r], d.q_stats[r, k, 0])
+            if y_g[r, k] == d.y[r, k] and not rel_ok(g["q_tok"][r, k], d.q_tok[r, k], rel=qt):
                 tally.failures.append(f"draft q_tok r={r} k={k}: {g['q_tok'][r, k]} vs {d.q_tok[r, k]}")
             if not rel_ok(g["q_stats"][r, k, 0], d.q_stats[r, k, 0], abs_floor=1e-5):
                 tally.failures.append(f"draft max s r={r} k={k}: {g['q_stats'][r, k, 0]} vs {d.q_stats[r, k, 0]}")
-            if not rel_ok(g["q_stats"][r, k, 1], d.q_stats[r, k, 1]):
+            if not rel_ok(g["q_stats"][r, k, 1], d.q_stats[r, k, 1], rel=qt):
                 tally.failures.append(f"draft Z r={r} k={k}: {g['q_stats'][r, k, 1]} vs {d.q_stats[r, k, 1]}")
     return d
 
@@ -264,7 +282,8 @@ def compare_verify(inp, g, reqs, tally: Tally, d=None):
             j = min(ng, n2)
             ratio = float(v2.p_tok[r, j]) / float(q_own[r, j])
             u = float(inp.u_accept[r, j])
-            if inp.temp[r] > 0 and abs(u - ratio) <= OWN_Q_BAND * ratio:
+            band = max(OWN_Q_BAND, q_rel_tol(inp.temp[r], d.q_stats[r, j, 0]))
+            if inp.temp[r] > 0 and abs(u - ratio) <= band * ratio:
                 tally.own_q_flips += 1
             else:
                 tally.failures.append(f"verify with the oracle's q_tok r={r}: gpu n_accept {ng} oracle {n2} "

@@ -168,6 +168,51 @@ def test_random_shapes_packed_or_cutoff(case):
     t.check()
 
 
+def masked_extreme(seed, R, gamma, V, rank, wd, pol, km, dens, n_ext):
+    """Inputs of a random shape with a -inf mask of density dens drawn per
+    (request, position) row of U (one entry of each row kept finite) and at
+    half that density per target row, and n_ext requests at extreme
+    temperatures (+inf, 1e35, 1e30, subnormal, 1e-30, 1e-3, NaN, negative,
+    50, 1, 0)."""
+    ext = np.array([np.inf, 1e35, 1e30, 1e-40, 1e-30, 1e-3, np.nan, -1.0, 50.0, 1.0, 0.0], np.float32)
+    inp = synth.make_custom(seed, R, gamma, V, rank, wdtype=wd, policy=pol, K_mode=km, U_std=3.0, noise_std=1.0,
+                            name=f"masked seed={seed} R={R} gamma={gamma} V={V} rank={rank} {wd} dens={dens}")
+    rng = np.random.default_rng(seed)
+    m = rng.random(inp.U.shape) < dens
+    keep = rng.integers(0, V, size=inp.U.shape[:2])
+    m[np.arange(R)[:, None], np.arange(gamma)[None, :], keep] = False
+    inp.U[m] = -np.inf
+    mt = rng.random(inp.target.shape) < dens * 0.5
+    kt = rng.integers(0, V, size=inp.target.shape[:2])
+    mt[np.arange(R)[:, None], np.arange(gamma + 1)[None, :], kt] = False
+    inp.target[mt] = -np.inf
+    if n_ext:
+        idx = rng.choice(R, size=min(R, n_ext), replace=False)
+        inp.temp[idx] = ext[rng.integers(0, len(ext), size=idx.size)]
+    return inp
+
+
+MASKED = [
+    # fp32 weights, one finite entry per row, T = 1e-40: the rescan's logits
+    # differ from the records' by rounding, which c ~ 1.4e30 magnified
+    (442002694, 48, 8, 13, 488, "f32", "temps", "2R", 0.99, 3),
+    # the same on the 64-row bf16 path
+    (671932773, 300, 10, 131, 184, "bf16", "temps", "fixed", 0.9, 3),
+    # T = 1e-3 with a second entry 0.0025 below the maximum: q and Z within
+    # the fp32 logits' rounding magnified by 1 / T
+    (864547394, 60, 5, 22824, 80, "bf16", "mixed", "2R", 0.5, 2),
+    (313279300, 256, 5, 24, 328, "bf16", "mixed", "fixed", 0.5, 3),
+    (417947361, 6, 7, 19113, 120, "bf16", "mixed", "uniformK", 0.99, 2),
+    (512710369, 47, 5, 15408, 224, "bf16", "temps", "2R", 0.5, 0),
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[f"mask{i}" for i in range(len(MASKED))])
+def test_random_masks_and_extreme_temperatures(case):
+    print("masked", case, flush=True)
+    _run(masked_extreme(*case))
+
+
 def test_target_only_fallback_K0():
     """K = 0: nothing is verified, one row per request, the emitted token is
     the bonus draw from row 0 (target-only decoding)."""
