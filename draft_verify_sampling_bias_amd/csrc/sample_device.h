@@ -292,15 +292,21 @@ struct SegPick {
 __device__ __forceinline__ SegPick seg_pick_own_max(float sv, int n, float c, float frac) {
   const int lane = threadIdx.x & 63;
   if (lane >= n) sv = -INFINITY;
+  // maximum over the lanes that hold rows (lanes past n keep -inf and
+  // weight 0 whatever they see)
   float mr = sv;
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mr = fmaxf(mr, __shfl_xor(mr, d));
+  for (int d = 32; d >= 1; d >>= 1)
+    if (d < n) mr = fmaxf(mr, __shfl_xor(mr, d));
   const float e = (sv == -INFINITY) ? 0.0f : exp2_rel(sv, mr, c);
-  float tot = e;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) tot += __shfl_xor(tot, d);
-  const int pos = pick64_reg(e, frac * tot);
-  const float ey = __shfl(e, pos < 0 ? 0 : pos);
+  // the inclusive scan gives the total at lane 63, then the pick as in pick64
+  const float cum = wave_incl_scan(e);
+  const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
+  const unsigned long long hit = __ballot(e > 0.0f && cum > frac * tot);
+  const unsigned long long any = __ballot(e > 0.0f);
+  const int pos = hit ? (__ffsll(static_cast<long long>(hit)) - 1)
+                      : (any ? 63 - __clzll(static_cast<long long>(any)) : -1);
+  const float ey = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), pos < 0 ? 0 : pos));
   return SegPick{pos, (pos >= 0 && tot > 0.0f) ? ey / tot : 0.0f};
 }
 
