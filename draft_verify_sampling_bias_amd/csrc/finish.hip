@@ -27,6 +27,9 @@ namespace {
 // maximum counts as the draft's maximum (rounding of fp32 dot products of
 // up to 512 terms in two summation orders stays far below it).
 constexpr float kRoundSnap = 0x1p-16f;
+// magnitude below which the distance is taken absolute (2^-16 * 2^-10): a
+// maximum of exactly 0 still admits the rounding of its dot product
+constexpr float kRoundFloor = 0x1p-10f;
 
 template <typename WT, int STAGE, int NT>
 __global__ void __launch_bounds__(NT) draft_finish_kernel(FinishParams p) {
@@ -127,7 +130,7 @@ __global__ void __launch_bounds__(256) residual_finish_kernel(VerifyParams p) {
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) mr = fmaxf(mr, __shfl_xor(mr, d));
       const float dq = mr - Mq;
-      const float ref = (fabsf(dq) <= kRoundSnap * fabsf(Mq) && fabsf(dq * c) > 1.0f) ? mr : Mq;
+      const float ref = (fabsf(dq) <= kRoundSnap * fmaxf(fabsf(Mq), kRoundFloor) && fabsf(dq * c) > 1.0f) ? mr : Mq;
       const float q = (sv == -INFINITY) ? 0.0f : exp2_rel(sv, ref, c) * iZq;
       const float pp = exp2_hw((tl - Mp) * c) * iZp;
       const int pos = pick64_reg(tid < ns ? fmaxf(pp - q, 0.0f) : 0.0f, th);
