@@ -157,14 +157,24 @@ __device__ __forceinline__ int wave_max_int(int x) {
   return x;
 }
 
-// Inclusive scan inside a wavefront (Hillis-Steele, fixed order).
+// v of the lane that DPP control CTRL names, 0 where it names none or the
+// row is outside ROW_MASK (VALU data-parallel primitives, no LDS round trip)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+}
+
+// Inclusive scan inside a wavefront (fixed order): Hillis-Steele inside each
+// 16-lane row (row_shr 1, 2, 4, 8), then row 0's total into row 1 and row
+// 2's into row 3 (row_bcast:15), then row 1's running total into rows 2 and
+// 3 (row_bcast:31).
 __device__ __forceinline__ float wave_incl_scan(float v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    float o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
+  v += dpp_or_zero<0x111, 0xf>(v);
+  v += dpp_or_zero<0x112, 0xf>(v);
+  v += dpp_or_zero<0x114, 0xf>(v);
+  v += dpp_or_zero<0x118, 0xf>(v);
+  v += dpp_or_zero<0x142, 0xa>(v);
+  v += dpp_or_zero<0x143, 0xc>(v);
   return v;
 }
 
